@@ -1,0 +1,377 @@
+"""Pins of the float64 oracle against things other than itself: library decode
+tables, exact-rational brute force, closed forms, invariants and a library
+attention routine. CPU only."""
+from fractions import Fraction
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import msa_oracle as O
+from synth import workloads as W
+
+
+# ------------------------------------------------------------------ format tables
+def test_e4m3_table_matches_torch_float8_e4m3fn():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    tab = O.e4m3_table()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(tab), nan)
+    assert nan.sum() == 2 and nan[0x7F] and nan[0xFF]
+    assert np.array_equal(tab[~nan], ref[~nan])
+
+
+def test_e4m3_table_anchors():
+    t = O.E4M3
+    assert t[0x7E] == 448.0 and t[0xFE] == -448.0
+    assert t[0x08] == 2.0 ** -6 and t[0x01] == 2.0 ** -9 and t[0x07] == 7 * 2.0 ** -9
+    assert t[0x38] == 1.0 and t[0x40] == 2.0 and t[0xC0] == -2.0 and t[0x00] == 0.0
+    finite = t[~np.isnan(t)]
+    assert np.nanmax(np.abs(finite)) == 448.0
+    # codes 0..126 are strictly increasing (used by the encoder as a grid)
+    assert np.all(np.diff(t[:127]) > 0)
+
+
+def test_e2m1_table_anchors():
+    t = O.E2M1
+    assert list(t[:8]) == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert list(t[8:]) == [-0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+
+
+# ------------------------------------------------------------------ encoders
+def _fr(x):
+    return Fraction(float(x))
+
+
+def _brute_nearest(x, values_by_code, codes, lsb_even):
+    """Nearest code by exact rational distance; ties to the code with even LSB."""
+    fx = _fr(x)
+    best, bestd = None, None
+    for c in codes:
+        d = abs(fx - _fr(values_by_code[c]))
+        if bestd is None or d < bestd or (d == bestd and lsb_even(c) and not lsb_even(best)):
+            best, bestd = c, d
+    return best
+
+
+def _brute_e4m3(x):
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    neg = math.copysign(1.0, float(x)) < 0
+    codes = [c for c in range(256) if not np.isnan(ref[c]) and ((c >= 0x80) == neg)]
+    if abs(float(x)) >= 448.0:
+        return 0xFE if neg else 0x7E
+    return _brute_nearest(x, ref, codes, lambda c: c % 2 == 0)
+
+
+def _e4m3_probe_values():
+    t = O.E4M3[:127]
+    mids = (t[:-1] + t[1:]) / 2            # exact ties
+    rng = np.random.default_rng(11)
+    rnd = rng.standard_normal(300) * np.exp2(rng.integers(-12, 10, 300))
+    v = np.concatenate([t, mids, np.nextafter(mids, 0), np.nextafter(mids, 1e9), rnd,
+                        [450.0, 463.9, 464.0, 1e6, 2.0 ** -10, 2.0 ** -11, 3 * 2.0 ** -11]])
+    v = np.concatenate([v, -v]).astype(np.float32).astype(np.float64)
+    return v
+
+
+def test_e4m3_encode_brute_force_and_torch():
+    v = _e4m3_probe_values()
+    got = O.e4m3_encode(v)
+    for x, c in zip(v, got):
+        assert c == _brute_e4m3(x), (x, c)
+    inr = np.abs(v) < 448.0
+    tor = torch.tensor(v[inr], dtype=torch.float32).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    # torch keeps the sign of values that round to zero, as we do
+    assert np.array_equal(tor, got[inr])
+
+
+def _brute_e2m1(x):
+    neg = math.copysign(1.0, float(x)) < 0
+    codes = list(range(8, 16)) if neg else list(range(8))
+    if abs(float(x)) >= 6.0:
+        return 15 if neg else 7
+    return _brute_nearest(x, O.E2M1, codes, lambda c: c % 2 == 0)
+
+
+def test_e2m1_encode_brute_force_with_ties():
+    grid = O.E2M1[:8]
+    mids = (grid[:-1] + grid[1:]) / 2
+    v = np.concatenate([grid, mids, np.nextafter(mids, 0), np.nextafter(mids, 10),
+                        [6.5, 7.0, 100.0, 0.1, 0.3]])
+    v = np.concatenate([v, -v])
+    got = O.e2m1_encode(v)
+    for x, c in zip(v, got):
+        assert c == _brute_e2m1(x), (x, c)
+    # explicit tie outcomes (round half to even code)
+    exp = {0.25: 0, 0.75: 2, 1.25: 2, 1.75: 4, 2.5: 4, 3.5: 6, 5.0: 6}
+    for x, c in exp.items():
+        assert O.e2m1_encode(np.array([x]))[0] == c
+
+
+def _f32(fr):
+    return Fraction(float(np.float32(float(fr))))
+
+
+def _brute_nvfp4_group(x16, t):
+    """The stated NVFP4 recipe computed with exact rationals and brute-force rounding."""
+    t = _f32(Fraction(float(t)))
+    amax = max(abs(_fr(v)) for v in x16)
+    y = _f32(amax / _f32(6 * t))
+    sc = _brute_e4m3(float(y))
+    dec = _fr(O.E4M3[sc])
+    if dec == 0:
+        return [0] * 16, sc
+    d = _f32(dec * t)
+    return [_brute_e2m1(float(_f32(_fr(v) / d))) for v in x16], sc
+
+
+def test_nvfp4_encode_matches_exact_rational_recipe():
+    rng = np.random.default_rng(5)
+    x = W.bf16_bits_to_f32(W.to_bf16_bits(rng.standard_normal((40, 32), dtype=np.float32)))
+    x[3, :16] *= 1e-4          # tiny group: scale rounds low
+    x[4, :16] = 0.0            # all-zero group
+    x[5, 16:] *= 60.0          # group above the tensor amax: saturating scale
+    t = float(np.float32(4.0 / (6 * 448)))
+    codes, sc = O.nvfp4_encode(x.astype(np.float64), t)
+    for r in range(x.shape[0]):
+        for g in range(2):
+            bc, bs = _brute_nvfp4_group(x[r, 16 * g:16 * g + 16], t)
+            assert sc[r, g] == bs
+            assert list(codes[r, 16 * g:16 * g + 16]) == bc
+
+
+def test_nvfp4_reconstruction_bound():
+    """Every element decodes to within half an E2M1 step (times the group scale)
+    unless it saturates; the group amax lands in the top binade."""
+    rng = np.random.default_rng(6)
+    x = W.bf16_bits_to_f32(W.to_bf16_bits(rng.standard_normal((500, 128), dtype=np.float32))).astype(np.float64)
+    t = float(np.float32(np.abs(x).max() / (6 * 448)))
+    codes, sc = O.nvfp4_encode(x, t)
+    d = np.repeat(O.E4M3[sc] * t, 16, axis=1)
+    rec = O.E2M1[codes] * d
+    step = np.where(np.abs(x / d) < 2, 0.5, np.where(np.abs(x / d) < 4, 1.0, 2.0)) * d
+    assert np.all(np.abs(rec - x) <= step / 2 * (1 + 1e-6) + 1e-30)
+    g = np.abs(x).reshape(500, 8, 16).max(-1) / O.E4M3[sc] / t
+    assert np.all((g > 5.0) & (g < 6.5))
+
+
+def test_pack_nibbles_low_is_even():
+    assert O.pack_nibbles(np.array([1, 2], np.uint8))[0] == 0x21
+    assert list(O.unpack_nibbles(np.array([0xA5], np.uint8))) == [5, 10]
+
+
+def test_fp8_kv_encode_is_scaled_e4m3():
+    x = np.array([1.0, -3.0, 0.0, 1000.0])
+    s = 0.5
+    assert list(O.fp8_kv_encode(x, s)) == [0x40, 0xCC, 0x00, 0x7E]  # 2.0, -6.0 (1.5*2^2), 0, sat
+
+
+# ------------------------------------------------------------------ append
+def test_kv_append_writes_only_its_slot_and_skips_negative():
+    pool = O.new_pool(O.FMT_NVFP4, 4, 2, k_tensor_scale=0.01, v_tensor_scale=0.01)
+    rng = np.random.default_rng(1)
+    kb = W.to_bf16_bits(rng.standard_normal((2, 2, 128), dtype=np.float32))
+    ib = W.to_bf16_bits(rng.standard_normal((2, 64), dtype=np.float32))
+    O.kv_append(pool, np.array([2 * 128 + 5, -1]), kb, kb, ib)
+    nz = np.argwhere(pool["k_codes"] != 0)
+    assert set(map(tuple, nz[:, [0, 2]])) == {(2, 5)}
+    assert np.argwhere(pool["index_k"] != 0)[:, :2].tolist() == [[2, 5]] * int((pool["index_k"] != 0).sum())
+    assert np.array_equal(pool["index_k"][2, 5], O.e4m3_encode(W.bf16_bits_to_f32(ib[0])))
+
+
+# ------------------------------------------------------------------ index score
+def _tiny_pool_with_keys(keys, Hkv=1):
+    """keys: float array [n_tok][64] of E4M3-representable values at positions 0.."""
+    n = keys.shape[0]
+    pages = (n + 127) // 128
+    pool = O.new_pool(O.FMT_FP8, pages + 1, Hkv)
+    bt = np.array([list(range(pages, 0, -1))], dtype=np.int32)   # reversed physical order
+    for p in range(n):
+        b, off = divmod(p, 128)
+        pool["index_k"][bt[0, b], off] = O.e4m3_encode(keys[p])
+    return pool, bt
+
+
+def test_index_score_unit_key_closed_form():
+    keys = np.zeros((130, 64))
+    keys[7, 13] = 1.0          # block 0, a unit key along dim 13
+    keys[129, 2] = 1.0         # block 1
+    pool, bt = _tiny_pool_with_keys(keys)
+    rng = np.random.default_rng(3)
+    q = W.to_bf16_bits(rng.standard_normal((1, 4, 64), dtype=np.float32))
+    w = np.array([[0.25, 0.5, 0.75, 1.0]], np.float32)
+    S = O.index_score(pool, bt, [0], [129], q, w, 3)
+    qf = W.bf16_bits_to_f32(q[0]).astype(np.float64)
+    exp0 = (w[0] * np.maximum(qf[:, 13], 0)).sum()
+    exp1 = (w[0] * np.maximum(qf[:, 2], 0)).sum()
+    assert S[0, 0] == pytest.approx(max(exp0, 0.0), abs=0, rel=1e-15)
+    assert S[0, 1] == pytest.approx(max(exp1, 0.0), abs=0, rel=1e-15)
+    assert S[0, 2] == -np.inf
+
+
+def test_index_score_negative_dots_give_zero_and_mask_hides_future():
+    keys = np.zeros((256, 64))
+    keys[:, 0] = -1.0                     # every dot negative when q[:,0] > 0
+    keys[200, 0] = 8.0                    # a strong key after row_pos
+    pool, bt = _tiny_pool_with_keys(keys)
+    q = np.zeros((1, 4, 64), np.float32)
+    q[0, :, 0] = 1.0
+    S = O.index_score(pool, bt, [0], [150], W.to_bf16_bits(q), np.ones((1, 4), np.float32), 2)
+    assert S[0, 0] == 0.0 and S[0, 1] == 0.0          # masked token 200 not seen
+    S2 = O.index_score(pool, bt, [0], [200], W.to_bf16_bits(q), np.ones((1, 4), np.float32), 2)
+    assert S2[0, 1] == 32.0                            # 4 heads * 1 * 8
+
+
+def test_index_score_invariant_to_physical_page_order():
+    wl = W.small(W.FMT_FP8, [700, 300], 0, num_kv_heads=1, k=2, seed=9)
+    pool = _oracle_pool(wl)
+    S = O.index_score(pool, wl.block_table, wl.row_seq, wl.row_pos, wl.q_idx, wl.w, wl.max_blocks)
+    # move every page to a new physical slot
+    perm = np.random.default_rng(2).permutation(wl.num_pages)
+    pool2 = dict(pool)
+    pool2["index_k"] = np.empty_like(pool["index_k"])
+    pool2["index_k"][perm] = pool["index_k"]
+    bt2 = np.where(wl.block_table >= 0, perm[np.maximum(wl.block_table, 0)], -1)
+    S2 = O.index_score(pool2, bt2, wl.row_seq, wl.row_pos, wl.q_idx, wl.w, wl.max_blocks)
+    assert np.array_equal(S, S2)
+
+
+# ------------------------------------------------------------------ select
+def _dominance_select(S_row, nb, k, n_init, n_local):
+    """The unique k-subset containing the forced blocks in which every chosen
+    free block beats every unchosen free block (higher score, then smaller index)."""
+    forced = set(range(min(n_init, nb))) | set(range(nb - n_local, nb))
+    free = [b for b in range(nb) if b not in forced]
+    beats = lambda a, b: (S_row[a] > S_row[b]) or (S_row[a] == S_row[b] and a < b)
+    found = []
+    for comb in itertools.combinations(free, k - len(forced)):
+        cs = set(comb)
+        if all(beats(a, b) for a in cs for b in free if b not in cs):
+            found.append(sorted(cs | forced))
+    assert len(found) == 1
+    return found[0]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_select_matches_dominance_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    nb, k = 9, 4
+    S = np.round(rng.standard_normal((3, nb + 2)), 1)     # coarse values: many ties
+    S[:, nb:] = -np.inf
+    pos = np.full(3, (nb - 1) * 128 + 17)
+    for n_init in (0, 1):
+        sel = O.select_topk(S, pos, k, n_init=n_init, n_local=1)
+        for r in range(3):
+            assert list(sel[r]) == _dominance_select(S[r], nb, k, n_init, 1)
+
+
+def test_select_tie_break_over_1024_ties():
+    nb, k = 2048, 32
+    S = np.full((1, nb), -5.0)
+    tied = np.sort(np.random.default_rng(4).choice(nb - 1, 1100, replace=False))
+    S[0, tied] = 7.25
+    sel = O.select_topk(S, [nb * 128 - 1], k)
+    assert list(sel[0]) == sorted(list(tied[:k - 1]) + [nb - 1])
+
+
+def test_select_identity_and_padding_and_forced_last():
+    S = np.array([[3.0, 2.0, 1.0, -np.inf, -np.inf]])
+    assert list(O.select_topk(S, [2 * 128 + 5], 5)[0]) == [0, 1, 2, -1, -1]
+    S = np.array([[9.0, 8.0, 7.0, 6.0, -1.0]])   # last block is the worst but forced
+    assert list(O.select_topk(S, [4 * 128], 3)[0]) == [0, 1, 4]
+
+
+# ------------------------------------------------------------------ attention
+def _oracle_pool(wl, with_step=True):
+    pool = O.new_pool(wl.fmt, wl.num_pages, wl.num_kv_heads, k_tensor_scale=wl.k_tensor_scale,
+                      v_tensor_scale=wl.v_tensor_scale, k_page_scale=wl.k_page_scale,
+                      v_page_scale=wl.v_page_scale)
+    sl, kb, vb, ib = wl.prefill_tokens()
+    O.kv_append(pool, sl, kb, vb, ib)
+    if with_step:
+        sl, kb, vb, ib = wl.step_tokens()
+        O.kv_append(pool, sl, kb, vb, ib)
+    return pool
+
+
+def _dense_sdpa(pool, wl, r):
+    """torch scaled_dot_product_attention (float64, CPU) over all visible tokens."""
+    seq, pos = int(wl.row_seq[r]), int(wl.row_pos[r])
+    toks = np.arange(pos + 1)
+    outs = []
+    q = torch.tensor(W.bf16_bits_to_f32(wl.q[r]).astype(np.float64))
+    for g in range(wl.num_kv_heads):
+        K = np.stack([O.dequant_page(pool, int(wl.block_table[seq][t // 128]), g, "k")[t % 128] for t in toks])
+        V = np.stack([O.dequant_page(pool, int(wl.block_table[seq][t // 128]), g, "v")[t % 128] for t in toks])
+        qg = q[16 * g:16 * g + 16][None]                       # [1, 16, D]
+        o = torch.nn.functional.scaled_dot_product_attention(
+            qg, torch.tensor(K)[None].contiguous(), torch.tensor(V)[None].contiguous(),
+            scale=wl.softmax_scale)
+        outs.append(o[0].numpy())
+    return np.concatenate(outs)
+
+
+@pytest.mark.parametrize("fmt", [W.FMT_FP8, W.FMT_NVFP4])
+def test_sparse_equals_dense_when_all_blocks_selected(fmt):
+    wl = W.small(fmt, [300, 129], 2, num_kv_heads=1, k=4, seed=21)
+    pool = _oracle_pool(wl)
+    sel = np.tile(np.arange(4, dtype=np.int32), (wl.num_rows, 1))
+    nb = wl.row_pos // 128 + 1
+    sel = np.where(np.arange(4)[None] < nb[:, None], sel, -1).astype(np.int32)
+    out = O.attend(pool, wl.block_table, wl.row_seq, wl.row_pos, wl.q, sel, wl.softmax_scale)
+    for r in range(wl.num_rows):
+        ref = _dense_sdpa(pool, wl, r)
+        assert np.max(np.abs(out[r] - ref)) < 1e-12
+
+
+def test_split_combine_identity():
+    wl = W.small(W.FMT_NVFP4, [900, 400], 1, num_kv_heads=2, k=5, seed=22)
+    pool = _oracle_pool(wl)
+    S = O.index_score(pool, wl.block_table, wl.row_seq, wl.row_pos, wl.q_idx, wl.w, wl.max_blocks)
+    sel = O.select_topk(S, wl.row_pos, wl.k)
+    ref = O.attend(pool, wl.block_table, wl.row_seq, wl.row_pos, wl.q, sel, wl.softmax_scale)
+    for ns in (1, 2, 3, 5):
+        m, l, Op = O.split_partials(pool, wl.block_table, wl.row_seq, wl.row_pos, wl.q, sel,
+                                    wl.softmax_scale, ns)
+        assert np.max(np.abs(O.combine(m, l, Op) - ref)) < 1e-12
+
+
+def test_attend_single_token_and_equal_logits():
+    pool = O.new_pool(O.FMT_FP8, 2, 1, k_page_scale=[1.0, 1.0], v_page_scale=[1.0, 1.0])
+    pool["v_codes"][1, 0, 0] = O.e4m3_encode(np.full(128, 1.5))
+    pool["v_codes"][1, 0, 1] = O.e4m3_encode(np.full(128, -0.5))
+    bt = np.array([[1]], np.int32)
+    q = W.to_bf16_bits(np.ones((1, 16, 128), np.float32))
+    out = O.attend(pool, bt, [0], [0], q, np.array([[0]], np.int32), 0.1)
+    assert np.all(out == 1.5)                  # one visible token: its V
+    out = O.attend(pool, bt, [0], [1], q, np.array([[0]], np.int32), 0.1)
+    assert np.allclose(out, 0.5, atol=0, rtol=1e-15)   # K = 0: equal logits, mean of V
+
+
+def test_partials_single_token_closed_form():
+    pool = O.new_pool(O.FMT_FP8, 1, 1, k_page_scale=[1.0], v_page_scale=[1.0])
+    pool["k_codes"][0, 0, 0] = O.e4m3_encode(np.full(128, 0.5))
+    pool["v_codes"][0, 0, 0] = O.e4m3_encode(np.full(128, 2.0))
+    q = W.to_bf16_bits(np.ones((1, 16, 128), np.float32))
+    m, l, Op = O.split_partials(pool, np.array([[0]], np.int32), [0], [0], q,
+                                np.array([[0, -1]], np.int32), 0.125, 2)
+    assert np.allclose(m[0, :, 0], 0.125 * 64 * oracle.LOG2E, rtol=1e-15)
+    assert np.all(l[0, :, 0] == 1.0) and np.all(Op[0, :, 0] == 2.0)
+    assert np.all(np.isneginf(m[0, :, 1])) and np.all(l[0, :, 1] == 0)
+
+
+def test_decode_step_small_verify_workload_runs():
+    wl = W.small(W.FMT_NVFP4, [1000, 2600, 130], 3, num_kv_heads=1, k=4, seed=23)
+    pool = _oracle_pool(wl, with_step=False)
+    sl, kb, vb, ib = wl.step_tokens()
+    S, sel, out = O.decode_step(pool, wl.block_table, wl.row_seq, wl.row_pos, sl, kb, vb, ib,
+                                wl.q_idx, wl.w, wl.q, wl.k, wl.softmax_scale, wl.max_blocks)
+    nb = wl.row_pos // 128 + 1
+    for r in range(wl.num_rows):
+        assert sel[r, min(nb[r], wl.k) - 1] == nb[r] - 1 if nb[r] > wl.k else True
+        assert np.all(np.isfinite(S[r, :nb[r]])) and np.all(np.isneginf(S[r, nb[r]:]))
+    assert np.all(np.isfinite(out))
