@@ -1,0 +1,210 @@
+/*
+ * msa_decode.h - C ABI of libmsadecode: block-sparse (MSA-style) attention decode
+ * over a paged FP8 / NVFP4 KV cache on AMD Instinct MI355X (gfx950).
+ *
+ * One decode step is five calls, in this order, all asynchronous on one HIP stream:
+ *
+ *   msa_kv_append      quantise the step's new K, V and index-K into their page slots
+ *   msa_index_score    score every visible token's index key, max-pool per 128-token block
+ *   msa_select_topk    pick k blocks per query row (ties to the smaller block)
+ *   msa_sparse_decode  GQA flash-decode over the selected pages, split-KV partials
+ *   msa_combine        fixed-order log-sum-exp merge of the partials into bf16 outputs
+ *
+ * The operations follow three public TensorRT-LLM pull-request pages:
+ *   [Rubin] "[None][feat] Add Rubin (sm_107) MiniMax-M3.1 low-latency decode targets" (#21136)
+ *   [GB300] "MiniMax-M3 NVFP4 low-latency decode megakernel for modeling_v2 for Blackwell" (#20306)
+ *   [P128]  "[None][perf] MiniMax-M3: native P128 draft KV view for the NVFP4 hybrid cache" (#19731)
+ *
+ * General rules for every entry point:
+ *   - Every array argument is caller-owned DEVICE memory, except the msa_kv_pool_t and
+ *     msa_step_t structs themselves, which live in HOST memory and are read during the
+ *     call only (the device pointers inside them are what the kernels use).
+ *   - Nothing is allocated or freed, no host synchronisation happens, no global state is
+ *     kept; calls on different streams may run concurrently if their outputs differ.
+ *   - Geometry is validated on the host before any launch. A call outside the supported
+ *     contract returns MSA_ERR_UNSUPPORTED and launches nothing; it never falls back to
+ *     another algorithm ([GB300] "The TP4 decode target": a covered shape whose
+ *     precondition is missing raises instead of falling back silently).
+ *   - Device-side metadata (page ids, positions, selections) is trusted: page ids must
+ *     be in [0, num_pages) and positions must be covered by the block table.
+ *   - All byte offsets are computed in 64 bits ([Rubin] "Disclosures and known gaps":
+ *     int32 KV offsets overflow at 1M-token contexts).
+ *   - `stream` is a hipStream_t (0 = the null stream).
+ */
+#ifndef MSA_DECODE_H_
+#define MSA_DECODE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MSA_OK = 0,
+  MSA_ERR_INVALID_ARG = -1,  /* null pointer, misaligned pointer, negative size      */
+  MSA_ERR_UNSUPPORTED = -2,  /* geometry or format outside the contract              */
+  MSA_ERR_LAUNCH = -3        /* the HIP runtime rejected a kernel launch             */
+} msa_status_t;
+
+typedef enum {
+  MSA_KV_FP8_E4M3 = 1, /* OCP E4M3FN codes, one fp32 scale per page for K and for V     */
+  MSA_KV_NVFP4 = 2     /* E2M1 codes + E4M3 scale per 16 elements + fp32 tensor scale   */
+} msa_kv_format_t;
+
+#define MSA_PAGE_SIZE 128     /* tokens per page ([P128] Description: native P128 pages) */
+#define MSA_HEAD_DIM 128
+#define MSA_INDEX_DIM 64
+#define MSA_HEADS_PER_KV 16   /* [Rubin] Description: 16 query heads per KV head          */
+#define MSA_MAX_TOPK 64
+#define MSA_MAX_BLOCKS 12288  /* blocks per sequence (1.5M tokens)                        */
+
+/*
+ * One layer's paged KV pool. A page holds 128 consecutive tokens of one sequence;
+ * inside a page the layout is head-major (HND). Token t of a page, KV head h:
+ *
+ *   NVFP4  k_codes/v_codes  u8 [num_pages][num_kv_heads][128][head_dim/2]
+ *                           byte j holds element 2j in its low nibble, 2j+1 in its high nibble
+ *          k_scales/v_scales u8 (E4M3) [num_pages][num_kv_heads][128][head_dim/16]
+ *                           scale g covers elements 16g..16g+15 of that token and head
+ *          value = E2M1(code) * E4M3(scale) * tensor_scale
+ *   FP8    k_codes/v_codes  u8 (E4M3) [num_pages][num_kv_heads][128][head_dim]
+ *          k_scales/v_scales fp32 [num_pages]  (one scale per page, all heads)
+ *          value = E4M3(code) * page_scale
+ *   index_k u8 (E4M3) [num_pages][128][index_dim], one unscaled key per token
+ *
+ * All five arrays are required and must be 16-byte aligned.
+ */
+typedef struct {
+  int32_t fmt;            /* msa_kv_format_t                                   */
+  int32_t num_pages;
+  int32_t num_kv_heads;
+  int32_t head_dim;       /* must be 128                                       */
+  int32_t page_size;      /* must be 128                                       */
+  int32_t index_dim;      /* must be 64                                        */
+  void* k_codes;
+  void* v_codes;
+  void* k_scales;
+  void* v_scales;
+  float k_tensor_scale;   /* NVFP4 only; > 0                                   */
+  float v_tensor_scale;   /* NVFP4 only; > 0                                   */
+  void* index_k;
+} msa_kv_pool_t;
+
+/*
+ * Per-step metadata (device arrays). Query rows are request-major: the rows of one
+ * request are contiguous. Row r belongs to request row_seq[r] and sits at absolute
+ * position row_pos[r]; it attends positions [0, row_pos[r]] (causal among the verify
+ * tokens of a speculative step). Its visible blocks are 0 .. row_pos[r] / 128.
+ */
+typedef struct {
+  int32_t num_seqs;
+  int32_t num_rows;
+  int32_t max_blocks_per_seq;
+  const int32_t* block_table; /* [num_seqs][max_blocks_per_seq] logical block -> page id */
+  const int32_t* row_seq;     /* [num_rows]                                              */
+  const int32_t* row_pos;     /* [num_rows]                                              */
+} msa_step_t;
+
+/*
+ * KV append ([GB300] "Step-loop runtime hooks": a hook for the KV update; [Rubin]
+ * Description: saturating FP8 casts). Token i is written to page slot[i] / 128, offset
+ * slot[i] % 128; slot[i] < 0 skips the token and writes nothing.
+ *   k_new, v_new : bf16 [n_new][num_kv_heads][head_dim]   (either may be NULL to skip)
+ *   idx_k_new    : bf16 [n_new][index_dim]                (may be NULL to skip)
+ * Encoding, all in correctly rounded fp32, rounding to nearest-even, saturating:
+ *   NVFP4 per 16 elements: amax = max|x|; sc = E4M3(amax / (6 * t)); if E4M3(sc) == 0
+ *         every code is +0, else d = E4M3(sc) * t and code_i = E2M1(x_i / d)
+ *   FP8   code = E4M3(x / page_scale[page])   (the page scale is read, never written)
+ *   index code = E4M3(x)
+ * Two tokens with the same slot in one call race. n_new may be 0.
+ */
+msa_status_t msa_kv_append(const msa_kv_pool_t* pool, int32_t n_new, const int64_t* slot,
+                           const void* k_new, const void* v_new, const void* idx_k_new,
+                           void* stream);
+
+/*
+ * Index score with block max-pool. For row r and visible token p (p <= row_pos[r]):
+ *   s_p = sum_h w[r][h] * max(0, q_idx[r][h] . E4M3(index_k[p]))
+ *   block_scores[r][b] = max over the visible tokens p of block b of s_p   (b < nb(r))
+ *   block_scores[r][b] = -inf                                   (nb(r) <= b < max_blocks)
+ * The pages name the scorer ([GB300] "The TP4 decode target": an index scorer over
+ * index-K pages) but not its formula; this is the definition the library adopts.
+ *   q_idx  : bf16 [num_rows][n_idx_heads][index_dim]
+ *   w      : fp32 [num_rows][n_idx_heads]
+ *   block_scores : fp32 [num_rows][max_blocks_per_seq] (output)
+ * n_idx_heads must be 1, 2 or 4. Accumulation is fp32 in a fixed order that does not
+ * depend on the token's position, so identical keys give bit-identical scores.
+ */
+msa_status_t msa_index_score(const msa_kv_pool_t* pool, const msa_step_t* step,
+                             int32_t n_idx_heads, const void* q_idx, const float* w,
+                             float* block_scores, void* stream);
+
+/*
+ * Top-k block selection ([Rubin] commit messages: the table is "ascending, -1-padded"
+ * with "init / local forcing"; [GB300] "The TP4 decode target", numerics: ties go to
+ * the smaller block). For row r with nb = row_pos[r] / 128 + 1 visible blocks:
+ *   nb <= k : sel[r] = 0, 1, ..., nb-1, then -1 padding (identity table, [GB300]
+ *             "Step-loop runtime hooks")
+ *   nb >  k : blocks 0..n_init-1 and nb-n_local..nb-1 are forced and count inside k;
+ *             the remaining k - |forced| slots take the best other blocks ordered by
+ *             (higher score, then smaller block index). Output ascending.
+ *   block_scores : fp32 [num_rows][max_blocks_per_seq]; only b < nb(r) is read
+ *   sel          : int32 [num_rows][k] (output, logical block ids)
+ * 1 <= k <= 64, n_init >= 0, n_local >= 0, n_init + n_local <= k,
+ * max_blocks_per_seq <= 12288. The result is deterministic for any tie width.
+ */
+msa_status_t msa_select_topk(const msa_step_t* step, const float* block_scores, int32_t k,
+                             int32_t n_init, int32_t n_local, int32_t* sel, void* stream);
+
+/*
+ * Sparse GQA flash-decode with split-KV partials ([Rubin] commit messages: one unit of
+ * work per (top-k split, KV head, query row), NVFP4 dequantised in registers). Query
+ * head h reads KV head h / 16. Split s of num_splits takes the selection entries
+ * [floor(s*k/S), floor((s+1)*k/S)); entry -1 is skipped; only tokens <= row_pos[r] are
+ * visible. With x_p = softmax_scale * (q[r][h] . K_p) * log2(e), each split writes
+ *   part_ml[r][h][s] = { m = max_p x_p, l = sum_p 2^(x_p - m) }  (m = -inf, l = 0 if empty)
+ *   part_o[r][h][s][:] = sum_p 2^(x_p - m) * V_p                   (0 if empty)
+ *   q       : bf16 [num_rows][num_q_heads][head_dim]
+ *   sel     : int32 [num_rows][k] as written by msa_select_topk
+ *   part_o  : fp32 [num_rows][num_q_heads][num_splits][head_dim]  (output)
+ *   part_ml : fp32 [num_rows][num_q_heads][num_splits][2]         (output)
+ * num_q_heads must be 16 * num_kv_heads; 1 <= num_splits <= k.
+ * Accumulation is fp32 on the matrix cores; K and V are dequantised exactly to fp16.
+ */
+msa_status_t msa_sparse_decode(const msa_kv_pool_t* pool, const msa_step_t* step,
+                               int32_t num_q_heads, const void* q, const int32_t* sel,
+                               int32_t k, float softmax_scale, int32_t num_splits,
+                               float* part_o, float* part_ml, void* stream);
+
+/*
+ * Log-sum-exp merge of split partials ([Rubin] "Items and numerics", LC_ONEDIV: the
+ * split-K merge divides once per output, in a fixed order, without atomics):
+ *   M = max_s m_s,  out = (sum_s 2^(m_s - M) O_s) / (sum_s 2^(m_s - M) l_s)
+ * summed over s = 0..num_splits-1 in order, rounded once to bf16 (nearest even).
+ * A row/head whose splits are all empty gets 0.
+ *   out : bf16 [rows][num_q_heads][head_dim] (output)
+ */
+msa_status_t msa_combine(int32_t rows, int32_t num_q_heads, int32_t head_dim,
+                         int32_t num_splits, const float* part_o, const float* part_ml,
+                         void* out, void* stream);
+
+/* Bytes of the part_o + part_ml workspace for the given geometry (part_o first, then
+ * part_ml at a 256-byte aligned offset). Returns 0 for invalid arguments. */
+size_t msa_decode_workspace_bytes(int32_t rows, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t num_splits);
+
+/* Exact bytes of each pool array for a geometry: out[0..4] = k_codes, v_codes,
+ * k_scales, v_scales, index_k. Returns MSA_ERR_UNSUPPORTED / INVALID_ARG like the
+ * entry points. */
+msa_status_t msa_pool_bytes(int32_t fmt, int32_t num_pages, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t index_dim, size_t out[5]);
+
+/* A static string naming the status. */
+const char* msa_status_string(msa_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MSA_DECODE_H_ */

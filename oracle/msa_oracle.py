@@ -236,22 +236,21 @@ def kv_append(pool: dict, slot: np.ndarray, k_new=None, v_new=None, idx_new=None
     Any of the three may be None to skip that part.
     """
     slot = np.asarray(slot, dtype=np.int64)
-    for i, s in enumerate(slot):
-        if s < 0:
+    keep = np.nonzero(slot >= 0)[0]
+    page, off = slot[keep] // PAGE, slot[keep] % PAGE
+    if idx_new is not None:
+        pool["index_k"][page, off] = e4m3_encode(bf16_bits_to_f64(np.asarray(idx_new)[keep]))
+    for kv, src in (("k", k_new), ("v", v_new)):
+        if src is None:
             continue
-        page, off = divmod(int(s), PAGE)
-        if idx_new is not None:
-            pool["index_k"][page, off] = e4m3_encode(bf16_bits_to_f64(idx_new[i]))
-        for kv, src in (("k", k_new), ("v", v_new)):
-            if src is None:
-                continue
-            x = bf16_bits_to_f64(src[i])                      # [Hkv][D]
-            if pool["fmt"] == FMT_NVFP4:
-                codes, sc = nvfp4_encode(x, pool[kv + "_tensor_scale"])
-                pool[kv + "_codes"][page, :, off] = pack_nibbles(codes)
-                pool[kv + "_scales"][page, :, off] = sc
-            else:
-                pool[kv + "_codes"][page, :, off] = fp8_kv_encode(x, pool[kv + "_scales"][page])
+        x = bf16_bits_to_f64(np.asarray(src)[keep])          # [n][Hkv][D]
+        if pool["fmt"] == FMT_NVFP4:
+            codes, sc = nvfp4_encode(x, pool[kv + "_tensor_scale"])
+            pool[kv + "_codes"][page, :, off] = pack_nibbles(codes)
+            pool[kv + "_scales"][page, :, off] = sc
+        else:
+            s = pool[kv + "_scales"][page].astype(np.float64)[:, None, None]
+            pool[kv + "_codes"][page, :, off] = e4m3_encode(f32(x / f32(s)))
 
 
 def dequant_page(pool: dict, page: int, head: int, kv: str) -> np.ndarray:

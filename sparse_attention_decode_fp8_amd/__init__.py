@@ -1,0 +1,11 @@
+"""libmsadecode: block-sparse FP8/NVFP4 attention decode for AMD MI355X (gfx950).
+
+The decode path lives in hand-written HIP kernels behind the C ABI declared in
+include/msa_decode.h; this package is the ctypes binding (marshalling only) plus
+the in-tree build script. Importing it loads the HIP library and fails loudly if
+it has not been built.
+"""
+from ._lib import (FMT_FP8, FMT_NVFP4, KVPool, MsaError, Step, msa_combine,  # noqa: F401
+                   msa_decode_workspace_bytes, msa_index_score, msa_kv_append, msa_select_topk,
+                   msa_sparse_decode)
+from .pipeline import DecodeBuffers, run_step  # noqa: F401

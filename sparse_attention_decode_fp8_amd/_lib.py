@@ -1,0 +1,197 @@
+"""ctypes binding of libmsadecode (argument marshalling only).
+
+Every function has the name of the C entry point it calls and takes torch tensors
+that already live on the GPU; it passes their device pointers and the current HIP
+stream to the library and raises MsaError on a non-OK status. No computation of
+the decode path happens in Python, and there is no fallback: if the HIP library is
+not built, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmsadecode.so")
+
+FMT_FP8 = 1
+FMT_NVFP4 = 2
+PAGE = 128
+HEAD_DIM = 128
+INDEX_DIM = 64
+
+MSA_OK = 0
+
+
+class MsaError(RuntimeError):
+    pass
+
+
+class MsaKvPool(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("index_dim", ctypes.c_int32),
+                ("k_codes", ctypes.c_void_p), ("v_codes", ctypes.c_void_p),
+                ("k_scales", ctypes.c_void_p), ("v_scales", ctypes.c_void_p),
+                ("k_tensor_scale", ctypes.c_float), ("v_tensor_scale", ctypes.c_float),
+                ("index_k", ctypes.c_void_p)]
+
+
+class MsaStep(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("num_rows", ctypes.c_int32),
+                ("max_blocks_per_seq", ctypes.c_int32), ("block_table", ctypes.c_void_p),
+                ("row_seq", ctypes.c_void_p), ("row_pos", ctypes.c_void_p)]
+
+
+EXPORTS = ["msa_kv_append", "msa_index_score", "msa_select_topk", "msa_sparse_decode",
+           "msa_combine", "msa_decode_workspace_bytes", "msa_pool_bytes", "msa_status_string"]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m sparse_attention_decode_fp8_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, F32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    sig = {
+        "msa_kv_append": (I32, [P, I32, P, P, P, P, P]),
+        "msa_index_score": (I32, [P, P, I32, P, P, P, P]),
+        "msa_select_topk": (I32, [P, P, I32, I32, I32, P, P]),
+        "msa_sparse_decode": (I32, [P, P, I32, P, P, I32, F32, I32, P, P, P]),
+        "msa_combine": (I32, [I32, I32, I32, I32, P, P, P, P]),
+        "msa_decode_workspace_bytes": (SZ, [I32, I32, I32, I32]),
+        "msa_pool_bytes": (I32, [I32, I32, I32, I32, I32, ctypes.POINTER(SZ)]),
+        "msa_status_string": (ctypes.c_char_p, [I32]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype, f.argtypes = res, args
+    return lib
+
+
+LIB = _load()
+
+
+def _check(status: int, what: str):
+    if status != MSA_OK:
+        raise MsaError(f"{what}: {LIB.msa_status_string(status).decode()}")
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ptr(t, dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise MsaError(f"{name} must be a CUDA (HIP) tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise MsaError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise MsaError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+class KVPool:
+    """One layer's paged pool on the GPU (layout documented in include/msa_decode.h)."""
+
+    def __init__(self, fmt, num_pages, num_kv_heads, device="cuda", k_tensor_scale=1.0,
+                 v_tensor_scale=1.0, k_page_scale=None, v_page_scale=None):
+        sizes = (ctypes.c_size_t * 5)()
+        _check(LIB.msa_pool_bytes(fmt, num_pages, num_kv_heads, HEAD_DIM, INDEX_DIM, sizes),
+               "msa_pool_bytes")
+        self.fmt, self.num_pages, self.num_kv_heads = fmt, num_pages, num_kv_heads
+        self.k_tensor_scale, self.v_tensor_scale = float(k_tensor_scale), float(v_tensor_scale)
+        z = lambda n: torch.zeros(n, dtype=torch.uint8, device=device)   # pools start zeroed
+        self.k_codes, self.v_codes = z(sizes[0]), z(sizes[1])
+        self.index_k = z(sizes[4])
+        if fmt == FMT_FP8:
+            mk = lambda s: (torch.ones(num_pages, dtype=torch.float32) if s is None
+                            else torch.as_tensor(s, dtype=torch.float32)).to(device)
+            self.k_scales, self.v_scales = mk(k_page_scale), mk(v_page_scale)
+        else:
+            self.k_scales, self.v_scales = z(sizes[2]), z(sizes[3])
+
+    def arrays(self):
+        return {"k_codes": self.k_codes, "v_codes": self.v_codes, "k_scales": self.k_scales,
+                "v_scales": self.v_scales, "index_k": self.index_k}
+
+    def cstruct(self) -> MsaKvPool:
+        return MsaKvPool(self.fmt, self.num_pages, self.num_kv_heads, HEAD_DIM, PAGE, INDEX_DIM,
+                         self.k_codes.data_ptr(), self.v_codes.data_ptr(), self.k_scales.data_ptr(),
+                         self.v_scales.data_ptr(), self.k_tensor_scale, self.v_tensor_scale,
+                         self.index_k.data_ptr())
+
+    def clone(self) -> "KVPool":
+        c = object.__new__(KVPool)
+        c.__dict__.update(self.__dict__)
+        for k, v in self.arrays().items():
+            setattr(c, k, v.clone())
+        return c
+
+
+class Step:
+    """Per-step metadata on the GPU: block table, row -> request, row -> position."""
+
+    def __init__(self, block_table, row_seq, row_pos, device="cuda"):
+        bt = torch.as_tensor(block_table, dtype=torch.int32).to(device).contiguous()
+        self.block_table = bt
+        self.row_seq = torch.as_tensor(row_seq, dtype=torch.int32).to(device).contiguous()
+        self.row_pos = torch.as_tensor(row_pos, dtype=torch.int32).to(device).contiguous()
+        self.num_seqs, self.max_blocks = bt.shape
+        self.num_rows = self.row_pos.numel()
+
+    def cstruct(self) -> MsaStep:
+        return MsaStep(self.num_seqs, self.num_rows, self.max_blocks, self.block_table.data_ptr(),
+                       self.row_seq.data_ptr(), self.row_pos.data_ptr())
+
+
+def msa_kv_append(pool: KVPool, slot, k_new=None, v_new=None, idx_k_new=None, stream=None):
+    n = slot.numel()
+    ps = pool.cstruct()
+    _check(LIB.msa_kv_append(ctypes.byref(ps), n, _ptr(slot, torch.int64, "slot"),
+                             _ptr(k_new, torch.bfloat16, "k_new"), _ptr(v_new, torch.bfloat16, "v_new"),
+                             _ptr(idx_k_new, torch.bfloat16, "idx_k_new"), _stream(stream)),
+           "msa_kv_append")
+
+
+def msa_index_score(pool: KVPool, step: Step, q_idx, w, block_scores, stream=None):
+    ps, ss = pool.cstruct(), step.cstruct()
+    _check(LIB.msa_index_score(ctypes.byref(ps), ctypes.byref(ss), q_idx.shape[1],
+                               _ptr(q_idx, torch.bfloat16, "q_idx"), _ptr(w, torch.float32, "w"),
+                               _ptr(block_scores, torch.float32, "block_scores"), _stream(stream)),
+           "msa_index_score")
+
+
+def msa_select_topk(step: Step, block_scores, k, n_init, n_local, sel, stream=None):
+    ss = step.cstruct()
+    _check(LIB.msa_select_topk(ctypes.byref(ss), _ptr(block_scores, torch.float32, "block_scores"),
+                               k, n_init, n_local, _ptr(sel, torch.int32, "sel"), _stream(stream)),
+           "msa_select_topk")
+
+
+def msa_sparse_decode(pool: KVPool, step: Step, q, sel, k, softmax_scale, num_splits, part_o,
+                      part_ml, stream=None):
+    ps, ss = pool.cstruct(), step.cstruct()
+    _check(LIB.msa_sparse_decode(ctypes.byref(ps), ctypes.byref(ss), q.shape[1],
+                                 _ptr(q, torch.bfloat16, "q"), _ptr(sel, torch.int32, "sel"), k,
+                                 float(softmax_scale), num_splits,
+                                 _ptr(part_o, torch.float32, "part_o"),
+                                 _ptr(part_ml, torch.float32, "part_ml"), _stream(stream)),
+           "msa_sparse_decode")
+
+
+def msa_combine(rows, num_q_heads, head_dim, num_splits, part_o, part_ml, out, stream=None):
+    _check(LIB.msa_combine(rows, num_q_heads, head_dim, num_splits,
+                           _ptr(part_o, torch.float32, "part_o"), _ptr(part_ml, torch.float32, "part_ml"),
+                           _ptr(out, torch.bfloat16, "out"), _stream(stream)),
+           "msa_combine")
+
+
+def msa_decode_workspace_bytes(rows, num_q_heads, head_dim, num_splits) -> int:
+    return int(LIB.msa_decode_workspace_bytes(rows, num_q_heads, head_dim, num_splits))

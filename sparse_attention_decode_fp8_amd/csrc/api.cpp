@@ -1,0 +1,42 @@
+// Host-only entry points of libmsadecode: sizes and status strings.
+#include <stddef.h>
+#include <stdint.h>
+
+#include "msa_decode.h"
+
+extern "C" size_t msa_decode_workspace_bytes(int32_t rows, int32_t num_q_heads, int32_t head_dim,
+                                             int32_t num_splits) {
+  if (rows < 0 || num_q_heads <= 0 || head_dim <= 0 || num_splits <= 0) return 0;
+  const size_t n = static_cast<size_t>(rows) * num_q_heads * num_splits;
+  size_t o = n * head_dim * sizeof(float);
+  o = (o + 255) / 256 * 256;
+  return o + n * 2 * sizeof(float);
+}
+
+extern "C" msa_status_t msa_pool_bytes(int32_t fmt, int32_t num_pages, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t index_dim, size_t out[5]) {
+  if (out == nullptr || num_pages <= 0 || num_kv_heads <= 0) return MSA_ERR_INVALID_ARG;
+  if (head_dim != MSA_HEAD_DIM || index_dim != MSA_INDEX_DIM) return MSA_ERR_UNSUPPORTED;
+  const size_t tok = static_cast<size_t>(num_pages) * num_kv_heads * MSA_PAGE_SIZE;
+  if (fmt == MSA_KV_NVFP4) {
+    out[0] = out[1] = tok * (head_dim / 2);
+    out[2] = out[3] = tok * (head_dim / 16);
+  } else if (fmt == MSA_KV_FP8_E4M3) {
+    out[0] = out[1] = tok * head_dim;
+    out[2] = out[3] = static_cast<size_t>(num_pages) * sizeof(float);
+  } else {
+    return MSA_ERR_UNSUPPORTED;
+  }
+  out[4] = static_cast<size_t>(num_pages) * MSA_PAGE_SIZE * index_dim;
+  return MSA_OK;
+}
+
+extern "C" const char* msa_status_string(msa_status_t status) {
+  switch (status) {
+    case MSA_OK: return "MSA_OK";
+    case MSA_ERR_INVALID_ARG: return "MSA_ERR_INVALID_ARG: null, misaligned or negative argument";
+    case MSA_ERR_UNSUPPORTED: return "MSA_ERR_UNSUPPORTED: geometry or format outside the contract";
+    case MSA_ERR_LAUNCH: return "MSA_ERR_LAUNCH: kernel launch failed";
+  }
+  return "MSA_ERR_UNKNOWN";
+}

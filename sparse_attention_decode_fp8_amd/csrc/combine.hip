@@ -1,0 +1,63 @@
+// msa_combine: fixed-order log-sum-exp merge of split-KV partials into bf16 outputs.
+//
+// [Rubin] "Items and numerics", LC_ONEDIV: the long-context sparse-decode split-K merge
+// divides once per output, in a fixed order, with no atomics. Each thread owns four
+// consecutive output dims of one (row, head); the splits are summed in ascending
+// order and each output is one division, rounded once to bf16 (nearest even).
+#include "msa_device.h"
+#include "msa_host.h"
+
+namespace msa {
+namespace {
+
+__global__ void __launch_bounds__(256)
+combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
+               uint16_t* __restrict__ out, int64_t row_heads, int num_splits) {
+  constexpr int kQuads = kHeadDim / 4;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= row_heads * kQuads) return;
+  const int64_t rh = idx / kQuads;
+  const int d4 = static_cast<int>(idx % kQuads);
+  const float* ml = part_ml + rh * num_splits * 2;
+  float M = -INFINITY;
+  for (int s = 0; s < num_splits; ++s) M = fmaxf(M, ml[2 * s]);
+  float4_t num = {0.0f, 0.0f, 0.0f, 0.0f};
+  float den = 0.0f;
+  if (M != -INFINITY) {
+    const float* po = part_o + rh * num_splits * kHeadDim + 4 * d4;
+    for (int s = 0; s < num_splits; ++s) {
+      const float m = ml[2 * s];
+      if (m == -INFINITY) continue;
+      const float wgt = exp2f(m - M);
+      den += wgt * ml[2 * s + 1];
+      num += wgt * *reinterpret_cast<const float4_t*>(po + static_cast<int64_t>(s) * kHeadDim);
+    }
+  }
+  uint16_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = den > 0.0f ? f32_to_bf16_rne(num[i] / den) : 0;
+  *reinterpret_cast<uint2*>(out + rh * kHeadDim + 4 * d4) =
+      make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16));
+}
+
+}  // namespace
+}  // namespace msa
+
+extern "C" msa_status_t msa_combine(int32_t rows, int32_t num_q_heads, int32_t head_dim,
+                                    int32_t num_splits, const float* part_o, const float* part_ml,
+                                    void* out, void* stream) {
+  using namespace msa;
+  if (rows < 0 || num_q_heads <= 0 || num_splits <= 0) return MSA_ERR_INVALID_ARG;
+  if (head_dim != MSA_HEAD_DIM || num_splits > MSA_MAX_TOPK) return MSA_ERR_UNSUPPORTED;
+  if (rows == 0) return MSA_OK;
+  if (part_o == nullptr || part_ml == nullptr || out == nullptr) return MSA_ERR_INVALID_ARG;
+  if (!aligned16(part_o) || (reinterpret_cast<uintptr_t>(out) & 7u) ||
+      (reinterpret_cast<uintptr_t>(part_ml) & 7u))
+    return MSA_ERR_INVALID_ARG;
+  const int64_t rh = static_cast<int64_t>(rows) * num_q_heads;
+  const int64_t threads = rh * (MSA_HEAD_DIM / 4);
+  combine_kernel<<<dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0,
+                   static_cast<hipStream_t>(stream)>>>(part_o, part_ml, static_cast<uint16_t*>(out),
+                                                        rh, num_splits);
+  return launch_status();
+}

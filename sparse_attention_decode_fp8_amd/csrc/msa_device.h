@@ -1,0 +1,137 @@
+// Device helpers shared by the libmsadecode kernels (gfx950 / CDNA4, wave64).
+//
+// Lane layouts used throughout (v_mfma_f32_16x16x32_f16, measured on gfx950):
+//   A operand: lane l holds A[l % 16][8 * (l / 16) + i], i = 0..7
+//   B operand: lane l holds B[8 * (l / 16) + i][l % 16], i = 0..7
+//   C/D:       lane l holds C[4 * (l / 16) + j][l % 16], j = 0..3
+// ds_read_b64_tr_b16: within each 16-lane group, lanes 4j..4j+3 each point at 4
+// consecutive 16-bit elements that together form row j (16 elements); lane i then
+// receives element i of rows j = 0..3.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "msa_decode.h"
+
+namespace msa {
+
+typedef _Float16 half_t;
+typedef half_t half2_t __attribute__((ext_vector_type(2)));
+typedef half_t half4_t __attribute__((ext_vector_type(4)));
+typedef half_t half8_t __attribute__((ext_vector_type(8)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kPage = MSA_PAGE_SIZE;
+constexpr int kHeadDim = MSA_HEAD_DIM;
+constexpr int kIndexDim = MSA_INDEX_DIM;
+constexpr int kHeadsPerKv = MSA_HEADS_PER_KV;
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bits (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Two OCP E4M3FN codes (bytes 0 and 1 of `v`) -> two exact fp16 values.
+__device__ __forceinline__ half2_t e4m3x2_to_f16(uint32_t v) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<short>(v & 0xffffu), 1.0f, false);
+}
+
+// Two E2M1 codes (byte `sel` of `v`: low nibble first) -> two exact fp16 values.
+template <int kSel>
+__device__ __forceinline__ half2_t e2m1x2_to_f16(uint32_t v) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, kSel);
+}
+
+// One E4M3 code (byte 0 of v) -> exact fp32.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t v) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(v & 0xffu), false)[0];
+}
+
+__device__ __forceinline__ float4_t mfma16x16x32(half8_t a, half8_t b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// 8 E4M3 codes (two dwords) -> 8 fp16 values in one MFMA operand.
+__device__ __forceinline__ half8_t e4m3x8_to_f16(uint32_t lo, uint32_t hi) {
+  half2_t a = e4m3x2_to_f16(lo), b = e4m3x2_to_f16(lo >> 16);
+  half2_t c = e4m3x2_to_f16(hi), d = e4m3x2_to_f16(hi >> 16);
+  return half8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// 8 E2M1 codes (one dword, element 0 in the low nibble) times an fp16 scale.
+__device__ __forceinline__ half8_t e2m1x8_to_f16(uint32_t v, half2_t scale2) {
+  half2_t a = e2m1x2_to_f16<0>(v) * scale2;
+  half2_t b = e2m1x2_to_f16<1>(v) * scale2;
+  half2_t c = e2m1x2_to_f16<2>(v) * scale2;
+  half2_t d = e2m1x2_to_f16<3>(v) * scale2;
+  return half8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Power-of-two exponent e such that amax * 2^e lies in [2^14, 2^15): converting
+// bf16 values times 2^e to fp16 is then exact down to amax * 2^-28.
+__device__ __forceinline__ int f16_prescale_exp(float amax) {
+  if (!(amax > 0.0f) || !(amax < 3.0e38f)) return 0;
+  int ex;
+  frexpf(amax, &ex);           // amax = m * 2^ex, m in [0.5, 1)
+  return 15 - ex;
+}
+
+__device__ __forceinline__ float xor_max(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask, 64));
+}
+__device__ __forceinline__ float xor_add(float v, int mask) {
+  return v + __shfl_xor(v, mask, 64);
+}
+
+// Order-preserving map of fp32 onto uint32 (larger float -> larger key).
+__device__ __forceinline__ uint32_t float_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---------------------------------------------------------------- encoders
+// Saturating round-to-nearest-even fp32 -> OCP E4M3FN. Magnitudes >= 448 give 448;
+// the sign bit follows the input's sign bit.
+__device__ __forceinline__ uint32_t f32_to_e4m3_sat(float x) {
+  uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  float a = fabsf(x);
+  uint32_t mag;
+  if (!(a < 448.0f)) {
+    mag = 0x7eu;
+  } else if (a < 0.015625f) {               // below 2^-6: grid of m * 2^-9, m = 0..8
+    mag = static_cast<uint32_t>(rintf(a * 512.0f));
+  } else {
+    uint32_t u = __float_as_uint(a);
+    uint32_t e = (u >> 23) - 120u;           // biased E4M3 exponent 1..15
+    uint32_t man = u & 0x7fffffu;
+    uint32_t r = man >> 20, rem = man & 0xfffffu;
+    if (rem > 0x80000u || (rem == 0x80000u && (r & 1u))) ++r;
+    mag = (e << 3) + r;                      // r == 8 carries into the exponent
+    if (mag > 0x7eu) mag = 0x7eu;
+  }
+  return sign | mag;
+}
+
+// Saturating round-to-nearest-even fp32 -> E2M1 (sign bit 3). Grid
+// {0, .5, 1, 1.5, 2, 3, 4, 6}; each comparison is one decision boundary, with the
+// tie at the boundary going to the even code.
+__device__ __forceinline__ uint32_t f32_to_e2m1_sat(float x) {
+  uint32_t sign = (__float_as_uint(x) >> 28) & 0x8u;
+  float a = fabsf(x);
+  uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
+               (a >= 3.5f) + (a > 5.0f);
+  return sign | c;
+}
+
+}  // namespace msa

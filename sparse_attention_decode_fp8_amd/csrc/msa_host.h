@@ -1,0 +1,45 @@
+// Host-side argument validation shared by the libmsadecode entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "msa_decode.h"
+
+namespace msa {
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline msa_status_t check_pool(const msa_kv_pool_t* pool) {
+  if (pool == nullptr) return MSA_ERR_INVALID_ARG;
+  if (pool->fmt != MSA_KV_FP8_E4M3 && pool->fmt != MSA_KV_NVFP4) return MSA_ERR_UNSUPPORTED;
+  if (pool->head_dim != MSA_HEAD_DIM || pool->page_size != MSA_PAGE_SIZE ||
+      pool->index_dim != MSA_INDEX_DIM)
+    return MSA_ERR_UNSUPPORTED;
+  if (pool->num_pages <= 0 || pool->num_kv_heads <= 0) return MSA_ERR_INVALID_ARG;
+  if (pool->num_kv_heads > 64) return MSA_ERR_UNSUPPORTED;
+  const void* arr[5] = {pool->k_codes, pool->v_codes, pool->k_scales, pool->v_scales,
+                        pool->index_k};
+  for (const void* p : arr)
+    if (p == nullptr || !aligned16(p)) return MSA_ERR_INVALID_ARG;
+  if (pool->fmt == MSA_KV_NVFP4 && !(pool->k_tensor_scale > 0.0f && pool->v_tensor_scale > 0.0f))
+    return MSA_ERR_INVALID_ARG;
+  return MSA_OK;
+}
+
+inline msa_status_t check_step(const msa_step_t* step) {
+  if (step == nullptr) return MSA_ERR_INVALID_ARG;
+  if (step->num_seqs < 0 || step->num_rows < 0 || step->max_blocks_per_seq <= 0)
+    return MSA_ERR_INVALID_ARG;
+  if (step->max_blocks_per_seq > MSA_MAX_BLOCKS) return MSA_ERR_UNSUPPORTED;
+  if (step->num_rows > 0 &&
+      (step->block_table == nullptr || step->row_seq == nullptr || step->row_pos == nullptr))
+    return MSA_ERR_INVALID_ARG;
+  return MSA_OK;
+}
+
+inline msa_status_t launch_status() {
+  return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_LAUNCH;
+}
+
+}  // namespace msa

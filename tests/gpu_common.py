@@ -1,0 +1,129 @@
+"""Helpers shared by the GPU parity tests: move seeded workloads to the GPU, run the
+HIP path through the C ABI, build the oracle's side independently on the CPU, and
+compare to the stated bars."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import msa_oracle as O
+from synth import workloads as W
+
+SCORE_RTOL = 1e-5      # |S_gpu - S_ref| <= 1e-5 * max(|S_ref|, 1)
+OUT_ATOL = 1e-2        # bf16 outputs vs float64 attention
+GAP_RTOL = 1e-4        # rows whose k-th / (k+1)-th score gap exceeds this must match bit for bit
+
+
+def dev_bf16(bits) -> torch.Tensor:
+    a = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16)).view(np.int16)
+    return torch.from_numpy(a).cuda().view(torch.bfloat16)
+
+
+def bf16_to_np(t: torch.Tensor) -> np.ndarray:
+    return W.bf16_bits_to_f32(t.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+
+
+def gpu_pool(M, wl: W.Workload):
+    """A device pool holding every cached token, written by msa_kv_append."""
+    pool = M.KVPool(wl.fmt, wl.num_pages, wl.num_kv_heads, k_tensor_scale=wl.k_tensor_scale,
+                    v_tensor_scale=wl.v_tensor_scale, k_page_scale=wl.k_page_scale,
+                    v_page_scale=wl.v_page_scale)
+    for s in range(len(wl.ctx_lens)):
+        L = int(wl.ctx_lens[s])
+        if L == 0:
+            continue
+        slot = torch.from_numpy(wl.slots(s, np.arange(L))).cuda()
+        M.msa_kv_append(pool, slot, dev_bf16(wl.k_src[s][:L]), dev_bf16(wl.v_src[s][:L]),
+                        dev_bf16(wl.idx_src[s][:L]))
+    return pool
+
+
+def gpu_step_inputs(M, wl: W.Workload):
+    step = M.Step(wl.block_table, wl.row_seq, wl.row_pos)
+    q = dev_bf16(wl.q)
+    q_idx = dev_bf16(wl.q_idx)
+    w = torch.from_numpy(wl.w).cuda()
+    sl, kb, vb, ib = wl.step_tokens()
+    app = None
+    if len(sl):
+        app = (torch.from_numpy(sl).cuda(), dev_bf16(kb), dev_bf16(vb), dev_bf16(ib))
+    return step, q, q_idx, w, app
+
+
+def run_gpu_step(M, wl, pool, num_splits):
+    step, q, q_idx, w, app = gpu_step_inputs(M, wl)
+    bufs = M.DecodeBuffers(wl.num_rows, wl.num_heads, wl.max_blocks, wl.k, num_splits)
+    kw = {}
+    if app is not None:
+        kw = dict(slot=app[0], k_new=app[1], v_new=app[2], idx_k_new=app[3])
+    M.run_step(pool, step, bufs, q, q_idx, w, wl.softmax_scale, n_init=wl.n_init,
+               n_local=wl.n_local, **kw)
+    torch.cuda.synchronize()
+    return bufs
+
+
+def oracle_pool(wl: W.Workload, seqs=None, kv_blocks=None):
+    """The oracle's own pool: index keys of every token of `seqs` (all requests if
+    None) and K/V of every token, or only of the (seq -> blocks) given in kv_blocks."""
+    pool = O.new_pool(wl.fmt, wl.num_pages, wl.num_kv_heads, k_tensor_scale=wl.k_tensor_scale,
+                      v_tensor_scale=wl.v_tensor_scale, k_page_scale=wl.k_page_scale,
+                      v_page_scale=wl.v_page_scale)
+    seqs = range(len(wl.ctx_lens)) if seqs is None else seqs
+    for s in seqs:
+        T = wl.total_len(s)
+        pos = np.arange(T)
+        O.kv_append(pool, wl.slots(s, pos), None, None, wl.idx_src[s])
+        if kv_blocks is None:
+            kv_pos = pos
+        else:
+            bl = sorted(set(int(b) for b in kv_blocks.get(s, []) if b >= 0))
+            kv_pos = np.concatenate([np.arange(b * 128, min((b + 1) * 128, T)) for b in bl]) if bl else \
+                np.zeros(0, np.int64)
+        if len(kv_pos):
+            O.kv_append(pool, wl.slots(s, kv_pos), wl.k_src[s][kv_pos], wl.v_src[s][kv_pos], None)
+    return pool
+
+
+def assert_scores_close(S_gpu, S_ref, rows=None):
+    rows = range(S_ref.shape[0]) if rows is None else rows
+    for r in rows:
+        g, e = S_gpu[r].astype(np.float64), S_ref[r]
+        ninf = np.isneginf(e)
+        assert np.array_equal(np.isneginf(g), ninf), f"row {r}: -inf pattern differs"
+        err = np.abs(g[~ninf] - e[~ninf]) / np.maximum(np.abs(e[~ninf]), 1.0)
+        assert err.size == 0 or err.max() <= SCORE_RTOL, f"row {r}: score rel err {err.max():.3g}"
+
+
+def gap_qualified(S_row, nb, k, n_init=0, n_local=1) -> bool:
+    if nb <= k:
+        return True
+    free = np.asarray([S_row[b] for b in range(n_init, nb - n_local)])
+    kk = k - n_init - n_local
+    if kk <= 0 or kk >= len(free):
+        return True
+    srt = np.sort(free)[::-1]
+    a, b = srt[kk - 1], srt[kk]
+    return (a - b) > GAP_RTOL * abs(a)
+
+
+def check_selection_valid(sel_row, S_ref_row, nb, k, n_init=0, n_local=1):
+    """Where the boundary is too close to call, the GPU's choice must still be a valid
+    top-k: forced blocks present, ascending, and every chosen free block's reference
+    score within tolerance of the boundary."""
+    chosen = [int(b) for b in sel_row if b >= 0]
+    assert chosen == sorted(chosen) and len(chosen) == min(nb, k)
+    forced = set(range(min(n_init, nb))) | set(range(nb - n_local, nb))
+    assert forced <= set(chosen)
+    free = [b for b in range(n_init, nb - n_local)]
+    kk = k - len(forced)
+    thr = np.sort([S_ref_row[b] for b in free])[::-1][kk - 1]
+    tol = 2 * SCORE_RTOL * max(abs(thr), 1.0)
+    for b in chosen:
+        if b not in forced:
+            assert S_ref_row[b] >= thr - tol
+
+
+def assert_out_close(out_gpu, out_ref, what=""):
+    err = np.abs(out_gpu - out_ref).max()
+    assert err <= OUT_ATOL, f"{what} max abs err {err:.4g}"
+    return err

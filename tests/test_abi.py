@@ -1,0 +1,117 @@
+"""The C-ABI library loads and exports every declared symbol; host-side validation
+rejects out-of-contract calls before any launch (no GPU work happens here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from sparse_attention_decode_fp8_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for f in os.listdir(inc):
+        if f.endswith(".h"):
+            src = open(os.path.join(inc, f)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(msa_[a-z_0-9]+)\s*\(", src))
+    return sorted(names)
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_symbols()
+    assert {"msa_kv_append", "msa_index_score", "msa_select_topk", "msa_sparse_decode",
+            "msa_combine"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (msa_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert getattr(L.LIB, n) is not None
+
+
+def test_binding_names_match_c_entry_points():
+    import sparse_attention_decode_fp8_amd as M
+    for n in ("msa_kv_append", "msa_index_score", "msa_select_topk", "msa_sparse_decode",
+              "msa_combine", "msa_decode_workspace_bytes"):
+        assert callable(getattr(M, n))
+
+
+def test_status_strings():
+    for st, tag in ((0, "MSA_OK"), (-1, "INVALID_ARG"), (-2, "UNSUPPORTED"), (-3, "LAUNCH")):
+        assert tag in L.LIB.msa_status_string(st).decode()
+
+
+def test_pool_bytes_and_workspace():
+    sz = (ctypes.c_size_t * 5)()
+    assert L.LIB.msa_pool_bytes(2, 10, 4, 128, 64, sz) == 0
+    assert list(sz) == [10 * 4 * 128 * 64] * 2 + [10 * 4 * 128 * 8] * 2 + [10 * 128 * 64]
+    assert L.LIB.msa_pool_bytes(1, 10, 4, 128, 64, sz) == 0
+    assert list(sz) == [10 * 4 * 128 * 128] * 2 + [40, 40, 10 * 128 * 64]
+    assert L.LIB.msa_pool_bytes(3, 10, 4, 128, 64, sz) == -2
+    assert L.LIB.msa_pool_bytes(2, 10, 4, 64, 64, sz) == -2
+    ws = L.LIB.msa_decode_workspace_bytes(8, 64, 128, 4)
+    assert ws == 8 * 64 * 4 * 128 * 4 + 8 * 64 * 4 * 2 * 4
+    assert L.LIB.msa_decode_workspace_bytes(-1, 64, 128, 4) == 0
+
+
+def _fake_pool(fmt=2, head_dim=128, k_t=1.0):
+    # 16-byte aligned non-null host addresses: validation only, never dereferenced
+    a = 1 << 20
+    return L.MsaKvPool(fmt, 4, 2, head_dim, 128, 64, a, a, a, a, k_t, 1.0, a)
+
+
+def _fake_step(rows=0, max_blocks=8):
+    a = 1 << 20
+    return L.MsaStep(1, rows, max_blocks, a, a, a)
+
+
+def test_validation_rejects_before_launch():
+    B = ctypes.byref
+    P = ctypes.c_void_p
+    pool, step = _fake_pool(), _fake_step()
+    # empty work is OK and launches nothing
+    assert L.LIB.msa_kv_append(B(pool), 0, None, None, None, None, None) == 0
+    assert L.LIB.msa_index_score(B(pool), B(step), 4, P(16), P(16), P(16), None) == 0
+    assert L.LIB.msa_select_topk(B(step), P(16), 8, 0, 1, P(16), None) == 0
+    assert L.LIB.msa_sparse_decode(B(pool), B(step), 32, P(16), P(16), 8, 0.1, 2, P(16), P(16), None) == 0
+    assert L.LIB.msa_combine(0, 32, 128, 2, P(16), P(16), P(16), None) == 0
+    # unsupported geometry
+    assert L.LIB.msa_kv_append(B(_fake_pool(head_dim=64)), 1, P(16), None, None, None, None) == -2
+    assert L.LIB.msa_kv_append(B(_fake_pool(fmt=7)), 1, P(16), None, None, None, None) == -2
+    assert L.LIB.msa_index_score(B(pool), B(step), 3, P(16), P(16), P(16), None) == -2
+    assert L.LIB.msa_select_topk(B(step), P(16), 0, 0, 1, P(16), None) == -2
+    assert L.LIB.msa_select_topk(B(step), P(16), 65, 0, 1, P(16), None) == -2
+    assert L.LIB.msa_select_topk(B(step), P(16), 4, 3, 2, P(16), None) == -2
+    assert L.LIB.msa_select_topk(B(_fake_step(max_blocks=12289)), P(16), 4, 0, 1, P(16), None) == -2
+    assert L.LIB.msa_sparse_decode(B(pool), B(step), 48, P(16), P(16), 8, 0.1, 2, P(16), P(16), None) == -2
+    assert L.LIB.msa_sparse_decode(B(pool), B(step), 32, P(16), P(16), 8, 0.1, 9, P(16), P(16), None) == -2
+    assert L.LIB.msa_combine(1, 32, 64, 2, P(16), P(16), P(16), None) == -2
+    # invalid arguments
+    assert L.LIB.msa_kv_append(None, 1, P(16), None, None, None, None) == -1
+    assert L.LIB.msa_kv_append(B(pool), -1, P(16), None, None, None, None) == -1
+    assert L.LIB.msa_kv_append(B(pool), 1, None, None, None, None, None) == -1
+    assert L.LIB.msa_kv_append(B(pool), 1, P(16), P(18), None, None, None) == -1   # misaligned
+    assert L.LIB.msa_kv_append(B(_fake_pool(k_t=0.0)), 1, P(16), None, None, None, None) == -1
+    bad = _fake_pool()
+    bad.k_codes = None
+    assert L.LIB.msa_kv_append(B(bad), 1, P(16), None, None, None, None) == -1
+    s1 = _fake_step(rows=1)
+    assert L.LIB.msa_index_score(B(pool), B(s1), 4, None, P(16), P(16), None) == -1
+    assert L.LIB.msa_select_topk(B(s1), None, 4, 0, 1, P(16), None) == -1
+    assert L.LIB.msa_sparse_decode(B(pool), B(s1), 32, P(16), P(16), 8, 0.0, 2, P(16), P(16), None) == -1
+    assert L.LIB.msa_sparse_decode(B(pool), B(s1), 32, P(24), P(16), 8, 0.1, 2, P(16), P(16), None) == -1
+    assert L.LIB.msa_combine(1, 32, 128, 2, None, P(16), P(16), None) == -1
+    nullstep = L.MsaStep(1, 1, 8, None, None, None)
+    assert L.LIB.msa_index_score(B(pool), B(nullstep), 4, P(16), P(16), P(16), None) == -1
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    with pytest.raises(L.MsaError):
+        L._ptr(torch.zeros(4), torch.float32, "x")

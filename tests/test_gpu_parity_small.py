@@ -1,0 +1,189 @@
+"""Element-by-element parity of the HIP path with the oracle at small sizes that
+still span several pages, ragged last pages, identity rows and several splits."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import msa_oracle as O
+from synth import workloads as W
+from tests import gpu_common as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def M():
+    import sparse_attention_decode_fp8_amd as M
+    return M
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+@pytest.mark.parametrize("fmt", [W.FMT_FP8, W.FMT_NVFP4])
+def test_append_bytes_bit_exact(M, fmt):
+    wl = W.small(fmt, [1000, 300, 129], 2, num_kv_heads=2, k=4, seed=41)
+    _print("append parity", wl.name, wl.num_pages)
+    pool = G.gpu_pool(M, wl)
+    step, q, q_idx, w, app = G.gpu_step_inputs(M, wl)
+    M.msa_kv_append(pool, *app)
+    # a negative slot is skipped
+    M.msa_kv_append(pool, torch.tensor([-1, -5], dtype=torch.int64, device="cuda"),
+                    app[1][:2].contiguous(), app[2][:2].contiguous(), app[3][:2].contiguous())
+    torch.cuda.synchronize()
+    ref = G.oracle_pool(wl)
+    for name, arr in pool.arrays().items():
+        g = arr.cpu().numpy()
+        e = ref[name]
+        if name in ("k_scales", "v_scales") and fmt == W.FMT_FP8:
+            assert np.array_equal(g, e.astype(np.float32))
+        else:
+            assert np.array_equal(g.reshape(-1), e.reshape(-1).view(np.uint8)), name
+
+
+@pytest.mark.parametrize("fmt", [W.FMT_FP8, W.FMT_NVFP4])
+@pytest.mark.parametrize("num_splits", [1, 2, 5])
+def test_full_step_parity(M, fmt, num_splits):
+    wl = W.small(fmt, [1000, 2600, 130, 640], 3, num_kv_heads=2, k=5, seed=31)
+    _print("step parity", wl.name, "splits", num_splits)
+    pool = G.gpu_pool(M, wl)
+    bufs = G.run_gpu_step(M, wl, pool, num_splits)
+    ref_pool = G.oracle_pool(wl)
+    S_ref = O.index_score(ref_pool, wl.block_table, wl.row_seq, wl.row_pos, wl.q_idx, wl.w, wl.max_blocks)
+    sel_ref = O.select_topk(S_ref, wl.row_pos, wl.k)
+    out_ref = O.attend(ref_pool, wl.block_table, wl.row_seq, wl.row_pos, wl.q, sel_ref, wl.softmax_scale)
+    S = bufs.block_scores.cpu().numpy()
+    G.assert_scores_close(S, S_ref)
+    sel = bufs.sel.cpu().numpy()
+    nb = wl.row_pos // 128 + 1
+    same = np.ones(wl.num_rows, bool)
+    for r in range(wl.num_rows):
+        if G.gap_qualified(S_ref[r], nb[r], wl.k):
+            assert np.array_equal(sel[r], sel_ref[r]), r
+        else:
+            G.check_selection_valid(sel[r], S_ref[r], nb[r], wl.k)
+            same[r] = np.array_equal(sel[r], sel_ref[r])
+    out = G.bf16_to_np(bufs.out)
+    G.assert_out_close(out[same], out_ref[same], "outputs")
+    # partials of the split that the kernel wrote
+    m, l, Op = O.split_partials(ref_pool, wl.block_table, wl.row_seq, wl.row_pos, wl.q, sel_ref,
+                                wl.softmax_scale, num_splits)
+    ml = bufs.part_ml.cpu().numpy()
+    po = bufs.part_o.cpu().numpy()
+    for r in np.nonzero(same)[0]:
+        fin = np.isfinite(m[r])
+        assert np.array_equal(np.isneginf(ml[r, :, :, 0]), ~fin)
+        assert np.allclose(ml[r, :, :, 0][fin], m[r][fin], rtol=1e-4, atol=1e-3)
+        lr = np.where(fin, l[r], 0)
+        assert np.allclose(ml[r, :, :, 1], lr, rtol=2e-2, atol=1e-3)
+        # O is unnormalised; compare relative to its sum of weights
+        den = np.maximum(lr, 1e-30)[..., None]
+        assert np.max(np.abs(po[r] / den - Op[r] / den)[fin]) < 1e-2
+
+
+def test_num_splits_agree(M):
+    wl = W.small(W.FMT_NVFP4, [3000, 2000], 1, num_kv_heads=1, k=16, seed=43)
+    pool = G.gpu_pool(M, wl)
+    outs = []
+    for ns in (1, 2, 4, 8, 16):
+        _print("splits", ns)
+        bufs = G.run_gpu_step(M, wl, pool.clone(), ns)
+        outs.append(bufs.out.float().cpu().numpy())
+    for o in outs[1:]:
+        assert np.max(np.abs(o - outs[0])) <= 2 ** -7   # one bf16 ulp at |x| < 2
+
+
+def _select_case(rng, rows, nb_max, k, quantum):
+    S = np.full((rows, nb_max), -np.inf, np.float32)
+    pos = rng.integers(0, nb_max * 128, size=rows).astype(np.int32)
+    pos[0] = nb_max * 128 - 1
+    for r in range(rows):
+        nb = pos[r] // 128 + 1
+        S[r, :nb] = (np.round(rng.standard_normal(nb) * 8 / quantum) * quantum).astype(np.float32)
+    return S, pos
+
+
+@pytest.mark.parametrize("nb_max,k,n_init,n_local,quantum", [
+    (40, 8, 0, 1, 1.0), (257, 16, 0, 1, 0.5), (2048, 32, 0, 1, 4.0), (1025, 16, 2, 2, 2.0),
+    (5000, 64, 1, 1, 0.25), (300, 7, 0, 0, 1.0)])
+def test_select_bit_exact_on_fp32_scores_with_ties(M, nb_max, k, n_init, n_local, quantum):
+    """Same fp32 scores on both sides (heavy exact ties): the tables must agree bit for bit."""
+    rng = np.random.default_rng(nb_max + k)
+    rows = 12
+    S, pos = _select_case(rng, rows, nb_max, k, quantum)
+    _print("select", nb_max, k, n_init, n_local)
+    step = M.Step(np.zeros((1, nb_max), np.int32), np.zeros(rows, np.int32), pos)
+    sel = torch.empty((rows, k), dtype=torch.int32, device="cuda")
+    M.msa_select_topk(step, torch.from_numpy(S).cuda(), k, n_init, n_local, sel)
+    ref = O.select_topk(S.astype(np.float64), pos, k, n_init, n_local)
+    assert np.array_equal(sel.cpu().numpy(), ref)
+
+
+def test_select_over_1024_way_tie(M):
+    nb = 2048
+    S = np.full((1, nb), 1.0, np.float32)
+    tied = np.sort(np.random.default_rng(5).choice(nb - 1, 1500, replace=False))
+    S[0, tied] = 3.5
+    step = M.Step(np.zeros((1, nb), np.int32), np.zeros(1, np.int32), np.array([nb * 128 - 1], np.int32))
+    sel = torch.empty((1, 32), dtype=torch.int32, device="cuda")
+    M.msa_select_topk(step, torch.from_numpy(S).cuda(), 32, 0, 1, sel)
+    assert list(sel.cpu().numpy()[0]) == sorted(list(tied[:31]) + [nb - 1])
+
+
+def test_index_scores_tie_exactly_for_identical_keys(M):
+    wl = W.small(W.FMT_FP8, [128 * 40], 0, num_kv_heads=1, k=8, seed=44)
+    W.inject_ties(wl, 20)
+    pool = G.gpu_pool(M, wl)
+    step, q, q_idx, w, _ = G.gpu_step_inputs(M, wl)
+    S = torch.empty((1, wl.max_blocks), dtype=torch.float32, device="cuda")
+    M.msa_index_score(pool, step, q_idx, w, S)
+    S = S.cpu().numpy()[0]
+    tied = wl.tie_blocks[0]
+    assert len(set(S[tied].tolist())) == 1
+    others = np.setdiff1d(np.arange(wl.max_blocks), tied)
+    assert S[tied[0]] > S[others].max()
+
+
+def test_decode_on_oracle_selection_matches_attention(M):
+    """msa_sparse_decode + msa_combine given the oracle's selection table."""
+    for fmt in (W.FMT_FP8, W.FMT_NVFP4):
+        wl = W.small(fmt, [700, 5000, 64], 1, num_kv_heads=3, k=6, seed=45)
+        _print("decode given selection", wl.name)
+        pool = G.gpu_pool(M, wl)
+        step, q, q_idx, w, app = G.gpu_step_inputs(M, wl)
+        M.msa_kv_append(pool, *app)
+        ref_pool = G.oracle_pool(wl)
+        S_ref = O.index_score(ref_pool, wl.block_table, wl.row_seq, wl.row_pos, wl.q_idx, wl.w,
+                              wl.max_blocks)
+        sel_ref = O.select_topk(S_ref, wl.row_pos, wl.k)
+        out_ref = O.attend(ref_pool, wl.block_table, wl.row_seq, wl.row_pos, wl.q, sel_ref,
+                           wl.softmax_scale)
+        sel = torch.from_numpy(sel_ref).cuda()
+        for ns in (1, 3, 6):
+            po = torch.empty((wl.num_rows, wl.num_heads, ns, 128), dtype=torch.float32, device="cuda")
+            pm = torch.empty((wl.num_rows, wl.num_heads, ns, 2), dtype=torch.float32, device="cuda")
+            out = torch.empty((wl.num_rows, wl.num_heads, 128), dtype=torch.bfloat16, device="cuda")
+            M.msa_sparse_decode(pool, step, q, sel, wl.k, wl.softmax_scale, ns, po, pm)
+            M.msa_combine(wl.num_rows, wl.num_heads, 128, ns, po, pm, out)
+            G.assert_out_close(G.bf16_to_np(out), out_ref, f"{wl.name} splits {ns}")
+
+
+def test_combine_matches_oracle_combine(M):
+    rng = np.random.default_rng(8)
+    rows, H, S = 3, 32, 5
+    m = rng.standard_normal((rows, H, S)) * 4
+    m[0, 0, 2] = -np.inf
+    l = rng.random((rows, H, S)) * 10 + 0.5
+    l[0, 0, 2] = 0.0
+    Op = rng.standard_normal((rows, H, S, 128)) * l[..., None]
+    Op[0, 0, 2] = 0.0
+    ml = np.stack([m, l], -1).astype(np.float32)
+    out = torch.empty((rows, H, 128), dtype=torch.bfloat16, device="cuda")
+    M.msa_combine(rows, H, 128, S, torch.from_numpy(Op.astype(np.float32)).cuda(),
+                  torch.from_numpy(ml).cuda(), out)
+    ref = O.combine(ml[..., 0].astype(np.float64), ml[..., 1].astype(np.float64),
+                    Op.astype(np.float32).astype(np.float64))
+    got = G.bf16_to_np(out)
+    # one bf16 rounding of the exact merge
+    assert np.all(np.abs(got - ref) <= np.abs(ref) * 2 ** -8 + 1e-6)
