@@ -1,0 +1,301 @@
+#!/usr/bin/env python3
+"""Benchmark of one block-sparse decode step on one MI355X.
+
+Workload: 8 requests x 1 query token, 4 KV heads x 16 query heads, head_dim 128,
+32768 cached tokens each + 1 appended token, NVFP4 KV in shuffled P128 pages, index
+keys E4M3, top-16 blocks. A step is the whole path: append -> index score -> select
+-> sparse decode -> combine.
+
+Timing. All inputs are resident in HBM before timing. The pool is replicated R times
+(16 x 169 MB) and step i uses replica i % R, so the ~26 MB a step touches has been
+evicted from the 256 MB Infinity Cache and the L2s before it is read again. Steps are
+captured in HIP graphs (one graph per replica, plus one graph of all R) and replayed;
+exactly K steps are timed between two synchronisations.
+
+Per-kernel durations are measured live with HIP events on the step's stream, in a
+second pass where the launches are queued behind a GPU sleep so that no host gap falls
+between the event pair. The roofline entry uses the decode kernel's mean duration and
+its algorithmic bytes (selected visible K/V bytes + Q + O + selection/block-table
+reads). HBM traffic comes from rocprofv3 FETCH_SIZE / WRITE_SIZE counters recorded in
+profiles/ and is reported only while the kernel source is unchanged since then.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+WORKLOAD_CFG = 1
+REPLICAS = 16
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--num-splits", type=int, default=0, help="0 = library default for k")
+    ap.add_argument("--replicas", type=int, default=REPLICAS)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after timing, run one device copy of this size (counter calibration)")
+    return ap.parse_args()
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for f in ("sparse_decode.hip", "msa_device.h"):
+        with open(os.path.join(ROOT, "sparse_attention_decode_fp8_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def decode_algorithmic_bytes(wl, sel, bytes_per_token):
+    """Selected visible tokens (union over a request's rows) x KV heads x bytes per
+    token, + Q and O (bf16), + selection table and block-table entries read."""
+    import numpy as np
+    tok = 0
+    for s in range(len(wl.ctx_lens)):
+        rows = np.nonzero(wl.row_seq == s)[0]
+        vis = set()
+        for r in rows:
+            for b in sel[r]:
+                if b >= 0:
+                    hi = min(128 * (int(b) + 1), int(wl.row_pos[r]) + 1)
+                    vis.update(range(128 * int(b), hi))
+        tok += len(vis)
+    kv = tok * wl.num_kv_heads * bytes_per_token
+    qo = 2 * wl.num_rows * wl.num_heads * 128 * 2
+    meta = sel.size * 4 + int((sel >= 0).sum()) * 4
+    return kv + qo + meta, tok
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the decode path has no multi-GPU part in this library)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import sparse_attention_decode_fp8_amd as M
+    from sparse_attention_decode_fp8_amd.pipeline import default_num_splits
+    from synth import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    wl = W.config(WORKLOAD_CFG)
+    ns = args.num_splits or default_num_splits(wl.k)
+    print(f"[bench] workload {wl.name} generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    def bf16(bits):
+        a = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16)).view(np.int16)
+        return torch.from_numpy(a).to(dev).view(torch.bfloat16)
+
+    pool0 = M.KVPool(wl.fmt, wl.num_pages, wl.num_kv_heads, k_tensor_scale=wl.k_tensor_scale,
+                     v_tensor_scale=wl.v_tensor_scale, k_page_scale=wl.k_page_scale,
+                     v_page_scale=wl.v_page_scale)
+    for s in range(len(wl.ctx_lens)):
+        L = int(wl.ctx_lens[s])
+        M.msa_kv_append(pool0, torch.from_numpy(wl.slots(s, np.arange(L))).to(dev),
+                        bf16(wl.k_src[s][:L]), bf16(wl.v_src[s][:L]), bf16(wl.idx_src[s][:L]))
+    torch.cuda.synchronize()
+    pools = [pool0] + [pool0.clone() for _ in range(args.replicas - 1)]
+    step = M.Step(wl.block_table, wl.row_seq, wl.row_pos)
+    q, q_idx = bf16(wl.q), bf16(wl.q_idx)
+    w = torch.from_numpy(wl.w).to(dev)
+    sl, kb, vb, ib = wl.step_tokens()
+    slot, k_new, v_new, idx_new = torch.from_numpy(sl).to(dev), bf16(kb), bf16(vb), bf16(ib)
+    bufs = M.DecodeBuffers(wl.num_rows, wl.num_heads, wl.max_blocks, wl.k, ns)
+    print(f"[bench] {args.replicas} pool replicas ready, splits {ns}", file=sys.stderr, flush=True)
+
+    def one_step(p, stream=None):
+        M.run_step(p, step, bufs, q, q_idx, w, wl.softmax_scale, slot=slot, k_new=k_new,
+                   v_new=v_new, idx_k_new=idx_new, n_init=wl.n_init, n_local=wl.n_local,
+                   stream=stream)
+
+    # ---- capture: one graph per replica and one graph of all replicas
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for p in pools:
+            one_step(p)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for p in pools:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            one_step(p)
+        graphs.append(g)
+    g_all = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_all):
+        for p in pools:
+            one_step(p)
+    torch.cuda.synchronize()
+
+    def run_steps(n):
+        full, rem = divmod(n, len(pools))
+        for _ in range(full):
+            g_all.replay()
+        for i in range(rem):
+            graphs[i].replay()
+
+    run_steps(args.warmup)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    run_steps(args.steps)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_total = ev0.elapsed_time(ev1)
+    ms_per_step = ms_total / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.2f} us/step", file=sys.stderr, flush=True)
+
+    # ---- per-kernel durations: events around each launch, queued behind a GPU sleep
+    names = ["msa_kv_append", "msa_index_score", "msa_select_topk", "msa_sparse_decode", "msa_combine"]
+    n_meas = min(args.steps, 160)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_meas)]
+    torch.cuda.synchronize()
+    cur = torch.cuda.current_stream()
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(50_000_000)
+    for i in range(n_meas):
+        p = pools[i % len(pools)]
+        e = evs[i]
+        e[0].record()
+        M.msa_kv_append(p, slot, k_new, v_new, idx_new)
+        e[1].record()
+        M.msa_index_score(p, step, q_idx, w, bufs.block_scores)
+        e[2].record()
+        M.msa_select_topk(step, bufs.block_scores, wl.k, wl.n_init, wl.n_local, bufs.sel)
+        e[3].record()
+        M.msa_sparse_decode(p, step, q, bufs.sel, wl.k, wl.softmax_scale, ns, bufs.part_o, bufs.part_ml)
+        e[4].record()
+        M.msa_combine(wl.num_rows, wl.num_heads, 128, ns, bufs.part_o, bufs.part_ml, bufs.out)
+        e[5].record()
+    torch.cuda.synchronize()
+    per_kernel_us = {}
+    for j, nm in enumerate(names):
+        d = np.array([evs[i][j].elapsed_time(evs[i][j + 1]) * 1e3 for i in range(n_meas)])
+        per_kernel_us[nm] = {"mean": float(d.mean()), "p10": float(np.percentile(d, 10)),
+                             "p50": float(np.median(d)), "p90": float(np.percentile(d, 90))}
+    del cur
+
+    sel = bufs.sel.cpu().numpy()
+    bpt = 144 if wl.fmt == W.FMT_NVFP4 else 256
+    dec_bytes, dec_tokens = decode_algorithmic_bytes(wl, sel, bpt)
+    idx_bytes = int(sum(int(wl.row_pos[r]) + 1 for r in range(wl.num_rows)) * 64)   # 1 row / request
+    t_dec = per_kernel_us["msa_sparse_decode"]["mean"] * 1e-6
+    t_idx = per_kernel_us["msa_index_score"]["mean"] * 1e-6
+    achieved = dec_bytes / t_dec / 1e9
+
+    traffic = None
+    prof = os.path.join(ROOT, "profiles", "msa_sparse_decode_b8_ctx32k_nvfp4_top16.counters.json")
+    if os.path.exists(prof):
+        with open(prof) as fh:
+            pc = json.load(fh)
+        if pc.get("source_digest") == kernel_source_digest() and pc.get("num_splits") == ns:
+            traffic = pc.get("hbm_bytes_per_launch")
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+
+    rows = wl.num_rows
+    line = {
+        "metric": "sparse-decode query tokens/s + achieved HBM GB/s (% of peak), B=8 ctx 32k",
+        "value": rows / (ms_per_step * 1e-3),
+        "unit": "q-tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4/e4m3 storage, fp16 MFMA operands, fp32 accumulate, bf16 out",
+        "data": "synthetic (seeded N(0,1) K/V/Q, shuffled page table)",
+        "config": {"workload": wl.name, "batch": 8, "query_rows": rows, "kv_heads": wl.num_kv_heads,
+                   "q_heads": wl.num_heads, "head_dim": 128, "cached_tokens": int(wl.ctx_lens[0]),
+                   "appended_tokens": wl.n_append, "top_k": wl.k, "kv_format": "nvfp4",
+                   "num_splits": ns, "pool_replicas": args.replicas, "parallelism": "single GPU"},
+        "roofline": {"kernel": "msa_sparse_decode", "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "algorithmic_bytes": dec_bytes,
+                     "visible_selected_tokens": dec_tokens, "mean_us": t_dec * 1e6},
+        "index_score_roofline": {"bound": "hbm", "achieved": idx_bytes / t_idx / 1e9,
+                                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac": idx_bytes / t_idx / 1e9 / HBM_PEAK_GBS,
+                                 "algorithmic_bytes": idx_bytes, "mean_us": t_idx * 1e6},
+        "kernel_us": per_kernel_us,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(wl, budget_s):
+    """The float64 oracle, unchanged, timed on host cores for a bounded sample of the
+    same workload: whole steps (append, index score, select, attention) of the 8
+    requests, round robin, until the time budget is spent; BLAS limited to one thread."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import msa_oracle as O
+
+    cases = []
+    with threadpool_limits(1):
+        for s in range(len(wl.ctx_lens)):
+            rows = np.nonzero(wl.row_seq == s)[0]
+            L = int(wl.ctx_lens[s])
+            pool = O.new_pool(wl.fmt, wl.num_pages, wl.num_kv_heads, k_tensor_scale=wl.k_tensor_scale,
+                              v_tensor_scale=wl.v_tensor_scale)
+            O.kv_append(pool, wl.slots(s, np.arange(L)), None, None, wl.idx_src[s][:L])
+            sl, kb, vb, ib = wl.prefill_slices(s, np.arange(L, L + wl.n_append))
+            args = (wl.block_table, wl.row_seq[rows], wl.row_pos[rows], sl, kb, vb, ib,
+                    wl.q_idx[rows], wl.w[rows], wl.q[rows], wl.k, wl.softmax_scale, wl.max_blocks)
+            # untimed: learn which pages the step attends and give the pool their K/V
+            S = O.index_score(pool, *args[:3], args[7], args[8], wl.max_blocks)
+            sel = O.select_topk(S, args[2], wl.k, wl.n_init, wl.n_local)
+            pos = np.concatenate([np.arange(128 * b, min(128 * (b + 1), L)) for b in sel.ravel() if b >= 0])
+            pos = np.unique(pos[pos < L])
+            O.kv_append(pool, wl.slots(s, pos), wl.k_src[s][pos], wl.v_src[s][pos], None)
+            cases.append((pool, args, len(rows)))
+        done, steps, t_total = 0, 0, 0.0
+        while t_total < budget_s:
+            pool, args, nrows = cases[steps % len(cases)]
+            t = time.perf_counter()
+            O.decode_step(pool, *args)
+            t_total += time.perf_counter() - t
+            done += nrows
+            steps += 1
+    return {"value": done / t_total, "unit": "q-tok/s", "cores": 1, "kind": "oracle",
+            "sample": f"{steps} oracle steps of single requests of the same workload (each: "
+                      f"append 1 token, index score over 32769 tokens, top-16 select, attention "
+                      f"over the selected pages for 64 heads), {done} query rows in {t_total:.1f} s, "
+                      f"numpy/BLAS limited to 1 thread"}
+
+
+if __name__ == "__main__":
+    main()

@@ -36,3 +36,9 @@ def run_step(pool, step, bufs: DecodeBuffers, q, q_idx, w, softmax_scale, slot=N
     L.msa_combine(step.num_rows, q.shape[1], L.HEAD_DIM, bufs.num_splits, bufs.part_o, bufs.part_ml,
                   bufs.out, stream)
     return bufs.out
+
+
+def default_num_splits(k: int) -> int:
+    """Split count used by the benchmark and the full-size parity tests: one split per
+    four selected pages (each split is one workgroup of four waves, one page per wave)."""
+    return max(1, (k + 3) // 4)

@@ -127,3 +127,24 @@ def assert_out_close(out_gpu, out_ref, what=""):
     err = np.abs(out_gpu - out_ref).max()
     assert err <= OUT_ATOL, f"{what} max abs err {err:.4g}"
     return err
+
+
+def oracle_rows(wl: W.Workload, rows):
+    """Index scores, selection and attention of the given rows, computed by the oracle
+    from the seeded source alone (it encodes only the pages those rows need)."""
+    rows = list(rows)
+    seqs = sorted(set(int(wl.row_seq[r]) for r in rows))
+    pool = oracle_pool(wl, seqs=seqs, kv_blocks={s: [] for s in seqs})
+    sub = np.asarray(rows)
+    S = O.index_score(pool, wl.block_table, wl.row_seq[sub], wl.row_pos[sub], wl.q_idx[sub],
+                      wl.w[sub], wl.max_blocks)
+    sel = O.select_topk(S, wl.row_pos[sub], wl.k, wl.n_init, wl.n_local)
+    for s in seqs:
+        blocks = sorted(set(int(b) for i, r in enumerate(rows) if wl.row_seq[r] == s
+                            for b in sel[i] if b >= 0))
+        T = wl.total_len(s)
+        pos = np.concatenate([np.arange(b * 128, min((b + 1) * 128, T)) for b in blocks])
+        O.kv_append(pool, wl.slots(s, pos), wl.k_src[s][pos], wl.v_src[s][pos], None)
+    out = O.attend(pool, wl.block_table, wl.row_seq[sub], wl.row_pos[sub], wl.q[sub], sel,
+                   wl.softmax_scale)
+    return S, sel, out, pool
