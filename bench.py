@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--num-splits", type=int, default=0, help="0 = library default for k")
     ap.add_argument("--replicas", type=int, default=REPLICAS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate", action="store_true",
+                    help="five launches per step (one per stage) instead of the two fused ones")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one device copy of this size (counter calibration)")
@@ -123,7 +125,7 @@ def main():
     def one_step(p, stream=None):
         M.run_step(p, step, bufs, q, q_idx, w, wl.softmax_scale, slot=slot, k_new=k_new,
                    v_new=v_new, idx_k_new=idx_new, n_init=wl.n_init, n_local=wl.n_local,
-                   stream=stream)
+                   fused=not args.separate, stream=stream)
 
     # ---- capture: one graph per replica and one graph of all replicas
     side = torch.cuda.Stream()
@@ -165,41 +167,55 @@ def main():
     print(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.2f} us/step", file=sys.stderr, flush=True)
 
     # ---- per-kernel durations: events around each launch, queued behind a GPU sleep
-    names = ["msa_kv_append", "msa_index_score", "msa_select_topk", "msa_sparse_decode", "msa_combine"]
+    if args.separate:
+        names = ["msa_kv_append", "msa_index_score", "msa_select_topk", "msa_sparse_decode", "msa_combine"]
+        calls = [
+            lambda p: M.msa_kv_append(p, slot, k_new, v_new, idx_new),
+            lambda p: M.msa_index_score(p, step, q_idx, w, bufs.block_scores),
+            lambda p: M.msa_select_topk(step, bufs.block_scores, wl.k, wl.n_init, wl.n_local, bufs.sel,
+                                        bufs.sel_pages),
+            lambda p: M.msa_sparse_decode(p, step, q, bufs.sel, wl.k, wl.softmax_scale, ns, bufs.part_o,
+                                          bufs.part_ml, sel_pages=bufs.sel_pages),
+            lambda p: M.msa_combine(wl.num_rows, wl.num_heads, 128, ns, bufs.part_o, bufs.part_ml, bufs.out),
+        ]
+        decode_kernels = ["msa_sparse_decode", "msa_combine"]
+    else:
+        names = ["msa_append_score_select", "msa_select_decode_combine"]
+        calls = [
+            lambda p: M.msa_append_score_select(p, step, q_idx, w, wl.k, wl.n_init, wl.n_local,
+                                                bufs.block_scores, slot=slot, k_new=k_new,
+                                                v_new=v_new, idx_k_new=idx_new),
+            lambda p: M.msa_select_decode_combine(p, step, q, bufs.block_scores, wl.k, wl.n_init,
+                                                  wl.n_local, wl.softmax_scale, ns, bufs.part_o,
+                                                  bufs.part_ml, bufs.counters, bufs.out,
+                                                  sel=bufs.sel, sel_pages=bufs.sel_pages),
+        ]
+        decode_kernels = ["msa_select_decode_combine"]
     n_meas = min(args.steps, 160)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_meas)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(n_meas)]
     torch.cuda.synchronize()
-    cur = torch.cuda.current_stream()
     if hasattr(torch.cuda, "_sleep"):
-        torch.cuda._sleep(50_000_000)
+        torch.cuda._sleep(200_000_000)
     for i in range(n_meas):
         p = pools[i % len(pools)]
         e = evs[i]
         e[0].record()
-        M.msa_kv_append(p, slot, k_new, v_new, idx_new)
-        e[1].record()
-        M.msa_index_score(p, step, q_idx, w, bufs.block_scores)
-        e[2].record()
-        M.msa_select_topk(step, bufs.block_scores, wl.k, wl.n_init, wl.n_local, bufs.sel)
-        e[3].record()
-        M.msa_sparse_decode(p, step, q, bufs.sel, wl.k, wl.softmax_scale, ns, bufs.part_o, bufs.part_ml)
-        e[4].record()
-        M.msa_combine(wl.num_rows, wl.num_heads, 128, ns, bufs.part_o, bufs.part_ml, bufs.out)
-        e[5].record()
+        for j, call in enumerate(calls):
+            call(p)
+            e[j + 1].record()
     torch.cuda.synchronize()
     per_kernel_us = {}
     for j, nm in enumerate(names):
         d = np.array([evs[i][j].elapsed_time(evs[i][j + 1]) * 1e3 for i in range(n_meas)])
         per_kernel_us[nm] = {"mean": float(d.mean()), "p10": float(np.percentile(d, 10)),
                              "p50": float(np.median(d)), "p90": float(np.percentile(d, 90))}
-    del cur
 
     sel = bufs.sel.cpu().numpy()
     bpt = 144 if wl.fmt == W.FMT_NVFP4 else 256
     dec_bytes, dec_tokens = decode_algorithmic_bytes(wl, sel, bpt)
     idx_bytes = int(sum(int(wl.row_pos[r]) + 1 for r in range(wl.num_rows)) * 64)   # 1 row / request
-    t_dec = per_kernel_us["msa_sparse_decode"]["mean"] * 1e-6
-    t_idx = per_kernel_us["msa_index_score"]["mean"] * 1e-6
+    t_dec = sum(per_kernel_us[k]["mean"] for k in decode_kernels) * 1e-6
+    t_idx = per_kernel_us[names[0] if not args.separate else "msa_index_score"]["mean"] * 1e-6
     achieved = dec_bytes / t_dec / 1e9
 
     traffic = None
@@ -241,11 +257,12 @@ def main():
                    "q_heads": wl.num_heads, "head_dim": 128, "cached_tokens": int(wl.ctx_lens[0]),
                    "appended_tokens": wl.n_append, "top_k": wl.k, "kv_format": "nvfp4",
                    "num_splits": ns, "pool_replicas": args.replicas, "parallelism": "single GPU"},
-        "roofline": {"kernel": "msa_sparse_decode", "bound": "hbm", "achieved": achieved,
+        "roofline": {"kernel": "+".join(decode_kernels), "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes": dec_bytes,
                      "visible_selected_tokens": dec_tokens, "mean_us": t_dec * 1e6},
-        "index_score_roofline": {"bound": "hbm", "achieved": idx_bytes / t_idx / 1e9,
+        "index_score_roofline": {"kernel": names[0] if not args.separate else "msa_index_score",
+                                 "bound": "hbm", "achieved": idx_bytes / t_idx / 1e9,
                                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                  "frac": idx_bytes / t_idx / 1e9 / HBM_PEAK_GBS,
                                  "algorithmic_bytes": idx_bytes, "mean_us": t_idx * 1e6},

@@ -10,6 +10,10 @@
  *   msa_sparse_decode  GQA flash-decode over the selected pages, split-KV partials
  *   msa_combine        fixed-order log-sum-exp merge of the partials into bf16 outputs
  *
+ * Fused entry points run the same step in two launches: msa_append_score_select
+ * (append + score, optionally + select) and msa_select_decode_combine (select + decode
+ * + combine) or msa_sparse_decode_combine (decode + combine).
+ *
  * The operations follow three public TensorRT-LLM pull-request pages:
  *   [Rubin] "[None][feat] Add Rubin (sm_107) MiniMax-M3.1 low-latency decode targets" (#21136)
  *   [GB300] "MiniMax-M3 NVFP4 low-latency decode megakernel for modeling_v2 for Blackwell" (#20306)
@@ -152,11 +156,35 @@ msa_status_t msa_index_score(const msa_kv_pool_t* pool, const msa_step_t* step,
  *             (higher score, then smaller block index). Output ascending.
  *   block_scores : fp32 [num_rows][max_blocks_per_seq]; only b < nb(r) is read
  *   sel          : int32 [num_rows][k] (output, logical block ids)
+ *   sel_pages    : int32 [num_rows][k] (output, may be NULL) the physical page of each
+ *                  selected block, block_table[row_seq[r]][sel[r][i]], -1 where sel is -1
  * 1 <= k <= 64, n_init >= 0, n_local >= 0, n_init + n_local <= k,
  * max_blocks_per_seq <= 12288. The result is deterministic for any tie width.
  */
 msa_status_t msa_select_topk(const msa_step_t* step, const float* block_scores, int32_t k,
-                             int32_t n_init, int32_t n_local, int32_t* sel, void* stream);
+                             int32_t n_init, int32_t n_local, int32_t* sel, int32_t* sel_pages,
+                             void* stream);
+
+/*
+ * msa_kv_append + msa_index_score + msa_select_topk in one launch, with the same
+ * results and outputs as the three calls in that order ([GB300] "The TP4 decode
+ * target": block selection and the KV update fused into the decode megakernels; "The
+ * TP8 decode target": index scoring fused with block selection). Arguments are those
+ * of the three calls; additionally:
+ *   counters : int32 [num_rows], all zero before the call; left zero again. Two calls
+ *              that share `counters` must not run concurrently.
+ * n_new <= 4096 (larger appends: call msa_kv_append first, then this with n_new = 0).
+ * block_scores is written as by msa_index_score and is the selection's workspace.
+ * With sel == NULL and counters == NULL the call only appends and scores (the
+ * selection then runs inside msa_select_decode_combine); sel_pages is ignored.
+ */
+msa_status_t msa_append_score_select(const msa_kv_pool_t* pool, const msa_step_t* step,
+                                     int32_t n_new, const int64_t* slot, const void* k_new,
+                                     const void* v_new, const void* idx_k_new,
+                                     int32_t n_idx_heads, const void* q_idx, const float* w,
+                                     int32_t k, int32_t n_init, int32_t n_local,
+                                     float* block_scores, int32_t* sel, int32_t* sel_pages,
+                                     int32_t* counters, void* stream);
 
 /*
  * Sparse GQA flash-decode with split-KV partials ([Rubin] commit messages: one unit of
@@ -166,17 +194,51 @@ msa_status_t msa_select_topk(const msa_step_t* step, const float* block_scores, 
  * visible. With x_p = softmax_scale * (q[r][h] . K_p) * log2(e), each split writes
  *   part_ml[r][h][s] = { m = max_p x_p, l = sum_p 2^(x_p - m) }  (m = -inf, l = 0 if empty)
  *   part_o[r][h][s][:] = sum_p 2^(x_p - m) * V_p                   (0 if empty)
- *   q       : bf16 [num_rows][num_q_heads][head_dim]
- *   sel     : int32 [num_rows][k] as written by msa_select_topk
- *   part_o  : fp32 [num_rows][num_q_heads][num_splits][head_dim]  (output)
- *   part_ml : fp32 [num_rows][num_q_heads][num_splits][2]         (output)
+ *   q         : bf16 [num_rows][num_q_heads][head_dim]
+ *   sel       : int32 [num_rows][k] as written by msa_select_topk
+ *   sel_pages : int32 [num_rows][k] page ids as written by msa_select_topk, or NULL to
+ *               look each block up in the block table
+ *   part_o    : fp32 [num_rows][num_q_heads][num_splits][head_dim]  (output)
+ *   part_ml   : fp32 [num_rows][num_q_heads][num_splits][2]         (output)
  * num_q_heads must be 16 * num_kv_heads; 1 <= num_splits <= k.
  * Accumulation is fp32 on the matrix cores; K and V are dequantised exactly to fp16.
  */
 msa_status_t msa_sparse_decode(const msa_kv_pool_t* pool, const msa_step_t* step,
                                int32_t num_q_heads, const void* q, const int32_t* sel,
-                               int32_t k, float softmax_scale, int32_t num_splits,
-                               float* part_o, float* part_ml, void* stream);
+                               const int32_t* sel_pages, int32_t k, float softmax_scale,
+                               int32_t num_splits, float* part_o, float* part_ml, void* stream);
+
+/*
+ * msa_sparse_decode followed by msa_combine in one launch: the last split of each
+ * (row, KV head) to finish merges all splits of that row and head exactly as
+ * msa_combine does ([Rubin] "Items and numerics", LC_ONEDIV) and writes bf16 `out`
+ * [num_rows][num_q_heads][head_dim]. part_o / part_ml are written as above (they are
+ * the workspace of the merge). counters : int32 [num_rows][num_kv_heads], all zero
+ * before the call; the call leaves them zero again. Two calls that share `counters`
+ * must not run concurrently. num_splits <= 16.
+ */
+msa_status_t msa_sparse_decode_combine(const msa_kv_pool_t* pool, const msa_step_t* step,
+                                       int32_t num_q_heads, const void* q, const int32_t* sel,
+                                       const int32_t* sel_pages, int32_t k, float softmax_scale,
+                                       int32_t num_splits, float* part_o, float* part_ml,
+                                       int32_t* counters, void* out, void* stream);
+
+/*
+ * msa_select_topk + msa_sparse_decode + msa_combine in one launch: every workgroup of a
+ * query row runs the row's selection (the deterministic contract of msa_select_topk)
+ * from block_scores itself, then decodes its split, and the last split of each
+ * (row, KV head) merges as msa_sparse_decode_combine does.
+ *   block_scores : fp32 [num_rows][max_blocks_per_seq] as written by msa_index_score
+ *   sel, sel_pages : optional outputs (may be NULL), the selection msa_select_topk writes
+ *   counters : int32 [num_rows][num_kv_heads], zero before the call, left zero
+ * Other arguments as msa_sparse_decode_combine; num_splits <= 16.
+ */
+msa_status_t msa_select_decode_combine(const msa_kv_pool_t* pool, const msa_step_t* step,
+                                       int32_t num_q_heads, const void* q,
+                                       const float* block_scores, int32_t k, int32_t n_init,
+                                       int32_t n_local, float softmax_scale, int32_t num_splits,
+                                       float* part_o, float* part_ml, int32_t* counters,
+                                       void* out, int32_t* sel, int32_t* sel_pages, void* stream);
 
 /*
  * Log-sum-exp merge of split partials ([Rubin] "Items and numerics", LC_ONEDIV: the

@@ -45,21 +45,25 @@ class MsaStep(ctypes.Structure):
                 ("row_seq", ctypes.c_void_p), ("row_pos", ctypes.c_void_p)]
 
 
-EXPORTS = ["msa_kv_append", "msa_index_score", "msa_select_topk", "msa_sparse_decode",
-           "msa_combine", "msa_decode_workspace_bytes", "msa_pool_bytes", "msa_status_string"]
+EXPORTS = ["msa_kv_append", "msa_index_score", "msa_select_topk", "msa_append_score_select",
+           "msa_sparse_decode",
+           "msa_sparse_decode_combine", "msa_select_decode_combine", "msa_combine", "msa_decode_workspace_bytes", "msa_pool_bytes", "msa_status_string"]
 
 
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m sparse_attention_decode_fp8_amd.build`")
+                          "`python sparse_attention_decode_fp8_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, F32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
     sig = {
         "msa_kv_append": (I32, [P, I32, P, P, P, P, P]),
         "msa_index_score": (I32, [P, P, I32, P, P, P, P]),
-        "msa_select_topk": (I32, [P, P, I32, I32, I32, P, P]),
-        "msa_sparse_decode": (I32, [P, P, I32, P, P, I32, F32, I32, P, P, P]),
+        "msa_select_topk": (I32, [P, P, I32, I32, I32, P, P, P]),
+        "msa_append_score_select": (I32, [P, P, I32, P, P, P, P, I32, P, P, I32, I32, I32, P, P, P, P, P]),
+        "msa_sparse_decode": (I32, [P, P, I32, P, P, P, I32, F32, I32, P, P, P]),
+        "msa_sparse_decode_combine": (I32, [P, P, I32, P, P, P, I32, F32, I32, P, P, P, P, P]),
+        "msa_select_decode_combine": (I32, [P, P, I32, P, P, I32, I32, I32, F32, I32, P, P, P, P, P, P, P]),
         "msa_combine": (I32, [I32, I32, I32, I32, P, P, P, P]),
         "msa_decode_workspace_bytes": (SZ, [I32, I32, I32, I32]),
         "msa_pool_bytes": (I32, [I32, I32, I32, I32, I32, ctypes.POINTER(SZ)]),
@@ -168,22 +172,64 @@ def msa_index_score(pool: KVPool, step: Step, q_idx, w, block_scores, stream=Non
            "msa_index_score")
 
 
-def msa_select_topk(step: Step, block_scores, k, n_init, n_local, sel, stream=None):
+def msa_select_topk(step: Step, block_scores, k, n_init, n_local, sel, sel_pages=None, stream=None):
     ss = step.cstruct()
     _check(LIB.msa_select_topk(ctypes.byref(ss), _ptr(block_scores, torch.float32, "block_scores"),
-                               k, n_init, n_local, _ptr(sel, torch.int32, "sel"), _stream(stream)),
+                               k, n_init, n_local, _ptr(sel, torch.int32, "sel"),
+                               _ptr(sel_pages, torch.int32, "sel_pages"), _stream(stream)),
            "msa_select_topk")
 
 
+def msa_append_score_select(pool: KVPool, step: Step, q_idx, w, k, n_init, n_local, block_scores,
+                            sel=None, sel_pages=None, counters=None, slot=None, k_new=None, v_new=None,
+                            idx_k_new=None, stream=None):
+    ps, ss = pool.cstruct(), step.cstruct()
+    n = 0 if slot is None else slot.numel()
+    _check(LIB.msa_append_score_select(
+        ctypes.byref(ps), ctypes.byref(ss), n, _ptr(slot, torch.int64, "slot"),
+        _ptr(k_new, torch.bfloat16, "k_new"), _ptr(v_new, torch.bfloat16, "v_new"),
+        _ptr(idx_k_new, torch.bfloat16, "idx_k_new"), q_idx.shape[1],
+        _ptr(q_idx, torch.bfloat16, "q_idx"), _ptr(w, torch.float32, "w"), k, n_init, n_local,
+        _ptr(block_scores, torch.float32, "block_scores"), _ptr(sel, torch.int32, "sel"),
+        _ptr(sel_pages, torch.int32, "sel_pages"), _ptr(counters, torch.int32, "counters"),
+        _stream(stream)),
+        "msa_append_score_select")
+
+
 def msa_sparse_decode(pool: KVPool, step: Step, q, sel, k, softmax_scale, num_splits, part_o,
-                      part_ml, stream=None):
+                      part_ml, sel_pages=None, stream=None):
     ps, ss = pool.cstruct(), step.cstruct()
     _check(LIB.msa_sparse_decode(ctypes.byref(ps), ctypes.byref(ss), q.shape[1],
-                                 _ptr(q, torch.bfloat16, "q"), _ptr(sel, torch.int32, "sel"), k,
-                                 float(softmax_scale), num_splits,
-                                 _ptr(part_o, torch.float32, "part_o"),
+                                 _ptr(q, torch.bfloat16, "q"), _ptr(sel, torch.int32, "sel"),
+                                 _ptr(sel_pages, torch.int32, "sel_pages"), k, float(softmax_scale),
+                                 num_splits, _ptr(part_o, torch.float32, "part_o"),
                                  _ptr(part_ml, torch.float32, "part_ml"), _stream(stream)),
            "msa_sparse_decode")
+
+
+def msa_sparse_decode_combine(pool: KVPool, step: Step, q, sel, k, softmax_scale, num_splits,
+                              part_o, part_ml, counters, out, sel_pages=None, stream=None):
+    ps, ss = pool.cstruct(), step.cstruct()
+    _check(LIB.msa_sparse_decode_combine(
+        ctypes.byref(ps), ctypes.byref(ss), q.shape[1], _ptr(q, torch.bfloat16, "q"),
+        _ptr(sel, torch.int32, "sel"), _ptr(sel_pages, torch.int32, "sel_pages"), k,
+        float(softmax_scale), num_splits, _ptr(part_o, torch.float32, "part_o"),
+        _ptr(part_ml, torch.float32, "part_ml"), _ptr(counters, torch.int32, "counters"),
+        _ptr(out, torch.bfloat16, "out"), _stream(stream)),
+        "msa_sparse_decode_combine")
+
+
+def msa_select_decode_combine(pool: KVPool, step: Step, q, block_scores, k, n_init, n_local,
+                              softmax_scale, num_splits, part_o, part_ml, counters, out, sel=None,
+                              sel_pages=None, stream=None):
+    ps, ss = pool.cstruct(), step.cstruct()
+    _check(LIB.msa_select_decode_combine(
+        ctypes.byref(ps), ctypes.byref(ss), q.shape[1], _ptr(q, torch.bfloat16, "q"),
+        _ptr(block_scores, torch.float32, "block_scores"), k, n_init, n_local, float(softmax_scale),
+        num_splits, _ptr(part_o, torch.float32, "part_o"), _ptr(part_ml, torch.float32, "part_ml"),
+        _ptr(counters, torch.int32, "counters"), _ptr(out, torch.bfloat16, "out"),
+        _ptr(sel, torch.int32, "sel"), _ptr(sel_pages, torch.int32, "sel_pages"), _stream(stream)),
+        "msa_select_decode_combine")
 
 
 def msa_combine(rows, num_q_heads, head_dim, num_splits, part_o, part_ml, out, stream=None):

@@ -1,6 +1,6 @@
 """Build libmsadecode.so in-tree with hipcc for gfx950.
 
-    python -m sparse_attention_decode_fp8_amd.build [--jobs N]
+    python sparse_attention_decode_fp8_amd/build.py [--jobs N]
 
 Every HIP source is compiled to an object with `hipcc --offload-arch=gfx950`, then
 linked into sparse_attention_decode_fp8_amd/libmsadecode.so next to this file.

@@ -19,19 +19,16 @@ combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_
   const int64_t rh = idx / kQuads;
   const int d4 = static_cast<int>(idx % kQuads);
   const float* ml = part_ml + rh * num_splits * 2;
+  const float* po = part_o + rh * num_splits * kHeadDim + 4 * d4;
   float M = -INFINITY;
   for (int s = 0; s < num_splits; ++s) M = fmaxf(M, ml[2 * s]);
   float4_t num = {0.0f, 0.0f, 0.0f, 0.0f};
   float den = 0.0f;
-  if (M != -INFINITY) {
-    const float* po = part_o + rh * num_splits * kHeadDim + 4 * d4;
-    for (int s = 0; s < num_splits; ++s) {
-      const float m = ml[2 * s];
-      if (m == -INFINITY) continue;
-      const float wgt = exp2f(m - M);
-      den += wgt * ml[2 * s + 1];
-      num += wgt * *reinterpret_cast<const float4_t*>(po + static_cast<int64_t>(s) * kHeadDim);
-    }
+  for (int s = 0; s < num_splits; ++s) {
+    const float m = ml[2 * s];
+    const float wgt = m == -INFINITY ? 0.0f : exp2f(m - M);   // M > -inf whenever m is
+    den += wgt * ml[2 * s + 1];
+    num += wgt * *reinterpret_cast<const float4_t*>(po + static_cast<int64_t>(s) * kHeadDim);
   }
   uint16_t o[4];
 #pragma unroll

@@ -1,4 +1,5 @@
-// msa_index_score: per-token index score, max-pooled over 128-token blocks.
+// msa_index_score: per-token index score, max-pooled over 128-token blocks; and
+// msa_append_score_select: KV append + index score + top-k select in one launch.
 //
 // The scorer streams every visible token's 64-byte E4M3 index key once per request
 // ([GB300] "The TP4 decode target": an index scorer reading index-K pages; [Rubin]
@@ -13,132 +14,245 @@
 // once for all of its query rows. MFMA A = queries (M = row * Hi + head), B = keys
 // (N = 16 tokens), so lane (n, q) ends up with all heads of row-slot q for token n:
 // the head sum is in-lane and its order never depends on the token's position.
-#include "msa_device.h"
+//
+// Fused launch ([GB300] "The TP4 decode target" fuses long-context block selection and
+// the KV update into its attention megakernels; the TP8 target fuses index scoring
+// with block selection): extra workgroups append the new tokens; scoring waves whose
+// page receives a new token encode that token's index key themselves (same encoder)
+// instead of waiting for the append; the scores are stored write-through (agent
+// coherent) and the last scoring workgroup of a row group, found with a counter,
+// runs the selection for those rows.
+#include "append_device.h"
 #include "msa_host.h"
+#include "select_device.h"
 
 namespace msa {
 namespace {
 
 constexpr int kWaves = 4;
 
-template <int kHi>
-__global__ void __launch_bounds__(64 * kWaves)
-index_score_kernel(const uint8_t* __restrict__ index_k, const int32_t* __restrict__ block_table,
-                   const int32_t* __restrict__ row_seq, const int32_t* __restrict__ row_pos,
-                   const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
-                   float* __restrict__ scores, int num_rows, int max_blocks) {
+struct ScoreArgs {
+  const uint8_t* index_k;
+  const int32_t* block_table;
+  const int32_t* row_seq;
+  const int32_t* row_pos;
+  const uint16_t* q_idx;
+  const float* w;
+  float* scores;
+  int num_rows, max_blocks;
+  // fused launch only
+  AppendArgs app;
+  int k, n_init, n_local;
+  int32_t* sel;
+  int32_t* sel_pages;
+  int32_t* counters;
+  int score_wgs_x;   // workgroups along x that score blocks
+};
+
+template <int kHi, int kFmt, bool kFused>
+__global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
+  extern __shared__ uint32_t sel_keys[];        // fused: selection scratch [max_blocks]
+  __shared__ SelectSmem sm;
+  __shared__ int s_last;
   constexpr int kRowsPerGroup = 16 / kHi;
   constexpr int kRowsPerLane = 4 / kHi;
+  if constexpr (kFused) {
+    if (static_cast<int>(blockIdx.y) == a.num_rows) {     // append workgroups
+      const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+      if (gid < static_cast<int64_t>(a.app.n_new) * a.app.groups_per_tok) append_group<kFmt>(a.app, gid);
+      return;
+    }
+    if (static_cast<int>(blockIdx.x) >= a.score_wgs_x) return;
+  }
   const int r0 = blockIdx.y;
-  const int seq = row_seq[r0];
+  const int seq = a.row_seq[r0];
   // Is r0 the first row of a group? Count earlier rows of the same request.
   int j = 0;
-  while (r0 - j - 1 >= 0 && row_seq[r0 - j - 1] == seq) ++j;
+  while (r0 - j - 1 >= 0 && a.row_seq[r0 - j - 1] == seq) ++j;
   if (j % kRowsPerGroup != 0) return;
   int nr = 1;
-  while (nr < kRowsPerGroup && r0 + nr < num_rows && row_seq[r0 + nr] == seq) ++nr;
+  while (nr < kRowsPerGroup && r0 + nr < a.num_rows && a.row_seq[r0 + nr] == seq) ++nr;
+  int max_pos = -1;
+  for (int i = 0; i < nr; ++i) max_pos = max(max_pos, a.row_pos[r0 + i]);
+  const int last_block = max_pos / kPage;
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int b = blockIdx.x * kWaves + wave;
-  if (b >= max_blocks) return;
   const int n = lane & 15, q = lane >> 4;
+  const int b = blockIdx.x * kWaves + wave;
+  const bool active = b < a.max_blocks && b <= last_block;   // this wave scores block b
+  const bool fill = b < a.max_blocks && b > last_block;      // past every row: -inf only
 
-  int max_pos = -1;
-  for (int i = 0; i < nr; ++i) max_pos = max(max_pos, row_pos[r0 + i]);
-  if (b > max_pos / kPage) {           // past every row's last visible block
-    if (lane < nr) scores[static_cast<int64_t>(r0 + lane) * max_blocks + b] = -INFINITY;
-    return;
-  }
-  const int64_t page = block_table[static_cast<int64_t>(seq) * max_blocks + b];
-
-  // Issue all 8 key loads of the block: lane (n, q) reads 16 bytes of token 16t + n,
-  // dims 16q .. 16q+15 (k-step 0 uses the first 8, k-step 1 the last 8).
-  const uint8_t* kp = index_k + (page * kPage + n) * kIndexDim + 16 * q;
-  uint4 key[8];
+  if (active) {
+    const int64_t page = a.block_table[static_cast<int64_t>(seq) * a.max_blocks + b];
+    // All 8 key loads of the block: lane (n, q) reads 16 bytes of token 16t + n,
+    // dims 16q .. 16q+15 (k-step 0 uses the first 8, k-step 1 the last 8).
+    const uint8_t* kp = a.index_k + (page * kPage + n) * kIndexDim + 16 * q;
+    uint4 key[8];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) key[t] = *reinterpret_cast<const uint4*>(kp + t * 16 * kIndexDim);
+    for (int t = 0; t < 8; ++t) key[t] = *reinterpret_cast<const uint4*>(kp + t * 16 * kIndexDim);
 
-  // A operand: lane (m, q) holds query row-slot m / Hi, head m % Hi, dims
-  // 16q + 8ks .. +7, times 2^e (e per (row, head), from the amax over 64 dims).
-  const int m = n;
-  const int rs = m / kHi, hd = m % kHi;
-  float qa[16];
-  bool has_row = rs < nr;
-  if (has_row) {
-    const uint16_t* qp = q_idx + (static_cast<int64_t>(r0 + rs) * kHi + hd) * kIndexDim + 16 * q;
-    const uint4 a0 = reinterpret_cast<const uint4*>(qp)[0], a1 = reinterpret_cast<const uint4*>(qp)[1];
-    const uint32_t wv[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    if constexpr (kFused) {
+      // New tokens landing in this page: encode their keys here (the append runs
+      // concurrently in other workgroups).
+      if (a.app.idx_new != nullptr) {
+        for (int base = 0; base < a.app.n_new; base += 64) {
+          const int i = base + lane;
+          const int64_t sl = i < a.app.n_new ? a.app.slot[i] : -1;
+          uint64_t hits = __ballot(sl >= 0 && sl / kPage == page);
+          while (hits) {
+            const int jj = __ffsll(static_cast<unsigned long long>(hits)) - 1;
+            hits &= hits - 1;
+            const int off = __shfl(static_cast<int>(sl % kPage), jj, 64);
+            if ((off & 15) == n) {
+              const uint4 v = encode_index16(a.app.idx_new + static_cast<int64_t>(base + jj) * kIndexDim + 16 * q);
+#pragma unroll
+              for (int t = 0; t < 8; ++t)
+                if (t == (off >> 4)) key[t] = v;
+            }
+          }
+        }
+      }
+    }
+
+    // A operand: lane (m, q) holds query row-slot m / Hi, head m % Hi, dims
+    // 16q + 8ks .. +7, times 2^e (e per (row, head), from the amax over 64 dims).
+    const int m = n;
+    const int rs = m / kHi, hd = m % kHi;
+    float qa[16];
+    if (rs < nr) {
+      const uint16_t* qp = a.q_idx + (static_cast<int64_t>(r0 + rs) * kHi + hd) * kIndexDim + 16 * q;
+      const uint4 a0 = reinterpret_cast<const uint4*>(qp)[0], a1 = reinterpret_cast<const uint4*>(qp)[1];
+      const uint32_t wv[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        qa[2 * i] = __uint_as_float(wv[i] << 16);
+        qa[2 * i + 1] = __uint_as_float(wv[i] & 0xffff0000u);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) qa[i] = 0.0f;
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(qa[i]));
+    amax = xor_max(xor_max(amax, 16), 32);
+    const int e = f16_prescale_exp(amax);
+    half8_t A0, A1;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      qa[2 * i] = __uint_as_float(wv[i] << 16);
-      qa[2 * i + 1] = __uint_as_float(wv[i] & 0xffff0000u);
+      A0[i] = static_cast<half_t>(ldexpf(qa[i], e));
+      A1[i] = static_cast<half_t>(ldexpf(qa[8 + i], e));
     }
-  } else {
+    // After the MFMA, lane (n, q) holds M = 4q + jj; fetch the matching (row, head)
+    // weight and inverse pre-scale from the lane that owns that M.
+    float wj[4], inv[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) qa[i] = 0.0f;
-  }
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(qa[i]));
-  amax = xor_max(xor_max(amax, 16), 32);
-  const int e = f16_prescale_exp(amax);
-  half8_t A0, A1;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    A0[i] = static_cast<half_t>(ldexpf(qa[i], e));
-    A1[i] = static_cast<half_t>(ldexpf(qa[8 + i], e));
-  }
-  // After the MFMA, lane (n, q) holds M = 4q + jj; fetch the matching (row, head)
-  // weight and inverse pre-scale from the lane that owns that M.
-  float wj[4], inv[4];
-  int rowslot[kRowsPerLane];
-#pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    const int mm = 4 * q + jj;
-    const int ej = __shfl(e, mm, 64);
-    inv[jj] = ldexpf(1.0f, -ej);
-    const int rr = mm / kHi, hh = mm % kHi;
-    wj[jj] = rr < nr ? w[static_cast<int64_t>(r0 + rr) * kHi + hh] : 0.0f;
-  }
-  int pos[kRowsPerLane];
-#pragma unroll
-  for (int i = 0; i < kRowsPerLane; ++i) {
-    rowslot[i] = q * kRowsPerLane + i;
-    pos[i] = rowslot[i] < nr ? row_pos[r0 + rowslot[i]] : -1;
-  }
-
-  float best[kRowsPerLane];
-#pragma unroll
-  for (int i = 0; i < kRowsPerLane; ++i) best[i] = -INFINITY;
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const half8_t B0 = e4m3x8_to_f16(key[t].x, key[t].y);
-    const half8_t B1 = e4m3x8_to_f16(key[t].z, key[t].w);
-    float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    acc = mfma16x16x32(A0, B0, acc);
-    acc = mfma16x16x32(A1, B1, acc);
-    const int p = b * kPage + 16 * t + n;      // absolute position of this lane's token
+    for (int jj = 0; jj < 4; ++jj) {
+      const int mm = 4 * q + jj;
+      inv[jj] = ldexpf(1.0f, -__shfl(e, mm, 64));
+      const int rr = mm / kHi, hh = mm % kHi;
+      wj[jj] = rr < nr ? a.w[static_cast<int64_t>(r0 + rr) * kHi + hh] : 0.0f;
+    }
+    int rowslot[kRowsPerLane], pos[kRowsPerLane];
 #pragma unroll
     for (int i = 0; i < kRowsPerLane; ++i) {
-      float s = 0.0f;
-#pragma unroll
-      for (int hh = 0; hh < kHi; ++hh) {
-        const int jj = i * kHi + hh;
-        s = fmaf(wj[jj], fmaxf(acc[jj] * inv[jj], 0.0f), s);
-      }
-      if (p <= pos[i]) best[i] = fmaxf(best[i], s);
+      rowslot[i] = q * kRowsPerLane + i;
+      pos[i] = rowslot[i] < nr ? a.row_pos[r0 + rowslot[i]] : -1;
     }
-  }
+
+    float best[kRowsPerLane];
 #pragma unroll
-  for (int i = 0; i < kRowsPerLane; ++i) {
-    float v = best[i];
-    v = xor_max(v, 1);
-    v = xor_max(v, 2);
-    v = xor_max(v, 4);
-    v = xor_max(v, 8);
-    if (n == 0 && rowslot[i] < nr)
-      scores[static_cast<int64_t>(r0 + rowslot[i]) * max_blocks + b] = v;
+    for (int i = 0; i < kRowsPerLane; ++i) best[i] = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const half8_t B0 = e4m3x8_to_f16(key[t].x, key[t].y);
+      const half8_t B1 = e4m3x8_to_f16(key[t].z, key[t].w);
+      float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      acc = mfma16x16x32(A0, B0, acc);
+      acc = mfma16x16x32(A1, B1, acc);
+      const int p = b * kPage + 16 * t + n;      // absolute position of this lane's token
+#pragma unroll
+      for (int i = 0; i < kRowsPerLane; ++i) {
+        float s = 0.0f;
+#pragma unroll
+        for (int hh = 0; hh < kHi; ++hh) {
+          const int jj = i * kHi + hh;
+          s = fmaf(wj[jj], fmaxf(acc[jj] * inv[jj], 0.0f), s);
+        }
+        if (p <= pos[i]) best[i] = fmaxf(best[i], s);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kRowsPerLane; ++i) {
+      float v = best[i];
+      v = xor_max(v, 1);
+      v = xor_max(v, 2);
+      v = xor_max(v, 4);
+      v = xor_max(v, 8);
+      if (n == 0 && rowslot[i] < nr) {
+        float* dst = a.scores + static_cast<int64_t>(r0 + rowslot[i]) * a.max_blocks + b;
+        if constexpr (kFused) __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else *dst = v;
+      }
+    }
+  } else if (fill) {
+    if (lane < nr) a.scores[static_cast<int64_t>(r0 + lane) * a.max_blocks + b] = -INFINITY;
   }
+
+  if constexpr (kFused) {
+    if (a.counters == nullptr) return;                 // append + score only
+    // The last scoring workgroup of this row group selects for its rows.
+    const int nwg = (last_block + kWaves) / kWaves;   // workgroups holding blocks 0..last_block
+    if (static_cast<int>(blockIdx.x) >= nwg) return;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's score stores are done
+    __syncthreads();
+    if (threadIdx.x == 0) s_last = atomicAdd(a.counters + r0, 1) == nwg - 1;
+    __syncthreads();
+    if (!s_last) return;
+    const int32_t* bt = a.block_table + static_cast<int64_t>(seq) * a.max_blocks;
+    for (int i = 0; i < nr; ++i) {
+      const int r = r0 + i;
+      const int nb = min(a.row_pos[r] / kPage + 1, a.max_blocks);
+      block_select_row<true>(a.scores + static_cast<int64_t>(r) * a.max_blocks, nb, a.k, a.n_init,
+                             a.n_local, bt, a.sel + static_cast<int64_t>(r) * a.k,
+                             a.sel_pages ? a.sel_pages + static_cast<int64_t>(r) * a.k : nullptr,
+                             sel_keys, sm);
+    }
+    if (threadIdx.x == 0) a.counters[r0] = 0;
+  }
+}
+
+ScoreArgs make_score_args(const msa_kv_pool_t* pool, const msa_step_t* step, const void* q_idx,
+                          const float* w, float* block_scores) {
+  ScoreArgs a{};
+  a.index_k = static_cast<const uint8_t*>(pool->index_k);
+  a.block_table = step->block_table;
+  a.row_seq = step->row_seq;
+  a.row_pos = step->row_pos;
+  a.q_idx = static_cast<const uint16_t*>(q_idx);
+  a.w = w;
+  a.scores = block_scores;
+  a.num_rows = step->num_rows;
+  a.max_blocks = step->max_blocks_per_seq;
+  a.score_wgs_x = (step->max_blocks_per_seq + kWaves - 1) / kWaves;
+  return a;
+}
+
+template <bool kFused>
+msa_status_t launch_score(const ScoreArgs& a, int fmt, int hi, dim3 grid, size_t lds, hipStream_t s) {
+  const dim3 block(64 * kWaves);
+#define MSA_SCORE_LAUNCH(HI, FMT) score_kernel<HI, FMT, kFused><<<grid, block, lds, s>>>(a)
+  if (fmt == MSA_KV_NVFP4) {
+    if (hi == 1) MSA_SCORE_LAUNCH(1, MSA_KV_NVFP4);
+    else if (hi == 2) MSA_SCORE_LAUNCH(2, MSA_KV_NVFP4);
+    else MSA_SCORE_LAUNCH(4, MSA_KV_NVFP4);
+  } else {
+    if (hi == 1) MSA_SCORE_LAUNCH(1, MSA_KV_FP8_E4M3);
+    else if (hi == 2) MSA_SCORE_LAUNCH(2, MSA_KV_FP8_E4M3);
+    else MSA_SCORE_LAUNCH(4, MSA_KV_FP8_E4M3);
+  }
+#undef MSA_SCORE_LAUNCH
+  return launch_status();
 }
 
 }  // namespace
@@ -156,22 +270,46 @@ extern "C" msa_status_t msa_index_score(const msa_kv_pool_t* pool, const msa_ste
   if (q_idx == nullptr || w == nullptr || block_scores == nullptr || !aligned16(q_idx))
     return MSA_ERR_INVALID_ARG;
   if (step->num_rows > 65535) return MSA_ERR_UNSUPPORTED;
-  dim3 grid((step->max_blocks_per_seq + kWaves - 1) / kWaves, step->num_rows);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  auto ik = static_cast<const uint8_t*>(pool->index_k);
-  auto qi = static_cast<const uint16_t*>(q_idx);
-  switch (n_idx_heads) {
-    case 1:
-      index_score_kernel<1><<<grid, 64 * kWaves, 0, s>>>(ik, step->block_table, step->row_seq,
-          step->row_pos, qi, w, block_scores, step->num_rows, step->max_blocks_per_seq);
-      break;
-    case 2:
-      index_score_kernel<2><<<grid, 64 * kWaves, 0, s>>>(ik, step->block_table, step->row_seq,
-          step->row_pos, qi, w, block_scores, step->num_rows, step->max_blocks_per_seq);
-      break;
-    default:
-      index_score_kernel<4><<<grid, 64 * kWaves, 0, s>>>(ik, step->block_table, step->row_seq,
-          step->row_pos, qi, w, block_scores, step->num_rows, step->max_blocks_per_seq);
+  const ScoreArgs a = make_score_args(pool, step, q_idx, w, block_scores);
+  dim3 grid(a.score_wgs_x, step->num_rows);
+  return launch_score<false>(a, pool->fmt, n_idx_heads, grid, 0, static_cast<hipStream_t>(stream));
+}
+
+extern "C" msa_status_t msa_append_score_select(
+    const msa_kv_pool_t* pool, const msa_step_t* step, int32_t n_new, const int64_t* slot,
+    const void* k_new, const void* v_new, const void* idx_k_new, int32_t n_idx_heads,
+    const void* q_idx, const float* w, int32_t k, int32_t n_init, int32_t n_local,
+    float* block_scores, int32_t* sel, int32_t* sel_pages, int32_t* counters, void* stream) {
+  using namespace msa;
+  msa_status_t st = check_pool(pool);
+  if (st != MSA_OK) return st;
+  if ((st = check_step(step)) != MSA_OK) return st;
+  if (n_idx_heads != 1 && n_idx_heads != 2 && n_idx_heads != 4) return MSA_ERR_UNSUPPORTED;
+  if (k < 1 || k > MSA_MAX_TOPK || n_init < 0 || n_local < 0 || n_init + n_local > k)
+    return MSA_ERR_UNSUPPORTED;
+  if (n_new < 0) return MSA_ERR_INVALID_ARG;
+  if (n_new > 4096) return MSA_ERR_UNSUPPORTED;
+  if (n_new > 0 && slot == nullptr) return MSA_ERR_INVALID_ARG;
+  for (const void* p : {k_new, v_new, idx_k_new})
+    if (p != nullptr && !aligned16(p)) return MSA_ERR_INVALID_ARG;
+  if (step->num_rows == 0) {
+    return n_new > 0 ? msa_kv_append(pool, n_new, slot, k_new, v_new, idx_k_new, stream) : MSA_OK;
   }
-  return launch_status();
+  if (q_idx == nullptr || w == nullptr || block_scores == nullptr || !aligned16(q_idx))
+    return MSA_ERR_INVALID_ARG;
+  if ((sel == nullptr) != (counters == nullptr)) return MSA_ERR_INVALID_ARG;
+  if (step->num_rows >= 65535) return MSA_ERR_UNSUPPORTED;
+  ScoreArgs a = make_score_args(pool, step, q_idx, w, block_scores);
+  a.app = make_append_args(pool, n_new, slot, k_new, v_new, idx_k_new);
+  a.k = k;
+  a.n_init = n_init;
+  a.n_local = n_local;
+  a.sel = sel;
+  a.sel_pages = sel_pages;
+  a.counters = counters;
+  const int64_t app_wgs = (static_cast<int64_t>(n_new) * a.app.groups_per_tok + 255) / 256;
+  dim3 grid(static_cast<unsigned>(std::max<int64_t>(a.score_wgs_x, app_wgs)),
+            step->num_rows + (n_new > 0 ? 1 : 0));
+  const size_t lds = sel ? static_cast<size_t>(step->max_blocks_per_seq) * sizeof(uint32_t) : 0;
+  return launch_score<true>(a, pool->fmt, n_idx_heads, grid, lds, static_cast<hipStream_t>(stream));
 }

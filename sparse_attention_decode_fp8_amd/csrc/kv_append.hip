@@ -2,108 +2,18 @@
 //
 // [GB300] "Step-loop runtime hooks" names the KV update as its own step; [Rubin]
 // Description requires saturating FP8 casts. One thread encodes one group of 16
-// contiguous elements of one token (NVFP4 scale group, or 16 FP8 / index codes),
-// so a token never touches another token's bytes and no atomics are needed.
-#include "msa_device.h"
+// contiguous elements of one token (the encoder is in append_device.h).
+#include "append_device.h"
 #include "msa_host.h"
 
 namespace msa {
 namespace {
 
-#pragma clang fp contract(off)
-
-struct AppendArgs {
-  const int64_t* slot;
-  const uint16_t* k_new;
-  const uint16_t* v_new;
-  const uint16_t* idx_new;
-  uint8_t* k_codes;
-  uint8_t* v_codes;
-  uint8_t* k_scales;   // NVFP4: e4m3 bytes; FP8: fp32 page scales
-  uint8_t* v_scales;
-  uint8_t* index_k;
-  float k_t, v_t;
-  int n_new, hkv;
-  int kv_groups;       // groups of 16 per token for K (and for V): hkv * 8
-  int groups_per_tok;  // K groups + V groups + index groups
-};
-
-__device__ __forceinline__ void load16(const uint16_t* src, float x[16]) {
-  const uint4* p = reinterpret_cast<const uint4*>(src);
-  uint4 a = p[0], b = p[1];
-  uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    x[2 * i] = __uint_as_float(w[i] << 16);
-    x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-  }
-}
-
 template <int kFmt>
 __global__ void __launch_bounds__(256) kv_append_kernel(AppendArgs a) {
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t total = static_cast<int64_t>(a.n_new) * a.groups_per_tok;
-  if (gid >= total) return;
-  const int tok = static_cast<int>(gid / a.groups_per_tok);
-  int grp = static_cast<int>(gid % a.groups_per_tok);
-  const int64_t slot = a.slot[tok];
-  if (slot < 0) return;
-  const int64_t page = slot / kPage;
-  const int off = static_cast<int>(slot % kPage);
-  float x[16];
-
-  if (grp >= 2 * a.kv_groups) {                    // index-K: E4M3, no scale
-    if (a.idx_new == nullptr) return;
-    const int g = grp - 2 * a.kv_groups;             // 0..3
-    load16(a.idx_new + static_cast<int64_t>(tok) * kIndexDim + 16 * g, x);
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      w[i] = f32_to_e4m3_sat(x[4 * i]) | (f32_to_e4m3_sat(x[4 * i + 1]) << 8) |
-             (f32_to_e4m3_sat(x[4 * i + 2]) << 16) | (f32_to_e4m3_sat(x[4 * i + 3]) << 24);
-    *reinterpret_cast<uint4*>(a.index_k + (page * kPage + off) * kIndexDim + 16 * g) =
-        make_uint4(w[0], w[1], w[2], w[3]);
-    return;
-  }
-  const bool is_v = grp >= a.kv_groups;
-  if (is_v) grp -= a.kv_groups;
-  const uint16_t* src = is_v ? a.v_new : a.k_new;
-  if (src == nullptr) return;
-  const int h = grp >> 3, g = grp & 7;
-  load16(src + (static_cast<int64_t>(tok) * a.hkv + h) * kHeadDim + 16 * g, x);
-  const int64_t row = (page * a.hkv + h) * kPage + off;   // token row inside the pool
-
-  if constexpr (kFmt == MSA_KV_NVFP4) {
-    const float t = is_v ? a.v_t : a.k_t;
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
-    const float six_t = 6.0f * t;
-    const uint32_t sc = f32_to_e4m3_sat(amax / six_t);
-    const float dec = e4m3_to_f32(sc);
-    uint32_t w0 = 0, w1 = 0;
-    if (dec != 0.0f) {
-      const float d = dec * t;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        w0 |= f32_to_e2m1_sat(x[i] / d) << (4 * i);
-        w1 |= f32_to_e2m1_sat(x[8 + i] / d) << (4 * i);
-      }
-    }
-    uint8_t* codes = is_v ? a.v_codes : a.k_codes;
-    uint8_t* scales = is_v ? a.v_scales : a.k_scales;
-    *reinterpret_cast<uint2*>(codes + row * (kHeadDim / 2) + 8 * g) = make_uint2(w0, w1);
-    scales[row * (kHeadDim / 16) + g] = static_cast<uint8_t>(sc);
-  } else {
-    const float s = reinterpret_cast<const float*>(is_v ? a.v_scales : a.k_scales)[page];
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      w[i] = f32_to_e4m3_sat(x[4 * i] / s) | (f32_to_e4m3_sat(x[4 * i + 1] / s) << 8) |
-             (f32_to_e4m3_sat(x[4 * i + 2] / s) << 16) | (f32_to_e4m3_sat(x[4 * i + 3] / s) << 24);
-    uint8_t* codes = is_v ? a.v_codes : a.k_codes;
-    *reinterpret_cast<uint4*>(codes + row * kHeadDim + 16 * g) = make_uint4(w[0], w[1], w[2], w[3]);
-  }
+  if (gid >= static_cast<int64_t>(a.n_new) * a.groups_per_tok) return;
+  append_group<kFmt>(a, gid);
 }
 
 }  // namespace
@@ -120,22 +30,7 @@ extern "C" msa_status_t msa_kv_append(const msa_kv_pool_t* pool, int32_t n_new, 
   if (slot == nullptr) return MSA_ERR_INVALID_ARG;
   for (const void* p : {k_new, v_new, idx_k_new})
     if (p != nullptr && !aligned16(p)) return MSA_ERR_INVALID_ARG;
-  AppendArgs a;
-  a.slot = slot;
-  a.k_new = static_cast<const uint16_t*>(k_new);
-  a.v_new = static_cast<const uint16_t*>(v_new);
-  a.idx_new = static_cast<const uint16_t*>(idx_k_new);
-  a.k_codes = static_cast<uint8_t*>(pool->k_codes);
-  a.v_codes = static_cast<uint8_t*>(pool->v_codes);
-  a.k_scales = static_cast<uint8_t*>(pool->k_scales);
-  a.v_scales = static_cast<uint8_t*>(pool->v_scales);
-  a.index_k = static_cast<uint8_t*>(pool->index_k);
-  a.k_t = pool->k_tensor_scale;
-  a.v_t = pool->v_tensor_scale;
-  a.n_new = n_new;
-  a.hkv = pool->num_kv_heads;
-  a.kv_groups = pool->num_kv_heads * (MSA_HEAD_DIM / 16);
-  a.groups_per_tok = 2 * a.kv_groups + MSA_INDEX_DIM / 16;
+  const AppendArgs a = make_append_args(pool, n_new, slot, k_new, v_new, idx_k_new);
   const int64_t total = static_cast<int64_t>(n_new) * a.groups_per_tok;
   const int64_t blocks = (total + 255) / 256;
   if (blocks > 0x7fffffff) return MSA_ERR_UNSUPPORTED;

@@ -94,6 +94,30 @@ __device__ __forceinline__ float xor_add(float v, int mask) {
   return v + __shfl_xor(v, mask, 64);
 }
 
+// Agent-scope relaxed atomic accesses (64-bit halves of a vector). They are performed at
+// the device's coherence point, so workgroups on different XCDs (each with its own L2)
+// see one another's values without cache writeback or invalidation. Used for the split
+// partials that the last-arriving workgroup of a launch merges.
+__device__ __forceinline__ void store_agent(float* p, float4_t v) {
+  uint64_t* q = reinterpret_cast<uint64_t*>(p);
+  __hip_atomic_store(q, __builtin_bit_cast(uint64_t, float2_t{v[0], v[1]}), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 1, __builtin_bit_cast(uint64_t, float2_t{v[2], v[3]}), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_agent(float* p, float2_t v) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2_t load_agent2(const float* p) {
+  return __builtin_bit_cast(float2_t, __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ float4_t load_agent4(const float* p) {
+  const float2_t a = load_agent2(p), b = load_agent2(p + 2);
+  return float4_t{a[0], a[1], b[0], b[1]};
+}
+
 // Order-preserving map of fp32 onto uint32 (larger float -> larger key).
 __device__ __forceinline__ uint32_t float_key(float f) {
   uint32_t u = __float_as_uint(f);

@@ -1,0 +1,256 @@
+// Block-level (256-thread) deterministic top-k block selection for one query row,
+// shared by msa_select_topk and the fused score-and-select kernel.
+//
+// Contract ([Rubin] commit messages: ascending, -1-padded table with init / local
+// forcing; [GB300] "The TP4 decode target", numerics: ties to the smaller block):
+// rows with nb <= k select 0..nb-1; otherwise the n_init first and n_local last blocks
+// are forced and the other k - n_init - n_local slots go to the best remaining blocks by
+// (score desc, index asc). The want-th largest score is found by an MSB-first radix
+// select over order-preserving uint32 keys (LDS histograms: counts do not depend on
+// atomic order), and blocks tied at that score are ranked by a scan in block order.
+#pragma once
+
+#include "msa_device.h"
+
+namespace msa {
+
+constexpr int kSelectThreads = 256;
+
+struct SelectSmem {
+  int hist[256];
+  int tmp[16];
+  int digit, above;
+};
+
+// Exclusive prefix sum over a block of kThreads threads, in thread order.
+template <int kThreads>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* lds_tmp) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) lds_tmp[wave] = x;
+  __syncthreads();
+  int base = 0;
+#pragma unroll
+  for (int i = 0; i < kThreads / 64; ++i)
+    if (i < wave) base += lds_tmp[i];
+  __syncthreads();
+  return base + x - v;
+}
+
+// Select for one row. All kThreads (>= 256, a multiple of 64) threads must call it. `srow` is the row's score array
+// (index = block), `bt` the request's block-table row, `out`/`outp` the row's k-entry
+// outputs (outp may be null), `keys` LDS scratch of at least nb - n_init - n_local
+// entries. kCoherent: read the scores with agent-coherent loads (they were written by
+// other workgroups of the same launch).
+template <bool kCoherent, int kThreads = kSelectThreads>
+__device__ void block_select_row(const float* srow, int nb, int k, int n_init, int n_local,
+                                 const int32_t* bt, int32_t* out, int32_t* outp, uint32_t* keys,
+                                 SelectSmem& sm) {
+  const int tid = threadIdx.x;
+  __syncthreads();                               // LDS may still be in use by a previous row
+  if (nb <= k) {                                 // identity table
+    for (int i = tid; i < k; i += kThreads) {
+      out[i] = i < nb ? i : -1;
+      if (outp) outp[i] = i < nb ? bt[i] : -1;
+    }
+    return;
+  }
+  const int lo = n_init, C = nb - n_init - n_local;   // candidates: blocks lo .. lo + C - 1
+  const int want = k - n_init - n_local;
+  for (int i = tid; i < n_init; i += kThreads) {
+    out[i] = i;
+    if (outp) outp[i] = bt[i];
+  }
+  for (int i = tid; i < n_local; i += kThreads) {
+    out[k - n_local + i] = nb - n_local + i;
+    if (outp) outp[k - n_local + i] = bt[nb - n_local + i];
+  }
+  if (want == 0) return;
+  for (int c = tid; c < C; c += kThreads) {
+    float v;
+    if constexpr (kCoherent)
+      v = __hip_atomic_load(srow + lo + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      v = srow[lo + c];
+    keys[c] = float_key(v);
+  }
+
+  uint32_t prefix = 0, pmask = 0;
+  int remaining = want;                          // rank still to find among matching keys
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    if (tid < 256) sm.hist[tid] = 0;
+    __syncthreads();
+    for (int c = tid; c < C; c += kThreads) {
+      const uint32_t kk = keys[c];
+      if ((kk & pmask) == prefix) atomicAdd(&sm.hist[(kk >> shift) & 255u], 1);
+    }
+    __syncthreads();
+    if (tid < 64) {                              // wave 0 finds the digit holding the rank
+      // lane L owns digits 255-4L .. 252-4L (descending); suffix sums from the top
+      int c4[4], s = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { c4[i] = sm.hist[255 - 4 * tid - i]; s += c4[i]; }
+      int incl = s;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(incl, d, 64);
+        if (tid >= d) incl += y;
+      }
+      int above = incl - s;                      // keys with a larger digit than my first
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (above < remaining && remaining <= above + c4[i]) {
+          sm.digit = 255 - 4 * tid - i;
+          sm.above = above;
+        }
+        above += c4[i];
+      }
+    }
+    __syncthreads();
+    remaining -= sm.above;
+    prefix |= static_cast<uint32_t>(sm.digit) << shift;
+    pmask |= 255u << shift;
+    __syncthreads();
+  }
+  // prefix is the exact key of the want-th largest candidate; `remaining` of the keys
+  // equal to it are taken, those with the smallest block index.
+  const uint32_t T = prefix;
+  const int chunk = (C + kThreads - 1) / kThreads;
+  const int c0 = min(tid * chunk, C), c1 = min(c0 + chunk, C);
+  int nties = 0;
+  for (int c = c0; c < c1; ++c) nties += keys[c] == T;
+  const int tie_before = block_exclusive_scan<kThreads>(nties, sm.tmp);
+  int nsel = 0;
+  {
+    int tb = tie_before;
+    for (int c = c0; c < c1; ++c) {
+      const uint32_t kk = keys[c];
+      nsel += kk > T || (kk == T && tb < remaining);
+      tb += kk == T;
+    }
+  }
+  const int sel_before = block_exclusive_scan<kThreads>(nsel, sm.tmp);
+  int tb = tie_before, at = n_init + sel_before;
+  for (int c = c0; c < c1; ++c) {
+    const uint32_t kk = keys[c];
+    const bool take = kk > T || (kk == T && tb < remaining);
+    tb += kk == T;
+    if (take && at < k - n_local) {
+      if (outp) outp[at] = bt[lo + c];
+      out[at++] = lo + c;
+    }
+  }
+}
+
+}  // namespace msa
+
+namespace msa {
+
+// Wave-level (64-lane) selection for one row, without barriers or LDS atomics. Lane L
+// holds candidates L*kR .. L*kR+kR-1 (block lo + c), so block order is lane-major. The
+// want-th largest key T is built bit by bit from the MSB (count of keys >= candidate via
+// ballot + popcount); keys above T are taken, and of the keys equal to T the ones with
+// the smallest block index (rank by mbcnt prefix counts). The scores and the block-table
+// row are read for every candidate slot inside the row's max_blocks (before the row's
+// length is known) so the two loads overlap. Returns entry e of the selection table and
+// its page in lane e (e < k), -1 padded. `scratch` is 128 ints of LDS private to the
+// calling wave. Every wave that runs it gets the same table.
+template <int kR>
+__device__ __forceinline__ void wave_select_table(const float* srow, const int32_t* bt, int max_blocks,
+                                                  int nb, int k, int n_init, int n_local,
+                                                  int* scratch, int& sel_out, int& page_out) {
+  const int lane = threadIdx.x & 63;
+  const int lo = n_init, C = nb - n_init - n_local, want = k - n_init - n_local;
+  uint32_t key[kR];
+  int32_t pg[kR];
+#pragma unroll
+  for (int i = 0; i < kR; ++i) {
+    const int c = lane * kR + i;
+    const bool in_row = lo + c < max_blocks;
+    const float v = in_row ? srow[lo + c] : 0.0f;
+    pg[i] = in_row ? bt[lo + c] : -1;
+    key[i] = c < C ? float_key(v) : 0u;                    // 0 is below every real key
+  }
+  if (nb <= k) {                                           // identity table
+    sel_out = lane < nb ? lane : -1;
+    page_out = lane < nb ? bt[lane] : -1;
+    return;
+  }
+  int out = -1, opg = -1;
+  if (lane < n_init) { out = lane; opg = bt[lane]; }
+  if (lane >= k - n_local && lane < k) { out = nb - k + lane; opg = bt[nb - k + lane]; }
+  if (want > 0) {
+    uint32_t T = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = T | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int i = 0; i < kR; ++i) cnt += __popcll(__ballot(key[i] >= cand));
+      if (cnt >= want) T = cand;
+    }
+    int gt = 0;
+#pragma unroll
+    for (int i = 0; i < kR; ++i) gt += __popcll(__ballot(key[i] > T));
+    const int need = want - gt;                            // keys equal to T to take
+    int tie_before = 0;
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+      const uint64_t m = __ballot(key[i] == T);
+      tie_before += __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                              __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+    }
+    bool take[kR];
+    int tb = tie_before;
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+      take[i] = key[i] > T || (key[i] == T && tb < need);
+      tb += key[i] == T;
+    }
+    int before = 0;
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+      const uint64_t m = __ballot(take[i]);
+      before += __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                          __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+    }
+    int at = before;
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+      if (take[i]) {
+        scratch[at] = lo + lane * kR + i;
+        scratch[64 + at] = pg[i];
+        ++at;
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (lane >= n_init && lane < n_init + want) {
+      out = scratch[lane - n_init];
+      opg = scratch[64 + lane - n_init];
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+  sel_out = out;
+  page_out = opg;
+}
+
+// Largest number of candidate blocks the wave-level selection handles (64 lanes x 32).
+constexpr int kWaveSelectMax = 64 * 32;
+
+// Dispatch on the largest candidate count the row table allows (known before the row's
+// length is): kR = 4, 8, 16 or 32 keys per lane.
+__device__ __forceinline__ void wave_select(const float* srow, const int32_t* bt, int max_blocks,
+                                            int nb, int k, int n_init, int n_local, int* scratch,
+                                            int& sel, int& page) {
+  const int C = max_blocks - n_init - n_local;
+  if (C <= 256) wave_select_table<4>(srow, bt, max_blocks, nb, k, n_init, n_local, scratch, sel, page);
+  else if (C <= 512) wave_select_table<8>(srow, bt, max_blocks, nb, k, n_init, n_local, scratch, sel, page);
+  else if (C <= 1024) wave_select_table<16>(srow, bt, max_blocks, nb, k, n_init, n_local, scratch, sel, page);
+  else wave_select_table<32>(srow, bt, max_blocks, nb, k, n_init, n_local, scratch, sel, page);
+}
+
+}  // namespace msa

@@ -1,14 +1,19 @@
-// msa_sparse_decode: GQA flash-decode over the selected P128 pages, split-KV partials.
+// Sparse GQA flash-decode over the selected P128 pages with split-KV partials:
+//   msa_sparse_decode          selection table in, partials out
+//   msa_sparse_decode_combine  selection table in, partials + merged bf16 output out
+//   msa_select_decode_combine  block scores in: each workgroup selects its row's blocks
+//                              itself, then decodes and merges
 //
 // Prior art on the pages: [Rubin] commit messages describe a block-sparse verify
 // decode with one unit of work per (top-k split, KV head, query row) and NVFP4
 // dequantised in registers, merging splits across CTAs; [Rubin] "Items and numerics"
 // (LC_ONEDIV) fixes the merge to a single divide per output in a fixed order.
 //
-// MI355X design. One workgroup of W waves per (split, KV head, query row); each wave
-// takes one selected page at a time (128 tokens, 4 chunks of 32) and keeps its own
-// online softmax, and the W waves merge in LDS at the end. All 16 query heads of the
-// KV head ride in the MFMA N dimension, so both contractions keep "head" on lane % 16:
+// MI355X design. One workgroup per (split, KV head, query row). The split's pages are
+// cut into 32-token chunks and each wave takes its chunks (one chunk per wave at the
+// default launch), so a page is consumed by several SIMDs at once; the waves merge
+// their softmax states in LDS. All 16 query heads of the KV head ride in the MFMA N
+// dimension, so both contractions keep "head" on lane % 16:
 //   S^T[token][head] = K[token][d] . Q^T[d][head]      A = K  (dequantised in registers)
 //   O^T[d][head]    += V^T[d][token] . P^T[token][head] A = V^T (LDS, transposing read)
 // and the softmax state (max, sum, rescale) is per lane, with no cross-lane transpose.
@@ -16,13 +21,28 @@
 // E4M3 fits fp16), Q is pre-scaled by a power of two per head so its fp16 conversion
 // is exact, accumulation is fp32. The NVFP4 tensor scales and FP8 page scales are
 // applied outside the MFMAs (folded into the logit scale and the output rescale).
+// Every load a wave needs (selection entry, page id, K/V codes and scales, Q) is
+// issued before the first MFMA, so the kernel pays the memory latency once.
+//
+// The combining variants have the last workgroup of each (row, KV head) to finish
+// merge all splits (a device-scope counter, reset by that workgroup), so the step needs
+// no separate combine launch. The partials cross workgroups (and XCDs, whose L2s are
+// not coherent with each other) as agent-scope atomic stores and loads, which need no
+// cache-flushing fence; on this part such fences cost more than the whole merge. The
+// selecting variant runs the top-k selection of its row in every workgroup (the scores
+// are 4 bytes per block), which costs less than a launch plus a cross-workgroup handoff.
+#include <algorithm>
+
 #include "msa_device.h"
 #include "msa_host.h"
+#include "select_device.h"
 
 namespace msa {
 namespace {
 
 constexpr int kVRowHalves = 144;   // 128 fp16 + 16 pad: 288-byte rows keep 4 rows on disjoint banks
+constexpr int kVBufBytes = 32 * kVRowHalves * 2;   // one wave's 32-token V chunk
+constexpr int kMaxCombineSplits = 16;
 
 struct DecodeArgs {
   const uint8_t* k_codes;
@@ -35,100 +55,199 @@ struct DecodeArgs {
   const int32_t* row_seq;
   const int32_t* row_pos;
   int max_blocks;
+  int num_rows;
   const uint16_t* q;
-  const int32_t* sel;
+  const int32_t* sel;         // selection table (table variants)
+  const int32_t* sel_pages;   // may be null: translate through the block table
+  int32_t* sel_out;           // selecting variant: optional copy of the selection
+  int32_t* sel_pages_out;
+  const float* scores;        // selecting variant
+  int n_init, n_local;
   int k;
   float softmax_scale;
   int num_splits;
   float* part_o;
   float* part_ml;
+  int32_t* counters;          // combining variants: [rows][hkv]
+  uint16_t* out;              // combining variants: bf16 [rows][hq][128]
 };
 
 __device__ __forceinline__ half2_t bcast_lo(half2_t v) { return half2_t{v[0], v[0]}; }
 __device__ __forceinline__ half2_t bcast_hi(half2_t v) { return half2_t{v[1], v[1]}; }
 
+// One 32-token chunk of one page, as held by a lane: tile u (tokens 16u .. 16u+15 of
+// the chunk), token 16u + (lane % 16), dims 32q .. 32q+31.
 template <int kFmt>
-struct PageRegs;
-
+struct ChunkRegs;
 template <>
-struct PageRegs<MSA_KV_NVFP4> {
-  uint4 k[8], v[8];          // [chunk * 2 + tile]: 32 E2M1 codes of one token (dims 32q..32q+31)
-  uint32_t ks[8], vs[8];     // the two E4M3 scales of those dims
+struct ChunkRegs<MSA_KV_NVFP4> {
+  uint4 k[2], v[2];        // 32 E2M1 codes
+  uint32_t ks[2], vs[2];   // the two E4M3 scales of those 32 dims
 };
 template <>
-struct PageRegs<MSA_KV_FP8_E4M3> {
-  uint4 k[16], v[16];        // [(chunk * 2 + tile) * 2 + half]: 32 E4M3 codes
+struct ChunkRegs<MSA_KV_FP8_E4M3> {
+  uint4 k[4], v[4];        // [tile * 2 + half]: 32 E4M3 codes
 };
 
 template <int kFmt>
-__device__ __forceinline__ void load_page(PageRegs<kFmt>& R, const DecodeArgs& a, int64_t page, int g,
-                                          int n, int q, int nchunks) {
-  const int64_t tok0 = (page * a.hkv + g) * kPage + n;      // token row of (page, head, n)
+__device__ __forceinline__ void load_chunk(ChunkRegs<kFmt>& R, const DecodeArgs& a, int64_t page,
+                                           int g, int c, int n, int q) {
+  const int64_t tok0 = (page * a.hkv + g) * kPage + 32 * c + n;
   if constexpr (kFmt == MSA_KV_NVFP4) {
     const uint8_t* kc = a.k_codes + tok0 * (kHeadDim / 2) + 16 * q;
     const uint8_t* vc = a.v_codes + tok0 * (kHeadDim / 2) + 16 * q;
     const uint8_t* kss = a.k_scales + tok0 * (kHeadDim / 16) + 2 * q;
     const uint8_t* vss = a.v_scales + tok0 * (kHeadDim / 16) + 2 * q;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (i / 2 < nchunks) {
-        R.k[i] = *reinterpret_cast<const uint4*>(kc + i * 16 * (kHeadDim / 2));
-        R.v[i] = *reinterpret_cast<const uint4*>(vc + i * 16 * (kHeadDim / 2));
-        R.ks[i] = *reinterpret_cast<const uint16_t*>(kss + i * 16 * (kHeadDim / 16));
-        R.vs[i] = *reinterpret_cast<const uint16_t*>(vss + i * 16 * (kHeadDim / 16));
-      }
+    for (int u = 0; u < 2; ++u) {
+      R.k[u] = *reinterpret_cast<const uint4*>(kc + u * 16 * (kHeadDim / 2));
+      R.v[u] = *reinterpret_cast<const uint4*>(vc + u * 16 * (kHeadDim / 2));
+      R.ks[u] = *reinterpret_cast<const uint16_t*>(kss + u * 16 * (kHeadDim / 16));
+      R.vs[u] = *reinterpret_cast<const uint16_t*>(vss + u * 16 * (kHeadDim / 16));
     }
   } else {
     const uint8_t* kc = a.k_codes + tok0 * kHeadDim + 32 * q;
     const uint8_t* vc = a.v_codes + tok0 * kHeadDim + 32 * q;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (i / 2 < nchunks) {
-        R.k[2 * i] = *reinterpret_cast<const uint4*>(kc + i * 16 * kHeadDim);
-        R.k[2 * i + 1] = *reinterpret_cast<const uint4*>(kc + i * 16 * kHeadDim + 16);
-        R.v[2 * i] = *reinterpret_cast<const uint4*>(vc + i * 16 * kHeadDim);
-        R.v[2 * i + 1] = *reinterpret_cast<const uint4*>(vc + i * 16 * kHeadDim + 16);
+    for (int u = 0; u < 2; ++u) {
+      R.k[2 * u] = *reinterpret_cast<const uint4*>(kc + u * 16 * kHeadDim);
+      R.k[2 * u + 1] = *reinterpret_cast<const uint4*>(kc + u * 16 * kHeadDim + 16);
+      R.v[2 * u] = *reinterpret_cast<const uint4*>(vc + u * 16 * kHeadDim);
+      R.v[2 * u + 1] = *reinterpret_cast<const uint4*>(vc + u * 16 * kHeadDim + 16);
+    }
+  }
+}
+
+// Dims 32q + 8j .. +7 of tile u as an fp16 MFMA operand.
+template <int kFmt>
+__device__ __forceinline__ half8_t dequant8(const uint4* codes, const uint32_t* scales, int u, int j) {
+  if constexpr (kFmt == MSA_KV_NVFP4) {
+    const uint4 c = codes[u];
+    const uint32_t w = j == 0 ? c.x : j == 1 ? c.y : j == 2 ? c.z : c.w;
+    const half2_t sc = e4m3x2_to_f16(scales[u]);
+    return e2m1x8_to_f16(w, j < 2 ? bcast_lo(sc) : bcast_hi(sc));
+  } else {
+    const uint4 c = codes[2 * u + (j >> 1)];
+    return (j & 1) ? e4m3x8_to_f16(c.z, c.w) : e4m3x8_to_f16(c.x, c.y);
+  }
+}
+
+template <int kFmt, int kItems>
+struct Round {
+  ChunkRegs<kFmt> R[kItems];
+  int nvis[kItems];                // visible tokens of each chunk (0: no chunk)
+  float kps[kItems], vps[kItems];  // FP8 page scales (1 for NVFP4)
+};
+
+// Issue every load of one round: chunk `it = round + wave + j * kW` of this split is
+// entry lo + it / 4, 32-token chunk it % 4. `lookup(e, b, page)` gives the logical
+// block and physical page of selection entry e (b < 0: empty entry).
+template <int kFmt, int kW, int kItems, class Lookup>
+__device__ __forceinline__ void load_round(Round<kFmt, kItems>& rd, const DecodeArgs& a,
+                                           const Lookup& lookup, int round, int wave, int g,
+                                           int pos, int lo, int n_items, int n, int q) {
+  int64_t pages[kItems];
+#pragma unroll
+  for (int j = 0; j < kItems; ++j) {
+    const int it = round + wave + j * kW;
+    rd.nvis[j] = 0;
+    pages[j] = 0;
+    if (it < n_items) {
+      const int e = lo + (it >> 2), c = it & 3;
+      int b;
+      int64_t page;
+      lookup(e, b, page);
+      const int nv = min(pos - b * kPage + 1, kPage) - 32 * c;   // visible tokens in the chunk
+      if (b >= 0 && nv > 0) {
+        rd.nvis[j] = min(nv, 32);
+        pages[j] = page;
+        load_chunk<kFmt>(rd.R[j], a, page, g, c, n, q);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kItems; ++j) {
+    rd.kps[j] = rd.vps[j] = 1.0f;
+    if constexpr (kFmt == MSA_KV_FP8_E4M3) {
+      if (rd.nvis[j] > 0) {
+        rd.kps[j] = reinterpret_cast<const float*>(a.k_scales)[pages[j]];
+        rd.vps[j] = reinterpret_cast<const float*>(a.v_scales)[pages[j]];
       }
     }
   }
 }
 
-// Dims 32q + 8j .. +7 of tile `ti` (= chunk * 2 + tile) as an fp16 MFMA operand.
-template <int kFmt>
-__device__ __forceinline__ half8_t dequant8(const uint4* codes, const uint32_t* scales, int ti, int j) {
-  if constexpr (kFmt == MSA_KV_NVFP4) {
-    const uint4 c = codes[ti];
-    const uint32_t w = j == 0 ? c.x : j == 1 ? c.y : j == 2 ? c.z : c.w;
-    const half2_t sc = e4m3x2_to_f16(scales[ti]);
-    return e2m1x8_to_f16(w, j < 2 ? bcast_lo(sc) : bcast_hi(sc));
-  } else {
-    const uint4 c = codes[2 * ti + (j >> 1)];
-    return (j & 1) ? e4m3x8_to_f16(c.z, c.w) : e4m3x8_to_f16(c.x, c.y);
-  }
-}
-
-template <int kFmt, int kW>
+template <int kFmt, int kW, int kItems, bool kCombine, bool kSelect>
 __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) half_t vbuf[kW][32 * kVRowHalves];
+  // Dynamic LDS: the row's selection keys (selecting variant, before any V is staged),
+  // then the per-wave V staging buffers and, at the end, the per-wave O tiles.
+  extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
   __shared__ float mbuf[kW][16], lbuf[kW][16];
-  const int s = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
+  __shared__ int s_last;
+  __shared__ int32_t lsel[kSelect ? MSA_MAX_TOPK : 1];
+  __shared__ int wsel[kSelect ? kW : 1][128];
+  __shared__ SelectSmem sm;
+  const int pair = blockIdx.y, s = blockIdx.x;   // (row, KV head) pair, split
+  if (pair >= a.num_rows * a.hkv) return;
+  const int r = pair / a.hkv, g = pair % a.hkv;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
   const int hq = a.hkv * kHeadsPerKv;
-  const int seq = a.row_seq[r], pos = a.row_pos[r];
+  const int pos = a.row_pos[r];
   const int lo = (s * a.k) / a.num_splits, hi = ((s + 1) * a.k) / a.num_splits;
+  const int n_items = (hi - lo) * 4;   // (entry, 32-token chunk) pairs of this split
 
   // Q^T operand: lane (n, q) holds head 16g + n, dims 32q + 8j .. +7 for k-step j.
+  const uint4* qp = reinterpret_cast<const uint4*>(
+      a.q + (static_cast<int64_t>(r) * hq + kHeadsPerKv * g + n) * kHeadDim + 32 * q);
+  uint4 qraw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) qraw[i] = qp[i];
+
+  // Selection table in a register: lane e < k holds entry e (block) and its page.
+  int selv = -1, pagev = -1;
+  if constexpr (kSelect) {
+    const int nb = min(pos / kPage + 1, a.max_blocks);
+    const int32_t* bt = a.block_table + static_cast<int64_t>(a.row_seq[r]) * a.max_blocks;
+    const float* srow = a.scores + static_cast<int64_t>(r) * a.max_blocks;
+    if (a.max_blocks - a.n_init - a.n_local <= kWaveSelectMax) {
+      // every wave selects on its own: no barrier, identical tables
+      wave_select(srow, bt, a.max_blocks, nb, a.k, a.n_init, a.n_local, &wsel[wave][0], selv, pagev);
+    } else {
+      block_select_row<false, 64 * kW>(srow, nb, a.k, a.n_init, a.n_local, bt, lsel, nullptr,
+                                       reinterpret_cast<uint32_t*>(dyn_lds), sm);
+      __syncthreads();
+      selv = lane < a.k ? lsel[lane] : -1;
+      pagev = selv >= 0 ? bt[selv] : -1;
+    }
+    if (lane >= a.k) selv = pagev = -1;
+    if (s == 0 && g == 0 && wave == 0 && a.sel_out != nullptr && lane < a.k) {
+      a.sel_out[static_cast<int64_t>(r) * a.k + lane] = selv;
+      if (a.sel_pages_out) a.sel_pages_out[static_cast<int64_t>(r) * a.k + lane] = pagev;
+    }
+  }
+  auto lookup = [&](int e, int& b, int64_t& page) {
+    if constexpr (kSelect) {
+      b = __shfl(selv, e, 64);
+      page = __shfl(pagev, e, 64);
+    } else {
+      b = a.sel[static_cast<int64_t>(r) * a.k + e];
+      page = b < 0 ? 0
+          : a.sel_pages ? a.sel_pages[static_cast<int64_t>(r) * a.k + e]
+                        : a.block_table[static_cast<int64_t>(a.row_seq[r]) * a.max_blocks + b];
+    }
+  };
+
+  Round<kFmt, kItems> rd;
+  load_round<kFmt, kW, kItems>(rd, a, lookup, 0, wave, g, pos, lo, n_items, n, q);
+
   half8_t Qop[4];
   float cscale;
   {
-    const uint4* qp = reinterpret_cast<const uint4*>(
-        a.q + (static_cast<int64_t>(r) * hq + kHeadsPerKv * g + n) * kHeadDim + 32 * q);
     float qf[32];
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint4 u = qp[i];
-      const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
+      const uint32_t wv[4] = {qraw[i].x, qraw[i].y, qraw[i].z, qraw[i].w};
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         qf[8 * i + 2 * t] = __uint_as_float(wv[t] << 16);
@@ -150,45 +269,35 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
   float m_run = -INFINITY, l_run = 0.0f, v_cur = 0.0f;   // v_cur: FP8 page scale O is kept in
   float4_t O[8];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) O[c] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  half_t* vb = vbuf[wave];
+  for (int d = 0; d < 8; ++d) O[d] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  half_t* vb = reinterpret_cast<half_t*>(dyn_lds + wave * kVBufBytes);
+  typedef __attribute__((address_space(3))) short4_t lds_s4;
 
-  for (int e = lo + wave; e < hi; e += kW) {
-    const int b = a.sel[static_cast<int64_t>(r) * a.k + e];
-    if (b < 0) continue;
-    int n_vis = pos - b * kPage + 1;
-    if (n_vis <= 0) continue;
-    n_vis = min(n_vis, kPage);
-    const int nchunks = (n_vis + 31) >> 5;
-    const int64_t page = a.block_table[static_cast<int64_t>(seq) * a.max_blocks + b];
-    PageRegs<kFmt> R;
-    load_page<kFmt>(R, a, page, g, n, q, nchunks);
-    float cs = cscale, ratio = 1.0f;
-    if constexpr (kFmt == MSA_KV_FP8_E4M3) {
-      cs *= reinterpret_cast<const float*>(a.k_scales)[page];
-      const float vp = reinterpret_cast<const float*>(a.v_scales)[page];
-      ratio = v_cur > 0.0f ? v_cur / vp : 1.0f;     // keep O in units of this page's scale
-      v_cur = vp;
-    }
-    const uint32_t* ksc = nullptr;
-    const uint32_t* vsc = nullptr;
-    if constexpr (kFmt == MSA_KV_NVFP4) { ksc = R.ks; vsc = R.vs; }
-
+  for (int round = 0; round < n_items; round += kW * kItems) {
+    if (round > 0)
+      load_round<kFmt, kW, kItems>(rd, a, lookup, round, wave, g, pos, lo, n_items, n, q);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      if (c >= nchunks) break;
+    for (int j = 0; j < kItems; ++j) {
+      if (rd.nvis[j] <= 0) continue;
+      const uint32_t* ksc = nullptr;
+      const uint32_t* vsc = nullptr;
+      if constexpr (kFmt == MSA_KV_NVFP4) { ksc = rd.R[j].ks; vsc = rd.R[j].vs; }
+      const float cs = cscale * rd.kps[j];
+      float ratio = 1.0f;
+      if constexpr (kFmt == MSA_KV_FP8_E4M3) {
+        ratio = v_cur > 0.0f ? v_cur / rd.vps[j] : 1.0f;   // keep O in units of this page's scale
+        v_cur = rd.vps[j];
+      }
       // ---- scores of 32 tokens for 16 heads
       float x[2][4];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc = mfma16x16x32(dequant8<kFmt>(R.k, ksc, 2 * c + u, j), Qop[j], acc);
+        for (int kk = 0; kk < 4; ++kk)
+          acc = mfma16x16x32(dequant8<kFmt>(rd.R[j].k, ksc, u, kk), Qop[kk], acc);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tok = 32 * c + 16 * u + 4 * q + i;
-          x[u][i] = tok < n_vis ? acc[i] * cs : -INFINITY;
-        }
+        for (int i = 0; i < 4; ++i) x[u][i] = (16 * u + 4 * q + i) < rd.nvis[j] ? acc[i] * cs : -INFINITY;
       }
       // ---- online softmax (per lane: one head)
       float mx = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
@@ -206,109 +315,169 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
           psum += p;
           Pt[4 * u + i] = static_cast<half_t>(p);
         }
+      if (m_run != -INFINITY) {                         // O is still zero on a wave's first chunk
+        const float ao = alpha * ratio;
+#pragma unroll
+        for (int d = 0; d < 8; ++d) O[d] *= ao;
+      }
       l_run = l_run * alpha + psum;
       m_run = m_new;
-      const float ao = c == 0 ? alpha * ratio : alpha;
-#pragma unroll
-      for (int d = 0; d < 8; ++d) O[d] *= ao;
-      // ---- V chunk to LDS (natural [token][d] layout, fp16)
+      // ---- V chunk to LDS (natural [token][d] layout, fp16), then O^T += V^T . P^T
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          *reinterpret_cast<half8_t*>(vb + (16 * u + n) * kVRowHalves + 32 * q + 8 * j) =
-              dequant8<kFmt>(R.v, vsc, 2 * c + u, j);
+        for (int kk = 0; kk < 4; ++kk)
+          *reinterpret_cast<half8_t*>(vb + (16 * u + n) * kVRowHalves + 32 * q + 8 * kk) =
+              dequant8<kFmt>(rd.R[j].v, vsc, u, kk);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      // ---- O^T += V^T . P^T over the 32 tokens, 8 tiles of 16 dims
-      typedef __attribute__((address_space(3))) short4_t lds_s4;
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
         const half_t* p0 = vb + (4 * q + (n >> 2)) * kVRowHalves + 16 * d + 4 * (n & 3);
         const half_t* p1 = p0 + 16 * kVRowHalves;
-        const short4_t r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p0));
-        const short4_t r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p1));
-        half8_t Vt;
-        const half4_t h0 = __builtin_bit_cast(half4_t, r0), h1 = __builtin_bit_cast(half4_t, r1);
-        Vt[0] = h0[0]; Vt[1] = h0[1]; Vt[2] = h0[2]; Vt[3] = h0[3];
-        Vt[4] = h1[0]; Vt[5] = h1[1]; Vt[6] = h1[2]; Vt[7] = h1[3];
+        const half4_t h0 = __builtin_bit_cast(half4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p0)));
+        const half4_t h1 = __builtin_bit_cast(half4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p1)));
+        const half8_t Vt = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
         O[d] = mfma16x16x32(Vt, Pt, O[d]);
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
   }
 
-  float l_tot = xor_add(xor_add(l_run, 16), 32);
+  // ---- merge the waves of the workgroup, write this split's partial
+  const float l_tot = xor_add(xor_add(l_run, 16), 32);
   float oscale;
   if constexpr (kFmt == MSA_KV_NVFP4) oscale = a.v_t; else oscale = v_cur;
-  const int64_t head = static_cast<int64_t>(r) * hq + kHeadsPerKv * g;
-  if constexpr (kW == 1) {
-    float* po = a.part_o + ((head + n) * a.num_splits + s) * kHeadDim + 4 * q;
+  const int64_t head0 = static_cast<int64_t>(r) * hq + kHeadsPerKv * g;
+  __syncthreads();                                     // every wave is done with its V buffer
+  {
+    float* ob = reinterpret_cast<float*>(dyn_lds + wave * kVBufBytes);   // [16 heads][128 d] fp32
 #pragma unroll
-    for (int d = 0; d < 8; ++d) *reinterpret_cast<float4_t*>(po + 16 * d) = O[d] * oscale;
-    if (q == 0) {
-      float* pm = a.part_ml + ((head + n) * a.num_splits + s) * 2;
-      pm[0] = m_run;
-      pm[1] = l_tot;
-    }
-  } else {
-    __syncthreads();                               // every wave is done with vbuf
-    float* ob = reinterpret_cast<float*>(vbuf[wave]);   // [16 heads][128 d] fp32 = 8 KiB
-#pragma unroll
-    for (int d = 0; d < 8; ++d) *reinterpret_cast<float4_t*>(ob + n * kHeadDim + 16 * d + 4 * q) = O[d] * oscale;
+    for (int d = 0; d < 8; ++d)
+      *reinterpret_cast<float4_t*>(ob + n * kHeadDim + 16 * d + 4 * q) = O[d] * oscale;
     if (q == 0) { mbuf[wave][n] = m_run; lbuf[wave][n] = l_tot; }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < 16 * (kHeadDim / 4); idx += 64 * kW) {
-      const int h = idx / (kHeadDim / 4), d4 = idx % (kHeadDim / 4);
-      float M = -INFINITY;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < 16 * (kHeadDim / 4); idx += 64 * kW) {
+    const int h = idx / (kHeadDim / 4), d4 = idx % (kHeadDim / 4);
+    float M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < kW; ++w) M = fmaxf(M, mbuf[w][h]);
-      float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-      float l = 0.0f;
-      if (M != -INFINITY) {
+    for (int w = 0; w < kW; ++w) M = fmaxf(M, mbuf[w][h]);
+    float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    float l = 0.0f;
+    if (M != -INFINITY) {
 #pragma unroll
-        for (int w = 0; w < kW; ++w) {
-          const float wt = exp2f(mbuf[w][h] - M);
-          acc += wt * *reinterpret_cast<const float4_t*>(reinterpret_cast<const float*>(vbuf[w]) +
-                                                         h * kHeadDim + 4 * d4);
-          l += wt * lbuf[w][h];
-        }
+      for (int w = 0; w < kW; ++w) {
+        const float wt = exp2f(mbuf[w][h] - M);
+        acc += wt * *reinterpret_cast<const float4_t*>(
+                        reinterpret_cast<const float*>(dyn_lds + w * kVBufBytes) + h * kHeadDim + 4 * d4);
+        l += wt * lbuf[w][h];
       }
-      float* po = a.part_o + ((head + h) * a.num_splits + s) * kHeadDim + 4 * d4;
+    }
+    float* po = a.part_o + ((head0 + h) * a.num_splits + s) * kHeadDim + 4 * d4;
+    float* pm = a.part_ml + ((head0 + h) * a.num_splits + s) * 2;
+    if constexpr (kCombine) {
+      store_agent(po, acc);
+      if (d4 == 0) store_agent(pm, float2_t{M, l});
+    } else {
       *reinterpret_cast<float4_t*>(po) = acc;
       if (d4 == 0) {
-        float* pm = a.part_ml + ((head + h) * a.num_splits + s) * 2;
         pm[0] = M;
         pm[1] = l;
       }
     }
   }
+  if constexpr (kCombine) {
+    // ---- the last split of this (row, KV head) to finish merges all splits. The partials
+    // were written with agent-scope atomic stores; waiting for them before the counter
+    // update orders them before it, and the merging workgroup reads them with agent-scope
+    // atomic loads issued after it saw the count, wherever the workgroups ran.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int old = atomicAdd(a.counters + static_cast<int64_t>(r) * a.hkv + g, 1);
+      s_last = old == a.num_splits - 1;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    for (int idx = threadIdx.x; idx < 16 * (kHeadDim / 4); idx += 64 * kW) {
+      const int h = idx / (kHeadDim / 4), d4 = idx % (kHeadDim / 4);
+      const float* ml = a.part_ml + (head0 + h) * a.num_splits * 2;
+      const float* po = a.part_o + (head0 + h) * a.num_splits * kHeadDim + 4 * d4;
+      float2_t mls[kMaxCombineSplits];
+      float4_t ot[kMaxCombineSplits];
+#pragma unroll
+      for (int t = 0; t < kMaxCombineSplits; ++t) {    // every load first, one wait
+        if (t < a.num_splits) {
+          mls[t] = load_agent2(ml + 2 * t);
+          ot[t] = load_agent4(po + static_cast<int64_t>(t) * kHeadDim);
+        }
+      }
+      float M = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < kMaxCombineSplits; ++t)
+        if (t < a.num_splits) M = fmaxf(M, mls[t][0]);
+      float4_t num = {0.0f, 0.0f, 0.0f, 0.0f};
+      float den = 0.0f;
+#pragma unroll
+      for (int t = 0; t < kMaxCombineSplits; ++t) {
+        if (t < a.num_splits) {
+          const float m = mls[t][0];
+          const float wgt = m == -INFINITY ? 0.0f : exp2f(m - M);   // M > -inf whenever m is
+          den += wgt * mls[t][1];
+          num += wgt * ot[t];
+        }
+      }
+      uint16_t o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = den > 0.0f ? f32_to_bf16_rne(num[i] / den) : 0;
+      *reinterpret_cast<uint2*>(a.out + (head0 + h) * kHeadDim + 4 * d4) =
+          make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16));
+    }
+    if (threadIdx.x == 0)   // ready for the next launch
+      __hip_atomic_store(a.counters + static_cast<int64_t>(r) * a.hkv + g, 0, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
-template <int kFmt, int kW>
+template <int kFmt, int kW, int kItems, bool kCombine, bool kSelect>
 void launch(const DecodeArgs& a, dim3 grid, hipStream_t s) {
-  sparse_decode_kernel<kFmt, kW><<<grid, dim3(64 * kW), 0, s>>>(a);
+  size_t lds = static_cast<size_t>(kW) * kVBufBytes;
+  if (kSelect) lds = std::max(lds, static_cast<size_t>(a.max_blocks) * sizeof(uint32_t));
+  sparse_decode_kernel<kFmt, kW, kItems, kCombine, kSelect><<<grid, dim3(64 * kW), lds, s>>>(a);
 }
 
-}  // namespace
-}  // namespace msa
+// Waves per workgroup and chunks per wave (per round) for a split of `per_split` pages:
+// one chunk per wave up to 16 waves; beyond that 8 waves of 4 chunks per round. The
+// selecting variant needs at least 4 waves (its selection uses 256 threads or more).
+template <int kFmt, bool kCombine, bool kSelect>
+msa_status_t dispatch(const DecodeArgs& a, dim3 grid, hipStream_t s) {
+  const int per_split = (a.k + a.num_splits - 1) / a.num_splits;
+  const int chunks = 4 * per_split;
+  if (chunks <= 4) launch<kFmt, 4, 1, kCombine, kSelect>(a, grid, s);
+  else if (chunks <= 8) launch<kFmt, 8, 1, kCombine, kSelect>(a, grid, s);
+  else if (chunks <= 16) launch<kFmt, 16, 1, kCombine, kSelect>(a, grid, s);
+  else launch<kFmt, 8, 4, kCombine, kSelect>(a, grid, s);   // rounds of 32 chunks
+  return launch_status();
+}
 
-extern "C" msa_status_t msa_sparse_decode(const msa_kv_pool_t* pool, const msa_step_t* step,
-                                          int32_t num_q_heads, const void* q, const int32_t* sel,
-                                          int32_t k, float softmax_scale, int32_t num_splits,
-                                          float* part_o, float* part_ml, void* stream) {
-  using namespace msa;
+msa_status_t decode_entry(const msa_kv_pool_t* pool, const msa_step_t* step, int32_t num_q_heads,
+                          const void* q, DecodeArgs a, hipStream_t s, bool combine, bool select) {
   msa_status_t st = check_pool(pool);
   if (st != MSA_OK) return st;
   if ((st = check_step(step)) != MSA_OK) return st;
   if (num_q_heads != MSA_HEADS_PER_KV * pool->num_kv_heads) return MSA_ERR_UNSUPPORTED;
-  if (k < 1 || k > MSA_MAX_TOPK || num_splits < 1 || num_splits > k) return MSA_ERR_UNSUPPORTED;
-  if (!(softmax_scale > 0.0f)) return MSA_ERR_INVALID_ARG;
+  if (a.k < 1 || a.k > MSA_MAX_TOPK || a.num_splits < 1 || a.num_splits > a.k) return MSA_ERR_UNSUPPORTED;
+  if (combine && a.num_splits > kMaxCombineSplits) return MSA_ERR_UNSUPPORTED;
+  if (select && (a.n_init < 0 || a.n_local < 0 || a.n_init + a.n_local > a.k)) return MSA_ERR_UNSUPPORTED;
+  if (!(a.softmax_scale > 0.0f)) return MSA_ERR_INVALID_ARG;
   if (step->num_rows == 0) return MSA_OK;
-  if (q == nullptr || sel == nullptr || part_o == nullptr || part_ml == nullptr) return MSA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(part_o) || (reinterpret_cast<uintptr_t>(part_ml) & 7u))
+  if (q == nullptr || a.part_o == nullptr || a.part_ml == nullptr) return MSA_ERR_INVALID_ARG;
+  if (select ? a.scores == nullptr : a.sel == nullptr) return MSA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(a.part_o) || (reinterpret_cast<uintptr_t>(a.part_ml) & 7u))
     return MSA_ERR_INVALID_ARG;
-  if (step->num_rows > 65535) return MSA_ERR_UNSUPPORTED;
-  DecodeArgs a;
+  if (combine && (a.counters == nullptr || a.out == nullptr || (reinterpret_cast<uintptr_t>(a.out) & 7u)))
+    return MSA_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(step->num_rows) * pool->num_kv_heads > 65535) return MSA_ERR_UNSUPPORTED;
   a.k_codes = static_cast<const uint8_t*>(pool->k_codes);
   a.v_codes = static_cast<const uint8_t*>(pool->v_codes);
   a.k_scales = static_cast<const uint8_t*>(pool->k_scales);
@@ -321,25 +490,71 @@ extern "C" msa_status_t msa_sparse_decode(const msa_kv_pool_t* pool, const msa_s
   a.row_pos = step->row_pos;
   a.max_blocks = step->max_blocks_per_seq;
   a.q = static_cast<const uint16_t*>(q);
+  a.num_rows = step->num_rows;
+  const int pairs = step->num_rows * pool->num_kv_heads;
+  dim3 grid(a.num_splits, pairs);
+#define MSA_DECODE_DISPATCH(FMT)                                              \
+  (select ? dispatch<FMT, true, true>(a, grid, s)                             \
+          : combine ? dispatch<FMT, true, false>(a, grid, s) : dispatch<FMT, false, false>(a, grid, s))
+  if (pool->fmt == MSA_KV_NVFP4) return MSA_DECODE_DISPATCH(MSA_KV_NVFP4);
+  return MSA_DECODE_DISPATCH(MSA_KV_FP8_E4M3);
+#undef MSA_DECODE_DISPATCH
+}
+
+DecodeArgs base_args(const int32_t* sel, const int32_t* sel_pages, int32_t k, float softmax_scale,
+                     int32_t num_splits, float* part_o, float* part_ml) {
+  DecodeArgs a{};
   a.sel = sel;
+  a.sel_pages = sel_pages;
   a.k = k;
   a.softmax_scale = softmax_scale;
   a.num_splits = num_splits;
   a.part_o = part_o;
   a.part_ml = part_ml;
-  // waves per workgroup: one per selected page of the split, up to 4
-  const int per_split = (k + num_splits - 1) / num_splits;
-  const int W = per_split >= 4 ? 4 : per_split >= 2 ? 2 : 1;
-  dim3 grid(num_splits, pool->num_kv_heads, step->num_rows);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (pool->fmt == MSA_KV_NVFP4) {
-    if (W == 4) launch<MSA_KV_NVFP4, 4>(a, grid, s);
-    else if (W == 2) launch<MSA_KV_NVFP4, 2>(a, grid, s);
-    else launch<MSA_KV_NVFP4, 1>(a, grid, s);
-  } else {
-    if (W == 4) launch<MSA_KV_FP8_E4M3, 4>(a, grid, s);
-    else if (W == 2) launch<MSA_KV_FP8_E4M3, 2>(a, grid, s);
-    else launch<MSA_KV_FP8_E4M3, 1>(a, grid, s);
-  }
-  return launch_status();
+  return a;
+}
+
+}  // namespace
+}  // namespace msa
+
+extern "C" msa_status_t msa_sparse_decode(const msa_kv_pool_t* pool, const msa_step_t* step,
+                                          int32_t num_q_heads, const void* q, const int32_t* sel,
+                                          const int32_t* sel_pages, int32_t k, float softmax_scale,
+                                          int32_t num_splits, float* part_o, float* part_ml,
+                                          void* stream) {
+  using namespace msa;
+  DecodeArgs a = base_args(sel, sel_pages, k, softmax_scale, num_splits, part_o, part_ml);
+  return decode_entry(pool, step, num_q_heads, q, a, static_cast<hipStream_t>(stream), false, false);
+}
+
+extern "C" msa_status_t msa_sparse_decode_combine(const msa_kv_pool_t* pool, const msa_step_t* step,
+                                                  int32_t num_q_heads, const void* q,
+                                                  const int32_t* sel, const int32_t* sel_pages,
+                                                  int32_t k, float softmax_scale, int32_t num_splits,
+                                                  float* part_o, float* part_ml, int32_t* counters,
+                                                  void* out, void* stream) {
+  using namespace msa;
+  if (counters == nullptr || out == nullptr) return MSA_ERR_INVALID_ARG;
+  DecodeArgs a = base_args(sel, sel_pages, k, softmax_scale, num_splits, part_o, part_ml);
+  a.counters = counters;
+  a.out = static_cast<uint16_t*>(out);
+  return decode_entry(pool, step, num_q_heads, q, a, static_cast<hipStream_t>(stream), true, false);
+}
+
+extern "C" msa_status_t msa_select_decode_combine(
+    const msa_kv_pool_t* pool, const msa_step_t* step, int32_t num_q_heads, const void* q,
+    const float* block_scores, int32_t k, int32_t n_init, int32_t n_local, float softmax_scale,
+    int32_t num_splits, float* part_o, float* part_ml, int32_t* counters, void* out, int32_t* sel,
+    int32_t* sel_pages, void* stream) {
+  using namespace msa;
+  if (counters == nullptr || out == nullptr) return MSA_ERR_INVALID_ARG;
+  DecodeArgs a = base_args(nullptr, nullptr, k, softmax_scale, num_splits, part_o, part_ml);
+  a.scores = block_scores;
+  a.n_init = n_init;
+  a.n_local = n_local;
+  a.sel_out = sel;
+  a.sel_pages_out = sel_pages;
+  a.counters = counters;
+  a.out = static_cast<uint16_t*>(out);
+  return decode_entry(pool, step, num_q_heads, q, a, static_cast<hipStream_t>(stream), true, true);
 }

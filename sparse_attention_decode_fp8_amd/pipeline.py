@@ -1,13 +1,19 @@
-"""Sequencing of one decode step through the five library calls.
+"""Sequencing of one decode step through the library calls.
 
-This only allocates output buffers once and issues the five calls in order on one
-stream; all arithmetic happens in the HIP kernels.
+This only allocates output buffers once and issues the calls in order on one stream;
+all arithmetic happens in the HIP kernels.
 """
 from __future__ import annotations
 
 import torch
 
 from . import _lib as L
+
+
+def default_num_splits(k: int) -> int:
+    """Split count used by the benchmark and the full-size parity tests: one split per
+    two selected pages (a workgroup of eight waves, one 32-token chunk per wave)."""
+    return max(1, (k + 1) // 2)
 
 
 class DecodeBuffers:
@@ -17,28 +23,37 @@ class DecodeBuffers:
         self.k, self.num_splits = k, num_splits
         self.block_scores = torch.empty((num_rows, max_blocks), dtype=torch.float32, device=device)
         self.sel = torch.empty((num_rows, k), dtype=torch.int32, device=device)
+        self.sel_pages = torch.empty((num_rows, k), dtype=torch.int32, device=device)
         self.part_o = torch.empty((num_rows, num_q_heads, num_splits, L.HEAD_DIM),
                                   dtype=torch.float32, device=device)
         self.part_ml = torch.empty((num_rows, num_q_heads, num_splits, 2), dtype=torch.float32,
                                    device=device)
+        self.counters = torch.zeros((num_rows, num_q_heads // 16), dtype=torch.int32, device=device)
+        self.score_counters = torch.zeros(num_rows, dtype=torch.int32, device=device)
         self.out = torch.empty((num_rows, num_q_heads, L.HEAD_DIM), dtype=torch.bfloat16, device=device)
 
 
 def run_step(pool, step, bufs: DecodeBuffers, q, q_idx, w, softmax_scale, slot=None, k_new=None,
-             v_new=None, idx_k_new=None, n_init=0, n_local=1, stream=None):
-    """append -> index score -> select -> sparse decode -> combine, on one stream."""
+             v_new=None, idx_k_new=None, n_init=0, n_local=1, fused=True, stream=None):
+    """One decode step on one stream: append -> index score -> select -> sparse decode
+    -> combine. fused=True issues two launches (append + score; select + decode +
+    combine); fused=False issues the five separate calls."""
+    if fused:
+        L.msa_append_score_select(pool, step, q_idx, w, bufs.k, n_init, n_local, bufs.block_scores,
+                                  slot=slot, k_new=k_new, v_new=v_new, idx_k_new=idx_k_new,
+                                  stream=stream)
+        L.msa_select_decode_combine(pool, step, q, bufs.block_scores, bufs.k, n_init, n_local,
+                                    softmax_scale, bufs.num_splits, bufs.part_o, bufs.part_ml,
+                                    bufs.counters, bufs.out, sel=bufs.sel, sel_pages=bufs.sel_pages,
+                                    stream=stream)
+        return bufs.out
     if slot is not None and slot.numel() > 0:
         L.msa_kv_append(pool, slot, k_new, v_new, idx_k_new, stream)
     L.msa_index_score(pool, step, q_idx, w, bufs.block_scores, stream)
-    L.msa_select_topk(step, bufs.block_scores, bufs.k, n_init, n_local, bufs.sel, stream)
+    L.msa_select_topk(step, bufs.block_scores, bufs.k, n_init, n_local, bufs.sel, bufs.sel_pages,
+                      stream)
     L.msa_sparse_decode(pool, step, q, bufs.sel, bufs.k, softmax_scale, bufs.num_splits,
-                        bufs.part_o, bufs.part_ml, stream)
-    L.msa_combine(step.num_rows, q.shape[1], L.HEAD_DIM, bufs.num_splits, bufs.part_o, bufs.part_ml,
-                  bufs.out, stream)
+                        bufs.part_o, bufs.part_ml, sel_pages=bufs.sel_pages, stream=stream)
+    L.msa_combine(step.num_rows, q.shape[1], L.HEAD_DIM, bufs.num_splits, bufs.part_o,
+                  bufs.part_ml, bufs.out, stream)
     return bufs.out
-
-
-def default_num_splits(k: int) -> int:
-    """Split count used by the benchmark and the full-size parity tests: one split per
-    four selected pages (each split is one workgroup of four waves, one page per wave)."""
-    return max(1, (k + 3) // 4)

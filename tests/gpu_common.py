@@ -50,14 +50,14 @@ def gpu_step_inputs(M, wl: W.Workload):
     return step, q, q_idx, w, app
 
 
-def run_gpu_step(M, wl, pool, num_splits):
+def run_gpu_step(M, wl, pool, num_splits, fused=True):
     step, q, q_idx, w, app = gpu_step_inputs(M, wl)
     bufs = M.DecodeBuffers(wl.num_rows, wl.num_heads, wl.max_blocks, wl.k, num_splits)
     kw = {}
     if app is not None:
         kw = dict(slot=app[0], k_new=app[1], v_new=app[2], idx_k_new=app[3])
     M.run_step(pool, step, bufs, q, q_idx, w, wl.softmax_scale, n_init=wl.n_init,
-               n_local=wl.n_local, **kw)
+               n_local=wl.n_local, fused=fused, **kw)
     torch.cuda.synchronize()
     return bufs
 

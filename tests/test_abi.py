@@ -78,19 +78,19 @@ def test_validation_rejects_before_launch():
     # empty work is OK and launches nothing
     assert L.LIB.msa_kv_append(B(pool), 0, None, None, None, None, None) == 0
     assert L.LIB.msa_index_score(B(pool), B(step), 4, P(16), P(16), P(16), None) == 0
-    assert L.LIB.msa_select_topk(B(step), P(16), 8, 0, 1, P(16), None) == 0
-    assert L.LIB.msa_sparse_decode(B(pool), B(step), 32, P(16), P(16), 8, 0.1, 2, P(16), P(16), None) == 0
+    assert L.LIB.msa_select_topk(B(step), P(16), 8, 0, 1, P(16), None, None) == 0
+    assert L.LIB.msa_sparse_decode(B(pool), B(step), 32, P(16), P(16), None, 8, 0.1, 2, P(16), P(16), None) == 0
     assert L.LIB.msa_combine(0, 32, 128, 2, P(16), P(16), P(16), None) == 0
     # unsupported geometry
     assert L.LIB.msa_kv_append(B(_fake_pool(head_dim=64)), 1, P(16), None, None, None, None) == -2
     assert L.LIB.msa_kv_append(B(_fake_pool(fmt=7)), 1, P(16), None, None, None, None) == -2
     assert L.LIB.msa_index_score(B(pool), B(step), 3, P(16), P(16), P(16), None) == -2
-    assert L.LIB.msa_select_topk(B(step), P(16), 0, 0, 1, P(16), None) == -2
-    assert L.LIB.msa_select_topk(B(step), P(16), 65, 0, 1, P(16), None) == -2
-    assert L.LIB.msa_select_topk(B(step), P(16), 4, 3, 2, P(16), None) == -2
-    assert L.LIB.msa_select_topk(B(_fake_step(max_blocks=12289)), P(16), 4, 0, 1, P(16), None) == -2
-    assert L.LIB.msa_sparse_decode(B(pool), B(step), 48, P(16), P(16), 8, 0.1, 2, P(16), P(16), None) == -2
-    assert L.LIB.msa_sparse_decode(B(pool), B(step), 32, P(16), P(16), 8, 0.1, 9, P(16), P(16), None) == -2
+    assert L.LIB.msa_select_topk(B(step), P(16), 0, 0, 1, P(16), None, None) == -2
+    assert L.LIB.msa_select_topk(B(step), P(16), 65, 0, 1, P(16), None, None) == -2
+    assert L.LIB.msa_select_topk(B(step), P(16), 4, 3, 2, P(16), None, None) == -2
+    assert L.LIB.msa_select_topk(B(_fake_step(max_blocks=12289)), P(16), 4, 0, 1, P(16), None, None) == -2
+    assert L.LIB.msa_sparse_decode(B(pool), B(step), 48, P(16), P(16), None, 8, 0.1, 2, P(16), P(16), None) == -2
+    assert L.LIB.msa_sparse_decode(B(pool), B(step), 32, P(16), P(16), None, 8, 0.1, 9, P(16), P(16), None) == -2
     assert L.LIB.msa_combine(1, 32, 64, 2, P(16), P(16), P(16), None) == -2
     # invalid arguments
     assert L.LIB.msa_kv_append(None, 1, P(16), None, None, None, None) == -1
@@ -103,10 +103,28 @@ def test_validation_rejects_before_launch():
     assert L.LIB.msa_kv_append(B(bad), 1, P(16), None, None, None, None) == -1
     s1 = _fake_step(rows=1)
     assert L.LIB.msa_index_score(B(pool), B(s1), 4, None, P(16), P(16), None) == -1
-    assert L.LIB.msa_select_topk(B(s1), None, 4, 0, 1, P(16), None) == -1
-    assert L.LIB.msa_sparse_decode(B(pool), B(s1), 32, P(16), P(16), 8, 0.0, 2, P(16), P(16), None) == -1
-    assert L.LIB.msa_sparse_decode(B(pool), B(s1), 32, P(24), P(16), 8, 0.1, 2, P(16), P(16), None) == -1
+    assert L.LIB.msa_select_topk(B(s1), None, 4, 0, 1, P(16), None, None) == -1
+    assert L.LIB.msa_sparse_decode(B(pool), B(s1), 32, P(16), P(16), None, 8, 0.0, 2, P(16), P(16), None) == -1
+    assert L.LIB.msa_sparse_decode(B(pool), B(s1), 32, P(24), P(16), None, 8, 0.1, 2, P(16), P(16), None) == -1
     assert L.LIB.msa_combine(1, 32, 128, 2, None, P(16), P(16), None) == -1
+    # the combining decode needs both its counters and its output
+    assert L.LIB.msa_sparse_decode_combine(B(pool), B(s1), 32, P(16), P(16), None, 8, 0.1, 2, P(16),
+                                           P(16), None, P(16), None) == -1
+    assert L.LIB.msa_sparse_decode_combine(B(pool), B(s1), 32, P(16), P(16), None, 8, 0.1, 2, P(16),
+                                           P(16), P(16), None, None) == -1
+    assert L.LIB.msa_sparse_decode_combine(B(pool), B(step), 32, P(16), P(16), None, 8, 0.1, 2, P(16),
+                                           P(16), P(16), P(16), None) == 0
+    # fused append + score + select
+    assert L.LIB.msa_append_score_select(B(pool), B(step), 0, None, None, None, None, 4, P(16), P(16),
+                                         8, 0, 1, P(16), P(16), None, P(16), None) == 0
+    assert L.LIB.msa_append_score_select(B(pool), B(s1), 4097, P(16), None, None, None, 4, P(16),
+                                         P(16), 8, 0, 1, P(16), P(16), None, P(16), None) == -2
+    assert L.LIB.msa_append_score_select(B(pool), B(s1), 1, None, None, None, None, 4, P(16), P(16),
+                                         8, 0, 1, P(16), P(16), None, P(16), None) == -1
+    assert L.LIB.msa_append_score_select(B(pool), B(s1), 0, None, None, None, None, 4, P(16), P(16),
+                                         8, 0, 1, P(16), P(16), None, None, None) == -1
+    assert L.LIB.msa_append_score_select(B(pool), B(s1), 0, None, None, None, None, 3, P(16), P(16),
+                                         8, 0, 1, P(16), P(16), None, P(16), None) == -2
     nullstep = L.MsaStep(1, 1, 8, None, None, None)
     assert L.LIB.msa_index_score(B(pool), B(nullstep), 4, P(16), P(16), P(16), None) == -1
 

@@ -43,12 +43,12 @@ def test_append_bytes_bit_exact(M, fmt):
 
 
 @pytest.mark.parametrize("fmt", [W.FMT_FP8, W.FMT_NVFP4])
-@pytest.mark.parametrize("num_splits", [1, 2, 5])
-def test_full_step_parity(M, fmt, num_splits):
+@pytest.mark.parametrize("num_splits,fused", [(1, True), (2, False), (2, True), (5, True)])
+def test_full_step_parity(M, fmt, num_splits, fused):
     wl = W.small(fmt, [1000, 2600, 130, 640], 3, num_kv_heads=2, k=5, seed=31)
-    _print("step parity", wl.name, "splits", num_splits)
+    _print("step parity", wl.name, "splits", num_splits, "fused", fused)
     pool = G.gpu_pool(M, wl)
-    bufs = G.run_gpu_step(M, wl, pool, num_splits)
+    bufs = G.run_gpu_step(M, wl, pool, num_splits, fused=fused)
     ref_pool = G.oracle_pool(wl)
     S_ref = O.index_score(ref_pool, wl.block_table, wl.row_seq, wl.row_pos, wl.q_idx, wl.w, wl.max_blocks)
     sel_ref = O.select_topk(S_ref, wl.row_pos, wl.k)
@@ -187,3 +187,57 @@ def test_combine_matches_oracle_combine(M):
     got = G.bf16_to_np(out)
     # one bf16 rounding of the exact merge
     assert np.all(np.abs(got - ref) <= np.abs(ref) * 2 ** -8 + 1e-6)
+
+
+def test_sel_pages_and_fused_combine(M):
+    """sel_pages is the block-table image of sel; the two fused launches (append + score +
+    select, decode + combine) equal the five separate calls bit for bit and leave their
+    counters at zero."""
+    wl = W.small(W.FMT_NVFP4, [3000, 700, 5000], 2, num_kv_heads=2, k=8, seed=46)
+    pool = G.gpu_pool(M, wl)
+    for ns in (1, 3, 4, 8):
+        _print("fused vs separate, splits", ns)
+        pa = pool.clone()
+        a = G.run_gpu_step(M, wl, pa, ns, fused=True)
+        b = G.run_gpu_step(M, wl, pool.clone(), ns, fused=False)
+        sel, sp = a.sel.cpu().numpy(), a.sel_pages.cpu().numpy()
+        exp = np.where(sel >= 0, wl.block_table[wl.row_seq[:, None], np.maximum(sel, 0)], -1)
+        assert np.array_equal(sp, exp)
+        assert torch.equal(a.out.view(torch.int16), b.out.view(torch.int16))
+        assert torch.equal(a.sel, b.sel)
+        nb = torch.from_numpy(wl.row_pos // 128 + 1).cuda()
+        vis = torch.arange(wl.max_blocks, device="cuda")[None] < nb[:, None]
+        assert torch.equal(a.block_scores[vis], b.block_scores[vis])
+        assert int(a.counters.abs().sum()) == 0 and int(a.score_counters.abs().sum()) == 0
+        # the scoring launch can also select (last workgroup per row group)
+        pc = pool.clone()
+        step, q, q_idx, w, app = G.gpu_step_inputs(M, wl)
+        bs = torch.empty_like(a.block_scores)
+        sel2 = torch.full_like(a.sel, -7)
+        sp2 = torch.full_like(a.sel, -7)
+        M.msa_append_score_select(pc, step, q_idx, w, wl.k, 0, 1, bs, sel2, sp2, a.score_counters,
+                                  slot=app[0], k_new=app[1], v_new=app[2], idx_k_new=app[3])
+        torch.cuda.synchronize()
+        assert torch.equal(sel2, b.sel) and torch.equal(sp2, b.sel_pages)
+        assert int(a.score_counters.abs().sum()) == 0
+        for name, arr in pa.arrays().items():
+            assert torch.equal(arr, pc.arrays()[name]), name
+        # a second call with the same counters still merges correctly
+        step, q, q_idx, w, _ = G.gpu_step_inputs(M, wl)
+        M.msa_sparse_decode_combine(pa, step, q, a.sel, wl.k, wl.softmax_scale, ns, a.part_o,
+                                    a.part_ml, a.counters, a.out, sel_pages=a.sel_pages)
+        torch.cuda.synchronize()
+        assert torch.equal(a.out.view(torch.int16), b.out.view(torch.int16))
+
+
+@pytest.mark.parametrize("fmt", [W.FMT_FP8, W.FMT_NVFP4])
+def test_fused_step_many_rows_per_request(M, fmt):
+    """Verify-style step (4 rows per request, appended tokens spanning a page boundary):
+    fused and separate launches agree bit for bit, repeatedly."""
+    wl = W.small(fmt, [126, 1022, 3000, 9000], 4, num_kv_heads=2, k=6, seed=47)
+    pool = G.gpu_pool(M, wl)
+    ref = G.run_gpu_step(M, wl, pool.clone(), 3, fused=False)
+    for rep in range(3):
+        got = G.run_gpu_step(M, wl, pool.clone(), 3, fused=True)
+        assert torch.equal(got.sel, ref.sel)
+        assert torch.equal(got.out.view(torch.int16), ref.out.view(torch.int16)), rep
