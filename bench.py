@@ -12,9 +12,10 @@ evicted from the 256 MB Infinity Cache and the L2s before it is read again. Step
 captured in HIP graphs (one graph per replica, plus one graph of all R) and replayed;
 exactly K steps are timed between two synchronisations.
 
-Per-kernel durations are measured live with HIP events on the step's stream, in a
-second pass where the launches are queued behind a GPU sleep so that no host gap falls
-between the event pair. The roofline entry uses the decode kernel's mean duration and
+Per-kernel durations are measured live with HIP events on the step's stream: each
+kernel is captured R times in a graph of its own (once per replica), and the replays of
+that graph are timed, so the mean includes the dispatch gap between back-to-back launches.
+The roofline entry uses the decode kernel's mean duration and
 its algorithmic bytes (selected visible K/V bytes + Q + O + selection/block-table
 reads). HBM traffic comes from rocprofv3 FETCH_SIZE / WRITE_SIZE counters recorded in
 profiles/ and is reported only while the kernel source is unchanged since then.
@@ -54,7 +55,7 @@ def parse():
 
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
-    for f in ("sparse_decode.hip", "msa_device.h"):
+    for f in ("sparse_decode.hip", "msa_device.h", "select_device.h"):
         with open(os.path.join(ROOT, "sparse_attention_decode_fp8_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -191,24 +192,30 @@ def main():
                                                   sel=bufs.sel, sel_pages=bufs.sel_pages),
         ]
         decode_kernels = ["msa_select_decode_combine"]
-    n_meas = min(args.steps, 160)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(n_meas)]
+    # One graph per kernel that launches it once on every pool replica (inputs as the step
+    # leaves them); events around replays of it give the mean launch duration, the
+    # dispatch gap between back-to-back launches included.
+    kgraphs = []
+    for call in calls:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for p in pools:
+                call(p)
+        kgraphs.append(g)
     torch.cuda.synchronize()
-    if hasattr(torch.cuda, "_sleep"):
-        torch.cuda._sleep(200_000_000)
-    for i in range(n_meas):
-        p = pools[i % len(pools)]
-        e = evs[i]
-        e[0].record()
-        for j, call in enumerate(calls):
-            call(p)
-            e[j + 1].record()
-    torch.cuda.synchronize()
+    reps = max(1, min(args.steps, 160) // len(pools))
     per_kernel_us = {}
-    for j, nm in enumerate(names):
-        d = np.array([evs[i][j].elapsed_time(evs[i][j + 1]) * 1e3 for i in range(n_meas)])
-        per_kernel_us[nm] = {"mean": float(d.mean()), "p10": float(np.percentile(d, 10)),
-                             "p50": float(np.median(d)), "p90": float(np.percentile(d, 90))}
+    for nm, g in zip(names, kgraphs):
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        per_kernel_us[nm] = {"mean": e0.elapsed_time(e1) * 1e3 / (reps * len(pools)),
+                             "launches": reps * len(pools)}
 
     sel = bufs.sel.cpu().numpy()
     bpt = 144 if wl.fmt == W.FMT_NVFP4 else 256
@@ -219,7 +226,7 @@ def main():
     achieved = dec_bytes / t_dec / 1e9
 
     traffic = None
-    prof = os.path.join(ROOT, "profiles", "msa_sparse_decode_b8_ctx32k_nvfp4_top16.counters.json")
+    prof = os.path.join(ROOT, "profiles", "msa_select_decode_combine_b8_ctx32k_nvfp4_top16.counters.json")
     if os.path.exists(prof):
         with open(prof) as fh:
             pc = json.load(fh)
