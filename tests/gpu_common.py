@@ -148,3 +148,42 @@ def oracle_rows(wl: W.Workload, rows):
     out = O.attend(pool, wl.block_table, wl.row_seq[sub], wl.row_pos[sub], wl.q[sub], sel,
                    wl.softmax_scale)
     return S, sel, out, pool
+
+
+def check_step_parity(M, wl: W.Workload, num_splits: int, fused: bool):
+    """Run one whole step on the GPU and compare scores, selection, outputs and the
+    split partials with the oracle, computed from the same seeded source."""
+    pool = gpu_pool(M, wl)
+    bufs = run_gpu_step(M, wl, pool, num_splits, fused=fused)
+    ref_pool = oracle_pool(wl)
+    S_ref = O.index_score(ref_pool, wl.block_table, wl.row_seq, wl.row_pos, wl.q_idx, wl.w, wl.max_blocks)
+    sel_ref = O.select_topk(S_ref, wl.row_pos, wl.k, wl.n_init, wl.n_local)
+    out_ref = O.attend(ref_pool, wl.block_table, wl.row_seq, wl.row_pos, wl.q, sel_ref, wl.softmax_scale)
+    S = bufs.block_scores.cpu().numpy()
+    assert_scores_close(S, S_ref)
+    sel = bufs.sel.cpu().numpy()
+    nb = wl.row_pos // 128 + 1
+    same = np.ones(wl.num_rows, bool)
+    for r in range(wl.num_rows):
+        if gap_qualified(S_ref[r], nb[r], wl.k, wl.n_init, wl.n_local):
+            assert np.array_equal(sel[r], sel_ref[r]), r
+        else:
+            check_selection_valid(sel[r], S_ref[r], nb[r], wl.k, wl.n_init, wl.n_local)
+            same[r] = np.array_equal(sel[r], sel_ref[r])
+    out = bf16_to_np(bufs.out)
+    assert_out_close(out[same], out_ref[same], "outputs")
+    # the split partials the kernel wrote
+    m, l, Op = O.split_partials(ref_pool, wl.block_table, wl.row_seq, wl.row_pos, wl.q, sel_ref,
+                                wl.softmax_scale, num_splits)
+    ml = bufs.part_ml.cpu().numpy()
+    po = bufs.part_o.cpu().numpy()
+    for r in np.nonzero(same)[0]:
+        fin = np.isfinite(m[r])
+        assert np.array_equal(np.isneginf(ml[r, :, :, 0]), ~fin)
+        assert np.allclose(ml[r, :, :, 0][fin], m[r][fin], rtol=1e-4, atol=1e-3)
+        lr = np.where(fin, l[r], 0)
+        assert np.allclose(ml[r, :, :, 1], lr, rtol=2e-2, atol=1e-3)
+        # O is unnormalised: compare relative to its sum of weights
+        den = np.maximum(lr, 1e-30)[..., None]
+        assert np.max(np.abs(po[r] / den - Op[r] / den)[fin]) < 1e-2
+    return bufs

@@ -47,39 +47,7 @@ def test_append_bytes_bit_exact(M, fmt):
 def test_full_step_parity(M, fmt, num_splits, fused):
     wl = W.small(fmt, [1000, 2600, 130, 640], 3, num_kv_heads=2, k=5, seed=31)
     _print("step parity", wl.name, "splits", num_splits, "fused", fused)
-    pool = G.gpu_pool(M, wl)
-    bufs = G.run_gpu_step(M, wl, pool, num_splits, fused=fused)
-    ref_pool = G.oracle_pool(wl)
-    S_ref = O.index_score(ref_pool, wl.block_table, wl.row_seq, wl.row_pos, wl.q_idx, wl.w, wl.max_blocks)
-    sel_ref = O.select_topk(S_ref, wl.row_pos, wl.k)
-    out_ref = O.attend(ref_pool, wl.block_table, wl.row_seq, wl.row_pos, wl.q, sel_ref, wl.softmax_scale)
-    S = bufs.block_scores.cpu().numpy()
-    G.assert_scores_close(S, S_ref)
-    sel = bufs.sel.cpu().numpy()
-    nb = wl.row_pos // 128 + 1
-    same = np.ones(wl.num_rows, bool)
-    for r in range(wl.num_rows):
-        if G.gap_qualified(S_ref[r], nb[r], wl.k):
-            assert np.array_equal(sel[r], sel_ref[r]), r
-        else:
-            G.check_selection_valid(sel[r], S_ref[r], nb[r], wl.k)
-            same[r] = np.array_equal(sel[r], sel_ref[r])
-    out = G.bf16_to_np(bufs.out)
-    G.assert_out_close(out[same], out_ref[same], "outputs")
-    # partials of the split that the kernel wrote
-    m, l, Op = O.split_partials(ref_pool, wl.block_table, wl.row_seq, wl.row_pos, wl.q, sel_ref,
-                                wl.softmax_scale, num_splits)
-    ml = bufs.part_ml.cpu().numpy()
-    po = bufs.part_o.cpu().numpy()
-    for r in np.nonzero(same)[0]:
-        fin = np.isfinite(m[r])
-        assert np.array_equal(np.isneginf(ml[r, :, :, 0]), ~fin)
-        assert np.allclose(ml[r, :, :, 0][fin], m[r][fin], rtol=1e-4, atol=1e-3)
-        lr = np.where(fin, l[r], 0)
-        assert np.allclose(ml[r, :, :, 1], lr, rtol=2e-2, atol=1e-3)
-        # O is unnormalised; compare relative to its sum of weights
-        den = np.maximum(lr, 1e-30)[..., None]
-        assert np.max(np.abs(po[r] / den - Op[r] / den)[fin]) < 1e-2
+    G.check_step_parity(M, wl, num_splits, fused)
 
 
 def test_num_splits_agree(M):
