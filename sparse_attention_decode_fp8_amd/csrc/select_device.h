@@ -185,13 +185,19 @@ __device__ __forceinline__ void wave_select_table(const float* srow, const int32
   if (lane < n_init) { out = lane; opg = bt[lane]; }
   if (lane >= k - n_local && lane < k) { out = nb - k + lane; opg = bt[nb - k + lane]; }
   if (want > 0) {
+    // T ends as a threshold with count(key >= T) >= want and, unless some count hit
+    // want exactly (then the keys >= T are the selection and the search stops early),
+    // as the exact want-th largest key.
     uint32_t T = 0;
     for (int bit = 31; bit >= 0; --bit) {
       const uint32_t cand = T | (1u << bit);
       int cnt = 0;
 #pragma unroll
       for (int i = 0; i < kR; ++i) cnt += __popcll(__ballot(key[i] >= cand));
-      if (cnt >= want) T = cand;
+      if (cnt >= want) {
+        T = cand;
+        if (cnt == want) break;
+      }
     }
     int gt = 0;
 #pragma unroll

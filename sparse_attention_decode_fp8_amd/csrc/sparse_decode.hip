@@ -42,6 +42,11 @@ namespace {
 
 constexpr int kVRowHalves = 144;   // 128 fp16 + 16 pad: 288-byte rows keep 4 rows on disjoint banks
 constexpr int kVBufBytes = 32 * kVRowHalves * 2;   // one wave's 32-token V chunk
+// A wave's O tile, [16 heads][128 d] fp32, reuses its V buffer. Rows are 132 floats
+// (33 16-byte quads, an odd count) so the 16 heads a quarter-wave writes at once fall
+// on distinct banks; 128-float rows would put all 16 on the same banks.
+constexpr int kORowFloats = kHeadDim + 4;
+static_assert(16 * kORowFloats * 4 <= kVBufBytes, "O tile must fit in a V buffer");
 constexpr int kMaxCombineSplits = 16;
 
 struct DecodeArgs {
@@ -184,8 +189,8 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
   __shared__ float mbuf[kW][16], lbuf[kW][16];
   __shared__ int s_last;
-  __shared__ int32_t lsel[kSelect ? MSA_MAX_TOPK : 1];
-  __shared__ int wsel[kSelect ? kW : 1][128];
+  __shared__ int32_t lsel[kSelect ? MSA_MAX_TOPK : 1], lpage[kSelect ? MSA_MAX_TOPK : 1];
+  __shared__ int wsel[kSelect ? 128 : 1];
   __shared__ SelectSmem sm;
   const int pair = blockIdx.y, s = blockIdx.x;   // (row, KV head) pair, split
   if (pair >= a.num_rows * a.hkv) return;
@@ -210,8 +215,15 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
     const int32_t* bt = a.block_table + static_cast<int64_t>(a.row_seq[r]) * a.max_blocks;
     const float* srow = a.scores + static_cast<int64_t>(r) * a.max_blocks;
     if (a.max_blocks - a.n_init - a.n_local <= kWaveSelectMax) {
-      // every wave selects on its own: no barrier, identical tables
-      wave_select(srow, bt, a.max_blocks, nb, a.k, a.n_init, a.n_local, &wsel[wave][0], selv, pagev);
+      // wave 0 selects (the other waves would only contend for the scalar unit) and
+      // hands the table over through LDS
+      if (wave == 0) {
+        wave_select(srow, bt, a.max_blocks, nb, a.k, a.n_init, a.n_local, wsel, selv, pagev);
+        if (lane < MSA_MAX_TOPK) { lsel[lane] = selv; lpage[lane] = pagev; }
+      }
+      __syncthreads();
+      selv = lane < MSA_MAX_TOPK ? lsel[lane] : -1;
+      pagev = lane < MSA_MAX_TOPK ? lpage[lane] : -1;
     } else {
       block_select_row<false, 64 * kW>(srow, nb, a.k, a.n_init, a.n_local, bt, lsel, nullptr,
                                        reinterpret_cast<uint32_t*>(dyn_lds), sm);
@@ -350,10 +362,10 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
   const int64_t head0 = static_cast<int64_t>(r) * hq + kHeadsPerKv * g;
   __syncthreads();                                     // every wave is done with its V buffer
   {
-    float* ob = reinterpret_cast<float*>(dyn_lds + wave * kVBufBytes);   // [16 heads][128 d] fp32
+    float* ob = reinterpret_cast<float*>(dyn_lds + wave * kVBufBytes);   // [16 heads][kORowFloats]
 #pragma unroll
     for (int d = 0; d < 8; ++d)
-      *reinterpret_cast<float4_t*>(ob + n * kHeadDim + 16 * d + 4 * q) = O[d] * oscale;
+      *reinterpret_cast<float4_t*>(ob + n * kORowFloats + 16 * d + 4 * q) = O[d] * oscale;
     if (q == 0) { mbuf[wave][n] = m_run; lbuf[wave][n] = l_tot; }
   }
   __syncthreads();
@@ -369,7 +381,7 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
       for (int w = 0; w < kW; ++w) {
         const float wt = exp2f(mbuf[w][h] - M);
         acc += wt * *reinterpret_cast<const float4_t*>(
-                        reinterpret_cast<const float*>(dyn_lds + w * kVBufBytes) + h * kHeadDim + 4 * d4);
+                        reinterpret_cast<const float*>(dyn_lds + w * kVBufBytes) + h * kORowFloats + 4 * d4);
         l += wt * lbuf[w][h];
       }
     }
