@@ -101,6 +101,8 @@ typedef struct {
  * request are contiguous. Row r belongs to request row_seq[r] and sits at absolute
  * position row_pos[r]; it attends positions [0, row_pos[r]] (causal among the verify
  * tokens of a speculative step). Its visible blocks are 0 .. row_pos[r] / 128.
+ * When num_rows > 0, num_seqs must be at least 1 and every row_seq value must lie in
+ * [0, num_seqs) (MSA_ERR_INVALID_ARG for num_seqs == 0; the values are trusted).
  */
 typedef struct {
   int32_t num_seqs;

@@ -39,7 +39,7 @@ struct ScoreArgs {
   const uint16_t* q_idx;
   const float* w;
   float* scores;
-  int num_rows, max_blocks;
+  int num_rows, num_seqs, max_blocks;
   // fused launch only
   AppendArgs app;
   int k, n_init, n_local;
@@ -65,31 +65,113 @@ __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
     if (static_cast<int>(blockIdx.x) >= a.score_wgs_x) return;
   }
   const int r0 = blockIdx.y;
-  const int seq = a.row_seq[r0];
-  // Is r0 the first row of a group? Count earlier rows of the same request.
-  int j = 0;
-  while (r0 - j - 1 >= 0 && a.row_seq[r0 - j - 1] == seq) ++j;
-  if (j % kRowsPerGroup != 0) return;
-  int nr = 1;
-  while (nr < kRowsPerGroup && r0 + nr < a.num_rows && a.row_seq[r0 + nr] == seq) ++nr;
-  int max_pos = -1;
-  for (int i = 0; i < nr; ++i) max_pos = max(max_pos, a.row_pos[r0 + i]);
-  const int last_block = max_pos / kPage;
-
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, q = lane >> 4;
   const int b = blockIdx.x * kWaves + wave;
+
+  // Row metadata in one round of loads: lanes 0..31 read row_seq of rows r0-32 .. r0-1,
+  // lanes 32..47 row_seq and row_pos of rows r0 .. r0+15, and every lane the block-table
+  // entry of block b for the request r0 belongs to when every request has the same
+  // number of rows (checked below, and read again if wrong).
+  const int rr = r0 - 32 + lane;
+  const bool in_rows = lane < 48 && rr >= 0 && rr < a.num_rows;
+  const int seq_l = in_rows ? a.row_seq[rr] : -1;
+  const int pos_l = in_rows && lane >= 32 ? a.row_pos[rr] : -1;
+  const int guess = static_cast<int>(static_cast<int64_t>(r0) * a.num_seqs / a.num_rows);
+  const int page_g = b < a.max_blocks ? a.block_table[static_cast<int64_t>(guess) * a.max_blocks + b] : -1;
+  // fused launch: the first 64 new tokens' slots, so that matching them against the
+  // page below waits for no further load
+  int64_t slot0 = -1;
+  if constexpr (kFused)
+    if (a.app.idx_new != nullptr && lane < a.app.n_new) slot0 = a.app.slot[lane];
+  const int seq = __shfl(seq_l, 32, 64);
+  const uint64_t same = __ballot(seq_l == seq);
+  // Is r0 the first row of a group? Count the earlier rows of the same request.
+  const uint32_t before = ~static_cast<uint32_t>(same);            // lanes 0..31: a different request
+  int j = before != 0 ? __builtin_clz(before) : 32;               // run of equal rows ending at r0-1
+  if (j == 32)
+    while (r0 - j - 1 >= 0 && a.row_seq[r0 - j - 1] == seq) ++j;
+  if (j % kRowsPerGroup != 0) return;
+  // rows r0 .. r0+nr-1 of the same request form the group
+  const uint32_t after = ~static_cast<uint32_t>(same >> 32);       // bit i: row r0+i differs
+  const int nr = min(kRowsPerGroup, __builtin_ctz(after | (1u << 16)));
+  int max_pos = lane >= 32 && lane < 32 + nr ? pos_l : -1;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) max_pos = max(max_pos, __shfl_xor(max_pos, m, 64));
+  const int last_block = max_pos / kPage;
+
   const bool active = b < a.max_blocks && b <= last_block;   // this wave scores block b
   const bool fill = b < a.max_blocks && b > last_block;      // past every row: -inf only
 
   if (active) {
-    const int64_t page = a.block_table[static_cast<int64_t>(seq) * a.max_blocks + b];
-    // All 8 key loads of the block: lane (n, q) reads 16 bytes of token 16t + n,
-    // dims 16q .. 16q+15 (k-step 0 uses the first 8, k-step 1 the last 8).
-    const uint8_t* kp = a.index_k + (page * kPage + n) * kIndexDim + 16 * q;
-    uint4 key[8];
+    // The query-side loads go out before the key loads: the vector memory counter
+    // retires in order, so converting the queries waits for them alone.
+    // A operand: lane (m, q) holds query row-slot m / Hi, head m % Hi, dims
+    // 16q + 8ks .. +7, times 2^e (e per (row, head), from the amax over 64 dims).
+    const int m = n;
+    const int rs = m / kHi, hd = m % kHi;
+    uint4 qa0 = make_uint4(0u, 0u, 0u, 0u), qa1 = qa0;
+    if (rs < nr) {
+      const uint16_t* qp = a.q_idx + (static_cast<int64_t>(r0 + rs) * kHi + hd) * kIndexDim + 16 * q;
+      qa0 = reinterpret_cast<const uint4*>(qp)[0];
+      qa1 = reinterpret_cast<const uint4*>(qp)[1];
+    }
+    // After the MFMA, lane (n, q) holds M = 4q + jj: the matching (row, head) weight.
+    float wj[4];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) key[t] = *reinterpret_cast<const uint4*>(kp + t * 16 * kIndexDim);
+    for (int jj = 0; jj < 4; ++jj) {
+      const int mm = 4 * q + jj;
+      const int rr = mm / kHi, hh = mm % kHi;
+      wj[jj] = rr < nr ? a.w[static_cast<int64_t>(r0 + rr) * kHi + hh] : 0.0f;
+    }
+    int rowslot[kRowsPerLane], pos[kRowsPerLane];
+#pragma unroll
+    for (int i = 0; i < kRowsPerLane; ++i) {
+      rowslot[i] = q * kRowsPerLane + i;
+      pos[i] = rowslot[i] < nr ? a.row_pos[r0 + rowslot[i]] : -1;
+    }
+
+    // All 8 key loads of the block: lane (n, q) reads 16 bytes of token 16t + n,
+    // dims 16q .. 16q+15 (k-step 0 uses the first 8, k-step 1 the last 8). They are
+    // issued from the guessed request's page (an unused entry reads page 0) and issued
+    // again from the right page if the guess was wrong.
+    int64_t page = page_g >= 0 ? page_g : 0;
+    uint4 key[8];
+    auto load_keys = [&]() {
+      const uint8_t* kp = a.index_k + (page * kPage + n) * kIndexDim + 16 * q;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) key[t] = *reinterpret_cast<const uint4*>(kp + t * 16 * kIndexDim);
+    };
+    load_keys();
+    if (seq != guess) {
+      page = a.block_table[static_cast<int64_t>(seq) * a.max_blocks + b];
+      load_keys();
+    }
+
+    float qa[16];
+    {
+      const uint32_t wv[8] = {qa0.x, qa0.y, qa0.z, qa0.w, qa1.x, qa1.y, qa1.z, qa1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        qa[2 * i] = __uint_as_float(wv[i] << 16);
+        qa[2 * i + 1] = __uint_as_float(wv[i] & 0xffff0000u);
+      }
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(qa[i]));
+    amax = xor_max(xor_max(amax, 16), 32);
+    const int e = f16_prescale_exp(amax);
+    half8_t A0, A1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      A0[i] = static_cast<half_t>(ldexpf(qa[i], e));
+      A1[i] = static_cast<half_t>(ldexpf(qa[8 + i], e));
+    }
+    // inverse pre-scale of the (row, head) that lane (n, q)'s result M = 4q + jj has
+    float inv[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) inv[jj] = ldexpf(1.0f, -__shfl(e, 4 * q + jj, 64));
 
     if constexpr (kFused) {
       // New tokens landing in this page: encode their keys here (the append runs
@@ -97,7 +179,7 @@ __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
       if (a.app.idx_new != nullptr) {
         for (int base = 0; base < a.app.n_new; base += 64) {
           const int i = base + lane;
-          const int64_t sl = i < a.app.n_new ? a.app.slot[i] : -1;
+          const int64_t sl = base == 0 ? slot0 : i < a.app.n_new ? a.app.slot[i] : -1;
           uint64_t hits = __ballot(sl >= 0 && sl / kPage == page);
           while (hits) {
             const int jj = __ffsll(static_cast<unsigned long long>(hits)) - 1;
@@ -112,52 +194,6 @@ __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
           }
         }
       }
-    }
-
-    // A operand: lane (m, q) holds query row-slot m / Hi, head m % Hi, dims
-    // 16q + 8ks .. +7, times 2^e (e per (row, head), from the amax over 64 dims).
-    const int m = n;
-    const int rs = m / kHi, hd = m % kHi;
-    float qa[16];
-    if (rs < nr) {
-      const uint16_t* qp = a.q_idx + (static_cast<int64_t>(r0 + rs) * kHi + hd) * kIndexDim + 16 * q;
-      const uint4 a0 = reinterpret_cast<const uint4*>(qp)[0], a1 = reinterpret_cast<const uint4*>(qp)[1];
-      const uint32_t wv[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        qa[2 * i] = __uint_as_float(wv[i] << 16);
-        qa[2 * i + 1] = __uint_as_float(wv[i] & 0xffff0000u);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) qa[i] = 0.0f;
-    }
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(qa[i]));
-    amax = xor_max(xor_max(amax, 16), 32);
-    const int e = f16_prescale_exp(amax);
-    half8_t A0, A1;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      A0[i] = static_cast<half_t>(ldexpf(qa[i], e));
-      A1[i] = static_cast<half_t>(ldexpf(qa[8 + i], e));
-    }
-    // After the MFMA, lane (n, q) holds M = 4q + jj; fetch the matching (row, head)
-    // weight and inverse pre-scale from the lane that owns that M.
-    float wj[4], inv[4];
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int mm = 4 * q + jj;
-      inv[jj] = ldexpf(1.0f, -__shfl(e, mm, 64));
-      const int rr = mm / kHi, hh = mm % kHi;
-      wj[jj] = rr < nr ? a.w[static_cast<int64_t>(r0 + rr) * kHi + hh] : 0.0f;
-    }
-    int rowslot[kRowsPerLane], pos[kRowsPerLane];
-#pragma unroll
-    for (int i = 0; i < kRowsPerLane; ++i) {
-      rowslot[i] = q * kRowsPerLane + i;
-      pos[i] = rowslot[i] < nr ? a.row_pos[r0 + rowslot[i]] : -1;
     }
 
     float best[kRowsPerLane];
@@ -233,6 +269,7 @@ ScoreArgs make_score_args(const msa_kv_pool_t* pool, const msa_step_t* step, con
   a.w = w;
   a.scores = block_scores;
   a.num_rows = step->num_rows;
+  a.num_seqs = step->num_seqs;
   a.max_blocks = step->max_blocks_per_seq;
   a.score_wgs_x = (step->max_blocks_per_seq + kWaves - 1) / kWaves;
   return a;

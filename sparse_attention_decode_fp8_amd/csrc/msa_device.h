@@ -21,6 +21,8 @@ typedef half_t half2_t __attribute__((ext_vector_type(2)));
 typedef half_t half4_t __attribute__((ext_vector_type(4)));
 typedef half_t half8_t __attribute__((ext_vector_type(8)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t uint2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t uint4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 
@@ -94,28 +96,30 @@ __device__ __forceinline__ float xor_add(float v, int mask) {
   return v + __shfl_xor(v, mask, 64);
 }
 
-// Agent-scope relaxed atomic accesses (64-bit halves of a vector). They are performed at
-// the device's coherence point, so workgroups on different XCDs (each with its own L2)
-// see one another's values without cache writeback or invalidation. Used for the split
-// partials that the last-arriving workgroup of a launch merges.
-__device__ __forceinline__ void store_agent(float* p, float4_t v) {
-  uint64_t* q = reinterpret_cast<uint64_t*>(p);
-  __hip_atomic_store(q, __builtin_bit_cast(uint64_t, float2_t{v[0], v[1]}), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(q + 1, __builtin_bit_cast(uint64_t, float2_t{v[2], v[3]}), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
+// Agent-scope coherent 16- and 8-byte accesses through a buffer resource: the sc1
+// cache-policy bit makes them coherent across the XCDs (each has its own L2), so one
+// workgroup can read what another wrote in the same launch once the writer's wait on
+// the vector memory counter and a device-scope atomic order the two. Offsets are in
+// bytes from the resource's base; the range is [base, base + bytes).
+constexpr int kCoherentPolicy = 16;   // sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
 }
-__device__ __forceinline__ void store_agent(float* p, float2_t v) {
-  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off, float4_t v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(uint4_t, v), r, static_cast<int>(off), 0,
+                                         kCoherentPolicy);
 }
-__device__ __forceinline__ float2_t load_agent2(const float* p) {
-  return __builtin_bit_cast(float2_t, __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
-                                                        __HIP_MEMORY_SCOPE_AGENT));
+__device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off, float2_t v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(uint2_t, v), r, static_cast<int>(off), 0,
+                                        kCoherentPolicy);
 }
-__device__ __forceinline__ float4_t load_agent4(const float* p) {
-  const float2_t a = load_agent2(p), b = load_agent2(p + 2);
-  return float4_t{a[0], a[1], b[0], b[1]};
+__device__ __forceinline__ float4_t load_coherent4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0,
+                                                                          kCoherentPolicy));
+}
+__device__ __forceinline__ float2_t load_coherent2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float2_t, __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(off), 0,
+                                                                         kCoherentPolicy));
 }
 
 // Order-preserving map of fp32 onto uint32 (larger float -> larger key).

@@ -32,8 +32,8 @@ inline msa_status_t check_step(const msa_step_t* step) {
   if (step->num_seqs < 0 || step->num_rows < 0 || step->max_blocks_per_seq <= 0)
     return MSA_ERR_INVALID_ARG;
   if (step->max_blocks_per_seq > MSA_MAX_BLOCKS) return MSA_ERR_UNSUPPORTED;
-  if (step->num_rows > 0 &&
-      (step->block_table == nullptr || step->row_seq == nullptr || step->row_pos == nullptr))
+  if (step->num_rows > 0 && (step->num_seqs == 0 || step->block_table == nullptr ||
+                             step->row_seq == nullptr || step->row_pos == nullptr))
     return MSA_ERR_INVALID_ARG;
   return MSA_OK;
 }

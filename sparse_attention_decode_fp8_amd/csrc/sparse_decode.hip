@@ -60,7 +60,7 @@ struct DecodeArgs {
   const int32_t* row_seq;
   const int32_t* row_pos;
   int max_blocks;
-  int num_rows;
+  int num_rows, num_seqs;
   const uint16_t* q;
   const int32_t* sel;         // selection table (table variants)
   const int32_t* sel_pages;   // may be null: translate through the block table
@@ -205,26 +205,37 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
   const uint4* qp = reinterpret_cast<const uint4*>(
       a.q + (static_cast<int64_t>(r) * hq + kHeadsPerKv * g + n) * kHeadDim + 32 * q);
   uint4 qraw[4];
+  auto load_q = [&]() {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) qraw[i] = qp[i];
+    for (int i = 0; i < 4; ++i) qraw[i] = qp[i];
+  };
+  if constexpr (!kSelect) load_q();
 
   // Selection table in a register: lane e < k holds entry e (block) and its page.
   int selv = -1, pagev = -1;
   if constexpr (kSelect) {
     const int nb = min(pos / kPage + 1, a.max_blocks);
-    const int32_t* bt = a.block_table + static_cast<int64_t>(a.row_seq[r]) * a.max_blocks;
+    const int seq = a.row_seq[r];
+    const int32_t* bt = a.block_table + static_cast<int64_t>(seq) * a.max_blocks;
     const float* srow = a.scores + static_cast<int64_t>(r) * a.max_blocks;
     if (a.max_blocks - a.n_init - a.n_local <= kWaveSelectMax) {
-      // wave 0 selects (the other waves would only contend for the scalar unit) and
-      // hands the table over through LDS
+      // Wave 0 selects (the other waves would only contend for the scalar unit) and
+      // hands the table over through LDS. Its block-table reads go out with the score
+      // reads, from the row of the request r belongs to when every request has the
+      // same number of rows; the pages are read again if row_seq says otherwise.
       if (wave == 0) {
-        wave_select(srow, bt, a.max_blocks, nb, a.k, a.n_init, a.n_local, wsel, selv, pagev);
+        const int guess = static_cast<int>(static_cast<int64_t>(r) * a.num_seqs / a.num_rows);
+        const int32_t* btg = a.block_table + static_cast<int64_t>(guess) * a.max_blocks;
+        wave_select(srow, btg, a.max_blocks, nb, a.k, a.n_init, a.n_local, wsel, selv, pagev);
+        if (seq != guess) pagev = selv >= 0 ? bt[selv] : -1;
         if (lane < MSA_MAX_TOPK) { lsel[lane] = selv; lpage[lane] = pagev; }
       }
+      load_q();   // after the selection's reads, which are on the critical path
       __syncthreads();
       selv = lane < MSA_MAX_TOPK ? lsel[lane] : -1;
       pagev = lane < MSA_MAX_TOPK ? lpage[lane] : -1;
     } else {
+      load_q();
       block_select_row<false, 64 * kW>(srow, nb, a.k, a.n_init, a.n_local, bt, lsel, nullptr,
                                        reinterpret_cast<uint32_t*>(dyn_lds), sm);
       __syncthreads();
@@ -369,6 +380,10 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
     if (q == 0) { mbuf[wave][n] = m_run; lbuf[wave][n] = l_tot; }
   }
   __syncthreads();
+  // this (row, KV head)'s partials: O [16 heads][S][128], (m, l) [16 heads][S][2]
+  const uint32_t o_bytes = 16u * a.num_splits * kHeadDim * 4, ml_bytes = 16u * a.num_splits * 8;
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.part_o + head0 * a.num_splits * kHeadDim, o_bytes);
+  const __amdgpu_buffer_rsrc_t rm = make_rsrc(a.part_ml + head0 * a.num_splits * 2, ml_bytes);
   for (int idx = threadIdx.x; idx < 16 * (kHeadDim / 4); idx += 64 * kW) {
     const int h = idx / (kHeadDim / 4), d4 = idx % (kHeadDim / 4);
     float M = -INFINITY;
@@ -385,12 +400,12 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
         l += wt * lbuf[w][h];
       }
     }
-    float* po = a.part_o + ((head0 + h) * a.num_splits + s) * kHeadDim + 4 * d4;
-    float* pm = a.part_ml + ((head0 + h) * a.num_splits + s) * 2;
     if constexpr (kCombine) {
-      store_agent(po, acc);
-      if (d4 == 0) store_agent(pm, float2_t{M, l});
+      store_coherent(ro, ((h * a.num_splits + s) * kHeadDim + 4 * d4) * 4u, acc);
+      if (d4 == 0) store_coherent(rm, (h * a.num_splits + s) * 8u, float2_t{M, l});
     } else {
+      float* po = a.part_o + ((head0 + h) * a.num_splits + s) * kHeadDim + 4 * d4;
+      float* pm = a.part_ml + ((head0 + h) * a.num_splits + s) * 2;
       *reinterpret_cast<float4_t*>(po) = acc;
       if (d4 == 0) {
         pm[0] = M;
@@ -400,9 +415,9 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
   }
   if constexpr (kCombine) {
     // ---- the last split of this (row, KV head) to finish merges all splits. The partials
-    // were written with agent-scope atomic stores; waiting for them before the counter
-    // update orders them before it, and the merging workgroup reads them with agent-scope
-    // atomic loads issued after it saw the count, wherever the workgroups ran.
+    // were written with agent-coherent stores; waiting for them before the counter
+    // update orders them before it, and the merging workgroup reads them with
+    // agent-coherent loads issued after it saw the count, wherever the workgroups ran.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -413,15 +428,13 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
     if (!s_last) return;
     for (int idx = threadIdx.x; idx < 16 * (kHeadDim / 4); idx += 64 * kW) {
       const int h = idx / (kHeadDim / 4), d4 = idx % (kHeadDim / 4);
-      const float* ml = a.part_ml + (head0 + h) * a.num_splits * 2;
-      const float* po = a.part_o + (head0 + h) * a.num_splits * kHeadDim + 4 * d4;
       float2_t mls[kMaxCombineSplits];
       float4_t ot[kMaxCombineSplits];
 #pragma unroll
       for (int t = 0; t < kMaxCombineSplits; ++t) {    // every load first, one wait
         if (t < a.num_splits) {
-          mls[t] = load_agent2(ml + 2 * t);
-          ot[t] = load_agent4(po + static_cast<int64_t>(t) * kHeadDim);
+          mls[t] = load_coherent2(rm, (h * a.num_splits + t) * 8u);
+          ot[t] = load_coherent4(ro, ((h * a.num_splits + t) * kHeadDim + 4 * d4) * 4u);
         }
       }
       float M = -INFINITY;
@@ -503,6 +516,7 @@ msa_status_t decode_entry(const msa_kv_pool_t* pool, const msa_step_t* step, int
   a.max_blocks = step->max_blocks_per_seq;
   a.q = static_cast<const uint16_t*>(q);
   a.num_rows = step->num_rows;
+  a.num_seqs = step->num_seqs;
   const int pairs = step->num_rows * pool->num_kv_heads;
   dim3 grid(a.num_splits, pairs);
 #define MSA_DECODE_DISPATCH(FMT)                                              \

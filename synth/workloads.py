@@ -235,6 +235,15 @@ def inject_ties(wl: Workload, n_tied: int, seed_tag: int = 3) -> Workload:
     return wl
 
 
+def keep_rows(wl: Workload, rows) -> Workload:
+    """The same workload with only the given query rows (request-major order kept):
+    requests then have different numbers of rows, or none."""
+    import dataclasses
+    rows = np.asarray(sorted(rows), dtype=np.int64)
+    return dataclasses.replace(wl, row_seq=wl.row_seq[rows], row_pos=wl.row_pos[rows], q=wl.q[rows],
+                               q_idx=wl.q_idx[rows], w=wl.w[rows])
+
+
 # --------------------------------------------------------------------------------
 # The five benchmark workloads and small parity workloads
 # --------------------------------------------------------------------------------

@@ -127,6 +127,11 @@ def test_validation_rejects_before_launch():
                                          8, 0, 1, P(16), P(16), None, P(16), None) == -2
     nullstep = L.MsaStep(1, 1, 8, None, None, None)
     assert L.LIB.msa_index_score(B(pool), B(nullstep), 4, P(16), P(16), P(16), None) == -1
+    # rows need at least one request
+    noseq = L.MsaStep(0, 1, 8, P(16), P(16), P(16))
+    assert L.LIB.msa_index_score(B(pool), B(noseq), 4, P(16), P(16), P(16), None) == -1
+    assert L.LIB.msa_select_topk(B(noseq), P(16), 4, 0, 1, P(16), None, None) == -1
+    assert L.LIB.msa_sparse_decode(B(pool), B(noseq), 32, P(16), P(16), None, 8, 0.1, 2, P(16), P(16), None) == -1
 
 
 def test_binding_rejects_host_tensors():

@@ -36,6 +36,17 @@ def test_max_topk(M, fmt, num_splits, fused):
     G.check_step_parity(M, wl, num_splits, fused)
 
 
+@pytest.mark.parametrize("fmt", [W.FMT_FP8, W.FMT_NVFP4])
+@pytest.mark.parametrize("fused", [True, False])
+def test_uneven_rows_per_request(M, fmt, fused):
+    # requests with 1, 3, 0, 2 and 3 query rows: the row -> request map is not uniform
+    full = W.small(fmt, [700, 2600, 900, 1300, 4000], 3, num_kv_heads=2, k=5, seed=54)
+    wl = W.keep_rows(full, [2, 3, 4, 5, 10, 11, 12, 13, 14])
+    assert list(wl.row_seq) == [0, 1, 1, 1, 3, 3, 4, 4, 4]
+    print("uneven rows", wl.name, "fused", fused, flush=True)
+    G.check_step_parity(M, wl, 2, fused)
+
+
 def test_nothing_to_do_leaves_outputs_untouched(M):
     wl = W.small(W.FMT_NVFP4, [300], 1, num_kv_heads=1, k=2, seed=53)
     pool = G.gpu_pool(M, wl)
