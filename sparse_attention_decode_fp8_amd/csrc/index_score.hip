@@ -39,7 +39,8 @@ struct ScoreArgs {
   const uint16_t* q_idx;
   const float* w;
   float* scores;
-  int num_rows, num_seqs, max_blocks;
+  int num_rows, max_blocks;
+  uint64_t seq_mul;   // seq_guess multiplier
   // fused launch only
   AppendArgs app;
   int k, n_init, n_local;
@@ -77,7 +78,7 @@ __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
   const bool in_rows = lane < 48 && rr >= 0 && rr < a.num_rows;
   const int seq_l = in_rows ? a.row_seq[rr] : -1;
   const int pos_l = in_rows && lane >= 32 ? a.row_pos[rr] : -1;
-  const int guess = static_cast<int>(static_cast<int64_t>(r0) * a.num_seqs / a.num_rows);
+  const int guess = seq_guess(r0, a.seq_mul);
   const int page_g = b < a.max_blocks ? a.block_table[static_cast<int64_t>(guess) * a.max_blocks + b] : -1;
   // fused launch: the first 64 new tokens' slots, so that matching them against the
   // page below waits for no further load
@@ -269,7 +270,7 @@ ScoreArgs make_score_args(const msa_kv_pool_t* pool, const msa_step_t* step, con
   a.w = w;
   a.scores = block_scores;
   a.num_rows = step->num_rows;
-  a.num_seqs = step->num_seqs;
+  a.seq_mul = seq_guess_mul(step->num_seqs, step->num_rows);
   a.max_blocks = step->max_blocks_per_seq;
   a.score_wgs_x = (step->max_blocks_per_seq + kWaves - 1) / kWaves;
   return a;

@@ -122,6 +122,12 @@ __device__ __forceinline__ float2_t load_coherent2(__amdgpu_buffer_rsrc_t r, uin
                                                                          kCoherentPolicy));
 }
 
+// Request a row belongs to when every request has the same number of rows (the
+// multiplier comes from seq_guess_mul on the host); callers check it against row_seq.
+__device__ __forceinline__ int seq_guess(int r, uint64_t mul) {
+  return static_cast<int>((static_cast<uint64_t>(r) * mul) >> 32);
+}
+
 // Order-preserving map of fp32 onto uint32 (larger float -> larger key).
 __device__ __forceinline__ uint32_t float_key(float f) {
   uint32_t u = __float_as_uint(f);

@@ -38,6 +38,16 @@ inline msa_status_t check_step(const msa_step_t* step) {
   return MSA_OK;
 }
 
+// Multiplier for the device-side guess of a row's request, r * num_seqs / num_rows,
+// as (r * mul) >> 32 with mul = ceil(2^32 * num_seqs / num_rows). For r < num_rows <=
+// 65535 this equals the exact floor quotient (the excess r * (ceil - exact) / 2^32 stays
+// below 1 / num_rows, the smallest nonzero distance to the next integer).
+inline uint64_t seq_guess_mul(int32_t num_seqs, int32_t num_rows) {
+  if (num_rows <= 0) return 0;
+  const uint64_t n = static_cast<uint64_t>(num_seqs) << 32;
+  return n / static_cast<uint64_t>(num_rows) + (n % static_cast<uint64_t>(num_rows) != 0);
+}
+
 inline msa_status_t launch_status() {
   return hipGetLastError() == hipSuccess ? MSA_OK : MSA_ERR_LAUNCH;
 }

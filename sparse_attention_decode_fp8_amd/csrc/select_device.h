@@ -156,26 +156,33 @@ namespace msa {
 // want-th largest key T is built bit by bit from the MSB (count of keys >= candidate via
 // ballot + popcount); keys above T are taken, and of the keys equal to T the ones with
 // the smallest block index (rank by mbcnt prefix counts). The scores and the block-table
-// row are read for every candidate slot inside the row's max_blocks (before the row's
-// length is known) so the two loads overlap. Returns entry e of the selection table and
-// its page in lane e (e < k), -1 padded. `scratch` is 128 ints of LDS private to the
-// calling wave. Every wave that runs it gets the same table.
+// row are read for every candidate slot inside the row's max_blocks before the row's
+// position (and so its length) is read, so all three loads overlap. Returns entry e of
+// the selection table and its page in lane e (e < k), -1 padded. `scratch` is 128 ints
+// of LDS private to the calling wave. Every wave that runs it gets the same table.
 template <int kR>
 __device__ __forceinline__ void wave_select_table(const float* srow, const int32_t* bt, int max_blocks,
-                                                  int nb, int k, int n_init, int n_local,
+                                                  const int32_t* row_pos, int k, int n_init, int n_local,
                                                   int* scratch, int& sel_out, int& page_out) {
   const int lane = threadIdx.x & 63;
-  const int lo = n_init, C = nb - n_init - n_local, want = k - n_init - n_local;
-  uint32_t key[kR];
+  const int lo = n_init, want = k - n_init - n_local;
+  float sv[kR];
   int32_t pg[kR];
 #pragma unroll
   for (int i = 0; i < kR; ++i) {
     const int c = lane * kR + i;
     const bool in_row = lo + c < max_blocks;
-    const float v = in_row ? srow[lo + c] : 0.0f;
+    sv[i] = in_row ? srow[lo + c] : 0.0f;
     pg[i] = in_row ? bt[lo + c] : -1;
-    key[i] = c < C ? float_key(v) : 0u;                    // 0 is below every real key
   }
+  // The row's position is read only now, so its load queues behind the score loads
+  // instead of holding them back.
+  asm volatile("" ::: "memory");
+  const int nb = min(*row_pos / MSA_PAGE_SIZE + 1, max_blocks);
+  const int C = nb - n_init - n_local;
+  uint32_t key[kR];
+#pragma unroll
+  for (int i = 0; i < kR; ++i) key[i] = lane * kR + i < C ? float_key(sv[i]) : 0u;   // 0: below every real key
   if (nb <= k) {                                           // identity table
     sel_out = lane < nb ? lane : -1;
     page_out = lane < nb ? bt[lane] : -1;
@@ -250,13 +257,13 @@ constexpr int kWaveSelectMax = 64 * 32;
 // Dispatch on the largest candidate count the row table allows (known before the row's
 // length is): kR = 4, 8, 16 or 32 keys per lane.
 __device__ __forceinline__ void wave_select(const float* srow, const int32_t* bt, int max_blocks,
-                                            int nb, int k, int n_init, int n_local, int* scratch,
-                                            int& sel, int& page) {
+                                            const int32_t* row_pos, int k, int n_init, int n_local,
+                                            int* scratch, int& sel, int& page) {
   const int C = max_blocks - n_init - n_local;
-  if (C <= 256) wave_select_table<4>(srow, bt, max_blocks, nb, k, n_init, n_local, scratch, sel, page);
-  else if (C <= 512) wave_select_table<8>(srow, bt, max_blocks, nb, k, n_init, n_local, scratch, sel, page);
-  else if (C <= 1024) wave_select_table<16>(srow, bt, max_blocks, nb, k, n_init, n_local, scratch, sel, page);
-  else wave_select_table<32>(srow, bt, max_blocks, nb, k, n_init, n_local, scratch, sel, page);
+  if (C <= 256) wave_select_table<4>(srow, bt, max_blocks, row_pos, k, n_init, n_local, scratch, sel, page);
+  else if (C <= 512) wave_select_table<8>(srow, bt, max_blocks, row_pos, k, n_init, n_local, scratch, sel, page);
+  else if (C <= 1024) wave_select_table<16>(srow, bt, max_blocks, row_pos, k, n_init, n_local, scratch, sel, page);
+  else wave_select_table<32>(srow, bt, max_blocks, row_pos, k, n_init, n_local, scratch, sel, page);
 }
 
 }  // namespace msa

@@ -60,7 +60,8 @@ struct DecodeArgs {
   const int32_t* row_seq;
   const int32_t* row_pos;
   int max_blocks;
-  int num_rows, num_seqs;
+  int num_rows;
+  uint64_t seq_mul;           // seq_guess multiplier
   const uint16_t* q;
   const int32_t* sel;         // selection table (table variants)
   const int32_t* sel_pages;   // may be null: translate through the block table
@@ -191,13 +192,14 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
   __shared__ int s_last;
   __shared__ int32_t lsel[kSelect ? MSA_MAX_TOPK : 1], lpage[kSelect ? MSA_MAX_TOPK : 1];
   __shared__ int wsel[kSelect ? 128 : 1];
+  __shared__ half8_t qlds[kSelect ? 4 : 1][64];   // selecting variant: the converted Q operand
+  __shared__ float qcs[kSelect ? 64 : 1];
   __shared__ SelectSmem sm;
   const int pair = blockIdx.y, s = blockIdx.x;   // (row, KV head) pair, split
   if (pair >= a.num_rows * a.hkv) return;
   const int r = pair / a.hkv, g = pair % a.hkv;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
   const int hq = a.hkv * kHeadsPerKv;
-  const int pos = a.row_pos[r];
   const int lo = (s * a.k) / a.num_splits, hi = ((s + 1) * a.k) / a.num_splits;
   const int n_items = (hi - lo) * 4;   // (entry, 32-token chunk) pairs of this split
 
@@ -209,63 +211,11 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) qraw[i] = qp[i];
   };
-  if constexpr (!kSelect) load_q();
-
-  // Selection table in a register: lane e < k holds entry e (block) and its page.
-  int selv = -1, pagev = -1;
-  if constexpr (kSelect) {
-    const int nb = min(pos / kPage + 1, a.max_blocks);
-    const int seq = a.row_seq[r];
-    const int32_t* bt = a.block_table + static_cast<int64_t>(seq) * a.max_blocks;
-    const float* srow = a.scores + static_cast<int64_t>(r) * a.max_blocks;
-    if (a.max_blocks - a.n_init - a.n_local <= kWaveSelectMax) {
-      // Wave 0 selects (the other waves would only contend for the scalar unit) and
-      // hands the table over through LDS. Its block-table reads go out with the score
-      // reads, from the row of the request r belongs to when every request has the
-      // same number of rows; the pages are read again if row_seq says otherwise.
-      if (wave == 0) {
-        const int guess = static_cast<int>(static_cast<int64_t>(r) * a.num_seqs / a.num_rows);
-        const int32_t* btg = a.block_table + static_cast<int64_t>(guess) * a.max_blocks;
-        wave_select(srow, btg, a.max_blocks, nb, a.k, a.n_init, a.n_local, wsel, selv, pagev);
-        if (seq != guess) pagev = selv >= 0 ? bt[selv] : -1;
-        if (lane < MSA_MAX_TOPK) { lsel[lane] = selv; lpage[lane] = pagev; }
-      }
-      load_q();   // after the selection's reads, which are on the critical path
-      __syncthreads();
-      selv = lane < MSA_MAX_TOPK ? lsel[lane] : -1;
-      pagev = lane < MSA_MAX_TOPK ? lpage[lane] : -1;
-    } else {
-      load_q();
-      block_select_row<false, 64 * kW>(srow, nb, a.k, a.n_init, a.n_local, bt, lsel, nullptr,
-                                       reinterpret_cast<uint32_t*>(dyn_lds), sm);
-      __syncthreads();
-      selv = lane < a.k ? lsel[lane] : -1;
-      pagev = selv >= 0 ? bt[selv] : -1;
-    }
-    if (lane >= a.k) selv = pagev = -1;
-    if (s == 0 && g == 0 && wave == 0 && a.sel_out != nullptr && lane < a.k) {
-      a.sel_out[static_cast<int64_t>(r) * a.k + lane] = selv;
-      if (a.sel_pages_out) a.sel_pages_out[static_cast<int64_t>(r) * a.k + lane] = pagev;
-    }
-  }
-  auto lookup = [&](int e, int& b, int64_t& page) {
-    if constexpr (kSelect) {
-      b = __shfl(selv, e, 64);
-      page = __shfl(pagev, e, 64);
-    } else {
-      b = a.sel[static_cast<int64_t>(r) * a.k + e];
-      page = b < 0 ? 0
-          : a.sel_pages ? a.sel_pages[static_cast<int64_t>(r) * a.k + e]
-                        : a.block_table[static_cast<int64_t>(a.row_seq[r]) * a.max_blocks + b];
-    }
-  };
-
-  Round<kFmt, kItems> rd;
-  load_round<kFmt, kW, kItems>(rd, a, lookup, 0, wave, g, pos, lo, n_items, n, q);
-
+  // Exact fp16 operand: each head is scaled by a power of two (folded into the logit
+  // scale) that brings its bf16 values into fp16's normal range.
   half8_t Qop[4];
   float cscale;
-  {
+  auto convert_q = [&]() {
     float qf[32];
     float amax = 0.0f;
 #pragma unroll
@@ -287,7 +237,86 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
       for (int i = 0; i < 8; ++i) Qop[j][i] = static_cast<half_t>(ldexpf(qf[8 * j + i], e));
     cscale = ldexpf(a.softmax_scale * kLog2e, -e);
     if constexpr (kFmt == MSA_KV_NVFP4) cscale *= a.k_t;
+  };
+  // Selecting variant: Q is the same for every wave of the workgroup, so wave 1 loads
+  // and converts it while wave 0 selects, and hands it over through LDS.
+  auto q_to_lds = [&]() {
+    load_q();
+    convert_q();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) qlds[j][lane] = Qop[j];
+    qcs[lane] = cscale;
+  };
+  auto q_from_lds = [&]() {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) Qop[j] = qlds[j][lane];
+    cscale = qcs[lane];
+  };
+  int pos;
+  if constexpr (!kSelect) {
+    pos = a.row_pos[r];
+    load_q();
   }
+
+  // Selection table in a register: lane e < k holds entry e (block) and its page.
+  int selv = -1, pagev = -1;
+  if constexpr (kSelect) {
+    const float* srow = a.scores + static_cast<int64_t>(r) * a.max_blocks;
+    if (a.max_blocks - a.n_init - a.n_local <= kWaveSelectMax) {
+      // Wave 0 selects (the other waves would only contend for the scalar unit) and
+      // hands the table over through LDS. Its block-table reads go out with the score
+      // reads, from the row of the request r belongs to when every request has the
+      // same number of rows; the pages are read again if row_seq says otherwise.
+      if (wave == 0) {
+        const int guess = seq_guess(r, a.seq_mul);
+        const int32_t* btg = a.block_table + static_cast<int64_t>(guess) * a.max_blocks;
+        wave_select(srow, btg, a.max_blocks, a.row_pos + r, a.k, a.n_init, a.n_local, wsel, selv, pagev);
+        const int seq = a.row_seq[r];
+        if (seq != guess) {
+          const int32_t* bt = a.block_table + static_cast<int64_t>(seq) * a.max_blocks;
+          pagev = selv >= 0 ? bt[selv] : -1;
+        }
+        if (lane < MSA_MAX_TOPK) { lsel[lane] = selv; lpage[lane] = pagev; }
+      }
+      if (wave == 1) q_to_lds();
+      pos = a.row_pos[r];
+      __syncthreads();
+      selv = lane < MSA_MAX_TOPK ? lsel[lane] : -1;
+      pagev = lane < MSA_MAX_TOPK ? lpage[lane] : -1;
+    } else {
+      if (wave == 1) q_to_lds();
+      pos = a.row_pos[r];
+      const int nb = min(pos / kPage + 1, a.max_blocks);
+      const int32_t* bt = a.block_table + static_cast<int64_t>(a.row_seq[r]) * a.max_blocks;
+      block_select_row<false, 64 * kW>(srow, nb, a.k, a.n_init, a.n_local, bt, lsel, nullptr,
+                                       reinterpret_cast<uint32_t*>(dyn_lds), sm);
+      __syncthreads();
+      selv = lane < a.k ? lsel[lane] : -1;
+      pagev = selv >= 0 ? bt[selv] : -1;
+    }
+    q_from_lds();
+    if (lane >= a.k) selv = pagev = -1;
+    if (s == 0 && g == 0 && wave == 0 && a.sel_out != nullptr && lane < a.k) {
+      a.sel_out[static_cast<int64_t>(r) * a.k + lane] = selv;
+      if (a.sel_pages_out) a.sel_pages_out[static_cast<int64_t>(r) * a.k + lane] = pagev;
+    }
+  }
+  auto lookup = [&](int e, int& b, int64_t& page) {
+    if constexpr (kSelect) {
+      b = __shfl(selv, e, 64);
+      page = __shfl(pagev, e, 64);
+    } else {
+      b = a.sel[static_cast<int64_t>(r) * a.k + e];
+      page = b < 0 ? 0
+          : a.sel_pages ? a.sel_pages[static_cast<int64_t>(r) * a.k + e]
+                        : a.block_table[static_cast<int64_t>(a.row_seq[r]) * a.max_blocks + b];
+    }
+  };
+
+  Round<kFmt, kItems> rd;
+  load_round<kFmt, kW, kItems>(rd, a, lookup, 0, wave, g, pos, lo, n_items, n, q);
+
+  if constexpr (!kSelect) convert_q();
 
   float m_run = -INFINITY, l_run = 0.0f, v_cur = 0.0f;   // v_cur: FP8 page scale O is kept in
   float4_t O[8];
@@ -516,7 +545,7 @@ msa_status_t decode_entry(const msa_kv_pool_t* pool, const msa_step_t* step, int
   a.max_blocks = step->max_blocks_per_seq;
   a.q = static_cast<const uint16_t*>(q);
   a.num_rows = step->num_rows;
-  a.num_seqs = step->num_seqs;
+  a.seq_mul = seq_guess_mul(step->num_seqs, step->num_rows);
   const int pairs = step->num_rows * pool->num_kv_heads;
   dim3 grid(a.num_splits, pairs);
 #define MSA_DECODE_DISPATCH(FMT)                                              \
