@@ -48,6 +48,7 @@ struct ScoreArgs {
   int32_t* sel_pages;
   int32_t* counters;
   int score_wgs_x;   // workgroups along x that score blocks
+  int append_row;    // fused launch: 1 if grid row 0 holds the append workgroups
 };
 
 template <int kHi, int kFmt, bool kFused>
@@ -58,14 +59,16 @@ __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
   constexpr int kRowsPerGroup = 16 / kHi;
   constexpr int kRowsPerLane = 4 / kHi;
   if constexpr (kFused) {
-    if (static_cast<int>(blockIdx.y) == a.num_rows) {     // append workgroups
+    // The append workgroups form grid row 0 (when there is anything to append), so
+    // they are dispatched first and run alongside the scoring.
+    if (a.append_row && blockIdx.y == 0) {
       const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
       if (gid < static_cast<int64_t>(a.app.n_new) * a.app.groups_per_tok) append_group<kFmt>(a.app, gid);
       return;
     }
     if (static_cast<int>(blockIdx.x) >= a.score_wgs_x) return;
   }
-  const int r0 = blockIdx.y;
+  const int r0 = static_cast<int>(blockIdx.y) - a.append_row;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, q = lane >> 4;
   const int b = blockIdx.x * kWaves + wave;
@@ -228,7 +231,9 @@ __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
       v = xor_max(v, 8);
       if (n == 0 && rowslot[i] < nr) {
         float* dst = a.scores + static_cast<int64_t>(r0 + rowslot[i]) * a.max_blocks + b;
-        if constexpr (kFused) __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // write-through only when this launch's last workgroup selects from the scores;
+        // a later kernel sees plain stores after the kernel boundary
+        if (kFused && a.counters != nullptr) __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         else *dst = v;
       }
     }
@@ -346,8 +351,8 @@ extern "C" msa_status_t msa_append_score_select(
   a.sel_pages = sel_pages;
   a.counters = counters;
   const int64_t app_wgs = (static_cast<int64_t>(n_new) * a.app.groups_per_tok + 255) / 256;
-  dim3 grid(static_cast<unsigned>(std::max<int64_t>(a.score_wgs_x, app_wgs)),
-            step->num_rows + (n_new > 0 ? 1 : 0));
+  a.append_row = n_new > 0 ? 1 : 0;
+  dim3 grid(static_cast<unsigned>(std::max<int64_t>(a.score_wgs_x, app_wgs)), step->num_rows + a.append_row);
   const size_t lds = sel ? static_cast<size_t>(step->max_blocks_per_seq) * sizeof(uint32_t) : 0;
   return launch_score<true>(a, pool->fmt, n_idx_heads, grid, lds, static_cast<hipStream_t>(stream));
 }

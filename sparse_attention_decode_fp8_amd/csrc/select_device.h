@@ -192,11 +192,23 @@ __device__ __forceinline__ void wave_select_table(const float* srow, const int32
   if (lane < n_init) { out = lane; opg = bt[lane]; }
   if (lane >= k - n_local && lane < k) { out = nb - k + lane; opg = bt[nb - k + lane]; }
   if (want > 0) {
+    // The bits every candidate shares are the threshold's too: start below them.
+    uint32_t k_or = 0u, k_and = ~0u;
+#pragma unroll
+    for (int i = 0; i < kR; ++i)
+      if (key[i] != 0u) { k_or |= key[i]; k_and &= key[i]; }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      k_or |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(k_or), m, 64));
+      k_and &= static_cast<uint32_t>(__shfl_xor(static_cast<int>(k_and), m, 64));
+    }
+    const uint32_t diff = k_or ^ k_and;
+    const int top = diff != 0u ? 31 - __builtin_clz(diff) : -1;   // highest differing bit
     // T ends as a threshold with count(key >= T) >= want and, unless some count hit
     // want exactly (then the keys >= T are the selection and the search stops early),
-    // as the exact want-th largest key.
-    uint32_t T = 0;
-    for (int bit = 31; bit >= 0; --bit) {
+    // as the exact want-th largest key. It starts as the shared prefix (<= every key).
+    uint32_t T = top < 0 ? k_and : top >= 31 ? 0u : (k_and & ~((2u << top) - 1u));
+    for (int bit = top; bit >= 0; --bit) {
       const uint32_t cand = T | (1u << bit);
       int cnt = 0;
 #pragma unroll

@@ -400,8 +400,8 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
   float oscale;
   if constexpr (kFmt == MSA_KV_NVFP4) oscale = a.v_t; else oscale = v_cur;
   const int64_t head0 = static_cast<int64_t>(r) * hq + kHeadsPerKv * g;
-  __syncthreads();                                     // every wave is done with its V buffer
   {
+    // each wave's O tile goes to its own V buffer, which only it used: no barrier first
     float* ob = reinterpret_cast<float*>(dyn_lds + wave * kVBufBytes);   // [16 heads][kORowFloats]
 #pragma unroll
     for (int d = 0; d < 8; ++d)
