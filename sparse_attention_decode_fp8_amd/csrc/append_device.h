@@ -37,16 +37,25 @@ __device__ __forceinline__ void load16_bf16(const uint16_t* src, float x[16]) {
   }
 }
 
-// 16 bf16 values -> 16 saturating E4M3 codes (no scale), packed little-endian.
-__device__ __forceinline__ uint4 encode_index16(const uint16_t* src) {
+// 16 bf16 values (as loaded: two 16-byte words) -> 16 saturating E4M3 codes (no
+// scale), packed little-endian.
+__device__ __forceinline__ uint4 encode_index16_bits(uint4 a, uint4 b) {
+  const uint32_t wv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
   float x[16];
-  load16_bf16(src, x);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    x[2 * i] = __uint_as_float(wv[i] << 16);
+    x[2 * i + 1] = __uint_as_float(wv[i] & 0xffff0000u);
+  }
   uint32_t w[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    w[i] = f32_to_e4m3_sat(x[4 * i]) | (f32_to_e4m3_sat(x[4 * i + 1]) << 8) |
-           (f32_to_e4m3_sat(x[4 * i + 2]) << 16) | (f32_to_e4m3_sat(x[4 * i + 3]) << 24);
+  for (int i = 0; i < 4; ++i) w[i] = f32x4_to_e4m3_sat(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
   return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__device__ __forceinline__ uint4 encode_index16(const uint16_t* src) {
+  const uint4* p = reinterpret_cast<const uint4*>(src);
+  return encode_index16_bits(p[0], p[1]);
 }
 
 // Encode group `gid` (token gid / groups_per_tok) of the new tokens into the pool.
@@ -102,8 +111,7 @@ __device__ __forceinline__ void append_group(const AppendArgs& a, int64_t gid) {
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      w[i] = f32_to_e4m3_sat(x[4 * i] / s) | (f32_to_e4m3_sat(x[4 * i + 1] / s) << 8) |
-             (f32_to_e4m3_sat(x[4 * i + 2] / s) << 16) | (f32_to_e4m3_sat(x[4 * i + 3] / s) << 24);
+      w[i] = f32x4_to_e4m3_sat(x[4 * i] / s, x[4 * i + 1] / s, x[4 * i + 2] / s, x[4 * i + 3] / s);
     uint8_t* codes = is_v ? a.v_codes : a.k_codes;
     *reinterpret_cast<uint4*>(codes + row * kHeadDim + 16 * g) = make_uint4(w[0], w[1], w[2], w[3]);
   }

@@ -146,11 +146,34 @@ __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
 #pragma unroll
       for (int t = 0; t < 8; ++t) key[t] = *reinterpret_cast<const uint4*>(kp + t * 16 * kIndexDim);
     };
-    load_keys();
-    if (seq != guess) {
-      page = a.block_table[static_cast<int64_t>(seq) * a.max_blocks + b];
-      load_keys();
+    if (seq != guess) page = a.block_table[static_cast<int64_t>(seq) * a.max_blocks + b];
+    // New tokens landing in this page (fused launch): their keys are encoded here from
+    // the bf16 source instead of waiting for the append. The first one's source is
+    // read together with the page's keys and its code replaces the stale key as the
+    // operand is formed; any further ones (several new tokens in one page, or more than
+    // 64 new tokens) overwrite the key registers afterwards.
+    int pt = -1;                                   // token row (0..7) this lane patches
+    uint4 pv = make_uint4(0u, 0u, 0u, 0u), pv1 = pv;
+    bool patch_more = false;
+    if constexpr (kFused) {
+      if (a.app.idx_new != nullptr) {
+        const uint64_t h0 = __ballot(slot0 >= 0 && slot0 / kPage == page);
+        patch_more = a.app.n_new > 64 || (h0 & (h0 - 1)) != 0;
+        if (h0 != 0) {
+          const int first = __ffsll(static_cast<unsigned long long>(h0)) - 1;
+          const int off0 = __shfl(static_cast<int>(slot0 % kPage), first, 64);
+          if ((off0 & 15) == n) {
+            const uint4* src = reinterpret_cast<const uint4*>(
+                a.app.idx_new + static_cast<int64_t>(first) * kIndexDim + 16 * q);
+            pv = src[0];
+            pv1 = src[1];
+            pt = off0 >> 4;
+          }
+        }
+      }
     }
+    load_keys();
+    if (pt >= 0) pv = encode_index16_bits(pv, pv1);
 
     float qa[16];
     {
@@ -180,11 +203,12 @@ __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
     if constexpr (kFused) {
       // New tokens landing in this page: encode their keys here (the append runs
       // concurrently in other workgroups).
-      if (a.app.idx_new != nullptr) {
+      if (patch_more) {
         for (int base = 0; base < a.app.n_new; base += 64) {
           const int i = base + lane;
           const int64_t sl = base == 0 ? slot0 : i < a.app.n_new ? a.app.slot[i] : -1;
           uint64_t hits = __ballot(sl >= 0 && sl / kPage == page);
+          if (base == 0) hits &= hits - 1;         // the first one is patched at the operand
           while (hits) {
             const int jj = __ffsll(static_cast<unsigned long long>(hits)) - 1;
             hits &= hits - 1;
@@ -205,8 +229,9 @@ __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
     for (int i = 0; i < kRowsPerLane; ++i) best[i] = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const half8_t B0 = e4m3x8_to_f16(key[t].x, key[t].y);
-      const half8_t B1 = e4m3x8_to_f16(key[t].z, key[t].w);
+      const uint4 kt = t == pt ? pv : key[t];
+      const half8_t B0 = e4m3x8_to_f16(kt.x, kt.y);
+      const half8_t B1 = e4m3x8_to_f16(kt.z, kt.w);
       float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
       acc = mfma16x16x32(A0, B0, acc);
       acc = mfma16x16x32(A1, B1, acc);

@@ -135,26 +135,18 @@ __device__ __forceinline__ uint32_t float_key(float f) {
 }
 
 // ---------------------------------------------------------------- encoders
-// Saturating round-to-nearest-even fp32 -> OCP E4M3FN. Magnitudes >= 448 give 448;
-// the sign bit follows the input's sign bit.
+// Saturating round-to-nearest-even fp32 -> OCP E4M3 (largest finite 448). The input is
+// clamped to +-448 first, so the hardware conversion (which rounds to nearest even)
+// never overflows; every magnitude above 448 becomes 448. The sign of zero is kept.
+__device__ __forceinline__ float e4m3_clamp(float x) { return __builtin_amdgcn_fmed3f(x, -448.0f, 448.0f); }
 __device__ __forceinline__ uint32_t f32_to_e4m3_sat(float x) {
-  uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
-  float a = fabsf(x);
-  uint32_t mag;
-  if (!(a < 448.0f)) {
-    mag = 0x7eu;
-  } else if (a < 0.015625f) {               // below 2^-6: grid of m * 2^-9, m = 0..8
-    mag = static_cast<uint32_t>(rintf(a * 512.0f));
-  } else {
-    uint32_t u = __float_as_uint(a);
-    uint32_t e = (u >> 23) - 120u;           // biased E4M3 exponent 1..15
-    uint32_t man = u & 0x7fffffu;
-    uint32_t r = man >> 20, rem = man & 0xfffffu;
-    if (rem > 0x80000u || (rem == 0x80000u && (r & 1u))) ++r;
-    mag = (e << 3) + r;                      // r == 8 carries into the exponent
-    if (mag > 0x7eu) mag = 0x7eu;
-  }
-  return sign | mag;
+  const float c = e4m3_clamp(x);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false)) & 0xffu;
+}
+// Four values -> four E4M3 codes, first value in the low byte.
+__device__ __forceinline__ uint32_t f32x4_to_e4m3_sat(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(a), e4m3_clamp(b), 0, false);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(c), e4m3_clamp(d), lo, true));
 }
 
 // Saturating round-to-nearest-even fp32 -> E2M1 (sign bit 3). Grid
