@@ -89,6 +89,31 @@ __device__ __forceinline__ int f16_prescale_exp(float amax) {
   return 15 - ex;
 }
 
+// Wave-wide OR / AND of a 32-bit value with DPP moves (row shifts 1, 2, 4, 8 within each
+// row of 16 lanes, then the row broadcasts of lanes 15 and 31), read back from lane 63:
+// vector ALU only, no LDS round trips. Lanes a move has no source for keep the
+// identity (0 for OR, all ones for AND).
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+  int x = static_cast<int>(v);
+  x |= __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+  x |= __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+  x |= __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+  x |= __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+  x |= __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  x |= __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(x, 63));
+}
+__device__ __forceinline__ uint32_t wave_and(uint32_t v) {
+  int x = static_cast<int>(v);
+  x &= __builtin_amdgcn_update_dpp(-1, x, 0x111, 0xf, 0xf, false);
+  x &= __builtin_amdgcn_update_dpp(-1, x, 0x112, 0xf, 0xf, false);
+  x &= __builtin_amdgcn_update_dpp(-1, x, 0x114, 0xf, 0xf, false);
+  x &= __builtin_amdgcn_update_dpp(-1, x, 0x118, 0xf, 0xf, false);
+  x &= __builtin_amdgcn_update_dpp(-1, x, 0x142, 0xa, 0xf, false);
+  x &= __builtin_amdgcn_update_dpp(-1, x, 0x143, 0xc, 0xf, false);
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(x, 63));
+}
+
 __device__ __forceinline__ float xor_max(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, 64));
 }

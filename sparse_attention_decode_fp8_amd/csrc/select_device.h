@@ -152,18 +152,22 @@ __device__ void block_select_row(const float* srow, int nb, int k, int n_init, i
 namespace msa {
 
 // Wave-level (64-lane) selection for one row, without barriers or LDS atomics. Lane L
-// holds candidates L*kR .. L*kR+kR-1 (block lo + c), so block order is lane-major. The
-// want-th largest key T is built bit by bit from the MSB (count of keys >= candidate via
-// ballot + popcount); keys above T are taken, and of the keys equal to T the ones with
-// the smallest block index (rank by mbcnt prefix counts). The scores and the block-table
-// row are read for every candidate slot inside the row's max_blocks before the row's
-// position (and so its length) is read, so all three loads overlap. Returns entry e of
-// the selection table and its page in lane e (e < k), -1 padded. `scratch` is 128 ints
-// of LDS private to the calling wave. Every wave that runs it gets the same table.
+// holds candidates L*kR .. L*kR+kR-1 (block lo + c), so block order is lane-major.
+//
+// The want-th largest key T is built two bits at a time from the highest bit in which
+// the candidates differ (three independent ballot + popcount counts per step). Keys
+// above T are taken, and of the keys equal to T the ones with the smallest block
+// index (rank by mbcnt prefix counts).
+//
+// The scores and the block-table row are read for every candidate slot inside the
+// row's max_blocks before the row's position (and so its length) is read, so all three
+// loads overlap. The table is written to LDS: entry e (block, and its page from `bt`)
+// at sel[e], pages[e] for e < 64, -1 past the k entries; the caller synchronises the
+// workgroup before reading it.
 template <int kR>
 __device__ __forceinline__ void wave_select_table(const float* srow, const int32_t* bt, int max_blocks,
                                                   const int32_t* row_pos, int k, int n_init, int n_local,
-                                                  int* scratch, int& sel_out, int& page_out) {
+                                                  int* sel, int* pages) {
   const int lane = threadIdx.x & 63;
   const int lo = n_init, want = k - n_init - n_local;
   float sv[kR];
@@ -175,6 +179,7 @@ __device__ __forceinline__ void wave_select_table(const float* srow, const int32
     sv[i] = in_row ? srow[lo + c] : 0.0f;
     pg[i] = in_row ? bt[lo + c] : -1;
   }
+  const int32_t pg_init = lane < n_init && lane < max_blocks ? bt[lane] : -1;   // blocks below lo
   // The row's position is read only now, so its load queues behind the score loads
   // instead of holding them back.
   asm volatile("" ::: "memory");
@@ -183,84 +188,105 @@ __device__ __forceinline__ void wave_select_table(const float* srow, const int32
   uint32_t key[kR];
 #pragma unroll
   for (int i = 0; i < kR; ++i) key[i] = lane * kR + i < C ? float_key(sv[i]) : 0u;   // 0: below every real key
+  // Pages come from the registers loaded above (block lo + c is in slot c), so writing
+  // the table never waits for another block-table read.
   if (nb <= k) {                                           // identity table
-    sel_out = lane < nb ? lane : -1;
-    page_out = lane < nb ? bt[lane] : -1;
+    if (lane < lo && lane < nb) { sel[lane] = lane; pages[lane] = pg_init; }
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+      const int b = lo + lane * kR + i;
+      if (b < nb) { sel[b] = b; pages[b] = pg[i]; }
+    }
+    if (lane >= nb) { sel[lane] = -1; pages[lane] = -1; }
     return;
   }
-  int out = -1, opg = -1;
-  if (lane < n_init) { out = lane; opg = bt[lane]; }
-  if (lane >= k - n_local && lane < k) { out = nb - k + lane; opg = bt[nb - k + lane]; }
-  if (want > 0) {
-    // The bits every candidate shares are the threshold's too: start below them.
-    uint32_t k_or = 0u, k_and = ~0u;
-#pragma unroll
-    for (int i = 0; i < kR; ++i)
-      if (key[i] != 0u) { k_or |= key[i]; k_and &= key[i]; }
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-      k_or |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(k_or), m, 64));
-      k_and &= static_cast<uint32_t>(__shfl_xor(static_cast<int>(k_and), m, 64));
-    }
-    const uint32_t diff = k_or ^ k_and;
-    const int top = diff != 0u ? 31 - __builtin_clz(diff) : -1;   // highest differing bit
-    // T ends as a threshold with count(key >= T) >= want and, unless some count hit
-    // want exactly (then the keys >= T are the selection and the search stops early),
-    // as the exact want-th largest key. It starts as the shared prefix (<= every key).
-    uint32_t T = top < 0 ? k_and : top >= 31 ? 0u : (k_and & ~((2u << top) - 1u));
-    for (int bit = top; bit >= 0; --bit) {
-      const uint32_t cand = T | (1u << bit);
-      int cnt = 0;
-#pragma unroll
-      for (int i = 0; i < kR; ++i) cnt += __popcll(__ballot(key[i] >= cand));
-      if (cnt >= want) {
-        T = cand;
-        if (cnt == want) break;
-      }
-    }
-    int gt = 0;
-#pragma unroll
-    for (int i = 0; i < kR; ++i) gt += __popcll(__ballot(key[i] > T));
-    const int need = want - gt;                            // keys equal to T to take
-    int tie_before = 0;
-#pragma unroll
-    for (int i = 0; i < kR; ++i) {
-      const uint64_t m = __ballot(key[i] == T);
-      tie_before += __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
-                                              __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
-    }
-    bool take[kR];
-    int tb = tie_before;
-#pragma unroll
-    for (int i = 0; i < kR; ++i) {
-      take[i] = key[i] > T || (key[i] == T && tb < need);
-      tb += key[i] == T;
-    }
-    int before = 0;
-#pragma unroll
-    for (int i = 0; i < kR; ++i) {
-      const uint64_t m = __ballot(take[i]);
-      before += __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
-                                          __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
-    }
-    int at = before;
-#pragma unroll
-    for (int i = 0; i < kR; ++i) {
-      if (take[i]) {
-        scratch[at] = lo + lane * kR + i;
-        scratch[64 + at] = pg[i];
-        ++at;
-      }
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (lane >= n_init && lane < n_init + want) {
-      out = scratch[lane - n_init];
-      opg = scratch[64 + lane - n_init];
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  // Forced entries and padding; the `want` entries in between come from the search.
+  // The last n_local blocks' pages are read now and written after the search, so that
+  // read overlaps it.
+  const int32_t pg_local = lane < n_local ? bt[nb - n_local + lane] : -1;
+  if (lane < n_init) { sel[lane] = lane; pages[lane] = pg_init; }
+  if (lane >= k) { sel[lane] = -1; pages[lane] = -1; }
+  auto write_local = [&]() {
+    if (lane < n_local) { sel[k - n_local + lane] = nb - n_local + lane; pages[k - n_local + lane] = pg_local; }
+  };
+  if (want == 0) {
+    write_local();
+    return;
   }
-  sel_out = out;
-  page_out = opg;
+
+  // The bits every candidate shares are the threshold's too: start below them.
+  uint32_t k_or = 0u, k_and = ~0u;
+#pragma unroll
+  for (int i = 0; i < kR; ++i)
+    if (key[i] != 0u) { k_or |= key[i]; k_and &= key[i]; }
+  k_or = wave_or(k_or);                          // wave-uniform (scalar) from here
+  k_and = wave_and(k_and);
+  const uint32_t diff = k_or ^ k_and;
+  const int top = diff != 0u ? 31 - __builtin_clz(diff) : -1;   // highest differing bit
+  // T keeps count(key >= T) >= want. It starts as the shared prefix (<= every key) and
+  // ends as the exact want-th largest key or, if some count hit want exactly (then the
+  // keys >= T are the selection and the search stops), as that candidate.
+  uint32_t T = top < 0 ? k_and : top >= 31 ? 0u : (k_and & ~((2u << top) - 1u));
+  auto count_ge = [&](uint32_t c) {
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < kR; ++i) n += __popcll(__ballot(key[i] >= c));
+    return n;
+  };
+  int bit = top;
+  bool done = false;
+  for (; bit >= 1; bit -= 2) {                   // bits bit, bit-1
+    const uint32_t c1 = T | (1u << (bit - 1)), c2 = T | (2u << (bit - 1)), c3 = T | (3u << (bit - 1));
+    const int n1 = count_ge(c1), n2 = count_ge(c2), n3 = count_ge(c3);   // n1 >= n2 >= n3
+    if (n3 >= want) {
+      T = c3;
+      done = n3 == want;
+    } else if (n2 >= want) {
+      T = c2;
+      done = n2 == want;
+    } else if (n1 >= want) {
+      T = c1;
+      done = n1 == want;
+    }
+    if (done) break;
+  }
+  if (!done && bit == 0 && count_ge(T | 1u) >= want) T |= 1u;
+
+  int gt = 0;
+#pragma unroll
+  for (int i = 0; i < kR; ++i) gt += __popcll(__ballot(key[i] > T));
+  const int need = want - gt;                            // keys equal to T to take
+  int tie_before = 0;
+#pragma unroll
+  for (int i = 0; i < kR; ++i) {
+    const uint64_t m = __ballot(key[i] == T);
+    tie_before += __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                            __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+  }
+  bool take[kR];
+  int tb = tie_before;
+#pragma unroll
+  for (int i = 0; i < kR; ++i) {
+    take[i] = key[i] > T || (key[i] == T && tb < need);
+    tb += key[i] == T;
+  }
+  int before = 0;
+#pragma unroll
+  for (int i = 0; i < kR; ++i) {
+    const uint64_t m = __ballot(take[i]);
+    before += __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                        __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+  }
+  int at = n_init + before;
+#pragma unroll
+  for (int i = 0; i < kR; ++i) {
+    if (take[i]) {
+      sel[at] = lo + lane * kR + i;
+      pages[at] = pg[i];
+      ++at;
+    }
+  }
+  write_local();
 }
 
 // Largest number of candidate blocks the wave-level selection handles (64 lanes x 32).
@@ -270,12 +296,12 @@ constexpr int kWaveSelectMax = 64 * 32;
 // length is): kR = 4, 8, 16 or 32 keys per lane.
 __device__ __forceinline__ void wave_select(const float* srow, const int32_t* bt, int max_blocks,
                                             const int32_t* row_pos, int k, int n_init, int n_local,
-                                            int* scratch, int& sel, int& page) {
+                                            int* sel, int* pages) {
   const int C = max_blocks - n_init - n_local;
-  if (C <= 256) wave_select_table<4>(srow, bt, max_blocks, row_pos, k, n_init, n_local, scratch, sel, page);
-  else if (C <= 512) wave_select_table<8>(srow, bt, max_blocks, row_pos, k, n_init, n_local, scratch, sel, page);
-  else if (C <= 1024) wave_select_table<16>(srow, bt, max_blocks, row_pos, k, n_init, n_local, scratch, sel, page);
-  else wave_select_table<32>(srow, bt, max_blocks, row_pos, k, n_init, n_local, scratch, sel, page);
+  if (C <= 256) wave_select_table<4>(srow, bt, max_blocks, row_pos, k, n_init, n_local, sel, pages);
+  else if (C <= 512) wave_select_table<8>(srow, bt, max_blocks, row_pos, k, n_init, n_local, sel, pages);
+  else if (C <= 1024) wave_select_table<16>(srow, bt, max_blocks, row_pos, k, n_init, n_local, sel, pages);
+  else wave_select_table<32>(srow, bt, max_blocks, row_pos, k, n_init, n_local, sel, pages);
 }
 
 }  // namespace msa

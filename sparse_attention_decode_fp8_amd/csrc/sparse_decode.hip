@@ -191,7 +191,6 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
   __shared__ float mbuf[kW][16], lbuf[kW][16];
   __shared__ int s_last;
   __shared__ int32_t lsel[kSelect ? MSA_MAX_TOPK : 1], lpage[kSelect ? MSA_MAX_TOPK : 1];
-  __shared__ int wsel[kSelect ? 128 : 1];
   __shared__ half8_t qlds[kSelect ? 4 : 1][64];   // selecting variant: the converted Q operand
   __shared__ float qcs[kSelect ? 64 : 1];
   __shared__ SelectSmem sm;
@@ -267,22 +266,21 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
       // hands the table over through LDS. Its block-table reads go out with the score
       // reads, from the row of the request r belongs to when every request has the
       // same number of rows; the pages are read again if row_seq says otherwise.
+      const int guess = seq_guess(r, a.seq_mul);
       if (wave == 0) {
-        const int guess = seq_guess(r, a.seq_mul);
         const int32_t* btg = a.block_table + static_cast<int64_t>(guess) * a.max_blocks;
-        wave_select(srow, btg, a.max_blocks, a.row_pos + r, a.k, a.n_init, a.n_local, wsel, selv, pagev);
-        const int seq = a.row_seq[r];
-        if (seq != guess) {
-          const int32_t* bt = a.block_table + static_cast<int64_t>(seq) * a.max_blocks;
-          pagev = selv >= 0 ? bt[selv] : -1;
-        }
-        if (lane < MSA_MAX_TOPK) { lsel[lane] = selv; lpage[lane] = pagev; }
+        wave_select(srow, btg, a.max_blocks, a.row_pos + r, a.k, a.n_init, a.n_local, lsel, lpage);
       }
       if (wave == 1) q_to_lds();
       pos = a.row_pos[r];
+      const int seq = a.row_seq[r];
       __syncthreads();
-      selv = lane < MSA_MAX_TOPK ? lsel[lane] : -1;
-      pagev = lane < MSA_MAX_TOPK ? lpage[lane] : -1;
+      selv = lsel[lane];
+      pagev = lpage[lane];
+      if (seq != guess) {
+        const int32_t* bt = a.block_table + static_cast<int64_t>(seq) * a.max_blocks;
+        pagev = selv >= 0 ? bt[selv] : -1;
+      }
     } else {
       if (wave == 1) q_to_lds();
       pos = a.row_pos[r];
