@@ -304,7 +304,8 @@ def cpu_baseline(wl, budget_s):
             rows = np.nonzero(wl.row_seq == s)[0]
             L = int(wl.ctx_lens[s])
             pool = O.new_pool(wl.fmt, wl.num_pages, wl.num_kv_heads, k_tensor_scale=wl.k_tensor_scale,
-                              v_tensor_scale=wl.v_tensor_scale)
+                              v_tensor_scale=wl.v_tensor_scale, index_fmt=wl.index_fmt,
+                              index_tensor_scale=wl.index_tensor_scale)
             O.kv_append(pool, wl.slots(s, np.arange(L)), None, None, wl.idx_src[s][:L])
             sl, kb, vb, ib = wl.prefill_slices(s, np.arange(L, L + wl.n_append))
             args = (wl.block_table, wl.row_seq[rows], wl.row_pos[rows], sl, kb, vb, ib,

@@ -20,6 +20,7 @@ listed in the design notes. Each function is the definition written out in
 numpy float64, in the order the method runs it:
 
   kv_append      quantise new K/V/index-K into their 128-token page slots
+  index_keys     exact value of a page's index keys (E4M3 or NVFP4)
   index_score    per-token index score, max-pooled into 128-token blocks
   select_topk    top-k blocks, ties to the smaller block, ascending, -1 padded
   split_partials split-KV online-softmax partials (m, l, O) per split
@@ -41,6 +42,8 @@ GROUP = 16          # NVFP4: one e4m3 scale per 16 contiguous elements (reading)
 HEADS_PER_KV = 16   # [Rubin] Description: "16 query heads per KV head"
 FMT_FP8 = 1
 FMT_NVFP4 = 2
+IDX_E4M3 = 1        # index-key formats
+IDX_NVFP4 = 2
 
 
 # --------------------------------------------------------------------------------
@@ -199,16 +202,27 @@ def fp8_kv_encode(x: np.ndarray, page_scale: float) -> np.ndarray:
 # --------------------------------------------------------------------------------
 def new_pool(fmt: int, num_pages: int, num_kv_heads: int, head_dim: int = 128,
              index_dim: int = 64, k_tensor_scale: float = 1.0,
-             v_tensor_scale: float = 1.0, k_page_scale=None, v_page_scale=None) -> dict:
+             v_tensor_scale: float = 1.0, k_page_scale=None, v_page_scale=None,
+             index_fmt: int = IDX_E4M3, index_tensor_scale: float = 1.0) -> dict:
     """A zero-filled pool. Layout per page, head-major inside the page
     ([Rubin] commit messages name the HND storage of the main KV pool):
 
       NVFP4: codes u8 [pages][Hkv][128][D/2], scales u8 (e4m3) [pages][Hkv][128][D/16]
       FP8:   codes u8 [pages][Hkv][128][D],   scales fp32 [pages]
-      index-K: u8 (e4m3) [pages][128][index_dim], one key per token, no scale
+      index-K, E4M3:  u8 [pages][128][index_dim], one unscaled key per token
+      index-K, NVFP4: codes u8 [pages][128][index_dim/2], scales u8 (e4m3)
+                      [pages][128][index_dim/16], one fp32 tensor scale
     """
     p = {"fmt": fmt, "num_pages": num_pages, "Hkv": num_kv_heads, "D": head_dim,
-         "di": index_dim, "index_k": np.zeros((num_pages, PAGE, index_dim), np.uint8)}
+         "di": index_dim, "index_fmt": index_fmt}
+    if index_fmt == IDX_E4M3:
+        p["index_k"] = np.zeros((num_pages, PAGE, index_dim), np.uint8)
+    elif index_fmt == IDX_NVFP4:
+        p["index_k"] = np.zeros((num_pages, PAGE, index_dim // 2), np.uint8)
+        p["index_scales"] = np.zeros((num_pages, PAGE, index_dim // GROUP), np.uint8)
+        p["index_tensor_scale"] = float(np.float32(index_tensor_scale))
+    else:
+        raise ValueError("unknown index-key format")
     if fmt == FMT_NVFP4:
         for kv in ("k", "v"):
             p[kv + "_codes"] = np.zeros((num_pages, num_kv_heads, PAGE, head_dim // 2), np.uint8)
@@ -239,7 +253,16 @@ def kv_append(pool: dict, slot: np.ndarray, k_new=None, v_new=None, idx_new=None
     keep = np.nonzero(slot >= 0)[0]
     page, off = slot[keep] // PAGE, slot[keep] % PAGE
     if idx_new is not None:
-        pool["index_k"][page, off] = e4m3_encode(bf16_bits_to_f64(np.asarray(idx_new)[keep]))
+        xi = bf16_bits_to_f64(np.asarray(idx_new)[keep])         # [n][index_dim]
+        if pool["index_fmt"] == IDX_NVFP4:
+            # reading: [Rubin] Description lists NVFP4 index-K pages
+            # (indexer_kv_dtype='nvfp4') without a recipe; they take the KV's NVFP4
+            # recipe, encoded from the bf16 key with the pool's index tensor scale
+            codes, sc = nvfp4_encode(xi, pool["index_tensor_scale"])
+            pool["index_k"][page, off] = pack_nibbles(codes)
+            pool["index_scales"][page, off] = sc
+        else:
+            pool["index_k"][page, off] = e4m3_encode(xi)
     for kv, src in (("k", k_new), ("v", v_new)):
         if src is None:
             continue
@@ -251,6 +274,15 @@ def kv_append(pool: dict, slot: np.ndarray, k_new=None, v_new=None, idx_new=None
         else:
             s = pool[kv + "_scales"][page].astype(np.float64)[:, None, None]
             pool[kv + "_codes"][page, :, off] = e4m3_encode(f32(x / f32(s)))
+
+
+def index_keys(pool: dict, page: int, n: int) -> np.ndarray:
+    """Exact value of the first n index keys of a page, float64 [n][index_dim]."""
+    if pool["index_fmt"] == IDX_NVFP4:
+        vals = E2M1[unpack_nibbles(pool["index_k"][page, :n])]
+        sc = E4M3[pool["index_scales"][page, :n]]
+        return vals * np.repeat(sc, GROUP, axis=1) * pool["index_tensor_scale"]
+    return E4M3[pool["index_k"][page, :n]]
 
 
 def dequant_page(pool: dict, page: int, head: int, kv: str) -> np.ndarray:
@@ -273,7 +305,8 @@ def index_score(pool: dict, block_table, row_seq, row_pos, q_idx_bits, w,
     The pages name the scorer ([GB300] "The TP4 decode target": "an index scorer
     that prefetches older index-K pages"; [Rubin] commits: a CuTe DSL scorer and
     an indexer proxy max-score pass) but not its formula. Reading: for a query
-    row r and a visible token p (p <= row_pos[r]) with E4M3 index key k_p,
+    row r and a visible token p (p <= row_pos[r]) with index key k_p (E4M3, or
+    NVFP4 decoded exactly),
         s_p = sum_h w[r,h] * max(0, q_idx[r,h] . k_p)
     and the block score is the max of s_p over the block's visible tokens.
     Blocks past the row's last visible block are -inf; so is nothing else.
@@ -287,7 +320,7 @@ def index_score(pool: dict, block_table, row_seq, row_pos, q_idx_bits, w,
         for b in range(pos // PAGE + 1):
             page = int(block_table[seq][b])
             n_vis = min(PAGE, pos - PAGE * b + 1)
-            K = E4M3[pool["index_k"][page, :n_vis]]             # [n_vis][di]
+            K = index_keys(pool, page, n_vis)                   # [n_vis][di]
             dots = K @ q.T                                       # [n_vis][Hi]
             s = (np.maximum(dots, 0.0) * wr).sum(axis=1)
             S[r, b] = s.max()

@@ -41,6 +41,8 @@ import numpy as np
 PAGE = 128
 FMT_FP8 = 1
 FMT_NVFP4 = 2
+IDX_E4M3 = 1
+IDX_NVFP4 = 2
 
 
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -80,6 +82,7 @@ class Workload:
     n_init: int = 0
     n_local: int = 1
     spare_pages: int = 3
+    index_fmt: int = IDX_E4M3
     # filled by build()
     num_pages: int = 0
     max_blocks: int = 0
@@ -94,6 +97,7 @@ class Workload:
     w: np.ndarray = field(default=None, repr=False)             # f32 [rows][Hi]
     k_tensor_scale: float = 1.0
     v_tensor_scale: float = 1.0
+    index_tensor_scale: float = 1.0   # NVFP4 index keys
     k_page_scale: np.ndarray = field(default=None, repr=False)  # f32 [pages] (FP8)
     v_page_scale: np.ndarray = field(default=None, repr=False)
     tie_blocks: list = field(default=None, repr=False)
@@ -195,6 +199,9 @@ def build(wl: Workload) -> Workload:
         r3 = np.random.default_rng([wl.seed, 2, s])
         wl.idx_src.append(to_bf16_bits(r3.standard_normal((totals[s], di), dtype=np.float32)))
     # scales (calibration inputs)
+    if wl.index_fmt == IDX_NVFP4:
+        ia = max(bf16_absmax(x) for x in wl.idx_src)
+        wl.index_tensor_scale = float(np.float32(ia / (6.0 * 448.0)))
     if wl.fmt == FMT_NVFP4:
         ka = max(bf16_absmax(x) for x in wl.k_src)
         va = max(bf16_absmax(x) for x in wl.v_src)
@@ -247,7 +254,9 @@ def keep_rows(wl: Workload, rows) -> Workload:
 # --------------------------------------------------------------------------------
 # The five benchmark workloads and small parity workloads
 # --------------------------------------------------------------------------------
-def config(cfg: int) -> Workload:
+def config(cfg: int, index_fmt: int = IDX_E4M3) -> Workload:
+    """The five workloads (index keys E4M3 as specified; index_fmt=IDX_NVFP4 gives
+    the same workload with NVFP4 index keys, which draws the same random numbers)."""
     seed = 1000 + cfg
     if cfg == 0:   # tiny FP8 case
         wl = Workload("tiny_fp8_b1_ctx4096", seed, FMT_FP8, 1, 8, np.array([4096]), 0, 1)
@@ -265,6 +274,9 @@ def config(cfg: int) -> Workload:
         wl = Workload("mixed48_lognormal8k_nvfp4_top16", seed, FMT_NVFP4, 4, 16, lens, 1, 1)
     else:
         raise ValueError(cfg)
+    wl.index_fmt = index_fmt
+    if index_fmt == IDX_NVFP4:
+        wl.name += "_idxnvfp4"
     build(wl)
     if cfg == 3:
         inject_ties(wl, 1100)
@@ -275,9 +287,11 @@ def config(cfg: int) -> Workload:
 
 
 def small(fmt: int, ctx_lens, n_append: int, num_kv_heads: int = 2, k: int = 4,
-          seed: int = 7, rows_per_req: int | None = None) -> Workload:
+          seed: int = 7, rows_per_req: int | None = None, index_fmt: int = IDX_E4M3) -> Workload:
     """A small workload for parity tests (several tiles and ragged tails)."""
     rows_per_req = rows_per_req or max(1, n_append)
     wl = Workload(f"small_{'fp8' if fmt == FMT_FP8 else 'nvfp4'}", seed, fmt, num_kv_heads, k,
-                  np.asarray(ctx_lens, dtype=np.int64), n_append, rows_per_req)
+                  np.asarray(ctx_lens, dtype=np.int64), n_append, rows_per_req, index_fmt=index_fmt)
+    if index_fmt == IDX_NVFP4:
+        wl.name += "_idxnvfp4"
     return build(wl)

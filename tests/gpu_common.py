@@ -27,7 +27,8 @@ def gpu_pool(M, wl: W.Workload):
     """A device pool holding every cached token, written by msa_kv_append."""
     pool = M.KVPool(wl.fmt, wl.num_pages, wl.num_kv_heads, k_tensor_scale=wl.k_tensor_scale,
                     v_tensor_scale=wl.v_tensor_scale, k_page_scale=wl.k_page_scale,
-                    v_page_scale=wl.v_page_scale)
+                    v_page_scale=wl.v_page_scale, index_fmt=wl.index_fmt,
+                    index_tensor_scale=wl.index_tensor_scale)
     for s in range(len(wl.ctx_lens)):
         L = int(wl.ctx_lens[s])
         if L == 0:
@@ -67,7 +68,8 @@ def oracle_pool(wl: W.Workload, seqs=None, kv_blocks=None):
     None) and K/V of every token, or only of the (seq -> blocks) given in kv_blocks."""
     pool = O.new_pool(wl.fmt, wl.num_pages, wl.num_kv_heads, k_tensor_scale=wl.k_tensor_scale,
                       v_tensor_scale=wl.v_tensor_scale, k_page_scale=wl.k_page_scale,
-                      v_page_scale=wl.v_page_scale)
+                      v_page_scale=wl.v_page_scale, index_fmt=wl.index_fmt,
+                      index_tensor_scale=wl.index_tensor_scale)
     seqs = range(len(wl.ctx_lens)) if seqs is None else seqs
     for s in seqs:
         T = wl.total_len(s)

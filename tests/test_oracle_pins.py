@@ -375,3 +375,58 @@ def test_decode_step_small_verify_workload_runs():
         assert sel[r, min(nb[r], wl.k) - 1] == nb[r] - 1 if nb[r] > wl.k else True
         assert np.all(np.isfinite(S[r, :nb[r]])) and np.all(np.isneginf(S[r, nb[r]:]))
     assert np.all(np.isfinite(out))
+
+
+# ---- NVFP4 index keys (reading: the KV's NVFP4 recipe applied to the 64-d index key)
+def _nvfp4_exact_keys(rng, n, t, pow2_scales=False):
+    """Keys that NVFP4 holds exactly: each 16-group is E2M1 values times one E4M3 scale
+    times t, with the group's largest magnitude 6 * scale * t (so the encoder picks
+    exactly that scale: amax / (6 t) is an E4M3 value). With power-of-two scales the
+    values have at most 2 significant bits, so E4M3 holds them exactly too."""
+    grid = np.array([0, .5, 1, 1.5, 2, 3, 4, 6])
+    keys = np.empty((n, 64))
+    for i in range(n):
+        for g in range(4):
+            sc = 2.0 ** rng.integers(-3, 4) * (1.0 if pow2_scales else rng.choice([1.0, 1.25, 1.5, 1.75]))
+            v = rng.choice(grid, 16) * rng.choice([-1, 1], 16)
+            v[rng.integers(16)] = 6.0 * rng.choice([-1, 1])        # the group's amax
+            keys[i, 16 * g:16 * g + 16] = v * sc * t
+    return keys
+
+
+def test_nvfp4_index_keys_round_trip_exactly():
+    rng = np.random.default_rng(61)
+    t = 0.0625                                   # a power of two keeps every product exact
+    keys = _nvfp4_exact_keys(rng, 40, t)
+    bits = W.to_bf16_bits(keys.astype(np.float32))
+    assert np.array_equal(W.bf16_bits_to_f32(bits), keys)       # exact in bf16 too
+    pool = O.new_pool(O.FMT_FP8, 2, 1, index_fmt=O.IDX_NVFP4, index_tensor_scale=t)
+    slots = np.concatenate([np.arange(3, 23), 128 + np.arange(100, 120)])
+    O.kv_append(pool, slots, None, None, bits)
+    got = np.concatenate([O.index_keys(pool, 0, 23)[3:], O.index_keys(pool, 1, 120)[100:]])
+    assert np.array_equal(got, keys)
+    # untouched slots stay zero; low nibble holds the even element
+    assert not pool["index_k"][0, :3].any() and not pool["index_scales"][1, :100].any()
+    c = O.unpack_nibbles(pool["index_k"][0, 3])
+    assert np.array_equal(O.E2M1[c][:16] * O.E4M3[pool["index_scales"][0, 3, 0]] * t, keys[0, :16])
+
+
+def test_index_score_same_for_nvfp4_and_e4m3_keys_that_both_hold_exactly():
+    rng = np.random.default_rng(62)
+    t = 1.0
+    L = 300
+    keys = _nvfp4_exact_keys(rng, L, t, pow2_scales=True)   # |keys| <= 6 * 8 < 448
+    bits = W.to_bf16_bits(keys.astype(np.float32))
+    bt = np.array([[2, 0, 1]], np.int32)
+    slots = bt[0][np.arange(L) // 128].astype(np.int64) * 128 + np.arange(L) % 128
+    pools = []
+    for fmt in (O.IDX_E4M3, O.IDX_NVFP4):
+        p = O.new_pool(O.FMT_FP8, 3, 1, index_fmt=fmt, index_tensor_scale=t)
+        O.kv_append(p, slots, None, None, bits)
+        pools.append(p)
+    assert np.array_equal(O.index_keys(pools[0], 2, 128), O.index_keys(pools[1], 2, 128))
+    q = W.to_bf16_bits(rng.standard_normal((2, 4, 64)).astype(np.float32))
+    w = rng.random((2, 4)).astype(np.float32)
+    S0 = O.index_score(pools[0], bt, [0, 0], [L - 1, 200], q, w, 3)
+    S1 = O.index_score(pools[1], bt, [0, 0], [L - 1, 200], q, w, 3)
+    assert np.array_equal(S0, S1) and np.isfinite(S0[0]).all() and np.isneginf(S0[1, 2])
