@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--num-splits", type=int, default=0, help="0 = library default for k")
     ap.add_argument("--replicas", type=int, default=REPLICAS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--index-fmt", choices=["e4m3", "nvfp4"], default="e4m3",
+                    help="index-key format (the workload specifies e4m3; nvfp4 is the option)")
     ap.add_argument("--separate", action="store_true",
                     help="five launches per step (one per stage) instead of the two fused ones")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget")
@@ -100,7 +102,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t0 = time.time()
-    wl = W.config(WORKLOAD_CFG)
+    wl = W.config(WORKLOAD_CFG, index_fmt=W.IDX_NVFP4 if args.index_fmt == "nvfp4" else W.IDX_E4M3)
     ns = args.num_splits or default_num_splits(wl.k)
     print(f"[bench] workload {wl.name} generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
@@ -110,7 +112,8 @@ def main():
 
     pool0 = M.KVPool(wl.fmt, wl.num_pages, wl.num_kv_heads, k_tensor_scale=wl.k_tensor_scale,
                      v_tensor_scale=wl.v_tensor_scale, k_page_scale=wl.k_page_scale,
-                     v_page_scale=wl.v_page_scale)
+                     v_page_scale=wl.v_page_scale, index_fmt=wl.index_fmt,
+                     index_tensor_scale=wl.index_tensor_scale)
     for s in range(len(wl.ctx_lens)):
         L = int(wl.ctx_lens[s])
         M.msa_kv_append(pool0, torch.from_numpy(wl.slots(s, np.arange(L))).to(dev),
@@ -222,7 +225,8 @@ def main():
     sel = bufs.sel.cpu().numpy()
     bpt = 144 if wl.fmt == W.FMT_NVFP4 else 256
     dec_bytes, dec_tokens = decode_algorithmic_bytes(wl, sel, bpt)
-    idx_bytes = int(sum(int(wl.row_pos[r]) + 1 for r in range(wl.num_rows)) * 64)   # 1 row / request
+    key_bytes = 64 if wl.index_fmt == W.IDX_E4M3 else 32 + 4        # per token: codes (+ scales)
+    idx_bytes = int(sum(int(wl.row_pos[r]) + 1 for r in range(wl.num_rows)) * key_bytes)   # 1 row / request
     t_dec = sum(per_kernel_us[k]["mean"] for k in decode_kernels) * 1e-6
     if args.separate:
         t_idx = per_kernel_us["msa_index_score"]["mean"] * 1e-6
@@ -270,6 +274,7 @@ def main():
         "dtype": "nvfp4/e4m3 storage, fp16 MFMA operands, fp32 accumulate, bf16 out",
         "data": "synthetic (seeded N(0,1) K/V/Q, shuffled page table)",
         "config": {"workload": wl.name, "batch": 8, "query_rows": rows, "kv_heads": wl.num_kv_heads,
+                   "index_keys": args.index_fmt,
                    "q_heads": wl.num_heads, "head_dim": 128, "cached_tokens": int(wl.ctx_lens[0]),
                    "appended_tokens": wl.n_append, "top_k": wl.k, "kv_format": "nvfp4",
                    "num_splits": ns, "pool_replicas": args.replicas, "parallelism": "single GPU"},

@@ -57,6 +57,11 @@ typedef enum {
   MSA_KV_NVFP4 = 2     /* E2M1 codes + E4M3 scale per 16 elements + fp32 tensor scale   */
 } msa_kv_format_t;
 
+typedef enum {
+  MSA_INDEX_E4M3 = 1,  /* one unscaled OCP E4M3 code per index-key element (0 means the same) */
+  MSA_INDEX_NVFP4 = 2  /* E2M1 codes + E4M3 scale per 16 elements + fp32 index tensor scale  */
+} msa_index_format_t;
+
 #define MSA_PAGE_SIZE 128     /* tokens per page ([P128] Description: native P128 pages) */
 #define MSA_HEAD_DIM 128
 #define MSA_INDEX_DIM 64
@@ -76,9 +81,15 @@ typedef enum {
  *   FP8    k_codes/v_codes  u8 (E4M3) [num_pages][num_kv_heads][128][head_dim]
  *          k_scales/v_scales fp32 [num_pages]  (one scale per page, all heads)
  *          value = E4M3(code) * page_scale
- *   index_k u8 (E4M3) [num_pages][128][index_dim], one unscaled key per token
+ *   index_k, MSA_INDEX_E4M3 (default): u8 [num_pages][128][index_dim], one unscaled
+ *          E4M3 key per token
+ *   index_k, MSA_INDEX_NVFP4: u8 [num_pages][128][index_dim/2] (low nibble = even
+ *          element), index_scales u8 (E4M3) [num_pages][128][index_dim/16]; value =
+ *          E2M1(code) * E4M3(scale) * index_tensor_scale. [Rubin] Description lists
+ *          NVFP4 index-K pages (indexer_kv_dtype='nvfp4', a prototype) without a
+ *          recipe; the key is encoded like the NVFP4 KV (see msa_kv_append).
  *
- * All five arrays are required and must be 16-byte aligned.
+ * All arrays in use are required and must be 16-byte aligned.
  */
 typedef struct {
   int32_t fmt;            /* msa_kv_format_t                                   */
@@ -94,6 +105,9 @@ typedef struct {
   float k_tensor_scale;   /* NVFP4 only; > 0                                   */
   float v_tensor_scale;   /* NVFP4 only; > 0                                   */
   void* index_k;
+  int32_t index_fmt;        /* msa_index_format_t; 0 = MSA_INDEX_E4M3             */
+  void* index_scales;       /* MSA_INDEX_NVFP4 only                               */
+  float index_tensor_scale; /* MSA_INDEX_NVFP4 only; > 0                          */
 } msa_kv_pool_t;
 
 /*
@@ -123,7 +137,8 @@ typedef struct {
  *   NVFP4 per 16 elements: amax = max|x|; sc = E4M3(amax / (6 * t)); if E4M3(sc) == 0
  *         every code is +0, else d = E4M3(sc) * t and code_i = E2M1(x_i / d)
  *   FP8   code = E4M3(x / page_scale[page])   (the page scale is read, never written)
- *   index code = E4M3(x)
+ *   index code = E4M3(x), or with MSA_INDEX_NVFP4 the NVFP4 rule above per 16 elements
+ *         of the key with t = index_tensor_scale
  * Two tokens with the same slot in one call race. n_new may be 0.
  */
 msa_status_t msa_kv_append(const msa_kv_pool_t* pool, int32_t n_new, const int64_t* slot,
@@ -132,7 +147,9 @@ msa_status_t msa_kv_append(const msa_kv_pool_t* pool, int32_t n_new, const int64
 
 /*
  * Index score with block max-pool. For row r and visible token p (p <= row_pos[r]):
- *   s_p = sum_h w[r][h] * max(0, q_idx[r][h] . E4M3(index_k[p]))
+ *   s_p = sum_h w[r][h] * max(0, q_idx[r][h] . key(p))
+ * where key(p) is the exact value of token p's index key (E4M3, or NVFP4 decoded as
+ * E2M1 * E4M3 scale * index_tensor_scale).
  *   block_scores[r][b] = max over the visible tokens p of block b of s_p   (b < nb(r))
  *   block_scores[r][b] = -inf                                   (nb(r) <= b < max_blocks)
  * The pages name the scorer ([GB300] "The TP4 decode target": an index scorer over
@@ -264,6 +281,10 @@ size_t msa_decode_workspace_bytes(int32_t rows, int32_t num_q_heads, int32_t hea
  * entry points. */
 msa_status_t msa_pool_bytes(int32_t fmt, int32_t num_pages, int32_t num_kv_heads,
                             int32_t head_dim, int32_t index_dim, size_t out[5]);
+
+/* Exact bytes of the index-key arrays: out[0] = index_k, out[1] = index_scales (0 for
+ * MSA_INDEX_E4M3). */
+msa_status_t msa_index_bytes(int32_t index_fmt, int32_t num_pages, int32_t index_dim, size_t out[2]);
 
 /* A static string naming the status. */
 const char* msa_status_string(msa_status_t status);

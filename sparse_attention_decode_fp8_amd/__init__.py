@@ -5,7 +5,7 @@ include/msa_decode.h; this package is the ctypes binding (marshalling only) plus
 the in-tree build script. Importing it loads the HIP library and fails loudly if
 it has not been built.
 """
-from ._lib import (FMT_FP8, FMT_NVFP4, KVPool, MsaError, Step, msa_combine,  # noqa: F401
+from ._lib import (FMT_FP8, FMT_NVFP4, IDX_E4M3, IDX_NVFP4, KVPool, MsaError, Step, msa_combine,  # noqa: F401
                    msa_decode_workspace_bytes, msa_index_score, msa_kv_append, msa_select_topk,
                    msa_sparse_decode, msa_sparse_decode_combine,
                    msa_append_score_select, msa_select_decode_combine)

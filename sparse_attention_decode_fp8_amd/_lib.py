@@ -18,6 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libmsadecode.so")
 
 FMT_FP8 = 1
 FMT_NVFP4 = 2
+IDX_E4M3 = 1
+IDX_NVFP4 = 2
 PAGE = 128
 HEAD_DIM = 128
 INDEX_DIM = 64
@@ -36,7 +38,8 @@ class MsaKvPool(ctypes.Structure):
                 ("k_codes", ctypes.c_void_p), ("v_codes", ctypes.c_void_p),
                 ("k_scales", ctypes.c_void_p), ("v_scales", ctypes.c_void_p),
                 ("k_tensor_scale", ctypes.c_float), ("v_tensor_scale", ctypes.c_float),
-                ("index_k", ctypes.c_void_p)]
+                ("index_k", ctypes.c_void_p), ("index_fmt", ctypes.c_int32),
+                ("index_scales", ctypes.c_void_p), ("index_tensor_scale", ctypes.c_float)]
 
 
 class MsaStep(ctypes.Structure):
@@ -47,7 +50,8 @@ class MsaStep(ctypes.Structure):
 
 EXPORTS = ["msa_kv_append", "msa_index_score", "msa_select_topk", "msa_append_score_select",
            "msa_sparse_decode",
-           "msa_sparse_decode_combine", "msa_select_decode_combine", "msa_combine", "msa_decode_workspace_bytes", "msa_pool_bytes", "msa_status_string"]
+           "msa_sparse_decode_combine", "msa_select_decode_combine", "msa_combine",
+           "msa_decode_workspace_bytes", "msa_pool_bytes", "msa_index_bytes", "msa_status_string"]
 
 
 def _load():
@@ -67,6 +71,7 @@ def _load():
         "msa_combine": (I32, [I32, I32, I32, I32, P, P, P, P]),
         "msa_decode_workspace_bytes": (SZ, [I32, I32, I32, I32]),
         "msa_pool_bytes": (I32, [I32, I32, I32, I32, I32, ctypes.POINTER(SZ)]),
+        "msa_index_bytes": (I32, [I32, I32, I32, ctypes.POINTER(SZ)]),
         "msa_status_string": (ctypes.c_char_p, [I32]),
     }
     for name, (res, args) in sig.items():
@@ -105,15 +110,20 @@ class KVPool:
     """One layer's paged pool on the GPU (layout documented in include/msa_decode.h)."""
 
     def __init__(self, fmt, num_pages, num_kv_heads, device="cuda", k_tensor_scale=1.0,
-                 v_tensor_scale=1.0, k_page_scale=None, v_page_scale=None):
+                 v_tensor_scale=1.0, k_page_scale=None, v_page_scale=None, index_fmt=IDX_E4M3,
+                 index_tensor_scale=1.0):
         sizes = (ctypes.c_size_t * 5)()
         _check(LIB.msa_pool_bytes(fmt, num_pages, num_kv_heads, HEAD_DIM, INDEX_DIM, sizes),
                "msa_pool_bytes")
+        isizes = (ctypes.c_size_t * 2)()
+        _check(LIB.msa_index_bytes(index_fmt, num_pages, INDEX_DIM, isizes), "msa_index_bytes")
         self.fmt, self.num_pages, self.num_kv_heads = fmt, num_pages, num_kv_heads
         self.k_tensor_scale, self.v_tensor_scale = float(k_tensor_scale), float(v_tensor_scale)
+        self.index_fmt, self.index_tensor_scale = index_fmt, float(index_tensor_scale)
         z = lambda n: torch.zeros(n, dtype=torch.uint8, device=device)   # pools start zeroed
         self.k_codes, self.v_codes = z(sizes[0]), z(sizes[1])
-        self.index_k = z(sizes[4])
+        self.index_k = z(isizes[0])
+        self.index_scales = z(isizes[1]) if isizes[1] else None
         if fmt == FMT_FP8:
             mk = lambda s: (torch.ones(num_pages, dtype=torch.float32) if s is None
                             else torch.as_tensor(s, dtype=torch.float32)).to(device)
@@ -122,14 +132,19 @@ class KVPool:
             self.k_scales, self.v_scales = z(sizes[2]), z(sizes[3])
 
     def arrays(self):
-        return {"k_codes": self.k_codes, "v_codes": self.v_codes, "k_scales": self.k_scales,
-                "v_scales": self.v_scales, "index_k": self.index_k}
+        a = {"k_codes": self.k_codes, "v_codes": self.v_codes, "k_scales": self.k_scales,
+             "v_scales": self.v_scales, "index_k": self.index_k}
+        if self.index_scales is not None:
+            a["index_scales"] = self.index_scales
+        return a
 
     def cstruct(self) -> MsaKvPool:
         return MsaKvPool(self.fmt, self.num_pages, self.num_kv_heads, HEAD_DIM, PAGE, INDEX_DIM,
                          self.k_codes.data_ptr(), self.v_codes.data_ptr(), self.k_scales.data_ptr(),
                          self.v_scales.data_ptr(), self.k_tensor_scale, self.v_tensor_scale,
-                         self.index_k.data_ptr())
+                         self.index_k.data_ptr(), self.index_fmt,
+                         self.index_scales.data_ptr() if self.index_scales is not None else None,
+                         self.index_tensor_scale)
 
     def clone(self) -> "KVPool":
         c = object.__new__(KVPool)

@@ -31,6 +31,23 @@ extern "C" msa_status_t msa_pool_bytes(int32_t fmt, int32_t num_pages, int32_t n
   return MSA_OK;
 }
 
+extern "C" msa_status_t msa_index_bytes(int32_t index_fmt, int32_t num_pages, int32_t index_dim,
+                                        size_t out[2]) {
+  if (out == nullptr || num_pages <= 0) return MSA_ERR_INVALID_ARG;
+  if (index_dim != MSA_INDEX_DIM) return MSA_ERR_UNSUPPORTED;
+  const size_t tok = static_cast<size_t>(num_pages) * MSA_PAGE_SIZE;
+  if (index_fmt == 0 || index_fmt == MSA_INDEX_E4M3) {
+    out[0] = tok * index_dim;
+    out[1] = 0;
+  } else if (index_fmt == MSA_INDEX_NVFP4) {
+    out[0] = tok * (index_dim / 2);
+    out[1] = tok * (index_dim / 16);
+  } else {
+    return MSA_ERR_UNSUPPORTED;
+  }
+  return MSA_OK;
+}
+
 extern "C" const char* msa_status_string(msa_status_t status) {
   switch (status) {
     case MSA_OK: return "MSA_OK";

@@ -20,7 +20,9 @@ struct AppendArgs {
   uint8_t* k_scales;   // NVFP4: e4m3 bytes; FP8: fp32 page scales
   uint8_t* v_scales;
   uint8_t* index_k;
-  float k_t, v_t;
+  uint8_t* index_scales;   // NVFP4 index keys: e4m3 bytes [pages][128][index_dim / 16]
+  float k_t, v_t, idx_t;
+  int index_nvfp4;
   int n_new, hkv;
   int kv_groups;       // groups of 16 per token for K (and for V): hkv * 8
   int groups_per_tok;  // K groups + V groups + index groups
@@ -58,6 +60,44 @@ __device__ __forceinline__ uint4 encode_index16(const uint16_t* src) {
   return encode_index16_bits(p[0], p[1]);
 }
 
+// One NVFP4 group: 16 values at tensor scale t -> 16 E2M1 codes (element 2j in the low
+// nibble of byte j, as w0 | w1 << 32) and the E4M3 scale code. amax = max|x|,
+// sc = E4M3(amax / (6 t)); a zero decoded scale gives all codes +0; otherwise
+// d = E4M3(sc) * t and code_i = E2M1(x_i / d). Every operation is a correctly rounded
+// fp32 operation (contraction off).
+__device__ __forceinline__ uint32_t nvfp4_encode16(const float x[16], float t, uint32_t& w0, uint32_t& w1) {
+#pragma clang fp contract(off)
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  const float six_t = 6.0f * t;
+  const uint32_t sc = f32_to_e4m3_sat(amax / six_t);
+  const float dec = e4m3_to_f32(sc);
+  w0 = 0;
+  w1 = 0;
+  if (dec != 0.0f) {
+    const float d = dec * t;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      w0 |= f32_to_e2m1_sat(x[i] / d) << (4 * i);
+      w1 |= f32_to_e2m1_sat(x[8 + i] / d) << (4 * i);
+    }
+  }
+  return sc;
+}
+
+// 16 bf16 values (two 16-byte words as loaded) -> one NVFP4 group.
+__device__ __forceinline__ uint32_t nvfp4_encode16_bits(uint4 a, uint4 b, float t, uint32_t& w0, uint32_t& w1) {
+  const uint32_t wv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    x[2 * i] = __uint_as_float(wv[i] << 16);
+    x[2 * i + 1] = __uint_as_float(wv[i] & 0xffff0000u);
+  }
+  return nvfp4_encode16(x, t, w0, w1);
+}
+
 // Encode group `gid` (token gid / groups_per_tok) of the new tokens into the pool.
 template <int kFmt>
 __device__ __forceinline__ void append_group(const AppendArgs& a, int64_t gid) {
@@ -69,11 +109,20 @@ __device__ __forceinline__ void append_group(const AppendArgs& a, int64_t gid) {
   const int64_t page = slot / kPage;
   const int off = static_cast<int>(slot % kPage);
 
-  if (grp >= 2 * a.kv_groups) {                    // index-K: E4M3, no scale
+  if (grp >= 2 * a.kv_groups) {                    // index-K: E4M3, no scale, or NVFP4
     if (a.idx_new == nullptr) return;
     const int g = grp - 2 * a.kv_groups;             // 0..3
-    *reinterpret_cast<uint4*>(a.index_k + (page * kPage + off) * kIndexDim + 16 * g) =
-        encode_index16(a.idx_new + static_cast<int64_t>(tok) * kIndexDim + 16 * g);
+    const uint16_t* src = a.idx_new + static_cast<int64_t>(tok) * kIndexDim + 16 * g;
+    const int64_t row = page * kPage + off;
+    if (a.index_nvfp4) {
+      const uint4* p = reinterpret_cast<const uint4*>(src);
+      uint32_t w0, w1;
+      const uint32_t sc = nvfp4_encode16_bits(p[0], p[1], a.idx_t, w0, w1);
+      *reinterpret_cast<uint2*>(a.index_k + row * (kIndexDim / 2) + 8 * g) = make_uint2(w0, w1);
+      a.index_scales[row * (kIndexDim / 16) + g] = static_cast<uint8_t>(sc);
+    } else {
+      *reinterpret_cast<uint4*>(a.index_k + row * kIndexDim + 16 * g) = encode_index16(src);
+    }
     return;
   }
   const bool is_v = grp >= a.kv_groups;
@@ -86,22 +135,8 @@ __device__ __forceinline__ void append_group(const AppendArgs& a, int64_t gid) {
   const int64_t row = (page * a.hkv + h) * kPage + off;   // token row inside the pool
 
   if constexpr (kFmt == MSA_KV_NVFP4) {
-    const float t = is_v ? a.v_t : a.k_t;
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
-    const float six_t = 6.0f * t;
-    const uint32_t sc = f32_to_e4m3_sat(amax / six_t);
-    const float dec = e4m3_to_f32(sc);
-    uint32_t w0 = 0, w1 = 0;
-    if (dec != 0.0f) {
-      const float d = dec * t;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        w0 |= f32_to_e2m1_sat(x[i] / d) << (4 * i);
-        w1 |= f32_to_e2m1_sat(x[8 + i] / d) << (4 * i);
-      }
-    }
+    uint32_t w0, w1;
+    const uint32_t sc = nvfp4_encode16(x, is_v ? a.v_t : a.k_t, w0, w1);
     uint8_t* codes = is_v ? a.v_codes : a.k_codes;
     uint8_t* scales = is_v ? a.v_scales : a.k_scales;
     *reinterpret_cast<uint2*>(codes + row * (kHeadDim / 2) + 8 * g) = make_uint2(w0, w1);
@@ -130,8 +165,11 @@ inline AppendArgs make_append_args(const msa_kv_pool_t* pool, int32_t n_new, con
   a.k_scales = static_cast<uint8_t*>(pool->k_scales);
   a.v_scales = static_cast<uint8_t*>(pool->v_scales);
   a.index_k = static_cast<uint8_t*>(pool->index_k);
+  a.index_scales = static_cast<uint8_t*>(pool->index_scales);
+  a.index_nvfp4 = pool->index_fmt == MSA_INDEX_NVFP4;
   a.k_t = pool->k_tensor_scale;
   a.v_t = pool->v_tensor_scale;
+  a.idx_t = pool->index_tensor_scale;
   a.n_new = n_new;
   a.hkv = pool->num_kv_heads;
   a.kv_groups = pool->num_kv_heads * (MSA_HEAD_DIM / 16);

@@ -33,6 +33,8 @@ constexpr int kWaves = 4;
 
 struct ScoreArgs {
   const uint8_t* index_k;
+  const uint8_t* index_scales;   // NVFP4 index keys: e4m3 [pages][128][4]
+  float idx_t;                   // NVFP4 index tensor scale
   const int32_t* block_table;
   const int32_t* row_seq;
   const int32_t* row_pos;
@@ -51,7 +53,35 @@ struct ScoreArgs {
   int append_row;    // fused launch: 1 if grid row 0 holds the append workgroups
 };
 
-template <int kHi, int kFmt, bool kFused>
+// A lane's share of one 16-token row of keys (token 16t + n, dims 16q .. 16q+15):
+// E4M3 keys: 16 codes. NVFP4 keys: .x, .y = 16 E2M1 codes (element 2j in the low
+// nibble of byte j), .z = the group's E4M3 scale code.
+template <bool kIdxNv>
+__device__ __forceinline__ void key_operands(uint4 kt, half8_t& B0, half8_t& B1) {
+  if constexpr (kIdxNv) {
+    const half2_t s2 = e4m3x2_to_f16(kt.z);
+    const half2_t sc2 = {s2[0], s2[0]};
+    B0 = e2m1x8_to_f16(kt.x, sc2);
+    B1 = e2m1x8_to_f16(kt.y, sc2);
+  } else {
+    B0 = e4m3x8_to_f16(kt.x, kt.y);
+    B1 = e4m3x8_to_f16(kt.z, kt.w);
+  }
+}
+
+// The same share of a new token's key, encoded from its 16 bf16 values.
+template <bool kIdxNv>
+__device__ __forceinline__ uint4 encode_key16(uint4 lo, uint4 hi, float idx_t) {
+  if constexpr (kIdxNv) {
+    uint32_t w0, w1;
+    const uint32_t sc = nvfp4_encode16_bits(lo, hi, idx_t, w0, w1);
+    return make_uint4(w0, w1, sc, 0u);
+  } else {
+    return encode_index16_bits(lo, hi);
+  }
+}
+
+template <int kHi, int kFmt, bool kFused, bool kIdxNv>
 __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
   extern __shared__ uint32_t sel_keys[];        // fused: selection scratch [max_blocks]
   __shared__ SelectSmem sm;
@@ -135,16 +165,28 @@ __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
       pos[i] = rowslot[i] < nr ? a.row_pos[r0 + rowslot[i]] : -1;
     }
 
-    // All 8 key loads of the block: lane (n, q) reads 16 bytes of token 16t + n,
-    // dims 16q .. 16q+15 (k-step 0 uses the first 8, k-step 1 the last 8). They are
-    // issued from the guessed request's page (an unused entry reads page 0) and issued
-    // again from the right page if the guess was wrong.
+    // All 8 key loads of the block: lane (n, q) reads its share of token 16t + n, dims
+    // 16q .. 16q+15 (k-step 0 uses the first 8, k-step 1 the last 8): 16 E4M3 bytes,
+    // or 8 NVFP4 code bytes and the group's scale byte. They are issued from the
+    // guessed request's page (an unused entry reads page 0) and issued again from the
+    // right page if the guess was wrong.
     int64_t page = page_g >= 0 ? page_g : 0;
     uint4 key[8];
     auto load_keys = [&]() {
-      const uint8_t* kp = a.index_k + (page * kPage + n) * kIndexDim + 16 * q;
+      const int64_t tok0 = page * kPage + n;
+      if constexpr (kIdxNv) {
+        const uint8_t* kp = a.index_k + tok0 * (kIndexDim / 2) + 8 * q;
+        const uint8_t* sp = a.index_scales + tok0 * (kIndexDim / 16) + q;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) key[t] = *reinterpret_cast<const uint4*>(kp + t * 16 * kIndexDim);
+        for (int t = 0; t < 8; ++t) {
+          const uint2 c = *reinterpret_cast<const uint2*>(kp + t * 16 * (kIndexDim / 2));
+          key[t] = make_uint4(c.x, c.y, sp[t * 16 * (kIndexDim / 16)], 0u);
+        }
+      } else {
+        const uint8_t* kp = a.index_k + tok0 * kIndexDim + 16 * q;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) key[t] = *reinterpret_cast<const uint4*>(kp + t * 16 * kIndexDim);
+      }
     };
     if (seq != guess) page = a.block_table[static_cast<int64_t>(seq) * a.max_blocks + b];
     // New tokens landing in this page (fused launch): their keys are encoded here from
@@ -173,7 +215,7 @@ __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
       }
     }
     load_keys();
-    if (pt >= 0) pv = encode_index16_bits(pv, pv1);
+    if (pt >= 0) pv = encode_key16<kIdxNv>(pv, pv1, a.idx_t);
 
     float qa[16];
     {
@@ -198,7 +240,10 @@ __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
     // inverse pre-scale of the (row, head) that lane (n, q)'s result M = 4q + jj has
     float inv[4];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) inv[jj] = ldexpf(1.0f, -__shfl(e, 4 * q + jj, 64));
+    for (int jj = 0; jj < 4; ++jj) {
+      inv[jj] = ldexpf(1.0f, -__shfl(e, 4 * q + jj, 64));
+      if constexpr (kIdxNv) inv[jj] *= a.idx_t;   // NVFP4 keys: their tensor scale (> 0)
+    }
 
     if constexpr (kFused) {
       // New tokens landing in this page: encode their keys here (the append runs
@@ -214,7 +259,9 @@ __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
             hits &= hits - 1;
             const int off = __shfl(static_cast<int>(sl % kPage), jj, 64);
             if ((off & 15) == n) {
-              const uint4 v = encode_index16(a.app.idx_new + static_cast<int64_t>(base + jj) * kIndexDim + 16 * q);
+              const uint4* src = reinterpret_cast<const uint4*>(
+                  a.app.idx_new + static_cast<int64_t>(base + jj) * kIndexDim + 16 * q);
+              const uint4 v = encode_key16<kIdxNv>(src[0], src[1], a.idx_t);
 #pragma unroll
               for (int t = 0; t < 8; ++t)
                 if (t == (off >> 4)) key[t] = v;
@@ -229,9 +276,8 @@ __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
     for (int i = 0; i < kRowsPerLane; ++i) best[i] = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const uint4 kt = t == pt ? pv : key[t];
-      const half8_t B0 = e4m3x8_to_f16(kt.x, kt.y);
-      const half8_t B1 = e4m3x8_to_f16(kt.z, kt.w);
+      half8_t B0, B1;
+      key_operands<kIdxNv>(t == pt ? pv : key[t], B0, B1);
       float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
       acc = mfma16x16x32(A0, B0, acc);
       acc = mfma16x16x32(A1, B1, acc);
@@ -293,6 +339,8 @@ ScoreArgs make_score_args(const msa_kv_pool_t* pool, const msa_step_t* step, con
                           const float* w, float* block_scores) {
   ScoreArgs a{};
   a.index_k = static_cast<const uint8_t*>(pool->index_k);
+  a.index_scales = static_cast<const uint8_t*>(pool->index_scales);
+  a.idx_t = pool->index_tensor_scale;
   a.block_table = step->block_table;
   a.row_seq = step->row_seq;
   a.row_pos = step->row_pos;
@@ -306,10 +354,10 @@ ScoreArgs make_score_args(const msa_kv_pool_t* pool, const msa_step_t* step, con
   return a;
 }
 
-template <bool kFused>
-msa_status_t launch_score(const ScoreArgs& a, int fmt, int hi, dim3 grid, size_t lds, hipStream_t s) {
+template <bool kFused, bool kIdxNv>
+void launch_score_idx(const ScoreArgs& a, int fmt, int hi, dim3 grid, size_t lds, hipStream_t s) {
   const dim3 block(64 * kWaves);
-#define MSA_SCORE_LAUNCH(HI, FMT) score_kernel<HI, FMT, kFused><<<grid, block, lds, s>>>(a)
+#define MSA_SCORE_LAUNCH(HI, FMT) score_kernel<HI, FMT, kFused, kIdxNv><<<grid, block, lds, s>>>(a)
   if (fmt == MSA_KV_NVFP4) {
     if (hi == 1) MSA_SCORE_LAUNCH(1, MSA_KV_NVFP4);
     else if (hi == 2) MSA_SCORE_LAUNCH(2, MSA_KV_NVFP4);
@@ -320,6 +368,13 @@ msa_status_t launch_score(const ScoreArgs& a, int fmt, int hi, dim3 grid, size_t
     else MSA_SCORE_LAUNCH(4, MSA_KV_FP8_E4M3);
   }
 #undef MSA_SCORE_LAUNCH
+}
+
+template <bool kFused>
+msa_status_t launch_score(const ScoreArgs& a, const msa_kv_pool_t* pool, int hi, dim3 grid, size_t lds,
+                          hipStream_t s) {
+  if (index_nvfp4(pool)) launch_score_idx<kFused, true>(a, pool->fmt, hi, grid, lds, s);
+  else launch_score_idx<kFused, false>(a, pool->fmt, hi, grid, lds, s);
   return launch_status();
 }
 
@@ -340,7 +395,7 @@ extern "C" msa_status_t msa_index_score(const msa_kv_pool_t* pool, const msa_ste
   if (step->num_rows > 65535) return MSA_ERR_UNSUPPORTED;
   const ScoreArgs a = make_score_args(pool, step, q_idx, w, block_scores);
   dim3 grid(a.score_wgs_x, step->num_rows);
-  return launch_score<false>(a, pool->fmt, n_idx_heads, grid, 0, static_cast<hipStream_t>(stream));
+  return launch_score<false>(a, pool, n_idx_heads, grid, 0, static_cast<hipStream_t>(stream));
 }
 
 extern "C" msa_status_t msa_append_score_select(
@@ -379,5 +434,5 @@ extern "C" msa_status_t msa_append_score_select(
   a.append_row = n_new > 0 ? 1 : 0;
   dim3 grid(static_cast<unsigned>(std::max<int64_t>(a.score_wgs_x, app_wgs)), step->num_rows + a.append_row);
   const size_t lds = sel ? static_cast<size_t>(step->max_blocks_per_seq) * sizeof(uint32_t) : 0;
-  return launch_score<true>(a, pool->fmt, n_idx_heads, grid, lds, static_cast<hipStream_t>(stream));
+  return launch_score<true>(a, pool, n_idx_heads, grid, lds, static_cast<hipStream_t>(stream));
 }

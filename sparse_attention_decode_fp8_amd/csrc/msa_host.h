@@ -24,8 +24,16 @@ inline msa_status_t check_pool(const msa_kv_pool_t* pool) {
     if (p == nullptr || !aligned16(p)) return MSA_ERR_INVALID_ARG;
   if (pool->fmt == MSA_KV_NVFP4 && !(pool->k_tensor_scale > 0.0f && pool->v_tensor_scale > 0.0f))
     return MSA_ERR_INVALID_ARG;
+  if (pool->index_fmt == MSA_INDEX_NVFP4) {
+    if (pool->index_scales == nullptr || !aligned16(pool->index_scales) || !(pool->index_tensor_scale > 0.0f))
+      return MSA_ERR_INVALID_ARG;
+  } else if (pool->index_fmt != 0 && pool->index_fmt != MSA_INDEX_E4M3) {
+    return MSA_ERR_UNSUPPORTED;
+  }
   return MSA_OK;
 }
+
+inline bool index_nvfp4(const msa_kv_pool_t* pool) { return pool->index_fmt == MSA_INDEX_NVFP4; }
 
 inline msa_status_t check_step(const msa_step_t* step) {
   if (step == nullptr) return MSA_ERR_INVALID_ARG;

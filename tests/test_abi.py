@@ -58,12 +58,20 @@ def test_pool_bytes_and_workspace():
     ws = L.LIB.msa_decode_workspace_bytes(8, 64, 128, 4)
     assert ws == 8 * 64 * 4 * 128 * 4 + 8 * 64 * 4 * 2 * 4
     assert L.LIB.msa_decode_workspace_bytes(-1, 64, 128, 4) == 0
+    isz = (ctypes.c_size_t * 2)()
+    assert L.LIB.msa_index_bytes(1, 10, 64, isz) == 0 and list(isz) == [10 * 128 * 64, 0]
+    assert L.LIB.msa_index_bytes(0, 10, 64, isz) == 0 and list(isz) == [10 * 128 * 64, 0]
+    assert L.LIB.msa_index_bytes(2, 10, 64, isz) == 0 and list(isz) == [10 * 128 * 32, 10 * 128 * 4]
+    assert L.LIB.msa_index_bytes(3, 10, 64, isz) == -2
+    assert L.LIB.msa_index_bytes(2, 10, 32, isz) == -2
+    assert L.LIB.msa_index_bytes(2, 0, 64, isz) == -1
 
 
-def _fake_pool(fmt=2, head_dim=128, k_t=1.0):
+def _fake_pool(fmt=2, head_dim=128, k_t=1.0, index_fmt=0, index_scales=None, index_t=0.0):
     # 16-byte aligned non-null host addresses: validation only, never dereferenced
     a = 1 << 20
-    return L.MsaKvPool(fmt, 4, 2, head_dim, 128, 64, a, a, a, a, k_t, 1.0, a)
+    return L.MsaKvPool(fmt, 4, 2, head_dim, 128, 64, a, a, a, a, k_t, 1.0, a, index_fmt,
+                       index_scales, index_t)
 
 
 def _fake_step(rows=0, max_blocks=8):
@@ -125,6 +133,17 @@ def test_validation_rejects_before_launch():
                                          8, 0, 1, P(16), P(16), None, None, None) == -1
     assert L.LIB.msa_append_score_select(B(pool), B(s1), 0, None, None, None, None, 3, P(16), P(16),
                                          8, 0, 1, P(16), P(16), None, P(16), None) == -2
+    # index-key formats: E4M3 (0 or 1) needs nothing more; NVFP4 needs its scales and
+    # a positive tensor scale; anything else is unsupported
+    a16 = 1 << 20
+    assert L.LIB.msa_kv_append(B(_fake_pool(index_fmt=1)), 0, None, None, None, None, None) == 0
+    assert L.LIB.msa_kv_append(B(_fake_pool(index_fmt=2, index_scales=a16, index_t=0.5)), 0, None,
+                               None, None, None, None) == 0
+    assert L.LIB.msa_kv_append(B(_fake_pool(index_fmt=2, index_t=0.5)), 0, None, None, None, None, None) == -1
+    assert L.LIB.msa_kv_append(B(_fake_pool(index_fmt=2, index_scales=a16)), 0, None, None, None, None, None) == -1
+    assert L.LIB.msa_kv_append(B(_fake_pool(index_fmt=2, index_scales=a16 + 4, index_t=0.5)), 0, None,
+                               None, None, None, None) == -1
+    assert L.LIB.msa_kv_append(B(_fake_pool(index_fmt=5)), 0, None, None, None, None, None) == -2
     nullstep = L.MsaStep(1, 1, 8, None, None, None)
     assert L.LIB.msa_index_score(B(pool), B(nullstep), 4, P(16), P(16), P(16), None) == -1
     # rows need at least one request

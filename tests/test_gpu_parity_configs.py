@@ -26,10 +26,11 @@ def _sample_rows(wl, cfg, n=8):
     return sorted(pick)
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
-def test_config_parity(cfg):
+@pytest.mark.parametrize("cfg,index_fmt", [(0, W.IDX_E4M3), (1, W.IDX_E4M3), (2, W.IDX_E4M3),
+                                           (3, W.IDX_E4M3), (4, W.IDX_E4M3), (1, W.IDX_NVFP4)])
+def test_config_parity(cfg, index_fmt):
     import sparse_attention_decode_fp8_amd as M
-    wl = W.config(cfg)
+    wl = W.config(cfg, index_fmt=index_fmt)
     ns = default_num_splits(wl.k)
     print(f"config {cfg} {wl.name}: rows {wl.num_rows} pages {wl.num_pages} splits {ns}", flush=True)
     pool = G.gpu_pool(M, wl)
@@ -70,9 +71,11 @@ def test_config_parity(cfg):
         names = ["k_codes", "v_codes", "index_k"]
         if wl.fmt == W.FMT_NVFP4:
             names += ["k_scales", "v_scales"]
+        if wl.index_fmt == W.IDX_NVFP4:
+            names += ["index_scales"]
         for name in names:
             g = arrays[name].reshape(opool[name].shape)
-            if name == "index_k":
+            if name.startswith("index"):
                 assert np.array_equal(g[page, off], opool[name][page, off])
             else:
                 assert np.array_equal(g[page, :, off], opool[name][page, :, off]), name
