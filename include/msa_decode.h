@@ -83,9 +83,12 @@ typedef enum {
  *          value = E4M3(code) * page_scale
  *   index_k, MSA_INDEX_E4M3 (default): u8 [num_pages][128][index_dim], one unscaled
  *          E4M3 key per token
- *   index_k, MSA_INDEX_NVFP4: u8 [num_pages][128][index_dim/2] (low nibble = even
- *          element), index_scales u8 (E4M3) [num_pages][128][index_dim/16]; value =
- *          E2M1(code) * E4M3(scale) * index_tensor_scale. [Rubin] Description lists
+ *   index_k, MSA_INDEX_NVFP4: per page, token p = 16 t + n (t < 8, n < 16) and key
+ *          group g (elements 16g .. 16g+15, g < index_dim/16), group-major:
+ *          index_k u8 [num_pages][g][n][t][8] (low nibble = even element),
+ *          index_scales u8 (E4M3) [num_pages][g][n][t]; value =
+ *          E2M1(code) * E4M3(scale) * index_tensor_scale. One group of a page's 8 token
+ *          rows {n, n+16, ..., n+112} is thus 64 contiguous code bytes. [Rubin] Description lists
  *          NVFP4 index-K pages (indexer_kv_dtype='nvfp4', a prototype) without a
  *          recipe; the key is encoded like the NVFP4 KV (see msa_kv_append).
  *
@@ -232,9 +235,10 @@ msa_status_t msa_sparse_decode(const msa_kv_pool_t* pool, const msa_step_t* step
  * (row, KV head) to finish merges all splits of that row and head exactly as
  * msa_combine does ([Rubin] "Items and numerics", LC_ONEDIV) and writes bf16 `out`
  * [num_rows][num_q_heads][head_dim]. part_o / part_ml are written as above (they are
- * the workspace of the merge). counters : int32 [num_rows][num_kv_heads], all zero
- * before the call; the call leaves them zero again. Two calls that share `counters`
- * must not run concurrently. num_splits <= 16.
+ * the workspace of the merge); with num_splits == 1 the one split writes `out`
+ * itself and part_o, part_ml and counters are left untouched. counters : int32
+ * [num_rows][num_kv_heads], all zero before the call; the call leaves them zero
+ * again. Two calls that share `counters` must not run concurrently. num_splits <= 16.
  */
 msa_status_t msa_sparse_decode_combine(const msa_kv_pool_t* pool, const msa_step_t* step,
                                        int32_t num_q_heads, const void* q, const int32_t* sel,

@@ -210,16 +210,19 @@ def new_pool(fmt: int, num_pages: int, num_kv_heads: int, head_dim: int = 128,
       NVFP4: codes u8 [pages][Hkv][128][D/2], scales u8 (e4m3) [pages][Hkv][128][D/16]
       FP8:   codes u8 [pages][Hkv][128][D],   scales fp32 [pages]
       index-K, E4M3:  u8 [pages][128][index_dim], one unscaled key per token
-      index-K, NVFP4: codes u8 [pages][128][index_dim/2], scales u8 (e4m3)
-                      [pages][128][index_dim/16], one fp32 tensor scale
+      index-K, NVFP4: token p of a page = 16 t + n (t = p // 16, n = p % 16), key
+                      group g = 16 elements: codes u8 [pages][g 4][n 16][t 8][8],
+                      scales u8 (e4m3) [pages][g 4][n 16][t 8], one fp32 tensor scale
+                      (group-major so that one group of 8 token rows is contiguous)
     """
     p = {"fmt": fmt, "num_pages": num_pages, "Hkv": num_kv_heads, "D": head_dim,
          "di": index_dim, "index_fmt": index_fmt}
     if index_fmt == IDX_E4M3:
         p["index_k"] = np.zeros((num_pages, PAGE, index_dim), np.uint8)
     elif index_fmt == IDX_NVFP4:
-        p["index_k"] = np.zeros((num_pages, PAGE, index_dim // 2), np.uint8)
-        p["index_scales"] = np.zeros((num_pages, PAGE, index_dim // GROUP), np.uint8)
+        G = index_dim // GROUP
+        p["index_k"] = np.zeros((num_pages, G, 16, PAGE // 16, GROUP // 2), np.uint8)
+        p["index_scales"] = np.zeros((num_pages, G, 16, PAGE // 16), np.uint8)
         p["index_tensor_scale"] = float(np.float32(index_tensor_scale))
     else:
         raise ValueError("unknown index-key format")
@@ -259,8 +262,10 @@ def kv_append(pool: dict, slot: np.ndarray, k_new=None, v_new=None, idx_new=None
             # (indexer_kv_dtype='nvfp4') without a recipe; they take the KV's NVFP4
             # recipe, encoded from the bf16 key with the pool's index tensor scale
             codes, sc = nvfp4_encode(xi, pool["index_tensor_scale"])
-            pool["index_k"][page, off] = pack_nibbles(codes)
-            pool["index_scales"][page, off] = sc
+            packed = pack_nibbles(codes)                            # [n][index_dim / 2]
+            for g in range(sc.shape[1]):
+                pool["index_k"][page, g, off % 16, off // 16] = packed[:, 8 * g:8 * g + 8]
+                pool["index_scales"][page, g, off % 16, off // 16] = sc[:, g]
         else:
             pool["index_k"][page, off] = e4m3_encode(xi)
     for kv, src in (("k", k_new), ("v", v_new)):
@@ -279,9 +284,12 @@ def kv_append(pool: dict, slot: np.ndarray, k_new=None, v_new=None, idx_new=None
 def index_keys(pool: dict, page: int, n: int) -> np.ndarray:
     """Exact value of the first n index keys of a page, float64 [n][index_dim]."""
     if pool["index_fmt"] == IDX_NVFP4:
-        vals = E2M1[unpack_nibbles(pool["index_k"][page, :n])]
-        sc = E4M3[pool["index_scales"][page, :n]]
-        return vals * np.repeat(sc, GROUP, axis=1) * pool["index_tensor_scale"]
+        p = np.arange(n)
+        codes = pool["index_k"][page][:, p % 16, p // 16]                  # [G][n][8]
+        vals = E2M1[unpack_nibbles(codes)]                                 # [G][n][16]
+        sc = E4M3[pool["index_scales"][page][:, p % 16, p // 16]]          # [G][n]
+        keys = vals * sc[:, :, None] * pool["index_tensor_scale"]
+        return np.concatenate(list(keys), axis=1)                          # [n][index_dim]
     return E4M3[pool["index_k"][page, :n]]
 
 

@@ -115,11 +115,13 @@ __device__ __forceinline__ void append_group(const AppendArgs& a, int64_t gid) {
     const uint16_t* src = a.idx_new + static_cast<int64_t>(tok) * kIndexDim + 16 * g;
     const int64_t row = page * kPage + off;
     if (a.index_nvfp4) {
+      // group-major page layout: group g of token 16 t + n at [g][n][t]
       const uint4* p = reinterpret_cast<const uint4*>(src);
       uint32_t w0, w1;
       const uint32_t sc = nvfp4_encode16_bits(p[0], p[1], a.idx_t, w0, w1);
-      *reinterpret_cast<uint2*>(a.index_k + row * (kIndexDim / 2) + 8 * g) = make_uint2(w0, w1);
-      a.index_scales[row * (kIndexDim / 16) + g] = static_cast<uint8_t>(sc);
+      const int64_t at = (page * (kIndexDim / 16) + g) * kPage + (off % 16) * 8 + off / 16;
+      *reinterpret_cast<uint2*>(a.index_k + at * 8) = make_uint2(w0, w1);
+      a.index_scales[at] = static_cast<uint8_t>(sc);
     } else {
       *reinterpret_cast<uint4*>(a.index_k + row * kIndexDim + 16 * g) = encode_index16(src);
     }

@@ -165,9 +165,9 @@ __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
       pos[i] = rowslot[i] < nr ? a.row_pos[r0 + rowslot[i]] : -1;
     }
 
-    // All 8 key loads of the block: lane (n, q) reads its share of token 16t + n, dims
-    // 16q .. 16q+15 (k-step 0 uses the first 8, k-step 1 the last 8): 16 E4M3 bytes,
-    // or 8 NVFP4 code bytes and the group's scale byte. They are issued from the
+    // All key loads of the block: lane (n, q) reads its share of tokens 16t + n, dims
+    // 16q .. 16q+15 (k-step 0 uses the first 8, k-step 1 the last 8): 16 E4M3 bytes per
+    // t, or (NVFP4) 8 code bytes and the group's scale byte per t. They are issued from the
     // guessed request's page (an unused entry reads page 0) and issued again from the
     // right page if the guess was wrong.
     int64_t page = page_g >= 0 ? page_g : 0;
@@ -175,12 +175,19 @@ __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
     auto load_keys = [&]() {
       const int64_t tok0 = page * kPage + n;
       if constexpr (kIdxNv) {
-        const uint8_t* kp = a.index_k + tok0 * (kIndexDim / 2) + 8 * q;
-        const uint8_t* sp = a.index_scales + tok0 * (kIndexDim / 16) + q;
+        // group-major page: lane (n, q)'s 8 token rows are 64 contiguous code bytes and
+        // 8 contiguous scale bytes
+        const int64_t at = (page * (kIndexDim / 16) + q) * kPage + n * 8;
+        const uint4* kp = reinterpret_cast<const uint4*>(a.index_k + at * 8);
+        const uint4 c0 = kp[0], c1 = kp[1], c2 = kp[2], c3 = kp[3];
+        const uint2 sc = *reinterpret_cast<const uint2*>(a.index_scales + at);
+        const uint4 c[4] = {c0, c1, c2, c3};
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-          const uint2 c = *reinterpret_cast<const uint2*>(kp + t * 16 * (kIndexDim / 2));
-          key[t] = make_uint4(c.x, c.y, sp[t * 16 * (kIndexDim / 16)], 0u);
+          const uint4 ct = c[t >> 1];
+          const uint32_t sw = t < 4 ? sc.x : sc.y;
+          key[t] = (t & 1) ? make_uint4(ct.z, ct.w, (sw >> (8 * (t & 3))) & 0xffu, 0u)
+                           : make_uint4(ct.x, ct.y, (sw >> (8 * (t & 3))) & 0xffu, 0u);
         }
       } else {
         const uint8_t* kp = a.index_k + tok0 * kIndexDim + 16 * q;

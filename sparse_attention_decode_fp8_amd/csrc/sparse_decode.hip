@@ -26,7 +26,8 @@
 //
 // The combining variants have the last workgroup of each (row, KV head) to finish
 // merge all splits (a device-scope counter, reset by that workgroup), so the step needs
-// no separate combine launch. The partials cross workgroups (and XCDs, whose L2s are
+// no separate combine launch; with a single split that workgroup writes the output
+// directly and the partials and counter are not touched. The partials cross workgroups (and XCDs, whose L2s are
 // not coherent with each other) as agent-scope atomic stores and loads, which need no
 // cache-flushing fence; on this part such fences cost more than the whole merge. The
 // selecting variant runs the top-k selection of its row in every workgroup (the scores
@@ -428,8 +429,16 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
       }
     }
     if constexpr (kCombine) {
-      store_coherent(ro, ((h * a.num_splits + s) * kHeadDim + 4 * d4) * 4u, acc);
-      if (d4 == 0) store_coherent(rm, (h * a.num_splits + s) * 8u, float2_t{M, l});
+      if (a.num_splits == 1) {   // the only split: its merge is the output (weight exp2(0) = 1)
+        uint16_t o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = l > 0.0f ? f32_to_bf16_rne(acc[i] / l) : 0;
+        *reinterpret_cast<uint2*>(a.out + (head0 + h) * kHeadDim + 4 * d4) =
+            make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16));
+      } else {
+        store_coherent(ro, ((h * a.num_splits + s) * kHeadDim + 4 * d4) * 4u, acc);
+        if (d4 == 0) store_coherent(rm, (h * a.num_splits + s) * 8u, float2_t{M, l});
+      }
     } else {
       float* po = a.part_o + ((head0 + h) * a.num_splits + s) * kHeadDim + 4 * d4;
       float* pm = a.part_ml + ((head0 + h) * a.num_splits + s) * 2;
@@ -441,6 +450,7 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
     }
   }
   if constexpr (kCombine) {
+    if (a.num_splits == 1) return;
     // ---- the last split of this (row, KV head) to finish merges all splits. The partials
     // were written with agent-coherent stores; waiting for them before the counter
     // update orders them before it, and the merging workgroup reads them with

@@ -10,10 +10,18 @@ import torch
 from . import _lib as L
 
 
-def default_num_splits(k: int) -> int:
-    """Split count used by the benchmark and the full-size parity tests: one split per
-    two selected pages (a workgroup of eight waves, one 32-token chunk per wave)."""
-    return max(1, (k + 1) // 2)
+def default_num_splits(k: int, pairs: int) -> int:
+    """Split count used by the benchmark and the full-size parity tests, for `pairs`
+    (query row, KV head) pairs: enough splits for about 256 decode workgroups (one per
+    compute unit), a power of two, at most min(k / 2, 16) so that each split holds at
+    least two blocks. Few pairs (a small batch) are spread over many workgroups whose
+    partials are merged; many pairs fill the GPU on their own and skip the merge (one
+    split writes its output directly)."""
+    target = max(1, 256 // max(1, pairs))
+    s = 1
+    while s * 2 <= min(target, k // 2, 16):
+        s *= 2
+    return s
 
 
 class DecodeBuffers:

@@ -174,6 +174,8 @@ def check_step_parity(M, wl: W.Workload, num_splits: int, fused: bool):
             same[r] = np.array_equal(sel[r], sel_ref[r])
     out = bf16_to_np(bufs.out)
     assert_out_close(out[same], out_ref[same], "outputs")
+    if fused and num_splits == 1:   # the one split writes the output itself: no partials
+        return bufs
     # the split partials the kernel wrote
     m, l, Op = O.split_partials(ref_pool, wl.block_table, wl.row_seq, wl.row_pos, wl.q, sel_ref,
                                 wl.softmax_scale, num_splits)

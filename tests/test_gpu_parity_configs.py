@@ -31,7 +31,7 @@ def _sample_rows(wl, cfg, n=8):
 def test_config_parity(cfg, index_fmt):
     import sparse_attention_decode_fp8_amd as M
     wl = W.config(cfg, index_fmt=index_fmt)
-    ns = default_num_splits(wl.k)
+    ns = default_num_splits(wl.k, wl.num_rows * wl.num_kv_heads)
     print(f"config {cfg} {wl.name}: rows {wl.num_rows} pages {wl.num_pages} splits {ns}", flush=True)
     pool = G.gpu_pool(M, wl)
     bufs = G.run_gpu_step(M, wl, pool, ns)
@@ -75,7 +75,10 @@ def test_config_parity(cfg, index_fmt):
             names += ["index_scales"]
         for name in names:
             g = arrays[name].reshape(opool[name].shape)
-            if name.startswith("index"):
+            if name.startswith("index") and wl.index_fmt == W.IDX_NVFP4:   # [page][g][n][t]
+                assert np.array_equal(g[page, :, off % 16, off // 16],
+                                      opool[name][page, :, off % 16, off // 16]), name
+            elif name.startswith("index"):
                 assert np.array_equal(g[page, off], opool[name][page, off])
             else:
                 assert np.array_equal(g[page, :, off], opool[name][page, :, off]), name

@@ -405,10 +405,16 @@ def test_nvfp4_index_keys_round_trip_exactly():
     O.kv_append(pool, slots, None, None, bits)
     got = np.concatenate([O.index_keys(pool, 0, 23)[3:], O.index_keys(pool, 1, 120)[100:]])
     assert np.array_equal(got, keys)
-    # untouched slots stay zero; low nibble holds the even element
-    assert not pool["index_k"][0, :3].any() and not pool["index_scales"][1, :100].any()
-    c = O.unpack_nibbles(pool["index_k"][0, 3])
-    assert np.array_equal(O.E2M1[c][:16] * O.E4M3[pool["index_scales"][0, 3, 0]] * t, keys[0, :16])
+    # untouched slots stay zero; token p = 16 t + n of group g sits at [g][n][t]; the
+    # low nibble holds the even element
+    written = np.zeros((2, 16, 8), bool)
+    for pg, p in [(0, p) for p in range(3, 23)] + [(1, p) for p in range(100, 120)]:
+        written[pg, p % 16, p // 16] = True
+    for pg in range(2):
+        assert not pool["index_scales"][pg][:, ~written[pg]].any()
+        assert not pool["index_k"][pg][:, ~written[pg]].any()
+    c = O.unpack_nibbles(pool["index_k"][0, 1, 3 % 16, 3 // 16])           # token 3, group 1
+    assert np.array_equal(O.E2M1[c] * O.E4M3[pool["index_scales"][0, 1, 3, 0]] * t, keys[0, 16:32])
 
 
 def test_index_score_same_for_nvfp4_and_e4m3_keys_that_both_hold_exactly():
