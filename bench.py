@@ -194,8 +194,8 @@ def main():
                                                 bufs.block_scores, slot=slot, k_new=k_new,
                                                 v_new=v_new, idx_k_new=idx_new),
             lambda p: M.msa_select_decode_combine(p, step, q, bufs.block_scores, wl.k, wl.n_init,
-                                                  wl.n_local, wl.softmax_scale, ns, bufs.part_o,
-                                                  bufs.part_ml, bufs.counters, bufs.out,
+                                                  wl.n_local, wl.softmax_scale, ns, bufs.merge_o,
+                                                  bufs.merge_ml, bufs.counters, bufs.out,
                                                   sel=bufs.sel, sel_pages=bufs.sel_pages),
         ]
         decode_kernels = ["msa_select_decode_combine"]

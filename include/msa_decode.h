@@ -68,6 +68,8 @@ typedef enum {
 #define MSA_HEADS_PER_KV 16   /* [Rubin] Description: 16 query heads per KV head          */
 #define MSA_MAX_TOPK 64
 #define MSA_MAX_BLOCKS 12288  /* blocks per sequence (1.5M tokens)                        */
+/* Bit pattern of every fp32 word of an idle split-merge workspace (a signalling NaN). */
+#define MSA_MERGE_IDLE_BITS 0x7fbadbadu
 
 /*
  * One layer's paged KV pool. A page holds 128 consecutive tokens of one sequence;
@@ -232,13 +234,18 @@ msa_status_t msa_sparse_decode(const msa_kv_pool_t* pool, const msa_step_t* step
 
 /*
  * msa_sparse_decode followed by msa_combine in one launch: the last split of each
- * (row, KV head) to finish merges all splits of that row and head exactly as
- * msa_combine does ([Rubin] "Items and numerics", LC_ONEDIV) and writes bf16 `out`
- * [num_rows][num_q_heads][head_dim]. part_o / part_ml are written as above (they are
- * the workspace of the merge); with num_splits == 1 the one split writes `out`
- * itself and part_o, part_ml and counters are left untouched. counters : int32
- * [num_rows][num_kv_heads], all zero before the call; the call leaves them zero
- * again. Two calls that share `counters` must not run concurrently. num_splits <= 16.
+ * (row, KV head) to count itself in merges all splits of that row and head exactly as
+ * msa_combine does ([Rubin] "Items and numerics", LC_ONEDIV: same order, same
+ * arithmetic, so `out` equals msa_sparse_decode + msa_combine bit for bit) and writes
+ * bf16 `out` [num_rows][num_q_heads][head_dim].
+ *   part_o, part_ml, counters : the merge workspace, sized as msa_sparse_decode's
+ *     part_o / part_ml and int32 [num_rows][num_kv_heads]. It must be IDLE before the
+ *     call (counters zero, every fp32 word of part_o and part_ml equal to
+ *     MSA_MERGE_IDLE_BITS; msa_merge_workspace_init sets this state) and the call
+ *     leaves it idle: the partials pass through it but are not left readable. With
+ *     num_splits == 1 the one split writes `out` itself and the workspace is not
+ *     touched. Two calls that share a workspace must not run concurrently. A workspace
+ *     sized for S splits serves any num_splits <= S. num_splits <= 16.
  */
 msa_status_t msa_sparse_decode_combine(const msa_kv_pool_t* pool, const msa_step_t* step,
                                        int32_t num_q_heads, const void* q, const int32_t* sel,
@@ -253,7 +260,7 @@ msa_status_t msa_sparse_decode_combine(const msa_kv_pool_t* pool, const msa_step
  * (row, KV head) merges as msa_sparse_decode_combine does.
  *   block_scores : fp32 [num_rows][max_blocks_per_seq] as written by msa_index_score
  *   sel, sel_pages : optional outputs (may be NULL), the selection msa_select_topk writes
- *   counters : int32 [num_rows][num_kv_heads], zero before the call, left zero
+ *   part_o, part_ml, counters : the idle merge workspace of msa_sparse_decode_combine
  * Other arguments as msa_sparse_decode_combine; num_splits <= 16.
  */
 msa_status_t msa_select_decode_combine(const msa_kv_pool_t* pool, const msa_step_t* step,
@@ -262,6 +269,17 @@ msa_status_t msa_select_decode_combine(const msa_kv_pool_t* pool, const msa_step
                                        int32_t n_local, float softmax_scale, int32_t num_splits,
                                        float* part_o, float* part_ml, int32_t* counters,
                                        void* out, int32_t* sel, int32_t* sel_pages, void* stream);
+
+/*
+ * Put a merge workspace for the two *_combine entries into its idle state: counters
+ * [rows][num_q_heads / 16] = 0 and part_o [rows][num_q_heads][num_splits][head_dim],
+ * part_ml [rows][num_q_heads][num_splits][2] = MSA_MERGE_IDLE_BITS in every word, by a
+ * fill kernel on `stream` (no memset nodes, so the call may be captured in a graph).
+ * Needed once after allocation, and again only if something else wrote the workspace.
+ */
+msa_status_t msa_merge_workspace_init(int32_t rows, int32_t num_q_heads, int32_t head_dim,
+                                      int32_t num_splits, float* part_o, float* part_ml,
+                                      int32_t* counters, void* stream);
 
 /*
  * Log-sum-exp merge of split partials ([Rubin] "Items and numerics", LC_ONEDIV: the

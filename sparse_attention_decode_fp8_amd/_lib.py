@@ -25,6 +25,7 @@ HEAD_DIM = 128
 INDEX_DIM = 64
 
 MSA_OK = 0
+MERGE_IDLE_BITS = 0x7fbadbad   # every fp32 word of an idle merge workspace
 
 
 class MsaError(RuntimeError):
@@ -51,6 +52,7 @@ class MsaStep(ctypes.Structure):
 EXPORTS = ["msa_kv_append", "msa_index_score", "msa_select_topk", "msa_append_score_select",
            "msa_sparse_decode",
            "msa_sparse_decode_combine", "msa_select_decode_combine", "msa_combine",
+           "msa_merge_workspace_init",
            "msa_decode_workspace_bytes", "msa_pool_bytes", "msa_index_bytes", "msa_status_string"]
 
 
@@ -69,6 +71,7 @@ def _load():
         "msa_sparse_decode_combine": (I32, [P, P, I32, P, P, P, I32, F32, I32, P, P, P, P, P]),
         "msa_select_decode_combine": (I32, [P, P, I32, P, P, I32, I32, I32, F32, I32, P, P, P, P, P, P, P]),
         "msa_combine": (I32, [I32, I32, I32, I32, P, P, P, P]),
+        "msa_merge_workspace_init": (I32, [I32, I32, I32, I32, P, P, P, P]),
         "msa_decode_workspace_bytes": (SZ, [I32, I32, I32, I32]),
         "msa_pool_bytes": (I32, [I32, I32, I32, I32, I32, ctypes.POINTER(SZ)]),
         "msa_index_bytes": (I32, [I32, I32, I32, ctypes.POINTER(SZ)]),
@@ -252,6 +255,15 @@ def msa_combine(rows, num_q_heads, head_dim, num_splits, part_o, part_ml, out, s
                            _ptr(part_o, torch.float32, "part_o"), _ptr(part_ml, torch.float32, "part_ml"),
                            _ptr(out, torch.bfloat16, "out"), _stream(stream)),
            "msa_combine")
+
+
+def msa_merge_workspace_init(rows, num_q_heads, head_dim, num_splits, part_o, part_ml, counters,
+                             stream=None):
+    _check(LIB.msa_merge_workspace_init(rows, num_q_heads, head_dim, num_splits,
+                                        _ptr(part_o, torch.float32, "part_o"),
+                                        _ptr(part_ml, torch.float32, "part_ml"),
+                                        _ptr(counters, torch.int32, "counters"), _stream(stream)),
+           "msa_merge_workspace_init")
 
 
 def msa_decode_workspace_bytes(rows, num_q_heads, head_dim, num_splits) -> int:

@@ -127,6 +127,15 @@ __device__ __forceinline__ float xor_add(float v, int mask) {
 // the vector memory counter and a device-scope atomic order the two. Offsets are in
 // bytes from the resource's base; the range is [base, base + bytes).
 constexpr int kCoherentPolicy = 16;   // sc1
+// A pointer the caller knows to be the same in every lane, moved to scalar registers
+// (a resource built from it then needs no per-lane loop).
+template <class T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<T*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
 }
@@ -145,6 +154,25 @@ __device__ __forceinline__ float4_t load_coherent4(__amdgpu_buffer_rsrc_t r, uin
 __device__ __forceinline__ float2_t load_coherent2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(float2_t, __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(off), 0,
                                                                          kCoherentPolicy));
+}
+
+// Split-merge slots hold MSA_MERGE_IDLE_BITS (a signalling NaN, which no arithmetic
+// produces) until written; a written value that happens to carry that pattern is
+// stored as the default quiet NaN instead.
+// Number of words still idle (no short-circuit: every load's value is inspected, so
+// the compiler has no reason to move a load into a branch behind another one's test).
+__device__ __forceinline__ uint32_t idle_words(float v) { return __float_as_uint(v) == MSA_MERGE_IDLE_BITS; }
+__device__ __forceinline__ uint32_t idle_words(float2_t v) { return idle_words(v[0]) + idle_words(v[1]); }
+__device__ __forceinline__ uint32_t idle_words(float4_t v) {
+  return idle_words(v[0]) + idle_words(v[1]) + idle_words(v[2]) + idle_words(v[3]);
+}
+__device__ __forceinline__ float not_idle(float v) {
+  return __float_as_uint(v) == MSA_MERGE_IDLE_BITS ? __uint_as_float(0x7fc00000u) : v;
+}
+// Workgroup barrier that orders LDS only: waits for this wave's LDS accesses, not for
+// its outstanding global stores.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Request a row belongs to when every request has the same number of rows (the

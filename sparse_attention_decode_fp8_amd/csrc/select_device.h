@@ -180,6 +180,9 @@ __device__ __forceinline__ void wave_select_table(const float* srow, const int32
     pg[i] = in_row ? bt[lo + c] : -1;
   }
   const int32_t pg_init = lane < n_init && lane < max_blocks ? bt[lane] : -1;   // blocks below lo
+  // Slots 64 kR .. 64 kR + 63 past the keys hold only forced last blocks (n_local <= 64):
+  // their pages are read now too, so no block-table read waits for the row's length.
+  const int32_t pg_tail = lo + 64 * kR + lane < max_blocks ? bt[lo + 64 * kR + lane] : -1;
   // The row's position is read only now, so its load queues behind the score loads
   // instead of holding them back.
   asm volatile("" ::: "memory");
@@ -201,9 +204,21 @@ __device__ __forceinline__ void wave_select_table(const float* srow, const int32
     return;
   }
   // Forced entries and padding; the `want` entries in between come from the search.
-  // The last n_local blocks' pages are read now and written after the search, so that
-  // read overlaps it.
-  const int32_t pg_local = lane < n_local ? bt[nb - n_local + lane] : -1;
+  // Lane j < n_local takes the page of block nb - n_local + j from the lane holding its
+  // slot c (lane c / kR, register c % kR, or the tail registers past 64 kR).
+  int32_t pg_local = -1;
+  {
+    const int c = nb - n_local + min(lane, n_local - 1) - lo;   // 0 <= c < 64 kR + 64
+    const bool tail = c >= 64 * kR;
+    const int src = tail ? c - 64 * kR : c / kR;
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+      const int32_t v = __shfl(pg[i], src, 64);
+      if (!tail && c % kR == i) pg_local = v;
+    }
+    const int32_t v = __shfl(pg_tail, src, 64);
+    if (tail) pg_local = v;
+  }
   if (lane < n_init) { sel[lane] = lane; pages[lane] = pg_init; }
   if (lane >= k) { sel[lane] = -1; pages[lane] = -1; }
   auto write_local = [&]() {

@@ -49,6 +49,10 @@ constexpr int kVBufBytes = 32 * kVRowHalves * 2;   // one wave's 32-token V chun
 constexpr int kORowFloats = kHeadDim + 4;
 static_assert(16 * kORowFloats * 4 <= kVBufBytes, "O tile must fit in a V buffer");
 constexpr int kMaxCombineSplits = 16;
+// Bound on the merger's polls of one slot. Every slot it polls has been stored by a
+// split that is already past its compute, so a few polls suffice; the bound only keeps
+// the loop finite (past it the merge uses what it read).
+constexpr int kMergePollLimit = 1 << 16;
 
 struct DecodeArgs {
   const uint8_t* k_codes;
@@ -180,6 +184,63 @@ __device__ __forceinline__ void load_round(Round<kFmt, kItems>& rd, const Decode
         rd.kps[j] = reinterpret_cast<const float*>(a.k_scales)[pages[j]];
         rd.vps[j] = reinterpret_cast<const float*>(a.v_scales)[pages[j]];
       }
+    }
+  }
+}
+
+// The merging split's read of one (head, 4 dims) item: all S <= kS slots (its own
+// included: the thread stored its part of it, so it reads its own values back), then
+// the fixed-order log-sum-exp sums of msa_combine. Slots whose words have not all
+// landed are read again, which is rare: the other splits counted themselves in
+// earlier. Entries S..kS-1 repeat the last slot and are not used, so every entry is
+// redefined on each read and none is carried from one poll to the next. The item's
+// words are put back to idle as soon as they have been read.
+template <int kS>
+__device__ __forceinline__ void merge_slots(__amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t rm, int S,
+                                            int h, int d4, float4_t& num, float& den) {
+  float2_t mls[kS];
+  float4_t ot[kS];
+  bool ready = false;
+  for (int spin = 0; !ready && spin < kMergePollLimit; ++spin) {
+    if (spin > 0) {
+      __builtin_amdgcn_s_sleep(2);
+      asm volatile("" ::: "memory");   // load again
+    }
+#pragma unroll
+    for (int t = 0; t < kS; ++t) {   // every load first, one wait
+      const int tt = min(t, S - 1);
+      mls[t] = load_coherent2(rm, (h * S + tt) * 8u);
+      ot[t] = load_coherent4(ro, ((h * S + tt) * kHeadDim + 4 * d4) * 4u);
+    }
+    asm volatile("" ::: "memory");   // the loads stay together, ahead of their tests
+    uint32_t idle = 0;
+#pragma unroll
+    for (int t = 0; t < kS; ++t) idle += idle_words(mls[t]) + idle_words(ot[t]);
+    ready = idle == 0;
+  }
+  // The slots go back to the idle pattern now, while the merge below is computed: this
+  // thread is the only reader of its O words, and the 32 readers of a head's (m, l)
+  // words are the lanes of this wave, whose loads have all returned.
+  const float idle_v = __uint_as_float(MSA_MERGE_IDLE_BITS);
+#pragma unroll
+  for (int t = 0; t < kS; ++t) {
+    const int tt = min(t, S - 1);
+    store_coherent(ro, ((h * S + tt) * kHeadDim + 4 * d4) * 4u, float4_t{idle_v, idle_v, idle_v, idle_v});
+    store_coherent(rm, (h * S + tt) * 8u, float2_t{idle_v, idle_v});
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < kS; ++t)
+    if (t < S) M = fmaxf(M, mls[t][0]);
+  num = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  den = 0.0f;
+#pragma unroll
+  for (int t = 0; t < kS; ++t) {
+    if (t < S) {
+      const float m = mls[t][0];
+      const float wgt = m == -INFINITY ? 0.0f : exp2f(m - M);   // M > -inf whenever m is
+      den += wgt * mls[t][1];
+      num += wgt * ot[t];
     }
   }
 }
@@ -410,36 +471,45 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
   __syncthreads();
   // this (row, KV head)'s partials: O [16 heads][S][128], (m, l) [16 heads][S][2]
   const uint32_t o_bytes = 16u * a.num_splits * kHeadDim * 4, ml_bytes = 16u * a.num_splits * 8;
-  const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.part_o + head0 * a.num_splits * kHeadDim, o_bytes);
-  const __amdgpu_buffer_rsrc_t rm = make_rsrc(a.part_ml + head0 * a.num_splits * 2, ml_bytes);
-  for (int idx = threadIdx.x; idx < 16 * (kHeadDim / 4); idx += 64 * kW) {
-    const int h = idx / (kHeadDim / 4), d4 = idx % (kHeadDim / 4);
-    float M = -INFINITY;
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(uniform_ptr(a.part_o + head0 * a.num_splits * kHeadDim), o_bytes);
+  const __amdgpu_buffer_rsrc_t rm = make_rsrc(uniform_ptr(a.part_ml + head0 * a.num_splits * 2), ml_bytes);
+  constexpr int kTasks = 16 * (kHeadDim / 4);                     // (head, 4 dims) items
+  constexpr int kPer = (kTasks + 64 * kW - 1) / (64 * kW);        // items per thread
+  // In-workgroup merge of one item over the waves' O tiles. Every LDS read is issued
+  // before the first use, so their latencies overlap.
+  auto wg_merge = [&](int h, int d4, float4_t& acc, float& M, float& l) {
+    float mw[kW], lw[kW];
+    float4_t tw[kW];
 #pragma unroll
-    for (int w = 0; w < kW; ++w) M = fmaxf(M, mbuf[w][h]);
-    float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    float l = 0.0f;
+    for (int w = 0; w < kW; ++w) {
+      mw[w] = mbuf[w][h];
+      lw[w] = lbuf[w][h];
+      tw[w] = *reinterpret_cast<const float4_t*>(reinterpret_cast<const float*>(dyn_lds + w * kVBufBytes) +
+                                                 h * kORowFloats + 4 * d4);
+    }
+    M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kW; ++w) M = fmaxf(M, mw[w]);
+    acc = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    l = 0.0f;
     if (M != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < kW; ++w) {
-        const float wt = exp2f(mbuf[w][h] - M);
-        acc += wt * *reinterpret_cast<const float4_t*>(
-                        reinterpret_cast<const float*>(dyn_lds + w * kVBufBytes) + h * kORowFloats + 4 * d4);
-        l += wt * lbuf[w][h];
+        const float wt = exp2f(mw[w] - M);
+        acc += wt * tw[w];
+        l += wt * lw[w];
       }
     }
-    if constexpr (kCombine) {
-      if (a.num_splits == 1) {   // the only split: its merge is the output (weight exp2(0) = 1)
-        uint16_t o[4];
+  };
+  if constexpr (!kCombine) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = l > 0.0f ? f32_to_bf16_rne(acc[i] / l) : 0;
-        *reinterpret_cast<uint2*>(a.out + (head0 + h) * kHeadDim + 4 * d4) =
-            make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16));
-      } else {
-        store_coherent(ro, ((h * a.num_splits + s) * kHeadDim + 4 * d4) * 4u, acc);
-        if (d4 == 0) store_coherent(rm, (h * a.num_splits + s) * 8u, float2_t{M, l});
-      }
-    } else {
+    for (int it = 0; it < kPer; ++it) {
+      const int idx = threadIdx.x + it * 64 * kW;
+      if (idx >= kTasks) break;
+      const int h = idx / (kHeadDim / 4), d4 = idx % (kHeadDim / 4);
+      float4_t acc;
+      float M, l;
+      wg_merge(h, d4, acc, M, l);
       float* po = a.part_o + ((head0 + h) * a.num_splits + s) * kHeadDim + 4 * d4;
       float* pm = a.part_ml + ((head0 + h) * a.num_splits + s) * 2;
       *reinterpret_cast<float4_t*>(po) = acc;
@@ -448,54 +518,70 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
         pm[1] = l;
       }
     }
-  }
-  if constexpr (kCombine) {
-    if (a.num_splits == 1) return;
-    // ---- the last split of this (row, KV head) to finish merges all splits. The partials
-    // were written with agent-coherent stores; waiting for them before the counter
-    // update orders them before it, and the merging workgroup reads them with
-    // agent-coherent loads issued after it saw the count, wherever the workgroups ran.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const int old = atomicAdd(a.counters + static_cast<int64_t>(r) * a.hkv + g, 1);
-      s_last = old == a.num_splits - 1;
-    }
-    __syncthreads();
-    if (!s_last) return;
-    for (int idx = threadIdx.x; idx < 16 * (kHeadDim / 4); idx += 64 * kW) {
+  } else if (a.num_splits == 1) {
+    // the only split: its merge is the output (merge weight exp2(0) = 1)
+#pragma unroll
+    for (int it = 0; it < kPer; ++it) {
+      const int idx = threadIdx.x + it * 64 * kW;
+      if (idx >= kTasks) break;
       const int h = idx / (kHeadDim / 4), d4 = idx % (kHeadDim / 4);
-      float2_t mls[kMaxCombineSplits];
-      float4_t ot[kMaxCombineSplits];
+      float4_t acc;
+      float M, l;
+      wg_merge(h, d4, acc, M, l);
+      uint16_t o[4];
 #pragma unroll
-      for (int t = 0; t < kMaxCombineSplits; ++t) {    // every load first, one wait
-        if (t < a.num_splits) {
-          mls[t] = load_coherent2(rm, (h * a.num_splits + t) * 8u);
-          ot[t] = load_coherent4(ro, ((h * a.num_splits + t) * kHeadDim + 4 * d4) * 4u);
-        }
-      }
-      float M = -INFINITY;
+      for (int i = 0; i < 4; ++i) o[i] = l > 0.0f ? f32_to_bf16_rne(acc[i] / l) : 0;
+      *reinterpret_cast<uint2*>(a.out + (head0 + h) * kHeadDim + 4 * d4) =
+          make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16));
+    }
+  } else {
+    // ---- several splits: the last split of this (row, KV head) to count itself in
+    // merges them all. Each split counts itself in as soon as its compute is done, then
+    // stores its partial (agent-coherent) and only then reads the old count, so nothing
+    // waits for the stores to land; the merger polls each slot until none of its words
+    // holds the idle pattern. Every split it waits for has counted itself in, so it is
+    // resident with only in-workgroup work left before its stores: the polls end. The
+    // merger then puts every slot back to the idle pattern and the counter back to
+    // zero, ready for the next launch.
+    int arrival = 0;
+    if (threadIdx.x == 0) arrival = atomicAdd(a.counters + static_cast<int64_t>(r) * a.hkv + g, 1);
 #pragma unroll
-      for (int t = 0; t < kMaxCombineSplits; ++t)
-        if (t < a.num_splits) M = fmaxf(M, mls[t][0]);
-      float4_t num = {0.0f, 0.0f, 0.0f, 0.0f};
-      float den = 0.0f;
+    for (int it = 0; it < kPer; ++it) {
+      // threads past the last item repeat an item (same values, same addresses), so no
+      // thread skips the stores
+      const int idx = (threadIdx.x + it * 64 * kW) % kTasks;
+      const int h = idx / (kHeadDim / 4), d4 = idx % (kHeadDim / 4);
+      float4_t acc;
+      float M, l;
+      wg_merge(h, d4, acc, M, l);
+      store_coherent(ro, ((h * a.num_splits + s) * kHeadDim + 4 * d4) * 4u,
+                     float4_t{not_idle(acc[0]), not_idle(acc[1]), not_idle(acc[2]), not_idle(acc[3])});
+      // (m, l) from all 32 threads of the head (same value): with no branch anywhere
+      // here, the number of stores issued after the count is fixed and reading the count
+      // does not wait for them
+      store_coherent(rm, (h * a.num_splits + s) * 8u, float2_t{not_idle(M), not_idle(l)});
+    }
+    if (threadIdx.x == 0) s_last = arrival == a.num_splits - 1;
+    lds_barrier();
+    if (!s_last) return;
 #pragma unroll
-      for (int t = 0; t < kMaxCombineSplits; ++t) {
-        if (t < a.num_splits) {
-          const float m = mls[t][0];
-          const float wgt = m == -INFINITY ? 0.0f : exp2f(m - M);   // M > -inf whenever m is
-          den += wgt * mls[t][1];
-          num += wgt * ot[t];
-        }
-      }
+    for (int it = 0; it < kPer; ++it) {
+      const int idx = threadIdx.x + it * 64 * kW;
+      if (idx >= kTasks) break;
+      const int h = idx / (kHeadDim / 4), d4 = idx % (kHeadDim / 4);
+      float4_t num;
+      float den;
+      if (a.num_splits <= 2) merge_slots<2>(ro, rm, a.num_splits, h, d4, num, den);
+      else if (a.num_splits <= 4) merge_slots<4>(ro, rm, a.num_splits, h, d4, num, den);
+      else if (a.num_splits <= 8) merge_slots<8>(ro, rm, a.num_splits, h, d4, num, den);
+      else merge_slots<16>(ro, rm, a.num_splits, h, d4, num, den);
       uint16_t o[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[i] = den > 0.0f ? f32_to_bf16_rne(num[i] / den) : 0;
       *reinterpret_cast<uint2*>(a.out + (head0 + h) * kHeadDim + 4 * d4) =
           make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16));
     }
-    if (threadIdx.x == 0)   // ready for the next launch
+    if (threadIdx.x == 0)
       __hip_atomic_store(a.counters + static_cast<int64_t>(r) * a.hkv + g, 0, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
   }

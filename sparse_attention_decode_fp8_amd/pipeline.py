@@ -25,7 +25,10 @@ def default_num_splits(k: int, pairs: int) -> int:
 
 
 class DecodeBuffers:
-    """Per-step outputs and the split-KV workspace for a fixed geometry."""
+    """Per-step outputs and the split-KV workspaces for a fixed geometry: part_o /
+    part_ml receive the partials of the separate msa_sparse_decode call; merge_o /
+    merge_ml / counters are the fused entries' merge workspace, put into its idle state
+    here and left idle by every fused call."""
 
     def __init__(self, num_rows, num_q_heads, max_blocks, k, num_splits, device="cuda"):
         self.k, self.num_splits = k, num_splits
@@ -36,7 +39,11 @@ class DecodeBuffers:
                                   dtype=torch.float32, device=device)
         self.part_ml = torch.empty((num_rows, num_q_heads, num_splits, 2), dtype=torch.float32,
                                    device=device)
-        self.counters = torch.zeros((num_rows, num_q_heads // 16), dtype=torch.int32, device=device)
+        self.merge_o = torch.empty_like(self.part_o)
+        self.merge_ml = torch.empty_like(self.part_ml)
+        self.counters = torch.empty((num_rows, num_q_heads // 16), dtype=torch.int32, device=device)
+        L.msa_merge_workspace_init(num_rows, num_q_heads, L.HEAD_DIM, num_splits, self.merge_o,
+                                   self.merge_ml, self.counters)
         self.score_counters = torch.zeros(num_rows, dtype=torch.int32, device=device)
         self.out = torch.empty((num_rows, num_q_heads, L.HEAD_DIM), dtype=torch.bfloat16, device=device)
 
@@ -51,7 +58,7 @@ def run_step(pool, step, bufs: DecodeBuffers, q, q_idx, w, softmax_scale, slot=N
                                   slot=slot, k_new=k_new, v_new=v_new, idx_k_new=idx_k_new,
                                   stream=stream)
         L.msa_select_decode_combine(pool, step, q, bufs.block_scores, bufs.k, n_init, n_local,
-                                    softmax_scale, bufs.num_splits, bufs.part_o, bufs.part_ml,
+                                    softmax_scale, bufs.num_splits, bufs.merge_o, bufs.merge_ml,
                                     bufs.counters, bufs.out, sel=bufs.sel, sel_pages=bufs.sel_pages,
                                     stream=stream)
         return bufs.out

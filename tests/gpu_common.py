@@ -152,6 +152,15 @@ def oracle_rows(wl: W.Workload, rows):
     return S, sel, out, pool
 
 
+def assert_merge_idle(bufs):
+    """The fused entries leave their merge workspace idle: counters zero, every word of
+    the partial slots the idle pattern."""
+    import sparse_attention_decode_fp8_amd as M
+    assert int(bufs.counters.abs().sum()) == 0
+    for t in (bufs.merge_o, bufs.merge_ml):
+        assert bool((t.view(torch.int32) == M.MERGE_IDLE_BITS).all())   # 0x7fbadbad < 2^31
+
+
 def check_step_parity(M, wl: W.Workload, num_splits: int, fused: bool):
     """Run one whole step on the GPU and compare scores, selection, outputs and the
     split partials with the oracle, computed from the same seeded source."""
@@ -174,7 +183,8 @@ def check_step_parity(M, wl: W.Workload, num_splits: int, fused: bool):
             same[r] = np.array_equal(sel[r], sel_ref[r])
     out = bf16_to_np(bufs.out)
     assert_out_close(out[same], out_ref[same], "outputs")
-    if fused and num_splits == 1:   # the one split writes the output itself: no partials
+    if fused:   # the partials passed through the merge workspace, which is idle again
+        assert_merge_idle(bufs)
         return bufs
     # the split partials the kernel wrote
     m, l, Op = O.split_partials(ref_pool, wl.block_table, wl.row_seq, wl.row_pos, wl.q, sel_ref,

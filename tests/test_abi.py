@@ -122,6 +122,13 @@ def test_validation_rejects_before_launch():
                                            P(16), P(16), None, None) == -1
     assert L.LIB.msa_sparse_decode_combine(B(pool), B(step), 32, P(16), P(16), None, 8, 0.1, 2, P(16),
                                            P(16), P(16), P(16), None) == 0
+    # the merge workspace fill: empty is OK; geometry and pointers are checked
+    assert L.LIB.msa_merge_workspace_init(0, 32, 128, 2, None, None, None, None) == 0
+    assert L.LIB.msa_merge_workspace_init(1, 32, 64, 2, P(16), P(16), P(16), None) == -2
+    assert L.LIB.msa_merge_workspace_init(1, 24, 128, 2, P(16), P(16), P(16), None) == -2
+    assert L.LIB.msa_merge_workspace_init(-1, 32, 128, 2, P(16), P(16), P(16), None) == -1
+    assert L.LIB.msa_merge_workspace_init(1, 32, 128, 0, P(16), P(16), P(16), None) == -1
+    assert L.LIB.msa_merge_workspace_init(1, 32, 128, 2, P(16), None, P(16), None) == -1
     # fused append + score + select
     assert L.LIB.msa_append_score_select(B(pool), B(step), 0, None, None, None, None, 4, P(16), P(16),
                                          8, 0, 1, P(16), P(16), None, P(16), None) == 0

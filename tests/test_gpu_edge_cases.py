@@ -67,7 +67,7 @@ def test_nothing_to_do_leaves_outputs_untouched(M):
     M.msa_combine(0, wl.num_heads, 128, 2, bufs.part_o, bufs.part_ml, bufs.out)
     M.msa_append_score_select(pool, empty, q_idx, w, wl.k, 0, 1, bufs.block_scores)
     M.msa_select_decode_combine(pool, empty, q, bufs.block_scores, wl.k, 0, 1, wl.softmax_scale, 2,
-                                bufs.part_o, bufs.part_ml, bufs.counters, bufs.out)
+                                bufs.merge_o, bufs.merge_ml, bufs.counters, bufs.out)
     torch.cuda.synchronize()
     for k, v in pool.arrays().items():
         assert torch.equal(v, before[k]), k

@@ -192,8 +192,8 @@ def test_sel_pages_and_fused_combine(M):
             assert torch.equal(arr, pc.arrays()[name]), name
         # a second call with the same counters still merges correctly
         step, q, q_idx, w, _ = G.gpu_step_inputs(M, wl)
-        M.msa_sparse_decode_combine(pa, step, q, a.sel, wl.k, wl.softmax_scale, ns, a.part_o,
-                                    a.part_ml, a.counters, a.out, sel_pages=a.sel_pages)
+        M.msa_sparse_decode_combine(pa, step, q, a.sel, wl.k, wl.softmax_scale, ns, a.merge_o,
+                                    a.merge_ml, a.counters, a.out, sel_pages=a.sel_pages)
         torch.cuda.synchronize()
         assert torch.equal(a.out.view(torch.int16), b.out.view(torch.int16))
 
