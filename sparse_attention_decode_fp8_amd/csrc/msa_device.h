@@ -89,7 +89,7 @@ __device__ __forceinline__ int f16_prescale_exp(float amax) {
   return 15 - ex;
 }
 
-// Wave-wide OR / AND of a 32-bit value with DPP moves (row shifts 1, 2, 4, 8 within each
+// Wave-wide OR / AND / max of a 32-bit value with DPP moves (row shifts 1, 2, 4, 8 within each
 // row of 16 lanes, then the row broadcasts of lanes 15 and 31), read back from lane 63:
 // vector ALU only, no LDS round trips. Lanes a move has no source for keep the
 // identity (0 for OR, all ones for AND).
@@ -112,6 +112,17 @@ __device__ __forceinline__ uint32_t wave_and(uint32_t v) {
   x &= __builtin_amdgcn_update_dpp(-1, x, 0x142, 0xa, 0xf, false);
   x &= __builtin_amdgcn_update_dpp(-1, x, 0x143, 0xc, 0xf, false);
   return static_cast<uint32_t>(__builtin_amdgcn_readlane(x, 63));
+}
+// Wave-wide unsigned maximum, the same moves (identity 0).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  uint32_t x = v;
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x111, 0xf, 0xf, false)));
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x112, 0xf, 0xf, false)));
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x114, 0xf, 0xf, false)));
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x118, 0xf, 0xf, false)));
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x142, 0xa, 0xf, false)));
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x143, 0xc, 0xf, false)));
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), 63));
 }
 
 __device__ __forceinline__ float xor_max(float v, int mask) {
@@ -156,18 +167,18 @@ __device__ __forceinline__ float2_t load_coherent2(__amdgpu_buffer_rsrc_t r, uin
                                                                          kCoherentPolicy));
 }
 
-// Split-merge slots hold MSA_MERGE_IDLE_BITS (a signalling NaN, which no arithmetic
-// produces) until written; a written value that happens to carry that pattern is
-// stored as the default quiet NaN instead.
-// Number of words still idle (no short-circuit: every load's value is inspected, so
-// the compiler has no reason to move a load into a branch behind another one's test).
-__device__ __forceinline__ uint32_t idle_words(float v) { return __float_as_uint(v) == MSA_MERGE_IDLE_BITS; }
-__device__ __forceinline__ uint32_t idle_words(float2_t v) { return idle_words(v[0]) + idle_words(v[1]); }
-__device__ __forceinline__ uint32_t idle_words(float4_t v) {
-  return idle_words(v[0]) + idle_words(v[1]) + idle_words(v[2]) + idle_words(v[3]);
+// Split-merge slots hold MSA_MERGE_IDLE_BITS (a signalling NaN) until written. A
+// written value is canonicalised first, which turns a signalling NaN into a quiet one
+// and leaves every other value as it is, so no written word carries the pattern.
+__device__ __forceinline__ float not_idle(float v) { return __builtin_canonicalizef(v); }
+// min over the words of (word ^ pattern): zero exactly when some word still holds the
+// pattern. Plain vector arithmetic, no compares into scalar masks.
+__device__ __forceinline__ uint32_t idle_key(uint32_t acc, float v) {
+  return min(acc, __float_as_uint(v) ^ MSA_MERGE_IDLE_BITS);
 }
-__device__ __forceinline__ float not_idle(float v) {
-  return __float_as_uint(v) == MSA_MERGE_IDLE_BITS ? __uint_as_float(0x7fc00000u) : v;
+__device__ __forceinline__ uint32_t idle_key(uint32_t acc, float2_t v) { return idle_key(idle_key(acc, v[0]), v[1]); }
+__device__ __forceinline__ uint32_t idle_key(uint32_t acc, float4_t v) {
+  return idle_key(idle_key(idle_key(idle_key(acc, v[0]), v[1]), v[2]), v[3]);
 }
 // Workgroup barrier that orders LDS only: waits for this wave's LDS accesses, not for
 // its outstanding global stores.

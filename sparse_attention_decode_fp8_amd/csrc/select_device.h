@@ -87,7 +87,20 @@ __device__ void block_select_row(const float* srow, int nb, int k, int n_init, i
     __syncthreads();
     for (int c = tid; c < C; c += kThreads) {
       const uint32_t kk = keys[c];
-      if ((kk & pmask) == prefix) atomicAdd(&sm.hist[(kk >> shift) & 255u], 1);
+      const bool match = (kk & pmask) == prefix;
+      const uint32_t dg = (kk >> shift) & 255u;
+      // Lanes that all add to the same bin (ties, or a shared digit) add once, by
+      // their first lane: equal keys would otherwise serialise on one LDS address.
+      const uint64_t mm = __ballot(match);
+      if (mm == 0) continue;
+      const int first = __ffsll(static_cast<unsigned long long>(mm)) - 1;
+      const uint32_t d0 = static_cast<uint32_t>(__shfl(static_cast<int>(dg), first, 64));
+      const uint64_t same = __ballot(match && dg == d0);
+      if (same == mm) {
+        if ((tid & 63) == first) atomicAdd(&sm.hist[d0], __popcll(mm));
+      } else if (match) {
+        atomicAdd(&sm.hist[dg], 1);
+      }
     }
     __syncthreads();
     if (tid < 64) {                              // wave 0 finds the digit holding the rank
@@ -229,6 +242,15 @@ __device__ __forceinline__ void wave_select_table(const float* srow, const int32
     return;
   }
 
+  // Ties at the largest key (want or more candidates share it): that key is the
+  // threshold, without a bit-by-bit search that could never stop early.
+  uint32_t k_max = 0u;
+#pragma unroll
+  for (int i = 0; i < kR; ++i) k_max = max(k_max, key[i]);
+  k_max = wave_max_u32(k_max);
+  int n_max = 0;
+#pragma unroll
+  for (int i = 0; i < kR; ++i) n_max += __popcll(__ballot(key[i] == k_max));
   // The bits every candidate shares are the threshold's too: start below them.
   uint32_t k_or = 0u, k_and = ~0u;
 #pragma unroll
@@ -250,6 +272,11 @@ __device__ __forceinline__ void wave_select_table(const float* srow, const int32
   };
   int bit = top;
   bool done = false;
+  if (n_max >= want) {
+    T = k_max;
+    bit = -1;
+    done = true;
+  }
   for (; bit >= 1; bit -= 2) {                   // bits bit, bit-1
     const uint32_t c1 = T | (1u << (bit - 1)), c2 = T | (2u << (bit - 1)), c3 = T | (3u << (bit - 1));
     const int n1 = count_ge(c1), n2 = count_ge(c2), n3 = count_ge(c3);   // n1 >= n2 >= n3

@@ -213,10 +213,10 @@ __device__ __forceinline__ void merge_slots(__amdgpu_buffer_rsrc_t ro, __amdgpu_
       ot[t] = load_coherent4(ro, ((h * S + tt) * kHeadDim + 4 * d4) * 4u);
     }
     asm volatile("" ::: "memory");   // the loads stay together, ahead of their tests
-    uint32_t idle = 0;
+    uint32_t key = ~0u;
 #pragma unroll
-    for (int t = 0; t < kS; ++t) idle += idle_words(mls[t]) + idle_words(ot[t]);
-    ready = idle == 0;
+    for (int t = 0; t < kS; ++t) key = idle_key(idle_key(key, mls[t]), ot[t]);
+    ready = key != 0u;
   }
   // The slots go back to the idle pattern now, while the merge below is computed: this
   // thread is the only reader of its O words, and the 32 readers of a head's (m, l)
