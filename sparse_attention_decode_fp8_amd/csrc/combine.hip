@@ -64,17 +64,18 @@ extern "C" msa_status_t msa_combine(int32_t rows, int32_t num_q_heads, int32_t h
 namespace msa {
 namespace {
 
-// Idle state of a split-merge workspace: every partial word holds the idle pattern
-// and every counter is zero.
+// Initial state of a split-merge workspace: every word of both exchange buffers holds
+// the idle pattern, and every pair's state word selects buffer 0 for the given split
+// count with no arrivals.
 __global__ void __launch_bounds__(256)
 merge_idle_kernel(uint32_t* __restrict__ part_o, int64_t n_o, uint32_t* __restrict__ part_ml,
-                  int64_t n_ml, int32_t* __restrict__ counters, int64_t n_c) {
+                  int64_t n_ml, int32_t* __restrict__ counters, int64_t n_c, uint32_t state0) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n_o + n_ml + n_c;
        i += stride) {
     if (i < n_o) part_o[i] = MSA_MERGE_IDLE_BITS;
     else if (i < n_o + n_ml) part_ml[i - n_o] = MSA_MERGE_IDLE_BITS;
-    else counters[i - n_o - n_ml] = 0;
+    else counters[i - n_o - n_ml] = static_cast<int32_t>(state0);
   }
 }
 
@@ -89,11 +90,13 @@ extern "C" msa_status_t msa_merge_workspace_init(int32_t rows, int32_t num_q_hea
   if (head_dim != MSA_HEAD_DIM || num_q_heads % MSA_HEADS_PER_KV != 0) return MSA_ERR_UNSUPPORTED;
   if (rows == 0) return MSA_OK;
   if (part_o == nullptr || part_ml == nullptr || counters == nullptr) return MSA_ERR_INVALID_ARG;
+  if (num_splits > kMaxMergeSplits) return MSA_ERR_UNSUPPORTED;
   const int64_t rh = static_cast<int64_t>(rows) * num_q_heads;
-  const int64_t n_o = rh * num_splits * MSA_HEAD_DIM, n_ml = rh * num_splits * 2;
+  const int64_t n_o = 2 * rh * num_splits * MSA_HEAD_DIM, n_ml = 2 * rh * num_splits * 2;   // two buffers
   const int64_t n_c = rh / MSA_HEADS_PER_KV;
   const int64_t blocks = std::min<int64_t>((n_o + n_ml + n_c + 255) / 256, 4096);
   merge_idle_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
-      reinterpret_cast<uint32_t*>(part_o), n_o, reinterpret_cast<uint32_t*>(part_ml), n_ml, counters, n_c);
+      reinterpret_cast<uint32_t*>(part_o), n_o, reinterpret_cast<uint32_t*>(part_ml), n_ml, counters, n_c,
+      merge_state(0, num_splits));
   return launch_status();
 }

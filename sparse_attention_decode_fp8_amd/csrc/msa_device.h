@@ -180,6 +180,19 @@ __device__ __forceinline__ uint32_t idle_key(uint32_t acc, float2_t v) { return 
 __device__ __forceinline__ uint32_t idle_key(uint32_t acc, float4_t v) {
   return idle_key(idle_key(idle_key(idle_key(acc, v[0]), v[1]), v[2]), v[3]);
 }
+// Most splits the combining decode merges in one launch.
+constexpr int kMaxMergeSplits = 16;
+
+// Merge state word of one (row, KV head) pair in the combining decode's workspace: bit
+// 31 = which of the two exchange buffers the next launch uses, bits 16..30 = the split
+// count the workspace was set up for, bits 0..15 = splits arrived in the current launch.
+__host__ __device__ __forceinline__ uint32_t merge_state(int buffer, int num_splits) {
+  return (static_cast<uint32_t>(buffer) << 31) | (static_cast<uint32_t>(num_splits) << 16);
+}
+__device__ __forceinline__ bool merge_state_ok(uint32_t w, int num_splits) {
+  return ((w >> 16) & 0x7fffu) == static_cast<uint32_t>(num_splits) && (w & 0xffffu) < static_cast<uint32_t>(num_splits);
+}
+
 // Workgroup barrier that orders LDS only: waits for this wave's LDS accesses, not for
 // its outstanding global stores.
 __device__ __forceinline__ void lds_barrier() {

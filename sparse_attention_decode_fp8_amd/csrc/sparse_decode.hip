@@ -48,7 +48,6 @@ constexpr int kVBufBytes = 32 * kVRowHalves * 2;   // one wave's 32-token V chun
 // on distinct banks; 128-float rows would put all 16 on the same banks.
 constexpr int kORowFloats = kHeadDim + 4;
 static_assert(16 * kORowFloats * 4 <= kVBufBytes, "O tile must fit in a V buffer");
-constexpr int kMaxCombineSplits = 16;
 // Bound on the merger's polls of one slot. Every slot it polls has been stored by a
 // split that is already past its compute, so a few polls suffice; the bound only keeps
 // the loop finite (past it the merge uses what it read).
@@ -193,8 +192,7 @@ __device__ __forceinline__ void load_round(Round<kFmt, kItems>& rd, const Decode
 // the fixed-order log-sum-exp sums of msa_combine. Slots whose words have not all
 // landed are read again, which is rare: the other splits counted themselves in
 // earlier. Entries S..kS-1 repeat the last slot and are not used, so every entry is
-// redefined on each read and none is carried from one poll to the next. The item's
-// words are put back to idle as soon as they have been read.
+// redefined on each read and none is carried from one poll to the next.
 template <int kS>
 __device__ __forceinline__ void merge_slots(__amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t rm, int S,
                                             int h, int d4, float4_t& num, float& den) {
@@ -217,16 +215,6 @@ __device__ __forceinline__ void merge_slots(__amdgpu_buffer_rsrc_t ro, __amdgpu_
 #pragma unroll
     for (int t = 0; t < kS; ++t) key = idle_key(idle_key(key, mls[t]), ot[t]);
     ready = key != 0u;
-  }
-  // The slots go back to the idle pattern now, while the merge below is computed: this
-  // thread is the only reader of its O words, and the 32 readers of a head's (m, l)
-  // words are the lanes of this wave, whose loads have all returned.
-  const float idle_v = __uint_as_float(MSA_MERGE_IDLE_BITS);
-#pragma unroll
-  for (int t = 0; t < kS; ++t) {
-    const int tt = min(t, S - 1);
-    store_coherent(ro, ((h * S + tt) * kHeadDim + 4 * d4) * 4u, float4_t{idle_v, idle_v, idle_v, idle_v});
-    store_coherent(rm, (h * S + tt) * 8u, float2_t{idle_v, idle_v});
   }
   float M = -INFINITY;
 #pragma unroll
@@ -263,6 +251,19 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
   const int hq = a.hkv * kHeadsPerKv;
   const int lo = (s * a.k) / a.num_splits, hi = ((s + 1) * a.k) / a.num_splits;
   const int n_items = (hi - lo) * 4;   // (entry, 32-token chunk) pairs of this split
+  const int64_t head0 = static_cast<int64_t>(r) * hq + kHeadsPerKv * g;
+
+  // Combining variants with several splits: the pair's merge state word (which of the
+  // two exchange buffers this launch uses, the split count the workspace was set up
+  // for, arrivals so far), read once at the start. Its buffer and split-count fields
+  // change only when this launch's merger finishes, after every split has arrived.
+  const bool merging = kCombine && a.num_splits > 1;
+  uint32_t mstate = 0u;
+  if (merging)
+    mstate = static_cast<uint32_t>(__hip_atomic_load(a.counters + static_cast<int64_t>(r) * a.hkv + g,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  const int64_t buf_o = static_cast<int64_t>(a.num_rows) * hq * a.num_splits * kHeadDim;   // one buffer
+  const int64_t buf_ml = static_cast<int64_t>(a.num_rows) * hq * a.num_splits * 2;
 
   // Q^T operand: lane (n, q) holds head 16g + n, dims 32q + 8j .. +7 for k-step j.
   const uint4* qp = reinterpret_cast<const uint4*>(
@@ -376,6 +377,24 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
   Round<kFmt, kItems> rd;
   load_round<kFmt, kW, kItems>(rd, a, lookup, 0, wave, g, pos, lo, n_items, n, q);
 
+  // This split's slot in the other exchange buffer was read by the previous launch's
+  // merger; the last wave puts it back to idle now, off the critical path (its page
+  // loads are already out, and they retire before these stores in the counter order).
+  if (merging && wave == kW - 1 && merge_state_ok(mstate, a.num_splits)) {
+    const int other = static_cast<int>(mstate >> 31) ^ 1;
+    const float iv = __uint_as_float(MSA_MERGE_IDLE_BITS);
+    const __amdgpu_buffer_rsrc_t xo = make_rsrc(
+        uniform_ptr(a.part_o + other * buf_o + head0 * a.num_splits * kHeadDim), 16u * a.num_splits * kHeadDim * 4);
+    const __amdgpu_buffer_rsrc_t xm =
+        make_rsrc(uniform_ptr(a.part_ml + other * buf_ml + head0 * a.num_splits * 2), 16u * a.num_splits * 8);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {   // 16 heads x 32 four-float groups
+      const int idx = lane + 64 * j, h = idx / (kHeadDim / 4), d4 = idx % (kHeadDim / 4);
+      store_coherent(xo, ((h * a.num_splits + s) * kHeadDim + 4 * d4) * 4u, float4_t{iv, iv, iv, iv});
+    }
+    if (lane < 16) store_coherent(xm, (lane * a.num_splits + s) * 8u, float2_t{iv, iv});
+  }
+
   if constexpr (!kSelect) convert_q();
 
   float m_run = -INFINITY, l_run = 0.0f, v_cur = 0.0f;   // v_cur: FP8 page scale O is kept in
@@ -459,7 +478,6 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
   const float l_tot = xor_add(xor_add(l_run, 16), 32);
   float oscale;
   if constexpr (kFmt == MSA_KV_NVFP4) oscale = a.v_t; else oscale = v_cur;
-  const int64_t head0 = static_cast<int64_t>(r) * hq + kHeadsPerKv * g;
   {
     // each wave's O tile goes to its own V buffer, which only it used: no barrier first
     float* ob = reinterpret_cast<float*>(dyn_lds + wave * kVBufBytes);   // [16 heads][kORowFloats]
@@ -471,8 +489,10 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
   __syncthreads();
   // this (row, KV head)'s partials: O [16 heads][S][128], (m, l) [16 heads][S][2]
   const uint32_t o_bytes = 16u * a.num_splits * kHeadDim * 4, ml_bytes = 16u * a.num_splits * 8;
-  const __amdgpu_buffer_rsrc_t ro = make_rsrc(uniform_ptr(a.part_o + head0 * a.num_splits * kHeadDim), o_bytes);
-  const __amdgpu_buffer_rsrc_t rm = make_rsrc(uniform_ptr(a.part_ml + head0 * a.num_splits * 2), ml_bytes);
+  const int cur = merging ? static_cast<int>(mstate >> 31) : 0;   // this launch's exchange buffer
+  const __amdgpu_buffer_rsrc_t ro =
+      make_rsrc(uniform_ptr(a.part_o + cur * buf_o + head0 * a.num_splits * kHeadDim), o_bytes);
+  const __amdgpu_buffer_rsrc_t rm = make_rsrc(uniform_ptr(a.part_ml + cur * buf_ml + head0 * a.num_splits * 2), ml_bytes);
   constexpr int kTasks = 16 * (kHeadDim / 4);                     // (head, 4 dims) items
   constexpr int kPer = (kTasks + 64 * kW - 1) / (64 * kW);        // items per thread
   // In-workgroup merge of one item over the waves' O tiles. Every LDS read is issued
@@ -537,13 +557,23 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
   } else {
     // ---- several splits: the last split of this (row, KV head) to count itself in
     // merges them all. Each split counts itself in as soon as its compute is done, then
-    // stores its partial (agent-coherent) and only then reads the old count, so nothing
-    // waits for the stores to land; the merger polls each slot until none of its words
-    // holds the idle pattern. Every split it waits for has counted itself in, so it is
-    // resident with only in-workgroup work left before its stores: the polls end. The
-    // merger then puts every slot back to the idle pattern and the counter back to
-    // zero, ready for the next launch.
-    int arrival = 0;
+    // stores its partial (agent-coherent) into this launch's exchange buffer and only
+    // then reads the old count, so nothing waits for the stores to land; the merger
+    // polls each slot until none of its words holds the idle pattern. Every split it
+    // waits for has counted itself in, so it is resident with only in-workgroup work
+    // left before its stores: the polls end. The merger leaves the slots as they are
+    // (each split returns its own slot to idle early in the next launch that uses the
+    // other buffer) and flips the state word to the other buffer with no arrivals.
+    if (!merge_state_ok(mstate, a.num_splits)) {
+      // The workspace was not set up for this split count (or not set up): touch
+      // nothing and make the failure visible in the output (bf16 NaN).
+      if (s == 0)
+        for (int idx = threadIdx.x; idx < kTasks; idx += 64 * kW)
+          *reinterpret_cast<uint2*>(a.out + (head0 + idx / (kHeadDim / 4)) * kHeadDim + 4 * (idx % (kHeadDim / 4))) =
+              make_uint2(0x7fc07fc0u, 0x7fc07fc0u);
+      return;
+    }
+    int32_t arrival = 0;   // the old state word; its low half counts the earlier splits
     if (threadIdx.x == 0) arrival = atomicAdd(a.counters + static_cast<int64_t>(r) * a.hkv + g, 1);
 #pragma unroll
     for (int it = 0; it < kPer; ++it) {
@@ -561,7 +591,10 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
       // does not wait for them
       store_coherent(rm, (h * a.num_splits + s) * 8u, float2_t{not_idle(M), not_idle(l)});
     }
-    if (threadIdx.x == 0) s_last = arrival == a.num_splits - 1;
+    // (the empty asm keeps the compiler from folding the mask into the atomic's block,
+    // where it would wait for the count before the stores above are issued)
+    asm volatile("" : "+v"(arrival));
+    if (threadIdx.x == 0) s_last = (arrival & 0xffff) == a.num_splits - 1;
     lds_barrier();
     if (!s_last) return;
 #pragma unroll
@@ -581,8 +614,9 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
       *reinterpret_cast<uint2*>(a.out + (head0 + h) * kHeadDim + 4 * d4) =
           make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16));
     }
-    if (threadIdx.x == 0)
-      __hip_atomic_store(a.counters + static_cast<int64_t>(r) * a.hkv + g, 0, __ATOMIC_RELAXED,
+    if (threadIdx.x == 0)   // the other buffer, no arrivals: ready for the next launch
+      __hip_atomic_store(a.counters + static_cast<int64_t>(r) * a.hkv + g,
+                         static_cast<int32_t>(merge_state(cur ^ 1, a.num_splits)), __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
   }
 }
@@ -615,7 +649,7 @@ msa_status_t decode_entry(const msa_kv_pool_t* pool, const msa_step_t* step, int
   if ((st = check_step(step)) != MSA_OK) return st;
   if (num_q_heads != MSA_HEADS_PER_KV * pool->num_kv_heads) return MSA_ERR_UNSUPPORTED;
   if (a.k < 1 || a.k > MSA_MAX_TOPK || a.num_splits < 1 || a.num_splits > a.k) return MSA_ERR_UNSUPPORTED;
-  if (combine && a.num_splits > kMaxCombineSplits) return MSA_ERR_UNSUPPORTED;
+  if (combine && a.num_splits > kMaxMergeSplits) return MSA_ERR_UNSUPPORTED;
   if (select && (a.n_init < 0 || a.n_local < 0 || a.n_init + a.n_local > a.k)) return MSA_ERR_UNSUPPORTED;
   if (!(a.softmax_scale > 0.0f)) return MSA_ERR_INVALID_ARG;
   if (step->num_rows == 0) return MSA_OK;

@@ -27,8 +27,8 @@ def default_num_splits(k: int, pairs: int) -> int:
 class DecodeBuffers:
     """Per-step outputs and the split-KV workspaces for a fixed geometry: part_o /
     part_ml receive the partials of the separate msa_sparse_decode call; merge_o /
-    merge_ml / counters are the fused entries' merge workspace, put into its idle state
-    here and left idle by every fused call."""
+    merge_ml (two exchange buffers) and counters (one state word per row and KV head)
+    are the fused entries' merge workspace, set up here for num_splits."""
 
     def __init__(self, num_rows, num_q_heads, max_blocks, k, num_splits, device="cuda"):
         self.k, self.num_splits = k, num_splits
@@ -39,8 +39,8 @@ class DecodeBuffers:
                                   dtype=torch.float32, device=device)
         self.part_ml = torch.empty((num_rows, num_q_heads, num_splits, 2), dtype=torch.float32,
                                    device=device)
-        self.merge_o = torch.empty_like(self.part_o)
-        self.merge_ml = torch.empty_like(self.part_ml)
+        self.merge_o = torch.empty((2,) + tuple(self.part_o.shape), dtype=torch.float32, device=device)
+        self.merge_ml = torch.empty((2,) + tuple(self.part_ml.shape), dtype=torch.float32, device=device)
         self.counters = torch.empty((num_rows, num_q_heads // 16), dtype=torch.int32, device=device)
         L.msa_merge_workspace_init(num_rows, num_q_heads, L.HEAD_DIM, num_splits, self.merge_o,
                                    self.merge_ml, self.counters)

@@ -152,13 +152,25 @@ def oracle_rows(wl: W.Workload, rows):
     return S, sel, out, pool
 
 
-def assert_merge_idle(bufs):
-    """The fused entries leave their merge workspace idle: counters zero, every word of
-    the partial slots the idle pattern."""
+def assert_merge_ready(bufs):
+    """A fused call leaves its merge workspace ready for the next one: every state word
+    names the workspace's split count with no arrivals, and the exchange buffer it
+    selects holds the idle pattern in that (row, KV head)'s region."""
     import sparse_attention_decode_fp8_amd as M
-    assert int(bufs.counters.abs().sum()) == 0
-    for t in (bufs.merge_o, bufs.merge_ml):
-        assert bool((t.view(torch.int32) == M.MERGE_IDLE_BITS).all())   # 0x7fbadbad < 2^31
+    S = bufs.num_splits
+    c = bufs.counters.cpu().numpy().view(np.uint32)
+    assert ((c & 0xffff) == 0).all(), "arrivals left in a state word"
+    assert (((c >> 16) & 0x7fff) == S).all(), "state word names another split count"
+    rows, hq = bufs.out.shape[0], bufs.out.shape[1]
+    # the buffers as laid out for S splits (a workspace may be allocated for more)
+    mo = bufs.merge_o.view(torch.int32).reshape(-1)[:2 * rows * hq * S * 128].reshape(2, rows, hq, S, 128)
+    mm = bufs.merge_ml.view(torch.int32).reshape(-1)[:2 * rows * hq * S * 2].reshape(2, rows, hq, S, 2)
+    mo, mm = mo.cpu().numpy(), mm.cpu().numpy()
+    for r in range(c.shape[0]):
+        for g in range(c.shape[1]):
+            e = int(c[r, g] >> 31)
+            assert (mo[e, r, 16 * g:16 * g + 16] == M.MERGE_IDLE_BITS).all(), (r, g)
+            assert (mm[e, r, 16 * g:16 * g + 16] == M.MERGE_IDLE_BITS).all(), (r, g)
 
 
 def check_step_parity(M, wl: W.Workload, num_splits: int, fused: bool):
@@ -183,8 +195,8 @@ def check_step_parity(M, wl: W.Workload, num_splits: int, fused: bool):
             same[r] = np.array_equal(sel[r], sel_ref[r])
     out = bf16_to_np(bufs.out)
     assert_out_close(out[same], out_ref[same], "outputs")
-    if fused:   # the partials passed through the merge workspace, which is idle again
-        assert_merge_idle(bufs)
+    if fused:   # the partials passed through the merge workspace, ready for the next call
+        assert_merge_ready(bufs)
         return bufs
     # the split partials the kernel wrote
     m, l, Op = O.split_partials(ref_pool, wl.block_table, wl.row_seq, wl.row_pos, wl.q, sel_ref,

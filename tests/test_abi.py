@@ -128,6 +128,7 @@ def test_validation_rejects_before_launch():
     assert L.LIB.msa_merge_workspace_init(1, 24, 128, 2, P(16), P(16), P(16), None) == -2
     assert L.LIB.msa_merge_workspace_init(-1, 32, 128, 2, P(16), P(16), P(16), None) == -1
     assert L.LIB.msa_merge_workspace_init(1, 32, 128, 0, P(16), P(16), P(16), None) == -1
+    assert L.LIB.msa_merge_workspace_init(1, 32, 128, 17, P(16), P(16), P(16), None) == -2
     assert L.LIB.msa_merge_workspace_init(1, 32, 128, 2, P(16), None, P(16), None) == -1
     # fused append + score + select
     assert L.LIB.msa_append_score_select(B(pool), B(step), 0, None, None, None, None, 4, P(16), P(16),

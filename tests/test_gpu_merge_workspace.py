@@ -1,6 +1,8 @@
-"""The fused entries' split-merge workspace: the fill entry sets the idle state, and one
-workspace serves successive fused calls with different split counts, each equal bit
-for bit to the separate decode + combine calls and each leaving the workspace idle."""
+"""The fused entries' split-merge workspace: msa_merge_workspace_init sets it up for one
+split count; successive fused calls (alternating exchange buffers) equal the separate
+decode + combine calls bit for bit and leave it ready for the next call; a call with
+another split count touches no workspace word and writes NaN; a fresh set-up serves
+the new split count."""
 import numpy as np
 import pytest
 import torch
@@ -17,49 +19,75 @@ def M():
     return M
 
 
-def test_workspace_init_sets_idle_state(M):
+def test_workspace_init_sets_up_state(M):
     rows, hq, S = 3, 32, 5
-    po = torch.full((rows, hq, S, 128), 1.5, dtype=torch.float32, device="cuda")
-    pm = torch.full((rows, hq, S, 2), -2.0, dtype=torch.float32, device="cuda")
+    po = torch.full((2, rows, hq, S, 128), 1.5, dtype=torch.float32, device="cuda")
+    pm = torch.full((2, rows, hq, S, 2), -2.0, dtype=torch.float32, device="cuda")
     cnt = torch.full((rows, hq // 16), 9, dtype=torch.int32, device="cuda")
     guard = torch.full((64,), 3.0, dtype=torch.float32, device="cuda")
     M.msa_merge_workspace_init(rows, hq, 128, S, po, pm, cnt)
     torch.cuda.synchronize()
     assert bool((po.view(torch.int32) == M.MERGE_IDLE_BITS).all())
     assert bool((pm.view(torch.int32) == M.MERGE_IDLE_BITS).all())
-    assert bool((cnt == 0).all())
+    assert bool((cnt == (S << 16)).all())
     assert bool((guard == 3.0).all())
 
 
+def _reference(M, wl, pool, step, q, scores, ns):
+    ref = M.DecodeBuffers(wl.num_rows, wl.num_heads, wl.max_blocks, wl.k, ns)
+    M.msa_select_topk(step, scores, wl.k, wl.n_init, wl.n_local, ref.sel, ref.sel_pages)
+    M.msa_sparse_decode(pool, step, q, ref.sel, wl.k, wl.softmax_scale, ns, ref.part_o, ref.part_ml,
+                        sel_pages=ref.sel_pages)
+    M.msa_combine(wl.num_rows, wl.num_heads, 128, ns, ref.part_o, ref.part_ml, ref.out)
+    return ref
+
+
 @pytest.mark.parametrize("fmt", [W.FMT_FP8, W.FMT_NVFP4])
-def test_one_workspace_many_split_counts(M, fmt):
+def test_successive_calls_and_split_changes(M, fmt):
     wl = W.small(fmt, [3000, 700, 5000, 9000], 2, num_kv_heads=2, k=16, seed=81)
-    print("merge workspace reuse", wl.name, flush=True)
+    print("merge workspace", wl.name, flush=True)
     pool = G.gpu_pool(M, wl)
     step, q, q_idx, w, app = G.gpu_step_inputs(M, wl)
     kw = dict(slot=app[0], k_new=app[1], v_new=app[2], idx_k_new=app[3])
-    big = M.DecodeBuffers(wl.num_rows, wl.num_heads, wl.max_blocks, wl.k, 16)
-    M.msa_append_score_select(pool, step, q_idx, w, wl.k, wl.n_init, wl.n_local, big.block_scores, **kw)
-    for ns in (8, 2, 16, 1, 3, 16, 5):
+    scores = torch.empty((wl.num_rows, wl.max_blocks), dtype=torch.float32, device="cuda")
+    M.msa_append_score_select(pool, step, q_idx, w, wl.k, wl.n_init, wl.n_local, scores, **kw)
+    # one workspace sized for 16 splits, set up in turn for each split count used
+    ws = M.DecodeBuffers(wl.num_rows, wl.num_heads, wl.max_blocks, wl.k, 16)
+    for ns in (8, 2, 16, 3):
         print("  splits", ns, flush=True)
-        ref = M.DecodeBuffers(wl.num_rows, wl.num_heads, wl.max_blocks, wl.k, ns)
-        M.msa_select_topk(step, big.block_scores, wl.k, wl.n_init, wl.n_local, ref.sel, ref.sel_pages)
-        M.msa_sparse_decode(pool, step, q, ref.sel, wl.k, wl.softmax_scale, ns, ref.part_o, ref.part_ml,
-                            sel_pages=ref.sel_pages)
-        M.msa_combine(wl.num_rows, wl.num_heads, 128, ns, ref.part_o, ref.part_ml, ref.out)
-        big.out.fill_(0)
-        M.msa_select_decode_combine(pool, step, q, big.block_scores, wl.k, wl.n_init, wl.n_local,
-                                    wl.softmax_scale, ns, big.merge_o, big.merge_ml, big.counters,
-                                    big.out, sel=big.sel, sel_pages=big.sel_pages)
+        ref = _reference(M, wl, pool, step, q, scores, ns)
+        M.msa_merge_workspace_init(wl.num_rows, wl.num_heads, 128, ns, ws.merge_o, ws.merge_ml, ws.counters)
+        ws.num_splits = ns
+        for call in range(5):   # both buffers, twice over, alternating the two entries
+            ws.out.fill_(0)
+            if call % 2 == 0:
+                M.msa_select_decode_combine(pool, step, q, scores, wl.k, wl.n_init, wl.n_local,
+                                            wl.softmax_scale, ns, ws.merge_o, ws.merge_ml, ws.counters,
+                                            ws.out, sel=ws.sel, sel_pages=ws.sel_pages)
+            else:
+                M.msa_sparse_decode_combine(pool, step, q, ref.sel, wl.k, wl.softmax_scale, ns, ws.merge_o,
+                                            ws.merge_ml, ws.counters, ws.out, sel_pages=ref.sel_pages)
+            torch.cuda.synchronize()
+            assert torch.equal(ws.out.view(torch.int16), ref.out.view(torch.int16)), (ns, call)
+            G.assert_merge_ready(ws)
+            if call % 2 == 0:
+                assert torch.equal(ws.sel, ref.sel)
+        epoch = (ws.counters.cpu().numpy().view(np.uint32) >> 31)
+        assert (epoch == 1).all()   # five calls: buffer 0, 1, 0, 1, 0 -> next is 1
+        # a call with another split count (within the allocation): workspace untouched,
+        # NaN outputs
+        other = 4 if ns != 4 else 2
+        before = [t.clone() for t in (ws.merge_o, ws.merge_ml, ws.counters)]
+        M.msa_select_decode_combine(pool, step, q, scores, wl.k, wl.n_init, wl.n_local, wl.softmax_scale,
+                                    other, ws.merge_o, ws.merge_ml, ws.counters, ws.out)
         torch.cuda.synchronize()
-        assert torch.equal(big.sel, ref.sel)
-        assert torch.equal(big.out.view(torch.int16), ref.out.view(torch.int16)), ns
-        G.assert_merge_idle(big)
-        # the table-driven combining entry on the same workspace
-        big.out.fill_(0)
-        M.msa_sparse_decode_combine(pool, step, q, ref.sel, wl.k, wl.softmax_scale, ns, big.merge_o,
-                                    big.merge_ml, big.counters, big.out, sel_pages=ref.sel_pages)
+        for t0, t in zip(before, (ws.merge_o, ws.merge_ml, ws.counters)):
+            assert torch.equal(t0.view(torch.int32), t.view(torch.int32))
+        assert bool(torch.isnan(ws.out.float()).all())
+        # after a fresh set-up the new split count works
+        M.msa_merge_workspace_init(wl.num_rows, wl.num_heads, 128, other, ws.merge_o, ws.merge_ml, ws.counters)
+        ref2 = _reference(M, wl, pool, step, q, scores, other)
+        M.msa_select_decode_combine(pool, step, q, scores, wl.k, wl.n_init, wl.n_local, wl.softmax_scale,
+                                    other, ws.merge_o, ws.merge_ml, ws.counters, ws.out)
         torch.cuda.synchronize()
-        assert torch.equal(big.out.view(torch.int16), ref.out.view(torch.int16)), ns
-        G.assert_merge_idle(big)
-    assert np.isfinite(G.bf16_to_np(big.out)).all()
+        assert torch.equal(ws.out.view(torch.int16), ref2.out.view(torch.int16)), ns

@@ -176,7 +176,8 @@ def test_sel_pages_and_fused_combine(M):
         nb = torch.from_numpy(wl.row_pos // 128 + 1).cuda()
         vis = torch.arange(wl.max_blocks, device="cuda")[None] < nb[:, None]
         assert torch.equal(a.block_scores[vis], b.block_scores[vis])
-        assert int(a.counters.abs().sum()) == 0 and int(a.score_counters.abs().sum()) == 0
+        G.assert_merge_ready(a)
+        assert int(a.score_counters.abs().sum()) == 0
         # the scoring launch can also select (last workgroup per row group)
         pc = pool.clone()
         step, q, q_idx, w, app = G.gpu_step_inputs(M, wl)
@@ -241,4 +242,4 @@ def test_fused_select_bit_exact_with_ties(M, nb_max, k, n_init, n_local, quantum
     sel = bufs.sel.cpu().numpy()
     assert np.array_equal(sel, ref)
     assert np.array_equal(bufs.sel_pages.cpu().numpy(), np.where(ref >= 0, bt[0][np.maximum(ref, 0)], -1))
-    G.assert_merge_idle(bufs)
+    G.assert_merge_ready(bufs)
