@@ -180,6 +180,14 @@ __device__ __forceinline__ uint32_t idle_key(uint32_t acc, float2_t v) { return 
 __device__ __forceinline__ uint32_t idle_key(uint32_t acc, float4_t v) {
   return idle_key(idle_key(idle_key(idle_key(acc, v[0]), v[1]), v[2]), v[3]);
 }
+// Zero that the compiler must treat as differing between lanes (an asm result): added
+// to an address, it keeps a load's result in a vector register.
+__device__ __forceinline__ int lane_varying_zero() {
+  int z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return z;
+}
+
 // Most splits the combining decode merges in one launch.
 constexpr int kMaxMergeSplits = 16;
 

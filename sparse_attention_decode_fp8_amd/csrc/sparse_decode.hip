@@ -259,9 +259,11 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
   // change only when this launch's merger finishes, after every split has arrived.
   const bool merging = kCombine && a.num_splits > 1;
   uint32_t mstate = 0u;
-  if (merging)
-    mstate = static_cast<uint32_t>(__hip_atomic_load(a.counters + static_cast<int64_t>(r) * a.hkv + g,
-                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  if (merging)   // (a per-lane address, so the word stays in a vector register and is
+                 // not moved to a scalar one, which would wait for the load right here)
+    mstate = static_cast<uint32_t>(__hip_atomic_load(
+        a.counters + static_cast<int64_t>(r) * a.hkv + g + lane_varying_zero(), __ATOMIC_RELAXED,
+        __HIP_MEMORY_SCOPE_AGENT));
   const int64_t buf_o = static_cast<int64_t>(a.num_rows) * hq * a.num_splits * kHeadDim;   // one buffer
   const int64_t buf_ml = static_cast<int64_t>(a.num_rows) * hq * a.num_splits * 2;
 
