@@ -244,12 +244,16 @@ __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
       A0[i] = static_cast<half_t>(ldexpf(qa[i], e));
       A1[i] = static_cast<half_t>(ldexpf(qa[8 + i], e));
     }
-    // inverse pre-scale of the (row, head) that lane (n, q)'s result M = 4q + jj has
-    float inv[4];
+    // Head weight times the inverse pre-scale of the (row, head) that lane (n, q)'s
+    // result M = 4q + jj has: the scale is positive, so w * relu(x * inv) =
+    // (w * inv) * relu(x) (exactly for E4M3 keys, whose scale is a power of two; up to
+    // rounding with the NVFP4 keys' tensor scale folded in).
+    float wi[4];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      inv[jj] = ldexpf(1.0f, -__shfl(e, 4 * q + jj, 64));
-      if constexpr (kIdxNv) inv[jj] *= a.idx_t;   // NVFP4 keys: their tensor scale (> 0)
+      float inv = ldexpf(1.0f, -__shfl(e, 4 * q + jj, 64));
+      if constexpr (kIdxNv) inv *= a.idx_t;   // NVFP4 keys: their tensor scale (> 0)
+      wi[jj] = wj[jj] * inv;
     }
 
     if constexpr (kFused) {
@@ -295,7 +299,7 @@ __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
 #pragma unroll
         for (int hh = 0; hh < kHi; ++hh) {
           const int jj = i * kHi + hh;
-          s = fmaf(wj[jj], fmaxf(acc[jj] * inv[jj], 0.0f), s);
+          s = fmaf(wi[jj], fmaxf(acc[jj], 0.0f), s);
         }
         if (p <= pos[i]) best[i] = fmaxf(best[i], s);
       }
