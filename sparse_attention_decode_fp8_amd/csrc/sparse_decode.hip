@@ -332,13 +332,15 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
       // reads, from the row of the request r belongs to when every request has the
       // same number of rows; the pages are read again if row_seq says otherwise.
       const int guess = seq_guess(r, a.seq_mul);
+      // every wave's own copy of the row's position and request, read before the
+      // selection so that wave 0 does not wait for them after it
+      pos = a.row_pos[r];
+      const int seq = a.row_seq[r];
       if (wave == 0) {
         const int32_t* btg = a.block_table + static_cast<int64_t>(guess) * a.max_blocks;
         wave_select(srow, btg, a.max_blocks, a.row_pos + r, a.k, a.n_init, a.n_local, lsel, lpage);
       }
       if (wave == 1) q_to_lds();
-      pos = a.row_pos[r];
-      const int seq = a.row_seq[r];
       __syncthreads();
       selv = lsel[lane];
       pagev = lpage[lane];
