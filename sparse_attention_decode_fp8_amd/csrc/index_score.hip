@@ -282,13 +282,19 @@ __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
       }
     }
 
+    // The first new token's key replaces its stale row, in the waves that have one.
+    if (__ballot(pt >= 0) != 0) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        if (t == pt) key[t] = pv;
+    }
     float best[kRowsPerLane];
 #pragma unroll
     for (int i = 0; i < kRowsPerLane; ++i) best[i] = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       half8_t B0, B1;
-      key_operands<kIdxNv>(t == pt ? pv : key[t], B0, B1);
+      key_operands<kIdxNv>(key[t], B0, B1);
       float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
       acc = mfma16x16x32(A0, B0, acc);
       acc = mfma16x16x32(A1, B1, acc);
@@ -299,7 +305,7 @@ __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
 #pragma unroll
         for (int hh = 0; hh < kHi; ++hh) {
           const int jj = i * kHi + hh;
-          s = fmaf(wi[jj], fmaxf(acc[jj], 0.0f), s);
+          s = fmaf(wi[jj], relu_raw(acc[jj]), s);
         }
         if (p <= pos[i]) best[i] = fmaxf(best[i], s);
       }

@@ -44,9 +44,20 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
-// Two OCP E4M3FN codes (bytes 0 and 1 of `v`) -> two exact fp16 values.
+// max(x, 0) as one instruction. Written as fmaxf, the compiler first canonicalises x
+// (a second instruction) to honour signalling NaNs, which the matrix-core results fed
+// here never are.
+__device__ __forceinline__ float relu_raw(float x) {
+  float r;
+  asm("v_max_f32 %0, 0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+
+// Two OCP E4M3FN codes (bytes 0 and 1 of `v`, or bytes 2 and 3 with kHi) -> two exact
+// fp16 values. The convert picks the half word itself, so no shift or extract first.
+template <bool kHi = false>
 __device__ __forceinline__ half2_t e4m3x2_to_f16(uint32_t v) {
-  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<short>(v & 0xffffu), 1.0f, false);
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, kHi);
 }
 
 // Two E2M1 codes (byte `sel` of `v`: low nibble first) -> two exact fp16 values.
@@ -66,8 +77,8 @@ __device__ __forceinline__ float4_t mfma16x16x32(half8_t a, half8_t b, float4_t 
 
 // 8 E4M3 codes (two dwords) -> 8 fp16 values in one MFMA operand.
 __device__ __forceinline__ half8_t e4m3x8_to_f16(uint32_t lo, uint32_t hi) {
-  half2_t a = e4m3x2_to_f16(lo), b = e4m3x2_to_f16(lo >> 16);
-  half2_t c = e4m3x2_to_f16(hi), d = e4m3x2_to_f16(hi >> 16);
+  half2_t a = e4m3x2_to_f16<false>(lo), b = e4m3x2_to_f16<true>(lo);
+  half2_t c = e4m3x2_to_f16<false>(hi), d = e4m3x2_to_f16<true>(hi);
   return half8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
