@@ -22,6 +22,8 @@
 // instead of waiting for the append; the scores are stored write-through (agent
 // coherent) and the last scoring workgroup of a row group, found with a counter,
 // runs the selection for those rows.
+#include <type_traits>
+
 #include "append_device.h"
 #include "msa_host.h"
 #include "select_device.h"
@@ -291,25 +293,38 @@ __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
     float best[kRowsPerLane];
 #pragma unroll
     for (int i = 0; i < kRowsPerLane; ++i) best[i] = -INFINITY;
+    // Tokens past a row's position are masked only in a block that holds one (the
+    // last visible block of some row of the group); elsewhere the loop skips the test.
+    bool ends_here = false;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      half8_t B0, B1;
-      key_operands<kIdxNv>(key[t], B0, B1);
-      float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-      acc = mfma16x16x32(A0, B0, acc);
-      acc = mfma16x16x32(A1, B1, acc);
-      const int p = b * kPage + 16 * t + n;      // absolute position of this lane's token
+    for (int i = 0; i < kRowsPerLane; ++i) ends_here |= rowslot[i] < nr && b * kPage + kPage - 1 > pos[i];
+    auto score_tokens = [&](auto masked) {
 #pragma unroll
-      for (int i = 0; i < kRowsPerLane; ++i) {
-        float s = 0.0f;
+      for (int t = 0; t < 8; ++t) {
+        half8_t B0, B1;
+        key_operands<kIdxNv>(key[t], B0, B1);
+        float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        acc = mfma16x16x32(A0, B0, acc);
+        acc = mfma16x16x32(A1, B1, acc);
+        const int p = b * kPage + 16 * t + n;      // absolute position of this lane's token
 #pragma unroll
-        for (int hh = 0; hh < kHi; ++hh) {
-          const int jj = i * kHi + hh;
-          s = fmaf(wi[jj], relu_raw(acc[jj]), s);
+        for (int i = 0; i < kRowsPerLane; ++i) {
+          float s = 0.0f;
+#pragma unroll
+          for (int hh = 0; hh < kHi; ++hh) {
+            const int jj = i * kHi + hh;
+            s = fmaf(wi[jj], relu_raw(acc[jj]), s);
+          }
+          if constexpr (decltype(masked)::value) {
+            if (p <= pos[i]) best[i] = max_raw(best[i], s);
+          } else {
+            best[i] = max_raw(best[i], s);
+          }
         }
-        if (p <= pos[i]) best[i] = fmaxf(best[i], s);
       }
-    }
+    };
+    if (__ballot(ends_here) != 0) score_tokens(std::true_type{});
+    else score_tokens(std::false_type{});
 #pragma unroll
     for (int i = 0; i < kRowsPerLane; ++i) {
       float v = best[i];

@@ -53,6 +53,14 @@ __device__ __forceinline__ float relu_raw(float x) {
   return r;
 }
 
+// max(a, b) as one instruction (no canonicalisation of the operands first; for values
+// that are never signalling NaNs).
+__device__ __forceinline__ float max_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // Two OCP E4M3FN codes (bytes 0 and 1 of `v`, or bytes 2 and 3 with kHi) -> two exact
 // fp16 values. The convert picks the half word itself, so no shift or extract first.
 template <bool kHi = false>
