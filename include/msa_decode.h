@@ -239,17 +239,18 @@ msa_status_t msa_sparse_decode(const msa_kv_pool_t* pool, const msa_step_t* step
  * arithmetic, so `out` equals msa_sparse_decode + msa_combine bit for bit) and writes
  * bf16 `out` [num_rows][num_q_heads][head_dim].
  *   part_o, part_ml, counters : the merge workspace. part_o fp32
- *     [2][num_rows][num_q_heads][num_splits][head_dim] and part_ml fp32
- *     [2][num_rows][num_q_heads][num_splits][2] are two exchange buffers, used by
- *     alternate calls; counters int32 [num_rows][num_kv_heads] holds one state word
+ *     [num_rows][num_kv_heads][2][16][num_splits][head_dim] and part_ml fp32
+ *     [num_rows][num_kv_heads][2][16][num_splits][2] hold two exchange buffers per
+ *     (row, KV head), used by alternate calls (the layout does not depend on num_rows,
+ *     so a workspace sized for R rows serves any call with num_rows <= R);
+ *     counters int32 [num_rows][num_kv_heads] holds one state word
  *     per (row, KV head): bit 31 = the buffer the next call uses, bits 16..30 = the
  *     split count the workspace is set up for, bits 0..15 = arrivals (zero between
  *     calls). msa_merge_workspace_init sets it up for one num_splits (both buffers
  *     idle: every word MSA_MERGE_IDLE_BITS); every call with that num_splits leaves it
  *     ready for the next one. The partials pass through the buffers and are not left
- *     readable. An allocation sized for S splits serves any num_splits <= S (the
- *     buffers are laid out for the num_splits in use: buffer 1 starts right after
- *     buffer 0's rows * num_q_heads * num_splits * head_dim words). A call whose num_splits (> 1) differs from the set-up one, or that
+ *     readable. An allocation sized for S splits serves any num_splits <= S after a
+ *     set-up for that num_splits (the words are laid out for the num_splits in use). A call whose num_splits (> 1) differs from the set-up one, or that
  *     finds a state word out of range, touches no workspace word and writes bf16 NaN
  *     to that (row, KV head)'s outputs: call msa_merge_workspace_init again before
  *     changing num_splits. With num_splits == 1 the one split writes `out` itself and
@@ -281,8 +282,9 @@ msa_status_t msa_select_decode_combine(const msa_kv_pool_t* pool, const msa_step
 
 /*
  * Set up a merge workspace of the two *_combine entries for `num_splits` splits: every
- * word of both exchange buffers, part_o [2][rows][num_q_heads][num_splits][head_dim]
- * and part_ml [2][rows][num_q_heads][num_splits][2], = MSA_MERGE_IDLE_BITS, and every
+ * word of both exchange buffers, part_o [rows][num_q_heads / 16][2][16][num_splits]
+ * [head_dim] and part_ml [rows][num_q_heads / 16][2][16][num_splits][2], =
+ * MSA_MERGE_IDLE_BITS, and every
  * state word in counters [rows][num_q_heads / 16] = buffer 0, num_splits, no arrivals
  * (num_splits << 16). A fill kernel on `stream` (no memset nodes, so the call may be
  * captured in a graph). Needed once after allocation, again before calls with another

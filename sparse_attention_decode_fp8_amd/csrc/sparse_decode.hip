@@ -264,8 +264,9 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
     mstate = static_cast<uint32_t>(__hip_atomic_load(
         a.counters + static_cast<int64_t>(r) * a.hkv + g + lane_varying_zero(), __ATOMIC_RELAXED,
         __HIP_MEMORY_SCOPE_AGENT));
-  const int64_t buf_o = static_cast<int64_t>(a.num_rows) * hq * a.num_splits * kHeadDim;   // one buffer
-  const int64_t buf_ml = static_cast<int64_t>(a.num_rows) * hq * a.num_splits * 2;
+  // The merge workspace is pair-major, [rows][KV heads][2 buffers][16 heads][S][...], so
+  // its layout does not depend on how many rows a call has: this pair's slots of
+  // buffer b start at row (2 * head0 + 16 * b) * S of 128 (or 2) words.
 
   // Q^T operand: lane (n, q) holds head 16g + n, dims 32q + 8j .. +7 for k-step j.
   const uint4* qp = reinterpret_cast<const uint4*>(
@@ -388,9 +389,9 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
     const int other = static_cast<int>(mstate >> 31) ^ 1;
     const float iv = __uint_as_float(MSA_MERGE_IDLE_BITS);
     const __amdgpu_buffer_rsrc_t xo = make_rsrc(
-        uniform_ptr(a.part_o + other * buf_o + head0 * a.num_splits * kHeadDim), 16u * a.num_splits * kHeadDim * 4);
+        uniform_ptr(a.part_o + (2 * head0 + 16 * other) * a.num_splits * kHeadDim), 16u * a.num_splits * kHeadDim * 4);
     const __amdgpu_buffer_rsrc_t xm =
-        make_rsrc(uniform_ptr(a.part_ml + other * buf_ml + head0 * a.num_splits * 2), 16u * a.num_splits * 8);
+        make_rsrc(uniform_ptr(a.part_ml + (2 * head0 + 16 * other) * a.num_splits * 2), 16u * a.num_splits * 8);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {   // 16 heads x 32 four-float groups
       const int idx = lane + 64 * j, h = idx / (kHeadDim / 4), d4 = idx % (kHeadDim / 4);
@@ -495,8 +496,9 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
   const uint32_t o_bytes = 16u * a.num_splits * kHeadDim * 4, ml_bytes = 16u * a.num_splits * 8;
   const int cur = merging ? static_cast<int>(mstate >> 31) : 0;   // this launch's exchange buffer
   const __amdgpu_buffer_rsrc_t ro =
-      make_rsrc(uniform_ptr(a.part_o + cur * buf_o + head0 * a.num_splits * kHeadDim), o_bytes);
-  const __amdgpu_buffer_rsrc_t rm = make_rsrc(uniform_ptr(a.part_ml + cur * buf_ml + head0 * a.num_splits * 2), ml_bytes);
+      make_rsrc(uniform_ptr(a.part_o + (2 * head0 + 16 * cur) * a.num_splits * kHeadDim), o_bytes);
+  const __amdgpu_buffer_rsrc_t rm =
+      make_rsrc(uniform_ptr(a.part_ml + (2 * head0 + 16 * cur) * a.num_splits * 2), ml_bytes);
   constexpr int kTasks = 16 * (kHeadDim / 4);                     // (head, 4 dims) items
   constexpr int kPer = (kTasks + 64 * kW - 1) / (64 * kW);        // items per thread
   // In-workgroup merge of one item over the waves' O tiles. Every LDS read is issued

@@ -39,8 +39,10 @@ class DecodeBuffers:
                                   dtype=torch.float32, device=device)
         self.part_ml = torch.empty((num_rows, num_q_heads, num_splits, 2), dtype=torch.float32,
                                    device=device)
-        self.merge_o = torch.empty((2,) + tuple(self.part_o.shape), dtype=torch.float32, device=device)
-        self.merge_ml = torch.empty((2,) + tuple(self.part_ml.shape), dtype=torch.float32, device=device)
+        hkv = num_q_heads // 16   # pair-major: [rows][KV heads][2 buffers][16 heads][splits][...]
+        self.merge_o = torch.empty((num_rows, hkv, 2, 16, num_splits, L.HEAD_DIM), dtype=torch.float32,
+                                   device=device)
+        self.merge_ml = torch.empty((num_rows, hkv, 2, 16, num_splits, 2), dtype=torch.float32, device=device)
         self.counters = torch.empty((num_rows, num_q_heads // 16), dtype=torch.int32, device=device)
         L.msa_merge_workspace_init(num_rows, num_q_heads, L.HEAD_DIM, num_splits, self.merge_o,
                                    self.merge_ml, self.counters)

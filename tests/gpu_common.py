@@ -161,16 +161,17 @@ def assert_merge_ready(bufs):
     c = bufs.counters.cpu().numpy().view(np.uint32)
     assert ((c & 0xffff) == 0).all(), "arrivals left in a state word"
     assert (((c >> 16) & 0x7fff) == S).all(), "state word names another split count"
-    rows, hq = bufs.out.shape[0], bufs.out.shape[1]
-    # the buffers as laid out for S splits (a workspace may be allocated for more)
-    mo = bufs.merge_o.view(torch.int32).reshape(-1)[:2 * rows * hq * S * 128].reshape(2, rows, hq, S, 128)
-    mm = bufs.merge_ml.view(torch.int32).reshape(-1)[:2 * rows * hq * S * 2].reshape(2, rows, hq, S, 2)
-    mo, mm = mo.cpu().numpy(), mm.cpu().numpy()
-    for r in range(c.shape[0]):
-        for g in range(c.shape[1]):
+    rows, hkv = c.shape
+    # pair-major, laid out for S splits (a workspace may be allocated for more)
+    mo = bufs.merge_o.view(torch.int32).reshape(-1)[:rows * hkv * 2 * 16 * S * 128]
+    mm = bufs.merge_ml.view(torch.int32).reshape(-1)[:rows * hkv * 2 * 16 * S * 2]
+    mo = mo.reshape(rows, hkv, 2, 16, S, 128).cpu().numpy()
+    mm = mm.reshape(rows, hkv, 2, 16, S, 2).cpu().numpy()
+    for r in range(rows):
+        for g in range(hkv):
             e = int(c[r, g] >> 31)
-            assert (mo[e, r, 16 * g:16 * g + 16] == M.MERGE_IDLE_BITS).all(), (r, g)
-            assert (mm[e, r, 16 * g:16 * g + 16] == M.MERGE_IDLE_BITS).all(), (r, g)
+            assert (mo[r, g, e] == M.MERGE_IDLE_BITS).all(), (r, g)
+            assert (mm[r, g, e] == M.MERGE_IDLE_BITS).all(), (r, g)
 
 
 def check_step_parity(M, wl: W.Workload, num_splits: int, fused: bool):

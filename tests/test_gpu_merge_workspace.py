@@ -21,8 +21,8 @@ def M():
 
 def test_workspace_init_sets_up_state(M):
     rows, hq, S = 3, 32, 5
-    po = torch.full((2, rows, hq, S, 128), 1.5, dtype=torch.float32, device="cuda")
-    pm = torch.full((2, rows, hq, S, 2), -2.0, dtype=torch.float32, device="cuda")
+    po = torch.full((rows, hq // 16, 2, 16, S, 128), 1.5, dtype=torch.float32, device="cuda")
+    pm = torch.full((rows, hq // 16, 2, 16, S, 2), -2.0, dtype=torch.float32, device="cuda")
     cnt = torch.full((rows, hq // 16), 9, dtype=torch.int32, device="cuda")
     guard = torch.full((64,), 3.0, dtype=torch.float32, device="cuda")
     M.msa_merge_workspace_init(rows, hq, 128, S, po, pm, cnt)
@@ -91,3 +91,26 @@ def test_successive_calls_and_split_changes(M, fmt):
                                     other, ws.merge_o, ws.merge_ml, ws.counters, ws.out)
         torch.cuda.synchronize()
         assert torch.equal(ws.out.view(torch.int16), ref2.out.view(torch.int16)), ns
+
+
+def test_calls_with_fewer_rows_share_the_workspace(M):
+    """The workspace is pair-major: calls with fewer rows (a different batch) use the
+    first rows' slots and state words and leave the others as they were."""
+    full = W.small(W.FMT_NVFP4, [3000, 700, 5000, 9000], 2, num_kv_heads=2, k=16, seed=82)
+    part = W.keep_rows(full, [0, 1, 4, 5])
+    pool = G.gpu_pool(M, full)
+    step, q, q_idx, w, app = G.gpu_step_inputs(M, full)
+    M.msa_kv_append(pool, app[0], app[1], app[2], app[3])
+    ns = 4
+    ws = M.DecodeBuffers(full.num_rows, full.num_heads, full.max_blocks, full.k, ns)
+    for call, wl in enumerate([full, part, full, part, part, full]):
+        st, qq, qi, ww, _ = G.gpu_step_inputs(M, wl)
+        scores = torch.empty((wl.num_rows, wl.max_blocks), dtype=torch.float32, device="cuda")
+        M.msa_index_score(pool, st, qi, ww, scores)
+        ref = _reference(M, wl, pool, st, qq, scores, ns)
+        out = torch.zeros_like(ref.out)
+        M.msa_select_decode_combine(pool, st, qq, scores, wl.k, wl.n_init, wl.n_local, wl.softmax_scale, ns,
+                                    ws.merge_o, ws.merge_ml, ws.counters, out)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.out.view(torch.int16)), call
+        G.assert_merge_ready(ws)
