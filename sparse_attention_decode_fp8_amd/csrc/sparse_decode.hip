@@ -24,14 +24,17 @@
 // Every load a wave needs (selection entry, page id, K/V codes and scales, Q) is
 // issued before the first MFMA, so the kernel pays the memory latency once.
 //
-// The combining variants have the last workgroup of each (row, KV head) to finish
-// merge all splits (a device-scope counter, reset by that workgroup), so the step needs
-// no separate combine launch; with a single split that workgroup writes the output
-// directly and the partials and counter are not touched. The partials cross workgroups (and XCDs, whose L2s are
-// not coherent with each other) as agent-scope atomic stores and loads, which need no
-// cache-flushing fence; on this part such fences cost more than the whole merge. The
-// selecting variant runs the top-k selection of its row in every workgroup (the scores
-// are 4 bytes per block), which costs less than a launch plus a cross-workgroup handoff.
+// The combining variants have the last workgroup of each (row, KV head) to count
+// itself in merge all splits, so the step needs no separate combine launch; with a
+// single split that workgroup writes the output directly and the merge workspace is
+// not touched. The partials cross workgroups (and XCDs, whose L2s are not coherent
+// with each other) through agent-coherent stores that the merger polls against an idle
+// pattern: no cache-flushing fence (on this part such fences cost more than the whole
+// merge) and no wait for store acknowledgements. Two exchange buffers alternate
+// between calls, and each split returns its slot of the idle one to the idle pattern
+// early in the call. The selecting variant runs the top-k selection of its row in
+// every workgroup (the scores are 4 bytes per block), which costs less than a launch
+// plus a cross-workgroup handoff.
 #include <algorithm>
 
 #include "msa_device.h"
@@ -78,7 +81,7 @@ struct DecodeArgs {
   int num_splits;
   float* part_o;
   float* part_ml;
-  int32_t* counters;          // combining variants: [rows][hkv]
+  int32_t* counters;          // combining variants: merge state words [rows][hkv]
   uint16_t* out;              // combining variants: bf16 [rows][hq][128]
 };
 
