@@ -238,7 +238,7 @@ __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(qa[i]));
-    amax = xor_max(xor_max(amax, 16), 32);
+    amax = rows_max(amax);
     const int e = f16_prescale_exp(amax);
     half8_t A0, A1;
 #pragma unroll
@@ -328,10 +328,7 @@ __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
 #pragma unroll
     for (int i = 0; i < kRowsPerLane; ++i) {
       float v = best[i];
-      v = xor_max(v, 1);
-      v = xor_max(v, 2);
-      v = xor_max(v, 4);
-      v = xor_max(v, 8);
+      v = row_max_to_first(v);   // the block maximum, in lane n == 0
       if (n == 0 && rowslot[i] < nr) {
         float* dst = a.scores + static_cast<int64_t>(r0 + rowslot[i]) * a.max_blocks + b;
         // write-through only when this launch's last workgroup selects from the scores;

@@ -61,6 +61,32 @@ __device__ __forceinline__ float max_raw(float a, float b) {
   return r;
 }
 
+// Max / sum over the four lanes l, l^16, l^32, l^48 (the rows of 16 lanes), in every
+// lane, with the row swaps of gfx950 (vector ALU; no LDS round trip). The sums pair
+// the operands as (row0 + row1) + (row2 + row3), in every lane.
+__device__ __forceinline__ float rows_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float a = max_raw(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+  return max_raw(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float a = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+// Max over each row of 16 lanes, delivered to the row's first lane (DPP row shifts
+// towards lane 0; lanes a shift has no source for keep -inf).
+__device__ __forceinline__ float row_max_to_first(float x) {
+  constexpr int kNegInf = static_cast<int>(0xff800000u);
+  x = max_raw(x, __int_as_float(__builtin_amdgcn_update_dpp(kNegInf, __float_as_int(x), 0x101, 0xf, 0xf, false)));
+  x = max_raw(x, __int_as_float(__builtin_amdgcn_update_dpp(kNegInf, __float_as_int(x), 0x102, 0xf, 0xf, false)));
+  x = max_raw(x, __int_as_float(__builtin_amdgcn_update_dpp(kNegInf, __float_as_int(x), 0x104, 0xf, 0xf, false)));
+  x = max_raw(x, __int_as_float(__builtin_amdgcn_update_dpp(kNegInf, __float_as_int(x), 0x108, 0xf, 0xf, false)));
+  return x;
+}
+
 // Two OCP E4M3FN codes (bytes 0 and 1 of `v`, or bytes 2 and 3 with kHi) -> two exact
 // fp16 values. The convert picks the half word itself, so no shift or extract first.
 template <bool kHi = false>
@@ -142,13 +168,6 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x142, 0xa, 0xf, false)));
   x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x143, 0xc, 0xf, false)));
   return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), 63));
-}
-
-__device__ __forceinline__ float xor_max(float v, int mask) {
-  return fmaxf(v, __shfl_xor(v, mask, 64));
-}
-__device__ __forceinline__ float xor_add(float v, int mask) {
-  return v + __shfl_xor(v, mask, 64);
 }
 
 // Agent-scope coherent 16- and 8-byte accesses through a buffer resource: the sc1

@@ -297,7 +297,7 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(qf[i]));
-    amax = xor_max(xor_max(amax, 16), 32);
+    amax = rows_max(amax);
     const int e = f16_prescale_exp(amax);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -441,7 +441,7 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
       // ---- online softmax (per lane: one head)
       float mx = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
                        fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
-      mx = xor_max(xor_max(mx, 16), 32);
+      mx = rows_max(mx);
       const float m_new = fmaxf(m_run, mx);
       const float alpha = exp2f(m_run - m_new);
       float psum = 0.0f;
@@ -483,7 +483,7 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
   }
 
   // ---- merge the waves of the workgroup, write this split's partial
-  const float l_tot = xor_add(xor_add(l_run, 16), 32);
+  const float l_tot = rows_sum(l_run);
   float oscale;
   if constexpr (kFmt == MSA_KV_NVFP4) oscale = a.v_t; else oscale = v_cur;
   {
