@@ -120,7 +120,7 @@ __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
   int64_t slot0 = -1;
   if constexpr (kFused)
     if (a.app.idx_new != nullptr && lane < a.app.n_new) slot0 = a.app.slot[lane];
-  const int seq = __shfl(seq_l, 32, 64);
+  const int seq = __builtin_amdgcn_readlane(seq_l, 32);
   const uint64_t same = __ballot(seq_l == seq);
   // Is r0 the first row of a group? Count the earlier rows of the same request.
   const uint32_t before = ~static_cast<uint32_t>(same);            // lanes 0..31: a different request
@@ -212,7 +212,7 @@ __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
         patch_more = a.app.n_new > 64 || (h0 & (h0 - 1)) != 0;
         if (h0 != 0) {
           const int first = __ffsll(static_cast<unsigned long long>(h0)) - 1;
-          const int off0 = __shfl(static_cast<int>(slot0 % kPage), first, 64);
+          const int off0 = __builtin_amdgcn_readlane(static_cast<int>(slot0 % kPage), first);
           if ((off0 & 15) == n) {
             const uint4* src = reinterpret_cast<const uint4*>(
                 a.app.idx_new + static_cast<int64_t>(first) * kIndexDim + 16 * q);
@@ -270,7 +270,7 @@ __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
           while (hits) {
             const int jj = __ffsll(static_cast<unsigned long long>(hits)) - 1;
             hits &= hits - 1;
-            const int off = __shfl(static_cast<int>(sl % kPage), jj, 64);
+            const int off = __builtin_amdgcn_readlane(static_cast<int>(sl % kPage), jj);
             if ((off & 15) == n) {
               const uint4* src = reinterpret_cast<const uint4*>(
                   a.app.idx_new + static_cast<int64_t>(base + jj) * kIndexDim + 16 * q);

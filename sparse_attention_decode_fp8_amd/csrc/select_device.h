@@ -94,7 +94,7 @@ __device__ void block_select_row(const float* srow, int nb, int k, int n_init, i
       const uint64_t mm = __ballot(match);
       if (mm == 0) continue;
       const int first = __ffsll(static_cast<unsigned long long>(mm)) - 1;
-      const uint32_t d0 = static_cast<uint32_t>(__shfl(static_cast<int>(dg), first, 64));
+      const uint32_t d0 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(dg), first));
       const uint64_t same = __ballot(match && dg == d0);
       if (same == mm) {
         if ((tid & 63) == first) atomicAdd(&sm.hist[d0], __popcll(mm));

@@ -372,8 +372,8 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
   }
   auto lookup = [&](int e, int& b, int64_t& page) {
     if constexpr (kSelect) {
-      b = __shfl(selv, e, 64);
-      page = __shfl(pagev, e, 64);
+      b = __builtin_amdgcn_readlane(selv, e);   // e is the same in every lane
+      page = __builtin_amdgcn_readlane(pagev, e);
     } else {
       b = a.sel[static_cast<int64_t>(r) * a.k + e];
       page = b < 0 ? 0
