@@ -28,7 +28,7 @@ combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_
   float den = 0.0f;
   for (int s = 0; s < num_splits; ++s) {
     const float m = ml[2 * s];
-    const float wgt = m == -INFINITY ? 0.0f : exp2f(m - M);   // M > -inf whenever m is
+    const float wgt = m == -INFINITY ? 0.0f : exp2_raw(m - M);   // M > -inf whenever m is
     den += wgt * ml[2 * s + 1];
     num += wgt * *reinterpret_cast<const float4_t*>(po + static_cast<int64_t>(s) * kHeadDim);
   }

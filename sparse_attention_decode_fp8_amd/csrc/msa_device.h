@@ -44,6 +44,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// 2^x as the hardware instruction alone (exp2f adds a range fix-up for results below
+// 2^-126). Used for softmax and merge weights, whose arguments are <= 0: a weight
+// below 2^-126 of the largest one may come out as zero, which changes no sum.
+__device__ __forceinline__ float exp2_raw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // max(x, 0) as one instruction. Written as fmaxf, the compiler first canonicalises x
 // (a second instruction) to honour signalling NaNs, which the matrix-core results fed
 // here never are.

@@ -229,7 +229,7 @@ __device__ __forceinline__ void merge_slots(__amdgpu_buffer_rsrc_t ro, __amdgpu_
   for (int t = 0; t < kS; ++t) {
     if (t < S) {
       const float m = mls[t][0];
-      const float wgt = m == -INFINITY ? 0.0f : exp2f(m - M);   // M > -inf whenever m is
+      const float wgt = m == -INFINITY ? 0.0f : exp2_raw(m - M);   // M > -inf whenever m is
       den += wgt * mls[t][1];
       num += wgt * ot[t];
     }
@@ -443,14 +443,14 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
                        fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
       mx = rows_max(mx);
       const float m_new = fmaxf(m_run, mx);
-      const float alpha = exp2f(m_run - m_new);
+      const float alpha = exp2_raw(m_run - m_new);
       float psum = 0.0f;
       half8_t Pt;
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = exp2f(x[u][i] - m_new);
+          const float p = exp2_raw(x[u][i] - m_new);
           psum += p;
           Pt[4 * u + i] = static_cast<half_t>(p);
         }
@@ -524,7 +524,7 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
     if (M != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < kW; ++w) {
-        const float wt = exp2f(mw[w] - M);
+        const float wt = exp2_raw(mw[w] - M);
         acc += wt * tw[w];
         l += wt * lw[w];
       }
