@@ -12,6 +12,36 @@
 namespace msa {
 namespace {
 
+template <int kS>
+__device__ __forceinline__ void combine_item(const float* ml, const float* po, int num_splits, float4_t& num,
+                                             float& den) {
+  // every split's (m, l) and O first (entries past the last split repeat it, unused),
+  // then the sums in ascending split order
+  float2_t mls[kS];
+  float4_t ot[kS];
+#pragma unroll
+  for (int t = 0; t < kS; ++t) {
+    const int tt = min(t, num_splits - 1);
+    mls[t] = *reinterpret_cast<const float2_t*>(ml + 2 * tt);
+    ot[t] = *reinterpret_cast<const float4_t*>(po + static_cast<int64_t>(tt) * kHeadDim);
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < kS; ++t)
+    if (t < num_splits) M = fmaxf(M, mls[t][0]);
+  num = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  den = 0.0f;
+#pragma unroll
+  for (int t = 0; t < kS; ++t) {
+    if (t < num_splits) {
+      const float m = mls[t][0];
+      const float wgt = m == -INFINITY ? 0.0f : exp2_raw(m - M);   // M > -inf whenever m is
+      den += wgt * mls[t][1];
+      num += wgt * ot[t];
+    }
+  }
+}
+
 __global__ void __launch_bounds__(256)
 combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
                uint16_t* __restrict__ out, int64_t row_heads, int num_splits) {
@@ -22,15 +52,21 @@ combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_
   const int d4 = static_cast<int>(idx % kQuads);
   const float* ml = part_ml + rh * num_splits * 2;
   const float* po = part_o + rh * num_splits * kHeadDim + 4 * d4;
-  float M = -INFINITY;
-  for (int s = 0; s < num_splits; ++s) M = fmaxf(M, ml[2 * s]);
-  float4_t num = {0.0f, 0.0f, 0.0f, 0.0f};
-  float den = 0.0f;
-  for (int s = 0; s < num_splits; ++s) {
-    const float m = ml[2 * s];
-    const float wgt = m == -INFINITY ? 0.0f : exp2_raw(m - M);   // M > -inf whenever m is
-    den += wgt * ml[2 * s + 1];
-    num += wgt * *reinterpret_cast<const float4_t*>(po + static_cast<int64_t>(s) * kHeadDim);
+  float4_t num;
+  float den;
+  if (num_splits <= 4) combine_item<4>(ml, po, num_splits, num, den);
+  else if (num_splits <= 16) combine_item<16>(ml, po, num_splits, num, den);
+  else {   // up to 64 splits: the same sums, loads in a loop
+    float M = -INFINITY;
+    for (int s = 0; s < num_splits; ++s) M = fmaxf(M, ml[2 * s]);
+    num = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    den = 0.0f;
+    for (int s = 0; s < num_splits; ++s) {
+      const float m = ml[2 * s];
+      const float wgt = m == -INFINITY ? 0.0f : exp2_raw(m - M);
+      den += wgt * ml[2 * s + 1];
+      num += wgt * *reinterpret_cast<const float4_t*>(po + static_cast<int64_t>(s) * kHeadDim);
+    }
   }
   uint16_t o[4];
 #pragma unroll
