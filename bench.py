@@ -224,6 +224,25 @@ def main():
         per_kernel_us[nm] = {"mean": e0.elapsed_time(e1) * 1e3 / (reps * len(pools)),
                              "launches": reps * len(pools)}
 
+    # The table-driven decode entry alone (msa_sparse_decode on the selection the fused
+    # step wrote; partials only), timed the same way: the kernel the decode target names.
+    sd_us = None
+    if not args.separate:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for p in pools:
+                M.msa_sparse_decode(p, step, q, bufs.sel, wl.k, wl.softmax_scale, ns, bufs.part_o,
+                                    bufs.part_ml, sel_pages=bufs.sel_pages)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        sd_us = e0.elapsed_time(e1) * 1e3 / (reps * len(pools))
+
     sel = bufs.sel.cpu().numpy()
     bpt = 144 if wl.fmt == W.FMT_NVFP4 else 256
     dec_bytes, dec_tokens = decode_algorithmic_bytes(wl, sel, bpt)
@@ -296,6 +315,11 @@ def main():
                                  "frac": idx_bytes / t_idx / 1e9 / HBM_PEAK_GBS,
                                  "algorithmic_bytes": idx_bytes, "mean_us": t_idx * 1e6,
                                  "method": idx_method},
+        "sparse_decode_roofline": None if sd_us is None else {
+            "kernel": "msa_sparse_decode", "bound": "hbm", "achieved": dec_bytes / (sd_us * 1e-6) / 1e9,
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dec_bytes / (sd_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "algorithmic_bytes": dec_bytes, "mean_us": sd_us,
+            "method": "the table-driven entry alone on the step's selection (partials, no merge)"},
         "kernel_us": per_kernel_us,
         "cpu_baseline": cpu,
     }
