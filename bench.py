@@ -21,6 +21,12 @@ The roofline entry uses the decode kernel's mean duration and
 its algorithmic bytes (selected visible K/V bytes + Q + O + selection/block-table
 reads). HBM traffic comes from rocprofv3 FETCH_SIZE / WRITE_SIZE counters recorded in
 profiles/ and is reported only while the kernel source is unchanged since then.
+Each duration also carries p10 / p50 / p90 over the replays (each a mean over R
+launches), and the rates are also stated against the read bandwidth a plain streaming
+read of 1 GiB reaches on the same GPU in the same run (`box_read_gbs`).
+
+The CPU baseline is the float64 oracle on a bounded sample of the same workload, timed
+with numpy's BLAS at one thread (`cpu_baseline`) and at up to 16 (`cpu_baseline_all_cores`).
 """
 from __future__ import annotations
 
@@ -53,7 +59,10 @@ def parse():
                     help="index-key format (the workload specifies e4m3; nvfp4 is the option)")
     ap.add_argument("--separate", action="store_true",
                     help="five launches per step (one per stage) instead of the two fused ones")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="oracle time budget, for each of the two thread counts")
+    ap.add_argument("--no-read-probe", action="store_true",
+                    help="skip the 1 GiB streaming-read reference measurement")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one device copy of this size (counter calibration)")
     return ap.parse_args()
@@ -65,6 +74,34 @@ def kernel_source_digest() -> str:
         with open(os.path.join(ROOT, "sparse_attention_decode_fp8_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def stream_read_gbs(torch, dev, gib=1, launches=10):
+    """Read bandwidth the part sustains: a plain streaming-read kernel (libmsaprobe) over
+    a 1 GiB buffer, median of `launches` timed launches after one warm-up launch."""
+    import ctypes
+
+    import numpy as np
+    lib = ctypes.CDLL(os.path.join(ROOT, "sparse_attention_decode_fp8_amd", "libmsaprobe.so"))
+    lib.msa_probe_stream_read.restype = ctypes.c_int
+    lib.msa_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                          ctypes.c_int32, ctypes.c_void_p]
+    nbytes = gib << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    buf.fill_(3)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    wgs = nbytes // (16 * 4 * 256)   # one pass: four 16-byte loads per lane (the fastest grid)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(launches + 1)]
+    assert lib.msa_probe_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), wgs, stream) == 0
+    ev[0].record()
+    for i in range(launches):
+        assert lib.msa_probe_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), wgs, stream) == 0
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    t = np.median([ev[i].elapsed_time(ev[i + 1]) * 1e-3 for i in range(launches)])
+    del buf
+    return nbytes / t / 1e9
 
 
 def decode_algorithmic_bytes(wl, sel, bytes_per_token):
@@ -210,19 +247,25 @@ def main():
                 call(p)
         kgraphs.append(g)
     torch.cuda.synchronize()
-    reps = max(1, min(args.steps, 160) // len(pools))
-    per_kernel_us = {}
-    for nm, g in zip(names, kgraphs):
+    reps = max(1, min(args.steps, 320) // len(pools))
+
+    def time_replays(g):
+        """Mean launch duration over `reps` back-to-back replays of a graph of one
+        launch per replica, and p10 / p50 / p90 of the per-replay means."""
         g.replay()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record()
+        for i in range(reps):
             g.replay()
-        e1.record()
+            ev[i + 1].record()
         torch.cuda.synchronize()
-        per_kernel_us[nm] = {"mean": e0.elapsed_time(e1) * 1e3 / (reps * len(pools)),
-                             "launches": reps * len(pools)}
+        per = np.array([ev[i].elapsed_time(ev[i + 1]) * 1e3 / len(pools) for i in range(reps)])
+        return {"mean": ev[0].elapsed_time(ev[reps]) * 1e3 / (reps * len(pools)),
+                "p10": float(np.percentile(per, 10)), "p50": float(np.percentile(per, 50)),
+                "p90": float(np.percentile(per, 90)), "launches": reps * len(pools)}
+
+    per_kernel_us = {nm: time_replays(g) for nm, g in zip(names, kgraphs)}
 
     # The table-driven decode entry alone (msa_sparse_decode on the selection the fused
     # step wrote; partials only), timed the same way: the kernel the decode target names.
@@ -233,15 +276,8 @@ def main():
             for p in pools:
                 M.msa_sparse_decode(p, step, q, bufs.sel, wl.k, wl.softmax_scale, ns, bufs.part_o,
                                     bufs.part_ml, sel_pages=bufs.sel_pages)
-        g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        sd_us = e0.elapsed_time(e1) * 1e3 / (reps * len(pools))
+        sd = time_replays(g)
+        sd_us = sd["mean"]
 
     sel = bufs.sel.cpu().numpy()
     bpt = 144 if wl.fmt == W.FMT_NVFP4 else 256
@@ -271,6 +307,8 @@ def main():
         if pc.get("source_digest") == kernel_source_digest() and pc.get("num_splits") == ns:
             traffic = pc.get("hbm_bytes_per_launch")
 
+    box_read = None if args.no_read_probe else stream_read_gbs(torch, dev)
+
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 20
         a = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -280,9 +318,9 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
 
-    cpu = None
+    cpu = cpu_all = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, args.cpu_seconds)
+        cpu, cpu_all = cpu_baseline(wl, args.cpu_seconds, [1, min(16, len(os.sched_getaffinity(0)))])
 
     rows = wl.num_rows
     line = {
@@ -308,7 +346,10 @@ def main():
         "roofline": {"kernel": "+".join(decode_kernels), "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes": dec_bytes,
-                     "visible_selected_tokens": dec_tokens, "mean_us": t_dec * 1e6},
+                     "visible_selected_tokens": dec_tokens, "mean_us": t_dec * 1e6,
+                     **({f"{q}_us": per_kernel_us[decode_kernels[0]][q] for q in ("p10", "p50", "p90")}
+                        if len(decode_kernels) == 1 else {}),
+                     "frac_of_box_read": None if box_read is None else achieved / box_read},
         "index_score_roofline": {"kernel": names[0] if not args.separate else "msa_index_score",
                                  "bound": "hbm", "achieved": idx_bytes / t_idx / 1e9,
                                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -319,17 +360,33 @@ def main():
             "kernel": "msa_sparse_decode", "bound": "hbm", "achieved": dec_bytes / (sd_us * 1e-6) / 1e9,
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dec_bytes / (sd_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "algorithmic_bytes": dec_bytes, "mean_us": sd_us,
+            "p10_us": sd["p10"], "p50_us": sd["p50"], "p90_us": sd["p90"],
+            "frac_of_box_read": None if box_read is None else dec_bytes / (sd_us * 1e-6) / 1e9 / box_read,
             "method": "the table-driven entry alone on the step's selection (partials, no merge)"},
+        "box_read_gbs": box_read,
         "kernel_us": per_kernel_us,
         "cpu_baseline": cpu,
+        "cpu_baseline_all_cores": cpu_all,
     }
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(wl, budget_s):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, budget_s, thread_counts):
     """The float64 oracle, unchanged, timed on host cores for a bounded sample of the
     same workload: whole steps (append, index score, select, attention) of the 8
-    requests, round robin, until the time budget is spent; BLAS limited to one thread."""
+    requests, round robin, until the time budget is spent; once per entry of
+    thread_counts, with numpy's BLAS limited to that many threads."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -354,20 +411,25 @@ def cpu_baseline(wl, budget_s):
             pos = np.unique(pos[pos < L])
             O.kv_append(pool, wl.slots(s, pos), wl.k_src[s][pos], wl.v_src[s][pos], None)
             cases.append((pool, args, len(rows)))
-        done, steps, t_total = 0, 0, 0.0
-        while t_total < budget_s:
-            pool, args, nrows = cases[steps % len(cases)]
-            t = time.perf_counter()
-            O.decode_step(pool, *args)
-            t_total += time.perf_counter() - t
-            done += nrows
-            steps += 1
-    return {"value": done / t_total, "unit": "q-tok/s", "cores": 1, "kind": "oracle",
-            "sample": f"{steps} oracle steps of single requests of the same workload, round robin "
-                      f"(each: append {wl.n_append} token(s), index score over the request's "
-                      f"tokens, top-{wl.k} select, attention over the selected pages for "
-                      f"{wl.num_heads} heads), {done} query rows in {t_total:.1f} s, "
-                      f"numpy/BLAS limited to 1 thread"}
+    out = []
+    for threads in thread_counts:
+        with threadpool_limits(threads):
+            done, steps, t_total = 0, 0, 0.0
+            while t_total < budget_s:
+                pool, args, nrows = cases[steps % len(cases)]
+                t = time.perf_counter()
+                O.decode_step(pool, *args)
+                t_total += time.perf_counter() - t
+                done += nrows
+                steps += 1
+        out.append({"value": done / t_total, "unit": "q-tok/s", "cores": threads, "kind": "oracle",
+                    "cpu": cpu_model(),
+                    "sample": f"{steps} oracle steps of single requests of the same workload, round robin "
+                              f"(each: append {wl.n_append} token(s), index score over the request's "
+                              f"tokens, top-{wl.k} select, attention over the selected pages for "
+                              f"{wl.num_heads} heads), {done} query rows in {t_total:.1f} s, "
+                              f"numpy/BLAS limited to {threads} thread(s)"})
+    return out
 
 
 if __name__ == "__main__":

@@ -3,7 +3,8 @@
     python sparse_attention_decode_fp8_amd/build.py [--jobs N]
 
 Every HIP source is compiled to an object with `hipcc --offload-arch=gfx950`, then
-linked into sparse_attention_decode_fp8_amd/libmsadecode.so next to this file.
+linked into sparse_attention_decode_fp8_amd/libmsadecode.so next to this file (and the
+bench's read-bandwidth reference into libmsaprobe.so).
 """
 from __future__ import annotations
 
@@ -21,6 +22,9 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmsadecode.so")
 SOURCES = ["kv_append.hip", "index_score.hip", "select_topk.hip", "sparse_decode.hip",
            "combine.hip", "api.cpp"]
+# The bench's read-bandwidth reference, a library of its own (not part of the decode path).
+PROBE_LIB = os.path.join(PKG, "libmsaprobe.so")
+PROBE_SOURCES = ["stream_read.hip"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
           "-Wall", "-Wno-unused-function"]
@@ -51,18 +55,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 6, verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(jobs: int = 6, verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(_compile, SOURCES + PROBE_SOURCES))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

@@ -35,6 +35,21 @@ def test_every_declared_symbol_is_exported():
         assert getattr(L.LIB, n) is not None
 
 
+def test_read_probe_library_loads_and_validates():
+    """The bench's streaming-read reference (libmsaprobe.so) exports its one entry and
+    rejects bad arguments before any launch."""
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(L.LIB_PATH), "libmsaprobe.so"))
+    f = lib.msa_probe_stream_read
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    assert f(None, 16, 16, 1, None) == -1            # null buffer
+    assert f(16, 24, 16, 1, None) == -1              # not a multiple of 16 bytes
+    assert f(16, 16, None, 1, None) == -1            # null sink
+    assert f(16, 16, 16, 0, None) == -1              # no workgroups
+    assert f(8, 16, 16, 1, None) == -1               # misaligned
+    assert f(16, 0, 16, 1, None) == 0                # nothing to read: no launch
+
+
 def test_binding_names_match_c_entry_points():
     import sparse_attention_decode_fp8_amd as M
     for n in ("msa_kv_append", "msa_index_score", "msa_select_topk", "msa_sparse_decode",
