@@ -21,7 +21,8 @@ numpy float64, in the order the method runs it:
 
   kv_append      quantise new K/V/index-K into their 128-token page slots
   index_keys     exact value of a page's index keys (E4M3 or NVFP4)
-  index_score    per-token index score, max-pooled into 128-token blocks
+  index_score    per-token index score, max-pooled into 128-token blocks (one
+                 table per row, or one per KV head over its share of index heads)
   select_topk    top-k blocks, ties to the smaller block, ascending, -1 padded
   split_partials split-KV online-softmax partials (m, l, O) per split
   combine        fixed-order log-sum-exp merge with one divide per output
@@ -307,8 +308,9 @@ def dequant_page(pool: dict, page: int, head: int, kv: str) -> np.ndarray:
 # Step a2: index score and block max-pool
 # --------------------------------------------------------------------------------
 def index_score(pool: dict, block_table, row_seq, row_pos, q_idx_bits, w,
-                max_blocks: int) -> np.ndarray:
-    """Block scores S [rows][max_blocks] (float64).
+                max_blocks: int, tables: int = 1) -> np.ndarray:
+    """Block scores S [rows][max_blocks] (float64), or S [rows][tables][max_blocks]
+    when tables > 1.
 
     The pages name the scorer ([GB300] "The TP4 decode target": "an index scorer
     that prefetches older index-K pages"; [Rubin] commits: a CuTe DSL scorer and
@@ -318,9 +320,19 @@ def index_score(pool: dict, block_table, row_seq, row_pos, q_idx_bits, w,
         s_p = sum_h w[r,h] * max(0, q_idx[r,h] . k_p)
     and the block score is the max of s_p over the block's visible tokens.
     Blocks past the row's last visible block are -inf; so is nothing else.
+
+    Per-KV-head tables ([Rubin] commits: the indexer hands "KV-head-reduced
+    scores" to its selector, and the prefill tile select runs one CTA per KV head
+    and writes a head-major table). Reading: with `tables` = T tables per row,
+    the Hi index heads are split into T equal consecutive groups and table t
+    sums only over its group, h in [t*Hi/T, (t+1)*Hi/T); T = 1 is the shared
+    score above.
     """
     rows = len(row_pos)
-    S = np.full((rows, max_blocks), -np.inf)
+    Hi = np.asarray(w).shape[1]
+    assert tables >= 1 and Hi % tables == 0, "index heads must split evenly into the tables"
+    per = Hi // tables
+    S = np.full((rows, tables, max_blocks), -np.inf)
     for r in range(rows):
         seq, pos = int(row_seq[r]), int(row_pos[r])
         q = bf16_bits_to_f64(q_idx_bits[r])                     # [Hi][di]
@@ -330,9 +342,10 @@ def index_score(pool: dict, block_table, row_seq, row_pos, q_idx_bits, w,
             n_vis = min(PAGE, pos - PAGE * b + 1)
             K = index_keys(pool, page, n_vis)                   # [n_vis][di]
             dots = K @ q.T                                       # [n_vis][Hi]
-            s = (np.maximum(dots, 0.0) * wr).sum(axis=1)
-            S[r, b] = s.max()
-    return S
+            terms = np.maximum(dots, 0.0) * wr                   # [n_vis][Hi]
+            for t in range(tables):
+                S[r, t, b] = terms[:, t * per:(t + 1) * per].sum(axis=1).max()
+    return S[:, 0] if tables == 1 else S
 
 
 # --------------------------------------------------------------------------------
@@ -350,7 +363,13 @@ def select_topk(S: np.ndarray, row_pos, k: int, n_init: int = 0, n_local: int = 
     selects 0..nb-1. Otherwise the first n_init and last n_local blocks are
     forced and count inside k; the other k - |forced| slots go to the best
     remaining blocks by (higher score, then smaller index).
+    Per-KV-head scores S [rows][T][max_blocks] give one table per (row, KV head),
+    sel [rows][T][k], each selected by the same rule from its own scores.
     """
+    if S.ndim == 3:
+        rows, T = S.shape[:2]
+        flat = select_topk(S.reshape(rows * T, -1), np.repeat(np.asarray(row_pos), T), k, n_init, n_local)
+        return flat.reshape(rows, T, k)
     rows = S.shape[0]
     sel = np.full((rows, k), -1, dtype=np.int32)
     for r in range(rows):
@@ -406,8 +425,10 @@ def split_partials(pool: dict, block_table, row_seq, row_pos, q_bits, sel, softm
     head, query row)". Reading: split s of S takes the selection entries
     [floor(s*k/S), floor((s+1)*k/S)); a split with no visible token has
     m = -inf, l = 0, O = 0. Returns m, l [rows][Hq][S] and O [rows][Hq][S][D].
+    sel is [rows][k] (one table per row) or [rows][Hkv][k] (KV head g reads
+    table g).
     """
-    rows, k = sel.shape
+    rows, k = sel.shape[0], sel.shape[-1]
     Hq = q_bits.shape[1]
     D = pool["D"]
     m = np.full((rows, Hq, num_splits), -np.inf)
@@ -418,10 +439,11 @@ def split_partials(pool: dict, block_table, row_seq, row_pos, q_bits, sel, softm
         q = bf16_bits_to_f64(q_bits[r])                           # [Hq][D]
         for s in range(num_splits):
             lo, hi = (s * k) // num_splits, ((s + 1) * k) // num_splits
-            toks = _row_tokens(sel[r, lo:hi], pos)
-            if len(toks) == 0:
-                continue
             for g in range(pool["Hkv"]):
+                table = sel[r] if sel.ndim == 2 else sel[r, g]
+                toks = _row_tokens(table[lo:hi], pos)
+                if len(toks) == 0:
+                    continue
                 K, V = _gather_kv(pool, block_table, seq, toks, g)
                 for h in range(g * HEADS_PER_KV, (g + 1) * HEADS_PER_KV):
                     x = softmax_scale * (K @ q[h]) * LOG2E
@@ -454,6 +476,8 @@ def attend(pool: dict, block_table, row_seq, row_pos, q_bits, sel, softmax_scale
 
     Query head h reads KV head h // 16 ([Rubin] Description: 16 query heads per
     KV head; reading: contiguous grouping). logit = softmax_scale * q . K_p.
+    sel is [rows][k] (one table per row) or [rows][Hkv][k] (KV head g attends
+    the blocks of table g).
     """
     rows = sel.shape[0]
     Hq = q_bits.shape[1]
@@ -461,8 +485,8 @@ def attend(pool: dict, block_table, row_seq, row_pos, q_bits, sel, softmax_scale
     for r in range(rows):
         seq, pos = int(row_seq[r]), int(row_pos[r])
         q = bf16_bits_to_f64(q_bits[r])
-        toks = _row_tokens(sel[r], pos)
         for g in range(pool["Hkv"]):
+            toks = _row_tokens(sel[r] if sel.ndim == 2 else sel[r, g], pos)
             K, V = _gather_kv(pool, block_table, seq, toks, g)
             for h in range(g * HEADS_PER_KV, (g + 1) * HEADS_PER_KV):
                 x = softmax_scale * (K @ q[h])
@@ -473,11 +497,12 @@ def attend(pool: dict, block_table, row_seq, row_pos, q_bits, sel, softmax_scale
 
 def decode_step(pool: dict, block_table, row_seq, row_pos, slot, k_new, v_new, idx_new,
                 q_idx_bits, w, q_bits, k: int, softmax_scale: float, max_blocks: int,
-                n_init: int = 0, n_local: int = 1):
+                n_init: int = 0, n_local: int = 1, tables: int = 1):
     """One decode step in the method's order: append, score, select, attend.
-    Mutates `pool` (the append). Returns (S, sel, out)."""
+    Mutates `pool` (the append). Returns (S, sel, out); tables = Hkv selects per
+    KV head."""
     kv_append(pool, slot, k_new, v_new, idx_new)
-    S = index_score(pool, block_table, row_seq, row_pos, q_idx_bits, w, max_blocks)
+    S = index_score(pool, block_table, row_seq, row_pos, q_idx_bits, w, max_blocks, tables)
     sel = select_topk(S, row_pos, k, n_init, n_local)
     out = attend(pool, block_table, row_seq, row_pos, q_bits, sel, softmax_scale)
     return S, sel, out

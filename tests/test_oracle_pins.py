@@ -436,3 +436,86 @@ def test_index_score_same_for_nvfp4_and_e4m3_keys_that_both_hold_exactly():
     S0 = O.index_score(pools[0], bt, [0, 0], [L - 1, 200], q, w, 3)
     S1 = O.index_score(pools[1], bt, [0, 0], [L - 1, 200], q, w, 3)
     assert np.array_equal(S0, S1) and np.isfinite(S0[0]).all() and np.isneginf(S0[1, 2])
+
+
+# ---- per-KV-head selection tables (reading: T tables per row, index heads split into
+# T consecutive equal groups; KV head g attends the blocks of table g)
+def test_index_score_per_table_unit_key_closed_form():
+    keys = np.zeros((130, 64))
+    keys[7, 13] = 1.0          # block 0: a unit key along dim 13
+    keys[129, 2] = 1.0         # block 1: along dim 2
+    pool, bt = _tiny_pool_with_keys(keys)
+    q = np.zeros((1, 4, 64), np.float32)
+    q[0, :, 13] = [1.0, -2.0, 3.0, 0.5]
+    q[0, :, 2] = [-1.0, 4.0, 0.25, 2.0]
+    w = np.array([[0.5, 0.25, 2.0, 1.0]], np.float32)
+    qb = W.to_bf16_bits(q)
+    S4 = O.index_score(pool, bt, [0], [129], qb, w, 3, tables=4)
+    # table t holds index head t alone: w_t * relu(q_t[d])
+    assert list(S4[0, :, 0]) == [0.5, 0.0, 6.0, 0.5]
+    assert list(S4[0, :, 1]) == [0.0, 1.0, 0.5, 2.0]
+    S2 = O.index_score(pool, bt, [0], [129], qb, w, 3, tables=2)
+    # table 0: heads 0, 1; table 1: heads 2, 3
+    assert list(S2[0, :, 0]) == [0.5, 6.5]
+    assert list(S2[0, :, 1]) == [1.0, 2.5]
+    assert np.all(np.isneginf(S4[0, :, 2])) and np.all(np.isneginf(S2[0, :, 2]))
+    S1 = O.index_score(pool, bt, [0], [129], qb, w, 3)
+    assert list(S1[0, :2]) == [7.0, 3.5]
+
+
+def test_index_score_tables_partition_the_heads():
+    """Every token's score is the sum of its per-table terms: with one token per block
+    the shared block score is the sum of the table scores."""
+    rng = np.random.default_rng(71)
+    keys = np.zeros((128 * 3, 64))
+    for b in range(3):
+        keys[128 * b + 5] = O.e4m3_table()[O.e4m3_encode(rng.standard_normal(64))]
+    pool, bt = _tiny_pool_with_keys(keys)
+    for p in range(128 * 3):
+        if p % 128 != 5:
+            pool["index_k"][bt[0, p // 128], p % 128] = 0      # zero keys score 0
+    q = W.to_bf16_bits(rng.standard_normal((1, 4, 64), dtype=np.float32))
+    w = rng.uniform(0, 1, (1, 4)).astype(np.float32)
+    S1 = O.index_score(pool, bt, [0], [3 * 128 - 1], q, w, 3)
+    for T in (2, 4):
+        ST = O.index_score(pool, bt, [0], [3 * 128 - 1], q, w, 3, tables=T)
+        assert np.allclose(ST[0].sum(axis=0), S1[0], rtol=1e-15, atol=0)
+
+
+def test_select_per_table_matches_dominance_brute_force():
+    rng = np.random.default_rng(72)
+    nb, k, T = 9, 4, 3
+    S = np.round(rng.standard_normal((2, T, nb + 1)), 1)
+    S[:, :, nb:] = -np.inf
+    pos = np.full(2, (nb - 1) * 128 + 3)
+    sel = O.select_topk(S, pos, k)
+    assert sel.shape == (2, T, k)
+    for r in range(2):
+        for t in range(T):
+            assert list(sel[r, t]) == _dominance_select(S[r, t], nb, k, 0, 1)
+
+
+def test_attend_per_kv_head_tables_reduce_to_shared_tables():
+    """KV head g with table g gives the heads of g exactly what a shared table equal
+    to table g gives them (and equal tables give the shared result everywhere)."""
+    wl = W.small(W.FMT_NVFP4, [900, 700], 1, num_kv_heads=2, k=3, seed=73)
+    pool = _oracle_pool(wl)
+    rng = np.random.default_rng(74)
+    nb = wl.row_pos // 128 + 1
+    sel3 = np.full((wl.num_rows, 2, wl.k), -1, np.int32)
+    for r in range(wl.num_rows):
+        for g in range(2):
+            pick = np.sort(rng.choice(nb[r] - 1, wl.k - 1, replace=False))
+            sel3[r, g] = list(pick) + [nb[r] - 1]
+    out3 = O.attend(pool, wl.block_table, wl.row_seq, wl.row_pos, wl.q, sel3, wl.softmax_scale)
+    for g in range(2):
+        shared = O.attend(pool, wl.block_table, wl.row_seq, wl.row_pos, wl.q, sel3[:, g],
+                          wl.softmax_scale)
+        assert np.array_equal(out3[:, 16 * g:16 * g + 16], shared[:, 16 * g:16 * g + 16])
+    same = np.repeat(sel3[:, :1], 2, axis=1)
+    assert np.array_equal(O.attend(pool, wl.block_table, wl.row_seq, wl.row_pos, wl.q, same, wl.softmax_scale),
+                          O.attend(pool, wl.block_table, wl.row_seq, wl.row_pos, wl.q, sel3[:, 0], wl.softmax_scale))
+    for ns in (1, 2, 3):
+        m, l, Op = O.split_partials(pool, wl.block_table, wl.row_seq, wl.row_pos, wl.q, sel3,
+                                    wl.softmax_scale, ns)
+        assert np.max(np.abs(O.combine(m, l, Op) - out3)) < 1e-12
