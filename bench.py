@@ -57,6 +57,8 @@ def parse():
                     help="workload (1, the default, is the one the metric is quoted on)")
     ap.add_argument("--index-fmt", choices=["e4m3", "nvfp4"], default="e4m3",
                     help="index-key format (the workload specifies e4m3; nvfp4 is the option)")
+    ap.add_argument("--per-kv-head", action="store_true",
+                    help="one selection per (row, KV head), each from its share of the index heads")
     ap.add_argument("--separate", action="store_true",
                     help="five launches per step (one per stage) instead of the two fused ones")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -106,19 +108,24 @@ def stream_read_gbs(torch, dev, gib=1, launches=10):
 
 def decode_algorithmic_bytes(wl, sel, bytes_per_token):
     """Selected visible tokens (union over a request's rows) x KV heads x bytes per
-    token, + Q and O (bf16), + selection table and block-table entries read."""
+    token, + Q and O (bf16), + selection table and block-table entries read. With
+    per-KV-head tables (sel [rows][H_kv][k]) each KV head counts its own union."""
     import numpy as np
-    tok = 0
-    for s in range(len(wl.ctx_lens)):
-        rows = np.nonzero(wl.row_seq == s)[0]
-        vis = set()
-        for r in rows:
-            for b in sel[r]:
-                if b >= 0:
-                    hi = min(128 * (int(b) + 1), int(wl.row_pos[r]) + 1)
-                    vis.update(range(128 * int(b), hi))
-        tok += len(vis)
-    kv = tok * wl.num_kv_heads * bytes_per_token
+    tables = sel.shape[1] if sel.ndim == 3 else 1
+    tok_heads = 0
+    for t in range(tables):
+        st = sel[:, t] if sel.ndim == 3 else sel
+        for s in range(len(wl.ctx_lens)):
+            rows = np.nonzero(wl.row_seq == s)[0]
+            vis = set()
+            for r in rows:
+                for b in st[r]:
+                    if b >= 0:
+                        hi = min(128 * (int(b) + 1), int(wl.row_pos[r]) + 1)
+                        vis.update(range(128 * int(b), hi))
+            tok_heads += len(vis)
+    tok = tok_heads // tables if tables > 1 else tok_heads
+    kv = tok_heads * (wl.num_kv_heads // tables) * bytes_per_token
     qo = 2 * wl.num_rows * wl.num_heads * 128 * 2
     meta = sel.size * 4 + int((sel >= 0).sum()) * 4
     return kv + qo + meta, tok
@@ -159,12 +166,13 @@ def main():
                         bf16(wl.k_src[s][:L]), bf16(wl.v_src[s][:L]), bf16(wl.idx_src[s][:L]))
     torch.cuda.synchronize()
     pools = [pool0] + [pool0.clone() for _ in range(args.replicas - 1)]
-    step = M.Step(wl.block_table, wl.row_seq, wl.row_pos)
+    tables = wl.num_kv_heads if args.per_kv_head else 1
+    step = M.Step(wl.block_table, wl.row_seq, wl.row_pos, sel_tables=tables)
     q, q_idx = bf16(wl.q), bf16(wl.q_idx)
     w = torch.from_numpy(wl.w).to(dev)
     sl, kb, vb, ib = wl.step_tokens()
     slot, k_new, v_new, idx_new = torch.from_numpy(sl).to(dev), bf16(kb), bf16(vb), bf16(ib)
-    bufs = M.DecodeBuffers(wl.num_rows, wl.num_heads, wl.max_blocks, wl.k, ns)
+    bufs = M.DecodeBuffers(wl.num_rows, wl.num_heads, wl.max_blocks, wl.k, ns, sel_tables=tables)
     print(f"[bench] {args.replicas} pool replicas ready, splits {ns}", file=sys.stderr, flush=True)
 
     def one_step(p, stream=None):
@@ -304,7 +312,8 @@ def main():
     if os.path.exists(prof):
         with open(prof) as fh:
             pc = json.load(fh)
-        if pc.get("source_digest") == kernel_source_digest() and pc.get("num_splits") == ns:
+        if (pc.get("source_digest") == kernel_source_digest() and pc.get("num_splits") == ns
+                and tables == 1 and args.config == WORKLOAD_CFG and args.index_fmt == "e4m3"):
             traffic = pc.get("hbm_bytes_per_launch")
 
     box_read = None if args.no_read_probe else stream_read_gbs(torch, dev)
@@ -320,7 +329,7 @@ def main():
 
     cpu = cpu_all = None
     if not args.no_cpu_baseline:
-        cpu, cpu_all = cpu_baseline(wl, args.cpu_seconds, [1, min(16, len(os.sched_getaffinity(0)))])
+        cpu, cpu_all = cpu_baseline(wl, args.cpu_seconds, [1, min(16, len(os.sched_getaffinity(0)))], tables)
 
     rows = wl.num_rows
     line = {
@@ -342,7 +351,8 @@ def main():
                    "q_heads": wl.num_heads, "head_dim": 128, "cached_tokens": int(wl.ctx_lens[0]) if len(set(wl.ctx_lens.tolist())) == 1 else
                    f"{int(wl.ctx_lens.min())}..{int(wl.ctx_lens.max())} (mean {float(wl.ctx_lens.mean()):.0f})",
                    "appended_tokens": wl.n_append, "top_k": wl.k, "kv_format": "nvfp4" if wl.fmt == W.FMT_NVFP4 else "fp8",
-                   "num_splits": ns, "pool_replicas": args.replicas, "parallelism": "single GPU"},
+                   "num_splits": ns, "selection": "per KV head" if tables > 1 else "per query row",
+                   "pool_replicas": args.replicas, "parallelism": "single GPU"},
         "roofline": {"kernel": "+".join(decode_kernels), "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes": dec_bytes,
@@ -382,7 +392,7 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(wl, budget_s, thread_counts):
+def cpu_baseline(wl, budget_s, thread_counts, tables=1):
     """The float64 oracle, unchanged, timed on host cores for a bounded sample of the
     same workload: whole steps (append, index score, select, attention) of the 8
     requests, round robin, until the time budget is spent; once per entry of
@@ -405,7 +415,7 @@ def cpu_baseline(wl, budget_s, thread_counts):
             args = (wl.block_table, wl.row_seq[rows], wl.row_pos[rows], sl, kb, vb, ib,
                     wl.q_idx[rows], wl.w[rows], wl.q[rows], wl.k, wl.softmax_scale, wl.max_blocks)
             # untimed: learn which pages the step attends and give the pool their K/V
-            S = O.index_score(pool, *args[:3], args[7], args[8], wl.max_blocks)
+            S = O.index_score(pool, *args[:3], args[7], args[8], wl.max_blocks, tables)
             sel = O.select_topk(S, args[2], wl.k, wl.n_init, wl.n_local)
             pos = np.concatenate([np.arange(128 * b, min(128 * (b + 1), L)) for b in sel.ravel() if b >= 0])
             pos = np.unique(pos[pos < L])
@@ -418,7 +428,7 @@ def cpu_baseline(wl, budget_s, thread_counts):
             while t_total < budget_s:
                 pool, args, nrows = cases[steps % len(cases)]
                 t = time.perf_counter()
-                O.decode_step(pool, *args)
+                O.decode_step(pool, *args, tables=tables)
                 t_total += time.perf_counter() - t
                 done += nrows
                 steps += 1

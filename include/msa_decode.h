@@ -68,6 +68,7 @@ typedef enum {
 #define MSA_HEADS_PER_KV 16   /* [Rubin] Description: 16 query heads per KV head          */
 #define MSA_MAX_TOPK 64
 #define MSA_MAX_BLOCKS 12288  /* blocks per sequence (1.5M tokens)                        */
+#define MSA_MAX_SEL_TABLES 4  /* per-KV-head selection: at most 4 tables per row          */
 /* Bit pattern of every fp32 word of an idle split-merge workspace (a signalling NaN). */
 #define MSA_MERGE_IDLE_BITS 0x7fbadbadu
 
@@ -122,6 +123,16 @@ typedef struct {
  * tokens of a speculative step). Its visible blocks are 0 .. row_pos[r] / 128.
  * When num_rows > 0, num_seqs must be at least 1 and every row_seq value must lie in
  * [0, num_seqs) (MSA_ERR_INVALID_ARG for num_seqs == 0; the values are trusted).
+ *
+ * sel_tables: selection tables per query row ([Rubin] commit messages: the indexer
+ * hands KV-head-reduced scores to its selector; the prefill tile select runs per KV
+ * head and writes a head-major table). 0 or 1: one table per row, shared by every KV
+ * head. T > 1: one table per (row, KV head); T must equal the pool's num_kv_heads, and
+ * every per-row array of the selection gains a table axis after the row:
+ *   block_scores [num_rows][T][max_blocks_per_seq], sel and sel_pages [num_rows][T][k].
+ * Table t is scored from index heads [t * n_idx_heads / T, (t + 1) * n_idx_heads / T)
+ * (n_idx_heads must be a multiple of T), selected by the same rule, and read by KV
+ * head t. At most MSA_MAX_SEL_TABLES; negative is MSA_ERR_INVALID_ARG.
  */
 typedef struct {
   int32_t num_seqs;
@@ -130,6 +141,7 @@ typedef struct {
   const int32_t* block_table; /* [num_seqs][max_blocks_per_seq] logical block -> page id */
   const int32_t* row_seq;     /* [num_rows]                                              */
   const int32_t* row_pos;     /* [num_rows]                                              */
+  int32_t sel_tables;         /* 0/1: shared selection; num_kv_heads: one per KV head    */
 } msa_step_t;
 
 /*
@@ -161,7 +173,9 @@ msa_status_t msa_kv_append(const msa_kv_pool_t* pool, int32_t n_new, const int64
  * index-K pages) but not its formula; this is the definition the library adopts.
  *   q_idx  : bf16 [num_rows][n_idx_heads][index_dim]
  *   w      : fp32 [num_rows][n_idx_heads]
- *   block_scores : fp32 [num_rows][max_blocks_per_seq] (output)
+ *   block_scores : fp32 [num_rows][max_blocks_per_seq] (output), or
+ *                  [num_rows][T][max_blocks_per_seq] with T = step->sel_tables > 1, where
+ *                  table t sums only the index heads of its share (see msa_step_t)
  * n_idx_heads must be 1, 2 or 4. Accumulation is fp32 in a fixed order that does not
  * depend on the token's position, so identical keys give bit-identical scores.
  */
@@ -182,6 +196,8 @@ msa_status_t msa_index_score(const msa_kv_pool_t* pool, const msa_step_t* step,
  *   sel          : int32 [num_rows][k] (output, logical block ids)
  *   sel_pages    : int32 [num_rows][k] (output, may be NULL) the physical page of each
  *                  selected block, block_table[row_seq[r]][sel[r][i]], -1 where sel is -1
+ * With step->sel_tables = T > 1 every (row, table) is selected on its own from
+ * block_scores [num_rows][T][max_blocks_per_seq] into sel / sel_pages [num_rows][T][k].
  * 1 <= k <= 64, n_init >= 0, n_local >= 0, n_init + n_local <= k,
  * max_blocks_per_seq <= 12288. The result is deterministic for any tie width.
  */
@@ -219,9 +235,10 @@ msa_status_t msa_append_score_select(const msa_kv_pool_t* pool, const msa_step_t
  *   part_ml[r][h][s] = { m = max_p x_p, l = sum_p 2^(x_p - m) }  (m = -inf, l = 0 if empty)
  *   part_o[r][h][s][:] = sum_p 2^(x_p - m) * V_p                   (0 if empty)
  *   q         : bf16 [num_rows][num_q_heads][head_dim]
- *   sel       : int32 [num_rows][k] as written by msa_select_topk
- *   sel_pages : int32 [num_rows][k] page ids as written by msa_select_topk, or NULL to
- *               look each block up in the block table
+ *   sel       : int32 [num_rows][k] as written by msa_select_topk ([num_rows][T][k] with
+ *               step->sel_tables = T > 1: KV head g reads table g)
+ *   sel_pages : int32, the shape of sel, page ids as written by msa_select_topk, or NULL
+ *               to look each block up in the block table
  *   part_o    : fp32 [num_rows][num_q_heads][num_splits][head_dim]  (output)
  *   part_ml   : fp32 [num_rows][num_q_heads][num_splits][2]         (output)
  * num_q_heads must be 16 * num_kv_heads; 1 <= num_splits <= k.

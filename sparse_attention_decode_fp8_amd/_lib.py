@@ -46,7 +46,8 @@ class MsaKvPool(ctypes.Structure):
 class MsaStep(ctypes.Structure):
     _fields_ = [("num_seqs", ctypes.c_int32), ("num_rows", ctypes.c_int32),
                 ("max_blocks_per_seq", ctypes.c_int32), ("block_table", ctypes.c_void_p),
-                ("row_seq", ctypes.c_void_p), ("row_pos", ctypes.c_void_p)]
+                ("row_seq", ctypes.c_void_p), ("row_pos", ctypes.c_void_p),
+                ("sel_tables", ctypes.c_int32)]
 
 
 EXPORTS = ["msa_kv_append", "msa_index_score", "msa_select_topk", "msa_append_score_select",
@@ -158,19 +159,22 @@ class KVPool:
 
 
 class Step:
-    """Per-step metadata on the GPU: block table, row -> request, row -> position."""
+    """Per-step metadata on the GPU: block table, row -> request, row -> position, and
+    the number of selection tables per row (1: shared by the KV heads; the pool's KV-head
+    count: one per KV head, with a table axis after the row in scores and selections)."""
 
-    def __init__(self, block_table, row_seq, row_pos, device="cuda"):
+    def __init__(self, block_table, row_seq, row_pos, device="cuda", sel_tables=1):
         bt = torch.as_tensor(block_table, dtype=torch.int32).to(device).contiguous()
         self.block_table = bt
         self.row_seq = torch.as_tensor(row_seq, dtype=torch.int32).to(device).contiguous()
         self.row_pos = torch.as_tensor(row_pos, dtype=torch.int32).to(device).contiguous()
         self.num_seqs, self.max_blocks = bt.shape
         self.num_rows = self.row_pos.numel()
+        self.sel_tables = sel_tables
 
     def cstruct(self) -> MsaStep:
         return MsaStep(self.num_seqs, self.num_rows, self.max_blocks, self.block_table.data_ptr(),
-                       self.row_seq.data_ptr(), self.row_pos.data_ptr())
+                       self.row_seq.data_ptr(), self.row_pos.data_ptr(), self.sel_tables)
 
 
 def msa_kv_append(pool: KVPool, slot, k_new=None, v_new=None, idx_k_new=None, stream=None):

@@ -83,8 +83,11 @@ __device__ __forceinline__ uint4 encode_key16(uint4 lo, uint4 hi, float idx_t) {
   }
 }
 
-template <int kHi, int kFmt, bool kFused, bool kIdxNv>
+// kG score tables per row: table t sums the index heads [t * kHi / kG, (t + 1) * kHi / kG).
+template <int kHi, int kG, int kFmt, bool kFused, bool kIdxNv>
 __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
+  static_assert(kHi % kG == 0, "index heads split evenly into the tables");
+  constexpr int kHpg = kHi / kG;
   extern __shared__ uint32_t sel_keys[];        // fused: selection scratch [max_blocks]
   __shared__ SelectSmem sm;
   __shared__ int s_last;
@@ -290,9 +293,11 @@ __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
       for (int t = 0; t < 8; ++t)
         if (t == pt) key[t] = pv;
     }
-    float best[kRowsPerLane];
+    float best[kRowsPerLane][kG];
 #pragma unroll
-    for (int i = 0; i < kRowsPerLane; ++i) best[i] = -INFINITY;
+    for (int i = 0; i < kRowsPerLane; ++i)
+#pragma unroll
+      for (int t = 0; t < kG; ++t) best[i][t] = -INFINITY;
     // Tokens past a row's position are masked only in a block that holds one (the
     // last visible block of some row of the group); elsewhere the loop skips the test.
     bool ends_here = false;
@@ -309,16 +314,19 @@ __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
         const int p = b * kPage + 16 * t + n;      // absolute position of this lane's token
 #pragma unroll
         for (int i = 0; i < kRowsPerLane; ++i) {
-          float s = 0.0f;
 #pragma unroll
-          for (int hh = 0; hh < kHi; ++hh) {
-            const int jj = i * kHi + hh;
-            s = fmaf(wi[jj], relu_raw(acc[jj]), s);
-          }
-          if constexpr (decltype(masked)::value) {
-            if (p <= pos[i]) best[i] = max_raw(best[i], s);
-          } else {
-            best[i] = max_raw(best[i], s);
+          for (int t = 0; t < kG; ++t) {
+            float s = 0.0f;
+#pragma unroll
+            for (int hh = t * kHpg; hh < (t + 1) * kHpg; ++hh) {
+              const int jj = i * kHi + hh;
+              s = fmaf(wi[jj], relu_raw(acc[jj]), s);
+            }
+            if constexpr (decltype(masked)::value) {
+              if (p <= pos[i]) best[i][t] = max_raw(best[i][t], s);
+            } else {
+              best[i][t] = max_raw(best[i][t], s);
+            }
           }
         }
       }
@@ -327,18 +335,21 @@ __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
     else score_tokens(std::false_type{});
 #pragma unroll
     for (int i = 0; i < kRowsPerLane; ++i) {
-      float v = best[i];
-      v = row_max_to_first(v);   // the block maximum, in lane n == 0
-      if (n == 0 && rowslot[i] < nr) {
-        float* dst = a.scores + static_cast<int64_t>(r0 + rowslot[i]) * a.max_blocks + b;
-        // write-through only when this launch's last workgroup selects from the scores;
-        // a later kernel sees plain stores after the kernel boundary
-        if (kFused && a.counters != nullptr) __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        else *dst = v;
+#pragma unroll
+      for (int t = 0; t < kG; ++t) {
+        const float v = row_max_to_first(best[i][t]);   // the block maximum, in lane n == 0
+        if (n == 0 && rowslot[i] < nr) {
+          float* dst = a.scores + (static_cast<int64_t>(r0 + rowslot[i]) * kG + t) * a.max_blocks + b;
+          // write-through only when this launch's last workgroup selects from the scores;
+          // a later kernel sees plain stores after the kernel boundary
+          if (kFused && a.counters != nullptr) __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          else *dst = v;
+        }
       }
     }
   } else if (fill) {
-    if (lane < nr) a.scores[static_cast<int64_t>(r0 + lane) * a.max_blocks + b] = -INFINITY;
+    // the group's rows' tables are consecutive: (r0 + i) * kG + t = r0 * kG + lane
+    if (lane < nr * kG) a.scores[(static_cast<int64_t>(r0) * kG + lane) * a.max_blocks + b] = -INFINITY;
   }
 
   if constexpr (kFused) {
@@ -352,16 +363,21 @@ __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
     __syncthreads();
     if (!s_last) return;
     const int32_t* bt = a.block_table + static_cast<int64_t>(seq) * a.max_blocks;
-    for (int i = 0; i < nr; ++i) {
-      const int r = r0 + i;
+    for (int i = 0; i < nr * kG; ++i) {
+      const int r = r0 + i / kG;
+      const int64_t tr = static_cast<int64_t>(r0) * kG + i;      // table row (r, i % kG)
       const int nb = min(a.row_pos[r] / kPage + 1, a.max_blocks);
-      block_select_row<true>(a.scores + static_cast<int64_t>(r) * a.max_blocks, nb, a.k, a.n_init,
-                             a.n_local, bt, a.sel + static_cast<int64_t>(r) * a.k,
-                             a.sel_pages ? a.sel_pages + static_cast<int64_t>(r) * a.k : nullptr,
+      block_select_row<true>(a.scores + tr * a.max_blocks, nb, a.k, a.n_init, a.n_local, bt,
+                             a.sel + tr * a.k, a.sel_pages ? a.sel_pages + tr * a.k : nullptr,
                              sel_keys, sm);
     }
     if (threadIdx.x == 0) a.counters[r0] = 0;
   }
+}
+
+// Per-KV-head score tables: one per KV head, each over an equal share of the index heads.
+bool tables_ok(const msa_kv_pool_t* pool, int tables, int n_idx_heads) {
+  return tables == 1 || (tables == pool->num_kv_heads && n_idx_heads % tables == 0);
 }
 
 ScoreArgs make_score_args(const msa_kv_pool_t* pool, const msa_step_t* step, const void* q_idx,
@@ -383,27 +399,34 @@ ScoreArgs make_score_args(const msa_kv_pool_t* pool, const msa_step_t* step, con
   return a;
 }
 
-template <bool kFused, bool kIdxNv>
-void launch_score_idx(const ScoreArgs& a, int fmt, int hi, dim3 grid, size_t lds, hipStream_t s) {
+template <int kFmt, bool kFused, bool kIdxNv>
+void launch_score_fmt(const ScoreArgs& a, int hi, int tables, dim3 grid, size_t lds, hipStream_t s) {
   const dim3 block(64 * kWaves);
-#define MSA_SCORE_LAUNCH(HI, FMT) score_kernel<HI, FMT, kFused, kIdxNv><<<grid, block, lds, s>>>(a)
-  if (fmt == MSA_KV_NVFP4) {
-    if (hi == 1) MSA_SCORE_LAUNCH(1, MSA_KV_NVFP4);
-    else if (hi == 2) MSA_SCORE_LAUNCH(2, MSA_KV_NVFP4);
-    else MSA_SCORE_LAUNCH(4, MSA_KV_NVFP4);
+#define MSA_SCORE_LAUNCH(HI, G) score_kernel<HI, G, kFmt, kFused, kIdxNv><<<grid, block, lds, s>>>(a)
+  if (hi == 1) MSA_SCORE_LAUNCH(1, 1);
+  else if (hi == 2) {
+    if (tables == 1) MSA_SCORE_LAUNCH(2, 1);
+    else MSA_SCORE_LAUNCH(2, 2);
   } else {
-    if (hi == 1) MSA_SCORE_LAUNCH(1, MSA_KV_FP8_E4M3);
-    else if (hi == 2) MSA_SCORE_LAUNCH(2, MSA_KV_FP8_E4M3);
-    else MSA_SCORE_LAUNCH(4, MSA_KV_FP8_E4M3);
+    if (tables == 1) MSA_SCORE_LAUNCH(4, 1);
+    else if (tables == 2) MSA_SCORE_LAUNCH(4, 2);
+    else MSA_SCORE_LAUNCH(4, 4);
   }
 #undef MSA_SCORE_LAUNCH
 }
 
+// hi in {1, 2, 4} and tables dividing hi are checked by the caller.
 template <bool kFused>
-msa_status_t launch_score(const ScoreArgs& a, const msa_kv_pool_t* pool, int hi, dim3 grid, size_t lds,
-                          hipStream_t s) {
-  if (index_nvfp4(pool)) launch_score_idx<kFused, true>(a, pool->fmt, hi, grid, lds, s);
-  else launch_score_idx<kFused, false>(a, pool->fmt, hi, grid, lds, s);
+msa_status_t launch_score(const ScoreArgs& a, const msa_kv_pool_t* pool, int hi, int tables, dim3 grid,
+                          size_t lds, hipStream_t s) {
+  const bool nv = index_nvfp4(pool);
+  if (pool->fmt == MSA_KV_NVFP4) {
+    if (nv) launch_score_fmt<MSA_KV_NVFP4, kFused, true>(a, hi, tables, grid, lds, s);
+    else launch_score_fmt<MSA_KV_NVFP4, kFused, false>(a, hi, tables, grid, lds, s);
+  } else {
+    if (nv) launch_score_fmt<MSA_KV_FP8_E4M3, kFused, true>(a, hi, tables, grid, lds, s);
+    else launch_score_fmt<MSA_KV_FP8_E4M3, kFused, false>(a, hi, tables, grid, lds, s);
+  }
   return launch_status();
 }
 
@@ -418,13 +441,15 @@ extern "C" msa_status_t msa_index_score(const msa_kv_pool_t* pool, const msa_ste
   if (st != MSA_OK) return st;
   if ((st = check_step(step)) != MSA_OK) return st;
   if (n_idx_heads != 1 && n_idx_heads != 2 && n_idx_heads != 4) return MSA_ERR_UNSUPPORTED;
+  const int tables = sel_tables(step);
+  if (!tables_ok(pool, tables, n_idx_heads)) return MSA_ERR_UNSUPPORTED;
   if (step->num_rows == 0) return MSA_OK;
   if (q_idx == nullptr || w == nullptr || block_scores == nullptr || !aligned16(q_idx))
     return MSA_ERR_INVALID_ARG;
   if (step->num_rows > 65535) return MSA_ERR_UNSUPPORTED;
   const ScoreArgs a = make_score_args(pool, step, q_idx, w, block_scores);
   dim3 grid(a.score_wgs_x, step->num_rows);
-  return launch_score<false>(a, pool, n_idx_heads, grid, 0, static_cast<hipStream_t>(stream));
+  return launch_score<false>(a, pool, n_idx_heads, tables, grid, 0, static_cast<hipStream_t>(stream));
 }
 
 extern "C" msa_status_t msa_append_score_select(
@@ -437,6 +462,8 @@ extern "C" msa_status_t msa_append_score_select(
   if (st != MSA_OK) return st;
   if ((st = check_step(step)) != MSA_OK) return st;
   if (n_idx_heads != 1 && n_idx_heads != 2 && n_idx_heads != 4) return MSA_ERR_UNSUPPORTED;
+  const int tables = sel_tables(step);
+  if (!tables_ok(pool, tables, n_idx_heads)) return MSA_ERR_UNSUPPORTED;
   if (k < 1 || k > MSA_MAX_TOPK || n_init < 0 || n_local < 0 || n_init + n_local > k)
     return MSA_ERR_UNSUPPORTED;
   if (n_new < 0) return MSA_ERR_INVALID_ARG;
@@ -463,5 +490,5 @@ extern "C" msa_status_t msa_append_score_select(
   a.append_row = n_new > 0 ? 1 : 0;
   dim3 grid(static_cast<unsigned>(std::max<int64_t>(a.score_wgs_x, app_wgs)), step->num_rows + a.append_row);
   const size_t lds = sel ? static_cast<size_t>(step->max_blocks_per_seq) * sizeof(uint32_t) : 0;
-  return launch_score<true>(a, pool, n_idx_heads, grid, lds, static_cast<hipStream_t>(stream));
+  return launch_score<true>(a, pool, n_idx_heads, tables, grid, lds, static_cast<hipStream_t>(stream));
 }

@@ -40,11 +40,16 @@ inline msa_status_t check_step(const msa_step_t* step) {
   if (step->num_seqs < 0 || step->num_rows < 0 || step->max_blocks_per_seq <= 0)
     return MSA_ERR_INVALID_ARG;
   if (step->max_blocks_per_seq > MSA_MAX_BLOCKS) return MSA_ERR_UNSUPPORTED;
+  if (step->sel_tables < 0) return MSA_ERR_INVALID_ARG;
+  if (step->sel_tables > MSA_MAX_SEL_TABLES) return MSA_ERR_UNSUPPORTED;
   if (step->num_rows > 0 && (step->num_seqs == 0 || step->block_table == nullptr ||
                              step->row_seq == nullptr || step->row_pos == nullptr))
     return MSA_ERR_INVALID_ARG;
   return MSA_OK;
 }
+
+// Selection tables per query row: 1 (0 in the struct) or one per KV head.
+inline int sel_tables(const msa_step_t* step) { return step->sel_tables > 1 ? step->sel_tables : 1; }
 
 // Multiplier for the device-side guess of a row's request, r * num_seqs / num_rows,
 // as (r * mul) >> 32 with mul = ceil(2^32 * num_seqs / num_rows). For r < num_rows <=

@@ -70,6 +70,7 @@ struct DecodeArgs {
   int num_rows;
   uint64_t seq_mul;           // seq_guess multiplier
   const uint16_t* q;
+  int sel_tables;             // 1: one table per row; hkv: one per (row, KV head)
   const int32_t* sel;         // selection table (table variants)
   const int32_t* sel_pages;   // may be null: translate through the block table
   int32_t* sel_out;           // selecting variant: optional copy of the selection
@@ -327,9 +328,11 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
   }
 
   // Selection table in a register: lane e < k holds entry e (block) and its page.
+  // With per-KV-head tables, KV head g reads table g of the row.
+  const int64_t trow = static_cast<int64_t>(r) * a.sel_tables + (a.sel_tables > 1 ? g : 0);
   int selv = -1, pagev = -1;
   if constexpr (kSelect) {
-    const float* srow = a.scores + static_cast<int64_t>(r) * a.max_blocks;
+    const float* srow = a.scores + trow * a.max_blocks;
     if (a.max_blocks - a.n_init - a.n_local <= kWaveSelectMax) {
       // Wave 0 selects (the other waves would only contend for the scalar unit) and
       // hands the table over through LDS. Its block-table reads go out with the score
@@ -365,9 +368,9 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
     }
     q_from_lds();
     if (lane >= a.k) selv = pagev = -1;
-    if (s == 0 && g == 0 && wave == 0 && a.sel_out != nullptr && lane < a.k) {
-      a.sel_out[static_cast<int64_t>(r) * a.k + lane] = selv;
-      if (a.sel_pages_out) a.sel_pages_out[static_cast<int64_t>(r) * a.k + lane] = pagev;
+    if (s == 0 && (g == 0 || a.sel_tables > 1) && wave == 0 && a.sel_out != nullptr && lane < a.k) {
+      a.sel_out[trow * a.k + lane] = selv;
+      if (a.sel_pages_out) a.sel_pages_out[trow * a.k + lane] = pagev;
     }
   }
   auto lookup = [&](int e, int& b, int64_t& page) {
@@ -375,9 +378,9 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
       b = __builtin_amdgcn_readlane(selv, e);   // e is the same in every lane
       page = __builtin_amdgcn_readlane(pagev, e);
     } else {
-      b = a.sel[static_cast<int64_t>(r) * a.k + e];
+      b = a.sel[trow * a.k + e];
       page = b < 0 ? 0
-          : a.sel_pages ? a.sel_pages[static_cast<int64_t>(r) * a.k + e]
+          : a.sel_pages ? a.sel_pages[trow * a.k + e]
                         : a.block_table[static_cast<int64_t>(a.row_seq[r]) * a.max_blocks + b];
     }
   };
@@ -661,6 +664,8 @@ msa_status_t decode_entry(const msa_kv_pool_t* pool, const msa_step_t* step, int
   if (combine && a.num_splits > kMaxMergeSplits) return MSA_ERR_UNSUPPORTED;
   if (select && (a.n_init < 0 || a.n_local < 0 || a.n_init + a.n_local > a.k)) return MSA_ERR_UNSUPPORTED;
   if (!(a.softmax_scale > 0.0f)) return MSA_ERR_INVALID_ARG;
+  a.sel_tables = sel_tables(step);
+  if (a.sel_tables != 1 && a.sel_tables != pool->num_kv_heads) return MSA_ERR_UNSUPPORTED;
   if (step->num_rows == 0) return MSA_OK;
   if (q == nullptr || a.part_o == nullptr || a.part_ml == nullptr) return MSA_ERR_INVALID_ARG;
   if (select ? a.scores == nullptr : a.sel == nullptr) return MSA_ERR_INVALID_ARG;

@@ -28,13 +28,16 @@ class DecodeBuffers:
     """Per-step outputs and the split-KV workspaces for a fixed geometry: part_o /
     part_ml receive the partials of the separate msa_sparse_decode call; merge_o /
     merge_ml (two exchange buffers) and counters (one state word per row and KV head)
-    are the fused entries' merge workspace, set up here for num_splits."""
+    are the fused entries' merge workspace, set up here for num_splits. With
+    sel_tables > 1 (one selection per KV head) block_scores, sel and sel_pages have a
+    table axis after the row."""
 
-    def __init__(self, num_rows, num_q_heads, max_blocks, k, num_splits, device="cuda"):
+    def __init__(self, num_rows, num_q_heads, max_blocks, k, num_splits, device="cuda", sel_tables=1):
         self.k, self.num_splits = k, num_splits
-        self.block_scores = torch.empty((num_rows, max_blocks), dtype=torch.float32, device=device)
-        self.sel = torch.empty((num_rows, k), dtype=torch.int32, device=device)
-        self.sel_pages = torch.empty((num_rows, k), dtype=torch.int32, device=device)
+        t = (sel_tables,) if sel_tables > 1 else ()
+        self.block_scores = torch.empty((num_rows, *t, max_blocks), dtype=torch.float32, device=device)
+        self.sel = torch.empty((num_rows, *t, k), dtype=torch.int32, device=device)
+        self.sel_pages = torch.empty((num_rows, *t, k), dtype=torch.int32, device=device)
         self.part_o = torch.empty((num_rows, num_q_heads, num_splits, L.HEAD_DIM),
                                   dtype=torch.float32, device=device)
         self.part_ml = torch.empty((num_rows, num_q_heads, num_splits, 2), dtype=torch.float32,

@@ -39,8 +39,8 @@ def gpu_pool(M, wl: W.Workload):
     return pool
 
 
-def gpu_step_inputs(M, wl: W.Workload):
-    step = M.Step(wl.block_table, wl.row_seq, wl.row_pos)
+def gpu_step_inputs(M, wl: W.Workload, tables=1):
+    step = M.Step(wl.block_table, wl.row_seq, wl.row_pos, sel_tables=tables)
     q = dev_bf16(wl.q)
     q_idx = dev_bf16(wl.q_idx)
     w = torch.from_numpy(wl.w).cuda()
@@ -51,9 +51,9 @@ def gpu_step_inputs(M, wl: W.Workload):
     return step, q, q_idx, w, app
 
 
-def run_gpu_step(M, wl, pool, num_splits, fused=True):
-    step, q, q_idx, w, app = gpu_step_inputs(M, wl)
-    bufs = M.DecodeBuffers(wl.num_rows, wl.num_heads, wl.max_blocks, wl.k, num_splits)
+def run_gpu_step(M, wl, pool, num_splits, fused=True, tables=1):
+    step, q, q_idx, w, app = gpu_step_inputs(M, wl, tables)
+    bufs = M.DecodeBuffers(wl.num_rows, wl.num_heads, wl.max_blocks, wl.k, num_splits, sel_tables=tables)
     kw = {}
     if app is not None:
         kw = dict(slot=app[0], k_new=app[1], v_new=app[2], idx_k_new=app[3])
@@ -174,26 +174,32 @@ def assert_merge_ready(bufs):
             assert (mm[r, g, e] == M.MERGE_IDLE_BITS).all(), (r, g)
 
 
-def check_step_parity(M, wl: W.Workload, num_splits: int, fused: bool):
+def check_step_parity(M, wl: W.Workload, num_splits: int, fused: bool, tables: int = 1):
     """Run one whole step on the GPU and compare scores, selection, outputs and the
-    split partials with the oracle, computed from the same seeded source."""
+    split partials with the oracle, computed from the same seeded source. tables > 1:
+    one selection per (row, KV head)."""
     pool = gpu_pool(M, wl)
-    bufs = run_gpu_step(M, wl, pool, num_splits, fused=fused)
+    bufs = run_gpu_step(M, wl, pool, num_splits, fused=fused, tables=tables)
     ref_pool = oracle_pool(wl)
-    S_ref = O.index_score(ref_pool, wl.block_table, wl.row_seq, wl.row_pos, wl.q_idx, wl.w, wl.max_blocks)
+    S_ref = O.index_score(ref_pool, wl.block_table, wl.row_seq, wl.row_pos, wl.q_idx, wl.w, wl.max_blocks,
+                          tables)
     sel_ref = O.select_topk(S_ref, wl.row_pos, wl.k, wl.n_init, wl.n_local)
     out_ref = O.attend(ref_pool, wl.block_table, wl.row_seq, wl.row_pos, wl.q, sel_ref, wl.softmax_scale)
-    S = bufs.block_scores.cpu().numpy()
-    assert_scores_close(S, S_ref)
-    sel = bufs.sel.cpu().numpy()
-    nb = wl.row_pos // 128 + 1
-    same = np.ones(wl.num_rows, bool)
-    for r in range(wl.num_rows):
-        if gap_qualified(S_ref[r], nb[r], wl.k, wl.n_init, wl.n_local):
-            assert np.array_equal(sel[r], sel_ref[r]), r
+    # per-(row, table) views: table rows r * T + t
+    S = bufs.block_scores.cpu().numpy().reshape(wl.num_rows * tables, -1)
+    S_flat = S_ref.reshape(wl.num_rows * tables, -1)
+    assert_scores_close(S, S_flat)
+    sel = bufs.sel.cpu().numpy().reshape(wl.num_rows * tables, -1)
+    sel_flat = sel_ref.reshape(wl.num_rows * tables, -1)
+    nb = np.repeat(wl.row_pos // 128 + 1, tables)
+    same_t = np.ones(wl.num_rows * tables, bool)
+    for r in range(wl.num_rows * tables):
+        if gap_qualified(S_flat[r], nb[r], wl.k, wl.n_init, wl.n_local):
+            assert np.array_equal(sel[r], sel_flat[r]), r
         else:
-            check_selection_valid(sel[r], S_ref[r], nb[r], wl.k, wl.n_init, wl.n_local)
-            same[r] = np.array_equal(sel[r], sel_ref[r])
+            check_selection_valid(sel[r], S_flat[r], nb[r], wl.k, wl.n_init, wl.n_local)
+            same_t[r] = np.array_equal(sel[r], sel_flat[r])
+    same = same_t.reshape(wl.num_rows, tables).all(axis=1)
     out = bf16_to_np(bufs.out)
     assert_out_close(out[same], out_ref[same], "outputs")
     if fused:   # the partials passed through the merge workspace, ready for the next call

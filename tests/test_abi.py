@@ -89,9 +89,9 @@ def _fake_pool(fmt=2, head_dim=128, k_t=1.0, index_fmt=0, index_scales=None, ind
                        index_scales, index_t)
 
 
-def _fake_step(rows=0, max_blocks=8):
+def _fake_step(rows=0, max_blocks=8, tables=0):
     a = 1 << 20
-    return L.MsaStep(1, rows, max_blocks, a, a, a)
+    return L.MsaStep(1, rows, max_blocks, a, a, a, tables)
 
 
 def test_validation_rejects_before_launch():
@@ -167,13 +167,40 @@ def test_validation_rejects_before_launch():
     assert L.LIB.msa_kv_append(B(_fake_pool(index_fmt=2, index_scales=a16 + 4, index_t=0.5)), 0, None,
                                None, None, None, None) == -1
     assert L.LIB.msa_kv_append(B(_fake_pool(index_fmt=5)), 0, None, None, None, None, None) == -2
-    nullstep = L.MsaStep(1, 1, 8, None, None, None)
+    nullstep = L.MsaStep(1, 1, 8, None, None, None, 0)
     assert L.LIB.msa_index_score(B(pool), B(nullstep), 4, P(16), P(16), P(16), None) == -1
     # rows need at least one request
-    noseq = L.MsaStep(0, 1, 8, P(16), P(16), P(16))
+    noseq = L.MsaStep(0, 1, 8, P(16), P(16), P(16), 0)
     assert L.LIB.msa_index_score(B(pool), B(noseq), 4, P(16), P(16), P(16), None) == -1
     assert L.LIB.msa_select_topk(B(noseq), P(16), 4, 0, 1, P(16), None, None) == -1
     assert L.LIB.msa_sparse_decode(B(pool), B(noseq), 32, P(16), P(16), None, 8, 0.1, 2, P(16), P(16), None) == -1
+
+
+def test_selection_table_count_is_validated():
+    """One table per row (0 or 1) or one per KV head (the fake pool has 2 KV heads);
+    the scorer also needs the index heads to split evenly into the tables."""
+    B, P = ctypes.byref, ctypes.c_void_p
+    pool = _fake_pool()
+    for T in (0, 1, 2):
+        st = _fake_step(tables=T)
+        assert L.LIB.msa_index_score(B(pool), B(st), 4, P(16), P(16), P(16), None) == 0
+        assert L.LIB.msa_index_score(B(pool), B(st), 2, P(16), P(16), P(16), None) == 0
+        assert L.LIB.msa_select_topk(B(st), P(16), 8, 0, 1, P(16), None, None) == 0
+        assert L.LIB.msa_sparse_decode(B(pool), B(st), 32, P(16), P(16), None, 8, 0.1, 2, P(16), P(16),
+                                       None) == 0
+        assert L.LIB.msa_append_score_select(B(pool), B(st), 0, None, None, None, None, 4, P(16), P(16),
+                                             8, 0, 1, P(16), P(16), None, P(16), None) == 0
+    t2 = _fake_step(tables=2)
+    assert L.LIB.msa_index_score(B(pool), B(t2), 1, P(16), P(16), P(16), None) == -2   # 1 head, 2 tables
+    t4 = _fake_step(tables=4)                        # 4 tables, 2 KV heads
+    assert L.LIB.msa_index_score(B(pool), B(t4), 4, P(16), P(16), P(16), None) == -2
+    assert L.LIB.msa_sparse_decode(B(pool), B(t4), 32, P(16), P(16), None, 8, 0.1, 2, P(16), P(16), None) == -2
+    assert L.LIB.msa_select_decode_combine(B(pool), B(t4), 32, P(16), P(16), 8, 0, 1, 0.1, 2, P(16), P(16),
+                                           P(16), P(16), None, None, None) == -2
+    assert L.LIB.msa_append_score_select(B(pool), B(t4), 0, None, None, None, None, 4, P(16), P(16),
+                                         8, 0, 1, P(16), P(16), None, P(16), None) == -2
+    assert L.LIB.msa_select_topk(B(_fake_step(tables=5)), P(16), 8, 0, 1, P(16), None, None) == -2
+    assert L.LIB.msa_select_topk(B(_fake_step(tables=-1)), P(16), 8, 0, 1, P(16), None, None) == -1
 
 
 def test_binding_rejects_host_tensors():
