@@ -57,6 +57,9 @@ def parse():
                     help="workload (1, the default, is the one the metric is quoted on)")
     ap.add_argument("--index-fmt", choices=["e4m3", "nvfp4"], default="e4m3",
                     help="index-key format (the workload specifies e4m3; nvfp4 is the option)")
+    ap.add_argument("--select-in", choices=["decode", "score"], default="decode",
+                    help="fused step: select inside the decode launch (default) or at the end of "
+                         "the scoring launch")
     ap.add_argument("--per-kv-head", action="store_true",
                     help="one selection per (row, KV head), each from its share of the index heads")
     ap.add_argument("--separate", action="store_true",
@@ -175,10 +178,12 @@ def main():
     bufs = M.DecodeBuffers(wl.num_rows, wl.num_heads, wl.max_blocks, wl.k, ns, sel_tables=tables)
     print(f"[bench] {args.replicas} pool replicas ready, splits {ns}", file=sys.stderr, flush=True)
 
+    select_in = args.select_in
+
     def one_step(p, stream=None):
         M.run_step(p, step, bufs, q, q_idx, w, wl.softmax_scale, slot=slot, k_new=k_new,
                    v_new=v_new, idx_k_new=idx_new, n_init=wl.n_init, n_local=wl.n_local,
-                   fused=not args.separate, stream=stream)
+                   fused=not args.separate, stream=stream, select_in=select_in)
 
     # ---- capture: one graph per replica and one graph of all replicas
     side = torch.cuda.Stream()
@@ -232,7 +237,7 @@ def main():
             lambda p: M.msa_combine(wl.num_rows, wl.num_heads, 128, ns, bufs.part_o, bufs.part_ml, bufs.out),
         ]
         decode_kernels = ["msa_sparse_decode", "msa_combine"]
-    else:
+    elif select_in == "decode":
         names = ["msa_append_score_select", "msa_select_decode_combine"]
         calls = [
             lambda p: M.msa_append_score_select(p, step, q_idx, w, wl.k, wl.n_init, wl.n_local,
@@ -244,6 +249,18 @@ def main():
                                                   sel=bufs.sel, sel_pages=bufs.sel_pages),
         ]
         decode_kernels = ["msa_select_decode_combine"]
+    else:
+        names = ["msa_append_score_select", "msa_sparse_decode_combine"]
+        calls = [
+            lambda p: M.msa_append_score_select(p, step, q_idx, w, wl.k, wl.n_init, wl.n_local,
+                                                bufs.block_scores, sel=bufs.sel, sel_pages=bufs.sel_pages,
+                                                counters=bufs.score_counters, slot=slot, k_new=k_new,
+                                                v_new=v_new, idx_k_new=idx_new),
+            lambda p: M.msa_sparse_decode_combine(p, step, q, bufs.sel, wl.k, wl.softmax_scale, ns,
+                                                  bufs.merge_o, bufs.merge_ml, bufs.counters, bufs.out,
+                                                  sel_pages=bufs.sel_pages),
+        ]
+        decode_kernels = ["msa_sparse_decode_combine"]
     # One graph per kernel that launches it once on every pool replica (inputs as the step
     # leaves them); events around replays of it give the mean launch duration, the
     # dispatch gap between back-to-back launches included.
@@ -303,7 +320,7 @@ def main():
     else:
         # Back-to-back launches of the scorer alone leave gaps between them that the
         # step does not have; within the step it takes what the decode leaves of it.
-        t_idx = ms_per_step * 1e-3 - per_kernel_us["msa_select_decode_combine"]["mean"] * 1e-6
+        t_idx = ms_per_step * 1e-3 - per_kernel_us[decode_kernels[0]]["mean"] * 1e-6
         idx_method = "step time minus the decode kernel's mean"
     achieved = dec_bytes / t_dec / 1e9
 
@@ -313,7 +330,8 @@ def main():
         with open(prof) as fh:
             pc = json.load(fh)
         if (pc.get("source_digest") == kernel_source_digest() and pc.get("num_splits") == ns
-                and tables == 1 and args.config == WORKLOAD_CFG and args.index_fmt == "e4m3"):
+                and tables == 1 and args.config == WORKLOAD_CFG and args.index_fmt == "e4m3"
+                and not args.separate and select_in == "decode"):
             traffic = pc.get("hbm_bytes_per_launch")
 
     box_read = None if args.no_read_probe else stream_read_gbs(torch, dev)
@@ -352,6 +370,7 @@ def main():
                    f"{int(wl.ctx_lens.min())}..{int(wl.ctx_lens.max())} (mean {float(wl.ctx_lens.mean()):.0f})",
                    "appended_tokens": wl.n_append, "top_k": wl.k, "kv_format": "nvfp4" if wl.fmt == W.FMT_NVFP4 else "fp8",
                    "num_splits": ns, "selection": "per KV head" if tables > 1 else "per query row",
+                   "select_in": "separate launch" if args.separate else select_in,
                    "pool_replicas": args.replicas, "parallelism": "single GPU"},
         "roofline": {"kernel": "+".join(decode_kernels), "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,

@@ -321,16 +321,23 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
     for (int j = 0; j < 4; ++j) Qop[j] = qlds[j][lane];
     cscale = qcs[lane];
   };
-  int pos;
-  if constexpr (!kSelect) {
-    pos = a.row_pos[r];
-    load_q();
-  }
-
   // Selection table in a register: lane e < k holds entry e (block) and its page.
   // With per-KV-head tables, KV head g reads table g of the row.
   const int64_t trow = static_cast<int64_t>(r) * a.sel_tables + (a.sel_tables > 1 ? g : 0);
   int selv = -1, pagev = -1;
+  int pos;
+  if constexpr (!kSelect) {
+    // the caller's table: one load per lane, issued before the query loads so that
+    // the page addresses wait for these alone (the counter retires in order)
+    if (lane < a.k) {
+      selv = a.sel[trow * a.k + lane];
+      if (a.sel_pages) pagev = a.sel_pages[trow * a.k + lane];
+    }
+    pos = a.row_pos[r];
+    load_q();
+    if (a.sel_pages == nullptr && selv >= 0)
+      pagev = a.block_table[static_cast<int64_t>(a.row_seq[r]) * a.max_blocks + selv];
+  }
   if constexpr (kSelect) {
     const float* srow = a.scores + trow * a.max_blocks;
     if (a.max_blocks - a.n_init - a.n_local <= kWaveSelectMax) {
@@ -374,15 +381,8 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
     }
   }
   auto lookup = [&](int e, int& b, int64_t& page) {
-    if constexpr (kSelect) {
-      b = __builtin_amdgcn_readlane(selv, e);   // e is the same in every lane
-      page = __builtin_amdgcn_readlane(pagev, e);
-    } else {
-      b = a.sel[trow * a.k + e];
-      page = b < 0 ? 0
-          : a.sel_pages ? a.sel_pages[trow * a.k + e]
-                        : a.block_table[static_cast<int64_t>(a.row_seq[r]) * a.max_blocks + b];
-    }
+    b = __builtin_amdgcn_readlane(selv, e);   // e is the same in every lane
+    page = __builtin_amdgcn_readlane(pagev, e);
   };
 
   Round<kFmt, kItems> rd;

@@ -54,18 +54,33 @@ class DecodeBuffers:
 
 
 def run_step(pool, step, bufs: DecodeBuffers, q, q_idx, w, softmax_scale, slot=None, k_new=None,
-             v_new=None, idx_k_new=None, n_init=0, n_local=1, fused=True, stream=None):
+             v_new=None, idx_k_new=None, n_init=0, n_local=1, fused=True, stream=None,
+             select_in="decode"):
     """One decode step on one stream: append -> index score -> select -> sparse decode
-    -> combine. fused=True issues two launches (append + score; select + decode +
-    combine); fused=False issues the five separate calls."""
+    -> combine. fused=True issues two launches: append + score, then select + decode +
+    combine (select_in="decode", the default: the selection is repeated by every decode
+    workgroup, which measured faster on every workload than one selection per row at the
+    end of the scoring launch), or append + score + select, then decode + combine
+    (select_in="score"). fused=False issues the five separate calls."""
     if fused:
-        L.msa_append_score_select(pool, step, q_idx, w, bufs.k, n_init, n_local, bufs.block_scores,
-                                  slot=slot, k_new=k_new, v_new=v_new, idx_k_new=idx_k_new,
-                                  stream=stream)
-        L.msa_select_decode_combine(pool, step, q, bufs.block_scores, bufs.k, n_init, n_local,
-                                    softmax_scale, bufs.num_splits, bufs.merge_o, bufs.merge_ml,
-                                    bufs.counters, bufs.out, sel=bufs.sel, sel_pages=bufs.sel_pages,
-                                    stream=stream)
+        if select_in == "decode":
+            L.msa_append_score_select(pool, step, q_idx, w, bufs.k, n_init, n_local, bufs.block_scores,
+                                      slot=slot, k_new=k_new, v_new=v_new, idx_k_new=idx_k_new,
+                                      stream=stream)
+            L.msa_select_decode_combine(pool, step, q, bufs.block_scores, bufs.k, n_init, n_local,
+                                        softmax_scale, bufs.num_splits, bufs.merge_o, bufs.merge_ml,
+                                        bufs.counters, bufs.out, sel=bufs.sel, sel_pages=bufs.sel_pages,
+                                        stream=stream)
+        elif select_in == "score":
+            L.msa_append_score_select(pool, step, q_idx, w, bufs.k, n_init, n_local, bufs.block_scores,
+                                      sel=bufs.sel, sel_pages=bufs.sel_pages, counters=bufs.score_counters,
+                                      slot=slot, k_new=k_new, v_new=v_new, idx_k_new=idx_k_new,
+                                      stream=stream)
+            L.msa_sparse_decode_combine(pool, step, q, bufs.sel, bufs.k, softmax_scale, bufs.num_splits,
+                                        bufs.merge_o, bufs.merge_ml, bufs.counters, bufs.out,
+                                        sel_pages=bufs.sel_pages, stream=stream)
+        else:
+            raise ValueError(f"select_in must be 'decode' or 'score', not {select_in!r}")
         return bufs.out
     if slot is not None and slot.numel() > 0:
         L.msa_kv_append(pool, slot, k_new, v_new, idx_k_new, stream)

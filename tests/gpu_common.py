@@ -51,14 +51,14 @@ def gpu_step_inputs(M, wl: W.Workload, tables=1):
     return step, q, q_idx, w, app
 
 
-def run_gpu_step(M, wl, pool, num_splits, fused=True, tables=1):
+def run_gpu_step(M, wl, pool, num_splits, fused=True, tables=1, select_in="decode"):
     step, q, q_idx, w, app = gpu_step_inputs(M, wl, tables)
     bufs = M.DecodeBuffers(wl.num_rows, wl.num_heads, wl.max_blocks, wl.k, num_splits, sel_tables=tables)
     kw = {}
     if app is not None:
         kw = dict(slot=app[0], k_new=app[1], v_new=app[2], idx_k_new=app[3])
     M.run_step(pool, step, bufs, q, q_idx, w, wl.softmax_scale, n_init=wl.n_init,
-               n_local=wl.n_local, fused=fused, **kw)
+               n_local=wl.n_local, fused=fused, select_in=select_in, **kw)
     torch.cuda.synchronize()
     return bufs
 
@@ -174,12 +174,13 @@ def assert_merge_ready(bufs):
             assert (mm[r, g, e] == M.MERGE_IDLE_BITS).all(), (r, g)
 
 
-def check_step_parity(M, wl: W.Workload, num_splits: int, fused: bool, tables: int = 1):
+def check_step_parity(M, wl: W.Workload, num_splits: int, fused: bool, tables: int = 1,
+                      select_in: str = "decode"):
     """Run one whole step on the GPU and compare scores, selection, outputs and the
     split partials with the oracle, computed from the same seeded source. tables > 1:
     one selection per (row, KV head)."""
     pool = gpu_pool(M, wl)
-    bufs = run_gpu_step(M, wl, pool, num_splits, fused=fused, tables=tables)
+    bufs = run_gpu_step(M, wl, pool, num_splits, fused=fused, tables=tables, select_in=select_in)
     ref_pool = oracle_pool(wl)
     S_ref = O.index_score(ref_pool, wl.block_table, wl.row_seq, wl.row_pos, wl.q_idx, wl.w, wl.max_blocks,
                           tables)

@@ -50,6 +50,16 @@ def test_full_step_parity(M, fmt, num_splits, fused):
     G.check_step_parity(M, wl, num_splits, fused)
 
 
+@pytest.mark.parametrize("fmt", [W.FMT_FP8, W.FMT_NVFP4])
+@pytest.mark.parametrize("num_splits", [1, 4])
+def test_full_step_parity_select_in_scoring_launch(M, fmt, num_splits):
+    """The fused step with the selection at the end of the scoring launch (one-wave
+    search per row) and the table-driven combining decode."""
+    wl = W.small(fmt, [1000, 2600, 130, 640], 3, num_kv_heads=2, k=5, seed=32)
+    _print("step parity, select in scoring launch", wl.name, "splits", num_splits)
+    G.check_step_parity(M, wl, num_splits, True, select_in="score")
+
+
 def test_num_splits_agree(M):
     wl = W.small(W.FMT_NVFP4, [3000, 2000], 1, num_kv_heads=1, k=16, seed=43)
     pool = G.gpu_pool(M, wl)

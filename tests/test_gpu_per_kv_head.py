@@ -82,3 +82,9 @@ def test_per_kv_head_select_bit_exact_on_fp32_scores(M):
         M.msa_select_topk(step, torch.from_numpy(S).cuda(), k, 0, 1, sel)
         ref = O.select_topk(S.astype(np.float64), pos, k)
         assert np.array_equal(sel.cpu().numpy(), ref)
+
+
+def test_per_kv_head_step_parity_select_in_scoring_launch(M):
+    wl = W.small(W.FMT_NVFP4, [1000, 2600, 130, 640], 3, num_kv_heads=4, k=5, seed=93)
+    _print("per-KV-head step, select in scoring launch", wl.name)
+    G.check_step_parity(M, wl, 2, True, tables=4, select_in="score")
