@@ -335,15 +335,19 @@ __device__ __forceinline__ void wave_select_table(const float* srow, const int32
 constexpr int kWaveSelectMax = 64 * 32;
 
 // Dispatch on the largest candidate count the row table allows (known before the row's
-// length is): kR = 4, 8, 16 or 32 keys per lane.
+// length is): kR = 4, 8, 16 or 32 keys per lane, up to kMaxR (a caller that never has
+// more than 64 kMaxR candidates leaves the wider searches, and their registers, out).
+template <int kMaxR = 32>
 __device__ __forceinline__ void wave_select(const float* srow, const int32_t* bt, int max_blocks,
                                             const int32_t* row_pos, int k, int n_init, int n_local,
                                             int* sel, int* pages) {
+  static_assert(kMaxR == 16 || kMaxR == 32, "16 or 32 keys per lane at most");
   const int C = max_blocks - n_init - n_local;
   if (C <= 256) wave_select_table<4>(srow, bt, max_blocks, row_pos, k, n_init, n_local, sel, pages);
   else if (C <= 512) wave_select_table<8>(srow, bt, max_blocks, row_pos, k, n_init, n_local, sel, pages);
-  else if (C <= 1024) wave_select_table<16>(srow, bt, max_blocks, row_pos, k, n_init, n_local, sel, pages);
-  else wave_select_table<32>(srow, bt, max_blocks, row_pos, k, n_init, n_local, sel, pages);
+  else if (kMaxR == 16 || C <= 1024)
+    wave_select_table<16>(srow, bt, max_blocks, row_pos, k, n_init, n_local, sel, pages);
+  else wave_select_table<kMaxR>(srow, bt, max_blocks, row_pos, k, n_init, n_local, sel, pages);
 }
 
 }  // namespace msa

@@ -237,7 +237,15 @@ __device__ __forceinline__ void merge_slots(__amdgpu_buffer_rsrc_t ro, __amdgpu_
   }
 }
 
-template <int kFmt, int kW, int kItems, bool kCombine, bool kSelect>
+// What a workgroup writes: its split's partial (kOutPartials), the bf16 output of the
+// only split (kOutDirect), or its partial through the merge workspace, the last split
+// of the (row, KV head) merging them all into the bf16 output (kOutMerged). The direct
+// variant holds none of the merge code, and so fewer registers. kSelect: 0 = the
+// caller's table; 16 or 32 = the workgroup selects, with the one-wave search for rows of
+// up to 64 x kSelect candidates (16 keeps its registers within four waves per SIMD).
+constexpr int kOutPartials = 0, kOutDirect = 1, kOutMerged = 2;
+
+template <int kFmt, int kW, int kItems, int kOut, int kSelect>
 __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
   // Dynamic LDS: the row's selection keys (selecting variant, before any V is staged),
   // then the per-wave V staging buffers and, at the end, the per-wave O tiles.
@@ -261,7 +269,7 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
   // two exchange buffers this launch uses, the split count the workspace was set up
   // for, arrivals so far), read once at the start. Its buffer and split-count fields
   // change only when this launch's merger finishes, after every split has arrived.
-  const bool merging = kCombine && a.num_splits > 1;
+  const bool merging = kOut == kOutMerged && a.num_splits > 1;
   uint32_t mstate = 0u;
   if (merging)   // (a per-lane address, so the word stays in a vector register and is
                  // not moved to a scalar one, which would wait for the load right here)
@@ -340,7 +348,7 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
   }
   if constexpr (kSelect) {
     const float* srow = a.scores + trow * a.max_blocks;
-    if (a.max_blocks - a.n_init - a.n_local <= kWaveSelectMax) {
+    if (a.max_blocks - a.n_init - a.n_local <= 64 * kSelect) {
       // Wave 0 selects (the other waves would only contend for the scalar unit) and
       // hands the table over through LDS. Its block-table reads go out with the score
       // reads, from the row of the request r belongs to when every request has the
@@ -352,7 +360,7 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
       const int seq = a.row_seq[r];
       if (wave == 0) {
         const int32_t* btg = a.block_table + static_cast<int64_t>(guess) * a.max_blocks;
-        wave_select(srow, btg, a.max_blocks, a.row_pos + r, a.k, a.n_init, a.n_local, lsel, lpage);
+        wave_select<kSelect>(srow, btg, a.max_blocks, a.row_pos + r, a.k, a.n_init, a.n_local, lsel, lpage);
       }
       if (wave == 1) q_to_lds();
       __syncthreads();
@@ -533,7 +541,7 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
       }
     }
   };
-  if constexpr (!kCombine) {
+  if constexpr (kOut == kOutPartials) {
 #pragma unroll
     for (int it = 0; it < kPer; ++it) {
       const int idx = threadIdx.x + it * 64 * kW;
@@ -550,7 +558,7 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
         pm[1] = l;
       }
     }
-  } else if (a.num_splits == 1) {
+  } else if constexpr (kOut == kOutDirect) {
     // the only split: its merge is the output (merge weight exp2(0) = 1)
 #pragma unroll
     for (int it = 0; it < kPer; ++it) {
@@ -633,24 +641,32 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
   }
 }
 
-template <int kFmt, int kW, int kItems, bool kCombine, bool kSelect>
+template <int kFmt, int kW, int kItems, int kOut, int kSelect>
 void launch(const DecodeArgs& a, dim3 grid, hipStream_t s) {
   size_t lds = static_cast<size_t>(kW) * kVBufBytes;
   if (kSelect) lds = std::max(lds, static_cast<size_t>(a.max_blocks) * sizeof(uint32_t));
-  sparse_decode_kernel<kFmt, kW, kItems, kCombine, kSelect><<<grid, dim3(64 * kW), lds, s>>>(a);
+  sparse_decode_kernel<kFmt, kW, kItems, kOut, kSelect><<<grid, dim3(64 * kW), lds, s>>>(a);
 }
 
-// Waves per workgroup and chunks per wave (per round) for a split of `per_split` pages:
-// one chunk per wave up to 16 waves; beyond that 8 waves of 4 chunks per round. The
-// selecting variant needs at least 4 waves (its selection uses 256 threads or more).
-template <int kFmt, bool kCombine, bool kSelect>
+// Waves per workgroup for a split of `per_split` pages, one chunk per wave and round:
+// up to 16 waves for one round. Longer splits take rounds: of 8 chunks, which keeps the
+// registers low enough for two workgroups per compute unit where the variant allows, or,
+// with one split and fewer workgroups than the 256 compute units, of 16 chunks (more
+// waves per compute unit; with several splits the merging variant would spill). Several
+// chunks per wave and round measured slower: fewer waves hide less of each chunk's
+// latency. The choice depends only on k, the split count and the launch size, so every
+// output variant of a call shape computes its partials in the same order (the merged
+// and direct outputs equal the partials + msa_combine bit for bit). The selecting
+// variant needs at least 4 waves (its selection uses 256 threads or more).
+template <int kFmt, int kOut, int kSelect>
 msa_status_t dispatch(const DecodeArgs& a, dim3 grid, hipStream_t s) {
   const int per_split = (a.k + a.num_splits - 1) / a.num_splits;
   const int chunks = 4 * per_split;
-  if (chunks <= 4) launch<kFmt, 4, 1, kCombine, kSelect>(a, grid, s);
-  else if (chunks <= 8) launch<kFmt, 8, 1, kCombine, kSelect>(a, grid, s);
-  else if (chunks <= 16) launch<kFmt, 16, 1, kCombine, kSelect>(a, grid, s);
-  else launch<kFmt, 8, 4, kCombine, kSelect>(a, grid, s);   // rounds of 32 chunks
+  const bool rounds16 = a.num_splits == 1 && static_cast<int64_t>(grid.x) * grid.y < 256;
+  if (chunks <= 4) launch<kFmt, 4, 1, kOut, kSelect>(a, grid, s);
+  else if (chunks <= 8) launch<kFmt, 8, 1, kOut, kSelect>(a, grid, s);
+  else if (chunks <= 16 || rounds16) launch<kFmt, 16, 1, kOut, kSelect>(a, grid, s);
+  else launch<kFmt, 8, 1, kOut, kSelect>(a, grid, s);   // rounds of 8 chunks
   return launch_status();
 }
 
@@ -690,9 +706,17 @@ msa_status_t decode_entry(const msa_kv_pool_t* pool, const msa_step_t* step, int
   a.seq_mul = seq_guess_mul(step->num_seqs, step->num_rows);
   const int pairs = step->num_rows * pool->num_kv_heads;
   dim3 grid(a.num_splits, pairs);
-#define MSA_DECODE_DISPATCH(FMT)                                              \
-  (select ? dispatch<FMT, true, true>(a, grid, s)                             \
-          : combine ? dispatch<FMT, true, false>(a, grid, s) : dispatch<FMT, false, false>(a, grid, s))
+  // The one-split selecting variant runs many workgroups per compute unit where the
+  // rows allow its narrower search (registers for four waves per SIMD); the merging one
+  // has at most about one workgroup per compute unit and keeps the full search (its
+  // code measured faster that way).
+  const bool direct = a.num_splits == 1;
+  const bool wide = a.max_blocks - a.n_init - a.n_local > 64 * 16;   // more than 16 keys per lane
+#define MSA_DECODE_DISPATCH(FMT)                                                                      \
+  (select ? (direct ? (wide ? dispatch<FMT, kOutDirect, 32>(a, grid, s) : dispatch<FMT, kOutDirect, 16>(a, grid, s)) \
+                    : dispatch<FMT, kOutMerged, 32>(a, grid, s))                                      \
+   : combine ? (direct ? dispatch<FMT, kOutDirect, 0>(a, grid, s) : dispatch<FMT, kOutMerged, 0>(a, grid, s)) \
+             : dispatch<FMT, kOutPartials, 0>(a, grid, s))
   if (pool->fmt == MSA_KV_NVFP4) return MSA_DECODE_DISPATCH(MSA_KV_NVFP4);
   return MSA_DECODE_DISPATCH(MSA_KV_FP8_E4M3);
 #undef MSA_DECODE_DISPATCH

@@ -114,3 +114,30 @@ def test_calls_with_fewer_rows_share_the_workspace(M):
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), ref.out.view(torch.int16)), call
         G.assert_merge_ready(ws)
+
+
+@pytest.mark.parametrize("fmt", [W.FMT_FP8, W.FMT_NVFP4])
+@pytest.mark.parametrize("k,ctx", [(16, [3000, 9000]), (16, [2500 + 37 * i for i in range(70)]), (5, [3000, 9000])])
+def test_one_split_direct_output_equals_partials_and_combine(M, fmt, k, ctx):
+    """With one split the combining entries write the output themselves (no workspace);
+    it equals msa_sparse_decode + msa_combine bit for bit, in both wave layouts the
+    decode picks by launch size (4 or 280 workgroups, against 256 compute units)."""
+    wl = W.small(fmt, ctx, 2, num_kv_heads=2, k=k, seed=85)
+    print("one split", wl.name, "k", k, "rows", wl.num_rows, flush=True)
+    pool = G.gpu_pool(M, wl)
+    step, q, q_idx, w, app = G.gpu_step_inputs(M, wl)
+    scores = torch.empty((wl.num_rows, wl.max_blocks), dtype=torch.float32, device="cuda")
+    M.msa_append_score_select(pool, step, q_idx, w, wl.k, wl.n_init, wl.n_local, scores, slot=app[0],
+                              k_new=app[1], v_new=app[2], idx_k_new=app[3])
+    ref = _reference(M, wl, pool, step, q, scores, 1)
+    ws = M.DecodeBuffers(wl.num_rows, wl.num_heads, wl.max_blocks, wl.k, 1)
+    M.msa_select_decode_combine(pool, step, q, scores, wl.k, wl.n_init, wl.n_local, wl.softmax_scale, 1,
+                                ws.merge_o, ws.merge_ml, ws.counters, ws.out, sel=ws.sel, sel_pages=ws.sel_pages)
+    torch.cuda.synchronize()
+    assert torch.equal(ws.sel, ref.sel) and torch.equal(ws.sel_pages, ref.sel_pages)
+    assert torch.equal(ws.out.view(torch.int16), ref.out.view(torch.int16))
+    ws.out.fill_(0)
+    M.msa_sparse_decode_combine(pool, step, q, ref.sel, wl.k, wl.softmax_scale, 1, ws.merge_o, ws.merge_ml,
+                                ws.counters, ws.out, sel_pages=ref.sel_pages)
+    torch.cuda.synchronize()
+    assert torch.equal(ws.out.view(torch.int16), ref.out.view(torch.int16))
