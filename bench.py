@@ -144,7 +144,7 @@ def main():
     import torch
 
     import sparse_attention_decode_fp8_amd as M
-    from sparse_attention_decode_fp8_amd.pipeline import default_num_splits
+    from sparse_attention_decode_fp8_amd.pipeline import FUSED_APPEND_MAX, default_num_splits
     from synth import workloads as W
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -179,6 +179,8 @@ def main():
     print(f"[bench] {args.replicas} pool replicas ready, splits {ns}", file=sys.stderr, flush=True)
 
     select_in = args.select_in
+    # run_step appends in a launch of its own when a step has this many new tokens
+    app_sep = not args.separate and select_in == "decode" and len(sl) > FUSED_APPEND_MAX
 
     def one_step(p, stream=None):
         M.run_step(p, step, bufs, q, q_idx, w, wl.softmax_scale, slot=slot, k_new=k_new,
@@ -249,6 +251,10 @@ def main():
                                                   sel=bufs.sel, sel_pages=bufs.sel_pages),
         ]
         decode_kernels = ["msa_select_decode_combine"]
+        if app_sep:   # (as run_step does for this many new tokens)
+            names = ["msa_kv_append", "msa_index_score"] + names[1:]
+            calls = [lambda p: M.msa_kv_append(p, slot, k_new, v_new, idx_new),
+                     lambda p: M.msa_index_score(p, step, q_idx, w, bufs.block_scores)] + calls[1:]
     else:
         names = ["msa_append_score_select", "msa_sparse_decode_combine"]
         calls = [
@@ -314,7 +320,7 @@ def main():
         last[int(wl.row_seq[r])] = max(last.get(int(wl.row_seq[r]), -1), int(wl.row_pos[r]))
     idx_bytes = int(sum(p + 1 for p in last.values()) * key_bytes)
     t_dec = sum(per_kernel_us[k]["mean"] for k in decode_kernels) * 1e-6
-    if args.separate:
+    if args.separate or app_sep:
         t_idx = per_kernel_us["msa_index_score"]["mean"] * 1e-6
         idx_method = "events around replays of a graph of this kernel alone"
     else:
@@ -379,7 +385,7 @@ def main():
                      **({f"{q}_us": per_kernel_us[decode_kernels[0]][q] for q in ("p10", "p50", "p90")}
                         if len(decode_kernels) == 1 else {}),
                      "frac_of_box_read": None if box_read is None else achieved / box_read},
-        "index_score_roofline": {"kernel": names[0] if not args.separate else "msa_index_score",
+        "index_score_roofline": {"kernel": "msa_index_score" if args.separate or app_sep else names[0],
                                  "bound": "hbm", "achieved": idx_bytes / t_idx / 1e9,
                                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                  "frac": idx_bytes / t_idx / 1e9 / HBM_PEAK_GBS,

@@ -53,6 +53,11 @@ class DecodeBuffers:
         self.out = torch.empty((num_rows, num_q_heads, L.HEAD_DIM), dtype=torch.bfloat16, device=device)
 
 
+# New tokens per step up to which the append rides in the scoring launch: one slot per
+# lane of a scoring wave; beyond it each wave would loop over the slots.
+FUSED_APPEND_MAX = 64
+
+
 def run_step(pool, step, bufs: DecodeBuffers, q, q_idx, w, softmax_scale, slot=None, k_new=None,
              v_new=None, idx_k_new=None, n_init=0, n_local=1, fused=True, stream=None,
              select_in="decode"):
@@ -61,12 +66,20 @@ def run_step(pool, step, bufs: DecodeBuffers, q, q_idx, w, softmax_scale, slot=N
     combine (select_in="decode", the default: the selection is repeated by every decode
     workgroup, which measured faster on every workload than one selection per row at the
     end of the scoring launch), or append + score + select, then decode + combine
-    (select_in="score"). fused=False issues the five separate calls."""
+    (select_in="score"). With more than FUSED_APPEND_MAX new tokens the default path
+    appends in a launch of its own before scoring. fused=False issues the five separate
+    calls."""
     if fused:
         if select_in == "decode":
-            L.msa_append_score_select(pool, step, q_idx, w, bufs.k, n_init, n_local, bufs.block_scores,
-                                      slot=slot, k_new=k_new, v_new=v_new, idx_k_new=idx_k_new,
-                                      stream=stream)
+            if slot is not None and slot.numel() > FUSED_APPEND_MAX:
+                # many new tokens: every scoring wave would scan them all for its page,
+                # so the append runs first and the scorer without it
+                L.msa_kv_append(pool, slot, k_new, v_new, idx_k_new, stream)
+                L.msa_index_score(pool, step, q_idx, w, bufs.block_scores, stream)
+            else:
+                L.msa_append_score_select(pool, step, q_idx, w, bufs.k, n_init, n_local, bufs.block_scores,
+                                          slot=slot, k_new=k_new, v_new=v_new, idx_k_new=idx_k_new,
+                                          stream=stream)
             L.msa_select_decode_combine(pool, step, q, bufs.block_scores, bufs.k, n_init, n_local,
                                         softmax_scale, bufs.num_splits, bufs.merge_o, bufs.merge_ml,
                                         bufs.counters, bufs.out, sel=bufs.sel, sel_pages=bufs.sel_pages,
