@@ -341,6 +341,35 @@ msa_status_t msa_index_bytes(int32_t index_fmt, int32_t num_pages, int32_t index
 /* A static string naming the status. */
 const char* msa_status_string(msa_status_t status);
 
+/*
+ * Device-side metadata checks. The release library trusts the device arrays (page ids,
+ * requests, positions, selections). The debug library, libmsadecode_debug.so (the same
+ * sources built with -DMSA_DEBUG_CHECKS), checks them where the kernels use them: a
+ * failed check writes its code to the caller's error word if the word is still 0 (the
+ * first failure wins) and skips the access it guards (the affected scores, selections
+ * or outputs are then meaningless, but nothing is read or written out of bounds).
+ *   MSA_DEBUG_BAD_PAGE : a page id from the block table or sel_pages outside [0, num_pages)
+ *   MSA_DEBUG_BAD_SEQ  : a row_seq value outside [0, num_seqs)
+ *   MSA_DEBUG_BAD_POS  : a row_pos whose block lies past max_blocks_per_seq
+ *   MSA_DEBUG_BAD_SEL  : a selection entry neither -1 nor a visible block of its row
+ *   MSA_DEBUG_BAD_SLOT : an append slot whose page lies outside [0, num_pages)
+ * msa_debug_set_error_word sets the device int32 word (NULL: none) that every later
+ * call of the debug library, on any stream, reports to; the caller zeroes and reads
+ * it. It is process-wide state of the debug library only. The release library returns
+ * MSA_ERR_UNSUPPORTED, and msa_debug_checks_enabled tells the two apart (1 / 0).
+ */
+typedef enum {
+  MSA_DEBUG_OK = 0,
+  MSA_DEBUG_BAD_PAGE = 1,
+  MSA_DEBUG_BAD_SEQ = 2,
+  MSA_DEBUG_BAD_POS = 3,
+  MSA_DEBUG_BAD_SEL = 4,
+  MSA_DEBUG_BAD_SLOT = 5
+} msa_debug_error_t;
+
+msa_status_t msa_debug_set_error_word(int32_t* word);
+int32_t msa_debug_checks_enabled(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -14,7 +14,11 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmsadecode.so")
+RELEASE_LIB_PATH = os.path.join(_HERE, "libmsadecode.so")
+# The same library with device-side metadata checks (msa_debug_set_error_word);
+# MSA_DEBUG_CHECKS=1 in the environment selects it at import.
+DEBUG_LIB_PATH = os.path.join(_HERE, "libmsadecode_debug.so")
+LIB_PATH = DEBUG_LIB_PATH if os.environ.get("MSA_DEBUG_CHECKS", "0") not in ("", "0") else RELEASE_LIB_PATH
 
 FMT_FP8 = 1
 FMT_NVFP4 = 2
@@ -54,14 +58,16 @@ EXPORTS = ["msa_kv_append", "msa_index_score", "msa_select_topk", "msa_append_sc
            "msa_sparse_decode",
            "msa_sparse_decode_combine", "msa_select_decode_combine", "msa_combine",
            "msa_merge_workspace_init",
-           "msa_decode_workspace_bytes", "msa_pool_bytes", "msa_index_bytes", "msa_status_string"]
+           "msa_decode_workspace_bytes", "msa_pool_bytes", "msa_index_bytes", "msa_status_string",
+           "msa_debug_set_error_word", "msa_debug_checks_enabled"]
 
 
-def _load():
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with "
+def load_library(path: str):
+    """Load one build of the library (release or debug) with its C signatures set."""
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
                           "`python sparse_attention_decode_fp8_amd/build.py`")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     P, I32, F32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
     sig = {
         "msa_kv_append": (I32, [P, I32, P, P, P, P, P]),
@@ -77,6 +83,8 @@ def _load():
         "msa_pool_bytes": (I32, [I32, I32, I32, I32, I32, ctypes.POINTER(SZ)]),
         "msa_index_bytes": (I32, [I32, I32, I32, ctypes.POINTER(SZ)]),
         "msa_status_string": (ctypes.c_char_p, [I32]),
+        "msa_debug_set_error_word": (I32, [P]),
+        "msa_debug_checks_enabled": (I32, []),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -84,7 +92,31 @@ def _load():
     return lib
 
 
-LIB = _load()
+LIB = load_library(LIB_PATH)
+
+
+class use_library:
+    """Context manager: the wrappers of this module call `lib` (from load_library)
+    inside the block, e.g. the debug build in a test next to the release one."""
+
+    def __init__(self, lib):
+        self.lib = lib
+
+    def __enter__(self):
+        global LIB
+        self.prev, LIB = LIB, self.lib
+        return self.lib
+
+    def __exit__(self, *exc):
+        global LIB
+        LIB = self.prev
+        return False
+
+
+def msa_debug_set_error_word(word):
+    """Debug library: device int32 word (a 1-element tensor, or None) that failed
+    metadata checks report to. The release library raises MsaError."""
+    _check(LIB.msa_debug_set_error_word(_ptr(word, torch.int32, "word")), "msa_debug_set_error_word")
 
 
 def _check(status: int, what: str):

@@ -3,8 +3,9 @@
     python sparse_attention_decode_fp8_amd/build.py [--jobs N]
 
 Every HIP source is compiled to an object with `hipcc --offload-arch=gfx950`, then
-linked into sparse_attention_decode_fp8_amd/libmsadecode.so next to this file (and the
-bench's read-bandwidth reference into libmsaprobe.so).
+linked into sparse_attention_decode_fp8_amd/libmsadecode.so next to this file; the same
+sources built with -DMSA_DEBUG_CHECKS (device-side metadata checks) into
+libmsadecode_debug.so; and the bench's read-bandwidth reference into libmsaprobe.so.
 """
 from __future__ import annotations
 
@@ -20,6 +21,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmsadecode.so")
+# The same sources with the device-side metadata checks (MSA_DEBUG_CHECKS).
+DEBUG_LIB = os.path.join(PKG, "libmsadecode_debug.so")
 SOURCES = ["kv_append.hip", "index_score.hip", "select_topk.hip", "sparse_decode.hip",
            "combine.hip", "api.cpp"]
 # The bench's read-bandwidth reference, a library of its own (not part of the decode path).
@@ -46,9 +49,11 @@ def hipcc() -> str:
 EXTRA = {"sparse_decode.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON, *HIP_FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, debug: bool = False) -> str:
+    out = os.path.join(BUILD, "debug") if debug else BUILD
+    obj = os.path.join(out, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *COMMON, *HIP_FLAGS, *EXTRA.get(src, []), *(["-DMSA_DEBUG_CHECKS"] if debug else []),
+           "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -65,13 +70,16 @@ def _link(objs, lib: str) -> None:
 
 
 def build(jobs: int = 6, verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+    os.makedirs(os.path.join(BUILD, "debug"), exist_ok=True)
+    jobs_list = [(f, False) for f in SOURCES + PROBE_SOURCES] + [(f, True) for f in SOURCES]
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES + PROBE_SOURCES))
-    _link(objs[:len(SOURCES)], LIB)
-    _link(objs[len(SOURCES):], PROBE_LIB)
+        objs = list(ex.map(lambda fd: _compile(*fd), jobs_list))
+    n = len(SOURCES)
+    _link(objs[:n], LIB)
+    _link(objs[n:n + len(PROBE_SOURCES)], PROBE_LIB)
+    _link(objs[n + len(PROBE_SOURCES):], DEBUG_LIB)
     if verbose:
-        print(f"built {LIB} and {PROBE_LIB}")
+        print(f"built {LIB}, {DEBUG_LIB} and {PROBE_LIB}")
     return LIB
 
 

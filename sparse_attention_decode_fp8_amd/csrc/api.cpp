@@ -48,6 +48,30 @@ extern "C" msa_status_t msa_index_bytes(int32_t index_fmt, int32_t num_pages, in
   return MSA_OK;
 }
 
+namespace msa {
+// The error word of the debug library's device-side checks (see msa_debug_set_error_word).
+static int32_t* g_debug_error_word = nullptr;
+int32_t* debug_error_word() { return g_debug_error_word; }
+}  // namespace msa
+
+extern "C" msa_status_t msa_debug_set_error_word(int32_t* word) {
+#ifdef MSA_DEBUG_CHECKS
+  msa::g_debug_error_word = word;
+  return MSA_OK;
+#else
+  (void)word;
+  return MSA_ERR_UNSUPPORTED;
+#endif
+}
+
+extern "C" int32_t msa_debug_checks_enabled(void) {
+#ifdef MSA_DEBUG_CHECKS
+  return 1;
+#else
+  return 0;
+#endif
+}
+
 extern "C" const char* msa_status_string(msa_status_t status) {
   switch (status) {
     case MSA_OK: return "MSA_OK";

@@ -7,6 +7,7 @@
 #pragma once
 
 #include "msa_device.h"
+#include "msa_host.h"
 
 namespace msa {
 
@@ -24,6 +25,8 @@ struct AppendArgs {
   float k_t, v_t, idx_t;
   int index_nvfp4;
   int n_new, hkv;
+  int num_pages;
+  int32_t* err;        // debug library: the error word of failed metadata checks
   int kv_groups;       // groups of 16 per token for K (and for V): hkv * 8
   int groups_per_tok;  // K groups + V groups + index groups
 };
@@ -108,6 +111,7 @@ __device__ __forceinline__ void append_group(const AppendArgs& a, int64_t gid) {
   if (slot < 0) return;
   const int64_t page = slot / kPage;
   const int off = static_cast<int>(slot % kPage);
+  if (!dcheck(page < a.num_pages, MSA_DEBUG_BAD_SLOT, a.err)) return;
 
   if (grp >= 2 * a.kv_groups) {                    // index-K: E4M3, no scale, or NVFP4
     if (a.idx_new == nullptr) return;
@@ -174,6 +178,8 @@ inline AppendArgs make_append_args(const msa_kv_pool_t* pool, int32_t n_new, con
   a.idx_t = pool->index_tensor_scale;
   a.n_new = n_new;
   a.hkv = pool->num_kv_heads;
+  a.num_pages = pool->num_pages;
+  a.err = debug_error_word();
   a.kv_groups = pool->num_kv_heads * (MSA_HEAD_DIM / 16);
   a.groups_per_tok = 2 * a.kv_groups + MSA_INDEX_DIM / 16;
   return a;

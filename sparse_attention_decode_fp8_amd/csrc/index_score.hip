@@ -44,6 +44,8 @@ struct ScoreArgs {
   const float* w;
   float* scores;
   int num_rows, max_blocks;
+  int num_seqs, num_pages;
+  int32_t* err;       // debug library: the error word of failed metadata checks
   uint64_t seq_mul;   // seq_guess multiplier
   // fused launch only
   AppendArgs app;
@@ -123,21 +125,23 @@ __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
   int64_t slot0 = -1;
   if constexpr (kFused)
     if (a.app.idx_new != nullptr && lane < a.app.n_new) slot0 = a.app.slot[lane];
-  const int seq = __builtin_amdgcn_readlane(seq_l, 32);
-  const uint64_t same = __ballot(seq_l == seq);
+  const int seq_raw = __builtin_amdgcn_readlane(seq_l, 32);
+  const uint64_t same = __ballot(seq_l == seq_raw);
   // Is r0 the first row of a group? Count the earlier rows of the same request.
   const uint32_t before = ~static_cast<uint32_t>(same);            // lanes 0..31: a different request
   int j = before != 0 ? __builtin_clz(before) : 32;               // run of equal rows ending at r0-1
   if (j == 32)
-    while (r0 - j - 1 >= 0 && a.row_seq[r0 - j - 1] == seq) ++j;
+    while (r0 - j - 1 >= 0 && a.row_seq[r0 - j - 1] == seq_raw) ++j;
   if (j % kRowsPerGroup != 0) return;
   // rows r0 .. r0+nr-1 of the same request form the group
   const uint32_t after = ~static_cast<uint32_t>(same >> 32);       // bit i: row r0+i differs
   const int nr = min(kRowsPerGroup, __builtin_ctz(after | (1u << 16)));
   int max_pos = lane >= 32 && lane < 32 + nr ? pos_l : -1;
+  if (lane >= 32 && lane < 32 + nr && blockIdx.x == 0) check_pos(pos_l, a.max_blocks, a.err);
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) max_pos = max(max_pos, __shfl_xor(max_pos, m, 64));
   const int last_block = max_pos / kPage;
+  const int seq = checked_seq(seq_raw, a.num_seqs, a.err);
 
   const bool active = b < a.max_blocks && b <= last_block;   // this wave scores block b
   const bool fill = b < a.max_blocks && b > last_block;      // past every row: -inf only
@@ -175,7 +179,7 @@ __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
     // t, or (NVFP4) 8 code bytes and the group's scale byte per t. They are issued from the
     // guessed request's page (an unused entry reads page 0) and issued again from the
     // right page if the guess was wrong.
-    int64_t page = page_g >= 0 ? page_g : 0;
+    int64_t page = page_g;
     uint4 key[8];
     auto load_keys = [&]() {
       const int64_t tok0 = page * kPage + n;
@@ -201,6 +205,8 @@ __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
       }
     };
     if (seq != guess) page = a.block_table[static_cast<int64_t>(seq) * a.max_blocks + b];
+    page = checked_page(page, a.num_pages, a.err);
+    if (page < 0) page = 0;   // (an entry of -1 here is invalid input: read page 0, not before the pool)
     // New tokens landing in this page (fused launch): their keys are encoded here from
     // the bf16 source instead of waiting for the append. The first one's source is
     // read together with the page's keys and its code replaces the stale key as the
@@ -395,6 +401,9 @@ ScoreArgs make_score_args(const msa_kv_pool_t* pool, const msa_step_t* step, con
   a.num_rows = step->num_rows;
   a.seq_mul = seq_guess_mul(step->num_seqs, step->num_rows);
   a.max_blocks = step->max_blocks_per_seq;
+  a.num_seqs = step->num_seqs;
+  a.num_pages = pool->num_pages;
+  a.err = debug_error_word();
   a.score_wgs_x = (step->max_blocks_per_seq + kWaves - 1) / kWaves;
   return a;
 }

@@ -225,6 +225,34 @@ __device__ __forceinline__ uint32_t idle_key(uint32_t acc, float4_t v) {
 }
 // Zero that the compiler must treat as differing between lanes (an asm result): added
 // to an address, it keeps a load's result in a vector register.
+// Device-side metadata check of the debug library (built with MSA_DEBUG_CHECKS): a
+// failed check records its msa_debug_error_t code in the caller's error word (if it is
+// still 0) and returns false, and the caller skips the access the check guards. The
+// release library trusts the metadata: the check is always true and compiles away.
+__device__ __forceinline__ bool dcheck(bool ok, int32_t code, int32_t* err) {
+#ifdef MSA_DEBUG_CHECKS
+  if (!ok && err != nullptr) atomicCAS(err, 0, code);
+  return ok;
+#else
+  (void)code;
+  (void)err;
+  return true;
+#endif
+}
+
+// Checked metadata of the debug library: a value out of range is recorded and replaced
+// by 0, which keeps every access in bounds (the results are then meaningless).
+__device__ __forceinline__ int checked_seq(int seq, int num_seqs, int32_t* err) {
+  return dcheck(seq >= 0 && seq < num_seqs, MSA_DEBUG_BAD_SEQ, err) ? seq : 0;
+}
+__device__ __forceinline__ int64_t checked_page(int64_t page, int num_pages, int32_t* err) {
+  return dcheck(page >= 0 && page < num_pages, MSA_DEBUG_BAD_PAGE, err) ? page : 0;
+}
+// A row position is valid when it is not negative and its block is inside the table.
+__device__ __forceinline__ void check_pos(int pos, int max_blocks, int32_t* err) {
+  dcheck(pos >= 0 && pos / MSA_PAGE_SIZE < max_blocks, MSA_DEBUG_BAD_POS, err);
+}
+
 __device__ __forceinline__ int lane_varying_zero() {
   int z;
   asm volatile("v_mov_b32 %0, 0" : "=v"(z));

@@ -8,6 +8,9 @@
 
 namespace msa {
 
+// The debug library's error word (null in the release library, or when unset).
+int32_t* debug_error_word();
+
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 inline msa_status_t check_pool(const msa_kv_pool_t* pool) {

@@ -20,14 +20,15 @@ __global__ void __launch_bounds__(kSelectThreads)
 select_topk_kernel(const float* __restrict__ scores, const int32_t* __restrict__ row_pos,
                    const int32_t* __restrict__ row_seq, const int32_t* __restrict__ block_table,
                    int32_t* __restrict__ sel, int32_t* __restrict__ sel_pages, int max_blocks, int k,
-                   int n_init, int n_local, int tables) {
+                   int n_init, int n_local, int tables, int num_seqs, int32_t* err) {
   extern __shared__ uint32_t keys[];            // [candidates]
   __shared__ SelectSmem sm;
   const int64_t tr = blockIdx.x;                // table row
   const int r = static_cast<int>(tr / tables);
+  if (threadIdx.x == 0) check_pos(row_pos[r], max_blocks, err);
   const int nb = min(row_pos[r] / kPage + 1, max_blocks);   // the table covers nb blocks
   block_select_row<false>(scores + tr * max_blocks, nb, k, n_init, n_local,
-                          block_table + static_cast<int64_t>(row_seq[r]) * max_blocks,
+                          block_table + static_cast<int64_t>(checked_seq(row_seq[r], num_seqs, err)) * max_blocks,
                           sel + tr * k, sel_pages ? sel_pages + tr * k : nullptr, keys, sm);
 }
 
@@ -40,14 +41,16 @@ __global__ void __launch_bounds__(64 * kRowsPerSelectWg)
 select_topk_wave_kernel(const float* __restrict__ scores, const int32_t* __restrict__ row_pos,
                         const int32_t* __restrict__ row_seq, const int32_t* __restrict__ block_table,
                         int32_t* __restrict__ sel, int32_t* __restrict__ sel_pages, int num_rows,
-                        int max_blocks, int k, int n_init, int n_local, uint64_t seq_mul, int tables) {
+                        int max_blocks, int k, int n_init, int n_local, uint64_t seq_mul, int tables,
+                        int num_seqs, int32_t* err) {
   __shared__ int32_t lsel[kRowsPerSelectWg][MSA_MAX_TOPK], lpage[kRowsPerSelectWg][MSA_MAX_TOPK];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int tr = blockIdx.x * kRowsPerSelectWg + wave;      // table row
   if (tr >= num_rows * tables) return;
   const int r = tr / tables;
   const int guess = seq_guess(r, seq_mul);
-  const int seq = row_seq[r];
+  const int seq = checked_seq(row_seq[r], num_seqs, err);
+  if (lane == 0) check_pos(row_pos[r], max_blocks, err);
   wave_select(scores + static_cast<int64_t>(tr) * max_blocks, block_table + static_cast<int64_t>(guess) * max_blocks,
               max_blocks, row_pos + r, k, n_init, n_local, lsel[wave], lpage[wave]);
   const int b = lsel[wave][lane];
@@ -80,13 +83,14 @@ extern "C" msa_status_t msa_select_topk(const msa_step_t* step, const float* blo
     const unsigned wgs = static_cast<unsigned>((table_rows + kRowsPerSelectWg - 1) / kRowsPerSelectWg);
     select_topk_wave_kernel<<<dim3(wgs), dim3(64 * kRowsPerSelectWg), 0, static_cast<hipStream_t>(stream)>>>(
         block_scores, step->row_pos, step->row_seq, step->block_table, sel, sel_pages, step->num_rows,
-        step->max_blocks_per_seq, k, n_init, n_local, seq_guess_mul(step->num_seqs, step->num_rows), tables);
+        step->max_blocks_per_seq, k, n_init, n_local, seq_guess_mul(step->num_seqs, step->num_rows), tables,
+        step->num_seqs, debug_error_word());
     return launch_status();
   }
   const size_t lds = static_cast<size_t>(step->max_blocks_per_seq) * sizeof(uint32_t);
   select_topk_kernel<<<dim3(static_cast<unsigned>(table_rows)), dim3(kSelectThreads), lds,
                        static_cast<hipStream_t>(stream)>>>(
       block_scores, step->row_pos, step->row_seq, step->block_table, sel, sel_pages,
-      step->max_blocks_per_seq, k, n_init, n_local, tables);
+      step->max_blocks_per_seq, k, n_init, n_local, tables, step->num_seqs, debug_error_word());
   return launch_status();
 }

@@ -83,6 +83,8 @@ struct DecodeArgs {
   float* part_o;
   float* part_ml;
   int32_t* counters;          // combining variants: merge state words [rows][hkv]
+  int num_seqs, num_pages;
+  int32_t* err;               // debug library: the error word of failed metadata checks
   uint16_t* out;              // combining variants: bf16 [rows][hq][128]
 };
 
@@ -174,6 +176,7 @@ __device__ __forceinline__ void load_round(Round<kFmt, kItems>& rd, const Decode
       const int nv = min(pos - b * kPage + 1, kPage) - 32 * c;   // visible tokens in the chunk
       if (b >= 0 && nv > 0) {
         rd.nvis[j] = min(nv, 32);
+        page = checked_page(page, a.num_pages, a.err);
         pages[j] = page;
         load_chunk<kFmt>(rd.R[j], a, page, g, c, n, q);
       }
@@ -343,8 +346,11 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
     }
     pos = a.row_pos[r];
     load_q();
+    // (debug library: an entry that is neither -1 nor a visible block is dropped)
+    if (lane < a.k && !dcheck(selv >= -1 && selv < min(pos / kPage + 1, a.max_blocks), MSA_DEBUG_BAD_SEL, a.err))
+      selv = -1;
     if (a.sel_pages == nullptr && selv >= 0)
-      pagev = a.block_table[static_cast<int64_t>(a.row_seq[r]) * a.max_blocks + selv];
+      pagev = a.block_table[static_cast<int64_t>(checked_seq(a.row_seq[r], a.num_seqs, a.err)) * a.max_blocks + selv];
   }
   if constexpr (kSelect) {
     const float* srow = a.scores + trow * a.max_blocks;
@@ -357,7 +363,7 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
       // every wave's own copy of the row's position and request, read before the
       // selection so that wave 0 does not wait for them after it
       pos = a.row_pos[r];
-      const int seq = a.row_seq[r];
+      const int seq = checked_seq(a.row_seq[r], a.num_seqs, a.err);
       if (wave == 0) {
         const int32_t* btg = a.block_table + static_cast<int64_t>(guess) * a.max_blocks;
         wave_select<kSelect>(srow, btg, a.max_blocks, a.row_pos + r, a.k, a.n_init, a.n_local, lsel, lpage);
@@ -374,7 +380,8 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
       if (wave == 1) q_to_lds();
       pos = a.row_pos[r];
       const int nb = min(pos / kPage + 1, a.max_blocks);
-      const int32_t* bt = a.block_table + static_cast<int64_t>(a.row_seq[r]) * a.max_blocks;
+      const int32_t* bt =
+          a.block_table + static_cast<int64_t>(checked_seq(a.row_seq[r], a.num_seqs, a.err)) * a.max_blocks;
       block_select_row<false, 64 * kW>(srow, nb, a.k, a.n_init, a.n_local, bt, lsel, nullptr,
                                        reinterpret_cast<uint32_t*>(dyn_lds), sm);
       __syncthreads();
@@ -388,6 +395,7 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
       if (a.sel_pages_out) a.sel_pages_out[trow * a.k + lane] = pagev;
     }
   }
+  if (wave == 0 && lane == 0 && s == 0) check_pos(pos, a.max_blocks, a.err);
   auto lookup = [&](int e, int& b, int64_t& page) {
     b = __builtin_amdgcn_readlane(selv, e);   // e is the same in every lane
     page = __builtin_amdgcn_readlane(pagev, e);
@@ -699,6 +707,9 @@ msa_status_t decode_entry(const msa_kv_pool_t* pool, const msa_step_t* step, int
   a.hkv = pool->num_kv_heads;
   a.block_table = step->block_table;
   a.row_seq = step->row_seq;
+  a.num_seqs = step->num_seqs;
+  a.num_pages = pool->num_pages;
+  a.err = debug_error_word();
   a.row_pos = step->row_pos;
   a.max_blocks = step->max_blocks_per_seq;
   a.q = static_cast<const uint16_t*>(q);

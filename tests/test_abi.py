@@ -35,6 +35,28 @@ def test_every_declared_symbol_is_exported():
         assert getattr(L.LIB, n) is not None
 
 
+def test_debug_library_exports_the_same_entry_points_and_its_setter():
+    """libmsadecode_debug.so (MSA_DEBUG_CHECKS) exports every declared symbol too; only
+    it accepts an error word, and each build reports which one it is."""
+    names = declared_symbols()
+    assert {"msa_debug_set_error_word", "msa_debug_checks_enabled"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", L.DEBUG_LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (msa_\w+)", out))
+    assert set(names) <= exported
+    rel, dbg = L.load_library(L.RELEASE_LIB_PATH), L.load_library(L.DEBUG_LIB_PATH)
+    assert rel.msa_debug_checks_enabled() == 0 and dbg.msa_debug_checks_enabled() == 1
+    assert rel.msa_debug_set_error_word(ctypes.c_void_p(16)) == -2
+    assert dbg.msa_debug_set_error_word(ctypes.c_void_p(16)) == 0
+    assert dbg.msa_debug_set_error_word(None) == 0
+    # host-side validation is the same in both builds
+    B, P = ctypes.byref, ctypes.c_void_p
+    pool, step = _fake_pool(), _fake_step()
+    for lib in (rel, dbg):
+        assert lib.msa_index_score(B(pool), B(step), 3, P(16), P(16), P(16), None) == -2
+        assert lib.msa_sparse_decode(B(pool), B(step), 32, P(16), P(16), None, 8, 0.1, 2, P(16), P(16), None) == 0
+
+
 def test_read_probe_library_loads_and_validates():
     """The bench's streaming-read reference (libmsaprobe.so) exports its one entry and
     rejects bad arguments before any launch."""

@@ -1,0 +1,117 @@
+"""The debug build (libmsadecode_debug.so, MSA_DEBUG_CHECKS): on valid inputs it reports
+nothing and computes exactly what the release build does; each kind of bad device-side
+metadata is reported in the caller's error word by the kernels' own checks, which skip
+or redirect the access they guard (so these cases stay in bounds by construction)."""
+import numpy as np
+import pytest
+import torch
+
+from synth import workloads as W
+from tests import gpu_common as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def M():
+    import sparse_attention_decode_fp8_amd as M
+    return M
+
+
+@pytest.fixture(scope="module")
+def dbg(M):
+    lib = M.load_library(M.DEBUG_LIB_PATH)
+    assert lib.msa_debug_checks_enabled() == 1
+    return lib
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+@pytest.mark.parametrize("fmt", [W.FMT_FP8, W.FMT_NVFP4])
+@pytest.mark.parametrize("fused", [True, False])
+def test_valid_step_reports_nothing_and_matches_release(M, dbg, fmt, fused):
+    wl = W.small(fmt, [1000, 2600, 130], 2, num_kv_heads=2, k=5, seed=95)
+    _print("debug build, valid step", wl.name, "fused", fused)
+    pool = G.gpu_pool(M, wl)
+    ref = G.run_gpu_step(M, wl, pool.clone(), 2, fused=fused)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    with M.use_library(dbg):
+        M.msa_debug_set_error_word(err)
+        try:
+            got = G.run_gpu_step(M, wl, pool.clone(), 2, fused=fused)
+        finally:
+            M.msa_debug_set_error_word(None)
+    assert int(err.item()) == 0
+    assert torch.equal(got.block_scores, ref.block_scores)
+    assert torch.equal(got.sel, ref.sel)
+    assert torch.equal(got.out.view(torch.int16), ref.out.view(torch.int16))
+
+
+def _bad_case_setup(M, fmt):
+    wl = W.small(fmt, [1000, 2600], 1, num_kv_heads=2, k=4, seed=96)
+    pool = G.gpu_pool(M, wl)
+    step, q, q_idx, w, app = G.gpu_step_inputs(M, wl)
+    bufs = M.DecodeBuffers(wl.num_rows, wl.num_heads, wl.max_blocks, wl.k, 2)
+    M.msa_index_score(pool, step, q_idx, w, bufs.block_scores)
+    M.msa_select_topk(step, bufs.block_scores, wl.k, 0, 1, bufs.sel, bufs.sel_pages)
+    torch.cuda.synchronize()
+    return wl, pool, step, q, q_idx, w, app, bufs
+
+
+@pytest.mark.parametrize("fmt", [W.FMT_FP8, W.FMT_NVFP4])
+def test_bad_metadata_is_reported(M, dbg, fmt):
+    wl, pool, step, q, q_idx, w, app, bufs = _bad_case_setup(M, fmt)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    with M.use_library(dbg):
+        M.msa_debug_set_error_word(err)
+        try:
+            def expect(code, what):
+                torch.cuda.synchronize()
+                assert int(err.item()) == code, (what, int(err.item()))
+                err.zero_()
+
+            # a page id past the pool in sel_pages: the decode reads page 0 instead
+            _print("debug: page id past the pool (sel_pages)")
+            sp = bufs.sel_pages.clone()
+            sp[0, 0] = wl.num_pages + 7
+            M.msa_sparse_decode(pool, step, q, bufs.sel, wl.k, wl.softmax_scale, 2, bufs.part_o, bufs.part_ml,
+                                sel_pages=sp)
+            expect(1, "page")
+            # a selection entry past the row's visible blocks: dropped
+            _print("debug: selection entry past the row")
+            sl = bufs.sel.clone()
+            sl[1, 0] = wl.max_blocks + 3
+            M.msa_sparse_decode(pool, step, q, sl, wl.k, wl.softmax_scale, 2, bufs.part_o, bufs.part_ml)
+            expect(4, "sel")
+            # a request id past num_seqs: the selection reads request 0's table
+            _print("debug: request id past num_seqs")
+            bad_seq = M.Step(wl.block_table, np.where(np.arange(wl.num_rows) == 0, len(wl.ctx_lens) + 3,
+                                                      wl.row_seq).astype(np.int32), wl.row_pos)
+            M.msa_select_topk(bad_seq, bufs.block_scores, wl.k, 0, 1, bufs.sel, bufs.sel_pages)
+            expect(2, "seq")
+            # a position past the block table: the selection clamps to the table
+            _print("debug: position past the table")
+            bad_pos = M.Step(wl.block_table, wl.row_seq,
+                             np.where(np.arange(wl.num_rows) == 1, wl.max_blocks * 128 + 5, wl.row_pos).astype(np.int32))
+            M.msa_select_topk(bad_pos, bufs.block_scores, wl.k, 0, 1, bufs.sel, bufs.sel_pages)
+            expect(3, "pos")
+            # a block-table page past the pool: the scorer reads page 0's keys instead
+            _print("debug: block-table page past the pool")
+            bt = wl.block_table.copy()
+            bt[1, 2] = wl.num_pages + 11
+            M.msa_index_score(pool, M.Step(bt, wl.row_seq, wl.row_pos), q_idx, w, bufs.block_scores)
+            expect(1, "table page")
+            # an append slot whose page lies past the pool: the token is not written
+            _print("debug: append slot past the pool")
+            slot = app[0].clone()
+            slot[0] = (wl.num_pages + 2) * 128 + 5
+            before = {k: v.clone() for k, v in pool.arrays().items()}
+            M.msa_kv_append(pool, slot[:1], app[1][:1].contiguous(), app[2][:1].contiguous(),
+                            app[3][:1].contiguous())
+            expect(5, "slot")
+            for k, v in pool.arrays().items():
+                assert torch.equal(v, before[k]), k
+        finally:
+            M.msa_debug_set_error_word(None)
