@@ -163,6 +163,22 @@ __device__ __forceinline__ uint32_t wave_and(uint32_t v) {
   x &= __builtin_amdgcn_update_dpp(-1, x, 0x143, 0xc, 0xf, false);
   return static_cast<uint32_t>(__builtin_amdgcn_readlane(x, 63));
 }
+// Inclusive prefix sum over the wave's lanes in lane order, the same moves (identity 0):
+// lane L gets v(0) + ... + v(L), lane 63 the total. Counts from several registers per
+// lane summed this way replace one ballot and popcount per register.
+__device__ __forceinline__ uint32_t wave_scan_add_u32(uint32_t v) {
+  int x = static_cast<int>(v);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31
+  return static_cast<uint32_t>(x);
+}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(wave_scan_add_u32(v)), 63));
+}
 // Wave-wide unsigned maximum, the same moves (identity 0).
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   uint32_t x = v;

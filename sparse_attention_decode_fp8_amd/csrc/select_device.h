@@ -248,9 +248,20 @@ __device__ __forceinline__ void wave_select_table(const float* srow, const int32
 #pragma unroll
   for (int i = 0; i < kR; ++i) k_max = max(k_max, key[i]);
   k_max = wave_max_u32(k_max);
+  // Counting: up to 16 keys per lane one ballot and popcount per register; with 32 each
+  // lane counts its own keys and one DPP sum (or prefix sum) adds the lanes (measured:
+  // faster with 32 keys per lane, slightly slower with 16, the same with 8).
+  constexpr bool kLaneCount = kR >= 32;
   int n_max = 0;
+  if constexpr (kLaneCount) {
+    uint32_t c = 0u;
 #pragma unroll
-  for (int i = 0; i < kR; ++i) n_max += __popcll(__ballot(key[i] == k_max));
+    for (int i = 0; i < kR; ++i) c += key[i] == k_max;
+    n_max = static_cast<int>(wave_sum_u32(c));
+  } else {
+#pragma unroll
+    for (int i = 0; i < kR; ++i) n_max += __popcll(__ballot(key[i] == k_max));
+  }
   // The bits every candidate shares are the threshold's too: start below them.
   uint32_t k_or = 0u, k_and = ~0u;
 #pragma unroll
@@ -266,9 +277,30 @@ __device__ __forceinline__ void wave_select_table(const float* srow, const int32
   uint32_t T = top < 0 ? k_and : top >= 31 ? 0u : (k_and & ~((2u << top) - 1u));
   auto count_ge = [&](uint32_t c) {
     int n = 0;
+    if constexpr (kLaneCount) {
+      uint32_t m = 0u;
 #pragma unroll
-    for (int i = 0; i < kR; ++i) n += __popcll(__ballot(key[i] >= c));
+      for (int i = 0; i < kR; ++i) m += key[i] >= c;
+      n = static_cast<int>(wave_sum_u32(m));
+    } else {
+#pragma unroll
+      for (int i = 0; i < kR; ++i) n += __popcll(__ballot(key[i] >= c));
+    }
     return n;
+  };
+  // Two thresholds in one sum: per-lane counts (at most 32) in the two 16-bit halves.
+  auto count_ge2 = [&](uint32_t c_lo, uint32_t c_hi, int& n_lo, int& n_hi) {
+    if constexpr (kLaneCount) {
+      uint32_t m = 0u;
+#pragma unroll
+      for (int i = 0; i < kR; ++i) m += (key[i] >= c_lo ? 1u : 0u) + (key[i] >= c_hi ? 0x10000u : 0u);
+      const uint32_t t = wave_sum_u32(m);
+      n_lo = static_cast<int>(t & 0xffffu);
+      n_hi = static_cast<int>(t >> 16);
+    } else {
+      n_lo = count_ge(c_lo);
+      n_hi = count_ge(c_hi);
+    }
   };
   int bit = top;
   bool done = false;
@@ -279,7 +311,9 @@ __device__ __forceinline__ void wave_select_table(const float* srow, const int32
   }
   for (; bit >= 1; bit -= 2) {                   // bits bit, bit-1
     const uint32_t c1 = T | (1u << (bit - 1)), c2 = T | (2u << (bit - 1)), c3 = T | (3u << (bit - 1));
-    const int n1 = count_ge(c1), n2 = count_ge(c2), n3 = count_ge(c3);   // n1 >= n2 >= n3
+    int n1, n2;
+    count_ge2(c1, c2, n1, n2);
+    const int n3 = count_ge(c3);   // n1 >= n2 >= n3
     if (n3 >= want) {
       T = c3;
       done = n3 == want;
@@ -295,16 +329,25 @@ __device__ __forceinline__ void wave_select_table(const float* srow, const int32
   if (!done && bit == 0 && count_ge(T | 1u) >= want) T |= 1u;
 
   int gt = 0;
+  int tie_before = 0;   // keys equal to T in earlier lanes (block order is lane-major)
+  if constexpr (kLaneCount) {
+    uint32_t m = 0u;   // this lane's keys above T (low half) and equal to T (high half)
 #pragma unroll
-  for (int i = 0; i < kR; ++i) gt += __popcll(__ballot(key[i] > T));
-  const int need = want - gt;                            // keys equal to T to take
-  int tie_before = 0;
+    for (int i = 0; i < kR; ++i) m += (key[i] > T ? 1u : 0u) + (key[i] == T ? 0x10000u : 0u);
+    const uint32_t incl = wave_scan_add_u32(m);
+    gt = static_cast<int>(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), 63)) & 0xffffu);
+    tie_before = static_cast<int>((incl - m) >> 16);
+  } else {
 #pragma unroll
-  for (int i = 0; i < kR; ++i) {
-    const uint64_t m = __ballot(key[i] == T);
-    tie_before += __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
-                                            __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+    for (int i = 0; i < kR; ++i) gt += __popcll(__ballot(key[i] > T));
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+      const uint64_t m = __ballot(key[i] == T);
+      tie_before += __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                              __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+    }
   }
+  const int need = want - gt;                            // keys equal to T to take
   bool take[kR];
   int tb = tie_before;
 #pragma unroll
@@ -312,12 +355,19 @@ __device__ __forceinline__ void wave_select_table(const float* srow, const int32
     take[i] = key[i] > T || (key[i] == T && tb < need);
     tb += key[i] == T;
   }
-  int before = 0;
+  int before = 0;   // taken keys in earlier lanes
+  if constexpr (kLaneCount) {
+    uint32_t m = 0u;
 #pragma unroll
-  for (int i = 0; i < kR; ++i) {
-    const uint64_t m = __ballot(take[i]);
-    before += __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
-                                        __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+    for (int i = 0; i < kR; ++i) m += take[i];
+    before = static_cast<int>(wave_scan_add_u32(m) - m);
+  } else {
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+      const uint64_t m = __ballot(take[i]);
+      before += __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                          __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+    }
   }
   int at = n_init + before;
 #pragma unroll
