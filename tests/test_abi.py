@@ -4,6 +4,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -229,3 +230,25 @@ def test_binding_rejects_host_tensors():
     import torch
     with pytest.raises(L.MsaError):
         L._ptr(torch.zeros(4), torch.float32, "x")
+
+
+def test_environment_selects_the_debug_library():
+    """MSA_DEBUG_CHECKS=1 at import makes the binding load libmsadecode_debug.so."""
+    code = ("import sparse_attention_decode_fp8_amd._lib as L; "
+            "print(L.LIB_PATH.endswith('libmsadecode_debug.so'), L.LIB.msa_debug_checks_enabled())")
+    env = dict(os.environ, MSA_DEBUG_CHECKS="1")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, check=True, env=env,
+                         cwd=ROOT).stdout.split()
+    assert out == ["True", "1"]
+    env["MSA_DEBUG_CHECKS"] = "0"
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, check=True, env=env,
+                         cwd=ROOT).stdout.split()
+    assert out == ["False", "0"]
+
+
+def test_use_library_switches_and_restores():
+    dbg = L.load_library(L.DEBUG_LIB_PATH)
+    before = L.LIB
+    with L.use_library(dbg) as lib:
+        assert L.LIB is dbg and lib.msa_debug_checks_enabled() == 1
+    assert L.LIB is before
