@@ -1,0 +1,56 @@
+"""Host-side logic without a GPU: the split-count policy and the benchmark's
+algorithmic-byte count (union of a request's selected visible tokens per KV head)."""
+import importlib.util
+import os
+import types
+
+import numpy as np
+
+from sparse_attention_decode_fp8_amd.pipeline import FUSED_APPEND_MAX, default_num_splits
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench():
+    spec = importlib.util.spec_from_file_location("bench_module", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_default_num_splits_policy():
+    # about 256 workgroups, a power of two, at most min(k / 2, 16)
+    assert default_num_splits(16, 32) == 8      # config 1: 8 rows x 4 KV heads
+    assert default_num_splits(8, 1) == 4        # config 0: k / 2
+    assert default_num_splits(32, 8) == 16      # config 3: capped at 16
+    assert default_num_splits(16, 640) == 1     # config 2: the pairs fill the GPU
+    assert default_num_splits(16, 192) == 1     # config 4
+    assert default_num_splits(1, 1) == 1
+    for k in range(1, 65):
+        for pairs in (1, 3, 17, 100, 256, 1000):
+            s = default_num_splits(k, pairs)
+            assert s >= 1 and (s & (s - 1)) == 0 and s <= max(1, min(k // 2, 16))
+    assert FUSED_APPEND_MAX == 64
+
+
+def test_algorithmic_bytes_count_the_union_per_request_and_kv_head():
+    B = _bench()
+    # two requests: request 0 has rows at positions 300 and 301 (3 blocks, the last
+    # with 45 / 46 visible tokens), request 1 one row at position 127 (one full block)
+    wl = types.SimpleNamespace(ctx_lens=np.array([300, 127]), row_seq=np.array([0, 0, 1]),
+                               row_pos=np.array([300, 301, 127]), num_kv_heads=2, num_rows=3, num_heads=32)
+    sel = np.array([[0, 2], [1, 2], [0, -1]], dtype=np.int32)
+    total, tok = B.decode_algorithmic_bytes(wl, sel, 144)
+    # request 0: blocks {0, 1, 2}: 128 + 128 + 46 (the later row sees token 301) = 302
+    # request 1: block 0, 128 tokens
+    assert tok == 302 + 128
+    qo = 2 * 3 * 32 * 128 * 2
+    meta = sel.size * 4 + 5 * 4
+    assert total == (302 + 128) * 2 * 144 + qo + meta
+    # per-KV-head tables: each KV head counts its own union
+    sel3 = np.array([[[0, 2], [1, 2]], [[1, 2], [1, 2]], [[0, -1], [0, -1]]], dtype=np.int32)
+    total3, tok3 = B.decode_algorithmic_bytes(wl, sel3, 144)
+    head0 = 302 + 128                      # blocks {0,1,2} of request 0, block 0 of request 1
+    head1 = (128 + 46) + 128               # blocks {1, 2} of request 0, block 0 of request 1
+    assert total3 == (head0 + head1) * 144 + qo + sel3.size * 4 + int((sel3 >= 0).sum()) * 4
+    assert tok3 == (head0 + head1) // 2
