@@ -298,15 +298,74 @@ def _oracle_pool(wl, with_step=True):
     return pool
 
 
-def _dense_sdpa(pool, wl, r):
-    """torch scaled_dot_product_attention (float64, CPU) over all visible tokens."""
+def _exact_nvfp4_vectors(rng, shape, t):
+    """Vectors (last axis a multiple of 16) that NVFP4 holds exactly at tensor scale t (a
+    power of two): each 16-group is E2M1 values times one E4M3 scale times t, with the
+    group's largest magnitude exactly 6 * scale * t, so the recipe picks that scale and
+    codes every element exactly. The scales of one vector's groups are all different
+    (some with a mantissa, 1.25 = 0x3A, 1.75 = 0x3E, ...), so a scale applied to the
+    wrong group changes the value."""
+    grid = np.array([0, .5, 1, 1.5, 2, 3, 4, 6])
+    n = shape[-1] // 16
+    scale_set = np.array([2.0 ** e * m for e in range(-4, 3) for m in (1.0, 1.25, 1.5, 1.75)])
+    out = np.empty(shape)
+    flat = out.reshape(-1, n, 16)
+    for i in range(flat.shape[0]):
+        scales = rng.choice(scale_set, n, replace=False)
+        for g in range(n):
+            v = rng.choice(grid, 16) * rng.choice([-1, 1], 16)
+            v[rng.integers(16)] = 6.0 * rng.choice([-1, 1])
+            flat[i, g] = v * scales[g] * t
+    return out
+
+
+def _exact_fp8_values(rng, shape, page_scale):
+    """Values E4M3(code) * page_scale for random non-NaN codes (subnormals, both signs
+    of zero and 448 included), exactly representable in bf16 for a power-of-two scale.
+    The code values come from torch's float8_e4m3fn, not from the oracle's table."""
+    lib = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    codes = rng.choice(np.array([c for c in range(256) if c not in (0x7F, 0xFF)]), shape)
+    return lib[codes] * page_scale, codes
+
+
+def _exact_kv(wl, rng):
+    """Rewrite a workload's K/V source with values its KV format holds exactly, and its
+    scales with distinct powers of two: NVFP4 tensor scales 2^-5 (K) and 2^-3 (V);
+    FP8 page scales 2^(page % 7 - 3) for K and 2^(2 - page % 5) for V. The source
+    is then the exact value of every appended token, independently of the oracle's
+    decoding."""
+    if wl.fmt == W.FMT_NVFP4:
+        wl.k_tensor_scale, wl.v_tensor_scale = 2.0 ** -5, 2.0 ** -3
+        for s in range(len(wl.ctx_lens)):
+            T = wl.total_len(s)
+            shp = (T, wl.num_kv_heads, wl.head_dim)
+            wl.k_src[s] = W.to_bf16_bits(_exact_nvfp4_vectors(rng, shp, wl.k_tensor_scale).astype(np.float32))
+            wl.v_src[s] = W.to_bf16_bits(_exact_nvfp4_vectors(rng, shp, wl.v_tensor_scale).astype(np.float32))
+    else:
+        pages = np.arange(wl.num_pages)
+        wl.k_page_scale = (2.0 ** (pages % 7 - 3)).astype(np.float32)
+        wl.v_page_scale = (2.0 ** (2 - pages % 5)).astype(np.float32)
+        for s in range(len(wl.ctx_lens)):
+            T = wl.total_len(s)
+            page = wl.block_table[s][np.arange(T) // 128]
+            shp = (T, wl.num_kv_heads, wl.head_dim)
+            kv, _ = _exact_fp8_values(rng, shp, wl.k_page_scale[page][:, None, None].astype(np.float64))
+            vv, _ = _exact_fp8_values(rng, shp, wl.v_page_scale[page][:, None, None].astype(np.float64))
+            wl.k_src[s] = W.to_bf16_bits(kv.astype(np.float32))
+            wl.v_src[s] = W.to_bf16_bits(vv.astype(np.float32))
+    return wl
+
+
+def _dense_sdpa(wl, r):
+    """torch scaled_dot_product_attention (float64, CPU) over all visible tokens, on the
+    workload's exact K/V source values (see _exact_kv): it never decodes the pool."""
     seq, pos = int(wl.row_seq[r]), int(wl.row_pos[r])
-    toks = np.arange(pos + 1)
     outs = []
     q = torch.tensor(W.bf16_bits_to_f32(wl.q[r]).astype(np.float64))
+    K_all = W.bf16_bits_to_f32(wl.k_src[seq][:pos + 1]).astype(np.float64)   # [T][Hkv][D]
+    V_all = W.bf16_bits_to_f32(wl.v_src[seq][:pos + 1]).astype(np.float64)
     for g in range(wl.num_kv_heads):
-        K = np.stack([O.dequant_page(pool, int(wl.block_table[seq][t // 128]), g, "k")[t % 128] for t in toks])
-        V = np.stack([O.dequant_page(pool, int(wl.block_table[seq][t // 128]), g, "v")[t % 128] for t in toks])
+        K, V = K_all[:, g], V_all[:, g]
         qg = q[16 * g:16 * g + 16][None]                       # [1, 16, D]
         o = torch.nn.functional.scaled_dot_product_attention(
             qg, torch.tensor(K)[None].contiguous(), torch.tensor(V)[None].contiguous(),
@@ -317,15 +376,63 @@ def _dense_sdpa(pool, wl, r):
 
 @pytest.mark.parametrize("fmt", [W.FMT_FP8, W.FMT_NVFP4])
 def test_sparse_equals_dense_when_all_blocks_selected(fmt):
-    wl = W.small(fmt, [300, 129], 2, num_kv_heads=1, k=4, seed=21)
+    wl = _exact_kv(W.small(fmt, [300, 129], 2, num_kv_heads=2, k=4, seed=21), np.random.default_rng(24))
     pool = _oracle_pool(wl)
     sel = np.tile(np.arange(4, dtype=np.int32), (wl.num_rows, 1))
     nb = wl.row_pos // 128 + 1
     sel = np.where(np.arange(4)[None] < nb[:, None], sel, -1).astype(np.int32)
     out = O.attend(pool, wl.block_table, wl.row_seq, wl.row_pos, wl.q, sel, wl.softmax_scale)
     for r in range(wl.num_rows):
-        ref = _dense_sdpa(pool, wl, r)
-        assert np.max(np.abs(out[r] - ref)) < 1e-12
+        ref = _dense_sdpa(wl, r)
+        # fp64 rounding only (the FP8 source reaches 448 * 8, so the bound is relative)
+        assert np.max(np.abs(out[r] - ref)) <= 1e-13 * max(1.0, np.max(np.abs(ref)))
+
+
+@pytest.mark.parametrize("fmt", [W.FMT_FP8, W.FMT_NVFP4])
+def test_kv_round_trips_exactly_through_append_and_dequant(fmt):
+    """K and V values the format holds exactly come back bit for bit from kv_append +
+    dequant_page, for every page and KV head, with NVFP4 group scales that differ
+    inside each token and non-unit tensor scales that differ between K and V, and FP8
+    page scales that differ from page to page and between K and V. A scale broadcast
+    that tiles instead of repeating, a dropped tensor scale, the other tensor's scale,
+    or the scale of a neighbouring page fails here. Slots never written decode to 0."""
+    rng = np.random.default_rng(25)
+    wl = _exact_kv(W.small(fmt, [200, 300], 1, num_kv_heads=2, k=4, seed=26), rng)
+    pool = _oracle_pool(wl)
+    written = np.zeros((wl.num_pages, 128), bool)
+    for s in range(len(wl.ctx_lens)):
+        T = wl.total_len(s)
+        for p in range(T):
+            page = int(wl.block_table[s][p // 128])
+            written[page, p % 128] = True
+            for kv, src in (("k", wl.k_src[s]), ("v", wl.v_src[s])):
+                exact = W.bf16_bits_to_f32(src[p]).astype(np.float64)          # [Hkv][D]
+                for g in range(wl.num_kv_heads):
+                    got = O.dequant_page(pool, page, g, kv)[p % 128]
+                    assert np.array_equal(got, exact[g]), (fmt, kv, s, p, g)
+    for page in range(wl.num_pages):
+        for g in range(wl.num_kv_heads):
+            for kv in ("k", "v"):
+                assert not O.dequant_page(pool, page, g, kv)[~written[page]].any()
+
+
+def test_fp8_kv_append_codes_use_each_pages_own_scales():
+    """FP8 append: the code written for x on page p is the E4M3 code c with
+    x = E4M3[c] * scale_p, for K with the K scale and for V with the V scale of that
+    page (closed form: the codes the values were made from)."""
+    rng = np.random.default_rng(27)
+    k_sc = np.array([0.25, 8.0, 2.0 ** -5, 2.0], np.float32)
+    v_sc = np.array([4.0, 0.125, 1.0, 2.0 ** -4], np.float32)
+    pool = O.new_pool(O.FMT_FP8, 4, 2, k_page_scale=k_sc, v_page_scale=v_sc)
+    slots = np.array([0 * 128 + 3, 1 * 128 + 0, 2 * 128 + 127, 3 * 128 + 64, 1 * 128 + 5])
+    page = slots // 128
+    kx, kc = _exact_fp8_values(rng, (5, 2, 128), k_sc[page][:, None, None].astype(np.float64))
+    vx, vc = _exact_fp8_values(rng, (5, 2, 128), v_sc[page][:, None, None].astype(np.float64))
+    O.kv_append(pool, slots, W.to_bf16_bits(kx.astype(np.float32)), W.to_bf16_bits(vx.astype(np.float32)), None)
+    for i, sl in enumerate(slots):
+        assert np.array_equal(pool["k_codes"][sl // 128, :, sl % 128], kc[i])
+        assert np.array_equal(pool["v_codes"][sl // 128, :, sl % 128], vc[i])
+    assert np.array_equal(pool["k_scales"], k_sc) and np.array_equal(pool["v_scales"], v_sc)   # read, not written
 
 
 def test_split_combine_identity():
