@@ -23,8 +23,10 @@
  *   - Every array argument is caller-owned DEVICE memory, except the msa_kv_pool_t and
  *     msa_step_t structs themselves, which live in HOST memory and are read during the
  *     call only (the device pointers inside them are what the kernels use).
- *   - Nothing is allocated or freed, no host synchronisation happens, no global state is
- *     kept; calls on different streams may run concurrently if their outputs differ.
+ *   - Nothing is allocated or freed and no host synchronisation happens; calls on
+ *     different streams may run concurrently if their outputs differ. The release library
+ *     keeps no global state (the debug library's two process-wide settings are described
+ *     at msa_debug_set_error_word).
  *   - Geometry is validated on the host before any launch. A call outside the supported
  *     contract returns MSA_ERR_UNSUPPORTED and launches nothing; it never falls back to
  *     another algorithm ([GB300] "The TP4 decode target": a covered shape whose
@@ -273,6 +275,13 @@ msa_status_t msa_sparse_decode(const msa_kv_pool_t* pool, const msa_step_t* step
  *     changing num_splits. With num_splits == 1 the one split writes `out` itself and
  *     the workspace is neither read nor written. Two calls that share a workspace must
  *     not run concurrently. num_splits <= 16.
+ *   The merging split waits for the other splits' partials with a bounded poll (about
+ *     2^16 rounds; every split it waits for is already running). If the bound is ever
+ *     reached (a split held off the GPU for milliseconds), the outputs it could not
+ *     merge are bf16 NaN and the pair's state word keeps a failure bit (bit 15), so
+ *     every later call writes NaN for that (row, KV head) as for a workspace set up for
+ *     another split count, until msa_merge_workspace_init; the debug library also
+ *     reports MSA_DEBUG_MERGE_TIMEOUT.
  */
 msa_status_t msa_sparse_decode_combine(const msa_kv_pool_t* pool, const msa_step_t* step,
                                        int32_t num_q_heads, const void* q, const int32_t* sel,
@@ -353,10 +362,16 @@ const char* msa_status_string(msa_status_t status);
  *   MSA_DEBUG_BAD_POS  : a row_pos whose block lies past max_blocks_per_seq
  *   MSA_DEBUG_BAD_SEL  : a selection entry neither -1 nor a visible block of its row
  *   MSA_DEBUG_BAD_SLOT : an append slot whose page lies outside [0, num_pages)
+ *   MSA_DEBUG_MERGE_TIMEOUT : a merging split gave up waiting for another split's
+ *                       partial (see msa_sparse_decode_combine)
  * msa_debug_set_error_word sets the device int32 word (NULL: none) that every later
  * call of the debug library, on any stream, reports to; the caller zeroes and reads
- * it. It is process-wide state of the debug library only. The release library returns
- * MSA_ERR_UNSUPPORTED, and msa_debug_checks_enabled tells the two apart (1 / 0).
+ * it. msa_debug_set_merge_poll_limit sets the number of poll rounds after which a
+ * merging split gives up (polls < 0: the release bound; 0: give up without reading,
+ * which lets a test force the failure path while every kernel still exits normally).
+ * Both are process-wide state of the debug library only. The release library returns
+ * MSA_ERR_UNSUPPORTED for both, and msa_debug_checks_enabled tells the two apart
+ * (1 / 0).
  */
 typedef enum {
   MSA_DEBUG_OK = 0,
@@ -364,10 +379,12 @@ typedef enum {
   MSA_DEBUG_BAD_SEQ = 2,
   MSA_DEBUG_BAD_POS = 3,
   MSA_DEBUG_BAD_SEL = 4,
-  MSA_DEBUG_BAD_SLOT = 5
+  MSA_DEBUG_BAD_SLOT = 5,
+  MSA_DEBUG_MERGE_TIMEOUT = 6
 } msa_debug_error_t;
 
 msa_status_t msa_debug_set_error_word(int32_t* word);
+msa_status_t msa_debug_set_merge_poll_limit(int32_t polls);
 int32_t msa_debug_checks_enabled(void);
 
 #ifdef __cplusplus

@@ -9,6 +9,7 @@ from ._lib import (FMT_FP8, FMT_NVFP4, IDX_E4M3, IDX_NVFP4, KVPool, MsaError, St
                    msa_decode_workspace_bytes, msa_index_score, msa_kv_append, msa_select_topk,
                    msa_sparse_decode, msa_sparse_decode_combine,
                    msa_append_score_select, msa_select_decode_combine, msa_merge_workspace_init,
-                   MERGE_IDLE_BITS, msa_debug_set_error_word, load_library, use_library,
+                   MERGE_IDLE_BITS, msa_debug_set_error_word, msa_debug_set_merge_poll_limit,
+                   load_library, use_library,
                    RELEASE_LIB_PATH, DEBUG_LIB_PATH)
 from .pipeline import DecodeBuffers, default_num_splits, run_step  # noqa: F401

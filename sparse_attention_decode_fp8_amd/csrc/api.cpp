@@ -3,6 +3,7 @@
 #include <stdint.h>
 
 #include "msa_decode.h"
+#include "msa_host.h"
 
 extern "C" size_t msa_decode_workspace_bytes(int32_t rows, int32_t num_q_heads, int32_t head_dim,
                                              int32_t num_splits) {
@@ -52,6 +53,9 @@ namespace msa {
 // The error word of the debug library's device-side checks (see msa_debug_set_error_word).
 static int32_t* g_debug_error_word = nullptr;
 int32_t* debug_error_word() { return g_debug_error_word; }
+// The debug library's bound on a merging split's poll rounds (< 0: the release bound).
+static int32_t g_merge_poll_limit = -1;
+int32_t merge_poll_limit() { return g_merge_poll_limit < 0 ? kMergePollLimit : g_merge_poll_limit; }
 }  // namespace msa
 
 extern "C" msa_status_t msa_debug_set_error_word(int32_t* word) {
@@ -60,6 +64,16 @@ extern "C" msa_status_t msa_debug_set_error_word(int32_t* word) {
   return MSA_OK;
 #else
   (void)word;
+  return MSA_ERR_UNSUPPORTED;
+#endif
+}
+
+extern "C" msa_status_t msa_debug_set_merge_poll_limit(int32_t polls) {
+#ifdef MSA_DEBUG_CHECKS
+  msa::g_merge_poll_limit = polls;
+  return MSA_OK;
+#else
+  (void)polls;
   return MSA_ERR_UNSUPPORTED;
 #endif
 }

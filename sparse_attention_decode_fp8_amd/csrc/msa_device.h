@@ -280,10 +280,15 @@ constexpr int kMaxMergeSplits = 16;
 
 // Merge state word of one (row, KV head) pair in the combining decode's workspace: bit
 // 31 = which of the two exchange buffers the next launch uses, bits 16..30 = the split
-// count the workspace was set up for, bits 0..15 = splits arrived in the current launch.
+// count the workspace was set up for, bits 0..15 = splits arrived in the current launch
+// (at most 16, so bit 15 is free for kMergeTimeoutBit, which makes the word invalid).
 __host__ __device__ __forceinline__ uint32_t merge_state(int buffer, int num_splits) {
   return (static_cast<uint32_t>(buffer) << 31) | (static_cast<uint32_t>(num_splits) << 16);
 }
+// Set for good by a merger that gave up polling: every later launch finds the word
+// invalid (its arrivals field then exceeds any split count) until the workspace is set up
+// again.
+constexpr uint32_t kMergeTimeoutBit = 1u << 15;
 __device__ __forceinline__ bool merge_state_ok(uint32_t w, int num_splits) {
   return ((w >> 16) & 0x7fffu) == static_cast<uint32_t>(num_splits) && (w & 0xffffu) < static_cast<uint32_t>(num_splits);
 }

@@ -10,6 +10,9 @@ namespace msa {
 
 // The debug library's error word (null in the release library, or when unset).
 int32_t* debug_error_word();
+// Bound on a merging split's poll rounds: kMergePollLimit, or the debug library's setting.
+constexpr int32_t kMergePollLimit = 1 << 16;
+int32_t merge_poll_limit();
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

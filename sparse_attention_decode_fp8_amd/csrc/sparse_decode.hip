@@ -51,10 +51,6 @@ constexpr int kVBufBytes = 32 * kVRowHalves * 2;   // one wave's 32-token V chun
 // on distinct banks; 128-float rows would put all 16 on the same banks.
 constexpr int kORowFloats = kHeadDim + 4;
 static_assert(16 * kORowFloats * 4 <= kVBufBytes, "O tile must fit in a V buffer");
-// Bound on the merger's polls of one slot. Every slot it polls has been stored by a
-// split that is already past its compute, so a few polls suffice; the bound only keeps
-// the loop finite (past it the merge uses what it read).
-constexpr int kMergePollLimit = 1 << 16;
 
 struct DecodeArgs {
   const uint8_t* k_codes;
@@ -86,6 +82,10 @@ struct DecodeArgs {
   int num_seqs, num_pages;
   int32_t* err;               // debug library: the error word of failed metadata checks
   uint16_t* out;              // combining variants: bf16 [rows][hq][128]
+  // Bound on the merger's poll rounds (kMergePollLimit; the debug library can lower it).
+  // Every slot it polls has been stored by a split that is already past its compute, so
+  // a few rounds suffice; the bound only keeps the loop finite.
+  int poll_limit;
 };
 
 __device__ __forceinline__ half2_t bcast_lo(half2_t v) { return half2_t{v[0], v[0]}; }
@@ -199,14 +199,15 @@ __device__ __forceinline__ void load_round(Round<kFmt, kItems>& rd, const Decode
 // the fixed-order log-sum-exp sums of msa_combine. Slots whose words have not all
 // landed are read again, which is rare: the other splits counted themselves in
 // earlier. Entries S..kS-1 repeat the last slot and are not used, so every entry is
-// redefined on each read and none is carried from one poll to the next.
+// redefined on each read and none is carried from one poll to the next. Returns false
+// if some word was still idle after `limit` rounds (num and den are then meaningless).
 template <int kS>
-__device__ __forceinline__ void merge_slots(__amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t rm, int S,
-                                            int h, int d4, float4_t& num, float& den) {
+__device__ __forceinline__ bool merge_slots(__amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t rm, int S,
+                                            int h, int d4, int limit, float4_t& num, float& den) {
   float2_t mls[kS];
   float4_t ot[kS];
   bool ready = false;
-  for (int spin = 0; !ready && spin < kMergePollLimit; ++spin) {
+  for (int spin = 0; !ready && spin < limit; ++spin) {
     if (spin > 0) {
       __builtin_amdgcn_s_sleep(2);
       asm volatile("" ::: "memory");   // load again
@@ -238,6 +239,7 @@ __device__ __forceinline__ void merge_slots(__amdgpu_buffer_rsrc_t ro, __amdgpu_
       num += wgt * ot[t];
     }
   }
+  return ready;
 }
 
 // What a workgroup writes: its split's partial (kOutPartials), the bf16 output of the
@@ -632,20 +634,32 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
       const int h = idx / (kHeadDim / 4), d4 = idx % (kHeadDim / 4);
       float4_t num;
       float den;
-      if (a.num_splits <= 2) merge_slots<2>(ro, rm, a.num_splits, h, d4, num, den);
-      else if (a.num_splits <= 4) merge_slots<4>(ro, rm, a.num_splits, h, d4, num, den);
-      else if (a.num_splits <= 8) merge_slots<8>(ro, rm, a.num_splits, h, d4, num, den);
-      else merge_slots<16>(ro, rm, a.num_splits, h, d4, num, den);
+      bool ok;
+      if (a.num_splits <= 2) ok = merge_slots<2>(ro, rm, a.num_splits, h, d4, a.poll_limit, num, den);
+      else if (a.num_splits <= 4) ok = merge_slots<4>(ro, rm, a.num_splits, h, d4, a.poll_limit, num, den);
+      else if (a.num_splits <= 8) ok = merge_slots<8>(ro, rm, a.num_splits, h, d4, a.poll_limit, num, den);
+      else ok = merge_slots<16>(ro, rm, a.num_splits, h, d4, a.poll_limit, num, den);
       uint16_t o[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[i] = den > 0.0f ? f32_to_bf16_rne(num[i] / den) : 0;
-      *reinterpret_cast<uint2*>(a.out + (head0 + h) * kHeadDim + 4 * d4) =
-          make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16));
+      uint2 ov = make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16));
+      if (!ok) {
+        // gave up waiting: NaN outputs, and the pair's state word stays invalid until
+        // the workspace is set up again (an OR that commutes with the flip below)
+        ov = make_uint2(0x7fc07fc0u, 0x7fc07fc0u);
+        dcheck(false, MSA_DEBUG_MERGE_TIMEOUT, a.err);
+        __hip_atomic_fetch_or(a.counters + static_cast<int64_t>(r) * a.hkv + g, static_cast<int32_t>(kMergeTimeoutBit),
+                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      *reinterpret_cast<uint2*>(a.out + (head0 + h) * kHeadDim + 4 * d4) = ov;
     }
-    if (threadIdx.x == 0)   // the other buffer, no arrivals: ready for the next launch
-      __hip_atomic_store(a.counters + static_cast<int64_t>(r) * a.hkv + g,
-                         static_cast<int32_t>(merge_state(cur ^ 1, a.num_splits)), __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+    // the other buffer, no arrivals: ready for the next launch. All num_splits arrivals
+    // have been counted (this split counted itself in last), so one XOR flips the buffer
+    // bit and clears the arrivals, and leaves any timeout bit set above in place.
+    if (threadIdx.x == 0)
+      __hip_atomic_fetch_xor(a.counters + static_cast<int64_t>(r) * a.hkv + g,
+                             static_cast<int32_t>((1u << 31) | static_cast<uint32_t>(a.num_splits)),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -710,6 +724,7 @@ msa_status_t decode_entry(const msa_kv_pool_t* pool, const msa_step_t* step, int
   a.num_seqs = step->num_seqs;
   a.num_pages = pool->num_pages;
   a.err = debug_error_word();
+  a.poll_limit = merge_poll_limit();
   a.row_pos = step->row_pos;
   a.max_blocks = step->max_blocks_per_seq;
   a.q = static_cast<const uint16_t*>(q);

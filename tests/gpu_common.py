@@ -110,12 +110,19 @@ def gap_qualified(S_row, nb, k, n_init=0, n_local=1) -> bool:
 
 def check_selection_valid(sel_row, S_ref_row, nb, k, n_init=0, n_local=1):
     """Where the boundary is too close to call, the GPU's choice must still be a valid
-    top-k: forced blocks present, ascending, and every chosen free block's reference
-    score within tolerance of the boundary."""
-    chosen = [int(b) for b in sel_row if b >= 0]
-    assert chosen == sorted(chosen) and len(chosen) == min(nb, k)
+    top-k: min(nb, k) entries of visible blocks in strictly ascending order (so no
+    block twice), then only -1 padding, the forced blocks present, and every chosen
+    free block's reference score within tolerance of the boundary."""
+    row = [int(b) for b in sel_row]
+    n = min(nb, k)
+    assert len(row) == k and all(b == -1 for b in row[n:]), f"padding {row}"
+    chosen = row[:n]
+    assert all(0 <= b < nb for b in chosen), f"entries outside the visible blocks {row}"
+    assert all(a < b for a, b in zip(chosen, chosen[1:])), f"not strictly ascending {row}"
     forced = set(range(min(n_init, nb))) | set(range(nb - n_local, nb))
     assert forced <= set(chosen)
+    if nb <= k:
+        return
     free = [b for b in range(n_init, nb - n_local)]
     kk = k - len(forced)
     thr = np.sort([S_ref_row[b] for b in free])[::-1][kk - 1]
@@ -131,25 +138,36 @@ def assert_out_close(out_gpu, out_ref, what=""):
     return err
 
 
-def oracle_rows(wl: W.Workload, rows):
+def oracle_rows(wl: W.Workload, rows, tables=1, also_sel=None):
     """Index scores, selection and attention of the given rows, computed by the oracle
-    from the seeded source alone (it encodes only the pages those rows need)."""
+    from the seeded source alone (it encodes only the pages those rows need). With
+    tables > 1, one selection per (row, KV head). also_sel (the rows' selection from
+    the GPU, [len(rows)][k] or [len(rows)][T][k]) adds the attention over that table as
+    a fifth result, for rows where several selections are valid: the output for a given
+    table is unique."""
     rows = list(rows)
     seqs = sorted(set(int(wl.row_seq[r]) for r in rows))
     pool = oracle_pool(wl, seqs=seqs, kv_blocks={s: [] for s in seqs})
     sub = np.asarray(rows)
     S = O.index_score(pool, wl.block_table, wl.row_seq[sub], wl.row_pos[sub], wl.q_idx[sub],
-                      wl.w[sub], wl.max_blocks)
+                      wl.w[sub], wl.max_blocks, tables)
     sel = O.select_topk(S, wl.row_pos[sub], wl.k, wl.n_init, wl.n_local)
     for s in seqs:
-        blocks = sorted(set(int(b) for i, r in enumerate(rows) if wl.row_seq[r] == s
-                            for b in sel[i] if b >= 0))
+        mine = [i for i, r in enumerate(rows) if wl.row_seq[r] == s]
+        blocks = set(int(b) for i in mine for b in np.ravel(sel[i]) if b >= 0)
+        if also_sel is not None:
+            blocks |= set(int(b) for i in mine for b in np.ravel(also_sel[i]) if b >= 0)
+        blocks = sorted(blocks)
         T = wl.total_len(s)
         pos = np.concatenate([np.arange(b * 128, min((b + 1) * 128, T)) for b in blocks])
         O.kv_append(pool, wl.slots(s, pos), wl.k_src[s][pos], wl.v_src[s][pos], None)
     out = O.attend(pool, wl.block_table, wl.row_seq[sub], wl.row_pos[sub], wl.q[sub], sel,
                    wl.softmax_scale)
-    return S, sel, out, pool
+    if also_sel is None:
+        return S, sel, out, pool
+    out_also = O.attend(pool, wl.block_table, wl.row_seq[sub], wl.row_pos[sub], wl.q[sub],
+                        np.asarray(also_sel, dtype=np.int32), wl.softmax_scale)
+    return S, sel, out, pool, out_also
 
 
 def assert_merge_ready(bufs):
@@ -203,6 +221,13 @@ def check_step_parity(M, wl: W.Workload, num_splits: int, fused: bool, tables: i
     same = same_t.reshape(wl.num_rows, tables).all(axis=1)
     out = bf16_to_np(bufs.out)
     assert_out_close(out[same], out_ref[same], "outputs")
+    if not same.all():
+        # rows where another selection is valid too: the output on the GPU's own
+        # (validated) table is unique
+        sel_gpu = bufs.sel.cpu().numpy()
+        out_gsel = O.attend(ref_pool, wl.block_table, wl.row_seq, wl.row_pos, wl.q, sel_gpu,
+                            wl.softmax_scale)
+        assert_out_close(out[~same], out_gsel[~same], "outputs on the GPU's selection")
     if fused:   # the partials passed through the merge workspace, ready for the next call
         assert_merge_ready(bufs)
         return bufs

@@ -115,3 +115,60 @@ def test_bad_metadata_is_reported(M, dbg, fmt):
                 assert torch.equal(v, before[k]), k
         finally:
             M.msa_debug_set_error_word(None)
+
+
+@pytest.mark.parametrize("entry", ["select_decode_combine", "sparse_decode_combine"])
+def test_merge_give_up_is_reported_and_sticky(M, dbg, entry):
+    """A merging split that gives up waiting (forced from the host: a poll limit of 0,
+    so the merger never reads and every kernel still exits normally) writes NaN, sets
+    the pair's failure bit, and the debug library reports MSA_DEBUG_MERGE_TIMEOUT. Later
+    calls keep writing NaN and touch no workspace word until the workspace is set up
+    again; then the merge equals msa_sparse_decode + msa_combine bit for bit."""
+    wl = W.small(W.FMT_NVFP4, [3000, 2000], 1, num_kv_heads=2, k=8, seed=97)
+    ns = 4
+    _print("forced merge give-up", entry, wl.name, "splits", ns)
+    pool = G.gpu_pool(M, wl)
+    step, q, q_idx, w, app = G.gpu_step_inputs(M, wl)
+    bufs = M.DecodeBuffers(wl.num_rows, wl.num_heads, wl.max_blocks, wl.k, ns)
+    M.msa_kv_append(pool, *app)
+    M.msa_index_score(pool, step, q_idx, w, bufs.block_scores)
+    M.msa_select_topk(step, bufs.block_scores, wl.k, 0, 1, bufs.sel, bufs.sel_pages)
+    M.msa_sparse_decode(pool, step, q, bufs.sel, wl.k, wl.softmax_scale, ns, bufs.part_o, bufs.part_ml,
+                        sel_pages=bufs.sel_pages)
+    ref = torch.empty_like(bufs.out)
+    M.msa_combine(wl.num_rows, wl.num_heads, 128, ns, bufs.part_o, bufs.part_ml, ref)
+
+    def call():
+        if entry == "select_decode_combine":
+            M.msa_select_decode_combine(pool, step, q, bufs.block_scores, wl.k, 0, 1, wl.softmax_scale, ns,
+                                        bufs.merge_o, bufs.merge_ml, bufs.counters, bufs.out)
+        else:
+            M.msa_sparse_decode_combine(pool, step, q, bufs.sel, wl.k, wl.softmax_scale, ns, bufs.merge_o,
+                                        bufs.merge_ml, bufs.counters, bufs.out, sel_pages=bufs.sel_pages)
+        torch.cuda.synchronize()
+
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    with M.use_library(dbg):
+        M.msa_debug_set_error_word(err)
+        try:
+            M.msa_debug_set_merge_poll_limit(0)
+            call()
+            assert int(err.item()) == 6                      # MSA_DEBUG_MERGE_TIMEOUT
+            assert torch.isnan(bufs.out.float()).all()
+            c = bufs.counters.cpu().numpy().view(np.uint32)
+            assert ((c & 0x8000) != 0).all() and (((c >> 16) & 0x7fff) == ns).all()
+            M.msa_debug_set_merge_poll_limit(-1)             # the release bound again
+            err.zero_()
+            words = [t.clone() for t in (bufs.counters, bufs.merge_o, bufs.merge_ml)]
+            bufs.out.zero_()
+            call()                                           # still failed: NaN, nothing touched
+            assert torch.isnan(bufs.out.float()).all() and int(err.item()) == 0
+            for a, b in zip(words, (bufs.counters, bufs.merge_o, bufs.merge_ml)):
+                assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+        finally:
+            M.msa_debug_set_merge_poll_limit(-1)
+            M.msa_debug_set_error_word(None)
+    M.msa_merge_workspace_init(wl.num_rows, wl.num_heads, 128, ns, bufs.merge_o, bufs.merge_ml, bufs.counters)
+    call()
+    assert torch.equal(bufs.out.view(torch.int16), ref.view(torch.int16))
+    G.assert_merge_ready(bufs)
