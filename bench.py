@@ -7,23 +7,31 @@ keys E4M3, top-16 blocks. A step is the whole path: append -> index score -> sel
 -> sparse decode -> combine.
 
 Timing. All inputs are resident in HBM before timing. The pool is replicated R times
-(16 x 169 MB) and step i uses replica i % R, so the ~26 MB a step touches has been
-evicted from the 256 MB Infinity Cache and the L2s before it is read again. Steps are
-captured in HIP graphs (one graph per replica, plus one graph of all R) and replayed;
-exactly K steps are timed between two synchronisations.
+and step i uses replica i % R; R is chosen so that at least 512 MiB of other data
+(about 64 x 9 MB of decode reads at the default workload) pass between two uses of a
+replica even by one kernel alone, which evicts the 256 MB Infinity Cache and the L2s.
+Steps are captured in HIP graphs: one of the R replicas in turn, one of the W warm-up
+steps and one of exactly the K timed steps. Before timing, the timed graph and the
+replica cycle each run once (whatever W is), then the W warm-up steps, ordered so
+that every replica's last use lies R - 1 steps before its next one; then the timed
+graph runs once between two events (behind a short GPU spin, so that the host's
+submission of the graph does not fall inside the timed region).
 
 Per-kernel durations are measured live with HIP events on the step's stream: each
-kernel is captured R times in a graph of its own (once per replica), and the replays of
-that graph are timed, so the mean includes the dispatch gap between back-to-back launches.
-(The fused scorer's figure is the step time minus the decode kernel's mean: launched
-alone back to back it shows gaps between launches that the step does not have.)
-The roofline entry uses the decode kernel's mean duration and
-its algorithmic bytes (selected visible K/V bytes + Q + O + selection/block-table
-reads). HBM traffic comes from rocprofv3 FETCH_SIZE / WRITE_SIZE counters recorded in
-profiles/ and is reported only while the kernel source is unchanged since then.
-Each duration also carries p10 / p50 / p90 over the replays (each a mean over R
-launches), and the rates are also stated against the read bandwidth a plain streaming
-read of 1 GiB reaches on the same GPU in the same run (`box_read_gbs`).
+kernel is captured R times in a graph of its own (once per replica), and at least 8
+replays of that graph are timed, so the mean includes the dispatch gap between
+back-to-back launches. (The fused scorer's figure is the step time minus the decode
+kernel's mean: launched alone back to back it shows gaps between launches that the
+step does not have.) The roofline entry uses the decode kernel's mean duration and its
+algorithmic bytes (selected visible K/V bytes + Q + O + selection/block-table reads).
+HBM traffic comes from rocprofv3 FETCH_SIZE / WRITE_SIZE counters recorded in
+profiles/ and is reported only while the kernel source is unchanged since then. Each
+duration also carries p10 / p50 / p90 over the replays (each a mean over R launches).
+
+Read references measured in the same run: `read_floor`, a plain kernel that reads the
+step's own selected K/V bytes (each selected block of each KV head once, through the
+page list, in the same replica rotation), and `box_read_gbs`, a streaming read of
+1 GiB. The decode's time is stated as a fraction of both.
 
 The CPU baseline is the float64 oracle on a bounded sample of the same workload, timed
 with numpy's BLAS at one thread (`cpu_baseline`) and at up to 16 (`cpu_baseline_all_cores`).
@@ -42,7 +50,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 WORKLOAD_CFG = 1
-REPLICAS = 16
+MIN_REUSE_BYTES = 512 << 20     # other data moved between two uses of a replica
+MIN_REPLAYS = 8                 # replays behind every percentile
 
 
 def parse():
@@ -51,7 +60,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--num-splits", type=int, default=0, help="0 = library default for k and the number of (row, KV head) pairs")
-    ap.add_argument("--replicas", type=int, default=REPLICAS)
+    ap.add_argument("--replicas", type=int, default=0,
+                    help="pool replicas (0: enough for 512 MiB between reuses, within a 48 GiB budget)")
+    ap.add_argument("--replays", type=int, default=MIN_REPLAYS,
+                    help=f"replays of each per-kernel graph for the durations (at least {MIN_REPLAYS})")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--config", type=int, default=WORKLOAD_CFG, choices=[0, 1, 2, 3, 4],
                     help="workload (1, the default, is the one the metric is quoted on)")
@@ -134,6 +146,59 @@ def decode_algorithmic_bytes(wl, sel, bytes_per_token):
     return kv + qo + meta, tok
 
 
+def selected_units(wl, sel):
+    """The step's selected K/V as read units (physical page, KV head, visible tokens):
+    each selected block of each KV head once per request, with the most tokens any of
+    the request's rows sees in it (the union decode_algorithmic_bytes counts)."""
+    import numpy as np
+    tables = sel.shape[1] if sel.ndim == 3 else 1
+    units = []
+    for s in range(len(wl.ctx_lens)):
+        rows = np.nonzero(wl.row_seq == s)[0]
+        for g in range(wl.num_kv_heads):
+            st = sel[:, g] if tables > 1 else sel
+            vis = {}
+            for r in rows:
+                for b in st[r]:
+                    if b >= 0:
+                        n = min(128, int(wl.row_pos[r]) - 128 * int(b) + 1)
+                        vis[int(b)] = max(vis.get(int(b), 0), n)
+            units += [(int(wl.block_table[s][b]), g, n) for b, n in sorted(vis.items()) if n > 0]
+    return np.asarray(units, dtype=np.int32).reshape(-1, 3)
+
+
+def auto_replicas(wl, pool_bytes, budget=48 << 30):
+    """Pool replicas so that at least MIN_REUSE_BYTES of decode reads alone pass between
+    two uses of a replica (the decode moves the fewest bytes of the step's kernels):
+    1 + 512 MiB / (bytes of k selected blocks per row and KV head), a multiple of 8, at
+    most 512 and within `budget` bytes of device memory."""
+    bpt = 144 if wl.fmt == 2 else 256
+    est = sum(min(int(p) // 128 + 1, wl.k) * 128 for p in wl.row_pos) * wl.num_kv_heads * bpt
+    r = 1 + -(-MIN_REUSE_BYTES // max(est, 1))
+    r = -(-r // 8) * 8
+    return int(max(8, min(r, 512, budget // max(pool_bytes, 1))))
+
+
+def page_read_probe(torch, pools, units, stream):
+    """Launcher of the read-floor probe (libmsaprobe msa_probe_page_read) on one pool."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "sparse_attention_decode_fp8_amd", "libmsaprobe.so"))
+    f = lib.msa_probe_page_read
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32] + [ctypes.c_void_p] * 4 + \
+        [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    dev_units = torch.from_numpy(units).to(pools[0].k_codes.device)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev_units.device)
+
+    def launch(p):
+        st = f(dev_units.data_ptr(), len(units), p.fmt, p.k_codes.data_ptr(), p.v_codes.data_ptr(),
+               p.k_scales.data_ptr(), p.v_scales.data_ptr(), p.num_kv_heads, sink.data_ptr(),
+               torch.cuda.current_stream().cuda_stream)
+        assert st == 0, f"msa_probe_page_read returned {st}"
+    launch.keep = (dev_units, sink)
+    return launch
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -168,7 +233,8 @@ def main():
         M.msa_kv_append(pool0, torch.from_numpy(wl.slots(s, np.arange(L))).to(dev),
                         bf16(wl.k_src[s][:L]), bf16(wl.v_src[s][:L]), bf16(wl.idx_src[s][:L]))
     torch.cuda.synchronize()
-    pools = [pool0] + [pool0.clone() for _ in range(args.replicas - 1)]
+    R = args.replicas or auto_replicas(wl, sum(a.numel() * a.element_size() for a in pool0.arrays().values()))
+    pools = [pool0] + [pool0.clone() for _ in range(R - 1)]
     tables = wl.num_kv_heads if args.per_kv_head else 1
     step = M.Step(wl.block_table, wl.row_seq, wl.row_pos, sel_tables=tables)
     q, q_idx = bf16(wl.q), bf16(wl.q_idx)
@@ -176,7 +242,7 @@ def main():
     sl, kb, vb, ib = wl.step_tokens()
     slot, k_new, v_new, idx_new = torch.from_numpy(sl).to(dev), bf16(kb), bf16(vb), bf16(ib)
     bufs = M.DecodeBuffers(wl.num_rows, wl.num_heads, wl.max_blocks, wl.k, ns, sel_tables=tables)
-    print(f"[bench] {args.replicas} pool replicas ready, splits {ns}", file=sys.stderr, flush=True)
+    print(f"[bench] {R} pool replicas ready, splits {ns}", file=sys.stderr, flush=True)
 
     select_in = args.select_in
     # run_step appends in a launch of its own when a step has this many new tokens
@@ -187,7 +253,9 @@ def main():
                    v_new=v_new, idx_k_new=idx_new, n_init=wl.n_init, n_local=wl.n_local,
                    fused=not args.separate, stream=stream, select_in=select_in)
 
-    # ---- capture: one graph per replica and one graph of all replicas
+    # ---- capture: the replica cycle, the warm-up steps and exactly the K timed steps.
+    # Warm-up step i uses replica (R - W + i) % R, so that it ends right before replica
+    # 0 and every replica's last use before the timed graph lies R - 1 steps back.
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -195,36 +263,57 @@ def main():
             one_step(p)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    graphs = []
-    for p in pools:
+
+    def capture(seq):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            one_step(p)
-        graphs.append(g)
-    g_all = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_all):
-        for p in pools:
-            one_step(p)
+            for i in seq:
+                one_step(pools[i])
+        return g
+
+    g_cycle = capture(range(R))
+    g_warm = capture([(R - args.warmup + i) % R for i in range(args.warmup)]) if args.warmup else None
+    g_timed = capture([i % R for i in range(args.steps)])
     torch.cuda.synchronize()
 
-    def run_steps(n):
-        full, rem = divmod(n, len(pools))
-        for _ in range(full):
-            g_all.replay()
-        for i in range(rem):
-            graphs[i].replay()
-
-    run_steps(args.warmup)
+    g_timed.replay()           # every graph runs once before timing, whatever --warmup is
+    g_cycle.replay()
+    if g_warm is not None:
+        g_warm.replay()
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    # A short spin on the GPU in front of the start event (untimed) keeps the GPU busy
+    # while the host submits the timed graph, so no submission gap lands in the timed
+    # region (at small K it would otherwise add its ~15 us to every step's mean).
+    torch.cuda._sleep(1 << 20)
     ev0.record()
-    run_steps(args.steps)
+    g_timed.replay()
     ev1.record()
     torch.cuda.synchronize()
     ms_total = ev0.elapsed_time(ev1)
     ms_per_step = ms_total / args.steps
     print(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.2f} us/step", file=sys.stderr, flush=True)
+    reps = max(MIN_REPLAYS, args.replays)
+
+    def time_replays(g, per_replay):
+        """Mean duration of one of the `per_replay` launches (or steps) a graph holds,
+        over `reps` back-to-back replays after one untimed replay, and p10 / p50 / p90
+        of the per-replay means."""
+        g.replay()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        torch.cuda._sleep(1 << 20)   # (as for the timed steps: no submission gap inside)
+        ev[0].record()
+        for i in range(reps):
+            g.replay()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        per = np.array([ev[i].elapsed_time(ev[i + 1]) * 1e3 / per_replay for i in range(reps)])
+        return {"mean": ev[0].elapsed_time(ev[reps]) * 1e3 / (reps * per_replay),
+                "p10": float(np.percentile(per, 10)), "p50": float(np.percentile(per, 50)),
+                "p90": float(np.percentile(per, 90)), "launches": reps * per_replay}
+
+    step_us = time_replays(g_cycle, R)   # the spread of the step time over replays
 
     # ---- per-kernel durations: events around each launch, queued behind a GPU sleep
     if args.separate:
@@ -278,25 +367,7 @@ def main():
                 call(p)
         kgraphs.append(g)
     torch.cuda.synchronize()
-    reps = max(1, min(args.steps, 320) // len(pools))
-
-    def time_replays(g):
-        """Mean launch duration over `reps` back-to-back replays of a graph of one
-        launch per replica, and p10 / p50 / p90 of the per-replay means."""
-        g.replay()
-        torch.cuda.synchronize()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
-        ev[0].record()
-        for i in range(reps):
-            g.replay()
-            ev[i + 1].record()
-        torch.cuda.synchronize()
-        per = np.array([ev[i].elapsed_time(ev[i + 1]) * 1e3 / len(pools) for i in range(reps)])
-        return {"mean": ev[0].elapsed_time(ev[reps]) * 1e3 / (reps * len(pools)),
-                "p10": float(np.percentile(per, 10)), "p50": float(np.percentile(per, 50)),
-                "p90": float(np.percentile(per, 90)), "launches": reps * len(pools)}
-
-    per_kernel_us = {nm: time_replays(g) for nm, g in zip(names, kgraphs)}
+    per_kernel_us = {nm: time_replays(g, R) for nm, g in zip(names, kgraphs)}
 
     # The table-driven decode entry alone (msa_sparse_decode on the selection the fused
     # step wrote; partials only), timed the same way: the kernel the decode target names.
@@ -307,12 +378,23 @@ def main():
             for p in pools:
                 M.msa_sparse_decode(p, step, q, bufs.sel, wl.k, wl.softmax_scale, ns, bufs.part_o,
                                     bufs.part_ml, sel_pages=bufs.sel_pages)
-        sd = time_replays(g)
+        sd = time_replays(g, R)
         sd_us = sd["mean"]
 
     sel = bufs.sel.cpu().numpy()
     bpt = 144 if wl.fmt == W.FMT_NVFP4 else 256
     dec_bytes, dec_tokens = decode_algorithmic_bytes(wl, sel, bpt)
+
+    # The read floor: the same selected K/V bytes read by a plain kernel through the page
+    # list, one launch per replica in the same rotation, timed like the kernels above.
+    units = selected_units(wl, sel)
+    probe = page_read_probe(torch, pools, units, None)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for p in pools:
+            probe(p)
+    floor = time_replays(g, R)
+    floor_bytes = int(units[:, 2].sum()) * bpt + (8 * len(units) if wl.fmt == W.FMT_FP8 else 0)
     key_bytes = 64 if wl.index_fmt == W.IDX_E4M3 else 32 + 4        # per token: codes (+ scales)
     # every visible index key once per request (its rows are scored together)
     last = {}
@@ -377,14 +459,17 @@ def main():
                    "appended_tokens": wl.n_append, "top_k": wl.k, "kv_format": "nvfp4" if wl.fmt == W.FMT_NVFP4 else "fp8",
                    "num_splits": ns, "selection": "per KV head" if tables > 1 else "per query row",
                    "select_in": "separate launch" if args.separate else select_in,
-                   "pool_replicas": args.replicas, "parallelism": "single GPU"},
+                   "pool_replicas": R, "reuse_distance_decode_bytes": (R - 1) * dec_bytes,
+                   "parallelism": "single GPU"},
+        "step_us": step_us,
         "roofline": {"kernel": "+".join(decode_kernels), "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes": dec_bytes,
                      "visible_selected_tokens": dec_tokens, "mean_us": t_dec * 1e6,
                      **({f"{q}_us": per_kernel_us[decode_kernels[0]][q] for q in ("p10", "p50", "p90")}
                         if len(decode_kernels) == 1 else {}),
-                     "frac_of_box_read": None if box_read is None else achieved / box_read},
+                     "frac_of_box_read": None if box_read is None else achieved / box_read,
+                     "frac_of_read_floor": floor["mean"] / (t_dec * 1e6)},
         "index_score_roofline": {"kernel": "msa_index_score" if args.separate or app_sep else names[0],
                                  "bound": "hbm", "achieved": idx_bytes / t_idx / 1e9,
                                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -397,7 +482,16 @@ def main():
             "algorithmic_bytes": dec_bytes, "mean_us": sd_us,
             "p10_us": sd["p10"], "p50_us": sd["p50"], "p90_us": sd["p90"],
             "frac_of_box_read": None if box_read is None else dec_bytes / (sd_us * 1e-6) / 1e9 / box_read,
+            "frac_of_read_floor": floor["mean"] / sd_us,
             "method": "the table-driven entry alone on the step's selection (partials, no merge)"},
+        "read_floor": {"kernel": "msa_probe_page_read", "bytes": floor_bytes, "units": int(len(units)),
+                       "mean_us": floor["mean"], "p10_us": floor["p10"], "p50_us": floor["p50"],
+                       "p90_us": floor["p90"], "gbs": floor_bytes / (floor["mean"] * 1e-6) / 1e9,
+                       "frac_of_peak": floor_bytes / (floor["mean"] * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                       "method": "the step's selected K/V bytes (each selected block of each KV head "
+                                 "once, its visible tokens) read cold through the page list by a plain "
+                                 "kernel, one workgroup per block, one launch per replica in the step's "
+                                 "rotation; frac_of_read_floor = its mean time / the decode's"},
         "box_read_gbs": box_read,
         "kernel_us": per_kernel_us,
         "cpu_baseline": cpu,

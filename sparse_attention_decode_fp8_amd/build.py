@@ -5,7 +5,8 @@
 Every HIP source is compiled to an object with `hipcc --offload-arch=gfx950`, then
 linked into sparse_attention_decode_fp8_amd/libmsadecode.so next to this file; the same
 sources built with -DMSA_DEBUG_CHECKS (device-side metadata checks) into
-libmsadecode_debug.so; and the bench's read-bandwidth reference into libmsaprobe.so.
+libmsadecode_debug.so; and the bench's read references (a streaming read and a read of
+the step's selected pages) into libmsaprobe.so.
 """
 from __future__ import annotations
 
@@ -25,9 +26,9 @@ LIB = os.path.join(PKG, "libmsadecode.so")
 DEBUG_LIB = os.path.join(PKG, "libmsadecode_debug.so")
 SOURCES = ["kv_append.hip", "index_score.hip", "select_topk.hip", "sparse_decode.hip",
            "combine.hip", "api.cpp"]
-# The bench's read-bandwidth reference, a library of its own (not part of the decode path).
+# The bench's read references, a library of their own (not part of the decode path).
 PROBE_LIB = os.path.join(PKG, "libmsaprobe.so")
-PROBE_SOURCES = ["stream_read.hip"]
+PROBE_SOURCES = ["stream_read.hip", "page_read.hip"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
           "-Wall", "-Wno-unused-function"]

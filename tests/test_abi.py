@@ -50,6 +50,8 @@ def test_debug_library_exports_the_same_entry_points_and_its_setter():
     assert rel.msa_debug_set_error_word(ctypes.c_void_p(16)) == -2
     assert dbg.msa_debug_set_error_word(ctypes.c_void_p(16)) == 0
     assert dbg.msa_debug_set_error_word(None) == 0
+    assert rel.msa_debug_set_merge_poll_limit(0) == -2
+    assert dbg.msa_debug_set_merge_poll_limit(0) == 0 and dbg.msa_debug_set_merge_poll_limit(-1) == 0
     # host-side validation is the same in both builds
     B, P = ctypes.byref, ctypes.c_void_p
     pool, step = _fake_pool(), _fake_step()
@@ -59,8 +61,8 @@ def test_debug_library_exports_the_same_entry_points_and_its_setter():
 
 
 def test_read_probe_library_loads_and_validates():
-    """The bench's streaming-read reference (libmsaprobe.so) exports its one entry and
-    rejects bad arguments before any launch."""
+    """The bench's read references (libmsaprobe.so: a streaming read and a read of the
+    step's selected pages) are exported and reject bad arguments before any launch."""
     lib = ctypes.CDLL(os.path.join(os.path.dirname(L.LIB_PATH), "libmsaprobe.so"))
     f = lib.msa_probe_stream_read
     f.restype = ctypes.c_int
@@ -71,6 +73,16 @@ def test_read_probe_library_loads_and_validates():
     assert f(16, 16, 16, 0, None) == -1              # no workgroups
     assert f(8, 16, 16, 1, None) == -1               # misaligned
     assert f(16, 0, 16, 1, None) == 0                # nothing to read: no launch
+    g = lib.msa_probe_page_read                      # the bench's page-list read floor
+    g.restype = ctypes.c_int
+    g.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32] + [ctypes.c_void_p] * 4 + \
+        [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    assert g(16, -1, 2, 16, 16, 16, 16, 4, 16, None) == -1   # negative unit count
+    assert g(16, 1, 3, 16, 16, 16, 16, 4, 16, None) == -1    # unknown format
+    assert g(16, 1, 2, 16, 16, 16, 16, 0, 16, None) == -1    # no KV heads
+    assert g(16, 1, 2, None, 16, 16, 16, 4, 16, None) == -1  # null array
+    assert g(16, 1, 2, 16, 16, 16, 16, 4, None, None) == -1  # null sink
+    assert g(None, 0, 2, 16, 16, 16, 16, 4, 16, None) == 0   # nothing to read: no launch
 
 
 def test_binding_names_match_c_entry_points():

@@ -54,3 +54,33 @@ def test_algorithmic_bytes_count_the_union_per_request_and_kv_head():
     head1 = (128 + 46) + 128               # blocks {1, 2} of request 0, block 0 of request 1
     assert total3 == (head0 + head1) * 144 + qo + sel3.size * 4 + int((sel3 >= 0).sum()) * 4
     assert tok3 == (head0 + head1) // 2
+
+
+def test_read_floor_units_are_the_union_per_request_and_kv_head():
+    B = _bench()
+    wl = types.SimpleNamespace(ctx_lens=np.array([300, 127]), row_seq=np.array([0, 0, 1]),
+                               row_pos=np.array([300, 301, 127]), num_kv_heads=2, num_rows=3, num_heads=32,
+                               block_table=np.array([[7, 3, 9], [5, -1, -1]], dtype=np.int32))
+    sel = np.array([[0, 2], [1, 2], [0, -1]], dtype=np.int32)
+    u = B.selected_units(wl, sel)
+    want = [(7, 0, 128), (3, 0, 128), (9, 0, 46), (7, 1, 128), (3, 1, 128), (9, 1, 46), (5, 0, 128), (5, 1, 128)]
+    assert sorted(map(tuple, u.tolist())) == sorted(want)
+    # the units hold exactly the tokens the algorithmic bytes count, per KV head
+    total, tok = B.decode_algorithmic_bytes(wl, sel, 144)
+    assert int(u[:, 2].sum()) == tok * 2
+    sel3 = np.array([[[0, 2], [1, 2]], [[1, 2], [1, 2]], [[0, -1], [0, -1]]], dtype=np.int32)
+    u3 = B.selected_units(wl, sel3)
+    assert sorted(map(tuple, u3.tolist())) == sorted([(7, 0, 128), (3, 0, 128), (9, 0, 46), (3, 1, 128),
+                                                      (9, 1, 46), (5, 0, 128), (5, 1, 128)])
+
+
+def test_auto_replicas_put_512_mib_between_reuses():
+    B = _bench()
+    # 8 rows of 32769 tokens, k 16, 4 KV heads, NVFP4: 9.44 MB of decode reads per step
+    wl = types.SimpleNamespace(fmt=2, k=16, num_kv_heads=4, row_pos=np.full(8, 32768))
+    est = 8 * 16 * 128 * 4 * 144
+    r = B.auto_replicas(wl, 169 << 20)
+    assert r % 8 == 0 and (r - 1) * est >= 512 << 20 and r == 64
+    assert B.auto_replicas(wl, 1 << 30) == 48            # 48 GiB budget
+    wl0 = types.SimpleNamespace(fmt=1, k=8, num_kv_heads=1, row_pos=np.array([4095]))
+    assert B.auto_replicas(wl0, 2 << 20) == 512          # capped
