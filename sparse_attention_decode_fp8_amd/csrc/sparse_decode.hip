@@ -35,6 +35,11 @@
 // early in the call. The selecting variant runs the top-k selection of its row in
 // every workgroup (the scores are 4 bytes per block), which costs less than a launch
 // plus a cross-workgroup handoff.
+//
+// Page data is read through buffer resources based at each selected (page, KV head):
+// every chunk issues the same loads (an empty one from a zero-byte resource, which
+// returns zeros without a memory access), so the query's conversion and everything
+// else that waits on earlier loads does not wait for the page data.
 #include <algorithm>
 
 #include "msa_device.h"
@@ -105,31 +110,43 @@ struct ChunkRegs<MSA_KV_FP8_E4M3> {
   uint4 k[4], v[4];        // [tile * 2 + half]: 32 E4M3 codes
 };
 
+// Loads of one 32-token chunk (chunk c of the page's 128 tokens) of one (page, KV head)
+// through buffer resources whose base is that (page, head)'s region of each array (a
+// wave-uniform address: the page comes from the selection table in scalar registers).
+// An empty chunk (valid = false) gets resources of zero bytes: its loads return zero
+// without touching memory, and every chunk issues the same loads, so the compiler
+// knows how many are in flight and can consume earlier loads (Q) without waiting for
+// the page data.
 template <int kFmt>
-__device__ __forceinline__ void load_chunk(ChunkRegs<kFmt>& R, const DecodeArgs& a, int64_t page,
-                                           int g, int c, int n, int q) {
-  const int64_t tok0 = (page * a.hkv + g) * kPage + 32 * c + n;
+__device__ __forceinline__ void load_chunk(ChunkRegs<kFmt>& R, const DecodeArgs& a, int64_t ph, bool valid,
+                                           int c, int n, int q) {
+  const uint32_t t0 = 32u * c + n;   // this lane's token in tile 0; tile 1 is 16 tokens on
   if constexpr (kFmt == MSA_KV_NVFP4) {
-    const uint8_t* kc = a.k_codes + tok0 * (kHeadDim / 2) + 16 * q;
-    const uint8_t* vc = a.v_codes + tok0 * (kHeadDim / 2) + 16 * q;
-    const uint8_t* kss = a.k_scales + tok0 * (kHeadDim / 16) + 2 * q;
-    const uint8_t* vss = a.v_scales + tok0 * (kHeadDim / 16) + 2 * q;
+    constexpr uint32_t kCodeBytes = kPage * kHeadDim / 2, kScaleBytes = kPage * kHeadDim / 16;
+    const __amdgpu_buffer_rsrc_t kc = make_rsrc(uniform_ptr(a.k_codes + ph * kCodeBytes), valid ? kCodeBytes : 0u);
+    const __amdgpu_buffer_rsrc_t vc = make_rsrc(uniform_ptr(a.v_codes + ph * kCodeBytes), valid ? kCodeBytes : 0u);
+    const __amdgpu_buffer_rsrc_t ks = make_rsrc(uniform_ptr(a.k_scales + ph * kScaleBytes), valid ? kScaleBytes : 0u);
+    const __amdgpu_buffer_rsrc_t vs = make_rsrc(uniform_ptr(a.v_scales + ph * kScaleBytes), valid ? kScaleBytes : 0u);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      R.k[u] = *reinterpret_cast<const uint4*>(kc + u * 16 * (kHeadDim / 2));
-      R.v[u] = *reinterpret_cast<const uint4*>(vc + u * 16 * (kHeadDim / 2));
-      R.ks[u] = *reinterpret_cast<const uint16_t*>(kss + u * 16 * (kHeadDim / 16));
-      R.vs[u] = *reinterpret_cast<const uint16_t*>(vss + u * 16 * (kHeadDim / 16));
+      const uint32_t t = t0 + 16u * u;
+      R.k[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kc, static_cast<int>(t * (kHeadDim / 2) + 16 * q), 0, 0));
+      R.v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vc, static_cast<int>(t * (kHeadDim / 2) + 16 * q), 0, 0));
+      R.ks[u] = __builtin_amdgcn_raw_buffer_load_b16(ks, static_cast<int>(t * (kHeadDim / 16) + 2 * q), 0, 0);
+      R.vs[u] = __builtin_amdgcn_raw_buffer_load_b16(vs, static_cast<int>(t * (kHeadDim / 16) + 2 * q), 0, 0);
     }
   } else {
-    const uint8_t* kc = a.k_codes + tok0 * kHeadDim + 32 * q;
-    const uint8_t* vc = a.v_codes + tok0 * kHeadDim + 32 * q;
+    constexpr uint32_t kCodeBytes = kPage * kHeadDim;
+    const __amdgpu_buffer_rsrc_t kc = make_rsrc(uniform_ptr(a.k_codes + ph * kCodeBytes), valid ? kCodeBytes : 0u);
+    const __amdgpu_buffer_rsrc_t vc = make_rsrc(uniform_ptr(a.v_codes + ph * kCodeBytes), valid ? kCodeBytes : 0u);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      R.k[2 * u] = *reinterpret_cast<const uint4*>(kc + u * 16 * kHeadDim);
-      R.k[2 * u + 1] = *reinterpret_cast<const uint4*>(kc + u * 16 * kHeadDim + 16);
-      R.v[2 * u] = *reinterpret_cast<const uint4*>(vc + u * 16 * kHeadDim);
-      R.v[2 * u + 1] = *reinterpret_cast<const uint4*>(vc + u * 16 * kHeadDim + 16);
+      const uint32_t t = t0 + 16u * u;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        R.k[2 * u + h] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kc, static_cast<int>(t * kHeadDim + 32 * q + 16 * h), 0, 0));
+        R.v[2 * u + h] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vc, static_cast<int>(t * kHeadDim + 32 * q + 16 * h), 0, 0));
+      }
     }
   }
 }
@@ -157,39 +174,35 @@ struct Round {
 
 // Issue every load of one round: chunk `it = round + wave + j * kW` of this split is
 // entry lo + it / 4, 32-token chunk it % 4. `lookup(e, b, page)` gives the logical
-// block and physical page of selection entry e (b < 0: empty entry).
+// block and physical page of selection entry e (b < 0: empty entry). Chunks past the
+// split, of empty entries or with no visible token issue the same loads from
+// zero-byte resources (see load_chunk).
 template <int kFmt, int kW, int kItems, class Lookup>
 __device__ __forceinline__ void load_round(Round<kFmt, kItems>& rd, const DecodeArgs& a,
                                            const Lookup& lookup, int round, int wave, int g,
                                            int pos, int lo, int n_items, int n, int q) {
-  int64_t pages[kItems];
+  // The row position, block and page are the same in every lane; reading them through
+  // readfirstlane tells the compiler so, and the buffer resources below stay in scalar
+  // registers (a resource it cannot prove uniform costs a loop over lanes per load).
+  const int upos = __builtin_amdgcn_readfirstlane(pos);
 #pragma unroll
   for (int j = 0; j < kItems; ++j) {
     const int it = round + wave + j * kW;
-    rd.nvis[j] = 0;
-    pages[j] = 0;
-    if (it < n_items) {
-      const int e = lo + (it >> 2), c = it & 3;
-      int b;
-      int64_t page;
-      lookup(e, b, page);
-      const int nv = min(pos - b * kPage + 1, kPage) - 32 * c;   // visible tokens in the chunk
-      if (b >= 0 && nv > 0) {
-        rd.nvis[j] = min(nv, 32);
-        page = checked_page(page, a.num_pages, a.err);
-        pages[j] = page;
-        load_chunk<kFmt>(rd.R[j], a, page, g, c, n, q);
-      }
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < kItems; ++j) {
+    const int e = lo + min(it, n_items - 1) / 4, c = it & 3;
+    int b;
+    int64_t page;
+    lookup(e, b, page);
+    b = __builtin_amdgcn_readfirstlane(b);
+    const int nv = min(upos - b * kPage + 1, kPage) - 32 * c;   // visible tokens in the chunk
+    const bool valid = it < n_items && b >= 0 && nv > 0;
+    rd.nvis[j] = valid ? min(nv, 32) : 0;
+    page = valid ? checked_page(page, a.num_pages, a.err) : 0;
+    page = static_cast<int64_t>(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(page))));
+    load_chunk<kFmt>(rd.R[j], a, page * a.hkv + g, valid, c, n, q);
     rd.kps[j] = rd.vps[j] = 1.0f;
-    if constexpr (kFmt == MSA_KV_FP8_E4M3) {
-      if (rd.nvis[j] > 0) {
-        rd.kps[j] = reinterpret_cast<const float*>(a.k_scales)[pages[j]];
-        rd.vps[j] = reinterpret_cast<const float*>(a.v_scales)[pages[j]];
-      }
+    if constexpr (kFmt == MSA_KV_FP8_E4M3) {   // the page's scales (page 0 for an empty chunk)
+      rd.kps[j] = reinterpret_cast<const float*>(a.k_scales)[page];
+      rd.vps[j] = reinterpret_cast<const float*>(a.v_scales)[page];
     }
   }
 }
@@ -264,7 +277,10 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
   const int pair = blockIdx.y, s = blockIdx.x;   // (row, KV head) pair, split
   if (pair >= a.num_rows * a.hkv) return;
   const int r = pair / a.hkv, g = pair % a.hkv;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
+  // (the wave index through readfirstlane: the compiler then knows it is the same in
+  // every lane, and so is everything derived from it, such as a chunk's page)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
   const int hq = a.hkv * kHeadsPerKv;
   const int lo = (s * a.k) / a.num_splits, hi = ((s + 1) * a.k) / a.num_splits;
   const int n_items = (hi - lo) * 4;   // (entry, 32-token chunk) pairs of this split
@@ -449,16 +465,30 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
         v_cur = rd.vps[j];
       }
       // ---- scores of 32 tokens for 16 heads
-      float x[2][4];
+      float4_t acc[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        acc[u] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
-          acc = mfma16x16x32(dequant8<kFmt>(rd.R[j].k, ksc, u, kk), Qop[kk], acc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[u][i] = (16 * u + 4 * q + i) < rd.nvis[j] ? acc[i] * cs : -INFINITY;
+          acc[u] = mfma16x16x32(dequant8<kFmt>(rd.R[j].k, ksc, u, kk), Qop[kk], acc[u]);
       }
+      // ---- V chunk to LDS (natural [token][d] layout, fp16). It does not depend on the
+      // scores, so its dequantisation runs while the matrix core computes them. (A wave's
+      // LDS accesses execute in order, so the transposing reads below see these writes
+      // without a wait; the empty asm only keeps the compiler from reordering them.)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          *reinterpret_cast<half8_t*>(vb + (16 * u + n) * kVRowHalves + 32 * q + 8 * kk) =
+              dequant8<kFmt>(rd.R[j].v, vsc, u, kk);
+      asm volatile("" ::: "memory");
+      float x[2][4];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[u][i] = (16 * u + 4 * q + i) < rd.nvis[j] ? acc[u][i] * cs : -INFINITY;
       // ---- online softmax (per lane: one head)
       float mx = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
                        fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
@@ -482,14 +512,7 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
       }
       l_run = l_run * alpha + psum;
       m_run = m_new;
-      // ---- V chunk to LDS (natural [token][d] layout, fp16), then O^T += V^T . P^T
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          *reinterpret_cast<half8_t*>(vb + (16 * u + n) * kVRowHalves + 32 * q + 8 * kk) =
-              dequant8<kFmt>(rd.R[j].v, vsc, u, kk);
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      // ---- O^T += V^T . P^T
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
         const half_t* p0 = vb + (4 * q + (n >> 2)) * kVRowHalves + 16 * d + 4 * (n & 3);
@@ -499,7 +522,7 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
         const half8_t Vt = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
         O[d] = mfma16x16x32(Vt, Pt, O[d]);
       }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      asm volatile("" ::: "memory");   // (the next chunk's V writes stay behind these reads)
     }
   }
 
@@ -671,24 +694,31 @@ void launch(const DecodeArgs& a, dim3 grid, hipStream_t s) {
 }
 
 // Waves per workgroup for a split of `per_split` pages, one chunk per wave and round:
-// up to 16 waves for one round. Longer splits take rounds: of 8 chunks, which keeps the
-// registers low enough for two workgroups per compute unit where the variant allows, or,
-// with one split and fewer workgroups than the 256 compute units, of 16 chunks (more
-// waves per compute unit; with several splits the merging variant would spill). Several
-// chunks per wave and round measured slower: fewer waves hide less of each chunk's
-// latency. The choice depends only on k, the split count and the launch size, so every
-// output variant of a call shape computes its partials in the same order (the merged
-// and direct outputs equal the partials + msa_combine bit for bit). The selecting
-// variant needs at least 4 waves (its selection uses 256 threads or more).
+// 4 waves for one page, 8 for two. Longer splits take rounds of 8 chunks, which keeps
+// the registers low enough for two workgroups per compute unit where the variant
+// allows, or, with one split, of 16 chunks (one round for up to four pages, or more
+// waves per compute unit when the launch has fewer workgroups than the 256 compute
+// units); with several splits 16 waves would leave the merging variant 128 registers
+// and make it spill. Several chunks per wave and round measured slower: fewer waves
+// hide less of each chunk's latency. The choice depends only on k, the split count and
+// the launch size, so every output variant of a call shape computes its partials in
+// the same order (the merged and direct outputs equal the partials + msa_combine bit
+// for bit). The selecting variant needs at least 4 waves (its selection uses 256
+// threads or more).
 template <int kFmt, int kOut, int kSelect>
 msa_status_t dispatch(const DecodeArgs& a, dim3 grid, hipStream_t s) {
   const int per_split = (a.k + a.num_splits - 1) / a.num_splits;
   const int chunks = 4 * per_split;
-  const bool rounds16 = a.num_splits == 1 && static_cast<int64_t>(grid.x) * grid.y < 256;
+  const bool one = a.num_splits == 1;
+  const bool rounds16 = one && (chunks <= 16 || static_cast<int64_t>(grid.x) * grid.y < 256);
   if (chunks <= 4) launch<kFmt, 4, 1, kOut, kSelect>(a, grid, s);
   else if (chunks <= 8) launch<kFmt, 8, 1, kOut, kSelect>(a, grid, s);
-  else if (chunks <= 16 || rounds16) launch<kFmt, 16, 1, kOut, kSelect>(a, grid, s);
-  else launch<kFmt, 8, 1, kOut, kSelect>(a, grid, s);   // rounds of 8 chunks
+  else if (rounds16) {
+    if constexpr (kOut != kOutMerged) launch<kFmt, 16, 1, kOut, kSelect>(a, grid, s);
+    else return MSA_ERR_UNSUPPORTED;   // (never: one split writes its output directly)
+  } else {
+    launch<kFmt, 8, 1, kOut, kSelect>(a, grid, s);   // rounds of 8 chunks
+  }
   return launch_status();
 }
 
