@@ -1,13 +1,16 @@
-// Block-level (256-thread) deterministic top-k block selection for one query row,
-// shared by msa_select_topk and the fused score-and-select kernel.
+// Deterministic top-k block selection for one query row, shared by msa_select_topk,
+// the fused score-and-select kernel and the selecting decode:
+//   block_select_row     256+ threads, radix select over LDS histograms (any length)
+//   wave_select_table    one wave, threshold search over the keys it holds (<= 2048)
+//   multiwave_select_*   several waves of a workgroup, two levels (the selecting decode)
 //
 // Contract ([Rubin] commit messages: ascending, -1-padded table with init / local
 // forcing; [GB300] "The TP4 decode target", numerics: ties to the smaller block):
 // rows with nb <= k select 0..nb-1; otherwise the n_init first and n_local last blocks
 // are forced and the other k - n_init - n_local slots go to the best remaining blocks by
-// (score desc, index asc). The want-th largest score is found by an MSB-first radix
-// select over order-preserving uint32 keys (LDS histograms: counts do not depend on
-// atomic order), and blocks tied at that score are ranked by a scan in block order.
+// (score desc, index asc). Every variant finds the exact want-th largest order-
+// preserving key and ranks the blocks tied at it in block order, so none depends on the
+// order in which atomics land.
 #pragma once
 
 #include "msa_device.h"
@@ -42,7 +45,9 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* lds_tmp) {
   return base + x - v;
 }
 
-// Select for one row. All kThreads (>= 256, a multiple of 64) threads must call it. `srow` is the row's score array
+// Radix select for one row: the want-th largest key by an MSB-first radix select over
+// LDS histograms, then the blocks tied at it ranked by a scan in block order.
+// All kThreads (>= 256, a multiple of 64) threads must call it. `srow` is the row's score array
 // (index = block), `bt` the request's block-table row, `out`/`outp` the row's k-entry
 // outputs (outp may be null), `keys` LDS scratch of at least nb - n_init - n_local
 // entries. kCoherent: read the scores with agent-coherent loads (they were written by
@@ -164,84 +169,31 @@ __device__ void block_select_row(const float* srow, int nb, int k, int n_init, i
 
 namespace msa {
 
-// Wave-level (64-lane) selection for one row, without barriers or LDS atomics. Lane L
-// holds candidates L*kR .. L*kR+kR-1 (block lo + c), so block order is lane-major.
+// Exact top `want` of the keys a wave holds, kR per lane in candidate order lane-major
+// (lane L holds candidates L*kR .. L*kR+kR-1): take[i] marks the chosen keys, those above
+// the want-th largest key T and, of the keys equal to T, the first ones in candidate
+// order; `before` counts the chosen keys in earlier lanes. Key 0 marks an empty slot
+// (below every real key); if there are no more than `want` real keys, all are taken.
 //
-// The want-th largest key T is built two bits at a time from the highest bit in which
-// the candidates differ (three independent ballot + popcount counts per step). Keys
-// above T are taken, and of the keys equal to T the ones with the smallest block
-// index (rank by mbcnt prefix counts).
-//
-// The scores and the block-table row are read for every candidate slot inside the
-// row's max_blocks before the row's position (and so its length) is read, so all three
-// loads overlap. The table is written to LDS: entry e (block, and its page from `bt`)
-// at sel[e], pages[e] for e < 64, -1 past the k entries; the caller synchronises the
-// workgroup before reading it.
+// T is built two bits at a time from the highest bit in which the candidates differ
+// (three independent counts per step); ties at T are ranked with mbcnt prefix counts.
+// No barriers, no LDS.
 template <int kR>
-__device__ __forceinline__ void wave_select_table(const float* srow, const int32_t* bt, int max_blocks,
-                                                  const int32_t* row_pos, int k, int n_init, int n_local,
-                                                  int* sel, int* pages) {
-  const int lane = threadIdx.x & 63;
-  const int lo = n_init, want = k - n_init - n_local;
-  float sv[kR];
-  int32_t pg[kR];
+__device__ __forceinline__ void wave_topk(const uint32_t (&key)[kR], int want, bool (&take)[kR], int& before) {
+  int n_real = 0;
 #pragma unroll
-  for (int i = 0; i < kR; ++i) {
-    const int c = lane * kR + i;
-    const bool in_row = lo + c < max_blocks;
-    sv[i] = in_row ? srow[lo + c] : 0.0f;
-    pg[i] = in_row ? bt[lo + c] : -1;
-  }
-  const int32_t pg_init = lane < n_init && lane < max_blocks ? bt[lane] : -1;   // blocks below lo
-  // Slots 64 kR .. 64 kR + 63 past the keys hold only forced last blocks (n_local <= 64):
-  // their pages are read now too, so no block-table read waits for the row's length.
-  const int32_t pg_tail = lo + 64 * kR + lane < max_blocks ? bt[lo + 64 * kR + lane] : -1;
-  // The row's position is read only now, so its load queues behind the score loads
-  // instead of holding them back.
-  asm volatile("" ::: "memory");
-  const int nb = min(*row_pos / MSA_PAGE_SIZE + 1, max_blocks);
-  const int C = nb - n_init - n_local;
-  uint32_t key[kR];
-#pragma unroll
-  for (int i = 0; i < kR; ++i) key[i] = lane * kR + i < C ? float_key(sv[i]) : 0u;   // 0: below every real key
-  // Pages come from the registers loaded above (block lo + c is in slot c), so writing
-  // the table never waits for another block-table read.
-  if (nb <= k) {                                           // identity table
-    if (lane < lo && lane < nb) { sel[lane] = lane; pages[lane] = pg_init; }
+  for (int i = 0; i < kR; ++i) n_real += __popcll(__ballot(key[i] != 0u));
+  if (n_real <= want) {                                   // every real key
+    int b = 0;
 #pragma unroll
     for (int i = 0; i < kR; ++i) {
-      const int b = lo + lane * kR + i;
-      if (b < nb) { sel[b] = b; pages[b] = pg[i]; }
+      take[i] = key[i] != 0u;
+      const uint64_t m = __ballot(take[i]);
+      b += __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
     }
-    if (lane >= nb) { sel[lane] = -1; pages[lane] = -1; }
+    before = b;
     return;
   }
-  // Forced entries and padding; the `want` entries in between come from the search.
-  // Lane j < n_local takes the page of block nb - n_local + j from the lane holding its
-  // slot c (lane c / kR, register c % kR, or the tail registers past 64 kR).
-  int32_t pg_local = -1;
-  {
-    const int c = nb - n_local + min(lane, n_local - 1) - lo;   // 0 <= c < 64 kR + 64
-    const bool tail = c >= 64 * kR;
-    const int src = tail ? c - 64 * kR : c / kR;
-#pragma unroll
-    for (int i = 0; i < kR; ++i) {
-      const int32_t v = __shfl(pg[i], src, 64);
-      if (!tail && c % kR == i) pg_local = v;
-    }
-    const int32_t v = __shfl(pg_tail, src, 64);
-    if (tail) pg_local = v;
-  }
-  if (lane < n_init) { sel[lane] = lane; pages[lane] = pg_init; }
-  if (lane >= k) { sel[lane] = -1; pages[lane] = -1; }
-  auto write_local = [&]() {
-    if (lane < n_local) { sel[k - n_local + lane] = nb - n_local + lane; pages[k - n_local + lane] = pg_local; }
-  };
-  if (want == 0) {
-    write_local();
-    return;
-  }
-
   // Ties at the largest key (want or more candidates share it): that key is the
   // threshold, without a bit-by-bit search that could never stop early.
   uint32_t k_max = 0u;
@@ -348,14 +300,13 @@ __device__ __forceinline__ void wave_select_table(const float* srow, const int32
     }
   }
   const int need = want - gt;                            // keys equal to T to take
-  bool take[kR];
   int tb = tie_before;
 #pragma unroll
   for (int i = 0; i < kR; ++i) {
     take[i] = key[i] > T || (key[i] == T && tb < need);
     tb += key[i] == T;
   }
-  int before = 0;   // taken keys in earlier lanes
+  before = 0;   // taken keys in earlier lanes
   if constexpr (kLaneCount) {
     uint32_t m = 0u;
 #pragma unroll
@@ -369,6 +320,89 @@ __device__ __forceinline__ void wave_select_table(const float* srow, const int32
                                           __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
     }
   }
+}
+
+// Wave-level (64-lane) selection for one row, without barriers or LDS atomics. Lane L
+// holds candidates L*kR .. L*kR+kR-1 (block lo + c), so block order is lane-major.
+//
+// The want-th largest key T is built two bits at a time from the highest bit in which
+// the candidates differ (three independent ballot + popcount counts per step). Keys
+// above T are taken, and of the keys equal to T the ones with the smallest block
+// index (rank by mbcnt prefix counts).
+//
+// The scores and the block-table row are read for every candidate slot inside the
+// row's max_blocks before the row's position (and so its length) is read, so all three
+// loads overlap. The table is written to LDS: entry e (block, and its page from `bt`)
+// at sel[e], pages[e] for e < 64, -1 past the k entries; the caller synchronises the
+// workgroup before reading it.
+template <int kR>
+__device__ __forceinline__ void wave_select_table(const float* srow, const int32_t* bt, int max_blocks,
+                                                  const int32_t* row_pos, int k, int n_init, int n_local,
+                                                  int* sel, int* pages) {
+  const int lane = threadIdx.x & 63;
+  const int lo = n_init, want = k - n_init - n_local;
+  float sv[kR];
+  int32_t pg[kR];
+#pragma unroll
+  for (int i = 0; i < kR; ++i) {
+    const int c = lane * kR + i;
+    const bool in_row = lo + c < max_blocks;
+    sv[i] = in_row ? srow[lo + c] : 0.0f;
+    pg[i] = in_row ? bt[lo + c] : -1;
+  }
+  const int32_t pg_init = lane < n_init && lane < max_blocks ? bt[lane] : -1;   // blocks below lo
+  // Slots 64 kR .. 64 kR + 63 past the keys hold only forced last blocks (n_local <= 64):
+  // their pages are read now too, so no block-table read waits for the row's length.
+  const int32_t pg_tail = lo + 64 * kR + lane < max_blocks ? bt[lo + 64 * kR + lane] : -1;
+  // The row's position is read only now, so its load queues behind the score loads
+  // instead of holding them back.
+  asm volatile("" ::: "memory");
+  const int nb = min(*row_pos / MSA_PAGE_SIZE + 1, max_blocks);
+  const int C = nb - n_init - n_local;
+  uint32_t key[kR];
+#pragma unroll
+  for (int i = 0; i < kR; ++i) key[i] = lane * kR + i < C ? float_key(sv[i]) : 0u;   // 0: below every real key
+  // Pages come from the registers loaded above (block lo + c is in slot c), so writing
+  // the table never waits for another block-table read.
+  if (nb <= k) {                                           // identity table
+    if (lane < lo && lane < nb) { sel[lane] = lane; pages[lane] = pg_init; }
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+      const int b = lo + lane * kR + i;
+      if (b < nb) { sel[b] = b; pages[b] = pg[i]; }
+    }
+    if (lane >= nb) { sel[lane] = -1; pages[lane] = -1; }
+    return;
+  }
+  // Forced entries and padding; the `want` entries in between come from the search.
+  // Lane j < n_local takes the page of block nb - n_local + j from the lane holding its
+  // slot c (lane c / kR, register c % kR, or the tail registers past 64 kR).
+  int32_t pg_local = -1;
+  {
+    const int c = nb - n_local + min(lane, n_local - 1) - lo;   // 0 <= c < 64 kR + 64
+    const bool tail = c >= 64 * kR;
+    const int src = tail ? c - 64 * kR : c / kR;
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+      const int32_t v = __shfl(pg[i], src, 64);
+      if (!tail && c % kR == i) pg_local = v;
+    }
+    const int32_t v = __shfl(pg_tail, src, 64);
+    if (tail) pg_local = v;
+  }
+  if (lane < n_init) { sel[lane] = lane; pages[lane] = pg_init; }
+  if (lane >= k) { sel[lane] = -1; pages[lane] = -1; }
+  auto write_local = [&]() {
+    if (lane < n_local) { sel[k - n_local + lane] = nb - n_local + lane; pages[k - n_local + lane] = pg_local; }
+  };
+  if (want == 0) {
+    write_local();
+    return;
+  }
+
+  bool take[kR];
+  int before;
+  wave_topk<kR>(key, want, take, before);
   int at = n_init + before;
 #pragma unroll
   for (int i = 0; i < kR; ++i) {
@@ -379,6 +413,144 @@ __device__ __forceinline__ void wave_select_table(const float* srow, const int32
     }
   }
   write_local();
+}
+
+// LDS of the two-level selection: each first-level wave's picks (key, block, page),
+// want slots per wave (at most 8 waves x 63).
+struct MultiSelectSmem {
+  uint32_t key[8 * MSA_MAX_TOPK];
+  int32_t blk[8 * MSA_MAX_TOPK];
+  int32_t pg[8 * MSA_MAX_TOPK];
+};
+
+// Two-level selection for one row by `nw` waves of a workgroup (1 <= nw <= 8; nw * 64 kR
+// slots cover every candidate, and nw * want <= 64 kR): multiwave_select_level1 in every
+// wave, a workgroup barrier, multiwave_select_level2 in wave 0, and another barrier;
+// the table is then in sel / pages as wave_select_table writes it.
+//
+// Level 1: wave w (< nw) takes candidate slots [64 kR w, 64 kR (w + 1)) (block lo + c,
+// lane-major inside the wave), reads their scores and pages, and picks its own top
+// `want` by the selection order (higher score, then smaller block); it writes them in
+// block order to slots [w want, (w + 1) want) of the LDS list (key 0 in unused slots).
+// The block-order list then holds every block of the row's top `want`: such a block is
+// also among the top `want` of its own wave's candidates. Level 1 also writes what
+// needs no search: the identity table of a short row (wave 0), the forced first blocks
+// (wave 0), the forced last blocks (the wave holding their slots, or the last wave for
+// slots past every wave's), and the padding.
+// Level 2: wave 0 picks the top `want` of the list (kR per lane, block order kept) and
+// writes them, ascending, between the forced entries.
+// Each level-1 wave searches 64 kR keys instead of one wave searching all of them.
+// Level 1 returns the row's visible block count in the waves below nw (0 in the others).
+template <int kR>
+__device__ __forceinline__ int multiwave_select_level1(const float* srow, const int32_t* bt, int max_blocks,
+                                                       const int32_t* row_pos, int k, int n_init, int n_local,
+                                                       int nw, int* sel, int* pages, MultiSelectSmem& ms) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lo = n_init, want = k - n_init - n_local;
+  int nb = 0;
+  if (wave < nw) {
+    const int c0 = 64 * kR * wave;
+    float sv[kR];
+    int32_t pg[kR];
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+      const int c = c0 + lane * kR + i;
+      const bool in_row = lo + c < max_blocks;
+      sv[i] = in_row ? srow[lo + c] : 0.0f;
+      pg[i] = in_row ? bt[lo + c] : -1;
+    }
+    const int32_t pg_init = wave == 0 && lane < n_init && lane < max_blocks ? bt[lane] : -1;   // blocks below lo
+    // slots past every wave's hold only forced last blocks (n_local <= 64): the last
+    // wave reads their pages too, so no block-table read waits for the row's length
+    const int ct = 64 * kR * nw + lane;
+    const int32_t pg_tail = wave == nw - 1 && lo + ct < max_blocks ? bt[lo + ct] : -1;
+    asm volatile("" ::: "memory");   // the position's load queues behind the others
+    nb = min(*row_pos / MSA_PAGE_SIZE + 1, max_blocks);
+    const int C = nb - n_init - n_local;
+    if (nb <= k) {                                           // identity table (wave 0 holds it all)
+      if (wave == 0) {
+        if (lane < lo && lane < nb) { sel[lane] = lane; pages[lane] = pg_init; }
+#pragma unroll
+        for (int i = 0; i < kR; ++i) {
+          const int b = lo + lane * kR + i;
+          if (b < nb) { sel[b] = b; pages[b] = pg[i]; }
+        }
+        if (lane >= nb) { sel[lane] = -1; pages[lane] = -1; }
+      }
+    } else {
+      if (wave == 0) {
+        if (lane < n_init) { sel[lane] = lane; pages[lane] = pg_init; }
+        if (lane >= k) { sel[lane] = -1; pages[lane] = -1; }
+      }
+      // forced last blocks: slots C .. C + n_local - 1
+#pragma unroll
+      for (int i = 0; i < kR; ++i) {
+        const int c = c0 + lane * kR + i;
+        if (c >= C && c < C + n_local) { sel[k - n_local + c - C] = lo + c; pages[k - n_local + c - C] = pg[i]; }
+      }
+      if (wave == nw - 1 && ct >= C && ct < C + n_local) {
+        sel[k - n_local + ct - C] = lo + ct;
+        pages[k - n_local + ct - C] = pg_tail;
+      }
+      uint32_t key[kR];
+#pragma unroll
+      for (int i = 0; i < kR; ++i) key[i] = c0 + lane * kR + i < C ? float_key(sv[i]) : 0u;   // 0: below every real key
+      if (want > 0) {
+        bool take[kR];
+        int before;
+        wave_topk<kR>(key, want, take, before);
+        // this wave's picks, in block order, then key-0 slots up to `want`
+        int at = wave * want + before;
+#pragma unroll
+        for (int i = 0; i < kR; ++i) {
+          if (take[i]) {
+            ms.key[at] = key[i];
+            ms.blk[at] = lo + c0 + lane * kR + i;
+            ms.pg[at] = pg[i];
+            ++at;
+          }
+        }
+        int n_taken = 0;
+#pragma unroll
+        for (int i = 0; i < kR; ++i) n_taken += __popcll(__ballot(take[i]));
+        for (int j = n_taken + lane; j < want; j += 64) ms.key[wave * want + j] = 0u;
+      }
+    }
+  }
+  return nb;
+}
+
+// Level 2, wave 0 (nb from its level 1): the top `want` of the nw * want picks (block
+// order: wave-major, ascending inside each wave), written between the forced entries.
+template <int kR>
+__device__ __forceinline__ void multiwave_select_level2(int nb, int k, int n_init, int n_local, int nw, int* sel,
+                                                        int* pages, const MultiSelectSmem& ms) {
+  const int lane = threadIdx.x & 63;
+  const int want = k - n_init - n_local;
+  if (nb <= k || want <= 0) return;
+  const int n = nw * want;
+  uint32_t key[kR];
+  int32_t blk[kR], pg[kR];
+#pragma unroll
+  for (int i = 0; i < kR; ++i) {
+    const int j = lane * kR + i;
+    key[i] = j < n ? ms.key[j] : 0u;
+    blk[i] = j < n ? ms.blk[j] : -1;
+    pg[i] = j < n ? ms.pg[j] : -1;
+  }
+  bool take[kR];
+  int before;
+  wave_topk<kR>(key, want, take, before);
+  int at = n_init + before;
+#pragma unroll
+  for (int i = 0; i < kR; ++i) {
+    if (take[i]) {
+      sel[at] = blk[i];
+      pages[at] = pg[i];
+      ++at;
+    }
+  }
 }
 
 // Largest number of candidate blocks the wave-level selection handles (64 lanes x 32).

@@ -78,6 +78,8 @@ struct DecodeArgs {
   int32_t* sel_pages_out;
   const float* scores;        // selecting variant
   int n_init, n_local;
+  int sel_waves;              // selecting variant: first-level waves of the two-level selection
+                              // (0: the row is too long for it; the block radix select runs)
   int k;
   float softmax_scale;
   int num_splits;
@@ -259,12 +261,19 @@ __device__ __forceinline__ bool merge_slots(__amdgpu_buffer_rsrc_t ro, __amdgpu_
 // only split (kOutDirect), or its partial through the merge workspace, the last split
 // of the (row, KV head) merging them all into the bf16 output (kOutMerged). The direct
 // variant holds none of the merge code, and so fewer registers. kSelect: 0 = the
-// caller's table; 16 or 32 = the workgroup selects, with the one-wave search for rows of
-// up to 64 x kSelect candidates (16 keeps its registers within four waves per SIMD).
+// caller's table; 1, 2, 4 or 8 = the workgroup selects, with the two-level selection at
+// kSelect keys per lane (or the block radix select for rows too long for it).
 constexpr int kOutPartials = 0, kOutDirect = 1, kOutMerged = 2;
 
+// 8-wave workgroups that do not merge run two per compute unit when the launch is large
+// (one split per (row, KV head) pair): four waves per SIMD, so at most 128 registers.
+template <int kW, int kOut>
+constexpr int decode_min_waves_per_simd() { return kW == 8 && kOut != 2 ? 4 : 1; }
+
 template <int kFmt, int kW, int kItems, int kOut, int kSelect>
-__global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(64 * kW)
+__attribute__((amdgpu_waves_per_eu(decode_min_waves_per_simd<kW, kOut>())))
+sparse_decode_kernel(DecodeArgs a) {
   // Dynamic LDS: the row's selection keys (selecting variant, before any V is staged),
   // then the per-wave V staging buffers and, at the end, the per-wave O tiles.
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
@@ -282,7 +291,10 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
   const int hq = a.hkv * kHeadsPerKv;
-  const int lo = (s * a.k) / a.num_splits, hi = ((s + 1) * a.k) / a.num_splits;
+  int lo = (s * a.k) / a.num_splits, hi = ((s + 1) * a.k) / a.num_splits;
+  // (computed here, in scalar registers: the compiler would otherwise sink the two
+  // divisions to their first use, after the selection)
+  asm volatile("" : "+s"(lo), "+s"(hi));
   const int n_items = (hi - lo) * 4;   // (entry, 32-token chunk) pairs of this split
   const int64_t head0 = static_cast<int64_t>(r) * hq + kHeadsPerKv * g;
 
@@ -372,21 +384,29 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
   }
   if constexpr (kSelect) {
     const float* srow = a.scores + trow * a.max_blocks;
-    if (a.max_blocks - a.n_init - a.n_local <= 64 * kSelect) {
-      // Wave 0 selects (the other waves would only contend for the scalar unit) and
-      // hands the table over through LDS. Its block-table reads go out with the score
-      // reads, from the row of the request r belongs to when every request has the
-      // same number of rows; the pages are read again if row_seq says otherwise.
+    if (a.sel_waves > 0) {
+      // The first-level waves read their share of the scores and the block-table row
+      // of the request r belongs to when every request has the same number of rows;
+      // the pages are read again if row_seq says otherwise. The last wave converts Q
+      // (its load goes out first) and hands it over through LDS with the table.
       const int guess = seq_guess(r, a.seq_mul);
+      if (wave == kW - 1) load_q();
       // every wave's own copy of the row's position and request, read before the
-      // selection so that wave 0 does not wait for them after it
+      // selection so that no wave waits for them after it
       pos = a.row_pos[r];
       const int seq = checked_seq(a.row_seq[r], a.num_seqs, a.err);
-      if (wave == 0) {
-        const int32_t* btg = a.block_table + static_cast<int64_t>(guess) * a.max_blocks;
-        wave_select<kSelect>(srow, btg, a.max_blocks, a.row_pos + r, a.k, a.n_init, a.n_local, lsel, lpage);
+      const int32_t* btg = a.block_table + static_cast<int64_t>(guess) * a.max_blocks;
+      MultiSelectSmem& ms = *reinterpret_cast<MultiSelectSmem*>(dyn_lds);
+      const int nb = multiwave_select_level1<kSelect>(srow, btg, a.max_blocks, a.row_pos + r, a.k, a.n_init,
+                                                      a.n_local, a.sel_waves, lsel, lpage, ms);
+      if (wave == kW - 1) {   // (while the first level runs, unless this wave is part of it)
+        convert_q();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) qlds[j][lane] = Qop[j];
+        qcs[lane] = cscale;
       }
-      if (wave == 1) q_to_lds();
+      __syncthreads();
+      if (wave == 0) multiwave_select_level2<kSelect>(nb, a.k, a.n_init, a.n_local, a.sel_waves, lsel, lpage, ms);
       __syncthreads();
       selv = lsel[lane];
       pagev = lpage[lane];
@@ -689,7 +709,7 @@ __global__ void __launch_bounds__(64 * kW) sparse_decode_kernel(DecodeArgs a) {
 template <int kFmt, int kW, int kItems, int kOut, int kSelect>
 void launch(const DecodeArgs& a, dim3 grid, hipStream_t s) {
   size_t lds = static_cast<size_t>(kW) * kVBufBytes;
-  if (kSelect) lds = std::max(lds, static_cast<size_t>(a.max_blocks) * sizeof(uint32_t));
+  if (kSelect) lds = std::max({lds, static_cast<size_t>(a.max_blocks) * sizeof(uint32_t), sizeof(MultiSelectSmem)});
   sparse_decode_kernel<kFmt, kW, kItems, kOut, kSelect><<<grid, dim3(64 * kW), lds, s>>>(a);
 }
 
@@ -705,21 +725,36 @@ void launch(const DecodeArgs& a, dim3 grid, hipStream_t s) {
 // the same order (the merged and direct outputs equal the partials + msa_combine bit
 // for bit). The selecting variant needs at least 4 waves (its selection uses 256
 // threads or more).
-template <int kFmt, int kOut, int kSelect>
-msa_status_t dispatch(const DecodeArgs& a, dim3 grid, hipStream_t s) {
+int decode_waves(const DecodeArgs& a, dim3 grid) {
   const int per_split = (a.k + a.num_splits - 1) / a.num_splits;
   const int chunks = 4 * per_split;
-  const bool one = a.num_splits == 1;
-  const bool rounds16 = one && (chunks <= 16 || static_cast<int64_t>(grid.x) * grid.y < 256);
-  if (chunks <= 4) launch<kFmt, 4, 1, kOut, kSelect>(a, grid, s);
-  else if (chunks <= 8) launch<kFmt, 8, 1, kOut, kSelect>(a, grid, s);
-  else if (rounds16) {
-    if constexpr (kOut != kOutMerged) launch<kFmt, 16, 1, kOut, kSelect>(a, grid, s);
-    else return MSA_ERR_UNSUPPORTED;   // (never: one split writes its output directly)
-  } else {
-    launch<kFmt, 8, 1, kOut, kSelect>(a, grid, s);   // rounds of 8 chunks
+  const bool rounds16 = a.num_splits == 1 && (chunks <= 16 || static_cast<int64_t>(grid.x) * grid.y < 256);
+  return chunks <= 4 ? 4 : chunks <= 8 ? 8 : rounds16 ? 16 : 8;
+}
+
+template <int kFmt, int kOut, int kSelect>
+msa_status_t dispatch(const DecodeArgs& a, dim3 grid, hipStream_t s) {
+  switch (decode_waves(a, grid)) {
+    case 4: launch<kFmt, 4, 1, kOut, kSelect>(a, grid, s); break;
+    case 8: launch<kFmt, 8, 1, kOut, kSelect>(a, grid, s); break;   // (rounds of 8 chunks past 8)
+    default:
+      if constexpr (kOut != kOutMerged) launch<kFmt, 16, 1, kOut, kSelect>(a, grid, s);
+      else return MSA_ERR_UNSUPPORTED;   // (never: one split writes its output directly)
   }
   return launch_status();
+}
+
+// Shape of the two-level selection for a launch of `waves` waves: the fewest keys per
+// lane (1, 2, 4 or 8) for which ceil(C / 64 kR) first-level waves fit in the workgroup
+// (and in 8) and their picks (nw * want) fit one wave at kR keys per lane. kR = 0: the
+// row is too long for it (the block radix select runs).
+void select_shape(int c_max, int want, int waves, int& kR, int& nw) {
+  for (kR = 1; kR <= 8; kR *= 2) {
+    nw = std::max(1, (c_max + 64 * kR - 1) / (64 * kR));
+    if (nw <= std::min(waves, 8) && nw * std::max(want, 0) <= 64 * kR) return;
+  }
+  kR = 0;
+  nw = 0;
 }
 
 msa_status_t decode_entry(const msa_kv_pool_t* pool, const msa_step_t* step, int32_t num_q_heads,
@@ -762,20 +797,23 @@ msa_status_t decode_entry(const msa_kv_pool_t* pool, const msa_step_t* step, int
   a.seq_mul = seq_guess_mul(step->num_seqs, step->num_rows);
   const int pairs = step->num_rows * pool->num_kv_heads;
   dim3 grid(a.num_splits, pairs);
-  // The one-split selecting variant runs many workgroups per compute unit where the
-  // rows allow its narrower search (registers for four waves per SIMD); the merging one
-  // has at most about one workgroup per compute unit and keeps the full search (its
-  // code measured faster that way).
   const bool direct = a.num_splits == 1;
-  const bool wide = a.max_blocks - a.n_init - a.n_local > 64 * 16;   // more than 16 keys per lane
-#define MSA_DECODE_DISPATCH(FMT)                                                                      \
-  (select ? (direct ? (wide ? dispatch<FMT, kOutDirect, 32>(a, grid, s) : dispatch<FMT, kOutDirect, 16>(a, grid, s)) \
-                    : dispatch<FMT, kOutMerged, 32>(a, grid, s))                                      \
+  int kr = 0;
+  if (select) select_shape(a.max_blocks - a.n_init - a.n_local, a.k - a.n_init - a.n_local, decode_waves(a, grid),
+                           kr, a.sel_waves);
+  // (rows too long for the two-level selection take the block radix select, in the
+  // 8-keys-per-lane instance of the kernel)
+#define MSA_DECODE_SELECT(FMT, OUT)                                                                    \
+  (kr == 1 ? dispatch<FMT, OUT, 1>(a, grid, s) : kr == 2 ? dispatch<FMT, OUT, 2>(a, grid, s)          \
+   : kr == 4 ? dispatch<FMT, OUT, 4>(a, grid, s) : dispatch<FMT, OUT, 8>(a, grid, s))
+#define MSA_DECODE_DISPATCH(FMT)                                                                       \
+  (select ? (direct ? MSA_DECODE_SELECT(FMT, kOutDirect) : MSA_DECODE_SELECT(FMT, kOutMerged))        \
    : combine ? (direct ? dispatch<FMT, kOutDirect, 0>(a, grid, s) : dispatch<FMT, kOutMerged, 0>(a, grid, s)) \
              : dispatch<FMT, kOutPartials, 0>(a, grid, s))
   if (pool->fmt == MSA_KV_NVFP4) return MSA_DECODE_DISPATCH(MSA_KV_NVFP4);
   return MSA_DECODE_DISPATCH(MSA_KV_FP8_E4M3);
 #undef MSA_DECODE_DISPATCH
+#undef MSA_DECODE_SELECT
 }
 
 DecodeArgs base_args(const int32_t* sel, const int32_t* sel_pages, int32_t k, float softmax_scale,

@@ -222,13 +222,17 @@ def test_fused_step_many_rows_per_request(M, fmt):
         assert torch.equal(got.out.view(torch.int16), ref.out.view(torch.int16)), rep
 
 
-@pytest.mark.parametrize("nb_max,k,n_init,n_local,quantum,tie_max", [
-    (40, 8, 0, 1, 1.0, 0), (257, 16, 0, 1, 0.5, 5), (257, 16, 0, 1, 0.5, 40), (600, 16, 1, 1, 2.0, 0),
-    (1025, 16, 2, 2, 2.0, 9), (2048, 32, 0, 1, 4.0, 0), (2048, 32, 0, 1, 0.25, 1200), (300, 7, 0, 0, 1.0, 3)])
-def test_fused_select_bit_exact_with_ties(M, nb_max, k, n_init, n_local, quantum, tie_max):
-    """The selection inside the fused decode (one wave per workgroup, any row length up
-    to 2048 candidates) on the same fp32 scores as the oracle, with heavy exact ties and
-    `tie_max` extra blocks tied at each row's maximum: tables identical."""
+@pytest.mark.parametrize("nb_max,k,n_init,n_local,quantum,tie_max,ns", [
+    (40, 8, 0, 1, 1.0, 0, 2), (257, 16, 0, 1, 0.5, 5, 2), (257, 16, 0, 1, 0.5, 40, 2), (600, 16, 1, 1, 2.0, 0, 2),
+    (1025, 16, 2, 2, 2.0, 9, 2), (2048, 32, 0, 1, 4.0, 0, 2), (2048, 32, 0, 1, 0.25, 1200, 2),
+    (300, 7, 0, 0, 1.0, 3, 2), (3000, 64, 0, 1, 1.0, 100, 4), (5000, 16, 0, 1, 1.0, 0, 2),
+    (1500, 8, 0, 1, 1.0, 20, 8), (257, 4, 0, 1, 0.5, 10, 1), (700, 16, 0, 1, 1.0, 0, 1)])
+def test_fused_select_bit_exact_with_ties(M, nb_max, k, n_init, n_local, quantum, tie_max, ns):
+    """The selection inside the fused decode on the same fp32 scores as the oracle, with
+    heavy exact ties and `tie_max` extra blocks tied at each row's maximum: tables
+    identical. The cases span every shape of the two-level selection (1, 2, 4 and 8 keys
+    per lane, one to eight first-level waves, in workgroups of 4, 8 and 16 waves) and the
+    block radix select that takes rows too long for it (5000 blocks)."""
     rng = np.random.default_rng(7 * nb_max + k + tie_max)
     rows = 6
     S, pos = _select_case(rng, rows, nb_max, k, quantum)
@@ -237,15 +241,15 @@ def test_fused_select_bit_exact_with_ties(M, nb_max, k, n_init, n_local, quantum
         if tie_max and nb > 2:
             top = S[r, :nb].max()
             S[r, rng.choice(nb - 1, min(tie_max, nb - 1), replace=False)] = top
-    _print("fused select", nb_max, k, n_init, n_local, tie_max)
+    _print("fused select", nb_max, k, n_init, n_local, tie_max, "splits", ns)
     wl = W.small(W.FMT_NVFP4, [300], 1, num_kv_heads=1, k=k, seed=91)
     pool = G.gpu_pool(M, wl)
     bt = rng.integers(0, wl.num_pages, size=(1, nb_max)).astype(np.int32)
     step = M.Step(bt, np.zeros(rows, np.int32), pos)
     q = torch.from_numpy(rng.standard_normal((rows, wl.num_heads, 128)).astype(np.float32)).to(torch.bfloat16).cuda()
-    bufs = M.DecodeBuffers(rows, wl.num_heads, nb_max, k, 2)
+    bufs = M.DecodeBuffers(rows, wl.num_heads, nb_max, k, ns)
     M.msa_select_decode_combine(pool, step, q, torch.from_numpy(S).cuda(), k, n_init, n_local,
-                                wl.softmax_scale, 2, bufs.merge_o, bufs.merge_ml, bufs.counters, bufs.out,
+                                wl.softmax_scale, ns, bufs.merge_o, bufs.merge_ml, bufs.counters, bufs.out,
                                 sel=bufs.sel, sel_pages=bufs.sel_pages)
     torch.cuda.synchronize()
     ref = O.select_topk(S.astype(np.float64), pos, k, n_init, n_local)
