@@ -242,6 +242,39 @@ def inject_ties(wl: Workload, n_tied: int, seed_tag: int = 3) -> Workload:
     return wl
 
 
+def verify_tables(wl: Workload, overlap: float, seed_tag: int = 5) -> np.ndarray:
+    """Seeded selection tables with the structure of a top-k selection ([rows][k], each
+    row's visible blocks in strictly ascending order, its last visible block always
+    present, -1 padding only when the row sees fewer than k blocks), where the rows of
+    one request share a fraction `overlap` of their picks: every request draws k - 1
+    blocks that all its rows see, and each row keeps each of them with probability
+    `overlap` (else it draws another block it sees). overlap = 1 gives every row of a
+    request the same earlier blocks; 0 gives independent draws."""
+    rng = np.random.default_rng([wl.seed, seed_tag])
+    k = wl.k
+    sel = np.full((wl.num_rows, k), -1, dtype=np.int32)
+    for s in range(len(wl.ctx_lens)):
+        rows = np.nonzero(wl.row_seq == s)[0]
+        if len(rows) == 0:
+            continue
+        nb_min = int(wl.row_pos[rows].min()) // PAGE + 1
+        shared = rng.choice(max(nb_min - 1, 1), size=min(k - 1, max(nb_min - 1, 0)), replace=False) \
+            if nb_min > 1 else np.zeros(0, np.int64)
+        for r in rows:
+            nb = int(wl.row_pos[r]) // PAGE + 1
+            if nb <= k:
+                sel[r, :nb] = np.arange(nb)
+                continue
+            picks = {nb - 1}
+            for b in shared:
+                if len(picks) < k and rng.random() < overlap:
+                    picks.add(int(b))
+            while len(picks) < k:
+                picks.add(int(rng.integers(0, nb - 1)))
+            sel[r] = np.sort(np.fromiter(picks, dtype=np.int64))
+    return sel
+
+
 def keep_rows(wl: Workload, rows) -> Workload:
     """The same workload with only the given query rows (request-major order kept):
     requests then have different numbers of rows, or none."""

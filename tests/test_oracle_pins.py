@@ -626,3 +626,67 @@ def test_attend_per_kv_head_tables_reduce_to_shared_tables():
         m, l, Op = O.split_partials(pool, wl.block_table, wl.row_seq, wl.row_pos, wl.q, sel3,
                                     wl.softmax_scale, ns)
         assert np.max(np.abs(O.combine(m, l, Op) - out3)) < 1e-12
+
+
+# ---- union partials (query pairing: groups of rows over the union of their tables)
+def _groups(row_seq, size):
+    starts = [0]
+    for i in range(1, len(row_seq) + 1):
+        if i == len(row_seq) or row_seq[i] != row_seq[i - 1] or i - starts[-1] == size:
+            starts.append(i)
+    return starts
+
+
+@pytest.mark.parametrize("fmt", [W.FMT_NVFP4, W.FMT_FP8])
+def test_union_partials_combine_to_each_rows_attention(fmt):
+    # verify rows that cross a page boundary (1022..1025, 126..129), so rows of a group
+    # see different numbers of tokens of a shared block
+    wl = W.small(fmt, [1022, 1500, 126], 4, num_kv_heads=2, k=5, seed=31)
+    pool = _oracle_pool(wl)
+    for overlap in (0.0, 0.6, 1.0):
+        sel = W.verify_tables(wl, overlap)
+        ref = O.attend(pool, wl.block_table, wl.row_seq, wl.row_pos, wl.q, sel, wl.softmax_scale)
+        for size in (4, 2, 3):
+            groups = _groups(wl.row_seq, size)
+            for ns in (1, 2, 3, 7):
+                m, l, Op = O.union_partials(pool, wl.block_table, wl.row_seq, wl.row_pos, wl.q, sel,
+                                            wl.softmax_scale, ns, groups)
+                err = np.max(np.abs(O.combine(m, l, Op) - ref))
+                assert err < 1e-12 * max(1.0, np.max(np.abs(ref))), (overlap, size, ns, err)
+
+
+def test_union_partials_of_one_row_groups_are_split_partials():
+    # a group of one row whose table has k distinct blocks: its union is its table, so
+    # the union split is the table split
+    wl = W.small(W.FMT_NVFP4, [1500, 2200], 1, num_kv_heads=2, k=6, seed=32)
+    pool = _oracle_pool(wl)
+    sel = W.verify_tables(wl, 0.0)
+    assert (sel >= 0).all()
+    groups = list(range(wl.num_rows + 1))
+    for ns in (1, 2, 4, 6):
+        a = O.union_partials(pool, wl.block_table, wl.row_seq, wl.row_pos, wl.q, sel, wl.softmax_scale, ns, groups)
+        b = O.split_partials(pool, wl.block_table, wl.row_seq, wl.row_pos, wl.q, sel, wl.softmax_scale, ns)
+        for x, y in zip(a, b):
+            assert np.array_equal(x, y)
+
+
+def test_union_split_follows_first_pick_order_and_row_masks():
+    # two rows of one request at positions 300 and 301; tables [0, 2] and [1, 2]: the
+    # union is [0, 2, 1] (first picks, rows in order), so with 3 splits block 0 is split 0
+    # (row 0 only), block 2 split 1 (both rows; row 0 sees 45 of its tokens, row 1 46)
+    # and block 1 split 2 (row 1 only)
+    wl = W.small(W.FMT_FP8, [300], 2, num_kv_heads=1, k=2, seed=33)
+    assert list(wl.row_pos) == [300, 301]
+    pool = _oracle_pool(wl)
+    sel = np.array([[0, 2], [1, 2]], np.int32)
+    m, l, Op = O.union_partials(pool, wl.block_table, wl.row_seq, wl.row_pos, wl.q, sel, wl.softmax_scale, 3, [0, 2])
+    assert np.isneginf(m[0, :, 2]).all() and (l[0, :, 2] == 0).all() and (Op[0, :, 2] == 0).all()
+    assert np.isneginf(m[1, :, 0]).all() and (l[1, :, 0] == 0).all()
+    assert np.isfinite(m[0, :, :2]).all() and np.isfinite(m[1, :, 1:]).all()
+    for r, b, s in ((0, 0, 0), (0, 2, 1), (1, 2, 1), (1, 1, 2)):
+        one = O.split_partials(pool, wl.block_table, wl.row_seq[r:r + 1], wl.row_pos[r:r + 1], wl.q[r:r + 1],
+                               np.array([[b]], np.int32), wl.softmax_scale, 1)
+        assert np.array_equal(m[r, :, s], one[0][0, :, 0]) and np.array_equal(l[r, :, s], one[1][0, :, 0])
+        assert np.array_equal(Op[r, :, s], one[2][0, :, 0])
+    # the rows' masks differ on the shared block: row 1 sees token 301, row 0 does not
+    assert not np.array_equal(l[0, :, 1], l[1, :, 1])
