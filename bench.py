@@ -80,6 +80,8 @@ def parse():
                     help="oracle time budget, for each of the two thread counts")
     ap.add_argument("--no-read-probe", action="store_true",
                     help="skip the 1 GiB streaming-read reference measurement")
+    ap.add_argument("--no-pairing", action="store_true",
+                    help="skip the query-pairing comparison (workloads with several rows per request)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one device copy of this size (counter calibration)")
     return ap.parse_args()
@@ -385,6 +387,42 @@ def main():
     bpt = 144 if wl.fmt == W.FMT_NVFP4 else 256
     dec_bytes, dec_tokens = decode_algorithmic_bytes(wl, sel, bpt)
 
+    # Query pairing (several verify rows per request): the rows of a request decoded
+    # together over the union of their tables (msa_sparse_decode_union, one split, bf16
+    # out) against the one-row decode with the same output (msa_sparse_decode_combine, one
+    # split), on the step's selection and on full-overlap tables (every row of a request
+    # takes its first row's table: the most sharing the rows can have).
+    pairing = None
+    if wl.rows_per_req > 1 and tables == 1 and not args.no_pairing:
+        groups = torch.from_numpy(M.group_rows_of(wl.row_seq, 4)).to(dev)
+        first = {}
+        for r in range(wl.num_rows):
+            first.setdefault(int(wl.row_seq[r]), r)
+        sel_full = np.stack([sel[first[int(x)]] for x in wl.row_seq]).astype(np.int32)
+        pair_out = torch.empty_like(bufs.out)
+        ws = M.DecodeBuffers(wl.num_rows, wl.num_heads, wl.max_blocks, wl.k, 1)
+        pairing = {"group_rows": 4, "num_splits": 1}
+        for tag, tab in (("step_selection", sel), ("full_overlap", sel_full)):
+            tab_d = torch.from_numpy(np.ascontiguousarray(tab, dtype=np.int32)).to(dev)
+            ub, _ = decode_algorithmic_bytes(wl, tab, bpt)
+            per_row = sum(min(int(wl.row_pos[r]) - 128 * int(b) + 1, 128) for r in range(wl.num_rows)
+                          for b in tab[r] if b >= 0) * wl.num_kv_heads * bpt
+            res = {"union_bytes": ub, "per_row_bytes": per_row}
+            for nm, call in (
+                    ("msa_sparse_decode_union", lambda p: M.msa_sparse_decode_union(
+                        p, step, q, tab_d, wl.k, groups, 4, wl.softmax_scale, 1, out=pair_out)),
+                    ("msa_sparse_decode_combine", lambda p: M.msa_sparse_decode_combine(
+                        p, step, q, tab_d, wl.k, wl.softmax_scale, 1, ws.merge_o, ws.merge_ml, ws.counters,
+                        pair_out))):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for p in pools:
+                        call(p)
+                t = time_replays(g, R)
+                res[nm] = {"mean_us": t["mean"], "p50_us": t["p50"],
+                           "union_gbs": ub / (t["mean"] * 1e-6) / 1e9}
+            pairing[tag] = res
+
     # The read floor: the same selected K/V bytes read by a plain kernel through the page
     # list, one launch per replica in the same rotation, timed like the kernels above.
     units = selected_units(wl, sel)
@@ -492,6 +530,7 @@ def main():
                                  "once, its visible tokens) read cold through the page list by a plain "
                                  "kernel, one workgroup per block, one launch per replica in the step's "
                                  "rotation; frac_of_read_floor = its mean time / the decode's"},
+        "query_pairing": pairing,
         "box_read_gbs": box_read,
         "kernel_us": per_kernel_us,
         "cpu_baseline": cpu,

@@ -12,7 +12,8 @@
  *
  * Fused entry points run the same step in two launches: msa_append_score_select
  * (append + score, optionally + select) and msa_select_decode_combine (select + decode
- * + combine) or msa_sparse_decode_combine (decode + combine).
+ * + combine) or msa_sparse_decode_combine (decode + combine). msa_sparse_decode_union
+ * decodes the rows of a request together over the union of their selected pages.
  *
  * The operations follow three public TensorRT-LLM pull-request pages:
  *   [Rubin] "[None][feat] Add Rubin (sm_107) MiniMax-M3.1 low-latency decode targets" (#21136)
@@ -71,6 +72,7 @@ typedef enum {
 #define MSA_MAX_TOPK 64
 #define MSA_MAX_BLOCKS 12288  /* blocks per sequence (1.5M tokens)                        */
 #define MSA_MAX_SEL_TABLES 4  /* per-KV-head selection: at most 4 tables per row          */
+#define MSA_MAX_GROUP_ROWS 4  /* msa_sparse_decode_union: rows per group (verify length)   */
 /* Bit pattern of every fp32 word of an idle split-merge workspace (a signalling NaN). */
 #define MSA_MERGE_IDLE_BITS 0x7fbadbadu
 
@@ -307,6 +309,43 @@ msa_status_t msa_select_decode_combine(const msa_kv_pool_t* pool, const msa_step
                                        void* out, int32_t* sel, int32_t* sel_pages, void* stream);
 
 /*
+ * Sparse decode of groups of query rows over the union of their selections (query
+ * pairing for speculative verify: [Rubin] commit messages name query pairing among
+ * the tuned parameters of the NVFP4 sparse decode at 4 query rows per request). A
+ * group is 1..max_group_rows rows of ONE request; the rows of a group that selected
+ * the same block share one read of its page, and each row applies its own causal
+ * mask (its visible tokens) and keeps its own softmax state, so every row's result
+ * is the attention msa_sparse_decode + msa_combine compute for it (up to the order
+ * of the fp32 sums).
+ *   sel, sel_pages : as msa_sparse_decode ([num_rows][k], or [num_rows][T][k] with
+ *     step->sel_tables = T > 1); a block is listed at most once in a row's table
+ *   group_rows : int32 [num_groups + 1], ascending row offsets: group i is the rows
+ *     [group_rows[i], group_rows[i + 1]), at most max_group_rows (1..MSA_MAX_GROUP_ROWS)
+ *     of them, all with the same row_seq; with sel_pages, a block has the same page in
+ *     every row of its group. Rows in no group are not written. The union of group i
+ *     lists each selected block once, in order of its first pick (rows in order, each
+ *     table in order); split s of num_splits takes its entries
+ *     [s N / num_splits, (s + 1) N / num_splits) of the N entries.
+ *   num_splits == 1 : writes bf16 out [num_rows][num_q_heads][head_dim] (part_o and
+ *     part_ml unused, may be NULL)
+ *   num_splits > 1  : writes the partials of msa_sparse_decode's layout, part_o fp32
+ *     [num_rows][num_q_heads][num_splits][head_dim] and part_ml fp32
+ *     [num_rows][num_q_heads][num_splits][2], for msa_combine (out unused, may be NULL);
+ *     a split that holds none of a row's blocks writes m = -inf, l = 0, O = 0 for it
+ * 1 <= num_splits <= max_group_rows * k. The release library drops a table entry that
+ * is neither -1 nor a visible block of its row; the debug library also reports it
+ * (MSA_DEBUG_BAD_SEL) and reports a group that breaks the rules above
+ * (MSA_DEBUG_BAD_GROUP), whose rows are then clamped to [0, num_rows) and to
+ * max_group_rows.
+ */
+msa_status_t msa_sparse_decode_union(const msa_kv_pool_t* pool, const msa_step_t* step,
+                                     int32_t num_q_heads, const void* q, const int32_t* sel,
+                                     const int32_t* sel_pages, int32_t k, int32_t num_groups,
+                                     const int32_t* group_rows, int32_t max_group_rows,
+                                     float softmax_scale, int32_t num_splits, float* part_o,
+                                     float* part_ml, void* out, void* stream);
+
+/*
  * Set up a merge workspace of the two *_combine entries for `num_splits` splits: every
  * word of both exchange buffers, part_o [rows][num_q_heads / 16][2][16][num_splits]
  * [head_dim] and part_ml [rows][num_q_heads / 16][2][16][num_splits][2], =
@@ -364,6 +403,8 @@ const char* msa_status_string(msa_status_t status);
  *   MSA_DEBUG_BAD_SLOT : an append slot whose page lies outside [0, num_pages)
  *   MSA_DEBUG_MERGE_TIMEOUT : a merging split gave up waiting for another split's
  *                       partial (see msa_sparse_decode_combine)
+ *   MSA_DEBUG_BAD_GROUP : a row group of msa_sparse_decode_union that is out of order,
+ *                       outside [0, num_rows), longer than max_group_rows or mixes requests
  * msa_debug_set_error_word sets the device int32 word (NULL: none) that every later
  * call of the debug library, on any stream, reports to; the caller zeroes and reads
  * it. msa_debug_set_merge_poll_limit sets the number of poll rounds after which a
@@ -380,7 +421,8 @@ typedef enum {
   MSA_DEBUG_BAD_POS = 3,
   MSA_DEBUG_BAD_SEL = 4,
   MSA_DEBUG_BAD_SLOT = 5,
-  MSA_DEBUG_MERGE_TIMEOUT = 6
+  MSA_DEBUG_MERGE_TIMEOUT = 6,
+  MSA_DEBUG_BAD_GROUP = 7
 } msa_debug_error_t;
 
 msa_status_t msa_debug_set_error_word(int32_t* word);

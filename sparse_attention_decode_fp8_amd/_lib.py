@@ -55,7 +55,7 @@ class MsaStep(ctypes.Structure):
 
 
 EXPORTS = ["msa_kv_append", "msa_index_score", "msa_select_topk", "msa_append_score_select",
-           "msa_sparse_decode",
+           "msa_sparse_decode", "msa_sparse_decode_union",
            "msa_sparse_decode_combine", "msa_select_decode_combine", "msa_combine",
            "msa_merge_workspace_init",
            "msa_decode_workspace_bytes", "msa_pool_bytes", "msa_index_bytes", "msa_status_string",
@@ -75,6 +75,7 @@ def load_library(path: str):
         "msa_select_topk": (I32, [P, P, I32, I32, I32, P, P, P]),
         "msa_append_score_select": (I32, [P, P, I32, P, P, P, P, I32, P, P, I32, I32, I32, P, P, P, P, P]),
         "msa_sparse_decode": (I32, [P, P, I32, P, P, P, I32, F32, I32, P, P, P]),
+        "msa_sparse_decode_union": (I32, [P, P, I32, P, P, P, I32, I32, P, I32, F32, I32, P, P, P, P]),
         "msa_sparse_decode_combine": (I32, [P, P, I32, P, P, P, I32, F32, I32, P, P, P, P, P]),
         "msa_select_decode_combine": (I32, [P, P, I32, P, P, I32, I32, I32, F32, I32, P, P, P, P, P, P, P]),
         "msa_combine": (I32, [I32, I32, I32, I32, P, P, P, P]),
@@ -266,6 +267,32 @@ def msa_sparse_decode(pool: KVPool, step: Step, q, sel, k, softmax_scale, num_sp
                                  num_splits, _ptr(part_o, torch.float32, "part_o"),
                                  _ptr(part_ml, torch.float32, "part_ml"), _stream(stream)),
            "msa_sparse_decode")
+
+
+def group_rows_of(row_seq, max_group_rows=4):
+    """Row groups for msa_sparse_decode_union: each request's consecutive rows, cut into
+    groups of at most max_group_rows. Returns the int32 offsets [groups + 1]."""
+    import numpy as np
+    rs = np.asarray(row_seq).ravel()
+    starts = [0]
+    for i in range(1, len(rs) + 1):
+        if i == len(rs) or rs[i] != rs[i - 1] or i - starts[-1] == max_group_rows:
+            starts.append(i)
+    return np.asarray(starts, dtype=np.int32)
+
+
+def msa_sparse_decode_union(pool: KVPool, step: Step, q, sel, k, group_rows, max_group_rows,
+                            softmax_scale, num_splits, part_o=None, part_ml=None, out=None,
+                            sel_pages=None, stream=None):
+    """group_rows: device int32 [groups + 1] offsets (see group_rows_of)."""
+    ps, ss = pool.cstruct(), step.cstruct()
+    _check(LIB.msa_sparse_decode_union(
+        ctypes.byref(ps), ctypes.byref(ss), q.shape[1], _ptr(q, torch.bfloat16, "q"),
+        _ptr(sel, torch.int32, "sel"), _ptr(sel_pages, torch.int32, "sel_pages"), k,
+        group_rows.numel() - 1, _ptr(group_rows, torch.int32, "group_rows"), max_group_rows,
+        float(softmax_scale), num_splits, _ptr(part_o, torch.float32, "part_o"),
+        _ptr(part_ml, torch.float32, "part_ml"), _ptr(out, torch.bfloat16, "out"), _stream(stream)),
+        "msa_sparse_decode_union")
 
 
 def msa_sparse_decode_combine(pool: KVPool, step: Step, q, sel, k, softmax_scale, num_splits,

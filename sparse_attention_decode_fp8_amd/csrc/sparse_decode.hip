@@ -44,18 +44,11 @@
 
 #include "msa_device.h"
 #include "msa_host.h"
+#include "decode_device.h"
 #include "select_device.h"
 
 namespace msa {
 namespace {
-
-constexpr int kVRowHalves = 144;   // 128 fp16 + 16 pad: 288-byte rows keep 4 rows on disjoint banks
-constexpr int kVBufBytes = 32 * kVRowHalves * 2;   // one wave's 32-token V chunk
-// A wave's O tile, [16 heads][128 d] fp32, reuses its V buffer. Rows are 132 floats
-// (33 16-byte quads, an odd count) so the 16 heads a quarter-wave writes at once fall
-// on distinct banks; 128-float rows would put all 16 on the same banks.
-constexpr int kORowFloats = kHeadDim + 4;
-static_assert(16 * kORowFloats * 4 <= kVBufBytes, "O tile must fit in a V buffer");
 
 struct DecodeArgs {
   const uint8_t* k_codes;
@@ -95,78 +88,6 @@ struct DecodeArgs {
   int poll_limit;
 };
 
-__device__ __forceinline__ half2_t bcast_lo(half2_t v) { return half2_t{v[0], v[0]}; }
-__device__ __forceinline__ half2_t bcast_hi(half2_t v) { return half2_t{v[1], v[1]}; }
-
-// One 32-token chunk of one page, as held by a lane: tile u (tokens 16u .. 16u+15 of
-// the chunk), token 16u + (lane % 16), dims 32q .. 32q+31.
-template <int kFmt>
-struct ChunkRegs;
-template <>
-struct ChunkRegs<MSA_KV_NVFP4> {
-  uint4 k[2], v[2];        // 32 E2M1 codes
-  uint32_t ks[2], vs[2];   // the two E4M3 scales of those 32 dims
-};
-template <>
-struct ChunkRegs<MSA_KV_FP8_E4M3> {
-  uint4 k[4], v[4];        // [tile * 2 + half]: 32 E4M3 codes
-};
-
-// Loads of one 32-token chunk (chunk c of the page's 128 tokens) of one (page, KV head)
-// through buffer resources whose base is that (page, head)'s region of each array (a
-// wave-uniform address: the page comes from the selection table in scalar registers).
-// An empty chunk (valid = false) gets resources of zero bytes: its loads return zero
-// without touching memory, and every chunk issues the same loads, so the compiler
-// knows how many are in flight and can consume earlier loads (Q) without waiting for
-// the page data.
-template <int kFmt>
-__device__ __forceinline__ void load_chunk(ChunkRegs<kFmt>& R, const DecodeArgs& a, int64_t ph, bool valid,
-                                           int c, int n, int q) {
-  const uint32_t t0 = 32u * c + n;   // this lane's token in tile 0; tile 1 is 16 tokens on
-  if constexpr (kFmt == MSA_KV_NVFP4) {
-    constexpr uint32_t kCodeBytes = kPage * kHeadDim / 2, kScaleBytes = kPage * kHeadDim / 16;
-    const __amdgpu_buffer_rsrc_t kc = make_rsrc(uniform_ptr(a.k_codes + ph * kCodeBytes), valid ? kCodeBytes : 0u);
-    const __amdgpu_buffer_rsrc_t vc = make_rsrc(uniform_ptr(a.v_codes + ph * kCodeBytes), valid ? kCodeBytes : 0u);
-    const __amdgpu_buffer_rsrc_t ks = make_rsrc(uniform_ptr(a.k_scales + ph * kScaleBytes), valid ? kScaleBytes : 0u);
-    const __amdgpu_buffer_rsrc_t vs = make_rsrc(uniform_ptr(a.v_scales + ph * kScaleBytes), valid ? kScaleBytes : 0u);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint32_t t = t0 + 16u * u;
-      R.k[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kc, static_cast<int>(t * (kHeadDim / 2) + 16 * q), 0, 0));
-      R.v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vc, static_cast<int>(t * (kHeadDim / 2) + 16 * q), 0, 0));
-      R.ks[u] = __builtin_amdgcn_raw_buffer_load_b16(ks, static_cast<int>(t * (kHeadDim / 16) + 2 * q), 0, 0);
-      R.vs[u] = __builtin_amdgcn_raw_buffer_load_b16(vs, static_cast<int>(t * (kHeadDim / 16) + 2 * q), 0, 0);
-    }
-  } else {
-    constexpr uint32_t kCodeBytes = kPage * kHeadDim;
-    const __amdgpu_buffer_rsrc_t kc = make_rsrc(uniform_ptr(a.k_codes + ph * kCodeBytes), valid ? kCodeBytes : 0u);
-    const __amdgpu_buffer_rsrc_t vc = make_rsrc(uniform_ptr(a.v_codes + ph * kCodeBytes), valid ? kCodeBytes : 0u);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint32_t t = t0 + 16u * u;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        R.k[2 * u + h] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kc, static_cast<int>(t * kHeadDim + 32 * q + 16 * h), 0, 0));
-        R.v[2 * u + h] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vc, static_cast<int>(t * kHeadDim + 32 * q + 16 * h), 0, 0));
-      }
-    }
-  }
-}
-
-// Dims 32q + 8j .. +7 of tile u as an fp16 MFMA operand.
-template <int kFmt>
-__device__ __forceinline__ half8_t dequant8(const uint4* codes, const uint32_t* scales, int u, int j) {
-  if constexpr (kFmt == MSA_KV_NVFP4) {
-    const uint4 c = codes[u];
-    const uint32_t w = j == 0 ? c.x : j == 1 ? c.y : j == 2 ? c.z : c.w;
-    const half2_t sc = e4m3x2_to_f16(scales[u]);
-    return e2m1x8_to_f16(w, j < 2 ? bcast_lo(sc) : bcast_hi(sc));
-  } else {
-    const uint4 c = codes[2 * u + (j >> 1)];
-    return (j & 1) ? e4m3x8_to_f16(c.z, c.w) : e4m3x8_to_f16(c.x, c.y);
-  }
-}
-
 template <int kFmt, int kItems>
 struct Round {
   ChunkRegs<kFmt> R[kItems];
@@ -200,7 +121,7 @@ __device__ __forceinline__ void load_round(Round<kFmt, kItems>& rd, const Decode
     rd.nvis[j] = valid ? min(nv, 32) : 0;
     page = valid ? checked_page(page, a.num_pages, a.err) : 0;
     page = static_cast<int64_t>(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(page))));
-    load_chunk<kFmt>(rd.R[j], a, page * a.hkv + g, valid, c, n, q);
+    load_chunk<kFmt>(rd.R[j], KvArrays{a.k_codes, a.v_codes, a.k_scales, a.v_scales}, page * a.hkv + g, valid, c, n, q);
     rd.kps[j] = rd.vps[j] = 1.0f;
     if constexpr (kFmt == MSA_KV_FP8_E4M3) {   // the page's scales (page 0 for an empty chunk)
       rd.kps[j] = reinterpret_cast<const float*>(a.k_scales)[page];
@@ -314,39 +235,13 @@ sparse_decode_kernel(DecodeArgs a) {
   // buffer b start at row (2 * head0 + 16 * b) * S of 128 (or 2) words.
 
   // Q^T operand: lane (n, q) holds head 16g + n, dims 32q + 8j .. +7 for k-step j.
-  const uint4* qp = reinterpret_cast<const uint4*>(
-      a.q + (static_cast<int64_t>(r) * hq + kHeadsPerKv * g + n) * kHeadDim + 32 * q);
+  const uint16_t* qh = a.q + (static_cast<int64_t>(r) * hq + kHeadsPerKv * g + n) * kHeadDim + 32 * q;
   uint4 qraw[4];
-  auto load_q = [&]() {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) qraw[i] = qp[i];
-  };
-  // Exact fp16 operand: each head is scaled by a power of two (folded into the logit
-  // scale) that brings its bf16 values into fp16's normal range.
+  auto load_q = [&]() { load_q_raw(qraw, qh); };
   half8_t Qop[4];
   float cscale;
   auto convert_q = [&]() {
-    float qf[32];
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t wv[4] = {qraw[i].x, qraw[i].y, qraw[i].z, qraw[i].w};
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        qf[8 * i + 2 * t] = __uint_as_float(wv[t] << 16);
-        qf[8 * i + 2 * t + 1] = __uint_as_float(wv[t] & 0xffff0000u);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(qf[i]));
-    amax = rows_max(amax);
-    const int e = f16_prescale_exp(amax);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) Qop[j][i] = static_cast<half_t>(ldexpf(qf[8 * j + i], e));
-    cscale = ldexpf(a.softmax_scale * kLog2e, -e);
-    if constexpr (kFmt == MSA_KV_NVFP4) cscale *= a.k_t;
+    convert_q_op(qraw, Qop, cscale, a.softmax_scale * kLog2e, kFmt == MSA_KV_NVFP4 ? a.k_t : 1.0f);
   };
   // Selecting variant: Q is the same for every wave of the workgroup, so wave 1 loads
   // and converts it while wave 0 selects, and hands it over through LDS.

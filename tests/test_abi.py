@@ -264,3 +264,30 @@ def test_use_library_switches_and_restores():
     with L.use_library(dbg) as lib:
         assert L.LIB is dbg and lib.msa_debug_checks_enabled() == 1
     assert L.LIB is before
+
+
+def test_union_decode_validation_rejects_before_launch():
+    B = ctypes.byref
+    P = ctypes.c_void_p
+    U = L.LIB.msa_sparse_decode_union
+    pool, step, s1 = _fake_pool(), _fake_step(), _fake_step(rows=1)
+    # args: pool, step, hq, q, sel, sel_pages, k, groups, group_rows, max_rows, scale, S, po, pm, out, stream
+    assert U(B(pool), B(step), 32, P(16), P(16), None, 8, 1, P(16), 4, 0.1, 1, None, None, P(16), None) == 0
+    assert U(B(pool), B(s1), 32, P(16), P(16), None, 8, 0, P(16), 4, 0.1, 1, None, None, P(16), None) == 0
+    # geometry: heads, k, split count (up to max_group_rows * k), group size
+    assert U(B(pool), B(s1), 48, P(16), P(16), None, 8, 1, P(16), 4, 0.1, 1, None, None, P(16), None) == -2
+    assert U(B(pool), B(s1), 32, P(16), P(16), None, 65, 1, P(16), 4, 0.1, 1, None, None, P(16), None) == -2
+    assert U(B(pool), B(s1), 32, P(16), P(16), None, 8, 1, P(16), 4, 0.1, 33, P(16), P(16), None, None) == -2
+    assert U(B(pool), B(s1), 32, P(16), P(16), None, 8, 1, P(16), 5, 0.1, 1, None, None, P(16), None) == -2
+    assert U(B(pool), B(s1), 32, P(16), P(16), None, 8, 1, P(16), 0, 0.1, 1, None, None, P(16), None) == -2
+    assert U(B(pool), B(s1), 32, P(16), P(16), None, 8, 65536 // 2, P(16), 4, 0.1, 1, None, None, P(16),
+             None) == -2
+    # arguments: one split needs out, several need both partial arrays; group_rows, q, sel
+    assert U(B(pool), B(s1), 32, P(16), P(16), None, 8, 1, P(16), 4, 0.1, 1, P(16), P(16), None, None) == -1
+    assert U(B(pool), B(s1), 32, P(16), P(16), None, 8, 1, P(16), 4, 0.1, 2, None, P(16), P(16), None) == -1
+    assert U(B(pool), B(s1), 32, P(16), P(16), None, 8, 1, P(16), 4, 0.1, 2, P(24), P(16), None, None) == -1
+    assert U(B(pool), B(s1), 32, P(16), P(16), None, 8, 1, None, 4, 0.1, 1, None, None, P(16), None) == -1
+    assert U(B(pool), B(s1), 32, None, P(16), None, 8, 1, P(16), 4, 0.1, 1, None, None, P(16), None) == -1
+    assert U(B(pool), B(s1), 32, P(16), None, None, 8, 1, P(16), 4, 0.1, 1, None, None, P(16), None) == -1
+    assert U(B(pool), B(s1), 32, P(16), P(16), None, 8, -1, P(16), 4, 0.1, 1, None, None, P(16), None) == -1
+    assert U(B(pool), B(s1), 32, P(16), P(16), None, 8, 1, P(16), 4, 0.0, 1, None, None, P(16), None) == -1

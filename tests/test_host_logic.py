@@ -84,3 +84,14 @@ def test_auto_replicas_put_512_mib_between_reuses():
     assert B.auto_replicas(wl, 1 << 30) == 48            # 48 GiB budget
     wl0 = types.SimpleNamespace(fmt=1, k=8, num_kv_heads=1, row_pos=np.array([4095]))
     assert B.auto_replicas(wl0, 2 << 20) == 512          # capped
+
+
+def test_group_rows_keep_a_requests_rows_together_up_to_the_group_size():
+    from sparse_attention_decode_fp8_amd import group_rows_of
+    rs = np.array([0, 0, 0, 0, 1, 2, 2, 3, 3, 3, 3, 3])
+    assert group_rows_of(rs, 4).tolist() == [0, 4, 5, 7, 11, 12]
+    assert group_rows_of(rs, 2).tolist() == [0, 2, 4, 5, 7, 9, 11, 12]
+    assert group_rows_of(rs, 1).tolist() == list(range(13))
+    assert group_rows_of(np.zeros(0, np.int32), 4).tolist() == [0]
+    # config 2's layout: 40 requests x 4 rows -> 40 groups of 4
+    assert group_rows_of(np.repeat(np.arange(40), 4), 4).tolist() == list(range(0, 161, 4))
