@@ -26,8 +26,9 @@
  *     call only (the device pointers inside them are what the kernels use).
  *   - Nothing is allocated or freed and no host synchronisation happens; calls on
  *     different streams may run concurrently if their outputs differ. The release library
- *     keeps no global state (the debug library's two process-wide settings are described
- *     at msa_debug_set_error_word).
+ *     keeps no global state beyond the fixed per-GPU array of the allocation-free entry
+ *     (msa_sparse_decode_combine_noalloc) and its address on each device; the debug
+ *     library's two process-wide settings are described at msa_debug_set_error_word.
  *   - Geometry is validated on the host before any launch. A call outside the supported
  *     contract returns MSA_ERR_UNSUPPORTED and launches nothing; it never falls back to
  *     another algorithm ([GB300] "The TP4 decode target": a covered shape whose
@@ -52,7 +53,8 @@ typedef enum {
   MSA_OK = 0,
   MSA_ERR_INVALID_ARG = -1,  /* null pointer, misaligned pointer, negative size      */
   MSA_ERR_UNSUPPORTED = -2,  /* geometry or format outside the contract              */
-  MSA_ERR_LAUNCH = -3        /* the HIP runtime rejected a kernel launch             */
+  MSA_ERR_LAUNCH = -3,       /* the HIP runtime rejected a kernel launch             */
+  MSA_ERR_TOO_LARGE = -4     /* more than an allocation-free entry's fixed scratch   */
 } msa_status_t;
 
 typedef enum {
@@ -344,6 +346,26 @@ msa_status_t msa_sparse_decode_union(const msa_kv_pool_t* pool, const msa_step_t
                                      const int32_t* group_rows, int32_t max_group_rows,
                                      float softmax_scale, int32_t num_splits, float* part_o,
                                      float* part_ml, void* out, void* stream);
+
+/*
+ * msa_sparse_decode_combine for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * arguments without the merge workspace, and the same bf16 `out` bit for bit. The split
+ * partials live in a fixed array of MSA_NOALLOC_SCRATCH_BYTES that the library holds on
+ * each GPU it runs on until the process ends; a call whose partials,
+ * num_rows * num_q_heads * num_splits * (head_dim + 2) fp32 (part_o rounded up to 256
+ * bytes), exceed it returns MSA_ERR_TOO_LARGE and launches nothing. num_splits == 1
+ * decodes in one launch without touching the array; num_splits > 1 (<= 16) decodes into
+ * it and merges with msa_combine, two launches. Nothing is allocated or freed (the
+ * first call on a device looks up the array's address). Every call on one GPU shares
+ * that GPU's array: calls that can overlap on one GPU (on different streams, or from
+ * several host threads) race and must be ordered by the caller.
+ */
+#define MSA_NOALLOC_SCRATCH_BYTES (8u << 20)
+msa_status_t msa_sparse_decode_combine_noalloc(const msa_kv_pool_t* pool, const msa_step_t* step,
+                                               int32_t num_q_heads, const void* q, const int32_t* sel,
+                                               const int32_t* sel_pages, int32_t k, float softmax_scale,
+                                               int32_t num_splits, void* out, void* stream);
 
 /*
  * Set up a merge workspace of the two *_combine entries for `num_splits` splits: every

@@ -8,6 +8,7 @@ it has not been built.
 from ._lib import (FMT_FP8, FMT_NVFP4, IDX_E4M3, IDX_NVFP4, KVPool, MsaError, Step, msa_combine,  # noqa: F401
                    msa_decode_workspace_bytes, msa_index_score, msa_kv_append, msa_select_topk,
                    msa_sparse_decode, msa_sparse_decode_combine, msa_sparse_decode_union, group_rows_of,
+                   msa_sparse_decode_combine_noalloc,
                    msa_append_score_select, msa_select_decode_combine, msa_merge_workspace_init,
                    MERGE_IDLE_BITS, msa_debug_set_error_word, msa_debug_set_merge_poll_limit,
                    load_library, use_library,

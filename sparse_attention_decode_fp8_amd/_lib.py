@@ -55,7 +55,7 @@ class MsaStep(ctypes.Structure):
 
 
 EXPORTS = ["msa_kv_append", "msa_index_score", "msa_select_topk", "msa_append_score_select",
-           "msa_sparse_decode", "msa_sparse_decode_union",
+           "msa_sparse_decode", "msa_sparse_decode_union", "msa_sparse_decode_combine_noalloc",
            "msa_sparse_decode_combine", "msa_select_decode_combine", "msa_combine",
            "msa_merge_workspace_init",
            "msa_decode_workspace_bytes", "msa_pool_bytes", "msa_index_bytes", "msa_status_string",
@@ -77,6 +77,7 @@ def load_library(path: str):
         "msa_sparse_decode": (I32, [P, P, I32, P, P, P, I32, F32, I32, P, P, P]),
         "msa_sparse_decode_union": (I32, [P, P, I32, P, P, P, I32, I32, P, I32, F32, I32, P, P, P, P]),
         "msa_sparse_decode_combine": (I32, [P, P, I32, P, P, P, I32, F32, I32, P, P, P, P, P]),
+        "msa_sparse_decode_combine_noalloc": (I32, [P, P, I32, P, P, P, I32, F32, I32, P, P]),
         "msa_select_decode_combine": (I32, [P, P, I32, P, P, I32, I32, I32, F32, I32, P, P, P, P, P, P, P]),
         "msa_combine": (I32, [I32, I32, I32, I32, P, P, P, P]),
         "msa_merge_workspace_init": (I32, [I32, I32, I32, I32, P, P, P, P]),
@@ -305,6 +306,16 @@ def msa_sparse_decode_combine(pool: KVPool, step: Step, q, sel, k, softmax_scale
         _ptr(part_ml, torch.float32, "part_ml"), _ptr(counters, torch.int32, "counters"),
         _ptr(out, torch.bfloat16, "out"), _stream(stream)),
         "msa_sparse_decode_combine")
+
+
+def msa_sparse_decode_combine_noalloc(pool: KVPool, step: Step, q, sel, k, softmax_scale, num_splits, out,
+                                      sel_pages=None, stream=None):
+    ps, ss = pool.cstruct(), step.cstruct()
+    _check(LIB.msa_sparse_decode_combine_noalloc(
+        ctypes.byref(ps), ctypes.byref(ss), q.shape[1], _ptr(q, torch.bfloat16, "q"),
+        _ptr(sel, torch.int32, "sel"), _ptr(sel_pages, torch.int32, "sel_pages"), k,
+        float(softmax_scale), num_splits, _ptr(out, torch.bfloat16, "out"), _stream(stream)),
+        "msa_sparse_decode_combine_noalloc")
 
 
 def msa_select_decode_combine(pool: KVPool, step: Step, q, block_scores, k, n_init, n_local,

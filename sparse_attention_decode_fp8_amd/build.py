@@ -24,7 +24,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmsadecode.so")
 # The same sources with the device-side metadata checks (MSA_DEBUG_CHECKS).
 DEBUG_LIB = os.path.join(PKG, "libmsadecode_debug.so")
-SOURCES = ["kv_append.hip", "index_score.hip", "select_topk.hip", "sparse_decode.hip", "union_decode.hip",
+SOURCES = ["kv_append.hip", "index_score.hip", "select_topk.hip", "sparse_decode.hip", "union_decode.hip", "decode_no_alloc.hip",
            "combine.hip", "api.cpp"]
 # The bench's read references, a library of their own (not part of the decode path).
 PROBE_LIB = os.path.join(PKG, "libmsaprobe.so")

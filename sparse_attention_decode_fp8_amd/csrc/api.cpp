@@ -92,6 +92,7 @@ extern "C" const char* msa_status_string(msa_status_t status) {
     case MSA_ERR_INVALID_ARG: return "MSA_ERR_INVALID_ARG: null, misaligned or negative argument";
     case MSA_ERR_UNSUPPORTED: return "MSA_ERR_UNSUPPORTED: geometry or format outside the contract";
     case MSA_ERR_LAUNCH: return "MSA_ERR_LAUNCH: kernel launch failed";
+    case MSA_ERR_TOO_LARGE: return "MSA_ERR_TOO_LARGE: the call needs more than the allocation-free entry's fixed scratch";
   }
   return "MSA_ERR_UNKNOWN";
 }

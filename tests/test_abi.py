@@ -291,3 +291,20 @@ def test_union_decode_validation_rejects_before_launch():
     assert U(B(pool), B(s1), 32, P(16), None, None, 8, 1, P(16), 4, 0.1, 1, None, None, P(16), None) == -1
     assert U(B(pool), B(s1), 32, P(16), P(16), None, 8, -1, P(16), 4, 0.1, 1, None, None, P(16), None) == -1
     assert U(B(pool), B(s1), 32, P(16), P(16), None, 8, 1, P(16), 4, 0.0, 1, None, None, P(16), None) == -1
+
+
+def test_no_alloc_entry_refuses_oversized_calls_on_the_host():
+    """The allocation-free decode checks its fixed scratch limit before any HIP call."""
+    B = ctypes.byref
+    P = ctypes.c_void_p
+    N = L.LIB.msa_sparse_decode_combine_noalloc
+    pool = _fake_pool()
+    # pool, step, hq, q, sel, sel_pages, k, scale, S, out, stream
+    assert N(B(pool), B(_fake_step()), 32, P(16), P(16), None, 8, 0.1, 2, P(16), None) == 0
+    # 8 MiB holds 16 rows x 32 heads x 16 splits x 130 fp32 (4.3 MB) but not 64 rows
+    assert N(B(pool), B(_fake_step(rows=64)), 32, P(16), P(16), None, 8, 0.1, 16, P(16), None) == -4
+    assert L.LIB.msa_status_string(-4).decode().startswith("MSA_ERR_TOO_LARGE")
+    assert N(B(pool), B(_fake_step(rows=1)), 32, P(16), P(16), None, 8, 0.1, 17, P(16), None) == -2
+    assert N(B(pool), B(_fake_step(rows=1)), 32, P(16), P(16), None, 8, 0.1, 0, P(16), None) == -1
+    assert N(B(pool), B(_fake_step(rows=1)), 32, P(16), P(16), None, 8, 0.1, 2, None, None) == -1
+    assert N(None, B(_fake_step(rows=1)), 32, P(16), P(16), None, 8, 0.1, 2, P(16), None) == -1
