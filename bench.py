@@ -82,6 +82,9 @@ def parse():
                     help="skip the 1 GiB streaming-read reference measurement")
     ap.add_argument("--no-pairing", action="store_true",
                     help="skip the query-pairing comparison (workloads with several rows per request)")
+    ap.add_argument("--counters-pass", action="store_true",
+                    help="rocprofv3 --pmc runs: only the replica cycle and the timed steps (then the "
+                         "calibration copy); pool replicas for 64 MiB between reuses unless --replicas")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one device copy of this size (counter calibration)")
     return ap.parse_args()
@@ -89,7 +92,7 @@ def parse():
 
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
-    for f in ("sparse_decode.hip", "msa_device.h", "select_device.h"):
+    for f in ("sparse_decode.hip", "decode_device.h", "msa_device.h", "select_device.h"):
         with open(os.path.join(ROOT, "sparse_attention_decode_fp8_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -169,14 +172,14 @@ def selected_units(wl, sel):
     return np.asarray(units, dtype=np.int32).reshape(-1, 3)
 
 
-def auto_replicas(wl, pool_bytes, budget=48 << 30):
-    """Pool replicas so that at least MIN_REUSE_BYTES of decode reads alone pass between
+def auto_replicas(wl, pool_bytes, budget=48 << 30, reuse=MIN_REUSE_BYTES):
+    """Pool replicas so that at least `reuse` bytes of decode reads alone pass between
     two uses of a replica (the decode moves the fewest bytes of the step's kernels):
-    1 + 512 MiB / (bytes of k selected blocks per row and KV head), a multiple of 8, at
+    1 + reuse / (bytes of k selected blocks per row and KV head), a multiple of 8, at
     most 512 and within `budget` bytes of device memory."""
     bpt = 144 if wl.fmt == 2 else 256
     est = sum(min(int(p) // 128 + 1, wl.k) * 128 for p in wl.row_pos) * wl.num_kv_heads * bpt
-    r = 1 + -(-MIN_REUSE_BYTES // max(est, 1))
+    r = 1 + -(-reuse // max(est, 1))
     r = -(-r // 8) * 8
     return int(max(8, min(r, 512, budget // max(pool_bytes, 1))))
 
@@ -199,6 +202,18 @@ def page_read_probe(torch, pools, units, stream):
         assert st == 0, f"msa_probe_page_read returned {st}"
     launch.keep = (dev_units, sink)
     return launch
+
+
+def calibration_copy(torch, dev, mib):
+    """One device copy of `mib` MiB (a kernel of known traffic for the counter scale)."""
+    if not mib:
+        return
+    a = torch.empty(mib << 20, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
 
 
 def main():
@@ -235,7 +250,8 @@ def main():
         M.msa_kv_append(pool0, torch.from_numpy(wl.slots(s, np.arange(L))).to(dev),
                         bf16(wl.k_src[s][:L]), bf16(wl.v_src[s][:L]), bf16(wl.idx_src[s][:L]))
     torch.cuda.synchronize()
-    R = args.replicas or auto_replicas(wl, sum(a.numel() * a.element_size() for a in pool0.arrays().values()))
+    pool_bytes = sum(a.numel() * a.element_size() for a in pool0.arrays().values())
+    R = args.replicas or auto_replicas(wl, pool_bytes, reuse=(64 << 20) if args.counters_pass else MIN_REUSE_BYTES)
     pools = [pool0] + [pool0.clone() for _ in range(R - 1)]
     tables = wl.num_kv_heads if args.per_kv_head else 1
     step = M.Step(wl.block_table, wl.row_seq, wl.row_pos, sel_tables=tables)
@@ -295,6 +311,11 @@ def main():
     ms_total = ev0.elapsed_time(ev1)
     ms_per_step = ms_total / args.steps
     print(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.2f} us/step", file=sys.stderr, flush=True)
+    if args.counters_pass:
+        calibration_copy(torch, dev, args.calib_copy_mib)
+        print(json.dumps({"counters_pass": wl.name, "replicas": R, "num_splits": ns, "steps": args.steps,
+                          "us_per_step": ms_per_step * 1e3}), flush=True)
+        return
     reps = max(MIN_REPLAYS, args.replays)
 
     def time_replays(g, per_replay):
@@ -451,25 +472,20 @@ def main():
     achieved = dec_bytes / t_dec / 1e9
 
     traffic = None
-    prof = os.path.join(ROOT, "profiles", "msa_select_decode_combine_b8_ctx32k_nvfp4_top16.counters.json")
+    # HBM bytes per launch of the decode kernel from the committed rocprofv3 counter
+    # digest of this workload, if it was taken from the current kernel sources
+    prof = os.path.join(ROOT, "profiles", f"{decode_kernels[0]}_{wl.name}.counters.json")
     if os.path.exists(prof):
         with open(prof) as fh:
             pc = json.load(fh)
         if (pc.get("source_digest") == kernel_source_digest() and pc.get("num_splits") == ns
-                and tables == 1 and args.config == WORKLOAD_CFG and args.index_fmt == "e4m3"
-                and not args.separate and select_in == "decode"):
+                and pc.get("workload") == wl.name and tables == 1 and not args.separate
+                and select_in == "decode"):
             traffic = pc.get("hbm_bytes_per_launch")
 
     box_read = None if args.no_read_probe else stream_read_gbs(torch, dev)
 
-    if args.calib_copy_mib:
-        n = args.calib_copy_mib << 20
-        a = torch.empty(n, dtype=torch.uint8, device=dev)
-        b = torch.empty_like(a)
-        a.fill_(1)
-        torch.cuda.synchronize()
-        b.copy_(a)
-        torch.cuda.synchronize()
+    calibration_copy(torch, dev, args.calib_copy_mib)
 
     cpu = cpu_all = None
     if not args.no_cpu_baseline:
