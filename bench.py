@@ -556,14 +556,21 @@ def main():
 
 
 def cpu_model() -> str:
+    """The host CPU as /proc/cpuinfo names it (model name, family / model / stepping,
+    max MHz from lscpu's source where present) and the logical CPUs this process may use."""
+    info = {}
     try:
         with open("/proc/cpuinfo") as fh:
             for ln in fh:
-                if ln.startswith("model name"):
-                    return ln.split(":", 1)[1].strip()
+                if ":" in ln:
+                    k, v = ln.split(":", 1)
+                    info.setdefault(k.strip(), v.strip())
     except OSError:
         pass
-    return "unknown"
+    name = info.get("model name", "unknown")
+    fam = f"family {info.get('cpu family', '?')} model {info.get('model', '?')} stepping {info.get('stepping', '?')}"
+    usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return f"{name} ({fam}; {os.cpu_count()} logical CPUs, {usable} usable by this process)"
 
 
 def cpu_baseline(wl, budget_s, thread_counts, tables=1):
