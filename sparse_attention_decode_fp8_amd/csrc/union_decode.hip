@@ -58,10 +58,16 @@ struct UnionArgs {
   int32_t* err;
 };
 
-// kR: the rows of a group the kernel is compiled for (1, 2 or 4).
+// kR: the rows of a group the kernel is compiled for (1, 2 or 4). kPipe: the next
+// round's chunk is loaded while the wave computes the current one (a second set of
+// chunk registers; off where those registers would not fit beside four rows' state).
+template <int kFmt, int kR, bool kDirect>
+constexpr bool union_pipelined() { return !(kFmt == MSA_KV_FP8_E4M3 && kR == 4); }
+
 template <int kFmt, int kR, bool kDirect>
 __global__ void __launch_bounds__(64 * kUnionWaves) union_decode_kernel(UnionArgs a) {
   constexpr int kW = kUnionWaves;
+  constexpr bool kPipe = union_pipelined<kFmt, kR, kDirect>();
   // Dynamic LDS: the union bitmap while the union is built, then the per-wave V staging
   // buffers and, at the end, the per-wave O tiles of one row at a time.
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
@@ -180,44 +186,53 @@ __global__ void __launch_bounds__(64 * kUnionWaves) union_decode_kernel(UnionArg
   typedef __attribute__((address_space(3))) short4_t lds_s4;
   const KvArrays kv = a.kv;
 
-  for (int round = 0; round < n_items; round += kW) {
-    // ---- this wave's chunk: union entry lo + it / 4, 32-token chunk it % 4
+  // One chunk of a round as a wave holds it: its registers and per-row visible tokens.
+  struct Item {
+    ChunkRegs<kFmt> R;
+    int nvis[kR];
+    bool valid;
+    float kps, vps;
+  };
+  // Issue every load of this wave's chunk of the round at `round`: union entry
+  // lo + it / 4, 32-token chunk it % 4 (past the split: zero-byte loads, not valid).
+  auto issue = [&](Item& X, int round) {
     const int it = round + wave;
     const int ue = lo + min(it, n_items - 1) / 4, c = it & 3;
     const int blk = __builtin_amdgcn_readfirstlane(ublk[ue]);
     const int msk = __builtin_amdgcn_readfirstlane(umask[ue]);
-    int nvis[kR];
     int nv_any = 0;
 #pragma unroll
     for (int i = 0; i < kR; ++i) {
       const int nv = min(pos_r[i] - blk * kPage + 1, kPage) - 32 * c;
-      nvis[i] = (it < n_items && i < nr && ((msk >> i) & 1)) ? min(max(nv, 0), 32) : 0;
-      nv_any = max(nv_any, nvis[i]);
+      X.nvis[i] = (it < n_items && i < nr && ((msk >> i) & 1)) ? min(max(nv, 0), 32) : 0;
+      nv_any = max(nv_any, X.nvis[i]);
     }
-    const bool valid = nv_any > 0;
-    int64_t pg = valid ? checked_page(upage[ue], a.num_pages, a.err) : 0;
+    X.valid = nv_any > 0;
+    int64_t pg = X.valid ? checked_page(upage[ue], a.num_pages, a.err) : 0;
     pg = static_cast<int64_t>(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(pg))));
-    ChunkRegs<kFmt> R;
-    load_chunk<kFmt>(R, kv, pg * a.hkv + g, valid, c, n, q);
-    float kps = 1.0f, vps = 1.0f;
+    load_chunk<kFmt>(X.R, kv, pg * a.hkv + g, X.valid, c, n, q);
+    X.kps = X.vps = 1.0f;
     if constexpr (kFmt == MSA_KV_FP8_E4M3) {
-      kps = reinterpret_cast<const float*>(a.kv.k_scales)[pg];
-      vps = reinterpret_cast<const float*>(a.kv.v_scales)[pg];
+      X.kps = reinterpret_cast<const float*>(a.kv.k_scales)[pg];
+      X.vps = reinterpret_cast<const float*>(a.kv.v_scales)[pg];
     }
-    if (!valid) continue;
+  };
+  auto compute = [&](Item& X) {
+    if (!X.valid) return;
+    const float kps = X.kps, vps = X.vps;
     const uint32_t* ksc = nullptr;
     const uint32_t* vsc = nullptr;
-    if constexpr (kFmt == MSA_KV_NVFP4) { ksc = R.ks; vsc = R.vs; }
+    if constexpr (kFmt == MSA_KV_NVFP4) { ksc = X.R.ks; vsc = X.R.vs; }
     // ---- V chunk to LDS once for every row (natural [token][d] layout, fp16)
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        *reinterpret_cast<half8_t*>(vb + (16 * u + n) * kVRowHalves + 32 * q + 8 * kk) = dequant8<kFmt>(R.v, vsc, u, kk);
+        *reinterpret_cast<half8_t*>(vb + (16 * u + n) * kVRowHalves + 32 * q + 8 * kk) = dequant8<kFmt>(X.R.v, vsc, u, kk);
     asm volatile("" ::: "memory");
 #pragma unroll
     for (int i = 0; i < kR; ++i) {
-      if (nvis[i] <= 0) continue;
+      if (X.nvis[i] <= 0) continue;
       half8_t Qi[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) Qi[j] = qlds[i][j][lane];
@@ -232,13 +247,13 @@ __global__ void __launch_bounds__(64 * kUnionWaves) union_decode_kernel(UnionArg
       for (int u = 0; u < 2; ++u) {
         acc[u] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) acc[u] = mfma16x16x32(dequant8<kFmt>(R.k, ksc, u, kk), Qi[kk], acc[u]);
+        for (int kk = 0; kk < 4; ++kk) acc[u] = mfma16x16x32(dequant8<kFmt>(X.R.k, ksc, u, kk), Qi[kk], acc[u]);
       }
       float x[2][4];
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) x[u][j] = (16 * u + 4 * q + j) < nvis[i] ? acc[u][j] * cs : -INFINITY;
+        for (int j = 0; j < 4; ++j) x[u][j] = (16 * u + 4 * q + j) < X.nvis[i] ? acc[u][j] * cs : -INFINITY;
       float mx = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
                        fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
       mx = rows_max(mx);
@@ -272,6 +287,26 @@ __global__ void __launch_bounds__(64 * kUnionWaves) union_decode_kernel(UnionArg
       }
     }
     asm volatile("" ::: "memory");   // (the next chunk's V writes stay behind these reads)
+  };
+
+  if constexpr (kPipe) {
+    // Two register sets: a round's loads are in flight while the wave computes the
+    // round before (every chunk issues the same loads, so the wait before each compute
+    // leaves exactly the later round's loads outstanding).
+    Item A, B;
+    issue(A, 0);
+    for (int round = 0; round < n_items; round += 2 * kW) {
+      issue(B, round + kW);
+      compute(A);
+      issue(A, round + 2 * kW);
+      compute(B);
+    }
+  } else {
+    Item A;
+    for (int round = 0; round < n_items; round += kW) {
+      issue(A, round);
+      compute(A);
+    }
   }
 
   // ---- per row: merge the waves' states through LDS, write the output or the partial
