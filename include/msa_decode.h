@@ -334,8 +334,8 @@ msa_status_t msa_select_decode_combine(const msa_kv_pool_t* pool, const msa_step
  *     [num_rows][num_q_heads][num_splits][head_dim] and part_ml fp32
  *     [num_rows][num_q_heads][num_splits][2], for msa_combine (out unused, may be NULL);
  *     a split that holds none of a row's blocks writes m = -inf, l = 0, O = 0 for it
- * 1 <= num_splits <= max_group_rows * k. The release library drops a table entry that
- * is neither -1 nor a visible block of its row; the debug library also reports it
+ * 1 <= num_splits <= 64 (msa_combine's limit). The release library drops a table entry
+ * that is neither -1 nor a visible block of its row, or whose page is negative; the debug library also reports it
  * (MSA_DEBUG_BAD_SEL) and reports a group that breaks the rules above
  * (MSA_DEBUG_BAD_GROUP), whose rows are then clamped to [0, num_rows) and to
  * max_group_rows.

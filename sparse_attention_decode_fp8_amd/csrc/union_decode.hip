@@ -113,6 +113,9 @@ __global__ void __launch_bounds__(64 * kUnionWaves) union_decode_kernel(UnionArg
     if (!dcheck(b >= -1 && b < min(pos / kPage + 1, a.max_blocks), MSA_DEBUG_BAD_SEL, a.err)) b = -1;
     if (b >= 0)
       page = a.sel_pages ? a.sel_pages[trow * a.k + e] : a.block_table[static_cast<int64_t>(seq0) * a.max_blocks + b];
+    // (a negative page, e.g. a -1 table entry reached through a group that mixes
+    // requests, is dropped rather than read before the pool)
+    if (page < 0) b = -1;
     if (e == 0) {
       s_pos[rho] = pos;
       dcheck(a.row_seq[r] == a.row_seq[r0], MSA_DEBUG_BAD_GROUP, a.err);
@@ -394,7 +397,8 @@ extern "C" msa_status_t msa_sparse_decode_union(const msa_kv_pool_t* pool, const
   if (st != MSA_OK) return st;
   if ((st = check_step(step)) != MSA_OK) return st;
   if (num_q_heads != MSA_HEADS_PER_KV * pool->num_kv_heads) return MSA_ERR_UNSUPPORTED;
-  if (k < 1 || k > MSA_MAX_TOPK || num_splits < 1 || num_splits > kMaxGroupRows * k) return MSA_ERR_UNSUPPORTED;
+  // (as many splits as msa_combine merges)
+  if (k < 1 || k > MSA_MAX_TOPK || num_splits < 1 || num_splits > MSA_MAX_TOPK) return MSA_ERR_UNSUPPORTED;
   if (max_group_rows < 1 || max_group_rows > kMaxGroupRows) return MSA_ERR_UNSUPPORTED;
   if (num_groups < 0) return MSA_ERR_INVALID_ARG;
   if (!(softmax_scale > 0.0f)) return MSA_ERR_INVALID_ARG;

@@ -274,10 +274,10 @@ def test_union_decode_validation_rejects_before_launch():
     # args: pool, step, hq, q, sel, sel_pages, k, groups, group_rows, max_rows, scale, S, po, pm, out, stream
     assert U(B(pool), B(step), 32, P(16), P(16), None, 8, 1, P(16), 4, 0.1, 1, None, None, P(16), None) == 0
     assert U(B(pool), B(s1), 32, P(16), P(16), None, 8, 0, P(16), 4, 0.1, 1, None, None, P(16), None) == 0
-    # geometry: heads, k, split count (up to max_group_rows * k), group size
+    # geometry: heads, k, split count (up to 64, as msa_combine), group size
     assert U(B(pool), B(s1), 48, P(16), P(16), None, 8, 1, P(16), 4, 0.1, 1, None, None, P(16), None) == -2
     assert U(B(pool), B(s1), 32, P(16), P(16), None, 65, 1, P(16), 4, 0.1, 1, None, None, P(16), None) == -2
-    assert U(B(pool), B(s1), 32, P(16), P(16), None, 8, 1, P(16), 4, 0.1, 33, P(16), P(16), None, None) == -2
+    assert U(B(pool), B(s1), 32, P(16), P(16), None, 8, 1, P(16), 4, 0.1, 65, P(16), P(16), None, None) == -2
     assert U(B(pool), B(s1), 32, P(16), P(16), None, 8, 1, P(16), 5, 0.1, 1, None, None, P(16), None) == -2
     assert U(B(pool), B(s1), 32, P(16), P(16), None, 8, 1, P(16), 0, 0.1, 1, None, None, P(16), None) == -2
     assert U(B(pool), B(s1), 32, P(16), P(16), None, 8, 65536 // 2, P(16), 4, 0.1, 1, None, None, P(16),

@@ -117,6 +117,32 @@ def test_bad_metadata_is_reported(M, dbg, fmt):
             M.msa_debug_set_error_word(None)
 
 
+def test_bad_union_groups_are_reported_and_stay_in_bounds(M, dbg):
+    """msa_sparse_decode_union with malformed row groups (longer than max_group_rows,
+    mixing two requests, past num_rows): the debug library reports
+    MSA_DEBUG_BAD_GROUP and the kernel clamps the group to its first rows inside the
+    call, so every access stays in bounds; a valid grouping reports nothing."""
+    wl = W.small(W.FMT_NVFP4, [1500, 2200], 4, num_kv_heads=2, k=5, seed=98)
+    pool = G.gpu_pool(M, wl)
+    step = M.Step(wl.block_table, wl.row_seq, wl.row_pos)
+    q = G.dev_bf16(wl.q)
+    sel = torch.from_numpy(W.verify_tables(wl, 0.5)).cuda()
+    out = torch.zeros(wl.num_rows, wl.num_heads, 128, dtype=torch.bfloat16, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    with M.use_library(dbg):
+        M.msa_debug_set_error_word(err)
+        try:
+            for groups, want in (([0, 4, 8], 0), ([0, 8], 7), ([2, 6], 7), ([4, 12], 7), ([0, 3, 4, 8], 0)):
+                _print("debug: union groups", groups)
+                gr = torch.tensor(groups, dtype=torch.int32, device="cuda")
+                M.msa_sparse_decode_union(pool, step, q, sel, wl.k, gr, 4, wl.softmax_scale, 1, out=out)
+                torch.cuda.synchronize()
+                assert int(err.item()) == want, (groups, int(err.item()))
+                err.zero_()
+        finally:
+            M.msa_debug_set_error_word(None)
+
+
 @pytest.mark.parametrize("entry", ["select_decode_combine", "sparse_decode_combine"])
 def test_merge_give_up_is_reported_and_sticky(M, dbg, entry):
     """A merging split that gives up waiting (forced from the host: a poll limit of 0,

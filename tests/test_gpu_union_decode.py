@@ -202,3 +202,45 @@ def test_union_config2_sampled_requests(M, shared):
     up = O.union_partials(opool, wl.block_table, wl.row_seq[sub], wl.row_pos[sub], wl.q[sub], sel[sub],
                           wl.softmax_scale, 2, sub_groups)
     _check_partials((parts[0][sub], parts[1][sub]), up, range(len(rows)))
+
+
+def test_union_edge_cases(M):
+    """k = 64 over 4 rows (256 picks), more splits than union entries, zero-row groups,
+    and rows in no group (left untouched)."""
+    wl = W.small(W.FMT_NVFP4, [9000, 12000], 4, num_kv_heads=1, k=64, seed=45)
+    _print("union edge cases", wl.name)
+    pool = _full_gpu_pool(M, wl)
+    opool = _oracle_pool_all(wl)
+    sel = W.verify_tables(wl, 0.4)
+    ref = O.attend(opool, wl.block_table, wl.row_seq, wl.row_pos, wl.q, sel, wl.softmax_scale)
+    groups = M.group_rows_of(wl.row_seq, 4)
+    for ns in (1, 5):
+        out, parts = _union(M, wl, pool, sel, groups, 4, ns)
+        G.assert_out_close(out, ref, f"k 64, {ns} splits")
+        if parts is not None:
+            up = O.union_partials(opool, wl.block_table, wl.row_seq, wl.row_pos, wl.q, sel, wl.softmax_scale,
+                                  ns, groups)
+            _check_partials(parts, up, range(wl.num_rows))
+    # full overlap at k = 5: 5 union entries per group over 20 splits, so most splits
+    # hold nothing
+    wl5 = W.small(W.FMT_FP8, [1022, 2600], 4, num_kv_heads=1, k=5, seed=46)
+    pool5, opool5 = _full_gpu_pool(M, wl5), _oracle_pool_all(wl5)
+    sel5 = W.verify_tables(wl5, 1.0)
+    groups5 = M.group_rows_of(wl5.row_seq, 4)
+    ref5 = O.attend(opool5, wl5.block_table, wl5.row_seq, wl5.row_pos, wl5.q, sel5, wl5.softmax_scale)
+    out, parts = _union(M, wl5, pool5, sel5, groups5, 4, 20)
+    G.assert_out_close(out, ref5, "20 splits over 5 or 6 entries")
+    up = O.union_partials(opool5, wl5.block_table, wl5.row_seq, wl5.row_pos, wl5.q, sel5, wl5.softmax_scale, 20,
+                          groups5)
+    _check_partials(parts, up, range(wl5.num_rows))
+    # zero-row groups and rows in no group: rows 4..7 are not in any group
+    step = M.Step(wl.block_table, wl.row_seq, wl.row_pos)
+    q = G.dev_bf16(wl.q)
+    sel_d = torch.from_numpy(sel).cuda()
+    gr = torch.tensor([0, 0, 2, 2, 4], dtype=torch.int32, device="cuda")
+    o = torch.full((wl.num_rows, wl.num_heads, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    M.msa_sparse_decode_union(pool, step, q, sel_d, wl.k, gr, 4, wl.softmax_scale, 1, out=o)
+    torch.cuda.synchronize()
+    got = G.bf16_to_np(o)
+    G.assert_out_close(got[:4], ref[:4], "groups [0,0) [0,2) [2,2) [2,4)")
+    assert np.isnan(got[4:]).all(), "rows in no group were written"
