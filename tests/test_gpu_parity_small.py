@@ -51,6 +51,17 @@ def test_full_step_parity(M, fmt, num_splits, fused):
 
 
 @pytest.mark.parametrize("fmt", [W.FMT_FP8, W.FMT_NVFP4])
+@pytest.mark.parametrize("num_kv_heads,num_splits,fused", [(8, 1, True), (8, 4, True), (8, 2, False), (3, 2, True)])
+def test_step_parity_other_kv_head_counts(M, fmt, num_kv_heads, num_splits, fused):
+    """8 KV heads (128 query heads) and 3 KV heads: the (row, KV head) grid, the query
+    and output strides and the per-KV-head page regions at head counts other than the
+    workloads' 1 and 4."""
+    wl = W.small(fmt, [1500, 700, 2600], 2, num_kv_heads=num_kv_heads, k=4, seed=33)
+    _print("step parity", wl.name, "KV heads", num_kv_heads, "splits", num_splits, "fused", fused)
+    G.check_step_parity(M, wl, num_splits, fused)
+
+
+@pytest.mark.parametrize("fmt", [W.FMT_FP8, W.FMT_NVFP4])
 @pytest.mark.parametrize("num_splits", [1, 4])
 def test_full_step_parity_select_in_scoring_launch(M, fmt, num_splits):
     """The fused step with the selection at the end of the scoring launch (one-wave

@@ -244,3 +244,21 @@ def test_union_edge_cases(M):
     got = G.bf16_to_np(o)
     G.assert_out_close(got[:4], ref[:4], "groups [0,0) [0,2) [2,2) [2,4)")
     assert np.isnan(got[4:]).all(), "rows in no group were written"
+
+
+@pytest.mark.parametrize("fmt", [W.FMT_NVFP4, W.FMT_FP8])
+def test_union_eight_kv_heads(M, fmt):
+    wl = W.small(fmt, [1022, 2600], 4, num_kv_heads=8, k=5, seed=47)
+    _print("union, 8 KV heads", wl.name)
+    pool = _full_gpu_pool(M, wl)
+    opool = _oracle_pool_all(wl)
+    sel = W.verify_tables(wl, 0.7)
+    ref = O.attend(opool, wl.block_table, wl.row_seq, wl.row_pos, wl.q, sel, wl.softmax_scale)
+    groups = M.group_rows_of(wl.row_seq, 4)
+    for ns in (1, 3):
+        out, parts = _union(M, wl, pool, sel, groups, 4, ns)
+        G.assert_out_close(out, ref, f"8 KV heads, {ns} splits")
+        if parts is not None:
+            up = O.union_partials(opool, wl.block_table, wl.row_seq, wl.row_pos, wl.q, sel, wl.softmax_scale,
+                                  ns, groups)
+            _check_partials(parts, up, range(wl.num_rows))
