@@ -12,14 +12,15 @@
 // which rows picked each block; the first pick of a block (rows in order, each table in
 // order) becomes a union entry (block, page, row mask). Split s of S takes the union
 // entries [s N / S, (s + 1) N / S) of the N entries. As in the one-row decode, each
-// wave takes one 32-token chunk per round, issues all of its loads before computing,
-// and stages V in its LDS buffer; here it does so once for every row of the entry's
-// mask, and then, for each of those rows that sees a token of the chunk, computes the
-// row's scores (K dequantised from the same registers), its online softmax and its O
-// update. Every wave holds the softmax state and O of all the group's rows (32 fp32
-// per row and lane), so the four-row variant takes more registers than the one-row
-// decode. The waves' states are merged row by row through LDS. One split writes the
-// bf16 output itself; several write partials in msa_sparse_decode's layout, which
+// wave takes one 32-token chunk per round and stages V in its LDS buffer; here it does
+// so once for every row of the entry's mask, and then, for each of those rows that sees
+// a token of the chunk, computes the row's scores (K dequantised from the same
+// registers, Q read from LDS), its online softmax and its O update. The rounds are
+// software-pipelined: the next round's chunk is loaded into a second register set while
+// the current one is computed. Every wave holds the softmax state and O of all the
+// group's rows (32 fp32 per row and lane), so the four-row variant runs two waves per
+// SIMD. The waves' states are merged row by row through LDS. One split writes the bf16
+// output itself; several write partials in msa_sparse_decode's layout, which
 // msa_combine merges.
 #include <algorithm>
 
