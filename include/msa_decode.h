@@ -335,10 +335,10 @@ msa_status_t msa_select_decode_combine(const msa_kv_pool_t* pool, const msa_step
  *     [num_rows][num_q_heads][num_splits][2], for msa_combine (out unused, may be NULL);
  *     a split that holds none of a row's blocks writes m = -inf, l = 0, O = 0 for it
  * 1 <= num_splits <= 64 (msa_combine's limit). The release library drops a table entry
- * that is neither -1 nor a visible block of its row, or whose page is negative; the debug library also reports it
- * (MSA_DEBUG_BAD_SEL) and reports a group that breaks the rules above
- * (MSA_DEBUG_BAD_GROUP), whose rows are then clamped to [0, num_rows) and to
- * max_group_rows.
+ * that is neither -1 nor a visible block of its row, or whose page is negative; the
+ * debug library also reports it (MSA_DEBUG_BAD_SEL) and reports a group that breaks
+ * the rules above (MSA_DEBUG_BAD_GROUP), whose rows are then clamped to
+ * [0, num_rows) and to max_group_rows.
  */
 msa_status_t msa_sparse_decode_union(const msa_kv_pool_t* pool, const msa_step_t* step,
                                      int32_t num_q_heads, const void* q, const int32_t* sel,
@@ -357,7 +357,8 @@ msa_status_t msa_sparse_decode_union(const msa_kv_pool_t* pool, const msa_step_t
  * bytes), exceed it returns MSA_ERR_TOO_LARGE and launches nothing. num_splits == 1
  * decodes in one launch without touching the array; num_splits > 1 (<= 16) decodes into
  * it and merges with msa_combine, two launches. Nothing is allocated or freed (the
- * first call on a device looks up the array's address). Every call on one GPU shares
+ * first call on a device looks up the array's address; MSA_ERR_LAUNCH if the runtime
+ * cannot give it). Other errors as msa_sparse_decode_combine. Every call on one GPU shares
  * that GPU's array: calls that can overlap on one GPU (on different streams, or from
  * several host threads) race and must be ordered by the caller.
  */
