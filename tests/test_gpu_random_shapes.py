@@ -62,3 +62,59 @@ def test_random_small_step(M, i):
 def M():
     import sparse_attention_decode_fp8_amd as M
     return M
+
+
+N_UNION_CASES = 24
+
+
+def _union_case(i):
+    r = np.random.default_rng([2027, i])
+    hkv = int(r.choice([1, 2, 4, 8]))
+    k = int(r.choice([1, 3, 5, 8, 16, 32]))
+    n_append = int(r.choice([2, 3, 4]))
+    lens = [max(1, int(x)) for x in r.integers(1, 7000, size=int(r.integers(1, 4)))]
+    return dict(fmt=int(r.choice([W.FMT_FP8, W.FMT_NVFP4])), hkv=hkv, k=k, n_append=n_append, lens=lens,
+                overlap=float(r.choice([0.0, 0.5, 0.9, 1.0])), group=int(r.integers(1, 5)),
+                splits=int(r.choice([1, 2, 3, 5, 9])), pages=bool(r.random() < 0.5),
+                tables=hkv if (hkv in (2, 4) and r.random() < 0.3) else 1, seed=4000 + i)
+
+
+@pytest.mark.parametrize("i", range(N_UNION_CASES))
+def test_random_union_decode(M, i):
+    import torch
+    from oracle import msa_oracle as O
+    c = _union_case(i)
+    print("random union", i, c, flush=True)
+    wl = W.small(c["fmt"], c["lens"], c["n_append"], num_kv_heads=c["hkv"], k=c["k"], seed=c["seed"])
+    pool = G.gpu_pool(M, wl)
+    sl, kb, vb, ib = wl.step_tokens()
+    M.msa_kv_append(pool, torch.from_numpy(sl).cuda(), G.dev_bf16(kb), G.dev_bf16(vb), G.dev_bf16(ib))
+    if c["tables"] > 1:
+        sel = np.stack([W.verify_tables(wl, c["overlap"], seed_tag=5 + t) for t in range(c["tables"])], axis=1)
+    else:
+        sel = W.verify_tables(wl, c["overlap"])
+    pages = None
+    if c["pages"]:
+        pages = np.where(sel >= 0, wl.block_table[wl.row_seq.reshape((-1,) + (1,) * (sel.ndim - 1)),
+                                                  np.maximum(sel, 0)], -1).astype(np.int32)
+    groups = M.group_rows_of(wl.row_seq, c["group"])
+    step = M.Step(wl.block_table, wl.row_seq, wl.row_pos, sel_tables=c["tables"])
+    q = G.dev_bf16(wl.q)
+    sel_d = torch.from_numpy(np.ascontiguousarray(sel, dtype=np.int32)).cuda()
+    pg_d = None if pages is None else torch.from_numpy(np.ascontiguousarray(pages)).cuda()
+    gr = torch.from_numpy(groups).cuda()
+    out = torch.zeros(wl.num_rows, wl.num_heads, 128, dtype=torch.bfloat16, device="cuda")
+    ns = c["splits"]
+    if ns == 1:
+        M.msa_sparse_decode_union(pool, step, q, sel_d, wl.k, gr, c["group"], wl.softmax_scale, 1, out=out,
+                                  sel_pages=pg_d)
+    else:
+        po = torch.zeros(wl.num_rows, wl.num_heads, ns, 128, device="cuda")
+        pm = torch.zeros(wl.num_rows, wl.num_heads, ns, 2, device="cuda")
+        M.msa_sparse_decode_union(pool, step, q, sel_d, wl.k, gr, c["group"], wl.softmax_scale, ns, part_o=po,
+                                  part_ml=pm, sel_pages=pg_d)
+        M.msa_combine(wl.num_rows, wl.num_heads, 128, ns, po, pm, out)
+    torch.cuda.synchronize()
+    opool = G.oracle_pool(wl)
+    ref = O.attend(opool, wl.block_table, wl.row_seq, wl.row_pos, wl.q, sel, wl.softmax_scale)
+    G.assert_out_close(G.bf16_to_np(out), ref, f"union case {i}")
