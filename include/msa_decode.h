@@ -334,6 +334,11 @@ msa_status_t msa_select_decode_combine(const msa_kv_pool_t* pool, const msa_step
  *     [num_rows][num_q_heads][num_splits][head_dim] and part_ml fp32
  *     [num_rows][num_q_heads][num_splits][2], for msa_combine (out unused, may be NULL);
  *     a split that holds none of a row's blocks writes m = -inf, l = 0, O = 0 for it
+ * Choosing group sizes: a group's rows share each page read and V's dequantisation,
+ * but every row of a group keeps its own scores, softmax and O, and the four-row
+ * variant runs two waves per SIMD. Groups of several rows pay only when the rows share
+ * nearly all of their blocks; groups of one row (the rounds software-pipelined) are
+ * the faster one-split table-driven decode of 40 x 4 verify rows on gfx950.
  * 1 <= num_splits <= 64 (msa_combine's limit). The release library drops a table entry
  * that is neither -1 nor a visible block of its row, or whose page is negative; the
  * debug library also reports it (MSA_DEBUG_BAD_SEL) and reports a group that breaks
