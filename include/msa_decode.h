@@ -256,9 +256,10 @@ msa_status_t msa_sparse_decode(const msa_kv_pool_t* pool, const msa_step_t* step
                                int32_t num_splits, float* part_o, float* part_ml, void* stream);
 
 /*
- * msa_sparse_decode followed by msa_combine in one launch: the last split of each
- * (row, KV head) to count itself in merges all splits of that row and head exactly as
- * msa_combine does ([Rubin] "Items and numerics", LC_ONEDIV: same order, same
+ * msa_sparse_decode followed by msa_combine in one launch: the last splits of each
+ * (row, KV head) to count themselves in (the largest power of two not above num_splits,
+ * each taking an equal slice of the 16 query heads) merge all splits of that row and
+ * head exactly as msa_combine does ([Rubin] "Items and numerics", LC_ONEDIV: same order, same
  * arithmetic, so `out` equals msa_sparse_decode + msa_combine bit for bit) and writes
  * bf16 `out` [num_rows][num_q_heads][head_dim].
  *   part_o, part_ml, counters : the merge workspace. part_o fp32
@@ -267,9 +268,10 @@ msa_status_t msa_sparse_decode(const msa_kv_pool_t* pool, const msa_step_t* step
  *     (row, KV head), used by alternate calls (the layout does not depend on num_rows,
  *     so a workspace sized for R rows serves any call with num_rows <= R);
  *     counters int32 [num_rows][num_kv_heads] holds one state word
- *     per (row, KV head): bit 31 = the buffer the next call uses, bits 16..30 = the
- *     split count the workspace is set up for, bits 0..15 = arrivals (zero between
- *     calls). msa_merge_workspace_init sets it up for one num_splits (both buffers
+ *     per (row, KV head): bit 31 = the buffer the next call uses, bits 26..30 = the
+ *     split count the workspace is set up for, bit 25 = a failure bit (below), bits
+ *     8..22 = slices handed from one merging split to another and bits 0..7 = arrivals
+ *     (both zero between calls). msa_merge_workspace_init sets it up for one num_splits (both buffers
  *     idle: every word MSA_MERGE_IDLE_BITS); every call with that num_splits leaves it
  *     ready for the next one. The partials pass through the buffers and are not left
  *     readable. An allocation sized for S splits serves any num_splits <= S after a
@@ -279,10 +281,12 @@ msa_status_t msa_sparse_decode(const msa_kv_pool_t* pool, const msa_step_t* step
  *     changing num_splits. With num_splits == 1 the one split writes `out` itself and
  *     the workspace is neither read nor written. Two calls that share a workspace must
  *     not run concurrently. num_splits <= 16.
- *   The merging split waits for the other splits' partials with a bounded poll (about
- *     2^16 rounds; every split it waits for is already running). If the bound is ever
- *     reached (a split held off the GPU for milliseconds), the outputs it could not
- *     merge are bf16 NaN and the pair's state word keeps a failure bit (bit 15), so
+ *   The last split to arrive waits for the other splits' partials with a bounded poll
+ *     (about 2^16 rounds; every split it waits for is already running). A merging split
+ *     that arrived earlier polls for a few dozen rounds at most, then hands its slice to
+ *     the last split (the outputs are the same either way). If the last split's bound is
+ *     ever reached (a split held off the GPU for milliseconds), the outputs it could not
+ *     merge are bf16 NaN and the pair's state word keeps the failure bit, so
  *     every later call writes NaN for that (row, KV head) as for a workspace set up for
  *     another split count, until msa_merge_workspace_init; the debug library also
  *     reports MSA_DEBUG_MERGE_TIMEOUT.
@@ -438,9 +442,13 @@ const char* msa_status_string(msa_status_t status);
  * it. msa_debug_set_merge_poll_limit sets the number of poll rounds after which a
  * merging split gives up (polls < 0: the release bound; 0: give up without reading,
  * which lets a test force the failure path while every kernel still exits normally).
- * Both are process-wide state of the debug library only. The release library returns
- * MSA_ERR_UNSUPPORTED for both, and msa_debug_checks_enabled tells the two apart
- * (1 / 0).
+ * msa_debug_set_merge_helper_poll_limit sets the number of poll rounds after which a
+ * merging split other than the last to arrive hands its slice of the heads to the last
+ * one (polls < 0: the release bound; 0: hand over at once wherever the last split has
+ * not yet arrived, which lets a test force the handoff path; the outputs are the same
+ * either way). All three are process-wide state of the debug library only. The release
+ * library returns MSA_ERR_UNSUPPORTED for them, and msa_debug_checks_enabled tells the
+ * two builds apart (1 / 0).
  */
 typedef enum {
   MSA_DEBUG_OK = 0,
@@ -455,6 +463,7 @@ typedef enum {
 
 msa_status_t msa_debug_set_error_word(int32_t* word);
 msa_status_t msa_debug_set_merge_poll_limit(int32_t polls);
+msa_status_t msa_debug_set_merge_helper_poll_limit(int32_t polls);
 int32_t msa_debug_checks_enabled(void);
 
 #ifdef __cplusplus

@@ -11,6 +11,7 @@ from ._lib import (FMT_FP8, FMT_NVFP4, IDX_E4M3, IDX_NVFP4, KVPool, MsaError, St
                    msa_sparse_decode_combine_noalloc,
                    msa_append_score_select, msa_select_decode_combine, msa_merge_workspace_init,
                    MERGE_IDLE_BITS, msa_debug_set_error_word, msa_debug_set_merge_poll_limit,
+                   msa_debug_set_merge_helper_poll_limit,
                    load_library, use_library,
                    RELEASE_LIB_PATH, DEBUG_LIB_PATH)
 from .pipeline import DecodeBuffers, default_num_splits, run_step  # noqa: F401

@@ -59,7 +59,8 @@ EXPORTS = ["msa_kv_append", "msa_index_score", "msa_select_topk", "msa_append_sc
            "msa_sparse_decode_combine", "msa_select_decode_combine", "msa_combine",
            "msa_merge_workspace_init",
            "msa_decode_workspace_bytes", "msa_pool_bytes", "msa_index_bytes", "msa_status_string",
-           "msa_debug_set_error_word", "msa_debug_set_merge_poll_limit", "msa_debug_checks_enabled"]
+           "msa_debug_set_error_word", "msa_debug_set_merge_poll_limit", "msa_debug_set_merge_helper_poll_limit",
+           "msa_debug_checks_enabled"]
 
 
 def load_library(path: str):
@@ -87,6 +88,7 @@ def load_library(path: str):
         "msa_status_string": (ctypes.c_char_p, [I32]),
         "msa_debug_set_error_word": (I32, [P]),
         "msa_debug_set_merge_poll_limit": (I32, [I32]),
+        "msa_debug_set_merge_helper_poll_limit": (I32, [I32]),
         "msa_debug_checks_enabled": (I32, []),
     }
     for name, (res, args) in sig.items():
@@ -126,6 +128,13 @@ def msa_debug_set_merge_poll_limit(polls: int):
     """Debug library: poll rounds after which a merging split gives up (< 0: the release
     bound; 0: at once, to force the failure path). The release library raises MsaError."""
     _check(LIB.msa_debug_set_merge_poll_limit(int(polls)), "msa_debug_set_merge_poll_limit")
+
+
+def msa_debug_set_merge_helper_poll_limit(polls: int):
+    """Debug library: poll rounds after which a merging split other than the last to
+    arrive hands its slice to the last one (< 0: the release bound; 0: at once, to force
+    the handoff path). The release library raises MsaError."""
+    _check(LIB.msa_debug_set_merge_helper_poll_limit(int(polls)), "msa_debug_set_merge_helper_poll_limit")
 
 
 def _check(status: int, what: str):

@@ -56,6 +56,10 @@ int32_t* debug_error_word() { return g_debug_error_word; }
 // The debug library's bound on a merging split's poll rounds (< 0: the release bound).
 static int32_t g_merge_poll_limit = -1;
 int32_t merge_poll_limit() { return g_merge_poll_limit < 0 ? kMergePollLimit : g_merge_poll_limit; }
+static int32_t g_merge_helper_poll_limit = -1;
+int32_t merge_helper_poll_limit() {
+  return g_merge_helper_poll_limit < 0 ? kMergeHelperPolls : g_merge_helper_poll_limit;
+}
 }  // namespace msa
 
 extern "C" msa_status_t msa_debug_set_error_word(int32_t* word) {
@@ -71,6 +75,16 @@ extern "C" msa_status_t msa_debug_set_error_word(int32_t* word) {
 extern "C" msa_status_t msa_debug_set_merge_poll_limit(int32_t polls) {
 #ifdef MSA_DEBUG_CHECKS
   msa::g_merge_poll_limit = polls;
+  return MSA_OK;
+#else
+  (void)polls;
+  return MSA_ERR_UNSUPPORTED;
+#endif
+}
+
+extern "C" msa_status_t msa_debug_set_merge_helper_poll_limit(int32_t polls) {
+#ifdef MSA_DEBUG_CHECKS
+  msa::g_merge_helper_poll_limit = polls;
   return MSA_OK;
 #else
   (void)polls;

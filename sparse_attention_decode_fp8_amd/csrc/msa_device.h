@@ -221,6 +221,9 @@ __device__ __forceinline__ float4_t load_coherent4(__amdgpu_buffer_rsrc_t r, uin
   return __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0,
                                                                           kCoherentPolicy));
 }
+__device__ __forceinline__ float load_coherent1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, kCoherentPolicy));
+}
 __device__ __forceinline__ float2_t load_coherent2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(float2_t, __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(off), 0,
                                                                          kCoherentPolicy));
@@ -279,18 +282,31 @@ __device__ __forceinline__ int lane_varying_zero() {
 constexpr int kMaxMergeSplits = 16;
 
 // Merge state word of one (row, KV head) pair in the combining decode's workspace: bit
-// 31 = which of the two exchange buffers the next launch uses, bits 16..30 = the split
-// count the workspace was set up for, bits 0..15 = splits arrived in the current launch
-// (at most 16, so bit 15 is free for kMergeTimeoutBit, which makes the word invalid).
+// 31 = which of the two exchange buffers the next launch uses, bits 26..30 = the split
+// count the workspace was set up for, bit 25 = kMergeTimeoutBit (which makes the word
+// invalid), bits 8..22 = slices handed to the last split by merging splits that gave up
+// waiting for it (kMergeHandoffShift), bits 0..7 = splits arrived in the current launch.
 __host__ __device__ __forceinline__ uint32_t merge_state(int buffer, int num_splits) {
-  return (static_cast<uint32_t>(buffer) << 31) | (static_cast<uint32_t>(num_splits) << 16);
+  return (static_cast<uint32_t>(buffer) << 31) | (static_cast<uint32_t>(num_splits) << 26);
 }
+constexpr uint32_t kMergeArrivalMask = 0xffu;
+constexpr int kMergeHandoffShift = 8;
+constexpr uint32_t kMergeHandoffMask = 0x7fffu << kMergeHandoffShift;
 // Set for good by a merger that gave up polling: every later launch finds the word
-// invalid (its arrivals field then exceeds any split count) until the workspace is set up
-// again.
-constexpr uint32_t kMergeTimeoutBit = 1u << 15;
+// invalid until the workspace is set up again.
+constexpr uint32_t kMergeTimeoutBit = 1u << 25;
 __device__ __forceinline__ bool merge_state_ok(uint32_t w, int num_splits) {
-  return ((w >> 16) & 0x7fffu) == static_cast<uint32_t>(num_splits) && (w & 0xffffu) < static_cast<uint32_t>(num_splits);
+  return ((w >> 26) & 0x1fu) == static_cast<uint32_t>(num_splits) && (w & kMergeTimeoutBit) == 0u &&
+         (w & kMergeArrivalMask) < static_cast<uint32_t>(num_splits);
+}
+// The split merge of a pair's 16 heads is shared by its last merge_slices(S) splits to
+// arrive, each taking 16 / merge_slices(S) heads: the largest power of two not above S
+// (at most 16, one head each; the handoff field holds one bit for each slice but the
+// last).
+__host__ __device__ __forceinline__ int merge_slices(int num_splits) {
+  int k = 1;
+  while (2 * k <= num_splits && 2 * k <= kMaxMergeSplits) k *= 2;
+  return k;
 }
 
 // Workgroup barrier that orders LDS only: waits for this wave's LDS accesses, not for

@@ -10,9 +10,15 @@ namespace msa {
 
 // The debug library's error word (null in the release library, or when unset).
 int32_t* debug_error_word();
-// Bound on a merging split's poll rounds: kMergePollLimit, or the debug library's setting.
+// Bound on the last split's merge poll rounds: kMergePollLimit, or the debug library's
+// setting.
 constexpr int32_t kMergePollLimit = 1 << 16;
 int32_t merge_poll_limit();
+// Bound on the poll rounds of a merging split that is not the last to arrive, before it
+// hands its slice to the last one: kMergeHelperPolls, or the debug library's setting.
+// (A poll round is one agent-coherent load round trip, about a microsecond.)
+constexpr int32_t kMergeHelperPolls = 32;
+int32_t merge_helper_poll_limit();
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

@@ -24,10 +24,11 @@
 // Every load a wave needs (selection entry, page id, K/V codes and scales, Q) is
 // issued before the first MFMA, so the kernel pays the memory latency once.
 //
-// The combining variants have the last workgroup of each (row, KV head) to count
-// itself in merge all splits, so the step needs no separate combine launch; with a
-// single split that workgroup writes the output directly and the merge workspace is
-// not touched. The partials cross workgroups (and XCDs, whose L2s are not coherent
+// The combining variants have the last workgroups of each (row, KV head) to count
+// themselves in merge all splits, each a slice of the 16 heads, so the step needs no
+// separate combine launch and no one compute unit pulls every partial; with a single
+// split that workgroup writes the output directly and the merge workspace is not
+// touched. The partials cross workgroups (and XCDs, whose L2s are not coherent
 // with each other) through agent-coherent stores that the merger polls against an idle
 // pattern: no cache-flushing fence (on this part such fences cost more than the whole
 // merge) and no wait for store acknowledgements. Two exchange buffers alternate
@@ -41,6 +42,7 @@
 // returns zeros without a memory access), so the query's conversion and everything
 // else that waits on earlier loads does not wait for the page data.
 #include <algorithm>
+#include <type_traits>
 
 #include "msa_device.h"
 #include "msa_host.h"
@@ -82,10 +84,13 @@ struct DecodeArgs {
   int num_seqs, num_pages;
   int32_t* err;               // debug library: the error word of failed metadata checks
   uint16_t* out;              // combining variants: bf16 [rows][hq][128]
-  // Bound on the merger's poll rounds (kMergePollLimit; the debug library can lower it).
-  // Every slot it polls has been stored by a split that is already past its compute, so
-  // a few rounds suffice; the bound only keeps the loop finite.
+  // Bound on the last split's poll rounds (kMergePollLimit; the debug library can lower
+  // it). Every slot it polls has been stored by a split that is already past its
+  // compute, so a few rounds suffice; the bound only keeps the loop finite.
   int poll_limit;
+  // Bound on the poll rounds of a merging split that is not the last to arrive, before
+  // it hands its slice to the last one (kMergeHelperPolls; the debug library can set it).
+  int helper_poll_limit;
 };
 
 template <int kFmt, int kItems>
@@ -130,18 +135,31 @@ __device__ __forceinline__ void load_round(Round<kFmt, kItems>& rd, const Decode
   }
 }
 
-// The merging split's read of one (head, 4 dims) item: all S <= kS slots (its own
-// included: the thread stored its part of it, so it reads its own values back), then
-// the fixed-order log-sum-exp sums of msa_combine. Slots whose words have not all
-// landed are read again, which is rare: the other splits counted themselves in
-// earlier. Entries S..kS-1 repeat the last slot and are not used, so every entry is
+// kV consecutive floats of one split's partial, read agent-coherently.
+template <int kV>
+__device__ __forceinline__ void load_slot(__amdgpu_buffer_rsrc_t r, uint32_t off, float (&v)[kV]) {
+  if constexpr (kV == 4) {
+    const float4_t x = load_coherent4(r, off);
+    v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
+  } else if constexpr (kV == 2) {
+    const float2_t x = load_coherent2(r, off);
+    v[0] = x[0]; v[1] = x[1];
+  } else {
+    v[0] = load_coherent1(r, off);
+  }
+}
+
+// A merging split's read of kV consecutive output dims d.. of head h: all S <= kS
+// slots (its own included: it stored them and reads them back), then the fixed-order
+// log-sum-exp sums of msa_combine. Slots whose words have not all landed are read
+// again. Entries S..kS-1 repeat the last slot and are not used, so every entry is
 // redefined on each read and none is carried from one poll to the next. Returns false
 // if some word was still idle after `limit` rounds (num and den are then meaningless).
-template <int kS>
+template <int kS, int kV>
 __device__ __forceinline__ bool merge_slots(__amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t rm, int S,
-                                            int h, int d4, int limit, float4_t& num, float& den) {
+                                            int h, int d, int limit, float (&num)[kV], float& den) {
   float2_t mls[kS];
-  float4_t ot[kS];
+  float ot[kS][kV];
   bool ready = false;
   for (int spin = 0; !ready && spin < limit; ++spin) {
     if (spin > 0) {
@@ -152,19 +170,24 @@ __device__ __forceinline__ bool merge_slots(__amdgpu_buffer_rsrc_t ro, __amdgpu_
     for (int t = 0; t < kS; ++t) {   // every load first, one wait
       const int tt = min(t, S - 1);
       mls[t] = load_coherent2(rm, (h * S + tt) * 8u);
-      ot[t] = load_coherent4(ro, ((h * S + tt) * kHeadDim + 4 * d4) * 4u);
+      load_slot<kV>(ro, ((h * S + tt) * kHeadDim + d) * 4u, ot[t]);
     }
     asm volatile("" ::: "memory");   // the loads stay together, ahead of their tests
     uint32_t key = ~0u;
 #pragma unroll
-    for (int t = 0; t < kS; ++t) key = idle_key(idle_key(key, mls[t]), ot[t]);
+    for (int t = 0; t < kS; ++t) {
+      key = idle_key(key, mls[t]);
+#pragma unroll
+      for (int i = 0; i < kV; ++i) key = idle_key(key, ot[t][i]);
+    }
     ready = key != 0u;
   }
   float M = -INFINITY;
 #pragma unroll
   for (int t = 0; t < kS; ++t)
     if (t < S) M = fmaxf(M, mls[t][0]);
-  num = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int i = 0; i < kV; ++i) num[i] = 0.0f;
   den = 0.0f;
 #pragma unroll
   for (int t = 0; t < kS; ++t) {
@@ -172,14 +195,45 @@ __device__ __forceinline__ bool merge_slots(__amdgpu_buffer_rsrc_t ro, __amdgpu_
       const float m = mls[t][0];
       const float wgt = m == -INFINITY ? 0.0f : exp2_raw(m - M);   // M > -inf whenever m is
       den += wgt * mls[t][1];
-      num += wgt * ot[t];
+#pragma unroll
+      for (int i = 0; i < kV; ++i) num[i] += wgt * ot[t][i];
     }
   }
   return ready;
 }
 
+template <int kV>
+__device__ __forceinline__ bool merge_slots_any(__amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t rm, int S, int h,
+                                                int d, int limit, float (&num)[kV], float& den) {
+  if (S <= 2) return merge_slots<2, kV>(ro, rm, S, h, d, limit, num, den);
+  if (S <= 4) return merge_slots<4, kV>(ro, rm, S, h, d, limit, num, den);
+  if (S <= 8) return merge_slots<8, kV>(ro, rm, S, h, d, limit, num, den);
+  return merge_slots<16, kV>(ro, rm, S, h, d, limit, num, den);
+}
+
+// A merging split that is not the last to arrive hands its slice to the last one: it
+// sets the slice's bit in the state word, which succeeds only while the last split has
+// not yet counted itself in (the bit is then in the old word that split's count
+// returns). Returns false once the last split has arrived (or the word is invalid):
+// every split has then counted itself in. Each failed exchange means the word changed
+// (an arrival or another slice's handoff, a bounded number per launch).
+__device__ __forceinline__ bool merge_handoff(int32_t* word, uint32_t buffer, int S, int slice) {
+  uint32_t w = static_cast<uint32_t>(__hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  for (int tries = 0; tries < 64; ++tries) {
+    if ((w >> 31) != buffer || (w & kMergeTimeoutBit) != 0u || (w & kMergeArrivalMask) >= static_cast<uint32_t>(S))
+      return false;
+    int32_t expected = static_cast<int32_t>(w);
+    if (__hip_atomic_compare_exchange_strong(word, &expected,
+                                             static_cast<int32_t>(w | (1u << (kMergeHandoffShift + slice))),
+                                             __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+      return true;
+    w = static_cast<uint32_t>(expected);
+  }
+  return false;
+}
+
 // What a workgroup writes: its split's partial (kOutPartials), the bf16 output of the
-// only split (kOutDirect), or its partial through the merge workspace, the last split
+// only split (kOutDirect), or its partial through the merge workspace, the last splits
 // of the (row, KV head) merging them all into the bf16 output (kOutMerged). The direct
 // variant holds none of the merge code, and so fewer registers. kSelect: 0 = the
 // caller's table; 1, 2, 4 or 8 = the workgroup selects, with the two-level selection at
@@ -199,7 +253,7 @@ sparse_decode_kernel(DecodeArgs a) {
   // then the per-wave V staging buffers and, at the end, the per-wave O tiles.
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
   __shared__ float mbuf[kW][16], lbuf[kW][16];
-  __shared__ int s_last;
+  __shared__ int s_word;
   __shared__ int32_t lsel[kSelect ? MSA_MAX_TOPK : 1], lpage[kSelect ? MSA_MAX_TOPK : 1];
   __shared__ half8_t qlds[kSelect ? 4 : 1][64];   // selecting variant: the converted Q operand
   __shared__ float qcs[kSelect ? 64 : 1];
@@ -462,6 +516,8 @@ sparse_decode_kernel(DecodeArgs a) {
   const __amdgpu_buffer_rsrc_t rm =
       make_rsrc(uniform_ptr(a.part_ml + (2 * head0 + 16 * cur) * a.num_splits * 2), ml_bytes);
   constexpr int kTasks = 16 * (kHeadDim / 4);                     // (head, 4 dims) items
+  // (a merger's slice, at most 8 heads, is at most 4 floats per thread)
+  static_assert(kOut != kOutMerged || kW >= 4, "merging needs 256 threads");
   constexpr int kPer = (kTasks + 64 * kW - 1) / (64 * kW);        // items per thread
   // In-workgroup merge of one item over the waves' O tiles. Every LDS read is issued
   // before the first use, so their latencies overlap.
@@ -523,15 +579,21 @@ sparse_decode_kernel(DecodeArgs a) {
           make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16));
     }
   } else {
-    // ---- several splits: the last split of this (row, KV head) to count itself in
-    // merges them all. Each split counts itself in as soon as its compute is done, then
-    // stores its partial (agent-coherent) into this launch's exchange buffer and only
-    // then reads the old count, so nothing waits for the stores to land; the merger
-    // polls each slot until none of its words holds the idle pattern. Every split it
-    // waits for has counted itself in, so it is resident with only in-workgroup work
-    // left before its stores: the polls end. The merger leaves the slots as they are
-    // (each split returns its own slot to idle early in the next launch that uses the
-    // other buffer) and flips the state word to the other buffer with no arrivals.
+    // ---- several splits: the last K = merge_slices(S) splits of this (row, KV head) to
+    // count themselves in merge them, each a slice of 16 / K heads. Each split counts
+    // itself in as soon as its compute is done, then stores its partial (agent-coherent)
+    // into this launch's exchange buffer and only then reads the old count, so nothing
+    // waits for the stores to land; a merger polls each slot of its slice until none of
+    // its words holds the idle pattern. The last split waits only for splits that have
+    // counted themselves in, which are resident with only in-workgroup work left before
+    // their stores: its polls end. The other mergers may wait for splits that have not
+    // counted themselves in yet, so their polls are bounded by helper_poll_limit, after
+    // which they hand their slice to the last split (merge_handoff) or, if it has arrived
+    // meanwhile, poll on under the last split's bound. Every slice is merged by exactly
+    // one workgroup with msa_combine's arithmetic. The mergers leave the slots as they
+    // are (each split returns its own slot to idle early in the next launch that uses
+    // the other buffer), and the last split flips the state word to the other buffer
+    // with no arrivals and no handoffs.
     if (!merge_state_ok(mstate, a.num_splits)) {
       // The workspace was not set up for this split count (or not set up): touch
       // nothing and make the failure visible in the output (bf16 NaN).
@@ -541,8 +603,9 @@ sparse_decode_kernel(DecodeArgs a) {
               make_uint2(0x7fc07fc0u, 0x7fc07fc0u);
       return;
     }
-    int32_t arrival = 0;   // the old state word; its low half counts the earlier splits
-    if (threadIdx.x == 0) arrival = atomicAdd(a.counters + static_cast<int64_t>(r) * a.hkv + g, 1);
+    int32_t* const word = a.counters + static_cast<int64_t>(r) * a.hkv + g;
+    int32_t arrival = 0;   // the old state word; its low byte counts the earlier splits
+    if (threadIdx.x == 0) arrival = atomicAdd(word, 1);
 #pragma unroll
     for (int it = 0; it < kPer; ++it) {
       // threads past the last item repeat an item (same values, same addresses), so no
@@ -559,44 +622,74 @@ sparse_decode_kernel(DecodeArgs a) {
       // does not wait for them
       store_coherent(rm, (h * a.num_splits + s) * 8u, float2_t{not_idle(M), not_idle(l)});
     }
-    // (the empty asm keeps the compiler from folding the mask into the atomic's block,
+    // (the empty asm keeps the compiler from folding the use into the atomic's block,
     // where it would wait for the count before the stores above are issued)
     asm volatile("" : "+v"(arrival));
-    if (threadIdx.x == 0) s_last = (arrival & 0xffff) == a.num_splits - 1;
+    if (threadIdx.x == 0) s_word = arrival;
     lds_barrier();
-    if (!s_last) return;
-#pragma unroll
-    for (int it = 0; it < kPer; ++it) {
-      const int idx = threadIdx.x + it * 64 * kW;
-      if (idx >= kTasks) break;
-      const int h = idx / (kHeadDim / 4), d4 = idx % (kHeadDim / 4);
-      float4_t num;
-      float den;
-      bool ok;
-      if (a.num_splits <= 2) ok = merge_slots<2>(ro, rm, a.num_splits, h, d4, a.poll_limit, num, den);
-      else if (a.num_splits <= 4) ok = merge_slots<4>(ro, rm, a.num_splits, h, d4, a.poll_limit, num, den);
-      else if (a.num_splits <= 8) ok = merge_slots<8>(ro, rm, a.num_splits, h, d4, a.poll_limit, num, den);
-      else ok = merge_slots<16>(ro, rm, a.num_splits, h, d4, a.poll_limit, num, den);
-      uint16_t o[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = den > 0.0f ? f32_to_bf16_rne(num[i] / den) : 0;
-      uint2 ov = make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16));
-      if (!ok) {
-        // gave up waiting: NaN outputs, and the pair's state word stays invalid until
-        // the workspace is set up again (an OR that commutes with the flip below)
-        ov = make_uint2(0x7fc07fc0u, 0x7fc07fc0u);
-        dcheck(false, MSA_DEBUG_MERGE_TIMEOUT, a.err);
-        __hip_atomic_fetch_or(a.counters + static_cast<int64_t>(r) * a.hkv + g, static_cast<int32_t>(kMergeTimeoutBit),
-                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t w0 = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(s_word));
+    const int S = a.num_splits, K = merge_slices(S);
+    const int slice0 = static_cast<int>(w0 & kMergeArrivalMask) - (S - K);
+    if (slice0 < 0) return;
+    const bool last = slice0 == K - 1;
+    // slices this workgroup merges: its own, and (the last split) every handed-over one
+    uint32_t todo = 1u << slice0;
+    if (last) todo |= (w0 >> kMergeHandoffShift) & ((1u << (K - 1)) - 1u);
+    const int slice_floats = (16 / K) * kHeadDim;
+    // floats per thread: 1, 2 or 4, whichever lets every thread's loads go out at once
+    const int per = min(4, max(1, slice_floats / (64 * kW)));
+    const bool active = static_cast<int>(threadIdx.x) * per < slice_floats;
+    auto merge_into = [&](auto kv, int slice, int limit, bool helper) -> bool {
+      constexpr int kV = decltype(kv)::value;
+      const int e = slice * slice_floats + min(static_cast<int>(threadIdx.x) * kV, slice_floats - kV);
+      const int h = e / kHeadDim, d = e % kHeadDim;
+      float num[kV], den;
+      bool ok = active ? merge_slots_any<kV>(ro, rm, S, h, d, limit, num, den) : true;
+      if (helper && !__syncthreads_and(ok)) {
+        // some word of the slice is still idle: hand the slice over, or, if the last
+        // split has arrived in the meantime, wait for it under that split's bound
+        if (threadIdx.x == 0) s_word = merge_handoff(word, mstate >> 31, S, slice);
+        __syncthreads();
+        if (s_word) return true;
+        if (!ok) ok = merge_slots_any<kV>(ro, rm, S, h, d, a.poll_limit, num, den);
       }
-      *reinterpret_cast<uint2*>(a.out + (head0 + h) * kHeadDim + 4 * d4) = ov;
+      if (!active) return true;
+      uint16_t o[kV];
+#pragma unroll
+      for (int i = 0; i < kV; ++i) o[i] = ok ? (den > 0.0f ? f32_to_bf16_rne(num[i] / den) : 0) : 0x7fc0;
+      uint16_t* dst = a.out + (head0 + h) * kHeadDim + d;
+      if constexpr (kV == 4)
+        *reinterpret_cast<uint2*>(dst) =
+            make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16));
+      else if constexpr (kV == 2)
+        *reinterpret_cast<uint32_t*>(dst) = o[0] | (static_cast<uint32_t>(o[1]) << 16);
+      else
+        *dst = o[0];
+      return ok;
+    };
+    bool all_ok = true;
+    while (todo != 0u) {
+      const int slice = __builtin_ctz(todo);
+      todo &= todo - 1u;
+      const int limit = last ? a.poll_limit : min(a.poll_limit, a.helper_poll_limit);
+      if (per == 4) all_ok &= merge_into(std::integral_constant<int, 4>{}, slice, limit, !last);
+      else if (per == 2) all_ok &= merge_into(std::integral_constant<int, 2>{}, slice, limit, !last);
+      else all_ok &= merge_into(std::integral_constant<int, 1>{}, slice, limit, !last);
     }
-    // the other buffer, no arrivals: ready for the next launch. All num_splits arrivals
-    // have been counted (this split counted itself in last), so one XOR flips the buffer
-    // bit and clears the arrivals, and leaves any timeout bit set above in place.
-    if (threadIdx.x == 0)
-      __hip_atomic_fetch_xor(a.counters + static_cast<int64_t>(r) * a.hkv + g,
-                             static_cast<int32_t>((1u << 31) | static_cast<uint32_t>(a.num_splits)),
+    if (!all_ok) {
+      // gave up waiting: NaN outputs (written above), and the pair's state word stays
+      // invalid until the workspace is set up again (an OR that commutes with the flip)
+      dcheck(false, MSA_DEBUG_MERGE_TIMEOUT, a.err);
+      __hip_atomic_fetch_or(word, static_cast<int32_t>(kMergeTimeoutBit), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // The last split: the other buffer, no arrivals, no handoffs: ready for the next
+    // launch. All S arrivals have been counted and no handoff can follow the last one,
+    // so one XOR flips the buffer bit, clears the arrivals and the handoff bits it saw,
+    // and leaves any timeout bit in place.
+    if (last && threadIdx.x == 0)
+      __hip_atomic_fetch_xor(word,
+                             static_cast<int32_t>((1u << 31) | static_cast<uint32_t>(S) |
+                                                  (w0 & kMergeHandoffMask)),
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
@@ -685,6 +778,7 @@ msa_status_t decode_entry(const msa_kv_pool_t* pool, const msa_step_t* step, int
   a.num_pages = pool->num_pages;
   a.err = debug_error_word();
   a.poll_limit = merge_poll_limit();
+  a.helper_poll_limit = merge_helper_poll_limit();
   a.row_pos = step->row_pos;
   a.max_blocks = step->max_blocks_per_seq;
   a.q = static_cast<const uint16_t*>(q);

@@ -177,8 +177,8 @@ def assert_merge_ready(bufs):
     import sparse_attention_decode_fp8_amd as M
     S = bufs.num_splits
     c = bufs.counters.cpu().numpy().view(np.uint32)
-    assert ((c & 0xffff) == 0).all(), "arrivals left in a state word"
-    assert (((c >> 16) & 0x7fff) == S).all(), "state word names another split count"
+    assert ((c & ((1 << 26) - 1)) == 0).all(), "arrivals, handoffs or a failure left in a state word"
+    assert (((c >> 26) & 0x1f) == S).all(), "state word names another split count"
     rows, hkv = c.shape
     # pair-major, laid out for S splits (a workspace may be allocated for more)
     mo = bufs.merge_o.view(torch.int32).reshape(-1)[:rows * hkv * 2 * 16 * S * 128]

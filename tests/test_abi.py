@@ -52,6 +52,8 @@ def test_debug_library_exports_the_same_entry_points_and_its_setter():
     assert dbg.msa_debug_set_error_word(None) == 0
     assert rel.msa_debug_set_merge_poll_limit(0) == -2
     assert dbg.msa_debug_set_merge_poll_limit(0) == 0 and dbg.msa_debug_set_merge_poll_limit(-1) == 0
+    assert rel.msa_debug_set_merge_helper_poll_limit(0) == -2
+    assert dbg.msa_debug_set_merge_helper_poll_limit(0) == 0 and dbg.msa_debug_set_merge_helper_poll_limit(-1) == 0
     # host-side validation is the same in both builds
     B, P = ctypes.byref, ctypes.c_void_p
     pool, step = _fake_pool(), _fake_step()

@@ -182,7 +182,7 @@ def test_merge_give_up_is_reported_and_sticky(M, dbg, entry):
             assert int(err.item()) == 6                      # MSA_DEBUG_MERGE_TIMEOUT
             assert torch.isnan(bufs.out.float()).all()
             c = bufs.counters.cpu().numpy().view(np.uint32)
-            assert ((c & 0x8000) != 0).all() and (((c >> 16) & 0x7fff) == ns).all()
+            assert ((c & (1 << 25)) != 0).all() and (((c >> 26) & 0x1f) == ns).all()
             M.msa_debug_set_merge_poll_limit(-1)             # the release bound again
             err.zero_()
             words = [t.clone() for t in (bufs.counters, bufs.merge_o, bufs.merge_ml)]
@@ -198,3 +198,49 @@ def test_merge_give_up_is_reported_and_sticky(M, dbg, entry):
     call()
     assert torch.equal(bufs.out.view(torch.int16), ref.view(torch.int16))
     G.assert_merge_ready(bufs)
+
+
+@pytest.mark.parametrize("fmt", [W.FMT_FP8, W.FMT_NVFP4])
+def test_forced_merge_handoffs_give_the_same_outputs(M, dbg, fmt):
+    """The split merge of a (row, KV head) is shared by its last splits to arrive, each
+    merging a slice of the heads; one that is not the last hands its slice to the last
+    split when its bounded wait runs out. With the debug library's bound set to 0 every
+    such split hands over at once unless the last split has already arrived: the
+    outputs stay those of msa_sparse_decode + msa_combine bit for bit, nothing is
+    reported and the workspace is left ready, for split counts with 2 and 4 slices."""
+    wl = W.small(fmt, [3000, 2000, 5100, 700], 2, num_kv_heads=2, k=16, seed=99)
+    pool = G.gpu_pool(M, wl)
+    step, q, q_idx, w, app = G.gpu_step_inputs(M, wl)
+    M.msa_kv_append(pool, *app)
+    scores = torch.empty((wl.num_rows, wl.max_blocks), dtype=torch.float32, device="cuda")
+    M.msa_index_score(pool, step, q_idx, w, scores)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for ns in (2, 3, 4, 5, 8, 16):
+        _print("forced merge handoffs", wl.name, "splits", ns)
+        ref = M.DecodeBuffers(wl.num_rows, wl.num_heads, wl.max_blocks, wl.k, ns)
+        M.msa_select_topk(step, scores, wl.k, wl.n_init, wl.n_local, ref.sel, ref.sel_pages)
+        M.msa_sparse_decode(pool, step, q, ref.sel, wl.k, wl.softmax_scale, ns, ref.part_o, ref.part_ml,
+                            sel_pages=ref.sel_pages)
+        M.msa_combine(wl.num_rows, wl.num_heads, 128, ns, ref.part_o, ref.part_ml, ref.out)
+        bufs = M.DecodeBuffers(wl.num_rows, wl.num_heads, wl.max_blocks, wl.k, ns)
+        with M.use_library(dbg):
+            M.msa_debug_set_error_word(err)
+            try:
+                M.msa_debug_set_merge_helper_poll_limit(0)
+                for call in range(4):   # both exchange buffers, both fused entries
+                    bufs.out.fill_(0)
+                    if call % 2 == 0:
+                        M.msa_select_decode_combine(pool, step, q, scores, wl.k, wl.n_init, wl.n_local,
+                                                    wl.softmax_scale, ns, bufs.merge_o, bufs.merge_ml,
+                                                    bufs.counters, bufs.out)
+                    else:
+                        M.msa_sparse_decode_combine(pool, step, q, ref.sel, wl.k, wl.softmax_scale, ns,
+                                                    bufs.merge_o, bufs.merge_ml, bufs.counters, bufs.out,
+                                                    sel_pages=ref.sel_pages)
+                    torch.cuda.synchronize()
+                    assert int(err.item()) == 0, (ns, call)
+                    assert torch.equal(bufs.out.view(torch.int16), ref.out.view(torch.int16)), (ns, call)
+                    G.assert_merge_ready(bufs)
+            finally:
+                M.msa_debug_set_merge_helper_poll_limit(-1)
+                M.msa_debug_set_error_word(None)

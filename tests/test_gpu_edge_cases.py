@@ -74,4 +74,4 @@ def test_nothing_to_do_leaves_outputs_untouched(M):
     for t in (bufs.block_scores, bufs.sel, bufs.sel_pages, bufs.part_o, bufs.part_ml):
         assert bool((t == 7).all())
     assert bool((bufs.out.float() == 7.0).all())
-    assert bool((bufs.counters == (2 << 16)).all())   # as set up for 2 splits
+    assert bool((bufs.counters == (2 << 26)).all())   # as set up for 2 splits

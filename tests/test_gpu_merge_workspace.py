@@ -29,7 +29,7 @@ def test_workspace_init_sets_up_state(M):
     torch.cuda.synchronize()
     assert bool((po.view(torch.int32) == M.MERGE_IDLE_BITS).all())
     assert bool((pm.view(torch.int32) == M.MERGE_IDLE_BITS).all())
-    assert bool((cnt == (S << 16)).all())
+    assert bool((cnt == (S << 26)).all())
     assert bool((guard == 3.0).all())
 
 
