@@ -500,12 +500,17 @@ sparse_decode_kernel(DecodeArgs a) {
   float oscale;
   if constexpr (kFmt == MSA_KV_NVFP4) oscale = a.v_t; else oscale = v_cur;
   {
+    // (the lane's head and dim quarter again, from the hardware lane count: otherwise
+    // the compiler keeps the lane index live across the loop, and in the 16-wave
+    // variants, at 128 registers, spills it to scratch and reloads it here)
+    const int lane_e = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const int ne = lane_e & 15, qe = lane_e >> 4;
     // each wave's O tile goes to its own V buffer, which only it used: no barrier first
     float* ob = reinterpret_cast<float*>(dyn_lds + wave * kVBufBytes);   // [16 heads][kORowFloats]
 #pragma unroll
     for (int d = 0; d < 8; ++d)
-      *reinterpret_cast<float4_t*>(ob + n * kORowFloats + 16 * d + 4 * q) = O[d] * oscale;
-    if (q == 0) { mbuf[wave][n] = m_run; lbuf[wave][n] = l_tot; }
+      *reinterpret_cast<float4_t*>(ob + ne * kORowFloats + 16 * d + 4 * qe) = O[d] * oscale;
+    if (qe == 0) { mbuf[wave][ne] = m_run; lbuf[wave][ne] = l_tot; }
   }
   __syncthreads();
   // this (row, KV head)'s partials: O [16 heads][S][128], (m, l) [16 heads][S][2]
