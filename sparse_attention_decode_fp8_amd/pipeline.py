@@ -13,13 +13,13 @@ from . import _lib as L
 def default_num_splits(k: int, pairs: int) -> int:
     """Split count used by the benchmark and the full-size parity tests, for `pairs`
     (query row, KV head) pairs: enough splits for about 256 decode workgroups (one per
-    compute unit), a power of two, at most min(k / 2, 16) so that each split holds at
-    least two blocks. Few pairs (a small batch) are spread over many workgroups whose
-    partials are merged; many pairs fill the GPU on their own and skip the merge (one
-    split writes its output directly)."""
+    compute unit), a power of two, at most min(k, 16) (the fused merge takes at most 16
+    splits). Few pairs (a small batch) are spread over many workgroups whose partials
+    are merged, down to one block per split; many pairs fill the GPU on their own and
+    skip the merge (one split writes its output directly)."""
     target = max(1, 256 // max(1, pairs))
     s = 1
-    while s * 2 <= min(target, k // 2, 16):
+    while s * 2 <= min(target, k, 16):
         s *= 2
     return s
 

@@ -19,9 +19,9 @@ def _bench():
 
 
 def test_default_num_splits_policy():
-    # about 256 workgroups, a power of two, at most min(k / 2, 16)
+    # about 256 workgroups, a power of two, at most min(k, 16)
     assert default_num_splits(16, 32) == 8      # config 1: 8 rows x 4 KV heads
-    assert default_num_splits(8, 1) == 4        # config 0: k / 2
+    assert default_num_splits(8, 1) == 8        # config 0: one block per split
     assert default_num_splits(32, 8) == 16      # config 3: capped at 16
     assert default_num_splits(16, 640) == 1     # config 2: the pairs fill the GPU
     assert default_num_splits(16, 192) == 1     # config 4
@@ -29,7 +29,7 @@ def test_default_num_splits_policy():
     for k in range(1, 65):
         for pairs in (1, 3, 17, 100, 256, 1000):
             s = default_num_splits(k, pairs)
-            assert s >= 1 and (s & (s - 1)) == 0 and s <= max(1, min(k // 2, 16))
+            assert s >= 1 and (s & (s - 1)) == 0 and s <= min(k, 16) and s * pairs <= max(256, pairs)
     assert FUSED_APPEND_MAX == 64
 
 
