@@ -139,6 +139,14 @@ typedef struct {
  * Table t is scored from index heads [t * n_idx_heads / T, (t + 1) * n_idx_heads / T)
  * (n_idx_heads must be a multiple of T), selected by the same rule, and read by KV
  * head t. At most MSA_MAX_SEL_TABLES; negative is MSA_ERR_INVALID_ARG.
+ *
+ * rows_per_seq: 0 = not stated. R > 0 states that every request has exactly R rows
+ * (num_rows == num_seqs * R, else MSA_ERR_INVALID_ARG; negative is
+ * MSA_ERR_INVALID_ARG), as in a speculative step with a fixed draft length. The index
+ * scorer then launches one workgroup row per group of a request's rows instead of one
+ * per row (the rows of a group share their key reads). Results are the same either
+ * way. Like row_seq itself the statement is trusted; the debug library reports a wrong
+ * one as MSA_DEBUG_BAD_SEQ.
  */
 typedef struct {
   int32_t num_seqs;
@@ -148,6 +156,7 @@ typedef struct {
   const int32_t* row_seq;     /* [num_rows]                                              */
   const int32_t* row_pos;     /* [num_rows]                                              */
   int32_t sel_tables;         /* 0/1: shared selection; num_kv_heads: one per KV head    */
+  int32_t rows_per_seq;       /* 0: not stated; R > 0: every request has exactly R rows  */
 } msa_step_t;
 
 /*

@@ -11,6 +11,8 @@ from __future__ import annotations
 import ctypes
 import os
 
+import numpy as np
+
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -51,7 +53,7 @@ class MsaStep(ctypes.Structure):
     _fields_ = [("num_seqs", ctypes.c_int32), ("num_rows", ctypes.c_int32),
                 ("max_blocks_per_seq", ctypes.c_int32), ("block_table", ctypes.c_void_p),
                 ("row_seq", ctypes.c_void_p), ("row_pos", ctypes.c_void_p),
-                ("sel_tables", ctypes.c_int32)]
+                ("sel_tables", ctypes.c_int32), ("rows_per_seq", ctypes.c_int32)]
 
 
 EXPORTS = ["msa_kv_append", "msa_index_score", "msa_select_topk", "msa_append_score_select",
@@ -208,23 +210,39 @@ class KVPool:
         return c
 
 
+def rows_per_seq_of(row_seq, num_seqs: int) -> int:
+    """R if the request-major `row_seq` (host array) gives every one of the num_seqs
+    requests exactly R consecutive rows, else 0 (not stated)."""
+    rs = np.asarray(row_seq, dtype=np.int64).reshape(-1)
+    if num_seqs <= 0 or rs.size == 0 or rs.size % num_seqs != 0:
+        return 0
+    r = rs.size // num_seqs
+    return r if np.array_equal(rs, np.repeat(np.arange(num_seqs), r)) else 0
+
+
 class Step:
     """Per-step metadata on the GPU: block table, row -> request, row -> position, and
     the number of selection tables per row (1: shared by the KV heads; the pool's KV-head
-    count: one per KV head, with a table axis after the row in scores and selections)."""
+    count: one per KV head, with a table axis after the row in scores and selections).
+    rows_per_seq (see msa_step_t): None derives it from a host `row_seq` (0 when
+    row_seq is already a device tensor); an int states it."""
 
-    def __init__(self, block_table, row_seq, row_pos, device="cuda", sel_tables=1):
+    def __init__(self, block_table, row_seq, row_pos, device="cuda", sel_tables=1, rows_per_seq=None):
         bt = torch.as_tensor(block_table, dtype=torch.int32).to(device).contiguous()
         self.block_table = bt
+        self.num_seqs, self.max_blocks = bt.shape
+        if rows_per_seq is None:
+            on_device = isinstance(row_seq, torch.Tensor) and row_seq.device.type != "cpu"
+            rows_per_seq = 0 if on_device else rows_per_seq_of(row_seq, self.num_seqs)
+        self.rows_per_seq = int(rows_per_seq)
         self.row_seq = torch.as_tensor(row_seq, dtype=torch.int32).to(device).contiguous()
         self.row_pos = torch.as_tensor(row_pos, dtype=torch.int32).to(device).contiguous()
-        self.num_seqs, self.max_blocks = bt.shape
         self.num_rows = self.row_pos.numel()
         self.sel_tables = sel_tables
 
     def cstruct(self) -> MsaStep:
         return MsaStep(self.num_seqs, self.num_rows, self.max_blocks, self.block_table.data_ptr(),
-                       self.row_seq.data_ptr(), self.row_pos.data_ptr(), self.sel_tables)
+                       self.row_seq.data_ptr(), self.row_pos.data_ptr(), self.sel_tables, self.rows_per_seq)
 
 
 def msa_kv_append(pool: KVPool, slot, k_new=None, v_new=None, idx_k_new=None, stream=None):

@@ -55,6 +55,9 @@ struct ScoreArgs {
   int32_t* counters;
   int score_wgs_x;   // workgroups along x that score blocks
   int append_row;    // fused launch: 1 if grid row 0 holds the append workgroups
+  // > 0: every request has this many rows, and the grid has one row per group of
+  // rows (groups_per_seq per request) instead of one per query row
+  int rows_per_seq, groups_per_seq;
 };
 
 // A lane's share of one 16-token row of keys (token 16t + n, dims 16q .. 16q+15):
@@ -105,7 +108,10 @@ __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
     }
     if (static_cast<int>(blockIdx.x) >= a.score_wgs_x) return;
   }
-  const int r0 = static_cast<int>(blockIdx.y) - a.append_row;
+  // The group's first row: grid row y - append_row is row r0 itself, or, with a stated
+  // row count per request, group (request, i) of that request's rows.
+  int r0 = static_cast<int>(blockIdx.y) - a.append_row;
+  if (a.rows_per_seq > 0) r0 = (r0 / a.groups_per_seq) * a.rows_per_seq + (r0 % a.groups_per_seq) * kRowsPerGroup;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, q = lane >> 4;
   const int b = blockIdx.x * kWaves + wave;
@@ -132,6 +138,10 @@ __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
   int j = before != 0 ? __builtin_clz(before) : 32;               // run of equal rows ending at r0-1
   if (j == 32)
     while (r0 - j - 1 >= 0 && a.row_seq[r0 - j - 1] == seq_raw) ++j;
+  // (a stated row count per request puts r0 at a group's start: checked by the debug
+  // library, trusted by the release one)
+  dcheck(a.rows_per_seq == 0 || (j % kRowsPerGroup == 0 && seq_raw == r0 / a.rows_per_seq), MSA_DEBUG_BAD_SEQ,
+         a.err);
   if (j % kRowsPerGroup != 0) return;
   // rows r0 .. r0+nr-1 of the same request form the group
   const uint32_t after = ~static_cast<uint32_t>(same >> 32);       // bit i: row r0+i differs
@@ -408,6 +418,17 @@ ScoreArgs make_score_args(const msa_kv_pool_t* pool, const msa_step_t* step, con
   return a;
 }
 
+// Grid rows of the scoring workgroups: one per query row, or, with a stated row count
+// per request, one per group of a request's rows (16 / n_idx_heads rows per group).
+void set_score_rows(ScoreArgs& a, const msa_step_t* step, int n_idx_heads) {
+  const int per_group = 16 / n_idx_heads;
+  a.rows_per_seq = step->rows_per_seq;
+  a.groups_per_seq = a.rows_per_seq > 0 ? (a.rows_per_seq + per_group - 1) / per_group : 0;
+}
+int score_rows(const ScoreArgs& a, const msa_step_t* step) {
+  return a.rows_per_seq > 0 ? step->num_seqs * a.groups_per_seq : step->num_rows;
+}
+
 template <int kFmt, bool kFused, bool kIdxNv>
 void launch_score_fmt(const ScoreArgs& a, int hi, int tables, dim3 grid, size_t lds, hipStream_t s) {
   const dim3 block(64 * kWaves);
@@ -456,8 +477,9 @@ extern "C" msa_status_t msa_index_score(const msa_kv_pool_t* pool, const msa_ste
   if (q_idx == nullptr || w == nullptr || block_scores == nullptr || !aligned16(q_idx))
     return MSA_ERR_INVALID_ARG;
   if (step->num_rows > 65535) return MSA_ERR_UNSUPPORTED;
-  const ScoreArgs a = make_score_args(pool, step, q_idx, w, block_scores);
-  dim3 grid(a.score_wgs_x, step->num_rows);
+  ScoreArgs a = make_score_args(pool, step, q_idx, w, block_scores);
+  set_score_rows(a, step, n_idx_heads);
+  dim3 grid(a.score_wgs_x, score_rows(a, step));
   return launch_score<false>(a, pool, n_idx_heads, tables, grid, 0, static_cast<hipStream_t>(stream));
 }
 
@@ -488,6 +510,7 @@ extern "C" msa_status_t msa_append_score_select(
   if ((sel == nullptr) != (counters == nullptr)) return MSA_ERR_INVALID_ARG;
   if (step->num_rows >= 65535) return MSA_ERR_UNSUPPORTED;
   ScoreArgs a = make_score_args(pool, step, q_idx, w, block_scores);
+  set_score_rows(a, step, n_idx_heads);
   a.app = make_append_args(pool, n_new, slot, k_new, v_new, idx_k_new);
   a.k = k;
   a.n_init = n_init;
@@ -497,7 +520,7 @@ extern "C" msa_status_t msa_append_score_select(
   a.counters = counters;
   const int64_t app_wgs = (static_cast<int64_t>(n_new) * a.app.groups_per_tok + 255) / 256;
   a.append_row = n_new > 0 ? 1 : 0;
-  dim3 grid(static_cast<unsigned>(std::max<int64_t>(a.score_wgs_x, app_wgs)), step->num_rows + a.append_row);
+  dim3 grid(static_cast<unsigned>(std::max<int64_t>(a.score_wgs_x, app_wgs)), score_rows(a, step) + a.append_row);
   const size_t lds = sel ? static_cast<size_t>(step->max_blocks_per_seq) * sizeof(uint32_t) : 0;
   return launch_score<true>(a, pool, n_idx_heads, tables, grid, lds, static_cast<hipStream_t>(stream));
 }

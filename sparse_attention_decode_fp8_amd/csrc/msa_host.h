@@ -57,6 +57,10 @@ inline msa_status_t check_step(const msa_step_t* step) {
   if (step->num_rows > 0 && (step->num_seqs == 0 || step->block_table == nullptr ||
                              step->row_seq == nullptr || step->row_pos == nullptr))
     return MSA_ERR_INVALID_ARG;
+  if (step->rows_per_seq < 0 ||
+      (step->rows_per_seq > 0 &&
+       static_cast<int64_t>(step->num_seqs) * step->rows_per_seq != static_cast<int64_t>(step->num_rows)))
+    return MSA_ERR_INVALID_ARG;
   return MSA_OK;
 }
 

@@ -126,9 +126,9 @@ def _fake_pool(fmt=2, head_dim=128, k_t=1.0, index_fmt=0, index_scales=None, ind
                        index_scales, index_t)
 
 
-def _fake_step(rows=0, max_blocks=8, tables=0):
+def _fake_step(rows=0, max_blocks=8, tables=0, rows_per_seq=0):
     a = 1 << 20
-    return L.MsaStep(1, rows, max_blocks, a, a, a, tables)
+    return L.MsaStep(1, rows, max_blocks, a, a, a, tables, rows_per_seq)
 
 
 def test_validation_rejects_before_launch():
@@ -163,6 +163,13 @@ def test_validation_rejects_before_launch():
     assert L.LIB.msa_kv_append(B(bad), 1, P(16), None, None, None, None) == -1
     s1 = _fake_step(rows=1)
     assert L.LIB.msa_index_score(B(pool), B(s1), 4, None, P(16), P(16), None) == -1
+    # a stated row count per request must be exact (num_rows == num_seqs * R) and >= 0
+    for rps in (-1, 2):
+        sr = _fake_step(rows=1, rows_per_seq=rps)
+        assert L.LIB.msa_index_score(B(pool), B(sr), 4, P(16), P(16), P(16), None) == -1
+        assert L.LIB.msa_select_topk(B(sr), P(16), 4, 0, 1, P(16), None, None) == -1
+        assert L.LIB.msa_sparse_decode(B(pool), B(sr), 32, P(16), P(16), None, 8, 0.1, 2, P(16), P(16),
+                                       None) == -1
     assert L.LIB.msa_select_topk(B(s1), None, 4, 0, 1, P(16), None, None) == -1
     assert L.LIB.msa_sparse_decode(B(pool), B(s1), 32, P(16), P(16), None, 8, 0.0, 2, P(16), P(16), None) == -1
     assert L.LIB.msa_sparse_decode(B(pool), B(s1), 32, P(24), P(16), None, 8, 0.1, 2, P(16), P(16), None) == -1

@@ -95,3 +95,15 @@ def test_group_rows_keep_a_requests_rows_together_up_to_the_group_size():
     assert group_rows_of(np.zeros(0, np.int32), 4).tolist() == [0]
     # config 2's layout: 40 requests x 4 rows -> 40 groups of 4
     assert group_rows_of(np.repeat(np.arange(40), 4), 4).tolist() == list(range(0, 161, 4))
+
+
+def test_rows_per_seq_of():
+    """The Python Step states rows_per_seq only when every request has the same number
+    of consecutive rows."""
+    from sparse_attention_decode_fp8_amd._lib import rows_per_seq_of
+    assert rows_per_seq_of([0, 0, 0, 0, 1, 1, 1, 1], 2) == 4
+    assert rows_per_seq_of([0, 1, 2], 3) == 1
+    assert rows_per_seq_of([0, 0, 0, 1, 1, 1, 1, 1], 2) == 0     # 3 and 5 rows
+    assert rows_per_seq_of([0, 1, 0, 1], 2) == 0                 # not request-major
+    assert rows_per_seq_of([0, 0, 1, 1], 3) == 0                 # request 2 has no rows
+    assert rows_per_seq_of([], 2) == 0
