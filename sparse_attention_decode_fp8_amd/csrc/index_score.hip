@@ -31,7 +31,10 @@
 namespace msa {
 namespace {
 
-constexpr int kWaves = 4;
+// Waves (blocks) per scoring workgroup: 2, or 4 where the launch's last workgroup of a
+// row group runs the block radix select (which takes 256 threads). Smaller workgroups
+// measured slightly faster at every workload (scores are identical).
+constexpr int score_waves(bool selects) { return selects ? 4 : 2; }
 
 struct ScoreArgs {
   const uint8_t* index_k;
@@ -89,7 +92,7 @@ __device__ __forceinline__ uint4 encode_key16(uint4 lo, uint4 hi, float idx_t) {
 }
 
 // kG score tables per row: table t sums the index heads [t * kHi / kG, (t + 1) * kHi / kG).
-template <int kHi, int kG, int kFmt, bool kFused, bool kIdxNv>
+template <int kHi, int kG, int kFmt, bool kFused, bool kIdxNv, int kWaves>
 __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
   static_assert(kHi % kG == 0, "index heads split evenly into the tables");
   constexpr int kHpg = kHi / kG;
@@ -368,7 +371,8 @@ __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
     if (lane < nr * kG) a.scores[(static_cast<int64_t>(r0) * kG + lane) * a.max_blocks + b] = -INFINITY;
   }
 
-  if constexpr (kFused) {
+  // (the selecting launch has 256-thread workgroups; smaller ones never select)
+  if constexpr (kFused && 64 * kWaves >= kSelectThreads) {
     if (a.counters == nullptr) return;                 // append + score only
     // The last scoring workgroup of this row group selects for its rows.
     const int nwg = (last_block + kWaves) / kWaves;   // workgroups holding blocks 0..last_block
@@ -414,7 +418,6 @@ ScoreArgs make_score_args(const msa_kv_pool_t* pool, const msa_step_t* step, con
   a.num_seqs = step->num_seqs;
   a.num_pages = pool->num_pages;
   a.err = debug_error_word();
-  a.score_wgs_x = (step->max_blocks_per_seq + kWaves - 1) / kWaves;
   return a;
 }
 
@@ -429,10 +432,10 @@ int score_rows(const ScoreArgs& a, const msa_step_t* step) {
   return a.rows_per_seq > 0 ? step->num_seqs * a.groups_per_seq : step->num_rows;
 }
 
-template <int kFmt, bool kFused, bool kIdxNv>
+template <int kFmt, bool kFused, bool kIdxNv, int kWaves>
 void launch_score_fmt(const ScoreArgs& a, int hi, int tables, dim3 grid, size_t lds, hipStream_t s) {
   const dim3 block(64 * kWaves);
-#define MSA_SCORE_LAUNCH(HI, G) score_kernel<HI, G, kFmt, kFused, kIdxNv><<<grid, block, lds, s>>>(a)
+#define MSA_SCORE_LAUNCH(HI, G) score_kernel<HI, G, kFmt, kFused, kIdxNv, kWaves><<<grid, block, lds, s>>>(a)
   if (hi == 1) MSA_SCORE_LAUNCH(1, 1);
   else if (hi == 2) {
     if (tables == 1) MSA_SCORE_LAUNCH(2, 1);
@@ -446,16 +449,16 @@ void launch_score_fmt(const ScoreArgs& a, int hi, int tables, dim3 grid, size_t 
 }
 
 // hi in {1, 2, 4} and tables dividing hi are checked by the caller.
-template <bool kFused>
+template <bool kFused, int kWaves>
 msa_status_t launch_score(const ScoreArgs& a, const msa_kv_pool_t* pool, int hi, int tables, dim3 grid,
                           size_t lds, hipStream_t s) {
   const bool nv = index_nvfp4(pool);
   if (pool->fmt == MSA_KV_NVFP4) {
-    if (nv) launch_score_fmt<MSA_KV_NVFP4, kFused, true>(a, hi, tables, grid, lds, s);
-    else launch_score_fmt<MSA_KV_NVFP4, kFused, false>(a, hi, tables, grid, lds, s);
+    if (nv) launch_score_fmt<MSA_KV_NVFP4, kFused, true, kWaves>(a, hi, tables, grid, lds, s);
+    else launch_score_fmt<MSA_KV_NVFP4, kFused, false, kWaves>(a, hi, tables, grid, lds, s);
   } else {
-    if (nv) launch_score_fmt<MSA_KV_FP8_E4M3, kFused, true>(a, hi, tables, grid, lds, s);
-    else launch_score_fmt<MSA_KV_FP8_E4M3, kFused, false>(a, hi, tables, grid, lds, s);
+    if (nv) launch_score_fmt<MSA_KV_FP8_E4M3, kFused, true, kWaves>(a, hi, tables, grid, lds, s);
+    else launch_score_fmt<MSA_KV_FP8_E4M3, kFused, false, kWaves>(a, hi, tables, grid, lds, s);
   }
   return launch_status();
 }
@@ -479,8 +482,10 @@ extern "C" msa_status_t msa_index_score(const msa_kv_pool_t* pool, const msa_ste
   if (step->num_rows > 65535) return MSA_ERR_UNSUPPORTED;
   ScoreArgs a = make_score_args(pool, step, q_idx, w, block_scores);
   set_score_rows(a, step, n_idx_heads);
+  constexpr int kW = score_waves(false);
+  a.score_wgs_x = (step->max_blocks_per_seq + kW - 1) / kW;
   dim3 grid(a.score_wgs_x, score_rows(a, step));
-  return launch_score<false>(a, pool, n_idx_heads, tables, grid, 0, static_cast<hipStream_t>(stream));
+  return launch_score<false, kW>(a, pool, n_idx_heads, tables, grid, 0, static_cast<hipStream_t>(stream));
 }
 
 extern "C" msa_status_t msa_append_score_select(
@@ -518,9 +523,13 @@ extern "C" msa_status_t msa_append_score_select(
   a.sel = sel;
   a.sel_pages = sel_pages;
   a.counters = counters;
-  const int64_t app_wgs = (static_cast<int64_t>(n_new) * a.app.groups_per_tok + 255) / 256;
+  const int waves = score_waves(sel != nullptr);
+  a.score_wgs_x = (step->max_blocks_per_seq + waves - 1) / waves;
+  const int64_t app_wgs = (static_cast<int64_t>(n_new) * a.app.groups_per_tok + 64 * waves - 1) / (64 * waves);
   a.append_row = n_new > 0 ? 1 : 0;
   dim3 grid(static_cast<unsigned>(std::max<int64_t>(a.score_wgs_x, app_wgs)), score_rows(a, step) + a.append_row);
   const size_t lds = sel ? static_cast<size_t>(step->max_blocks_per_seq) * sizeof(uint32_t) : 0;
-  return launch_score<true>(a, pool, n_idx_heads, tables, grid, lds, static_cast<hipStream_t>(stream));
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (sel != nullptr) return launch_score<true, score_waves(true)>(a, pool, n_idx_heads, tables, grid, lds, hs);
+  return launch_score<true, score_waves(false)>(a, pool, n_idx_heads, tables, grid, lds, hs);
 }
