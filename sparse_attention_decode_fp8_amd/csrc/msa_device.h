@@ -49,22 +49,25 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 // below 2^-126 of the largest one may come out as zero, which changes no sum.
 __device__ __forceinline__ float exp2_raw(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// max(x, 0) as one instruction. Written as fmaxf, the compiler first canonicalises x
-// (a second instruction) to honour signalling NaNs, which the matrix-core results fed
-// here never are.
-__device__ __forceinline__ float relu_raw(float x) {
-  float r;
-  asm("v_max_f32 %0, 0, %1" : "=v"(r) : "v"(x));
-  return r;
+// max(x, 0) as one instruction: the median of (x, 0, +inf). Written as fmaxf, the
+// compiler first canonicalises x (a second instruction) to honour signalling NaNs,
+// which the matrix-core results fed here never are. (Not inline asm: the compiler
+// cannot see an asm's register reads, so it would not insert the wait states a
+// matrix-core result needs before a vector instruction may read it, once it keeps that
+// result in vector rather than accumulator registers.)
+// +inf that the compiler cannot see as a constant (an asm with no instruction that only
+// claims to rewrite its register): with a constant bound it would rewrite the median
+// into a max and canonicalise the operand again.
+__device__ __forceinline__ float opaque_inf() {
+  float v = __builtin_inff();
+  asm("" : "+v"(v));
+  return v;
 }
+__device__ __forceinline__ float relu_raw(float x) { return __builtin_amdgcn_fmed3f(x, 0.0f, opaque_inf()); }
 
-// max(a, b) as one instruction (no canonicalisation of the operands first; for values
-// that are never signalling NaNs).
-__device__ __forceinline__ float max_raw(float a, float b) {
-  float r;
-  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-}
+// max(a, b) as one instruction, the median of (a, b, +inf) (no canonicalisation of the
+// operands first; for values that are never NaN).
+__device__ __forceinline__ float max_raw(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, opaque_inf()); }
 
 // Max / sum over the four lanes l, l^16, l^32, l^48 (the rows of 16 lanes), in every
 // lane, with the row swaps of gfx950 (vector ALU; no LDS round trip). The sums pair
