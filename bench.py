@@ -74,6 +74,9 @@ def parse():
                          "the scoring launch")
     ap.add_argument("--per-kv-head", action="store_true",
                     help="one selection per (row, KV head), each from its share of the index heads")
+    ap.add_argument("--launches", type=int, choices=[1, 2], default=2,
+                    help="fused step: 1 = the whole step in one msa_decode_step launch (where its shape "
+                         "allows), 2 = append + score, then select + decode + combine")
     ap.add_argument("--separate", action="store_true",
                     help="five launches per step (one per stage) instead of the two fused ones")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -263,13 +266,26 @@ def main():
     print(f"[bench] {R} pool replicas ready, splits {ns}", file=sys.stderr, flush=True)
 
     select_in = args.select_in
+
+    def step_call(p, stream=None):
+        """The single launch (msa_decode_step); False if the shape is outside it."""
+        return M.msa_decode_step(p, step, q_idx, w, q, wl.k, wl.n_init, wl.n_local, wl.softmax_scale, ns,
+                                 bufs.score_x, bufs.score_words, bufs.merge_o, bufs.merge_ml, bufs.counters,
+                                 bufs.out, block_scores=bufs.block_scores, sel=bufs.sel, sel_pages=bufs.sel_pages,
+                                 slot=slot, k_new=k_new, v_new=v_new, idx_k_new=idx_new, stream=stream,
+                                 unsupported_ok=True)
+
+    single = (args.launches == 1 and not args.separate and select_in == "decode" and tables == 1
+              and step_call(pools[0]))
+    if args.launches == 1 and not single:
+        print("[bench] the single launch does not cover this shape: two launches", file=sys.stderr, flush=True)
     # run_step appends in a launch of its own when a step has this many new tokens
-    app_sep = not args.separate and select_in == "decode" and len(sl) > FUSED_APPEND_MAX
+    app_sep = not args.separate and not single and select_in == "decode" and len(sl) > FUSED_APPEND_MAX
 
     def one_step(p, stream=None):
         M.run_step(p, step, bufs, q, q_idx, w, wl.softmax_scale, slot=slot, k_new=k_new,
                    v_new=v_new, idx_k_new=idx_new, n_init=wl.n_init, n_local=wl.n_local,
-                   fused=not args.separate, stream=stream, select_in=select_in)
+                   fused=not args.separate, stream=stream, select_in=select_in, single_launch=single)
 
     # ---- capture: the replica cycle, the warm-up steps and exactly the K timed steps.
     # Warm-up step i uses replica (R - W + i) % R, so that it ends right before replica
@@ -351,6 +367,10 @@ def main():
             lambda p: M.msa_combine(wl.num_rows, wl.num_heads, 128, ns, bufs.part_o, bufs.part_ml, bufs.out),
         ]
         decode_kernels = ["msa_sparse_decode", "msa_combine"]
+    elif single:
+        names = ["msa_decode_step"]
+        calls = [lambda p: step_call(p)]
+        decode_kernels = ["msa_decode_step"]
     elif select_in == "decode":
         names = ["msa_append_score_select", "msa_select_decode_combine"]
         calls = [
@@ -461,7 +481,10 @@ def main():
         last[int(wl.row_seq[r])] = max(last.get(int(wl.row_seq[r]), -1), int(wl.row_pos[r]))
     idx_bytes = int(sum(p + 1 for p in last.values()) * key_bytes)
     t_dec = sum(per_kernel_us[k]["mean"] for k in decode_kernels) * 1e-6
-    if args.separate or app_sep:
+    if single:
+        t_idx = None   # (the scoring runs inside the one launch)
+        idx_method = None
+    elif args.separate or app_sep:
         t_idx = per_kernel_us["msa_index_score"]["mean"] * 1e-6
         idx_method = "events around replays of a graph of this kernel alone"
     else:
@@ -469,7 +492,10 @@ def main():
         # step does not have; within the step it takes what the decode leaves of it.
         t_idx = ms_per_step * 1e-3 - per_kernel_us[decode_kernels[0]]["mean"] * 1e-6
         idx_method = "step time minus the decode kernel's mean"
-    achieved = dec_bytes / t_dec / 1e9
+    # The single launch is the whole step: its algorithmic bytes are the index keys' and
+    # the decode's together.
+    roof_bytes = dec_bytes + (idx_bytes if single else 0)
+    achieved = roof_bytes / t_dec / 1e9
 
     traffic = None
     # HBM bytes per launch of the decode kernel from the committed rocprofv3 counter
@@ -513,18 +539,19 @@ def main():
                    "appended_tokens": wl.n_append, "top_k": wl.k, "kv_format": "nvfp4" if wl.fmt == W.FMT_NVFP4 else "fp8",
                    "num_splits": ns, "selection": "per KV head" if tables > 1 else "per query row",
                    "select_in": "separate launch" if args.separate else select_in,
+                   "launches": "separate" if args.separate else 1 if single else 2,
                    "pool_replicas": R, "reuse_distance_decode_bytes": (R - 1) * dec_bytes,
                    "parallelism": "single GPU"},
         "step_us": step_us,
         "roofline": {"kernel": "+".join(decode_kernels), "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic, "algorithmic_bytes": dec_bytes,
+                     "traffic": traffic, "algorithmic_bytes": roof_bytes,
                      "visible_selected_tokens": dec_tokens, "mean_us": t_dec * 1e6,
                      **({f"{q}_us": per_kernel_us[decode_kernels[0]][q] for q in ("p10", "p50", "p90")}
                         if len(decode_kernels) == 1 else {}),
                      "frac_of_box_read": None if box_read is None else achieved / box_read,
-                     "frac_of_read_floor": floor["mean"] / (t_dec * 1e6)},
-        "index_score_roofline": {"kernel": "msa_index_score" if args.separate or app_sep else names[0],
+                     "frac_of_read_floor": None if single else floor["mean"] / (t_dec * 1e6)},
+        "index_score_roofline": None if single else {"kernel": "msa_index_score" if args.separate or app_sep else names[0],
                                  "bound": "hbm", "achieved": idx_bytes / t_idx / 1e9,
                                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                  "frac": idx_bytes / t_idx / 1e9 / HBM_PEAK_GBS,

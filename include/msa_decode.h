@@ -12,8 +12,9 @@
  *
  * Fused entry points run the same step in two launches: msa_append_score_select
  * (append + score, optionally + select) and msa_select_decode_combine (select + decode
- * + combine) or msa_sparse_decode_combine (decode + combine). msa_sparse_decode_union
- * decodes the rows of a request together over the union of their selected pages.
+ * + combine) or msa_sparse_decode_combine (decode + combine); msa_decode_step runs the
+ * whole step in one launch where its shape allows. msa_sparse_decode_union decodes the
+ * rows of a request together over the union of their selected pages.
  *
  * The operations follow three public TensorRT-LLM pull-request pages:
  *   [Rubin] "[None][feat] Add Rubin (sm_107) MiniMax-M3.1 low-latency decode targets" (#21136)
@@ -324,6 +325,61 @@ msa_status_t msa_select_decode_combine(const msa_kv_pool_t* pool, const msa_step
                                        void* out, int32_t* sel, int32_t* sel_pages, void* stream);
 
 /*
+ * The whole decode step in ONE launch: msa_kv_append + msa_index_score +
+ * msa_select_topk + msa_sparse_decode + msa_combine, with the results of those calls
+ * ([GB300] "The TP4 decode target": the decode megakernels fuse block selection and
+ * the KV update; "The TP8 decode target": index scoring fused with block selection).
+ * Saves the launch between msa_append_score_select and msa_select_decode_combine.
+ * The decode workgroups of each group of rows (up to 4 rows of one request) first score
+ * that group's blocks, each wave at most two blocks, into the score exchange; every
+ * workgroup then selects its row's blocks from the exchange as the scores land (an
+ * agent-coherent poll), decodes its split and merges as msa_select_decode_combine
+ * does. New tokens are encoded into the pool by the same launch; the scorer and the
+ * decode take each new token's key, K and V from its bf16 source (the same encoding)
+ * rather than from the pool, so out, sel and block_scores equal those of the calls
+ * above bit for bit.
+ *   Arguments of msa_kv_append, msa_index_score, msa_select_topk and
+ *   msa_select_decode_combine, and:
+ *   score_x     : fp32 [num_rows][max_blocks_per_seq], the score exchange. Every word
+ *                 must be MSA_MERGE_IDLE_BITS before the call, and is so again after it
+ *                 (msa_step_workspace_init sets it up).
+ *   score_words : int32 [num_rows], zero before the call and again after it.
+ *   block_scores : optional output (may be NULL), [num_rows][max_blocks_per_seq] as
+ *                 msa_index_score writes it; sel, sel_pages : optional outputs as in
+ *                 msa_select_decode_combine.
+ *   part_o, part_ml, counters : the merge workspace of msa_select_decode_combine.
+ * The single launch covers: n_idx_heads == 4, MSA_INDEX_E4M3 keys, one selection table
+ * per row, a stated row count per request (step->rows_per_seq = R > 0), n_new <= 64,
+ * the decode shape of 4 or 8 waves per workgroup (at most 2 selected blocks per split)
+ * and rows of at most 64 * 2 * 8 candidate blocks, max_blocks_per_seq at most twice the
+ * waves of the smallest group of rows ((R % 4, or 4) * num_kv_heads * num_splits
+ * workgroups of 4 or 8 waves), and at most 256 workgroups per group. Other shapes
+ * return MSA_ERR_UNSUPPORTED and launch nothing: use the two-launch entries. Two
+ * calls that share score_x, score_words or the merge workspace must not run
+ * concurrently. A workgroup waits only for workgroups of its own group of rows, which
+ * are dispatched before it or with it; its poll is bounded (about 2^16 rounds), and if
+ * the bound is ever reached its outputs are bf16 NaN (the debug library reports
+ * MSA_DEBUG_SCORE_TIMEOUT).
+ */
+msa_status_t msa_decode_step(const msa_kv_pool_t* pool, const msa_step_t* step, int32_t n_new,
+                             const int64_t* slot, const void* k_new, const void* v_new,
+                             const void* idx_k_new, int32_t n_idx_heads, const void* q_idx,
+                             const float* w, int32_t num_q_heads, const void* q, int32_t k,
+                             int32_t n_init, int32_t n_local, float softmax_scale,
+                             int32_t num_splits, float* score_x, int32_t* score_words,
+                             float* part_o, float* part_ml, int32_t* counters, void* out,
+                             float* block_scores, int32_t* sel, int32_t* sel_pages, void* stream);
+
+/*
+ * Set up msa_decode_step's score exchange for `rows` rows of max_blocks_per_seq
+ * blocks: every word of score_x [rows][max_blocks] = MSA_MERGE_IDLE_BITS, every word of
+ * score_words [rows] = 0. A fill kernel on `stream` (no memset nodes). Needed once after
+ * allocation and again if anything else wrote the exchange.
+ */
+msa_status_t msa_step_workspace_init(int32_t rows, int32_t max_blocks, float* score_x,
+                                     int32_t* score_words, void* stream);
+
+/*
  * Sparse decode of groups of query rows over the union of their selections (query
  * pairing for speculative verify: [Rubin] commit messages name query pairing among
  * the tuned parameters of the NVFP4 sparse decode at 4 query rows per request). A
@@ -446,6 +502,8 @@ const char* msa_status_string(msa_status_t status);
  *                       partial (see msa_sparse_decode_combine)
  *   MSA_DEBUG_BAD_GROUP : a row group of msa_sparse_decode_union that is out of order,
  *                       outside [0, num_rows), longer than max_group_rows or mixes requests
+ *   MSA_DEBUG_SCORE_TIMEOUT : a workgroup of msa_decode_step gave up waiting for its
+ *                       row's scores (see msa_decode_step)
  * msa_debug_set_error_word sets the device int32 word (NULL: none) that every later
  * call of the debug library, on any stream, reports to; the caller zeroes and reads
  * it. msa_debug_set_merge_poll_limit sets the number of poll rounds after which a
@@ -467,7 +525,8 @@ typedef enum {
   MSA_DEBUG_BAD_SEL = 4,
   MSA_DEBUG_BAD_SLOT = 5,
   MSA_DEBUG_MERGE_TIMEOUT = 6,
-  MSA_DEBUG_BAD_GROUP = 7
+  MSA_DEBUG_BAD_GROUP = 7,
+  MSA_DEBUG_SCORE_TIMEOUT = 8
 } msa_debug_error_t;
 
 msa_status_t msa_debug_set_error_word(int32_t* word);

@@ -10,6 +10,7 @@ from ._lib import (FMT_FP8, FMT_NVFP4, IDX_E4M3, IDX_NVFP4, KVPool, MsaError, St
                    msa_sparse_decode, msa_sparse_decode_combine, msa_sparse_decode_union, group_rows_of,
                    msa_sparse_decode_combine_noalloc,
                    msa_append_score_select, msa_select_decode_combine, msa_merge_workspace_init,
+                   msa_decode_step, msa_step_workspace_init,
                    MERGE_IDLE_BITS, msa_debug_set_error_word, msa_debug_set_merge_poll_limit,
                    msa_debug_set_merge_helper_poll_limit,
                    load_library, use_library,

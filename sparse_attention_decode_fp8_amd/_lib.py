@@ -31,6 +31,7 @@ HEAD_DIM = 128
 INDEX_DIM = 64
 
 MSA_OK = 0
+MSA_ERR_UNSUPPORTED = -2
 MERGE_IDLE_BITS = 0x7fbadbad   # every fp32 word of an idle merge workspace
 
 
@@ -58,8 +59,8 @@ class MsaStep(ctypes.Structure):
 
 EXPORTS = ["msa_kv_append", "msa_index_score", "msa_select_topk", "msa_append_score_select",
            "msa_sparse_decode", "msa_sparse_decode_union", "msa_sparse_decode_combine_noalloc",
-           "msa_sparse_decode_combine", "msa_select_decode_combine", "msa_combine",
-           "msa_merge_workspace_init",
+           "msa_sparse_decode_combine", "msa_select_decode_combine", "msa_decode_step", "msa_combine",
+           "msa_merge_workspace_init", "msa_step_workspace_init",
            "msa_decode_workspace_bytes", "msa_pool_bytes", "msa_index_bytes", "msa_status_string",
            "msa_debug_set_error_word", "msa_debug_set_merge_poll_limit", "msa_debug_set_merge_helper_poll_limit",
            "msa_debug_checks_enabled"]
@@ -82,6 +83,9 @@ def load_library(path: str):
         "msa_sparse_decode_combine": (I32, [P, P, I32, P, P, P, I32, F32, I32, P, P, P, P, P]),
         "msa_sparse_decode_combine_noalloc": (I32, [P, P, I32, P, P, P, I32, F32, I32, P, P]),
         "msa_select_decode_combine": (I32, [P, P, I32, P, P, I32, I32, I32, F32, I32, P, P, P, P, P, P, P]),
+        "msa_decode_step": (I32, [P, P, I32, P, P, P, P, I32, P, P, I32, P, I32, I32, I32, F32, I32, P, P, P, P, P,
+                                  P, P, P, P, P]),
+        "msa_step_workspace_init": (I32, [I32, I32, P, P, P]),
         "msa_combine": (I32, [I32, I32, I32, I32, P, P, P, P]),
         "msa_merge_workspace_init": (I32, [I32, I32, I32, I32, P, P, P, P]),
         "msa_decode_workspace_bytes": (SZ, [I32, I32, I32, I32]),
@@ -356,6 +360,36 @@ def msa_select_decode_combine(pool: KVPool, step: Step, q, block_scores, k, n_in
         _ptr(counters, torch.int32, "counters"), _ptr(out, torch.bfloat16, "out"),
         _ptr(sel, torch.int32, "sel"), _ptr(sel_pages, torch.int32, "sel_pages"), _stream(stream)),
         "msa_select_decode_combine")
+
+
+def msa_decode_step(pool: KVPool, step: Step, q_idx, w, q, k, n_init, n_local, softmax_scale, num_splits,
+                    score_x, score_words, part_o, part_ml, counters, out, block_scores=None, sel=None,
+                    sel_pages=None, slot=None, k_new=None, v_new=None, idx_k_new=None, stream=None,
+                    unsupported_ok=False) -> bool:
+    """The whole step in one launch. Returns True when launched; with unsupported_ok,
+    False (nothing launched) for a shape outside the single-launch contract."""
+    ps, ss = pool.cstruct(), step.cstruct()
+    n = 0 if slot is None else slot.numel()
+    st = LIB.msa_decode_step(
+        ctypes.byref(ps), ctypes.byref(ss), n, _ptr(slot, torch.int64, "slot"),
+        _ptr(k_new, torch.bfloat16, "k_new"), _ptr(v_new, torch.bfloat16, "v_new"),
+        _ptr(idx_k_new, torch.bfloat16, "idx_k_new"), q_idx.shape[1], _ptr(q_idx, torch.bfloat16, "q_idx"),
+        _ptr(w, torch.float32, "w"), q.shape[1], _ptr(q, torch.bfloat16, "q"), k, n_init, n_local,
+        float(softmax_scale), num_splits, _ptr(score_x, torch.float32, "score_x"),
+        _ptr(score_words, torch.int32, "score_words"), _ptr(part_o, torch.float32, "part_o"),
+        _ptr(part_ml, torch.float32, "part_ml"), _ptr(counters, torch.int32, "counters"),
+        _ptr(out, torch.bfloat16, "out"), _ptr(block_scores, torch.float32, "block_scores"),
+        _ptr(sel, torch.int32, "sel"), _ptr(sel_pages, torch.int32, "sel_pages"), _stream(stream))
+    if unsupported_ok and st == MSA_ERR_UNSUPPORTED:
+        return False
+    _check(st, "msa_decode_step")
+    return True
+
+
+def msa_step_workspace_init(rows, max_blocks, score_x, score_words, stream=None):
+    _check(LIB.msa_step_workspace_init(rows, max_blocks, _ptr(score_x, torch.float32, "score_x"),
+                                       _ptr(score_words, torch.int32, "score_words"), _stream(stream)),
+           "msa_step_workspace_init")
 
 
 def msa_combine(rows, num_q_heads, head_dim, num_splits, part_o, part_ml, out, stream=None):

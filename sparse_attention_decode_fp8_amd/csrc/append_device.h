@@ -89,16 +89,32 @@ __device__ __forceinline__ uint32_t nvfp4_encode16(const float x[16], float t, u
   return sc;
 }
 
-// 16 bf16 values (two 16-byte words as loaded) -> one NVFP4 group.
-__device__ __forceinline__ uint32_t nvfp4_encode16_bits(uint4 a, uint4 b, float t, uint32_t& w0, uint32_t& w1) {
+// 16 bf16 values as loaded (two 16-byte words) -> fp32.
+__device__ __forceinline__ void bf16x16_to_f32(uint4 a, uint4 b, float x[16]) {
   const uint32_t wv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-  float x[16];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     x[2 * i] = __uint_as_float(wv[i] << 16);
     x[2 * i + 1] = __uint_as_float(wv[i] & 0xffff0000u);
   }
+}
+
+// 16 bf16 values (two 16-byte words as loaded) -> one NVFP4 group.
+__device__ __forceinline__ uint32_t nvfp4_encode16_bits(uint4 a, uint4 b, float t, uint32_t& w0, uint32_t& w1) {
+  float x[16];
+  bf16x16_to_f32(a, b, x);
   return nvfp4_encode16(x, t, w0, w1);
+}
+
+// 16 values -> 16 saturating E4M3 codes of x / s, packed little-endian (the FP8 KV
+// encoding at page scale s; one correctly rounded fp32 division per value).
+__device__ __forceinline__ uint4 fp8_encode16(const float x[16], float s) {
+#pragma clang fp contract(off)
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = f32x4_to_e4m3_sat(x[4 * i] / s, x[4 * i + 1] / s, x[4 * i + 2] / s, x[4 * i + 3] / s);
+  return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 // Encode group `gid` (token gid / groups_per_tok) of the new tokens into the pool.
@@ -149,12 +165,8 @@ __device__ __forceinline__ void append_group(const AppendArgs& a, int64_t gid) {
     scales[row * (kHeadDim / 16) + g] = static_cast<uint8_t>(sc);
   } else {
     const float s = reinterpret_cast<const float*>(is_v ? a.v_scales : a.k_scales)[page];
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      w[i] = f32x4_to_e4m3_sat(x[4 * i] / s, x[4 * i + 1] / s, x[4 * i + 2] / s, x[4 * i + 3] / s);
     uint8_t* codes = is_v ? a.v_codes : a.k_codes;
-    *reinterpret_cast<uint4*>(codes + row * kHeadDim + 16 * g) = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint4*>(codes + row * kHeadDim + 16 * g) = fp8_encode16(x, s);
   }
 }
 

@@ -136,3 +136,18 @@ extern "C" msa_status_t msa_merge_workspace_init(int32_t rows, int32_t num_q_hea
       merge_state(0, num_splits));
   return launch_status();
 }
+
+extern "C" msa_status_t msa_step_workspace_init(int32_t rows, int32_t max_blocks, float* score_x,
+                                                int32_t* score_words, void* stream) {
+  using namespace msa;
+  if (rows < 0 || max_blocks <= 0) return MSA_ERR_INVALID_ARG;
+  if (max_blocks > MSA_MAX_BLOCKS) return MSA_ERR_UNSUPPORTED;
+  if (rows == 0) return MSA_OK;
+  if (score_x == nullptr || score_words == nullptr) return MSA_ERR_INVALID_ARG;
+  const int64_t n_x = static_cast<int64_t>(rows) * max_blocks;
+  const int64_t blocks = std::min<int64_t>((n_x + rows + 255) / 256, 4096);
+  // (the merge workspace's fill kernel: idle words, then zero state words)
+  merge_idle_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
+      reinterpret_cast<uint32_t*>(score_x), n_x, nullptr, 0, score_words, rows, 0u);
+  return launch_status();
+}

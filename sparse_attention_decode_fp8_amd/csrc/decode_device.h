@@ -9,6 +9,7 @@
 //   O^T[d][head]    += V^T[d][token] . P^T[token][head] A = V^T (LDS, transposing read)
 #pragma once
 
+#include "append_device.h"
 #include "msa_device.h"
 
 namespace msa {
@@ -82,6 +83,144 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<kFmt>& R, const KvArrays& a
       for (int h = 0; h < 2; ++h) {
         R.k[2 * u + h] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kc, static_cast<int>(t * kHeadDim + 32 * q + 16 * h), 0, 0));
         R.v[2 * u + h] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vc, static_cast<int>(t * kHeadDim + 32 * q + 16 * h), 0, 0));
+      }
+    }
+  }
+}
+
+// The new tokens' K and V of one KV head as the append encodes them, held in LDS by the
+// single-launch step (at most 64 tokens): NVFP4 codes [token][K, V][group of 16 dims]
+// (8 bytes) and scale codes; FP8 codes [token][K, V][group] (16 bytes).
+template <int kFmt>
+struct NewKv;
+template <>
+struct NewKv<MSA_KV_NVFP4> {
+  uint2 codes[64][2][8];
+  uint8_t scales[64][2][8];
+};
+template <>
+struct NewKv<MSA_KV_FP8_E4M3> {
+  uint4 codes[64][2][8];
+};
+
+// Encode group `grp` of KV head g into `nk`: new token grp / 16, K (or V when
+// (grp / 8) is odd), dims 16 (grp % 8) .. +15, by the append's rules (NVFP4 at the
+// tensor scale; FP8 at the scale of the token's page); with `owner`, also write it to
+// the token's slot in the pool (msa_kv_append's layout). A token with a negative slot,
+// or a null source, is not appended and is skipped.
+// Position of the k-th set bit (k from 0) of m; k < popcount(m).
+__device__ __forceinline__ int nth_set_bit(uint64_t m, int k) {
+  int pos = 0;
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) {
+    const int c = __popcll(m & ((1ull << w) - 1));
+    if (k >= c) {
+      k -= c;
+      m >>= w;
+      pos += w;
+    }
+  }
+  return pos;
+}
+
+// One 16-element group encoded by the 16 lanes of a row, lane l holding element l:
+// the same arithmetic per element as nvfp4_encode16 / fp8_encode16 / encode_index16
+// (the group maximum by exact max operations, from max(|x|, 0) in every lane, so a NaN
+// is ignored as there), so the codes are bit-identical. The packed codes are returned
+// in lane 0 of the row (and the NVFP4 scale code in every lane).
+// NVFP4 at tensor scale t: codes as w0 | w1 << 32 (element 2j in the low nibble of byte j).
+__device__ __forceinline__ uint32_t nvfp4_encode_row(float x, float t, uint2& codes) {
+#pragma clang fp contract(off)
+  const int l = threadIdx.x & 15;
+  float amax = fmaxf(fabsf(x), 0.0f);
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 16));
+  const float six_t = 6.0f * t;
+  const uint32_t sc = f32_to_e4m3_sat(amax / six_t);
+  const float dec = e4m3_to_f32(sc);
+  uint32_t v = 0;
+  if (dec != 0.0f) {
+    const float d = dec * t;
+    v = f32_to_e2m1_sat(x / d) << (4 * (l & 7));
+  }
+#pragma unroll
+  for (int m = 1; m < 8; m <<= 1) v |= __shfl_xor(v, m, 16);   // each half row's 8 nibbles
+  codes = make_uint2(v, __shfl_down(v, 8, 16));
+  return sc;
+}
+// E4M3 codes of x / s (s = 1: the index-key rule), bytes in element order.
+__device__ __forceinline__ uint4 e4m3_encode_row(float x, float s) {
+#pragma clang fp contract(off)
+  const int l = threadIdx.x & 15;
+  uint32_t v = f32_to_e4m3_sat(x / s) << (8 * (l & 3));
+#pragma unroll
+  for (int m = 1; m < 4; m <<= 1) v |= __shfl_xor(v, m, 16);   // each quarter row's 4 bytes
+  return make_uint4(v, __shfl_down(v, 4, 16), __shfl_down(v, 8, 16), __shfl_down(v, 12, 16));
+}
+
+// The new tokens that land in chunk c of `page` (bit i: new token i; slot0: lane i <
+// n_new holds new token i's slot, else -1).
+__device__ __forceinline__ uint64_t new_tokens_in_chunk(int64_t slot0, int64_t page, int c) {
+  return __ballot(slot0 >= 0 && (slot0 >> 7) == page && ((slot0 & (kPage - 1)) >> 5) == c);
+}
+
+// Tokens appended by the same launch (the single-launch step): the lanes that hold one
+// of the chunk's new tokens (`hits`, from new_tokens_in_chunk) replace its codes and
+// scales with the token's encoding, so the decode never depends on when the append's
+// stores to the pool land. Tokens in `in_lds` (bit i: new token i) take it from `nk`;
+// any other is encoded here from its bf16 source, by the append's rules, by the lanes
+// that hold it (KV head g; FP8 at the page's scales kps / vps). Called once the chunk's
+// loads have arrived (the registers it writes are those loads' destinations). A K or V
+// source that is null is not appended, and the loaded bytes stay.
+template <int kFmt>
+__device__ __forceinline__ void patch_new_tokens(ChunkRegs<kFmt>& R, const NewKv<kFmt>& nk, const AppendArgs& app,
+                                                 int64_t slot0, uint64_t hits, uint64_t in_lds, int g, int n, int q,
+                                                 float kps, float vps) {
+  while (hits != 0u) {
+    const int i = __ffsll(static_cast<unsigned long long>(hits)) - 1;
+    hits &= hits - 1;
+    const int off = __builtin_amdgcn_readlane(static_cast<int>(slot0 & 31), i);   // token in the chunk
+    if ((off & 15) != n) continue;
+    const int u = off >> 4;
+    const bool from_lds = (in_lds >> i) & 1u;
+#pragma unroll
+    for (int kv = 0; kv < 2; ++kv) {
+      const uint16_t* src = kv == 0 ? app.k_new : app.v_new;
+      if (src == nullptr) continue;
+      uint4* codes = kv == 0 ? R.k : R.v;
+      if constexpr (kFmt == MSA_KV_NVFP4) {   // dims 32q .. 32q+31: groups 2q and 2q+1
+        uint2 a, b;
+        uint32_t sc;
+        if (from_lds) {
+          a = nk.codes[i][kv][2 * q];
+          b = nk.codes[i][kv][2 * q + 1];
+          sc = nk.scales[i][kv][2 * q] | (static_cast<uint32_t>(nk.scales[i][kv][2 * q + 1]) << 8);
+        } else {
+          const uint4* p = reinterpret_cast<const uint4*>(src + (static_cast<int64_t>(i) * app.hkv + g) * kHeadDim + 32 * q);
+          const float t = kv == 0 ? app.k_t : app.v_t;
+          const uint32_t sa = nvfp4_encode16_bits(p[0], p[1], t, a.x, a.y);
+          const uint32_t sb = nvfp4_encode16_bits(p[2], p[3], t, b.x, b.y);
+          sc = sa | (sb << 8);
+        }
+        uint32_t* scales = kv == 0 ? R.ks : R.vs;
+        if (u == 0) { codes[0] = make_uint4(a.x, a.y, b.x, b.y); scales[0] = sc; }
+        else { codes[1] = make_uint4(a.x, a.y, b.x, b.y); scales[1] = sc; }
+      } else {
+        uint4 a, b;
+        if (from_lds) {
+          a = nk.codes[i][kv][2 * q];
+          b = nk.codes[i][kv][2 * q + 1];
+        } else {
+          const uint4* p = reinterpret_cast<const uint4*>(src + (static_cast<int64_t>(i) * app.hkv + g) * kHeadDim + 32 * q);
+          const float ps = kv == 0 ? kps : vps;
+          float x[16];
+          bf16x16_to_f32(p[0], p[1], x);
+          a = fp8_encode16(x, ps);
+          bf16x16_to_f32(p[2], p[3], x);
+          b = fp8_encode16(x, ps);
+        }
+        if (u == 0) { codes[0] = a; codes[1] = b; }
+        else { codes[2] = a; codes[3] = b; }
       }
     }
   }

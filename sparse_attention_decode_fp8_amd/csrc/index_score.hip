@@ -26,6 +26,7 @@
 
 #include "append_device.h"
 #include "msa_host.h"
+#include "score_device.h"
 #include "select_device.h"
 
 namespace msa {
@@ -62,34 +63,6 @@ struct ScoreArgs {
   // rows (groups_per_seq per request) instead of one per query row
   int rows_per_seq, groups_per_seq;
 };
-
-// A lane's share of one 16-token row of keys (token 16t + n, dims 16q .. 16q+15):
-// E4M3 keys: 16 codes. NVFP4 keys: .x, .y = 16 E2M1 codes (element 2j in the low
-// nibble of byte j), .z = the group's E4M3 scale code.
-template <bool kIdxNv>
-__device__ __forceinline__ void key_operands(uint4 kt, half8_t& B0, half8_t& B1) {
-  if constexpr (kIdxNv) {
-    const half2_t s2 = e4m3x2_to_f16(kt.z);
-    const half2_t sc2 = {s2[0], s2[0]};
-    B0 = e2m1x8_to_f16(kt.x, sc2);
-    B1 = e2m1x8_to_f16(kt.y, sc2);
-  } else {
-    B0 = e4m3x8_to_f16(kt.x, kt.y);
-    B1 = e4m3x8_to_f16(kt.z, kt.w);
-  }
-}
-
-// The same share of a new token's key, encoded from its 16 bf16 values.
-template <bool kIdxNv>
-__device__ __forceinline__ uint4 encode_key16(uint4 lo, uint4 hi, float idx_t) {
-  if constexpr (kIdxNv) {
-    uint32_t w0, w1;
-    const uint32_t sc = nvfp4_encode16_bits(lo, hi, idx_t, w0, w1);
-    return make_uint4(w0, w1, sc, 0u);
-  } else {
-    return encode_index16_bits(lo, hi);
-  }
-}
 
 // kG score tables per row: table t sums the index heads [t * kHi / kG, (t + 1) * kHi / kG).
 template <int kHi, int kG, int kFmt, bool kFused, bool kIdxNv, int kWaves>

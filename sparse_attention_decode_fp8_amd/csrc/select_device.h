@@ -441,10 +441,23 @@ struct MultiSelectSmem {
 // writes them, ascending, between the forced entries.
 // Each level-1 wave searches 64 kR keys instead of one wave searching all of them.
 // Level 1 returns the row's visible block count in the waves below nw (0 in the others).
-template <int kR>
+//
+// kPoll: the scores are still being written, by other workgroups of the same launch,
+// into an exchange row whose words hold MSA_MERGE_IDLE_BITS until written (the
+// single-launch step). The row's length is then read first, and the words of its
+// visible blocks are read agent-coherently, again until none is idle, for at most
+// poll->limit rounds (poll->timed_out reports the bound reached; the picks are then
+// meaningless). A row with nb <= k needs no score and reads none.
+struct ScorePoll {
+  const float* row;   // the row's exchange words, [0, nb) written in this launch
+  int limit;
+  bool timed_out;
+};
+template <int kR, bool kPoll = false>
 __device__ __forceinline__ int multiwave_select_level1(const float* srow, const int32_t* bt, int max_blocks,
                                                        const int32_t* row_pos, int k, int n_init, int n_local,
-                                                       int nw, int* sel, int* pages, MultiSelectSmem& ms) {
+                                                       int nw, int* sel, int* pages, MultiSelectSmem& ms,
+                                                       ScorePoll* poll = nullptr) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lo = n_init, want = k - n_init - n_local;
@@ -453,11 +466,12 @@ __device__ __forceinline__ int multiwave_select_level1(const float* srow, const 
     const int c0 = 64 * kR * wave;
     float sv[kR];
     int32_t pg[kR];
+    if constexpr (kPoll) nb = min(*row_pos / MSA_PAGE_SIZE + 1, max_blocks);
 #pragma unroll
     for (int i = 0; i < kR; ++i) {
       const int c = c0 + lane * kR + i;
       const bool in_row = lo + c < max_blocks;
-      sv[i] = in_row ? srow[lo + c] : 0.0f;
+      if constexpr (!kPoll) sv[i] = in_row ? srow[lo + c] : 0.0f;
       pg[i] = in_row ? bt[lo + c] : -1;
     }
     const int32_t pg_init = wave == 0 && lane < n_init && lane < max_blocks ? bt[lane] : -1;   // blocks below lo
@@ -465,8 +479,29 @@ __device__ __forceinline__ int multiwave_select_level1(const float* srow, const 
     // wave reads their pages too, so no block-table read waits for the row's length
     const int ct = 64 * kR * nw + lane;
     const int32_t pg_tail = wave == nw - 1 && lo + ct < max_blocks ? bt[lo + ct] : -1;
-    asm volatile("" ::: "memory");   // the position's load queues behind the others
-    nb = min(*row_pos / MSA_PAGE_SIZE + 1, max_blocks);
+    if constexpr (kPoll) {
+#pragma unroll
+      for (int i = 0; i < kR; ++i) sv[i] = 0.0f;
+      if (nb > k) {
+        // (words past nb lie outside the resource: they read as 0, which is not idle)
+        const __amdgpu_buffer_rsrc_t xr = make_rsrc(uniform_ptr(poll->row), static_cast<uint32_t>(nb) * 4u);
+        bool ready = false;
+        for (int spin = 0; !ready && spin < poll->limit; ++spin) {
+          if (spin > 0) __builtin_amdgcn_s_sleep(2);
+          uint32_t key = ~0u;
+#pragma unroll
+          for (int i = 0; i < kR; ++i) {
+            sv[i] = load_coherent1(xr, static_cast<uint32_t>(lo + c0 + lane * kR + i) * 4u);
+            key = idle_key(key, sv[i]);
+          }
+          ready = __ballot(key == 0u) == 0;
+        }
+        if (!ready) poll->timed_out = true;
+      }
+    } else {
+      asm volatile("" ::: "memory");   // the position's load queues behind the others
+      nb = min(*row_pos / MSA_PAGE_SIZE + 1, max_blocks);
+    }
     const int C = nb - n_init - n_local;
     if (nb <= k) {                                           // identity table (wave 0 holds it all)
       if (wave == 0) {

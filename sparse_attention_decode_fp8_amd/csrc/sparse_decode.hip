@@ -47,6 +47,7 @@
 #include "msa_device.h"
 #include "msa_host.h"
 #include "decode_device.h"
+#include "score_device.h"
 #include "select_device.h"
 
 namespace msa {
@@ -93,10 +94,23 @@ struct DecodeArgs {
   int helper_poll_limit;
 };
 
+// The single-launch step (msa_decode_step): scoring, append and the row's score
+// exchange, on top of the selecting decode's arguments.
+struct StepArgs {
+  StepScoreArgs sc;
+  int32_t* words;      // [rows]: workgroups that have read the row's scores (0 between launches)
+  int rows_per_seq;    // every request's row count (stated by the caller)
+  int readers;         // workgroups that read one row's scores: hkv * num_splits
+  AppendArgs app;      // at most 64 new tokens
+};
+// Index heads of the single-launch step.
+constexpr int kStepHi = 4;
+
 template <int kFmt, int kItems>
 struct Round {
   ChunkRegs<kFmt> R[kItems];
   int nvis[kItems];                // visible tokens of each chunk (0: no chunk)
+  uint64_t hits[kItems];           // single-launch step: new tokens in each chunk
   float kps[kItems], vps[kItems];  // FP8 page scales (1 for NVFP4)
 };
 
@@ -105,10 +119,12 @@ struct Round {
 // block and physical page of selection entry e (b < 0: empty entry). Chunks past the
 // split, of empty entries or with no visible token issue the same loads from
 // zero-byte resources (see load_chunk).
-template <int kFmt, int kW, int kItems, class Lookup>
-__device__ __forceinline__ void load_round(Round<kFmt, kItems>& rd, const DecodeArgs& a,
-                                           const Lookup& lookup, int round, int wave, int g,
-                                           int pos, int lo, int n_items, int n, int q) {
+// kStep: tokens appended in the same launch are patched into the loaded chunk from
+// their encoding in LDS (patch_new_tokens; slot0 as there).
+template <int kFmt, int kW, int kItems, bool kStep, class Lookup>
+__device__ __forceinline__ void load_round(Round<kFmt, kItems>& rd, const DecodeArgs& a, const StepArgs& st,
+                                           const NewKv<kFmt>* nk, int64_t slot0, const Lookup& lookup, int round,
+                                           int wave, int g, int pos, int lo, int n_items, int n, int q) {
   // The row position, block and page are the same in every lane; reading them through
   // readfirstlane tells the compiler so, and the buffer resources below stay in scalar
   // registers (a resource it cannot prove uniform costs a loop over lanes per load).
@@ -132,6 +148,9 @@ __device__ __forceinline__ void load_round(Round<kFmt, kItems>& rd, const Decode
       rd.kps[j] = reinterpret_cast<const float*>(a.k_scales)[page];
       rd.vps[j] = reinterpret_cast<const float*>(a.v_scales)[page];
     }
+    rd.hits[j] = 0u;
+    if constexpr (kStep)
+      if (valid) rd.hits[j] = new_tokens_in_chunk(slot0, page, c);
   }
 }
 
@@ -240,20 +259,52 @@ __device__ __forceinline__ bool merge_handoff(int32_t* word, uint32_t buffer, in
 // kSelect keys per lane (or the block radix select for rows too long for it).
 constexpr int kOutPartials = 0, kOutDirect = 1, kOutMerged = 2;
 
+// The single-launch step's scoring share of one workgroup. The decode workgroups of a
+// group of rows (up to 16 / kStepHi rows of one request, cut in request order, as the
+// scorer groups them) score that group's blocks: block b by the group's wave
+// b mod (its waves), so with max_blocks at most twice the smallest group's waves (a
+// host check) a wave scores at most two blocks, whose loads go out together.
+// Returns the page of row r's last visible block.
+template <int kW>
+__device__ __forceinline__ int32_t step_score_share(const DecodeArgs& a, const StepArgs& st, int r, int g, int s,
+                                                    int wave, int64_t slot0) {
+  constexpr int kRpg = 16 / kStepHi;
+  const int R = st.rows_per_seq;
+  const int seq = r / R, i = r - seq * R;
+  const int r0 = seq * R + (i / kRpg) * kRpg, nr = min(kRpg, R - (i / kRpg) * kRpg);
+  const int nwv = nr * a.hkv * a.num_splits * kW;
+  const int gw = (((r - r0) * a.hkv + g) * a.num_splits + s) * kW + wave;
+  const int b[2] = {gw, gw + nwv};
+  return score_blocks<kStepHi, 2>(st.sc, a.block_table, a.row_pos, a.max_blocks, a.num_pages, a.err, r0, nr, seq,
+                                  b, slot0, r - r0);
+}
+
 // 8-wave workgroups that do not merge run two per compute unit when the launch is large
 // (one split per (row, KV head) pair): four waves per SIMD, so at most 128 registers.
-template <int kW, int kOut>
-constexpr int decode_min_waves_per_simd() { return kW == 8 && kOut != 2 ? 4 : 1; }
+// (Not the single-launch step, whose scoring phase holds two blocks of keys at once.)
+template <int kW, int kOut, bool kStep>
+constexpr int decode_min_waves_per_simd() { return kW == 8 && kOut != 2 && !kStep ? 4 : 1; }
 
-template <int kFmt, int kW, int kItems, int kOut, int kSelect>
+// kStep (the single-launch step, selecting variants only): the workgroup first scores
+// its share of its row group's blocks into the score exchange and encodes its share of
+// the new tokens into the pool, then selects from the exchange as the scores land
+// (multiwave_select_level1 in its polling form), decodes with the new tokens patched
+// into its registers, and merges. The workgroups of a row group are consecutive in the
+// grid (split fastest, then KV head, then row), so those it waits for are dispatched
+// before it or with it.
+template <int kFmt, int kW, int kItems, int kOut, int kSelect, bool kStep = false>
 __global__ void __launch_bounds__(64 * kW)
-__attribute__((amdgpu_waves_per_eu(decode_min_waves_per_simd<kW, kOut>())))
-sparse_decode_kernel(DecodeArgs a) {
+__attribute__((amdgpu_waves_per_eu(decode_min_waves_per_simd<kW, kOut, kStep>())))
+sparse_decode_kernel(DecodeArgs a, StepArgs st) {
+  static_assert(!kStep || kSelect, "the single-launch step selects");
   // Dynamic LDS: the row's selection keys (selecting variant, before any V is staged),
   // then the per-wave V staging buffers and, at the end, the per-wave O tiles.
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
   __shared__ float mbuf[kW][16], lbuf[kW][16];
   __shared__ int s_word;
+  __shared__ int s_rlast;   // kStep: this workgroup was the row's last reader
+  // kStep: the new tokens' K and V of this KV head, encoded
+  __shared__ typename std::conditional<kStep, NewKv<kFmt>, char>::type newkv;
   __shared__ int32_t lsel[kSelect ? MSA_MAX_TOPK : 1], lpage[kSelect ? MSA_MAX_TOPK : 1];
   __shared__ half8_t qlds[kSelect ? 4 : 1][64];   // selecting variant: the converted Q operand
   __shared__ float qcs[kSelect ? 64 : 1];
@@ -272,6 +323,105 @@ sparse_decode_kernel(DecodeArgs a) {
   asm volatile("" : "+s"(lo), "+s"(hi));
   const int n_items = (hi - lo) * 4;   // (entry, 32-token chunk) pairs of this split
   const int64_t head0 = static_cast<int64_t>(r) * hq + kHeadsPerKv * g;
+
+  int64_t slot0 = -1;     // kStep: lane i < n_new holds new token i's slot
+  uint64_t in_lds = 0u;   // kStep: new tokens whose K and V of this KV head are encoded in LDS
+  if constexpr (kStep) {
+    if (lane < st.app.n_new) slot0 = st.app.slot[lane];
+    // (the scorer also reads the page of this row's last visible block)
+    const int32_t last_page = step_score_share<kW>(a, st, r, g, s, wave, slot0);
+    // The append (which nothing in this launch reads: the scorer and the decode encode
+    // the new tokens themselves) is written by split 0 of row i % num_rows for new token
+    // i: its K and V of each KV head, and its index key from the workgroup of KV head 0.
+    // The split that holds the row's last block (split S - 1: the forced local blocks
+    // are the table's last entries) is the one that meets tokens appended to the row's
+    // last page; it encodes those for its KV head. Both kinds are encoded into LDS (the
+    // decode patches them in from there; any other new token it meets is encoded where
+    // it is met) by the waves that take no part in the first selection level (all of
+    // them if every wave does), during that level's wait for the scores: one group of
+    // 16 elements per row of 16 lanes.
+    in_lds = __ballot(slot0 >= 0 && ((s == 0 && lane % a.num_rows == r) ||
+                                     (s == a.num_splits - 1 && (slot0 >> 7) == last_page)));
+    const uint64_t own_idx = s == 0 && g == 0 && st.app.idx_new != nullptr
+                                 ? __ballot(lane < st.app.n_new && lane % a.num_rows == r)
+                                 : 0u;
+    const int enc0 = a.sel_waves < kW ? 64 * a.sel_waves : 0;   // (whole waves)
+    const int e = static_cast<int>(threadIdx.x) - enc0;
+    if (e >= 0) {
+      const int rows = (64 * kW - enc0) >> 4, row = e >> 4, l = e & 15;
+      // items: 16 K/V groups of each token in in_lds, then 4 index-key groups of each
+      // token in own_idx
+      const int n_kv = 16 * __popcll(in_lds), n_items = n_kv + 4 * __popcll(own_idx);
+      // up to four items per row at a time: every element load of the four goes out
+      // before the first encoding
+      for (int base = 0; base < n_items; base += 4 * rows) {   // (the same trip count in every lane)
+        int it_[4], tok_[4];
+        int64_t sl_[4];
+        float x_[4], ps_[4];   // (ps_: FP8 K/V items, the page's scale)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int it = base + u * rows + row;
+          it_[u] = it;
+          tok_[u] = it >= n_items ? 0 : it < n_kv ? nth_set_bit(in_lds, it >> 4) : nth_set_bit(own_idx, (it - n_kv) >> 2);
+          sl_[u] = __shfl(slot0, tok_[u], 64);
+          x_[u] = 0.0f;
+          ps_[u] = 1.0f;
+          if (it < n_items && sl_[u] >= 0) {
+            const uint16_t* src;
+            int64_t at;
+            if (it < n_kv) {
+              src = ((it >> 3) & 1) == 0 ? st.app.k_new : st.app.v_new;
+              at = (static_cast<int64_t>(tok_[u]) * a.hkv + g) * kHeadDim + 16 * (it & 7) + l;
+              if constexpr (kFmt == MSA_KV_FP8_E4M3)
+                if (sl_[u] / kPage < a.num_pages)
+                  ps_[u] = reinterpret_cast<const float*>(((it >> 3) & 1) == 0 ? a.k_scales : a.v_scales)[sl_[u] / kPage];
+            } else {
+              src = st.app.idx_new;
+              at = static_cast<int64_t>(tok_[u]) * kIndexDim + 16 * ((it - n_kv) & 3) + l;
+            }
+            if (src != nullptr) x_[u] = bf16_to_f32(src[at]);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int it = it_[u], tok = tok_[u];
+          const int64_t sl = sl_[u];
+          // (everything below is the same in the 16 lanes of a row)
+          if (it >= n_items || sl < 0 || !dcheck(sl / kPage < a.num_pages, MSA_DEBUG_BAD_SLOT, a.err)) continue;
+          if (it < n_kv) {
+            const int kv = (it >> 3) & 1, gg = it & 7;
+            if ((kv == 0 ? st.app.k_new : st.app.v_new) == nullptr) continue;
+            const int64_t prow = (sl / kPage * a.hkv + g) * kPage + sl % kPage;   // the token's row in the pool
+            const bool owner = s == 0 && tok % a.num_rows == r;
+            if constexpr (kFmt == MSA_KV_NVFP4) {
+              uint2 c;
+              const uint32_t sc = nvfp4_encode_row(x_[u], kv == 0 ? a.k_t : a.v_t, c);
+              if (l == 0) {
+                newkv.codes[tok][kv][gg] = c;
+                newkv.scales[tok][kv][gg] = static_cast<uint8_t>(sc);
+                if (owner) {
+                  *reinterpret_cast<uint2*>((kv == 0 ? st.app.k_codes : st.app.v_codes) + prow * (kHeadDim / 2) +
+                                            8 * gg) = c;
+                  (kv == 0 ? st.app.k_scales : st.app.v_scales)[prow * (kHeadDim / 16) + gg] = static_cast<uint8_t>(sc);
+                }
+              }
+            } else {
+              const uint4 c = e4m3_encode_row(x_[u], ps_[u]);
+              if (l == 0) {
+                newkv.codes[tok][kv][gg] = c;
+                if (owner)
+                  *reinterpret_cast<uint4*>((kv == 0 ? st.app.k_codes : st.app.v_codes) + prow * kHeadDim + 16 * gg) = c;
+              }
+            }
+          } else if (st.app.idx_new != nullptr) {
+            const int j = (it - n_kv) & 3;
+            const uint4 c = e4m3_encode_row(x_[u], 1.0f);
+            if (l == 0) *reinterpret_cast<uint4*>(st.app.index_k + sl * kIndexDim + 16 * j) = c;
+          }
+        }
+      }
+    }
+  }
 
   // Combining variants with several splits: the pair's merge state word (which of the
   // two exchange buffers this launch uses, the split count the workspace was set up
@@ -316,6 +466,8 @@ sparse_decode_kernel(DecodeArgs a) {
   const int64_t trow = static_cast<int64_t>(r) * a.sel_tables + (a.sel_tables > 1 ? g : 0);
   int selv = -1, pagev = -1;
   int pos;
+  bool score_timeout = false;   // kStep: some score was still idle after the poll bound
+  int32_t reader_old = 0;       // kStep, thread 0: readers of the row before this one
   if constexpr (!kSelect) {
     // the caller's table: one load per lane, issued before the query loads so that
     // the page addresses wait for these alone (the counter retires in order)
@@ -346,15 +498,23 @@ sparse_decode_kernel(DecodeArgs a) {
       const int seq = checked_seq(a.row_seq[r], a.num_seqs, a.err);
       const int32_t* btg = a.block_table + static_cast<int64_t>(guess) * a.max_blocks;
       MultiSelectSmem& ms = *reinterpret_cast<MultiSelectSmem*>(dyn_lds);
-      const int nb = multiwave_select_level1<kSelect>(srow, btg, a.max_blocks, a.row_pos + r, a.k, a.n_init,
-                                                      a.n_local, a.sel_waves, lsel, lpage, ms);
+      ScorePoll sp{kStep ? st.sc.xscores + trow * a.max_blocks : nullptr, a.poll_limit, false};
+      const int nb = multiwave_select_level1<kSelect, kStep>(srow, btg, a.max_blocks, a.row_pos + r, a.k,
+                                                             a.n_init, a.n_local, a.sel_waves, lsel, lpage, ms,
+                                                             &sp);
       if (wave == kW - 1) {   // (while the first level runs, unless this wave is part of it)
         convert_q();
 #pragma unroll
         for (int j = 0; j < 4; ++j) qlds[j][lane] = Qop[j];
         qcs[lane] = cscale;
       }
-      __syncthreads();
+      if constexpr (kStep) {
+        // every score read of the workgroup is done: count it in as a reader of the row
+        score_timeout = __syncthreads_or(sp.timed_out);
+        if (threadIdx.x == 0) reader_old = atomicAdd(st.words + r, 1);
+      } else {
+        __syncthreads();
+      }
       if (wave == 0) multiwave_select_level2<kSelect>(nb, a.k, a.n_init, a.n_local, a.sel_waves, lsel, lpage, ms);
       __syncthreads();
       selv = lsel[lane];
@@ -376,6 +536,13 @@ sparse_decode_kernel(DecodeArgs a) {
       pagev = selv >= 0 ? bt[selv] : -1;
     }
     q_from_lds();
+    if constexpr (kStep) {
+      // the selection came from scores that never landed: make every output NaN
+      if (score_timeout) {
+        dcheck(false, MSA_DEBUG_SCORE_TIMEOUT, a.err);
+        cscale = __builtin_nanf("");
+      }
+    }
     if (lane >= a.k) selv = pagev = -1;
     if (s == 0 && (g == 0 || a.sel_tables > 1) && wave == 0 && a.sel_out != nullptr && lane < a.k) {
       a.sel_out[trow * a.k + lane] = selv;
@@ -389,7 +556,9 @@ sparse_decode_kernel(DecodeArgs a) {
   };
 
   Round<kFmt, kItems> rd;
-  load_round<kFmt, kW, kItems>(rd, a, lookup, 0, wave, g, pos, lo, n_items, n, q);
+  const NewKv<kFmt>* nk = nullptr;
+  if constexpr (kStep) nk = &newkv;
+  load_round<kFmt, kW, kItems, kStep>(rd, a, st, nk, slot0, lookup, 0, wave, g, pos, lo, n_items, n, q);
 
   // This split's slot in the other exchange buffer was read by the previous launch's
   // merger; the last wave puts it back to idle now, off the critical path (its page
@@ -420,10 +589,13 @@ sparse_decode_kernel(DecodeArgs a) {
 
   for (int round = 0; round < n_items; round += kW * kItems) {
     if (round > 0)
-      load_round<kFmt, kW, kItems>(rd, a, lookup, round, wave, g, pos, lo, n_items, n, q);
+      load_round<kFmt, kW, kItems, kStep>(rd, a, st, nk, slot0, lookup, round, wave, g, pos, lo, n_items, n, q);
 #pragma unroll
     for (int j = 0; j < kItems; ++j) {
       if (rd.nvis[j] <= 0) continue;
+      if constexpr (kStep)
+        if (rd.hits[j] != 0u)
+          patch_new_tokens<kFmt>(rd.R[j], *nk, st.app, slot0, rd.hits[j], in_lds, g, n, q, rd.kps[j], rd.vps[j]);
       const uint32_t* ksc = nullptr;
       const uint32_t* vsc = nullptr;
       if constexpr (kFmt == MSA_KV_NVFP4) { ksc = rd.R[j].ks; vsc = rd.R[j].vs; }
@@ -512,7 +684,21 @@ sparse_decode_kernel(DecodeArgs a) {
       *reinterpret_cast<float4_t*>(ob + ne * kORowFloats + 16 * d + 4 * qe) = O[d] * oscale;
     if (qe == 0) { mbuf[wave][ne] = m_run; lbuf[wave][ne] = l_tot; }
   }
+  if constexpr (kStep)
+    if (threadIdx.x == 0) s_rlast = reader_old == st.readers - 1;
   __syncthreads();
+  if constexpr (kStep) {
+    // The row's last reader: every reader of the row is past its score reads, so its
+    // exchange words go back to idle (and its reader count to zero) for the next launch.
+    if (s_rlast) {
+      const int nbr = min(pos / kPage + 1, a.max_blocks);
+      float* xr = st.sc.xscores + trow * a.max_blocks;
+      for (int b = threadIdx.x; b < nbr; b += 64 * kW)
+        __hip_atomic_store(xr + b, __uint_as_float(MSA_MERGE_IDLE_BITS), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      if (threadIdx.x == 0) __hip_atomic_store(st.words + r, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
   // this (row, KV head)'s partials: O [16 heads][S][128], (m, l) [16 heads][S][2]
   const uint32_t o_bytes = 16u * a.num_splits * kHeadDim * 4, ml_bytes = 16u * a.num_splits * 8;
   const int cur = merging ? static_cast<int>(mstate >> 31) : 0;   // this launch's exchange buffer
@@ -699,11 +885,11 @@ sparse_decode_kernel(DecodeArgs a) {
   }
 }
 
-template <int kFmt, int kW, int kItems, int kOut, int kSelect>
-void launch(const DecodeArgs& a, dim3 grid, hipStream_t s) {
+template <int kFmt, int kW, int kItems, int kOut, int kSelect, bool kStep = false>
+void launch(const DecodeArgs& a, dim3 grid, hipStream_t s, const StepArgs& st = StepArgs{}) {
   size_t lds = static_cast<size_t>(kW) * kVBufBytes;
   if (kSelect) lds = std::max({lds, static_cast<size_t>(a.max_blocks) * sizeof(uint32_t), sizeof(MultiSelectSmem)});
-  sparse_decode_kernel<kFmt, kW, kItems, kOut, kSelect><<<grid, dim3(64 * kW), lds, s>>>(a);
+  sparse_decode_kernel<kFmt, kW, kItems, kOut, kSelect, kStep><<<grid, dim3(64 * kW), lds, s>>>(a, st);
 }
 
 // Waves per workgroup for a split of `per_split` pages, one chunk per wave and round:
@@ -750,8 +936,10 @@ void select_shape(int c_max, int want, int waves, int& kR, int& nw) {
   nw = 0;
 }
 
-msa_status_t decode_entry(const msa_kv_pool_t* pool, const msa_step_t* step, int32_t num_q_heads,
-                          const void* q, DecodeArgs a, hipStream_t s, bool combine, bool select) {
+// Host checks and arguments common to every decode entry; `grid` receives the launch
+// grid. Returns MSA_OK with a.num_rows == 0 for an empty step (nothing to launch).
+msa_status_t prepare_decode(const msa_kv_pool_t* pool, const msa_step_t* step, int32_t num_q_heads,
+                            const void* q, DecodeArgs& a, bool combine, bool select, dim3& grid) {
   msa_status_t st = check_pool(pool);
   if (st != MSA_OK) return st;
   if ((st = check_step(step)) != MSA_OK) return st;
@@ -762,6 +950,7 @@ msa_status_t decode_entry(const msa_kv_pool_t* pool, const msa_step_t* step, int
   if (!(a.softmax_scale > 0.0f)) return MSA_ERR_INVALID_ARG;
   a.sel_tables = sel_tables(step);
   if (a.sel_tables != 1 && a.sel_tables != pool->num_kv_heads) return MSA_ERR_UNSUPPORTED;
+  a.num_rows = step->num_rows;
   if (step->num_rows == 0) return MSA_OK;
   if (q == nullptr || a.part_o == nullptr || a.part_ml == nullptr) return MSA_ERR_INVALID_ARG;
   if (select ? a.scores == nullptr : a.sel == nullptr) return MSA_ERR_INVALID_ARG;
@@ -787,10 +976,16 @@ msa_status_t decode_entry(const msa_kv_pool_t* pool, const msa_step_t* step, int
   a.row_pos = step->row_pos;
   a.max_blocks = step->max_blocks_per_seq;
   a.q = static_cast<const uint16_t*>(q);
-  a.num_rows = step->num_rows;
   a.seq_mul = seq_guess_mul(step->num_seqs, step->num_rows);
-  const int pairs = step->num_rows * pool->num_kv_heads;
-  dim3 grid(a.num_splits, pairs);
+  grid = dim3(a.num_splits, step->num_rows * pool->num_kv_heads);
+  return MSA_OK;
+}
+
+msa_status_t decode_entry(const msa_kv_pool_t* pool, const msa_step_t* step, int32_t num_q_heads,
+                          const void* q, DecodeArgs a, hipStream_t s, bool combine, bool select) {
+  dim3 grid;
+  const msa_status_t st = prepare_decode(pool, step, num_q_heads, q, a, combine, select, grid);
+  if (st != MSA_OK || a.num_rows == 0) return st;
   const bool direct = a.num_splits == 1;
   int kr = 0;
   if (select) select_shape(a.max_blocks - a.n_init - a.n_local, a.k - a.n_init - a.n_local, decode_waves(a, grid),
@@ -808,6 +1003,13 @@ msa_status_t decode_entry(const msa_kv_pool_t* pool, const msa_step_t* step, int
   return MSA_DECODE_DISPATCH(MSA_KV_FP8_E4M3);
 #undef MSA_DECODE_DISPATCH
 #undef MSA_DECODE_SELECT
+}
+
+template <int kFmt, int kOut, int kSelect>
+msa_status_t dispatch_step(const DecodeArgs& a, const StepArgs& st, dim3 grid, int waves, hipStream_t s) {
+  if (waves == 4) launch<kFmt, 4, 1, kOut, kSelect, true>(a, grid, s, st);
+  else launch<kFmt, 8, 1, kOut, kSelect, true>(a, grid, s, st);
+  return launch_status();
 }
 
 DecodeArgs base_args(const int32_t* sel, const int32_t* sel_pages, int32_t k, float softmax_scale,
@@ -866,4 +1068,74 @@ extern "C" msa_status_t msa_select_decode_combine(
   a.counters = counters;
   a.out = static_cast<uint16_t*>(out);
   return decode_entry(pool, step, num_q_heads, q, a, static_cast<hipStream_t>(stream), true, true);
+}
+
+extern "C" msa_status_t msa_decode_step(
+    const msa_kv_pool_t* pool, const msa_step_t* step, int32_t n_new, const int64_t* slot, const void* k_new,
+    const void* v_new, const void* idx_k_new, int32_t n_idx_heads, const void* q_idx, const float* w,
+    int32_t num_q_heads, const void* q, int32_t k, int32_t n_init, int32_t n_local, float softmax_scale,
+    int32_t num_splits, float* score_x, int32_t* score_words, float* part_o, float* part_ml, int32_t* counters,
+    void* out, float* block_scores, int32_t* sel, int32_t* sel_pages, void* stream) {
+  using namespace msa;
+  if (counters == nullptr || out == nullptr) return MSA_ERR_INVALID_ARG;
+  if (n_new < 0) return MSA_ERR_INVALID_ARG;
+  DecodeArgs a = base_args(nullptr, nullptr, k, softmax_scale, num_splits, part_o, part_ml);
+  a.scores = score_x;   // (checked as the selection's input)
+  a.n_init = n_init;
+  a.n_local = n_local;
+  a.sel_out = sel;
+  a.sel_pages_out = sel_pages;
+  a.counters = counters;
+  a.out = static_cast<uint16_t*>(out);
+  dim3 grid;
+  msa_status_t st = prepare_decode(pool, step, num_q_heads, q, a, true, true, grid);
+  if (st != MSA_OK) return st;
+  if (n_new > 0 && slot == nullptr) return MSA_ERR_INVALID_ARG;
+  for (const void* p : {k_new, v_new, idx_k_new})
+    if (p != nullptr && !aligned16(p)) return MSA_ERR_INVALID_ARG;
+  if (step->num_rows == 0) {
+    return n_new > 0 ? msa_kv_append(pool, n_new, slot, k_new, v_new, idx_k_new, stream) : MSA_OK;
+  }
+  // the single-launch contract: 4 index heads, E4M3 keys, one table per row, a stated
+  // row count per request, at most 64 new tokens
+  if (n_idx_heads != kStepHi || index_nvfp4(pool) || a.sel_tables != 1 || step->rows_per_seq <= 0 || n_new > 64)
+    return MSA_ERR_UNSUPPORTED;
+  if (q_idx == nullptr || w == nullptr || score_words == nullptr || !aligned16(q_idx)) return MSA_ERR_INVALID_ARG;
+  const int waves = decode_waves(a, grid);
+  int kr = 0;
+  select_shape(a.max_blocks - a.n_init - a.n_local, a.k - a.n_init - a.n_local, waves, kr, a.sel_waves);
+  // Workgroup and selection shapes of the single launch, and at most two scoring blocks
+  // per wave: a group of rows (16 / 4 index heads = 4 rows of one request) has
+  // rows * hkv * num_splits workgroups; the smallest group has R % 4 rows (4 if R is a
+  // multiple of 4), and max_blocks must be at most twice its waves. A group waits only
+  // on its own workgroups, which must fit on the GPU at once (at most 256 workgroups,
+  // one per compute unit).
+  constexpr int kRpg = 16 / kStepHi;
+  const int R = step->rows_per_seq;
+  const int64_t per_row = static_cast<int64_t>(a.hkv) * a.num_splits;
+  const int64_t small_waves = (R % kRpg == 0 ? kRpg : R % kRpg) * per_row * waves;
+  if ((waves != 4 && waves != 8) || (kr != 1 && kr != 2) || a.max_blocks > 2 * small_waves ||
+      std::min(R, kRpg) * per_row > 256)
+    return MSA_ERR_UNSUPPORTED;
+  StepArgs sa{};
+  sa.sc.index_k = static_cast<const uint8_t*>(pool->index_k);
+  sa.sc.q_idx = static_cast<const uint16_t*>(q_idx);
+  sa.sc.w = w;
+  sa.sc.idx_new = static_cast<const uint16_t*>(idx_k_new);
+  sa.sc.xscores = score_x;
+  sa.sc.scores_out = block_scores;
+  sa.words = score_words;
+  sa.rows_per_seq = R;
+  sa.readers = static_cast<int>(per_row);
+  sa.app = make_append_args(pool, n_new, slot, k_new, v_new, idx_k_new);
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  const bool direct = a.num_splits == 1;
+#define MSA_STEP_DISPATCH(FMT)                                                                              \
+  (direct ? (kr == 1 ? dispatch_step<FMT, kOutDirect, 1>(a, sa, grid, waves, hs)                           \
+                     : dispatch_step<FMT, kOutDirect, 2>(a, sa, grid, waves, hs))                          \
+          : (kr == 1 ? dispatch_step<FMT, kOutMerged, 1>(a, sa, grid, waves, hs)                           \
+                     : dispatch_step<FMT, kOutMerged, 2>(a, sa, grid, waves, hs)))
+  if (pool->fmt == MSA_KV_NVFP4) return MSA_STEP_DISPATCH(MSA_KV_NVFP4);
+  return MSA_STEP_DISPATCH(MSA_KV_FP8_E4M3);
+#undef MSA_STEP_DISPATCH
 }

@@ -28,7 +28,8 @@ class DecodeBuffers:
     """Per-step outputs and the split-KV workspaces for a fixed geometry: part_o /
     part_ml receive the partials of the separate msa_sparse_decode call; merge_o /
     merge_ml (two exchange buffers) and counters (one state word per row and KV head)
-    are the fused entries' merge workspace, set up here for num_splits. With
+    are the fused entries' merge workspace, set up here for num_splits; score_x (idle
+    words) and score_words (zeros) are the single-launch step's score exchange. With
     sel_tables > 1 (one selection per KV head) block_scores, sel and sel_pages have a
     table axis after the row."""
 
@@ -50,6 +51,9 @@ class DecodeBuffers:
         L.msa_merge_workspace_init(num_rows, num_q_heads, L.HEAD_DIM, num_splits, self.merge_o,
                                    self.merge_ml, self.counters)
         self.score_counters = torch.zeros(num_rows, dtype=torch.int32, device=device)
+        self.score_x = torch.empty((num_rows, max_blocks), dtype=torch.float32, device=device)
+        self.score_words = torch.empty(num_rows, dtype=torch.int32, device=device)
+        L.msa_step_workspace_init(num_rows, max_blocks, self.score_x, self.score_words)
         self.out = torch.empty((num_rows, num_q_heads, L.HEAD_DIM), dtype=torch.bfloat16, device=device)
 
 
@@ -60,15 +64,22 @@ FUSED_APPEND_MAX = 64
 
 def run_step(pool, step, bufs: DecodeBuffers, q, q_idx, w, softmax_scale, slot=None, k_new=None,
              v_new=None, idx_k_new=None, n_init=0, n_local=1, fused=True, stream=None,
-             select_in="decode"):
+             select_in="decode", single_launch=False):
     """One decode step on one stream: append -> index score -> select -> sparse decode
-    -> combine. fused=True issues two launches: append + score, then select + decode +
-    combine (select_in="decode", the default: the selection is repeated by every decode
-    workgroup, which measured faster on every workload than one selection per row at the
-    end of the scoring launch), or append + score + select, then decode + combine
-    (select_in="score"). With more than FUSED_APPEND_MAX new tokens the default path
-    appends in a launch of its own before scoring. fused=False issues the five separate
-    calls."""
+    -> combine. fused=True runs two launches (with single_launch, the whole step as one
+    msa_decode_step launch where its shape allows, else the two): append + score, then
+    select + decode + combine (select_in="decode":
+    the selection is repeated by every decode workgroup, which measured faster on every
+    workload than one selection per row at the end of the scoring launch), or append +
+    score + select, then decode + combine (select_in="score"). With more than
+    FUSED_APPEND_MAX new tokens the two-launch path appends in a launch of its own before
+    scoring. fused=False issues the five separate calls. Returns the output tensor."""
+    if fused and single_launch and select_in == "decode":
+        if L.msa_decode_step(pool, step, q_idx, w, q, bufs.k, n_init, n_local, softmax_scale, bufs.num_splits,
+                             bufs.score_x, bufs.score_words, bufs.merge_o, bufs.merge_ml, bufs.counters, bufs.out,
+                             block_scores=bufs.block_scores, sel=bufs.sel, sel_pages=bufs.sel_pages, slot=slot,
+                             k_new=k_new, v_new=v_new, idx_k_new=idx_k_new, stream=stream, unsupported_ok=True):
+            return bufs.out
     if fused:
         if select_in == "decode":
             if slot is not None and slot.numel() > FUSED_APPEND_MAX:

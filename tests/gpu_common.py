@@ -52,13 +52,21 @@ def gpu_step_inputs(M, wl: W.Workload, tables=1):
 
 
 def run_gpu_step(M, wl, pool, num_splits, fused=True, tables=1, select_in="decode"):
+    """One step. fused: True (the two fused launches, run_step's default), "single"
+    (msa_decode_step, the whole step in one launch, which must accept the shape), False
+    (the five separate calls)."""
     step, q, q_idx, w, app = gpu_step_inputs(M, wl, tables)
     bufs = M.DecodeBuffers(wl.num_rows, wl.num_heads, wl.max_blocks, wl.k, num_splits, sel_tables=tables)
     kw = {}
     if app is not None:
         kw = dict(slot=app[0], k_new=app[1], v_new=app[2], idx_k_new=app[3])
-    M.run_step(pool, step, bufs, q, q_idx, w, wl.softmax_scale, n_init=wl.n_init,
-               n_local=wl.n_local, fused=fused, select_in=select_in, **kw)
+    if fused == "single":
+        M.msa_decode_step(pool, step, q_idx, w, q, wl.k, wl.n_init, wl.n_local, wl.softmax_scale, num_splits,
+                          bufs.score_x, bufs.score_words, bufs.merge_o, bufs.merge_ml, bufs.counters, bufs.out,
+                          block_scores=bufs.block_scores, sel=bufs.sel, sel_pages=bufs.sel_pages, **kw)
+    else:
+        M.run_step(pool, step, bufs, q, q_idx, w, wl.softmax_scale, n_init=wl.n_init,
+                   n_local=wl.n_local, fused=bool(fused), select_in=select_in, **kw)
     torch.cuda.synchronize()
     return bufs
 
@@ -192,6 +200,15 @@ def assert_merge_ready(bufs):
             assert (mm[r, g, e] == M.MERGE_IDLE_BITS).all(), (r, g)
 
 
+def assert_score_exchange_idle(bufs):
+    """msa_decode_step leaves its score exchange as it found it: every word idle, every
+    reader count zero."""
+    import sparse_attention_decode_fp8_amd as M
+    x = bufs.score_x.view(torch.int32).cpu().numpy().view(np.uint32)
+    assert (x == M.MERGE_IDLE_BITS).all(), "score exchange words left written"
+    assert int(bufs.score_words.abs().sum().item()) == 0, "reader counts left"
+
+
 def check_step_parity(M, wl: W.Workload, num_splits: int, fused: bool, tables: int = 1,
                       select_in: str = "decode"):
     """Run one whole step on the GPU and compare scores, selection, outputs and the
@@ -230,6 +247,8 @@ def check_step_parity(M, wl: W.Workload, num_splits: int, fused: bool, tables: i
         assert_out_close(out[~same], out_gsel[~same], "outputs on the GPU's selection")
     if fused:   # the partials passed through the merge workspace, ready for the next call
         assert_merge_ready(bufs)
+        if fused == "single":
+            assert_score_exchange_idle(bufs)
         return bufs
     # the split partials the kernel wrote
     m, l, Op = O.split_partials(ref_pool, wl.block_table, wl.row_seq, wl.row_pos, wl.q, sel_ref,

@@ -317,3 +317,43 @@ def test_no_alloc_entry_refuses_oversized_calls_on_the_host():
     assert N(B(pool), B(_fake_step(rows=1)), 32, P(16), P(16), None, 8, 0.1, 0, P(16), None) == -1
     assert N(B(pool), B(_fake_step(rows=1)), 32, P(16), P(16), None, 8, 0.1, 2, None, None) == -1
     assert N(None, B(_fake_step(rows=1)), 32, P(16), P(16), None, 8, 0.1, 2, P(16), None) == -1
+
+
+def test_single_launch_step_validation_rejects_before_launch():
+    """msa_decode_step: arguments and the single-launch contract are checked on the host
+    (nothing reaches a launch here: every call below returns before it)."""
+    B, P = ctypes.byref, ctypes.c_void_p
+    pool = _fake_pool()
+    one = _fake_step(rows=1, rows_per_seq=1)
+
+    def call(pool_=pool, step_=one, n_new=0, slot=None, n_idx=4, k=8, n_init=0, n_local=1, splits=2,
+             counters=P(16), out=P(16), score_x=P(16), words=P(16), q_idx=P(16)):
+        return L.LIB.msa_decode_step(B(pool_), B(step_), n_new, slot, None, None, None, n_idx, q_idx, P(16), 32,
+                                     P(16), k, n_init, n_local, 0.1, splits, score_x, words, P(16), P(16),
+                                     counters, out, None, None, None, None)
+
+    # an empty step launches nothing
+    assert call(step_=_fake_step(rows=0, rows_per_seq=0)) == 0
+    # outside the single-launch contract: MSA_ERR_UNSUPPORTED, so the caller takes the
+    # two-launch entries
+    assert call(n_idx=2) == -2                                       # index heads other than 4
+    assert call(pool_=_fake_pool(index_fmt=2, index_scales=1 << 20, index_t=0.5)) == -2   # NVFP4 keys
+    assert call(step_=_fake_step(rows=1, tables=2, rows_per_seq=1)) == -2                  # per-KV-head tables
+    assert call(step_=_fake_step(rows=1, rows_per_seq=0)) == -2      # row count per request not stated
+    assert call(n_new=65, slot=P(16)) == -2                          # more than 64 new tokens
+    assert call(k=8, splits=1) == -2                                 # one split of 8 blocks: 16-wave workgroups
+    assert call(step_=_fake_step(rows=1, max_blocks=200, rows_per_seq=1), k=4, splits=4) == -2   # 200 blocks > 2 x 32 waves
+    # invalid arguments
+    assert call(n_new=-1) == -1
+    assert call(n_new=1, slot=None) == -1
+    assert call(counters=None) == -1
+    assert call(out=None) == -1
+    assert call(score_x=None) == -1
+    assert call(words=None) == -1
+    assert call(q_idx=None) == -1
+    # the exchange set-up: empty is OK; geometry and pointers are checked
+    assert L.LIB.msa_step_workspace_init(0, 8, None, None, None) == 0
+    assert L.LIB.msa_step_workspace_init(-1, 8, P(16), P(16), None) == -1
+    assert L.LIB.msa_step_workspace_init(1, 0, P(16), P(16), None) == -1
+    assert L.LIB.msa_step_workspace_init(1, 12289, P(16), P(16), None) == -2
+    assert L.LIB.msa_step_workspace_init(1, 8, None, P(16), None) == -1

@@ -56,8 +56,8 @@ def _replay_and_check(g, outputs, spoil, reps=4):
                                r.view(torch.int8) if r.dtype == torch.bfloat16 else r), (rep, i)
 
 
-@pytest.mark.parametrize("cfg,fused,select_in", [(1, True, "decode"), (3, True, "decode"), (1, True, "score"),
-                                                 (0, False, "decode")])
+@pytest.mark.parametrize("cfg,fused,select_in", [(1, True, "decode"), (1, "single", "decode"), (0, "single", "decode"),
+                                                 (3, True, "decode"), (1, True, "score"), (0, False, "decode")])
 def test_step_graph_replays_equal_the_eager_step(M, cfg, fused, select_in):
     wl = W.config(cfg)
     ns = default_num_splits(wl.k, wl.num_rows * wl.num_kv_heads)
@@ -69,7 +69,7 @@ def test_step_graph_replays_equal_the_eager_step(M, cfg, fused, select_in):
 
     def step_fn():
         M.run_step(pool, step, bufs, q, q_idx, w, wl.softmax_scale, n_init=wl.n_init, n_local=wl.n_local,
-                   fused=fused, select_in=select_in, **kw)
+                   fused=bool(fused), select_in=select_in, single_launch=fused == "single", **kw)
 
     step_fn()                                  # the eager reference
     torch.cuda.synchronize()
@@ -90,6 +90,8 @@ def test_step_graph_replays_equal_the_eager_step(M, cfg, fused, select_in):
         assert int(bufs.score_counters.abs().sum().item()) == 0
     if fused and ns > 1:
         G.assert_merge_ready(bufs)
+    if fused == "single":   # the single launch's score exchange is idle again
+        G.assert_score_exchange_idle(bufs)
 
 
 def test_no_alloc_and_union_graph_replays(M):

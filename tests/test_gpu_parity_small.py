@@ -43,7 +43,8 @@ def test_append_bytes_bit_exact(M, fmt):
 
 
 @pytest.mark.parametrize("fmt", [W.FMT_FP8, W.FMT_NVFP4])
-@pytest.mark.parametrize("num_splits,fused", [(1, True), (2, False), (2, True), (5, True)])
+@pytest.mark.parametrize("num_splits,fused", [(1, True), (2, False), (2, True), (5, True), (2, "single"),
+                                              (5, "single")])
 def test_full_step_parity(M, fmt, num_splits, fused):
     wl = W.small(fmt, [1000, 2600, 130, 640], 3, num_kv_heads=2, k=5, seed=31)
     _print("step parity", wl.name, "splits", num_splits, "fused", fused)
@@ -51,7 +52,8 @@ def test_full_step_parity(M, fmt, num_splits, fused):
 
 
 @pytest.mark.parametrize("fmt", [W.FMT_FP8, W.FMT_NVFP4])
-@pytest.mark.parametrize("num_kv_heads,num_splits,fused", [(8, 1, True), (8, 4, True), (8, 2, False), (3, 2, True)])
+@pytest.mark.parametrize("num_kv_heads,num_splits,fused", [(8, 1, True), (8, 4, True), (8, 2, False), (3, 2, True),
+                                                           (8, 4, "single"), (3, 2, "single")])
 def test_step_parity_other_kv_head_counts(M, fmt, num_kv_heads, num_splits, fused):
     """8 KV heads (128 query heads) and 3 KV heads: the (row, KV head) grid, the query
     and output strides and the per-KV-head page regions at head counts other than the
