@@ -122,9 +122,10 @@ struct Round {
 // kStep: tokens appended in the same launch are patched into the loaded chunk from
 // their encoding in LDS (patch_new_tokens; slot0 as there).
 template <int kFmt, int kW, int kItems, bool kStep, class Lookup>
-__device__ __forceinline__ void load_round(Round<kFmt, kItems>& rd, const DecodeArgs& a, const StepArgs& st,
-                                           const NewKv<kFmt>* nk, int64_t slot0, const Lookup& lookup, int round,
-                                           int wave, int g, int pos, int lo, int n_items, int n, int q) {
+__device__ __forceinline__ void load_round(Round<kFmt, kItems>& rd, const DecodeArgs& a, const KvArrays& kv,
+                                           const StepArgs& st, const NewKv<kFmt>* nk, int64_t slot0,
+                                           const Lookup& lookup, int round, int wave, int g, int pos, int lo,
+                                           int n_items, int n, int q) {
   // The row position, block and page are the same in every lane; reading them through
   // readfirstlane tells the compiler so, and the buffer resources below stay in scalar
   // registers (a resource it cannot prove uniform costs a loop over lanes per load).
@@ -142,11 +143,11 @@ __device__ __forceinline__ void load_round(Round<kFmt, kItems>& rd, const Decode
     rd.nvis[j] = valid ? min(nv, 32) : 0;
     page = valid ? checked_page(page, a.num_pages, a.err) : 0;
     page = static_cast<int64_t>(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(page))));
-    load_chunk<kFmt>(rd.R[j], KvArrays{a.k_codes, a.v_codes, a.k_scales, a.v_scales}, page * a.hkv + g, valid, c, n, q);
+    load_chunk<kFmt>(rd.R[j], kv, page * a.hkv + g, valid, c, n, q);
     rd.kps[j] = rd.vps[j] = 1.0f;
     if constexpr (kFmt == MSA_KV_FP8_E4M3) {   // the page's scales (page 0 for an empty chunk)
-      rd.kps[j] = reinterpret_cast<const float*>(a.k_scales)[page];
-      rd.vps[j] = reinterpret_cast<const float*>(a.v_scales)[page];
+      rd.kps[j] = reinterpret_cast<const float*>(kv.k_scales)[page];
+      rd.vps[j] = reinterpret_cast<const float*>(kv.v_scales)[page];
     }
     rd.hits[j] = 0u;
     if constexpr (kStep)
@@ -323,6 +324,13 @@ sparse_decode_kernel(DecodeArgs a, StepArgs st) {
   asm volatile("" : "+s"(lo), "+s"(hi));
   const int n_items = (hi - lo) * 4;   // (entry, 32-token chunk) pairs of this split
   const int64_t head0 = static_cast<int64_t>(r) * hq + kHeadsPerKv * g;
+  // The pool's arrays and the partials, held in scalar registers from here (the compiler
+  // would otherwise reload them from the kernel arguments between the selection and the
+  // page loads, behind a wait that also covers the selection's LDS reads).
+  KvArrays kv{uniform_ptr(a.k_codes), uniform_ptr(a.v_codes), uniform_ptr(a.k_scales), uniform_ptr(a.v_scales)};
+  float* const part_o = uniform_ptr(a.part_o);
+  float* const part_ml = uniform_ptr(a.part_ml);
+  asm volatile("" : "+s"(kv.k_codes), "+s"(kv.v_codes), "+s"(kv.k_scales), "+s"(kv.v_scales));
 
   int64_t slot0 = -1;     // kStep: lane i < n_new holds new token i's slot
   uint64_t in_lds = 0u;   // kStep: new tokens whose K and V of this KV head are encoded in LDS
@@ -535,19 +543,7 @@ sparse_decode_kernel(DecodeArgs a, StepArgs st) {
       selv = lane < a.k ? lsel[lane] : -1;
       pagev = selv >= 0 ? bt[selv] : -1;
     }
-    q_from_lds();
-    if constexpr (kStep) {
-      // the selection came from scores that never landed: make every output NaN
-      if (score_timeout) {
-        dcheck(false, MSA_DEBUG_SCORE_TIMEOUT, a.err);
-        cscale = __builtin_nanf("");
-      }
-    }
     if (lane >= a.k) selv = pagev = -1;
-    if (s == 0 && (g == 0 || a.sel_tables > 1) && wave == 0 && a.sel_out != nullptr && lane < a.k) {
-      a.sel_out[trow * a.k + lane] = selv;
-      if (a.sel_pages_out) a.sel_pages_out[trow * a.k + lane] = pagev;
-    }
   }
   if (wave == 0 && lane == 0 && s == 0) check_pos(pos, a.max_blocks, a.err);
   auto lookup = [&](int e, int& b, int64_t& page) {
@@ -558,7 +554,22 @@ sparse_decode_kernel(DecodeArgs a, StepArgs st) {
   Round<kFmt, kItems> rd;
   const NewKv<kFmt>* nk = nullptr;
   if constexpr (kStep) nk = &newkv;
-  load_round<kFmt, kW, kItems, kStep>(rd, a, st, nk, slot0, lookup, 0, wave, g, pos, lo, n_items, n, q);
+  load_round<kFmt, kW, kItems, kStep>(rd, a, kv, st, nk, slot0, lookup, 0, wave, g, pos, lo, n_items, n, q);
+  if constexpr (kSelect) {
+    // with the page loads out: the query operand from LDS, and the optional outputs
+    q_from_lds();
+    if constexpr (kStep) {
+      // the selection came from scores that never landed: make every output NaN
+      if (score_timeout) {
+        dcheck(false, MSA_DEBUG_SCORE_TIMEOUT, a.err);
+        cscale = __builtin_nanf("");
+      }
+    }
+    if (s == 0 && (g == 0 || a.sel_tables > 1) && wave == 0 && a.sel_out != nullptr && lane < a.k) {
+      a.sel_out[trow * a.k + lane] = selv;
+      if (a.sel_pages_out) a.sel_pages_out[trow * a.k + lane] = pagev;
+    }
+  }
 
   // This split's slot in the other exchange buffer was read by the previous launch's
   // merger; the last wave puts it back to idle now, off the critical path (its page
@@ -567,9 +578,9 @@ sparse_decode_kernel(DecodeArgs a, StepArgs st) {
     const int other = static_cast<int>(mstate >> 31) ^ 1;
     const float iv = __uint_as_float(MSA_MERGE_IDLE_BITS);
     const __amdgpu_buffer_rsrc_t xo = make_rsrc(
-        uniform_ptr(a.part_o + (2 * head0 + 16 * other) * a.num_splits * kHeadDim), 16u * a.num_splits * kHeadDim * 4);
+        uniform_ptr(part_o + (2 * head0 + 16 * other) * a.num_splits * kHeadDim), 16u * a.num_splits * kHeadDim * 4);
     const __amdgpu_buffer_rsrc_t xm =
-        make_rsrc(uniform_ptr(a.part_ml + (2 * head0 + 16 * other) * a.num_splits * 2), 16u * a.num_splits * 8);
+        make_rsrc(uniform_ptr(part_ml + (2 * head0 + 16 * other) * a.num_splits * 2), 16u * a.num_splits * 8);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {   // 16 heads x 32 four-float groups
       const int idx = lane + 64 * j, h = idx / (kHeadDim / 4), d4 = idx % (kHeadDim / 4);
@@ -589,7 +600,7 @@ sparse_decode_kernel(DecodeArgs a, StepArgs st) {
 
   for (int round = 0; round < n_items; round += kW * kItems) {
     if (round > 0)
-      load_round<kFmt, kW, kItems, kStep>(rd, a, st, nk, slot0, lookup, round, wave, g, pos, lo, n_items, n, q);
+      load_round<kFmt, kW, kItems, kStep>(rd, a, kv, st, nk, slot0, lookup, round, wave, g, pos, lo, n_items, n, q);
 #pragma unroll
     for (int j = 0; j < kItems; ++j) {
       if (rd.nvis[j] <= 0) continue;
@@ -703,9 +714,9 @@ sparse_decode_kernel(DecodeArgs a, StepArgs st) {
   const uint32_t o_bytes = 16u * a.num_splits * kHeadDim * 4, ml_bytes = 16u * a.num_splits * 8;
   const int cur = merging ? static_cast<int>(mstate >> 31) : 0;   // this launch's exchange buffer
   const __amdgpu_buffer_rsrc_t ro =
-      make_rsrc(uniform_ptr(a.part_o + (2 * head0 + 16 * cur) * a.num_splits * kHeadDim), o_bytes);
+      make_rsrc(uniform_ptr(part_o + (2 * head0 + 16 * cur) * a.num_splits * kHeadDim), o_bytes);
   const __amdgpu_buffer_rsrc_t rm =
-      make_rsrc(uniform_ptr(a.part_ml + (2 * head0 + 16 * cur) * a.num_splits * 2), ml_bytes);
+      make_rsrc(uniform_ptr(part_ml + (2 * head0 + 16 * cur) * a.num_splits * 2), ml_bytes);
   constexpr int kTasks = 16 * (kHeadDim / 4);                     // (head, 4 dims) items
   // (a merger's slice, at most 8 heads, is at most 4 floats per thread)
   static_assert(kOut != kOutMerged || kW >= 4, "merging needs 256 threads");
@@ -745,8 +756,8 @@ sparse_decode_kernel(DecodeArgs a, StepArgs st) {
       float4_t acc;
       float M, l;
       wg_merge(h, d4, acc, M, l);
-      float* po = a.part_o + ((head0 + h) * a.num_splits + s) * kHeadDim + 4 * d4;
-      float* pm = a.part_ml + ((head0 + h) * a.num_splits + s) * 2;
+      float* po = part_o + ((head0 + h) * a.num_splits + s) * kHeadDim + 4 * d4;
+      float* pm = part_ml + ((head0 + h) * a.num_splits + s) * 2;
       *reinterpret_cast<float4_t*>(po) = acc;
       if (d4 == 0) {
         pm[0] = M;
