@@ -180,6 +180,46 @@ namespace msa {
 // No barriers, no LDS.
 template <int kR>
 __device__ __forceinline__ void wave_topk(const uint32_t (&key)[kR], int want, bool (&take)[kR], int& before) {
+  // Counting: up to 16 keys per lane one ballot and popcount per register; with 32 each
+  // lane counts its own keys and one DPP sum (or prefix sum) adds the lanes (measured:
+  // faster with 32 keys per lane, slightly slower with 16, the same with 8).
+  constexpr bool kLaneCount = kR >= 32;
+  // Ties at the largest real key (want or more candidates share it): that key is the
+  // threshold, nothing lies above it, and the first `want` keys equal to it in candidate
+  // order are the selection, found without the bit-by-bit search (which could never
+  // stop early) and without the counts below.
+  uint32_t k_max = 0u;
+#pragma unroll
+  for (int i = 0; i < kR; ++i) k_max = max(k_max, key[i]);
+  k_max = wave_max_u32(k_max);
+  int n_max = 0;
+  int max_before = 0;   // keys equal to k_max in earlier lanes
+  if constexpr (kLaneCount) {
+    uint32_t c = 0u;
+#pragma unroll
+    for (int i = 0; i < kR; ++i) c += key[i] == k_max;
+    const uint32_t incl = wave_scan_add_u32(c);
+    n_max = static_cast<int>(__builtin_amdgcn_readlane(static_cast<int>(incl), 63));
+    max_before = static_cast<int>(incl - c);
+  } else {
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+      const uint64_t m = __ballot(key[i] == k_max);
+      n_max += __popcll(m);
+      max_before += __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                              __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+    }
+  }
+  if (k_max != 0u && n_max >= want) {
+    int tb = max_before;
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+      take[i] = key[i] == k_max && tb < want;
+      tb += key[i] == k_max;
+    }
+    before = min(max_before, want);   // the taken keys are the first `want` ties
+    return;
+  }
   int n_real = 0;
 #pragma unroll
   for (int i = 0; i < kR; ++i) n_real += __popcll(__ballot(key[i] != 0u));
@@ -193,26 +233,6 @@ __device__ __forceinline__ void wave_topk(const uint32_t (&key)[kR], int want, b
     }
     before = b;
     return;
-  }
-  // Ties at the largest key (want or more candidates share it): that key is the
-  // threshold, without a bit-by-bit search that could never stop early.
-  uint32_t k_max = 0u;
-#pragma unroll
-  for (int i = 0; i < kR; ++i) k_max = max(k_max, key[i]);
-  k_max = wave_max_u32(k_max);
-  // Counting: up to 16 keys per lane one ballot and popcount per register; with 32 each
-  // lane counts its own keys and one DPP sum (or prefix sum) adds the lanes (measured:
-  // faster with 32 keys per lane, slightly slower with 16, the same with 8).
-  constexpr bool kLaneCount = kR >= 32;
-  int n_max = 0;
-  if constexpr (kLaneCount) {
-    uint32_t c = 0u;
-#pragma unroll
-    for (int i = 0; i < kR; ++i) c += key[i] == k_max;
-    n_max = static_cast<int>(wave_sum_u32(c));
-  } else {
-#pragma unroll
-    for (int i = 0; i < kR; ++i) n_max += __popcll(__ballot(key[i] == k_max));
   }
   // The bits every candidate shares are the threshold's too: start below them.
   uint32_t k_or = 0u, k_and = ~0u;
@@ -256,11 +276,6 @@ __device__ __forceinline__ void wave_topk(const uint32_t (&key)[kR], int want, b
   };
   int bit = top;
   bool done = false;
-  if (n_max >= want) {
-    T = k_max;
-    bit = -1;
-    done = true;
-  }
   for (; bit >= 1; bit -= 2) {                   // bits bit, bit-1
     const uint32_t c1 = T | (1u << (bit - 1)), c2 = T | (2u << (bit - 1)), c3 = T | (3u << (bit - 1));
     int n1, n2;
@@ -467,12 +482,16 @@ __device__ __forceinline__ int multiwave_select_level1(const float* srow, const 
     float sv[kR];
     int32_t pg[kR];
     if constexpr (kPoll) nb = min(*row_pos / MSA_PAGE_SIZE + 1, max_blocks);
+    // Candidate slots past the row's table read as 0 through buffer resources of the
+    // table's extent (no branch around a load); nothing uses their values.
+    const uint32_t row_bytes = static_cast<uint32_t>(max(max_blocks - lo, 0)) * 4u;
+    const __amdgpu_buffer_rsrc_t br = make_rsrc(uniform_ptr(bt + lo), row_bytes);
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(uniform_ptr(srow + lo), kPoll ? 0u : row_bytes);
 #pragma unroll
     for (int i = 0; i < kR; ++i) {
-      const int c = c0 + lane * kR + i;
-      const bool in_row = lo + c < max_blocks;
-      if constexpr (!kPoll) sv[i] = in_row ? srow[lo + c] : 0.0f;
-      pg[i] = in_row ? bt[lo + c] : -1;
+      const int off = (c0 + lane * kR + i) * 4;
+      if constexpr (!kPoll) sv[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, off, 0, 0));
+      pg[i] = static_cast<int32_t>(__builtin_amdgcn_raw_buffer_load_b32(br, off, 0, 0));
     }
     const int32_t pg_init = wave == 0 && lane < n_init && lane < max_blocks ? bt[lane] : -1;   // blocks below lo
     // slots past every wave's hold only forced last blocks (n_local <= 64): the last
@@ -561,18 +580,22 @@ __device__ __forceinline__ int multiwave_select_level1(const float* srow, const 
 template <int kR>
 __device__ __forceinline__ void multiwave_select_level2(int nb, int k, int n_init, int n_local, int nw, int* sel,
                                                         int* pages, const MultiSelectSmem& ms) {
+  static_assert(64 * kR <= 8 * MSA_MAX_TOPK, "the level-2 reads stay inside the lists");
   const int lane = threadIdx.x & 63;
   const int want = k - n_init - n_local;
   if (nb <= k || want <= 0) return;
   const int n = nw * want;
   uint32_t key[kR];
   int32_t blk[kR], pg[kR];
+  // (every read stays inside the lists, 64 kR <= 8 * MSA_MAX_TOPK entries; blk and pg
+  // of a slot past n are never used, since its key is 0 and it is not taken)
 #pragma unroll
   for (int i = 0; i < kR; ++i) {
     const int j = lane * kR + i;
-    key[i] = j < n ? ms.key[j] : 0u;
-    blk[i] = j < n ? ms.blk[j] : -1;
-    pg[i] = j < n ? ms.pg[j] : -1;
+    key[i] = ms.key[j];
+    blk[i] = ms.blk[j];
+    pg[i] = ms.pg[j];
+    if (j >= n) key[i] = 0u;
   }
   bool take[kR];
   int before;

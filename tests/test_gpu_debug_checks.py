@@ -30,7 +30,7 @@ def _print(*a):
 
 
 @pytest.mark.parametrize("fmt", [W.FMT_FP8, W.FMT_NVFP4])
-@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("fused", [True, False, "single"])
 def test_valid_step_reports_nothing_and_matches_release(M, dbg, fmt, fused):
     wl = W.small(fmt, [1000, 2600, 130], 2, num_kv_heads=2, k=5, seed=95)
     _print("debug build, valid step", wl.name, "fused", fused)
