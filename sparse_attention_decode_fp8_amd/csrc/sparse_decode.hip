@@ -146,8 +146,12 @@ __device__ __forceinline__ void load_round(Round<kFmt, kItems>& rd, const Decode
     load_chunk<kFmt>(rd.R[j], kv, page * a.hkv + g, valid, c, n, q);
     rd.kps[j] = rd.vps[j] = 1.0f;
     if constexpr (kFmt == MSA_KV_FP8_E4M3) {   // the page's scales (page 0 for an empty chunk)
-      rd.kps[j] = reinterpret_cast<const float*>(kv.k_scales)[page];
-      rd.vps[j] = reinterpret_cast<const float*>(kv.v_scales)[page];
+      // (vector loads through resources: a plain load from the register-pinned pointer
+      // would be a flat access, which every later wait on the LDS counter also waits for)
+      rd.kps[j] = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(kv.k_scales + page * 4, 4u), 0, 0, 0));
+      rd.vps[j] = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(kv.v_scales + page * 4, 4u), 0, 0, 0));
     }
     rd.hits[j] = 0u;
     if constexpr (kStep)
@@ -756,8 +760,9 @@ sparse_decode_kernel(DecodeArgs a, StepArgs st) {
       float4_t acc;
       float M, l;
       wg_merge(h, d4, acc, M, l);
-      float* po = part_o + ((head0 + h) * a.num_splits + s) * kHeadDim + 4 * d4;
-      float* pm = part_ml + ((head0 + h) * a.num_splits + s) * 2;
+      // (through the argument pointers, which the compiler knows to be global memory)
+      float* po = a.part_o + ((head0 + h) * a.num_splits + s) * kHeadDim + 4 * d4;
+      float* pm = a.part_ml + ((head0 + h) * a.num_splits + s) * 2;
       *reinterpret_cast<float4_t*>(po) = acc;
       if (d4 == 0) {
         pm[0] = M;
