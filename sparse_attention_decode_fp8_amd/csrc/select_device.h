@@ -169,21 +169,70 @@ __device__ void block_select_row(const float* srow, int nb, int k, int n_init, i
 
 namespace msa {
 
-// Exact top `want` of the keys a wave holds, kR per lane in candidate order lane-major
-// (lane L holds candidates L*kR .. L*kR+kR-1): take[i] marks the chosen keys, those above
-// the want-th largest key T and, of the keys equal to T, the first ones in candidate
-// order; `before` counts the chosen keys in earlier lanes. Key 0 marks an empty slot
+// Candidate order of the keys a wave holds, kR per lane: lane-major (lane L holds
+// candidates L kR .. L kR + kR - 1) or register-major (register i of lane L holds
+// candidate 64 i + L, so that a load of one register is 64 consecutive words).
+//
+// Ranks in candidate order of the keys where p holds: r[i] counts the such keys before
+// key i; returns their number. With 32 keys per lane (lane-major only) each lane counts
+// its own and one DPP prefix sum adds the lanes; otherwise one ballot per register.
+template <int kR, bool kLaneMajor>
+__device__ __forceinline__ int wave_ranks(const bool (&p)[kR], int (&r)[kR]) {
+  if constexpr (kLaneMajor && kR >= 32) {
+    uint32_t c = 0u;
+#pragma unroll
+    for (int i = 0; i < kR; ++i) c += p[i];
+    const uint32_t incl = wave_scan_add_u32(c);
+    int b = static_cast<int>(incl - c);
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+      r[i] = b;
+      b += p[i];
+    }
+    return __builtin_amdgcn_readlane(static_cast<int>(incl), 63);
+  } else if constexpr (kLaneMajor) {
+    int b = 0, total = 0;
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+      const uint64_t m = __ballot(p[i]);
+      b += __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+      total += __popcll(m);
+    }
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+      r[i] = b;
+      b += p[i];
+    }
+    return total;
+  } else {
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+      const uint64_t m = __ballot(p[i]);
+      r[i] = base + static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                               __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u)));
+      base += __popcll(m);
+    }
+    return base;
+  }
+}
+
+// Exact top `want` of the keys a wave holds (kR per lane, in the candidate order above):
+// take[i] marks the chosen keys, those above the want-th largest key T and, of the keys
+// equal to T, the first ones in candidate order; pos[i] is a chosen key's rank among the
+// chosen ones in candidate order. Returns how many are chosen. Key 0 marks an empty slot
 // (below every real key); if there are no more than `want` real keys, all are taken.
 //
 // T is built two bits at a time from the highest bit in which the candidates differ
-// (three independent counts per step); ties at T are ranked with mbcnt prefix counts.
+// (three independent counts per step); ties at T are ranked in candidate order.
 // No barriers, no LDS.
-template <int kR>
-__device__ __forceinline__ void wave_topk(const uint32_t (&key)[kR], int want, bool (&take)[kR], int& before) {
+template <int kR, bool kLaneMajor = true>
+__device__ __forceinline__ int wave_topk(const uint32_t (&key)[kR], int want, bool (&take)[kR], int (&pos)[kR]) {
   // Counting: up to 16 keys per lane one ballot and popcount per register; with 32 each
   // lane counts its own keys and one DPP sum (or prefix sum) adds the lanes (measured:
   // faster with 32 keys per lane, slightly slower with 16, the same with 8).
   constexpr bool kLaneCount = kR >= 32;
+  static_assert(kLaneMajor || !kLaneCount, "32 keys per lane are held lane-major");
   // Ties at the largest real key (want or more candidates share it): that key is the
   // threshold, nothing lies above it, and the first `want` keys equal to it in candidate
   // order are the selection, found without the bit-by-bit search (which could never
@@ -192,47 +241,27 @@ __device__ __forceinline__ void wave_topk(const uint32_t (&key)[kR], int want, b
 #pragma unroll
   for (int i = 0; i < kR; ++i) k_max = max(k_max, key[i]);
   k_max = wave_max_u32(k_max);
-  int n_max = 0;
-  int max_before = 0;   // keys equal to k_max in earlier lanes
-  if constexpr (kLaneCount) {
-    uint32_t c = 0u;
+  bool p[kR];
+  int r[kR];
 #pragma unroll
-    for (int i = 0; i < kR; ++i) c += key[i] == k_max;
-    const uint32_t incl = wave_scan_add_u32(c);
-    n_max = static_cast<int>(__builtin_amdgcn_readlane(static_cast<int>(incl), 63));
-    max_before = static_cast<int>(incl - c);
-  } else {
-#pragma unroll
-    for (int i = 0; i < kR; ++i) {
-      const uint64_t m = __ballot(key[i] == k_max);
-      n_max += __popcll(m);
-      max_before += __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
-                                              __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
-    }
-  }
+  for (int i = 0; i < kR; ++i) p[i] = key[i] == k_max;
+  const int n_max = wave_ranks<kR, kLaneMajor>(p, r);
   if (k_max != 0u && n_max >= want) {
-    int tb = max_before;
 #pragma unroll
     for (int i = 0; i < kR; ++i) {
-      take[i] = key[i] == k_max && tb < want;
-      tb += key[i] == k_max;
+      take[i] = p[i] && r[i] < want;
+      pos[i] = r[i];
     }
-    before = min(max_before, want);   // the taken keys are the first `want` ties
-    return;
+    return want;
   }
   int n_real = 0;
 #pragma unroll
   for (int i = 0; i < kR; ++i) n_real += __popcll(__ballot(key[i] != 0u));
   if (n_real <= want) {                                   // every real key
-    int b = 0;
 #pragma unroll
-    for (int i = 0; i < kR; ++i) {
-      take[i] = key[i] != 0u;
-      const uint64_t m = __ballot(take[i]);
-      b += __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
-    }
-    before = b;
-    return;
+    for (int i = 0; i < kR; ++i) take[i] = key[i] != 0u;
+    wave_ranks<kR, kLaneMajor>(take, pos);
+    return n_real;
   }
   // The bits every candidate shares are the threshold's too: start below them.
   uint32_t k_or = 0u, k_and = ~0u;
@@ -295,46 +324,32 @@ __device__ __forceinline__ void wave_topk(const uint32_t (&key)[kR], int want, b
   }
   if (!done && bit == 0 && count_ge(T | 1u) >= want) T |= 1u;
 
+  // keys above T (their number) and the ranks of the keys equal to T
   int gt = 0;
-  int tie_before = 0;   // keys equal to T in earlier lanes (block order is lane-major)
   if constexpr (kLaneCount) {
     uint32_t m = 0u;   // this lane's keys above T (low half) and equal to T (high half)
 #pragma unroll
     for (int i = 0; i < kR; ++i) m += (key[i] > T ? 1u : 0u) + (key[i] == T ? 0x10000u : 0u);
     const uint32_t incl = wave_scan_add_u32(m);
     gt = static_cast<int>(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), 63)) & 0xffffu);
-    tie_before = static_cast<int>((incl - m) >> 16);
+    int tb = static_cast<int>((incl - m) >> 16);
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+      r[i] = tb;
+      tb += key[i] == T;
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < kR; ++i) gt += __popcll(__ballot(key[i] > T));
 #pragma unroll
-    for (int i = 0; i < kR; ++i) {
-      const uint64_t m = __ballot(key[i] == T);
-      tie_before += __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
-                                              __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
-    }
+    for (int i = 0; i < kR; ++i) p[i] = key[i] == T;
+    wave_ranks<kR, kLaneMajor>(p, r);
   }
   const int need = want - gt;                            // keys equal to T to take
-  int tb = tie_before;
 #pragma unroll
-  for (int i = 0; i < kR; ++i) {
-    take[i] = key[i] > T || (key[i] == T && tb < need);
-    tb += key[i] == T;
-  }
-  before = 0;   // taken keys in earlier lanes
-  if constexpr (kLaneCount) {
-    uint32_t m = 0u;
-#pragma unroll
-    for (int i = 0; i < kR; ++i) m += take[i];
-    before = static_cast<int>(wave_scan_add_u32(m) - m);
-  } else {
-#pragma unroll
-    for (int i = 0; i < kR; ++i) {
-      const uint64_t m = __ballot(take[i]);
-      before += __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
-                                          __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
-    }
-  }
+  for (int i = 0; i < kR; ++i) take[i] = key[i] > T || (key[i] == T && r[i] < need);
+  wave_ranks<kR, kLaneMajor>(take, pos);
+  return want;
 }
 
 // Wave-level (64-lane) selection for one row, without barriers or LDS atomics. Lane L
@@ -416,15 +431,13 @@ __device__ __forceinline__ void wave_select_table(const float* srow, const int32
   }
 
   bool take[kR];
-  int before;
-  wave_topk<kR>(key, want, take, before);
-  int at = n_init + before;
+  int pos[kR];
+  wave_topk<kR>(key, want, take, pos);
 #pragma unroll
   for (int i = 0; i < kR; ++i) {
     if (take[i]) {
-      sel[at] = lo + lane * kR + i;
-      pages[at] = pg[i];
-      ++at;
+      sel[n_init + pos[i]] = lo + lane * kR + i;
+      pages[n_init + pos[i]] = pg[i];
     }
   }
   write_local();
@@ -444,7 +457,9 @@ struct MultiSelectSmem {
 // the table is then in sel / pages as wave_select_table writes it.
 //
 // Level 1: wave w (< nw) takes candidate slots [64 kR w, 64 kR (w + 1)) (block lo + c,
-// lane-major inside the wave), reads their scores and pages, and picks its own top
+// register-major inside the wave: one load per register reads 64 consecutive words, where
+// lane-major loads would touch kR times as many cache lines each, and the compute unit
+// looks them up one by one), reads their scores and pages, and picks its own top
 // `want` by the selection order (higher score, then smaller block); it writes them in
 // block order to slots [w want, (w + 1) want) of the LDS list (key 0 in unused slots).
 // The block-order list then holds every block of the row's top `want`: such a block is
@@ -489,7 +504,7 @@ __device__ __forceinline__ int multiwave_select_level1(const float* srow, const 
     const __amdgpu_buffer_rsrc_t sr = make_rsrc(uniform_ptr(srow + lo), kPoll ? 0u : row_bytes);
 #pragma unroll
     for (int i = 0; i < kR; ++i) {
-      const int off = (c0 + lane * kR + i) * 4;
+      const int off = (c0 + 64 * i + lane) * 4;
       if constexpr (!kPoll) sv[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, off, 0, 0));
       pg[i] = static_cast<int32_t>(__builtin_amdgcn_raw_buffer_load_b32(br, off, 0, 0));
     }
@@ -510,7 +525,7 @@ __device__ __forceinline__ int multiwave_select_level1(const float* srow, const 
           uint32_t key = ~0u;
 #pragma unroll
           for (int i = 0; i < kR; ++i) {
-            sv[i] = load_coherent1(xr, static_cast<uint32_t>(lo + c0 + lane * kR + i) * 4u);
+            sv[i] = load_coherent1(xr, static_cast<uint32_t>(lo + c0 + 64 * i + lane) * 4u);
             key = idle_key(key, sv[i]);
           }
           ready = __ballot(key == 0u) == 0;
@@ -527,7 +542,7 @@ __device__ __forceinline__ int multiwave_select_level1(const float* srow, const 
         if (lane < lo && lane < nb) { sel[lane] = lane; pages[lane] = pg_init; }
 #pragma unroll
         for (int i = 0; i < kR; ++i) {
-          const int b = lo + lane * kR + i;
+          const int b = lo + 64 * i + lane;
           if (b < nb) { sel[b] = b; pages[b] = pg[i]; }
         }
         if (lane >= nb) { sel[lane] = -1; pages[lane] = -1; }
@@ -540,7 +555,7 @@ __device__ __forceinline__ int multiwave_select_level1(const float* srow, const 
       // forced last blocks: slots C .. C + n_local - 1
 #pragma unroll
       for (int i = 0; i < kR; ++i) {
-        const int c = c0 + lane * kR + i;
+        const int c = c0 + 64 * i + lane;
         if (c >= C && c < C + n_local) { sel[k - n_local + c - C] = lo + c; pages[k - n_local + c - C] = pg[i]; }
       }
       if (wave == nw - 1 && ct >= C && ct < C + n_local) {
@@ -549,25 +564,21 @@ __device__ __forceinline__ int multiwave_select_level1(const float* srow, const 
       }
       uint32_t key[kR];
 #pragma unroll
-      for (int i = 0; i < kR; ++i) key[i] = c0 + lane * kR + i < C ? float_key(sv[i]) : 0u;   // 0: below every real key
+      for (int i = 0; i < kR; ++i) key[i] = c0 + 64 * i + lane < C ? float_key(sv[i]) : 0u;   // 0: below every real key
       if (want > 0) {
         bool take[kR];
-        int before;
-        wave_topk<kR>(key, want, take, before);
+        int pos[kR];
+        const int n_taken = wave_topk<kR, false>(key, want, take, pos);
         // this wave's picks, in block order, then key-0 slots up to `want`
-        int at = wave * want + before;
 #pragma unroll
         for (int i = 0; i < kR; ++i) {
           if (take[i]) {
+            const int at = wave * want + pos[i];
             ms.key[at] = key[i];
-            ms.blk[at] = lo + c0 + lane * kR + i;
+            ms.blk[at] = lo + c0 + 64 * i + lane;
             ms.pg[at] = pg[i];
-            ++at;
           }
         }
-        int n_taken = 0;
-#pragma unroll
-        for (int i = 0; i < kR; ++i) n_taken += __popcll(__ballot(take[i]));
         for (int j = n_taken + lane; j < want; j += 64) ms.key[wave * want + j] = 0u;
       }
     }
@@ -598,15 +609,13 @@ __device__ __forceinline__ void multiwave_select_level2(int nb, int k, int n_ini
     if (j >= n) key[i] = 0u;
   }
   bool take[kR];
-  int before;
-  wave_topk<kR>(key, want, take, before);
-  int at = n_init + before;
+  int pos[kR];
+  wave_topk<kR>(key, want, take, pos);
 #pragma unroll
   for (int i = 0; i < kR; ++i) {
     if (take[i]) {
-      sel[at] = blk[i];
-      pages[at] = pg[i];
-      ++at;
+      sel[n_init + pos[i]] = blk[i];
+      pages[n_init + pos[i]] = pg[i];
     }
   }
 }
