@@ -453,8 +453,10 @@ struct MultiSelectSmem {
 
 // Two-level selection for one row by `nw` waves of a workgroup (1 <= nw <= 8; nw * 64 kR
 // slots cover every candidate, and nw * want <= 64 kR): multiwave_select_level1 in every
-// wave, a workgroup barrier, multiwave_select_level2 in wave 0, and another barrier;
-// the table is then in sel / pages as wave_select_table writes it.
+// wave, a workgroup barrier, and, with nw > 1, multiwave_select_level2 in wave 0 and
+// another barrier; the table is then in sel / pages as wave_select_table writes it.
+// kOneWave (the caller's nw is 1): the single first-level wave writes the whole table
+// itself, and the caller runs no second level.
 //
 // Level 1: wave w (< nw) takes candidate slots [64 kR w, 64 kR (w + 1)) (block lo + c,
 // register-major inside the wave: one load per register reads 64 consecutive words, where
@@ -483,7 +485,7 @@ struct ScorePoll {
   int limit;
   bool timed_out;
 };
-template <int kR, bool kPoll = false>
+template <int kR, bool kPoll = false, bool kOneWave = false>
 __device__ __forceinline__ int multiwave_select_level1(const float* srow, const int32_t* bt, int max_blocks,
                                                        const int32_t* row_pos, int k, int n_init, int n_local,
                                                        int nw, int* sel, int* pages, MultiSelectSmem& ms,
@@ -569,17 +571,28 @@ __device__ __forceinline__ int multiwave_select_level1(const float* srow, const 
         bool take[kR];
         int pos[kR];
         const int n_taken = wave_topk<kR, false>(key, want, take, pos);
-        // this wave's picks, in block order, then key-0 slots up to `want`
+        if constexpr (kOneWave) {
+          // one first-level wave: its picks are the selection (no second level)
 #pragma unroll
-        for (int i = 0; i < kR; ++i) {
-          if (take[i]) {
-            const int at = wave * want + pos[i];
-            ms.key[at] = key[i];
-            ms.blk[at] = lo + c0 + 64 * i + lane;
-            ms.pg[at] = pg[i];
+          for (int i = 0; i < kR; ++i) {
+            if (take[i]) {
+              sel[n_init + pos[i]] = lo + c0 + 64 * i + lane;
+              pages[n_init + pos[i]] = pg[i];
+            }
           }
+        } else {
+          // this wave's picks, in block order, then key-0 slots up to `want`
+#pragma unroll
+          for (int i = 0; i < kR; ++i) {
+            if (take[i]) {
+              const int at = wave * want + pos[i];
+              ms.key[at] = key[i];
+              ms.blk[at] = lo + c0 + 64 * i + lane;
+              ms.pg[at] = pg[i];
+            }
+          }
+          for (int j = n_taken + lane; j < want; j += 64) ms.key[wave * want + j] = 0u;
         }
-        for (int j = n_taken + lane; j < want; j += 64) ms.key[wave * want + j] = 0u;
       }
     }
   }

@@ -261,8 +261,10 @@ __device__ __forceinline__ bool merge_handoff(int32_t* word, uint32_t buffer, in
 // of the (row, KV head) merging them all into the bf16 output (kOutMerged). The direct
 // variant holds none of the merge code, and so fewer registers. kSelect: 0 = the
 // caller's table; 1, 2, 4 or 8 = the workgroup selects, with the two-level selection at
-// kSelect keys per lane (or the block radix select for rows too long for it).
+// kSelect keys per lane (or the block radix select for rows too long for it);
+// kSelectOneWave = at most 64 candidates, one first-level wave and no second level.
 constexpr int kOutPartials = 0, kOutDirect = 1, kOutMerged = 2;
+constexpr int kSelectOneWave = 16;
 
 // The single-launch step's scoring share of one workgroup. The decode workgroups of a
 // group of rows (up to 16 / kStepHi rows of one request, cut in request order, as the
@@ -302,6 +304,7 @@ __global__ void __launch_bounds__(64 * kW)
 __attribute__((amdgpu_waves_per_eu(decode_min_waves_per_simd<kW, kOut, kStep>())))
 sparse_decode_kernel(DecodeArgs a, StepArgs st) {
   static_assert(!kStep || kSelect, "the single-launch step selects");
+  constexpr int kSelR = kSelect == kSelectOneWave ? 1 : kSelect;   // keys per lane of the selection
   // Dynamic LDS: the row's selection keys (selecting variant, before any V is staged),
   // then the per-wave V staging buffers and, at the end, the per-wave O tiles.
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
@@ -511,9 +514,8 @@ sparse_decode_kernel(DecodeArgs a, StepArgs st) {
       const int32_t* btg = a.block_table + static_cast<int64_t>(guess) * a.max_blocks;
       MultiSelectSmem& ms = *reinterpret_cast<MultiSelectSmem*>(dyn_lds);
       ScorePoll sp{kStep ? st.sc.xscores + trow * a.max_blocks : nullptr, a.poll_limit, false};
-      const int nb = multiwave_select_level1<kSelect, kStep>(srow, btg, a.max_blocks, a.row_pos + r, a.k,
-                                                             a.n_init, a.n_local, a.sel_waves, lsel, lpage, ms,
-                                                             &sp);
+      const int nb = multiwave_select_level1<kSelR, kStep, kSelect == kSelectOneWave>(
+          srow, btg, a.max_blocks, a.row_pos + r, a.k, a.n_init, a.n_local, a.sel_waves, lsel, lpage, ms, &sp);
       if (wave == kW - 1) {   // (while the first level runs, unless this wave is part of it)
         convert_q();
 #pragma unroll
@@ -527,8 +529,10 @@ sparse_decode_kernel(DecodeArgs a, StepArgs st) {
       } else {
         __syncthreads();
       }
-      if (wave == 0) multiwave_select_level2<kSelect>(nb, a.k, a.n_init, a.n_local, a.sel_waves, lsel, lpage, ms);
-      __syncthreads();
+      if constexpr (kSelect != kSelectOneWave) {   // (one first-level wave wrote the table itself)
+        if (wave == 0) multiwave_select_level2<kSelR>(nb, a.k, a.n_init, a.n_local, a.sel_waves, lsel, lpage, ms);
+        __syncthreads();
+      }
       selv = lsel[lane];
       pagev = lpage[lane];
       if (seq != guess) {
@@ -1009,7 +1013,8 @@ msa_status_t decode_entry(const msa_kv_pool_t* pool, const msa_step_t* step, int
   // (rows too long for the two-level selection take the block radix select, in the
   // 8-keys-per-lane instance of the kernel)
 #define MSA_DECODE_SELECT(FMT, OUT)                                                                    \
-  (kr == 1 ? dispatch<FMT, OUT, 1>(a, grid, s) : kr == 2 ? dispatch<FMT, OUT, 2>(a, grid, s)          \
+  (kr == 1 ? (a.sel_waves == 1 ? dispatch<FMT, OUT, kSelectOneWave>(a, grid, s) : dispatch<FMT, OUT, 1>(a, grid, s)) \
+   : kr == 2 ? dispatch<FMT, OUT, 2>(a, grid, s)                                                       \
    : kr == 4 ? dispatch<FMT, OUT, 4>(a, grid, s) : dispatch<FMT, OUT, 8>(a, grid, s))
 #define MSA_DECODE_DISPATCH(FMT)                                                                       \
   (select ? (direct ? MSA_DECODE_SELECT(FMT, kOutDirect) : MSA_DECODE_SELECT(FMT, kOutMerged))        \
