@@ -67,8 +67,10 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<kFmt>& R, const KvArrays& a
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const uint32_t t = t0 + 16u * u;
-      R.k[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kc, static_cast<int>(t * (kHeadDim / 2) + 16 * q), 0, 0));
-      R.v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vc, static_cast<int>(t * (kHeadDim / 2) + 16 * q), 0, 0));
+      R.k[u] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(kc, static_cast<int>(t * (kHeadDim / 2) + 16 * q), 0, kStreamPolicy));
+      R.v[u] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(vc, static_cast<int>(t * (kHeadDim / 2) + 16 * q), 0, kStreamPolicy));
       R.ks[u] = __builtin_amdgcn_raw_buffer_load_b16(ks, static_cast<int>(t * (kHeadDim / 16) + 2 * q), 0, 0);
       R.vs[u] = __builtin_amdgcn_raw_buffer_load_b16(vs, static_cast<int>(t * (kHeadDim / 16) + 2 * q), 0, 0);
     }

@@ -174,7 +174,8 @@ __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
         // 8 contiguous scale bytes
         const int64_t at = (page * (kIndexDim / 16) + q) * kPage + n * 8;
         const uint4* kp = reinterpret_cast<const uint4*>(a.index_k + at * 8);
-        const uint4 c0 = kp[0], c1 = kp[1], c2 = kp[2], c3 = kp[3];
+        const uint4 c0 = load_stream16(kp), c1 = load_stream16(kp + 1), c2 = load_stream16(kp + 2),
+                    c3 = load_stream16(kp + 3);
         const uint2 sc = *reinterpret_cast<const uint2*>(a.index_scales + at);
         const uint4 c[4] = {c0, c1, c2, c3};
 #pragma unroll
@@ -187,7 +188,7 @@ __global__ void __launch_bounds__(64 * kWaves) score_kernel(ScoreArgs a) {
       } else {
         const uint8_t* kp = a.index_k + tok0 * kIndexDim + 16 * q;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) key[t] = *reinterpret_cast<const uint4*>(kp + t * 16 * kIndexDim);
+        for (int t = 0; t < 8; ++t) key[t] = load_stream16(kp + t * 16 * kIndexDim);
       }
     };
     if (seq != guess) page = a.block_table[static_cast<int64_t>(seq) * a.max_blocks + b];

@@ -124,7 +124,8 @@ __device__ __forceinline__ int32_t score_blocks(const StepScoreArgs& sa, const i
 #pragma unroll
     for (int t = 0; t < 8; ++t)
       key[j][t] = __builtin_bit_cast(
-          uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, static_cast<int>((16 * t + n) * kIndexDim + 16 * q), 0, 0));
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, static_cast<int>((16 * t + n) * kIndexDim + 16 * q), 0,
+                                                       kStreamPolicy));
   }
   // the page of row r0 + self's last visible block (its load queues behind the keys')
   const int32_t self_last_page = btr[min(__shfl(pl, self, 64) / kPage, max_blocks - 1)];
